@@ -1,0 +1,342 @@
+// C ABI of the KDA library: host-side validation, workspace carving and
+// kernel launches.  No arithmetic of the method happens here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_stage_ev[3] = {nullptr, nullptr, nullptr};
+
+hipError_t record_stage(int i, hipStream_t s) {
+  return g_stage_ev[i] ? hipEventRecord(g_stage_ev[i], s) : hipSuccess;
+}
+
+kda_status_t fail(kda_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kda_status_t fail(kda_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+kda_status_t ok() {
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+constexpr int kBT = 64;
+constexpr uint32_t kAllFlags = KDA_GATE_IN_KERNEL | KDA_SAFE_GATE | KDA_QK_L2NORM | KDA_BETA_SIGMOID;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Plan {
+  int64_t tokens = 0;     // tokens in the token tensors
+  int64_t nchunks = 0;    // chunks over all sequences
+  int N = 0;
+  size_t es = 0;          // element size of token tensors
+  // workspace offsets
+  size_t off_chunk = 0, off_w = 0, off_u = 0, off_kg = 0, off_qg = 0, off_aqk = 0, off_gd = 0;
+  size_t bytes = 0;
+};
+
+// Shape / flag validation shared by every token-level call; fills the plan.
+kda_status_t plan_problem(const kda_problem_t* p, bool forward, Plan& pl) {
+  if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "problem descriptor is NULL");
+  if (p->layout != KDA_LAYOUT_BSND && p->layout != KDA_LAYOUT_TND)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "layout %d is neither BSND (0) nor TND (1)", p->layout);
+  if (p->dtype != KDA_F32 && p->dtype != KDA_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dtype %d is neither F32 (0) nor BF16 (1)", p->dtype);
+  if (p->chunk_size != kBT)
+    return fail(KDA_ERR_UNSUPPORTED, "chunk_size %d: only 64 is built", p->chunk_size);
+  if (p->Hk < 1 || p->Hv < 1 || p->Hv % p->Hk != 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "heads Hk=%d Hv=%d: need Hk >= 1 and Hv %% Hk == 0", p->Hk, p->Hv);
+  if (p->Hv > 65535) return fail(KDA_ERR_UNSUPPORTED, "Hv=%d exceeds 65535", p->Hv);
+  if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128))
+    return fail(KDA_ERR_UNSUPPORTED, "head dims K=%d V=%d: each must be 64 or 128", p->K, p->V);
+  if (p->dtype == KDA_F32 && p->K != 64)
+    return fail(KDA_ERR_UNSUPPORTED, "fp32 token tensors are built for K=64 only (got K=%d)", p->K);
+  if (p->flags & ~kAllFlags) return fail(KDA_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", p->flags & ~kAllFlags);
+  if (!std::isfinite(p->scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(KDA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if ((p->flags & KDA_SAFE_GATE) && !std::isfinite(p->lower_bound))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "lower_bound is not finite");
+  if (p->B < 0 || p->T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative B=%d or T=%d", p->B, p->T);
+  if (p->state_rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative state_rows");
+  if (!forward && p->state_rows != 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "summaries take no state cache (state_rows must be 0)");
+
+  pl.es = p->dtype == KDA_BF16 ? 2 : 4;
+  if (p->layout == KDA_LAYOUT_BSND) {
+    if (p->num_seqs != p->B)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "BSND needs num_seqs == B (got %d vs %d)", p->num_seqs, p->B);
+    if (p->cu_seqlens_host) return fail(KDA_ERR_INVALID_ARGUMENT, "BSND takes no cu_seqlens");
+    pl.N = p->B;
+    pl.tokens = (int64_t)p->B * p->T;
+    pl.nchunks = (int64_t)p->B * ((p->T + kBT - 1) / kBT);
+  } else {
+    if (p->B != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "TND needs B == 1 (got %d)", p->B);
+    if (p->num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative num_seqs");
+    if (!p->cu_seqlens_host) return fail(KDA_ERR_INVALID_ARGUMENT, "TND needs the host copy of cu_seqlens");
+    const int32_t* cu = p->cu_seqlens_host;
+    if (cu[0] != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] = %d, must be 0", cu[0]);
+    int64_t nc = 0;
+    for (int i = 0; i < p->num_seqs; ++i) {
+      if (cu[i + 1] < cu[i])
+        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %d (%d -> %d)", i, cu[i], cu[i + 1]);
+      nc += (cu[i + 1] - cu[i] + kBT - 1) / kBT;
+    }
+    if (cu[p->num_seqs] != p->T)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[N] = %d differs from T = %d", cu[p->num_seqs], p->T);
+    pl.N = p->num_seqs;
+    pl.tokens = p->T;
+    pl.nchunks = nc;
+  }
+  if (pl.nchunks > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many chunks (%lld)", (long long)pl.nchunks);
+  const int VA = forward ? p->V : p->V + p->K;
+  if ((int64_t)(VA / 32) * p->Hv * pl.N > 0x7fffffffLL)
+    return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head, tile) workgroups");
+
+  const size_t slots = (size_t)p->Hv * (size_t)pl.nchunks;
+  size_t off = 0;
+  pl.off_chunk = off;  off = align256(off + sizeof(int32_t) * (size_t)(pl.N + 1));
+  pl.off_w = off;      off = align256(off + slots * kBT * p->K * pl.es);
+  pl.off_u = off;      off = align256(off + slots * kBT * p->V * pl.es);
+  pl.off_kg = off;     off = align256(off + slots * kBT * p->K * pl.es);
+  if (forward) {
+    pl.off_qg = off;   off = align256(off + slots * kBT * p->K * pl.es);
+    pl.off_aqk = off;  off = align256(off + slots * kBT * kBT * pl.es);
+  }
+  pl.off_gd = off;     off = align256(off + slots * p->K * sizeof(float));
+  pl.bytes = off;
+  return KDA_OK;
+}
+
+kda_status_t check_token_ptr(const void* ptr, const char* name, size_t align) {
+  if (!ptr) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned(ptr, align)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %zu-byte aligned", name, align);
+  return KDA_OK;
+}
+
+kda::SeqInfo seq_info(const kda_problem_t* p, const Plan& pl, const int32_t* cu, void* ws) {
+  kda::SeqInfo s;
+  s.tnd = p->layout == KDA_LAYOUT_TND;
+  s.T = p->T;
+  s.N = pl.N;
+  s.cu = cu;
+  s.chunk_off = s.tnd ? reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + pl.off_chunk) : nullptr;
+  return s;
+}
+
+kda_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return KDA_OK;
+}
+
+// Launch the chunk-offset prologue (TND) and the chunk-local kernel.
+kda_status_t run_intra(const kda_problem_t* p, const Plan& pl, const kda::SeqInfo& si, const int32_t* cu,
+                       const void* q, const void* k, const void* v, const void* g, const void* beta,
+                       const float* A_log, const float* dt_bias, char* ws, hipStream_t s) {
+  if (si.tnd && pl.N > 0) {
+    kda_status_t st = hip_status(
+        kda::launch_chunk_offsets(cu, pl.N, reinterpret_cast<int32_t*>(ws + pl.off_chunk), s),
+        "chunk offsets launch");
+    if (st != KDA_OK) return st;
+  }
+  kda::IntraArgs a{};
+  a.seq = si;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.A_log = A_log; a.dt_bias = dt_bias;
+  a.Hk = p->Hk; a.Hv = p->Hv; a.nchunks = (int)pl.nchunks;
+  a.flags = p->flags; a.scale = p->scale; a.eps = p->eps; a.lower_bound = p->lower_bound;
+  a.w = ws + pl.off_w; a.u = ws + pl.off_u; a.kgT = ws + pl.off_kg;
+  a.qg = q ? ws + pl.off_qg : nullptr;
+  a.Aqk = q ? ws + pl.off_aqk : nullptr;
+  a.gdec = reinterpret_cast<float*>(ws + pl.off_gd);
+  return hip_status(kda::launch_intra(p->K, p->V, p->dtype, a, s), "intra-chunk kernel launch");
+}
+
+kda_status_t common_inputs(const kda_problem_t* p, const Plan& pl, const void* k, const void* v,
+                           const void* g, const void* beta, const float* A_log, const int32_t* cu) {
+  if (pl.tokens > 0) {
+    kda_status_t st;
+    if ((st = check_token_ptr(k, "k", 16)) != KDA_OK) return st;
+    if ((st = check_token_ptr(v, "v", 16)) != KDA_OK) return st;
+    if ((st = check_token_ptr(g, "g", 16)) != KDA_OK) return st;
+    if ((st = check_token_ptr(beta, "beta", pl.es)) != KDA_OK) return st;
+    if ((p->flags & KDA_GATE_IN_KERNEL) && !A_log)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "KDA_GATE_IN_KERNEL needs A_log");
+  }
+  if (p->layout == KDA_LAYOUT_TND && !cu) return fail(KDA_ERR_INVALID_ARGUMENT, "TND needs device cu_seqlens");
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status_t s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KDA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+kda_status_t kda_set_stage_events(void* begin, void* after_chunk_local, void* end) {
+  const bool all = begin && after_chunk_local && end, none = !begin && !after_chunk_local && !end;
+  if (!all && !none) return fail(KDA_ERR_INVALID_ARGUMENT, "pass three events or none");
+  g_stage_ev[0] = static_cast<hipEvent_t>(begin);
+  g_stage_ev[1] = static_cast<hipEvent_t>(after_chunk_local);
+  g_stage_ev[2] = static_cast<hipEvent_t>(end);
+  return ok();
+}
+
+kda_status_t kda_chunk_offsets_host(const int32_t* cu, int32_t N, int32_t chunk, int32_t* out) {
+  if (!cu || !out || N < 0 || chunk < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "bad chunk-offset arguments");
+  if (cu[0] != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] must be 0");
+  int64_t run = 0;
+  for (int i = 0; i < N; ++i) {
+    if (cu[i + 1] < cu[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %d", i);
+    out[i] = (int32_t)run;
+    run += (cu[i + 1] - cu[i] + chunk - 1) / chunk;
+    if (run > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many chunks");
+  }
+  out[N] = (int32_t)run;
+  return ok();
+}
+
+kda_status_t kda_chunk_fwd_workspace_size(const kda_problem_t* p, size_t* bytes) {
+  if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Plan pl;
+  kda_status_t st = plan_problem(p, true, pl);
+  if (st != KDA_OK) return st;
+  *bytes = pl.bytes;
+  return ok();
+}
+
+kda_status_t kda_segment_summary_workspace_size(const kda_problem_t* p, size_t* bytes) {
+  if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Plan pl;
+  kda_status_t st = plan_problem(p, false, pl);
+  if (st != KDA_OK) return st;
+  *bytes = pl.bytes;
+  return ok();
+}
+
+kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k, const void* v,
+                           const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                           const float* initial_state, const int32_t* cu_seqlens,
+                           const int32_t* state_indices, void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  kda_status_t st = plan_problem(p, true, pl);
+  if (st != KDA_OK) return st;
+  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, cu_seqlens)) != KDA_OK) return st;
+  if (pl.tokens > 0) {
+    if ((st = check_token_ptr(q, "q", 16)) != KDA_OK) return st;
+    if ((st = check_token_ptr(o, "o", 16)) != KDA_OK) return st;
+  }
+  if (p->state_rows > 0 && !state_indices)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "state_rows > 0 needs state_indices");
+  if (p->state_rows == 0 && state_indices)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "state_indices given without a state cache (state_rows == 0)");
+  if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "states must be 16-byte aligned");
+  if (workspace_bytes < pl.bytes)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+  if (pl.bytes && !workspace) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (pl.N == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  kda::SeqInfo si = seq_info(p, pl, cu_seqlens, ws);
+  if ((st = hip_status(record_stage(0, s), "stage event")) != KDA_OK) return st;
+  if ((st = run_intra(p, pl, si, cu_seqlens, q, k, v, g, beta, A_log, dt_bias, ws, s)) != KDA_OK) return st;
+  if ((st = hip_status(record_stage(1, s), "stage event")) != KDA_OK) return st;
+  kda::ScanArgs a{};
+  a.seq = si;
+  a.Hv = p->Hv; a.nchunks = (int)pl.nchunks; a.state_rows = p->state_rows; a.summary = 0;
+  a.w = ws + pl.off_w; a.u = ws + pl.off_u; a.kgT = ws + pl.off_kg;
+  a.qg = ws + pl.off_qg; a.Aqk = ws + pl.off_aqk;
+  a.gdec = reinterpret_cast<const float*>(ws + pl.off_gd);
+  a.h0 = initial_state; a.state_idx = state_indices; a.hT = final_state; a.M = nullptr; a.o = o;
+  if ((st = hip_status(kda::launch_scan(p->K, p->V, p->dtype, a, s), "state-scan kernel launch")) != KDA_OK)
+    return st;
+  if ((st = hip_status(record_stage(2, s), "stage event")) != KDA_OK) return st;
+  return ok();
+}
+
+kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const void* v, const void* g,
+                                 const void* beta, const float* A_log, const float* dt_bias,
+                                 const int32_t* cu_seqlens, float* M, float* S_tilde, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  Plan pl;
+  kda_status_t st = plan_problem(p, false, pl);
+  if (st != KDA_OK) return st;
+  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, cu_seqlens)) != KDA_OK) return st;
+  if (pl.N > 0 && (!M || !S_tilde)) return fail(KDA_ERR_INVALID_ARGUMENT, "M and S_tilde are required");
+  if ((M && !aligned(M, 16)) || (S_tilde && !aligned(S_tilde, 16)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "M and S_tilde must be 16-byte aligned");
+  if (workspace_bytes < pl.bytes)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+  if (pl.bytes && !workspace) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (pl.N == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  kda::SeqInfo si = seq_info(p, pl, cu_seqlens, ws);
+  if ((st = hip_status(record_stage(0, s), "stage event")) != KDA_OK) return st;
+  if ((st = run_intra(p, pl, si, cu_seqlens, nullptr, k, v, g, beta, A_log, dt_bias, ws, s)) != KDA_OK)
+    return st;
+  if ((st = hip_status(record_stage(1, s), "stage event")) != KDA_OK) return st;
+  kda::ScanArgs a{};
+  a.seq = si;
+  a.Hv = p->Hv; a.nchunks = (int)pl.nchunks; a.state_rows = 0; a.summary = 1;
+  a.w = ws + pl.off_w; a.u = ws + pl.off_u; a.kgT = ws + pl.off_kg;
+  a.gdec = reinterpret_cast<const float*>(ws + pl.off_gd);
+  a.hT = S_tilde; a.M = M;
+  if ((st = hip_status(kda::launch_scan(p->K, p->V, p->dtype, a, s), "summary scan kernel launch")) != KDA_OK)
+    return st;
+  if ((st = hip_status(record_stage(2, s), "stage event")) != KDA_OK) return st;
+  return ok();
+}
+
+kda_status_t kda_summary_merge(int32_t P, int32_t Hv, int32_t K, int32_t V, const float* M,
+                               const float* S_tilde, float* state, void* stream) {
+  if (P < 0 || Hv < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "need P >= 0 and Hv >= 1 (P=%d Hv=%d)", P, Hv);
+  if ((K != 64 && K != 128) || (V != 64 && V != 128))
+    return fail(KDA_ERR_UNSUPPORTED, "head dims K=%d V=%d: each must be 64 or 128", K, V);
+  if ((int64_t)Hv * (V / 32) > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many heads");
+  if (!state || !aligned(state, 16)) return fail(KDA_ERR_INVALID_ARGUMENT, "state is NULL or misaligned");
+  if (P == 0) return ok();
+  if (!M || !S_tilde || !aligned(M, 16) || !aligned(S_tilde, 16))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "M and S_tilde must be non-NULL and 16-byte aligned");
+  kda::MergeArgs a{P, Hv, M, S_tilde, state};
+  kda_status_t st = hip_status(kda::launch_merge(K, V, a, static_cast<hipStream_t>(stream)), "merge kernel launch");
+  if (st != KDA_OK) return st;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+// Device-side helpers shared by the KDA kernels (gfx950 / CDNA4, wave64).
+//
+// Matrix-core tiles use v_mfma_f32_16x16x32_bf16.  Operand and result
+// fragments, for lane l of the wave:
+//   A (16 x 32, rows x reduction): row  l % 16, reduction slots 8*(l/16) .. +7
+//   B (32 x 16, reduction x cols): col  l % 16, reduction slots 8*(l/16) .. +7
+//   C (16 x 16):                   col  l % 16, rows 4*(l/16) .. +3
+// A and B always load the same reduction slots, so the order of the 32
+// reduction terms inside one instruction does not affect the result.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Native vector types (HIP's uint4/float4 wrapper structs defeat scalar
+// replacement of register arrays, which then land in scratch or LDS).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t bf16_t;   // bf16 storage (raw bits)
+
+constexpr int BT = 64;     // chunk length (tokens)
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;                     // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(bf16_t, b);
+}
+template <typename T> __device__ __forceinline__ float to_f(T x);
+template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t x) { return bf2f(x); }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return f2bf(x); }
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// Eight values -> bf16 fragment (hi) and the rounding remainder (lo), so that
+// hi + lo carries ~16 significant bits of each fp32 value.
+struct Frag { bf16x8 hi, lo; };
+
+__device__ __forceinline__ Frag split8(const float (&x)[8]) {
+  Frag f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __bf16 h = (__bf16)x[i];
+    f.hi[i] = h;
+    f.lo[i] = (__bf16)(x[i] - (float)h);
+  }
+  return f;
+}
+__device__ __forceinline__ bf16x8 round8(const float (&x)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
+  return r;
+}
+
+// Load 8 consecutive elements (16-byte aligned for bf16, 32-byte for fp32) as floats.
+__device__ __forceinline__ void load8(const bf16_t* p, float (&x)[8]) {
+  u32x4 u = *reinterpret_cast<const u32x4*>(p);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+}
+// Store 8 floats as 8 consecutive elements of type bf16 (16-byte aligned) or fp32.
+__device__ __forceinline__ void store8(bf16_t* p, const float (&x)[8]) {
+  u32x4 u = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+             pack_bf16x2(x[6], x[7])};
+  *reinterpret_cast<u32x4*>(p) = u;
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+  f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// acc += A * B where the operands are stored as T (bf16: exact single pass;
+// fp32: split into hi/lo and accumulated in three passes, dropping lo*lo).
+__device__ __forceinline__ f32x4 mma_stored(const bf16_t* a, const bf16_t* b, f32x4 acc) {
+  return mfma(load_bf16x8(a), load_bf16x8(b), acc);
+}
+__device__ __forceinline__ f32x4 mma_stored(const float* a, const float* b, f32x4 acc) {
+  float xa[8], xb[8];
+  load8(a, xa);
+  load8(b, xb);
+  Frag fa = split8(xa), fb = split8(xb);
+  acc = mfma(fa.hi, fb.hi, acc);
+  acc = mfma(fa.lo, fb.hi, acc);
+  acc = mfma(fa.hi, fb.lo, acc);
+  return acc;
+}
+
+// Stored-operand A against a B operand kept as bf16 hi/lo pair in LDS.
+__device__ __forceinline__ f32x4 mma_a_bsplit(const bf16_t* a, const bf16_t* bhi, const bf16_t* blo,
+                                              f32x4 acc) {
+  bf16x8 fa = load_bf16x8(a);
+  acc = mfma(fa, load_bf16x8(bhi), acc);
+  acc = mfma(fa, load_bf16x8(blo), acc);
+  return acc;
+}
+__device__ __forceinline__ f32x4 mma_a_bsplit(const float* a, const bf16_t* bhi, const bf16_t* blo,
+                                              f32x4 acc) {
+  float xa[8];
+  load8(a, xa);
+  Frag fa = split8(xa);
+  bf16x8 h = load_bf16x8(bhi), l = load_bf16x8(blo);
+  acc = mfma(fa.hi, h, acc);
+  acc = mfma(fa.hi, l, acc);
+  acc = mfma(fa.lo, h, acc);
+  return acc;
+}
+// Stored-operand A against the hi part only of a split B operand.
+__device__ __forceinline__ f32x4 mma_a_bhi(const bf16_t* a, const bf16_t* bhi, f32x4 acc) {
+  return mfma(load_bf16x8(a), load_bf16x8(bhi), acc);
+}
+__device__ __forceinline__ f32x4 mma_a_bhi(const float* a, const bf16_t* bhi, f32x4 acc) {
+  float xa[8];
+  load8(a, xa);
+  Frag fa = split8(xa);
+  bf16x8 h = load_bf16x8(bhi);
+  acc = mfma(fa.hi, h, acc);
+  acc = mfma(fa.lo, h, acc);
+  return acc;
+}
+
+// Sequence bookkeeping shared by the kernels.  BSND: sequence n = batch n,
+// tokens [n*T, n*T + T).  TND: tokens [cu[n], cu[n+1]); chunk_off[n] is the
+// first global chunk of sequence n (chunk_off[N] = total chunks).
+struct SeqInfo {
+  int tnd;                    // 0: BSND, 1: TND
+  int T;                      // BSND tokens per sequence
+  int N;                      // sequences
+  const int32_t* cu;          // TND device cu_seqlens [N+1]
+  const int32_t* chunk_off;   // TND device chunk offsets [N+1]
+};
+
+__device__ __forceinline__ void seq_range(const SeqInfo& s, int n, int64_t& tok0, int& len) {
+  if (s.tnd) {
+    int a = s.cu[n], b = s.cu[n + 1];
+    tok0 = a;
+    len = b - a;
+  } else {
+    tok0 = (int64_t)n * s.T;
+    len = s.T;
+  }
+}
+__device__ __forceinline__ int chunk_base(const SeqInfo& s, int n) {
+  return s.tnd ? s.chunk_off[n] : n * ((s.T + BT - 1) / BT);
+}
+// Sequence owning global chunk gc: the n with chunk_base(n) <= gc < chunk_base(n+1).
+__device__ __forceinline__ int seq_of_chunk(const SeqInfo& s, int gc) {
+  if (!s.tnd) return gc / ((s.T + BT - 1) / BT);
+  int lo = 0, hi = s.N - 1;            // largest n with chunk_off[n] <= gc
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (s.chunk_off[mid] <= gc) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace kda

@@ -1,0 +1,68 @@
+// Prefix merge of segment summaries ("KDA Context Parallelism (KCP)",
+// algorithm step 4; "Hyper-Parallel Chunk KDA" section 5.3, forward merge):
+// for j = 0..P-1 in order, state <- M_j state + S~_j, in fp32.
+// One workgroup per (value head, 32-column tile of the state); the state tile
+// stays in LDS across the P steps and each M_j is staged through LDS.
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+template <int KD, int VD>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int BVm = 32, PS = BVm + 4, PM = KD + 4;
+  constexpr int RPT = KD * BVm / 256;            // outputs per thread
+  __shared__ __attribute__((aligned(16))) float sS[KD * PS];
+  __shared__ __attribute__((aligned(16))) float sM[KD * PM];
+  const int tile = blockIdx.x % (VD / BVm), h = blockIdx.x / (VD / BVm);
+  const int v0 = tile * BVm, tid = threadIdx.x;
+  const int col = tid % BVm, rg = tid / BVm;     // rows rg, rg + 8, ...
+  float* st = a.state + (int64_t)h * KD * VD;
+  for (int i = tid; i < KD * BVm; i += 256) sS[(i / BVm) * PS + i % BVm] = st[(i / BVm) * VD + v0 + i % BVm];
+  for (int j = 0; j < a.P; ++j) {
+    const float* Mj = a.M + ((int64_t)j * a.Hv + h) * KD * KD;
+    const float* Sj = a.S + ((int64_t)j * a.Hv + h) * KD * VD;
+    for (int i = tid * 4; i < KD * KD; i += 256 * 4) {
+      f32x4 x = *reinterpret_cast<const f32x4*>(Mj + i);
+      *reinterpret_cast<f32x4*>(sM + (i / KD) * PM + i % KD) = x;
+    }
+    __syncthreads();
+    float acc[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) acc[r] = Sj[(int64_t)(rg + 8 * r) * VD + v0 + col];
+    for (int m = 0; m < KD; m += 4) {
+      float s0 = sS[(m + 0) * PS + col], s1 = sS[(m + 1) * PS + col];
+      float s2 = sS[(m + 2) * PS + col], s3 = sS[(m + 3) * PS + col];
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        f32x4 mv = *reinterpret_cast<const f32x4*>(sM + (rg + 8 * r) * PM + m);
+        acc[r] += mv.x * s0 + mv.y * s1 + mv.z * s2 + mv.w * s3;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) sS[(rg + 8 * r) * PS + col] = acc[r];
+    __syncthreads();
+  }
+  for (int i = tid; i < KD * BVm; i += 256) st[(i / BVm) * VD + v0 + i % BVm] = sS[(i / BVm) * PS + i % BVm];
+}
+
+}  // namespace
+
+hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s) {
+  if (a.P == 0 || a.Hv == 0) return hipSuccess;
+#define KDA_MERGE_CASE(KK, VV)                                                          \
+  if (K == KK && V == VV) {                                                             \
+    hipLaunchKernelGGL((merge_kernel<KK, VV>), dim3(a.Hv * (VV / 32)), dim3(256), 0, s, a); \
+    return hipGetLastError();                                                           \
+  }
+  KDA_MERGE_CASE(128, 128)
+  KDA_MERGE_CASE(64, 64)
+  KDA_MERGE_CASE(128, 64)
+  KDA_MERGE_CASE(64, 128)
+#undef KDA_MERGE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -1,0 +1,252 @@
+"""ctypes binding of the KDA C ABI (include/kda.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libkda_mi355x.so``.  PyTorch provides device memory and the
+current stream.  If the library is missing the calls raise; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda_mi355x.so")
+
+KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+KDA_LAYOUT_BSND, KDA_LAYOUT_TND = 0, 1
+KDA_GATE_IN_KERNEL, KDA_SAFE_GATE, KDA_QK_L2NORM, KDA_BETA_SIGMOID = 1, 2, 4, 8
+CHUNK = 64
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"KDA status {status}: {message}")
+        self.status = status
+
+
+class KdaProblem(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("B", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("Hk", ctypes.c_int32), ("Hv", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("scale", ctypes.c_float), ("eps", ctypes.c_float), ("lower_bound", ctypes.c_float),
+                ("num_seqs", ctypes.c_int32),
+                ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
+                ("state_rows", ctypes.c_int32)]
+
+
+_lib = None
+EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_segment_summary_workspace_size",
+           "kda_segment_summary", "kda_summary_merge", "kda_chunk_offsets_host",
+           "kda_set_stage_events", "kda_status_string", "kda_last_error", "kda_abi_version")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library (once); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m chunkwise_kimi_delta_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, VP, SZ, I32 = ctypes.POINTER(KdaProblem), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    lib.kda_chunk_fwd_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
+    lib.kda_segment_summary_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
+    lib.kda_chunk_fwd.argtypes = [P] + [VP] * 13 + [SZ, VP]
+    lib.kda_segment_summary.argtypes = [P] + [VP] * 10 + [SZ, VP]
+    lib.kda_summary_merge.argtypes = [I32, I32, I32, I32, VP, VP, VP, VP]
+    lib.kda_chunk_offsets_host.argtypes = [VP, I32, I32, VP]
+    lib.kda_set_stage_events.argtypes = [VP, VP, VP]
+    lib.kda_status_string.argtypes = [I32]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_abi_version.restype = I32
+    for name in ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_segment_summary_workspace_size",
+                 "kda_segment_summary", "kda_summary_merge", "kda_chunk_offsets_host",
+                 "kda_set_stage_events"):
+        getattr(lib, name).restype = I32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != KDA_OK:
+        lib = load()
+        raise KdaError(status, f"{lib.kda_status_string(status).decode()}: {lib.kda_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"token tensors must be bf16 or fp32, got {t.dtype}")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def make_problem(q_or_k: torch.Tensor, v: torch.Tensor, *, scale: float, flags: int, eps: float,
+                 lower_bound: float, cu_host: Optional[torch.Tensor], state_rows: int = 0):
+    """Fill the C problem descriptor from tensor shapes (BSND if 4-D, TND if 3-D)."""
+    if q_or_k.dim() == 4:
+        B, T, Hk, K = q_or_k.shape
+        layout, N, cu_ptr = KDA_LAYOUT_BSND, B, None
+    elif q_or_k.dim() == 3:
+        if cu_host is None:
+            raise ValueError("3-D (TND) token tensors need cu_seqlens")
+        T, Hk, K = q_or_k.shape
+        B, layout, N = 1, KDA_LAYOUT_TND, cu_host.numel() - 1
+        cu_ptr = ctypes.cast(cu_host.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+    else:
+        raise ValueError("token tensors are [B,T,H,D] or [T,H,D]")
+    Hv, V = v.shape[-2], v.shape[-1]
+    p = KdaProblem(layout, _dtype_code(v), B, T, Hk, Hv, K, V, CHUNK, flags, scale, eps, lower_bound,
+                   N, cu_ptr, state_rows)
+    return p, N
+
+
+def _cu_pair(cu_seqlens, cu_seqlens_host, device):
+    if cu_seqlens is None:
+        return None, None
+    cu_h = cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens.detach().to("cpu")
+    cu_h = cu_h.to(torch.int32).contiguous()
+    cu_d = cu_seqlens if cu_seqlens.is_cuda else cu_h.to(device)
+    cu_d = cu_d.to(torch.int32).contiguous()
+    return cu_d, cu_h
+
+
+def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None, dt_bias=None,
+                  initial_state=None, cu_seqlens=None, cu_seqlens_host=None, state_indices=None,
+                  output_final_state: bool = True, gate_in_kernel: bool = False,
+                  safe_gate: bool = False, lower_bound: float = -5.0, qk_l2norm: bool = False,
+                  beta_sigmoid: bool = False, eps: float = 1e-6, o=None, final_state=None,
+                  workspace=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA forward.  Returns (o, final_state).
+
+    With ``state_indices`` the ``initial_state`` is a state cache
+    [rows,Hv,K,V]; final states are scattered into ``final_state`` (default:
+    the same cache, in place) and that cache is returned.
+    """
+    lib = load()
+    dev = v.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta")):
+        _need(t, n, v.dtype)
+    _need(A_log, "A_log", torch.float32)
+    _need(dt_bias, "dt_bias", torch.float32)
+    _need(initial_state, "initial_state", torch.float32)
+    cu_d, cu_h = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    flags = ((KDA_GATE_IN_KERNEL if gate_in_kernel else 0) | (KDA_SAFE_GATE if safe_gate else 0)
+             | (KDA_QK_L2NORM if qk_l2norm else 0) | (KDA_BETA_SIGMOID if beta_sigmoid else 0))
+    cache = state_indices is not None
+    rows = initial_state.shape[0] if cache else 0
+    p, N = make_problem(q, v, scale=scale, flags=flags, eps=eps, lower_bound=lower_bound,
+                        cu_host=cu_h, state_rows=rows)
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    K, V, Hv = q.shape[-1], v.shape[-1], v.shape[-2]
+    if cache:
+        si = state_indices.to(device=dev, dtype=torch.int32).contiguous()
+        if final_state is None and output_final_state:
+            final_state = initial_state
+    else:
+        si = None
+        if final_state is None and output_final_state:
+            final_state = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev)
+    ws_bytes = ctypes.c_size_t()
+    _check(lib.kda_chunk_fwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
+    if workspace is None or workspace.numel() < ws_bytes.value:
+        workspace = torch.empty(max(ws_bytes.value, 256), dtype=torch.uint8, device=dev)
+    _check(lib.kda_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_d), _ptr(si),
+                             _ptr(o), _ptr(final_state), _ptr(workspace), workspace.numel(),
+                             _stream(dev)))
+    return o, final_state
+
+
+def kda_segment_summary(k, v, g, beta, *, A_log=None, dt_bias=None, cu_seqlens=None,
+                        cu_seqlens_host=None, gate_in_kernel: bool = False, safe_gate: bool = False,
+                        lower_bound: float = -5.0, qk_l2norm: bool = False,
+                        beta_sigmoid: bool = False, eps: float = 1e-6, M=None, S_tilde=None,
+                        workspace=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-sequence affine summary (M [N,Hv,K,K], S~ [N,Hv,K,V]), fp32."""
+    lib = load()
+    dev = v.device
+    for t, n in ((k, "k"), (v, "v"), (g, "g"), (beta, "beta")):
+        _need(t, n, v.dtype)
+    _need(A_log, "A_log", torch.float32)
+    _need(dt_bias, "dt_bias", torch.float32)
+    cu_d, cu_h = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    flags = ((KDA_GATE_IN_KERNEL if gate_in_kernel else 0) | (KDA_SAFE_GATE if safe_gate else 0)
+             | (KDA_QK_L2NORM if qk_l2norm else 0) | (KDA_BETA_SIGMOID if beta_sigmoid else 0))
+    p, N = make_problem(k, v, scale=1.0, flags=flags, eps=eps, lower_bound=lower_bound, cu_host=cu_h)
+    K, V, Hv = k.shape[-1], v.shape[-1], v.shape[-2]
+    if M is None:
+        M = torch.empty((N, Hv, K, K), dtype=torch.float32, device=dev)
+    if S_tilde is None:
+        S_tilde = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev)
+    ws_bytes = ctypes.c_size_t()
+    _check(lib.kda_segment_summary_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
+    if workspace is None or workspace.numel() < ws_bytes.value:
+        workspace = torch.empty(max(ws_bytes.value, 256), dtype=torch.uint8, device=dev)
+    _check(lib.kda_segment_summary(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(A_log), _ptr(dt_bias), _ptr(cu_d), _ptr(M), _ptr(S_tilde),
+                                   _ptr(workspace), workspace.numel(), _stream(dev)))
+    return M, S_tilde
+
+
+def kda_summary_merge(M: torch.Tensor, S_tilde: torch.Tensor, state: torch.Tensor) -> torch.Tensor:
+    """In place: state <- M[j] state + S_tilde[j] for j in order.  Returns ``state``."""
+    lib = load()
+    for t, n in ((M, "M"), (S_tilde, "S_tilde"), (state, "state")):
+        _need(t, n, torch.float32)
+    P, Hv, K, V = S_tilde.shape if S_tilde.dim() == 4 else (0,) + tuple(state.shape)
+    _check(lib.kda_summary_merge(P, Hv, K, V, _ptr(M), _ptr(S_tilde), _ptr(state),
+                                 _stream(state.device)))
+    return state
+
+
+def kda_chunk_offsets_host(cu_seqlens_host: torch.Tensor, chunk: int = CHUNK) -> torch.Tensor:
+    """First chunk index of each packed sequence, plus the total, computed by the library."""
+    lib = load()
+    cu = cu_seqlens_host.to(torch.int32).contiguous()
+    out = torch.empty(cu.numel(), dtype=torch.int32)
+    _check(lib.kda_chunk_offsets_host(cu.data_ptr(), cu.numel() - 1, chunk, out.data_ptr()))
+    return out
+
+
+def kda_set_stage_events(begin: Optional[int], after_chunk_local: Optional[int], end: Optional[int]):
+    """Register raw hipEvent_t handles recorded at the stage boundaries of later calls."""
+    _check(load().kda_set_stage_events(begin, after_chunk_local, end))
+
+
+def workspace_bytes(q_or_k: torch.Tensor, v: torch.Tensor, cu_seqlens_host=None, summary: bool = False) -> int:
+    """Device workspace bytes a forward (or summary) call needs for these shapes."""
+    lib = load()
+    cu = None if cu_seqlens_host is None else cu_seqlens_host.to(torch.int32).contiguous()
+    p, _ = make_problem(q_or_k, v, scale=1.0, flags=0, eps=0.0, lower_bound=0.0, cu_host=cu)
+    sz = ctypes.c_size_t()
+    fn = lib.kda_segment_summary_workspace_size if summary else lib.kda_chunk_fwd_workspace_size
+    _check(fn(ctypes.byref(p), ctypes.byref(sz)))
+    return sz.value

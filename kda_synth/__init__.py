@@ -160,10 +160,17 @@ def make_layer(seed=1001, B=1, T=8192, H=32, K=128, V=128, dtype="bf16", h0_std=
 
 
 def make_varlen(seed=1002, n_seqs=16, min_len=512, max_len=8192, H=32, K=128, V=128,
-                dtype="bf16", cache_rows=64, n_invalid=2) -> Problem:
-    """Packed TND prefill with a state cache gathered/scattered by index."""
+                dtype="bf16", cache_rows=64, n_invalid=2, lens=None) -> Problem:
+    """Packed TND prefill with a state cache gathered/scattered by index.
+
+    ``lens`` overrides the drawn sequence lengths (zero-length sequences allowed).
+    """
     rng = np.random.Generator(np.random.PCG64(seed))
-    lens = rng.integers(min_len, max_len + 1, size=n_seqs)
+    if lens is None:
+        lens = rng.integers(min_len, max_len + 1, size=n_seqs)
+    else:
+        lens = np.asarray(lens, dtype=np.int64)
+        n_seqs = len(lens)
     cu = np.zeros(n_seqs + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lens)
     T = int(cu[-1])
@@ -199,9 +206,10 @@ def make_segment(seed=1003, T=131072, H=32, K=128, V=128, dtype="bf16", n_prev=7
     # `factors_per_prev` delta-rule factors drawn here (raw keys, raw beta
     # logits and natural-log decays -softplus(N(0,1))*0.1); S~ ~ N(0, 0.02^2).
     n_f = n_prev * factors_per_prev
-    pk = _normal(rng, (n_f, H, K))
-    pb = _normal(rng, (n_f, H))
-    pg = (-np.logaddexp(0.0, _normal(rng, (n_f, H, K)).astype(np.float64)) * 0.1).astype(np.float32)
+    pk = _store(_normal(rng, (n_f, H, K)), dtype)
+    pb = _store(_normal(rng, (n_f, H)), dtype)
+    pg = _store((-np.logaddexp(0.0, _normal(rng, (n_f, H, K)).astype(np.float64)) * 0.1)
+                .astype(np.float32), dtype)
     pS = _normal(rng, (n_prev, H, K, V), 0.02)
     extras = dict(prev_k=pk, prev_beta=pb, prev_g=pg, prev_S=pS, n_prev=n_prev,
                   factors_per_prev=factors_per_prev)
@@ -216,7 +224,7 @@ def preceding_summary_inputs(p: Problem) -> Problem:
 
     Each preceding segment j is a sequence of ``factors_per_prev`` tokens
     whose zero-value summary transition is the ordered product of its
-    delta-rule factors.  Returned in TND layout, fp32, precomputed gate,
+    delta-rule factors.  Returned in TND layout with the segment's dtype, precomputed gate,
     raw keys with L2Norm on and raw beta logits with sigmoid on.
     """
     ex = p.extras
@@ -224,7 +232,7 @@ def preceding_summary_inputs(p: Problem) -> Problem:
     H, K, V = p.Hv, p.K, p.V
     cu = (np.arange(n + 1, dtype=np.int32) * f).astype(np.int32)
     z = np.zeros((n * f, H, V), dtype=np.float32)
-    return Problem(name="segment-prev", layout="tnd", dtype="f32", B=1, T=n * f, Hk=H, Hv=H,
+    return Problem(name="segment-prev", layout="tnd", dtype=p.dtype, B=1, T=n * f, Hk=H, Hv=H,
                    K=K, V=V, q=None, k=ex["prev_k"], v=z, g=ex["prev_g"], beta=ex["prev_beta"],
                    scale=p.scale, l2norm=True, beta_sigmoid=True, cu_seqlens=cu)
 

@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars: bf16 outputs err_max <= 2e-2; fp32 states, summaries and merged states
+<= 5e-3; fp32-input runs <= 5e-3 everywhere.  err_max = max|x - ref| / max|ref|.
+Small cases span several 64-token chunks with a ragged tail; full-size cases
+compare sampled heads (every token and state entry of those heads).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kda_synth as ks
+from kda_synth.torch_io import flag_kwargs, to_torch
+from oracle import kda_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16_OUT = 2e-2
+TOL_STATE = 5e-3
+TOL_F32 = 5e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(name, x, ref, tol):
+    c = orc.compare(x, ref)
+    say(f"  {name}: err_max={c['err_max']:.3e} rel_l2={c['rel_l2']:.3e} nonfinite={c['nonfinite']}")
+    assert c["nonfinite"] == 0, name
+    assert c["err_max"] <= tol, (name, c)
+    return c
+
+
+def run_fwd(kda, p, t=None, **over):
+    t = t or to_torch(p)
+    kw = flag_kwargs(p)
+    kw.update(over)
+    o, f = kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=p.scale,
+                             A_log=t["A_log"], dt_bias=t["dt_bias"],
+                             initial_state=None if p.h0 is None else t["h0"],
+                             cu_seqlens=t["cu"], cu_seqlens_host=t["cu_host"],
+                             state_indices=t["state_indices"], **kw)
+    torch.cuda.synchronize()
+    return o, f
+
+
+def fwd_case(kda, p, heads=None, o_tol=None, f_tol=TOL_STATE):
+    say(f"case {p.name}: layout={p.layout} dtype={p.dtype} B={p.B} T={p.T} Hk={p.Hk} Hv={p.Hv} "
+        f"K={p.K} V={p.V} heads={heads}")
+    o, f = run_fwd(kda, p)
+    ro, rf = orc.forward(p, heads=heads)
+    o_tol = o_tol or (TOL_F32 if p.dtype == "f32" else TOL_BF16_OUT)
+    go, gf = np64(o), np64(f)
+    if heads is not None:
+        go, ro = go[..., heads, :], ro[..., heads, :]
+        if p.state_indices is None:
+            gf, rf = gf[:, heads], rf[:, heads]
+        else:
+            gf, rf = gf[:, heads], rf[:, heads]
+    check("o", go, ro, o_tol)
+    check("final_state", gf, rf, f_tol if p.dtype != "f32" else TOL_F32)
+    return o, f
+
+
+# ------------------------------------------------------------------ small cases
+def test_tiny_fp32_prenormalised(gpu_lib):
+    fwd_case(gpu_lib, ks.make("tiny"))
+
+
+def test_tiny_fp32_in_kernel_l2norm_and_sigmoid(gpu_lib):
+    fwd_case(gpu_lib, ks.make("tiny", normalized_qk=False, preactivated_beta=False))
+
+
+def test_tiny_flag_paths_agree(gpu_lib):
+    """Raw q/k with in-kernel L2Norm equals pre-normalised q/k with it off."""
+    a = ks.make("tiny", normalized_qk=False)
+    b = ks.make("tiny", normalized_qk=True)
+    oa, fa = run_fwd(gpu_lib, a)
+    ob, fb = run_fwd(gpu_lib, b)
+    check("o(raw+l2) vs o(pre)", np64(oa), np64(ob), 1e-4)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+def test_layer_small_ragged(gpu_lib, T):
+    fwd_case(gpu_lib, ks.make("layer", T=T, H=4))
+
+
+def test_layer_batch2_no_h0(gpu_lib):
+    fwd_case(gpu_lib, ks.make("layer", B=2, T=130, H=3, h0_std=0.0))
+
+
+@pytest.mark.parametrize("K,V", [(64, 64), (64, 128), (128, 64)])
+def test_layer_head_dims_bf16(gpu_lib, K, V):
+    fwd_case(gpu_lib, ks.make("layer", T=150, H=2, K=K, V=V))
+
+
+def test_fp32_k64_v128(gpu_lib):
+    fwd_case(gpu_lib, ks.make("layer", T=150, H=2, K=64, V=128, dtype="f32"))
+
+
+def test_beta_zero_is_pure_decay(gpu_lib):
+    """beta = 0 (sigmoid off): the state only decays; o reads the decayed h0."""
+    p = ks.make("layer", T=100, H=2)
+    p.beta_sigmoid = False
+    p.beta = np.zeros_like(p.beta)
+    fwd_case(gpu_lib, p)
+
+
+def test_varlen_small_with_cache(gpu_lib):
+    p = ks.make("varlen", lens=[70, 0, 1, 130, 64, 5], H=3, cache_rows=9, n_invalid=2)
+    cache_before = p.h0.copy()
+    t = to_torch(p)
+    o, cache = run_fwd(gpu_lib, p, t)
+    ro, rcache = orc.forward(p)
+    check("o", np64(o), ro, TOL_BF16_OUT)
+    check("cache", np64(cache), rcache, TOL_STATE)
+    touched = set(int(i) for i in p.state_indices if i >= 0)
+    got = cache.cpu().numpy()
+    for r in range(p.h0.shape[0]):
+        if r not in touched:
+            assert np.array_equal(got[r], cache_before[r]), f"row {r} changed"
+
+
+def test_varlen_cache_out_of_range_index_reads_zero(gpu_lib):
+    p = ks.make("varlen", lens=[40, 90], H=2, cache_rows=4, n_invalid=0)
+    p.state_indices = np.array([7, 2], dtype=np.int32)     # 7 >= rows: invalid
+    t = to_torch(p)
+    o, cache = run_fwd(gpu_lib, p, t)
+    ro, rcache = orc.forward(p)
+    check("o", np64(o), ro, TOL_BF16_OUT)
+    check("cache", np64(cache), rcache, TOL_STATE)
+
+
+def test_gqa_small_safe_gate(gpu_lib):
+    fwd_case(gpu_lib, ks.make("gqa", B=2, T=150, Hk=2, Hv=8))
+
+
+def test_two_calls_carry_state(gpu_lib):
+    """Running T in two calls (final -> initial) equals one call."""
+    p = ks.make("layer", T=200, H=2)
+    a = ks.make("layer", T=200, H=2)
+    o_full, f_full = run_fwd(gpu_lib, p)
+    cut = 96
+    for name in ("q", "k", "v", "g", "beta"):
+        setattr(a, name, getattr(p, name)[:, :cut])
+    a.T = cut
+    o1, f1 = run_fwd(gpu_lib, a)
+    b = ks.make("layer", T=200, H=2)
+    for name in ("q", "k", "v", "g", "beta"):
+        setattr(b, name, getattr(p, name)[:, cut:])
+    b.T = 200 - cut
+    b.h0 = f1.cpu().numpy()
+    o2, f2 = run_fwd(gpu_lib, b)
+    check("o split", np64(torch.cat([o1, o2], dim=1)), np64(o_full), 1e-2)
+    check("final split", np64(f2), np64(f_full), 1e-3)
+
+
+def test_deterministic(gpu_lib):
+    p = ks.make("layer", T=300, H=4)
+    t = to_torch(p)
+    o1, f1 = run_fwd(gpu_lib, p, t)
+    o2, f2 = run_fwd(gpu_lib, p, t)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+# ---------------------------------------------------------- summary and merge
+def _summary_gpu(kda, p, t=None):
+    t = t or to_torch(p)
+    kw = flag_kwargs(p)
+    M, S = kda.kda_segment_summary(t["k"], t["v"], t["g"], t["beta"], A_log=t["A_log"],
+                                   dt_bias=t["dt_bias"], cu_seqlens=t["cu"],
+                                   cu_seqlens_host=t["cu_host"], **kw)
+    torch.cuda.synchronize()
+    return M, S
+
+
+def test_summary_small_matches_oracle(gpu_lib):
+    p = ks.make("layer", T=150, H=2, h0_std=0.0)
+    # a gentler gate keeps the transition product away from zero
+    p.gate_in_kernel = False
+    rng = np.random.default_rng(5)
+    p.g = ks.bf16_round((-0.05 * rng.random(p.g.shape)).astype(np.float32))
+    M, S = _summary_gpu(gpu_lib, p)
+    rM, rS = orc.segment_summary(p)
+    check("M", np64(M), rM, TOL_STATE)
+    check("S~", np64(S), rS, TOL_STATE)
+
+
+def test_summary_varlen_matches_oracle(gpu_lib):
+    p = ks.make("varlen", lens=[20, 0, 129], H=2, cache_rows=3, n_invalid=0)
+    p.state_indices, p.h0 = None, None
+    M, S = _summary_gpu(gpu_lib, p)
+    rM, rS = orc.segment_summary(p)
+    check("M", np64(M), rM, TOL_STATE)
+    check("S~", np64(S), rS, TOL_STATE)
+
+
+def test_merge_matches_oracle(gpu_lib):
+    rng = np.random.default_rng(7)
+    P, H, K, V = 5, 3, 128, 128
+    M = (rng.standard_normal((P, H, K, K)) / math.sqrt(K)).astype(np.float32)
+    S = (rng.standard_normal((P, H, K, V)) * 0.02).astype(np.float32)
+    X = (rng.standard_normal((H, K, V)) * 0.02).astype(np.float32)
+    st = torch.from_numpy(X.copy()).cuda()
+    gpu_lib.kda_summary_merge(torch.from_numpy(M).cuda(), torch.from_numpy(S).cuda(), st)
+    torch.cuda.synchronize()
+    check("merged", np64(st), orc.summary_merge(M, S, X), 1e-5)
+
+
+def _segment_case(kda, p, heads):
+    """Summaries of the preceding segments -> merge -> this segment's summary and fwd."""
+    say(f"case segment T={p.T} H={p.Hv} heads={heads}")
+    prev = ks.preceding_summary_inputs(p)
+    Mp, Sp_unused = _summary_gpu(kda, prev)
+    rMp, _ = orc.segment_summary(prev, heads=heads)
+    check("preceding M", np64(Mp)[:, heads], rMp[:, heads], TOL_STATE)
+    S_prev = p.extras["prev_S"]
+    state = torch.zeros((p.Hv, p.K, p.V), dtype=torch.float32, device="cuda")
+    kda.kda_summary_merge(Mp, torch.from_numpy(S_prev).cuda(), state)
+    torch.cuda.synchronize()
+    r_state = orc.summary_merge(rMp[:, heads], S_prev[:, heads])
+    check("rebuilt state", np64(state)[heads], r_state, TOL_STATE)
+    t = to_torch(p)
+    M, S = _summary_gpu(kda, p, t)
+    rM, rS = orc.segment_summary(p, heads=heads)
+    check("segment M", np64(M)[:, heads], rM[:, heads], TOL_STATE)
+    check("segment S~", np64(S)[:, heads], rS[:, heads], TOL_STATE)
+    p.h0 = state.cpu().numpy()[None]
+    t["h0"] = state[None].contiguous()
+    o, f = run_fwd(kda, p, t)
+    ro, rf = orc.forward(p, heads=heads)
+    check("o", np64(o)[..., heads, :], ro[..., heads, :], TOL_BF16_OUT)
+    check("final_state", np64(f)[:, heads], rf[:, heads], TOL_STATE)
+    # the segment's summary applied to the rebuilt state gives its final state
+    check("M X + S~", np64(torch.matmul(M[0], state) + S[0])[heads], np64(f)[0, heads], 1e-4)
+
+
+def test_segment_small(gpu_lib):
+    _segment_case(gpu_lib, ks.make("segment", T=300, H=2), heads=[0, 1])
+
+
+# --------------------------------------------------------- full-size, sampled
+def test_layer_full_sampled(gpu_lib):
+    fwd_case(gpu_lib, ks.make("layer"), heads=[0, 13, 31])
+
+
+def test_varlen_full_sampled(gpu_lib):
+    fwd_case(gpu_lib, ks.make("varlen"), heads=[0, 21])
+
+
+def test_gqa_full_sampled(gpu_lib):
+    fwd_case(gpu_lib, ks.make("gqa"), heads=[0, 5, 63])
+
+
+def test_segment_full_sampled(gpu_lib):
+    _segment_case(gpu_lib, ks.make("segment"), heads=[3])
