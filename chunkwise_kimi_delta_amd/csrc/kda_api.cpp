@@ -113,8 +113,8 @@ kda_status_t plan_problem(const kda_problem_t* p, bool forward, Plan& pl) {
   size_t off = 0;
   pl.off_chunk = off;  off = align256(off + sizeof(int32_t) * (size_t)(pl.N + 1));
   pl.off_w = off;      off = align256(off + slots * kBT * p->K * pl.es);
-  pl.off_u = off;      off = align256(off + slots * kBT * p->V * pl.es);
-  pl.off_kg = off;     off = align256(off + slots * kBT * p->K * pl.es);
+  pl.off_u = off;      off = align256(off + slots * kBT * p->V * sizeof(float));
+  pl.off_kg = off;     off = align256(off + slots * kBT * p->K * sizeof(float));
   if (forward) {
     pl.off_qg = off;   off = align256(off + slots * kBT * p->K * pl.es);
     pl.off_aqk = off;  off = align256(off + slots * kBT * kBT * pl.es);

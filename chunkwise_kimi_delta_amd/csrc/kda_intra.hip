@@ -12,6 +12,8 @@
 //   A         = (I + L)^-1
 //   u = A (beta * v),  w = A (beta * k * 2^gamma)
 //   kgT = (k * 2^(gamma_C - gamma))^T,  qg = scale * q * 2^gamma,  gdec = 2^gamma_C
+// u and kgT feed the state update directly and are kept in fp32; w, qg and
+// Aqk are stored in the token dtype.
 //
 // Range safety of the decay products.  Within one chunk gamma can fall by
 // hundreds, so 2^gamma_i * 2^-gamma_j overflows fp32.  Every pair i > j is
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(512) void intra_kernel(IntraArgs a) {
         store8(qg + i * KD + c0, outv);
       }
     }
-    ST* kgT = static_cast<ST*>(a.kgT) + ch * (KD * BT);
+    float* kgT = static_cast<float*>(a.kgT) + ch * (KD * BT);
     for (int idx = tid; idx < KD * 8; idx += NTH) {
       const int c = idx >> 3, t0 = (idx & 7) * 8;
       const float gC = sG[63 * PG + c];
@@ -389,7 +391,8 @@ __global__ __launch_bounds__(512) void intra_kernel(IntraArgs a) {
     }
     const int ND = isw ? KD : VD;
     const ST* Bsrc = isw ? sXT : sQV;
-    ST* dst = isw ? static_cast<ST*>(a.w) + ch * (BT * KD) : static_cast<ST*>(a.u) + ch * (BT * VD);
+    ST* dstw = static_cast<ST*>(a.w) + ch * (BT * KD);       // w in the token dtype
+    float* dstu = static_cast<float*>(a.u) + ch * (BT * VD);  // u in fp32
     for (int ct = 0; ct < ND / 16; ++ct) {
       f32x4 acc = zero4();
 #pragma unroll
@@ -411,7 +414,11 @@ __global__ __launch_bounds__(512) void intra_kernel(IntraArgs a) {
         }
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(16 * I + 4 * quad + e) * ND + 16 * ct + r16] = from_f<ST>(acc[e]);
+      for (int e = 0; e < 4; ++e) {
+        const int idx = (16 * I + 4 * quad + e) * ND + 16 * ct + r16;
+        if (isw) dstw[idx] = from_f<ST>(acc[e]);
+        else dstu[idx] = acc[e];
+      }
     }
   }
 }

@@ -9,7 +9,8 @@
 //   o     = qg h + tril(Aqk) v_new               (forward mode only)
 //   h     = Diag(gdec) h + kg^T v_new
 // The state stays in the matrix-core accumulators (fp32) for the whole
-// sequence; it is rounded to a bf16 hi/lo pair only as an operand, so each
+// sequence; it is rounded to a bf16 hi/lo pair only as an operand, and u,
+// kg^T and v_new enter the state update as fp32 (hi/lo pairs), so each
 // state-feeding product carries ~16 significant bits.  The next chunk's
 // inputs are prefetched into registers while the current chunk computes.
 //
@@ -33,8 +34,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   constexpr int ES = sizeof(ST);
   constexpr int EI = 16 / ES;
   constexpr int PK = KD + EI;          // rows of K elements (w, qg), ST
-  constexpr int PT = 64 + EI;          // rows of 64 elements (kg^T, Aqk), ST
-  constexpr int PU = BV + EI;          // u tile rows
+  constexpr int PT = 64 + EI;          // rows of 64 elements (Aqk), ST
+  constexpr int PKG = 64 + 4;          // kg^T rows (fp32)
+  constexpr int PU = BV + 4;           // u tile rows (fp32)
   constexpr int PH = KD + 8;           // h^T rows (bf16)
   constexpr int PV = 64 + 8;           // v_new^T rows (bf16)
   constexpr int VA = SUM ? VD + KD : VD;
@@ -43,10 +45,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   constexpr int CT = BV / 16;          // column tiles
 
   __shared__ __attribute__((aligned(16))) ST sW[64 * PK];
-  __shared__ __attribute__((aligned(16))) ST sKg[KD * PT];
+  __shared__ __attribute__((aligned(16))) float sKg[KD * PKG];
   __shared__ __attribute__((aligned(16))) ST sQg[SUM ? 8 : 64 * PK];
   __shared__ __attribute__((aligned(16))) ST sAq[SUM ? 8 : 64 * PT];
-  __shared__ __attribute__((aligned(16))) ST sU[64 * PU];
+  __shared__ __attribute__((aligned(16))) float sU[64 * PU];
   __shared__ __attribute__((aligned(16))) float sGd[KD];
   __shared__ __attribute__((aligned(16))) bf16_t sHhi[BV * PH];
   __shared__ __attribute__((aligned(16))) bf16_t sHlo[BV * PH];
@@ -72,9 +74,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int v0 = mtile ? tv * BV - VD : tv * BV;        // first column inside S~ or M
 
   // ---- register staging of one chunk's inputs (16-byte pieces)
-  constexpr int NWp = 64 * KD * ES / 16, NKp = KD * 64 * ES / 16;
+  constexpr int NWp = 64 * KD * ES / 16, NKp = KD * 64 * 4 / 16;
   constexpr int NQp = SUM ? 0 : 64 * KD * ES / 16, NAp = SUM ? 0 : 64 * 64 * ES / 16;
-  constexpr int NUp = 64 * BV * ES / 16, NGp = KD * 4 / 16;
+  constexpr int NUp = 64 * BV * 4 / 16, NGp = KD * 4 / 16;
   constexpr int CW = cdiv(NWp, NTH), CK = cdiv(NKp, NTH), CQ = imax(1, cdiv(NQp, NTH));
   constexpr int CA = imax(1, cdiv(NAp, NTH)), CU = cdiv(NUp, NTH), CG = cdiv(NGp, NTH);
   u32x4 rW[CW], rK[CK], rQ[CQ], rA[CA], rU[CU], rG[CG];
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   auto load_chunk = [&](int c) __attribute__((always_inline)) {
     const int64_t ch = (int64_t)h * a.nchunks + cb + c;
     const u32x4* gw = reinterpret_cast<const u32x4*>(static_cast<const ST*>(a.w) + ch * (64 * KD));
-    const u32x4* gk = reinterpret_cast<const u32x4*>(static_cast<const ST*>(a.kgT) + ch * (64 * KD));
+    const u32x4* gk = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.kgT) + ch * (64 * KD));
 #pragma unroll
     for (int i = 0; i < CW; ++i) { int p = tid + i * NTH; if (p < NWp) rW[i] = gw[p]; }
 #pragma unroll
@@ -95,14 +97,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 #pragma unroll
       for (int i = 0; i < CA; ++i) { int p = tid + i * NTH; if (p < NAp) rA[i] = ga[p]; }
     }
-    const ST* gu = static_cast<const ST*>(a.u) + ch * (64 * VD) + v0;
-    constexpr int UPR = BV * ES / 16;     // pieces per u row
+    const float* gu = static_cast<const float*>(a.u) + ch * (64 * VD) + v0;
+    constexpr int UPR = BV / 4;           // pieces per u row
 #pragma unroll
     for (int i = 0; i < CU; ++i) {
       int p = tid + i * NTH;
       if (p < NUp) {
         if (mtile) rU[i] = u32x4{0u, 0u, 0u, 0u};
-        else rU[i] = *reinterpret_cast<const u32x4*>(gu + (p / UPR) * VD + (p % UPR) * EI);
+        else rU[i] = *reinterpret_cast<const u32x4*>(gu + (p / UPR) * VD + (p % UPR) * 4);
       }
     }
     const u32x4* gg = reinterpret_cast<const u32x4*>(a.gdec + ch * KD);
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     for (int i = 0; i < CG; ++i) { int p = tid + i * NTH; if (p < NGp) rG[i] = gg[p]; }
   };
   auto stage_chunk = [&]() __attribute__((always_inline)) {
-    constexpr int WPR = KD * ES / 16, KPR = 64 * ES / 16, UPR = BV * ES / 16;
+    constexpr int WPR = KD * ES / 16, KPR = 64 * ES / 16, KGPR = 64 / 4, UPR = BV / 4;
 #pragma unroll
     for (int i = 0; i < CW; ++i) {
       int p = tid + i * NTH;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
       int p = tid + i * NTH;
-      if (p < NKp) *reinterpret_cast<u32x4*>(sKg + (p / KPR) * PT + (p % KPR) * EI) = rK[i];
+      if (p < NKp) *reinterpret_cast<u32x4*>(sKg + (p / KGPR) * PKG + (p % KGPR) * 4) = rK[i];
     }
     if (!SUM) {
 #pragma unroll
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int i = 0; i < CU; ++i) {
       int p = tid + i * NTH;
-      if (p < NUp) *reinterpret_cast<u32x4*>(sU + (p / UPR) * PU + (p % UPR) * EI) = rU[i];
+      if (p < NUp) *reinterpret_cast<u32x4*>(sU + (p / UPR) * PU + (p % UPR) * 4) = rU[i];
     }
 #pragma unroll
     for (int i = 0; i < CG; ++i) {
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       const int t0 = 16 * wave + 4 * quad, col = 16 * ct + r16;
       float vn[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vn[e] = to_f<ST>(sU[(t0 + e) * PU + col]) - acc[e];
+      for (int e = 0; e < 4; ++e) vn[e] = sU[(t0 + e) * PU + col] - acc[e];
       float lv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) lv[e] = vn[e] - bf2f(f2bf(vn[e]));
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int k0 = ks * 32 + 8 * quad;
-          acc = mma_a_bsplit(sKg + (16 * R + r16) * PT + k0, sVhi + (16 * ct + r16) * PV + k0,
+          acc = mma_a_bsplit(sKg + (16 * R + r16) * PKG + k0, sVhi + (16 * ct + r16) * PV + k0,
                              sVlo + (16 * ct + r16) * PV + k0, acc);
         }
         hs[rt][ct] = acc;

@@ -50,8 +50,8 @@ def _ws(lib, p, summary=False):
 def test_workspace_size_layer_and_monotone(lib):
     st, b = _ws(lib, _problem())
     assert st == 0
-    # w, u, kgT, qg, Aqk (bf16) + decay (fp32) per (head, chunk), 256-byte aligned regions.
-    per = 64 * 128 * 2 * 4 + 64 * 64 * 2 + 128 * 4
+    # w, qg, Aqk (bf16), u, kgT and the chunk decay (fp32) per (head, chunk), 256-byte aligned regions.
+    per = 64 * 128 * (2 + 4 + 4 + 2) + 64 * 64 * 2 + 128 * 4
     assert b >= 32 * 128 * per and b < 32 * 128 * per + 8 * 256
     prev = 0
     for T in (0, 1, 64, 65, 1000, 8192):
