@@ -1,59 +1,110 @@
-// Chunk-local KDA work, one workgroup (8 waves) per (64-token chunk, value head).
+// Chunk-local KDA work, one workgroup (4 waves) per (64-token chunk, value head).
 //
 // Follows "KDA Chunk Backward — TPU/Pallas Kernel Design", section 1.2 (WY
 // representation, log2-space chunk-local gate) and section 3.7 (sub-block
 // normalisation with a reference gate), and the prepare stage of
 // "Hyper-Parallel Chunk KDA" section 5.1 (gate, L2Norm, beta, Akk/Aqk, w, u,
 // qg, kg).  Per chunk with tokens i = 0..63 (rows >= C of a partial chunk are
-// zero-padded and inert):
+// zero and inert):
 //   gamma_i   = log2(e) * sum_{r<=i} g_r         (inclusive, per channel)
 //   L_ij      = beta_i * sum_c k_ic k_jc 2^(gamma_ic - gamma_jc)   (i > j)
 //   Aqk_ij    = scale  * sum_c q_ic k_jc 2^(gamma_ic - gamma_jc)   (i >= j)
 //   A         = (I + L)^-1
 //   u = A (beta * v),  w = A (beta * k * 2^gamma)
-//   kgT = (k * 2^(gamma_C - gamma))^T,  qg = scale * q * 2^gamma,  gdec = 2^gamma_C
-// u and kgT feed the state update directly and are kept in fp32; w, qg and
-// Aqk are stored in the token dtype.
+//   kg = k * 2^(gamma_C - gamma),  qg = scale * q * 2^gamma,  gdec = 2^gamma_C
+// Workspace per (head, chunk): w, qg [64][K] and Aqk [64][64] in the token
+// dtype; kg^T [K][64], u^T [V][64] and gdec [K] in fp32 (they feed the state
+// update directly).
+//
+// Each wave owns 16 token rows and keeps them in registers in the matrix-core
+// operand layout (lane: row 16*wave + lane%16, channels 32*ks + 8*(lane/16) + e),
+// so a row is both the A operand of its own row tile and the B operand of its
+// own column tile.
 //
 // Range safety of the decay products.  Within one chunk gamma can fall by
 // hundreds, so 2^gamma_i * 2^-gamma_j overflows fp32.  Every pair i > j is
-// instead evaluated at the level of a binary split of the chunk where i lies
-// in the upper half and j in the lower half of one block, with the reference
+// evaluated at the level of a binary split of the chunk where i lies in the
+// upper half and j in the lower half of one block, with the reference
 // r = first row of the upper half:
 //   2^(gamma_i - gamma_j) = 2^(gamma_i - gamma_r) * 2^(gamma_r - gamma_j),
-// both factors <= 1.  Level 64 and 32 blocks are full 16x16 matrix-core tiles;
-// levels 16, 8, 4, 2 live inside the diagonal tiles and are masked per entry.
-// The diagonal of Aqk (factor 1) is a plain dot product.
+// both factors <= 1.  Levels 64 and 32 are full 16x16 tiles; levels 16, 8, 4
+// and 2 live inside the diagonal tiles and are masked per entry.  The diagonal
+// of Aqk (factor 1) is a plain dot product.
 #include "kda_launch.h"
 
 namespace kda {
 
 namespace {
 
-template <int KD, int VD, typename IT>
-__global__ __launch_bounds__(512) void intra_kernel(IntraArgs a) {
-  using ST = IT;                                   // workspace element type
-  constexpr int NTH = 512;
-  constexpr bool F32 = sizeof(IT) == 4;
-  constexpr int EI = 16 / sizeof(IT);              // elements per 16 bytes
-  constexpr int PQ = KD + EI;                      // row stride of sQ / sK
-  constexpr int PG = KD + 4;                       // row stride of sG (floats)
-  constexpr int P64 = 64 + 4;                      // row stride of sL / sA
-  constexpr int PT = 64 + EI;                      // row stride of transposed operands
-  constexpr int UQ = 64 * PQ > VD * PT ? 64 * PQ : VD * PT;
+constexpr float LN2 = 0.6931471805599453f;
 
-  __shared__ __attribute__((aligned(16))) IT sQV[UQ];        // q, later v^T
-  __shared__ __attribute__((aligned(16))) IT sK[64 * PQ];
-  __shared__ __attribute__((aligned(16))) float sG[64 * PG];  // gamma (log2)
+template <int N>
+__device__ __forceinline__ float dpp_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
+}
+// Inclusive prefix sum across the 16 lanes of each DPP row.
+__device__ __forceinline__ float row_scan16(float x) {
+  x += dpp_shr<1>(x);
+  x += dpp_shr<2>(x);
+  x += dpp_shr<4>(x);
+  x += dpp_shr<8>(x);
+  return x;
+}
+
+// 2^x and log2(x) on the transcendental unit (v_exp_f32 / v_log_f32).  Every
+// exponent used here is <= 0; results below the normal range flush towards
+// zero, where the products they scale are negligible.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ void zero8(float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = 0.f;
+}
+
+// acc += A * B with both operands split into bf16 hi/lo (three passes).
+__device__ __forceinline__ f32x4 mma3(const Frag& A, const Frag& B, f32x4 acc) {
+  acc = mfma(A.hi, B.hi, acc);
+  acc = mfma(A.lo, B.hi, acc);
+  acc = mfma(A.hi, B.lo, acc);
+  return acc;
+}
+
+template <typename ST>
+__device__ __forceinline__ void store_val(ST* p, float v) { *p = from_f<ST>(v); }
+
+template <int KD, int VD, typename IT>
+__global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
+  using ST = IT;                                   // workspace type of w, qg, Aqk
+  constexpr bool F32 = sizeof(IT) == 4;
+  constexpr int NKS = KD / 32, NVS = VD / 32;
+  constexpr int P64 = 64 + 4;                      // row stride of sL / sA (floats)
+  constexpr int PB = KD + 8;                       // row stride of bf16 column operands
+  constexpr int PT = 64 + 16 / (int)sizeof(ST);    // row stride of v^T / X^T
+  constexpr int BOP_BYTES = (32 + 16 + 16) * PB * 2 * 2;
+  constexpr int VX_BYTES = (VD + KD) * PT * (int)sizeof(ST);
+  constexpr int UB = BOP_BYTES > VX_BYTES ? BOP_BYTES : VX_BYTES;
+
+  __shared__ __attribute__((aligned(16))) float sTot[4][KD];   // per-wave gate totals
+  __shared__ __attribute__((aligned(16))) float sRef[3][KD];   // gamma of rows 16, 32, 48
   __shared__ __attribute__((aligned(16))) float sL[64 * P64];
   __shared__ __attribute__((aligned(16))) float sA[64 * P64];
-  __shared__ __attribute__((aligned(16))) ST sXT[KD * PT];    // (beta-free) k*2^gamma, transposed
-  __shared__ float sTot[NTH];
   __shared__ float sX[3 * 256];
-  __shared__ float sBeta[64], sRq[64], sRk[64], sDg[64];
+  __shared__ float sBeta[64];
+  // column operands of the off-diagonal levels, later reused for v^T and X^T
+  __shared__ __attribute__((aligned(16))) unsigned char sU8[UB];
+  bf16_t* b64hi = reinterpret_cast<bf16_t*>(sU8);  // rows 0..31, reference row 32
+  bf16_t* b64lo = b64hi + 32 * PB;
+  bf16_t* b32ahi = b64lo + 32 * PB;                // rows 0..15, reference row 16
+  bf16_t* b32alo = b32ahi + 16 * PB;
+  bf16_t* b32bhi = b32alo + 16 * PB;               // rows 32..47, reference row 48
+  bf16_t* b32blo = b32bhi + 16 * PB;
+  ST* sVT = reinterpret_cast<ST*>(sU8);            // [VD][PT]
+  ST* sXT = sVT + VD * PT;                         // [KD][PT]
 
   const int gc = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, quad = lane >> 4;
   const int n = seq_of_chunk(a.seq, gc);
   int64_t tok0s;
   int len;
@@ -64,279 +115,282 @@ __global__ __launch_bounds__(512) void intra_kernel(IntraArgs a) {
   const int hk = h / (a.Hv / a.Hk);
   const int64_t ch = (int64_t)h * a.nchunks + gc;      // head-major chunk slot
   const bool has_q = a.q != nullptr;
+  const int i = 16 * wave + r16;                       // this lane's token row
+  const bool live = i < C;
 
-  for (int i = tid; i < 64 * P64; i += NTH) sA[i] = 0.f;
-
-  // ---- gate activation + chunk-local inclusive cumsum (log2 units)
+  // ---- loads: gate, k, q, v rows of this lane; beta
+  float gl[NKS][8], kx[NKS][8], qx[NKS][8], vx[NVS][8];
   {
-    constexpr int G = NTH / KD, RPG = BT / G;
-    const int c = tid % KD, grp = tid / KD;
-    const IT* gp = static_cast<const IT*>(a.g);
-    const bool gik = a.flags & F_GATE, safe = a.flags & F_SAFE;
-    float Aexp = 0.f, bias = 0.f;
-    if (gik) {
-      Aexp = expf(a.A_log[h]);
-      bias = a.dt_bias ? a.dt_bias[h * KD + c] : 0.f;
+    const int64_t tok = tok0 + i;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int c0 = 32 * ks + 8 * quad;
+      if (live) {
+        load8(static_cast<const IT*>(a.g) + tok * (int64_t)(a.Hv * KD) + h * KD + c0, gl[ks]);
+        load8(static_cast<const IT*>(a.k) + tok * (int64_t)(a.Hk * KD) + hk * KD + c0, kx[ks]);
+        if (has_q) load8(static_cast<const IT*>(a.q) + tok * (int64_t)(a.Hk * KD) + hk * KD + c0, qx[ks]);
+        else zero8(qx[ks]);
+      } else {
+        zero8(gl[ks]);
+        zero8(kx[ks]);
+        zero8(qx[ks]);
+      }
     }
-    const int64_t gstride = (int64_t)a.Hv * KD;
-    float run = 0.f;
-#pragma unroll 4
-    for (int r = 0; r < RPG; ++r) {
-      const int i = grp * RPG + r;
-      float gl = 0.f;
-      if (i < C) {
-        float x = to_f<IT>(gp[(tok0 + i) * gstride + h * KD + c]);
-        float gn;
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs) {
+      if (live) load8(static_cast<const IT*>(a.v) + tok * (int64_t)(a.Hv * VD) + h * VD + 32 * vs + 8 * quad, vx[vs]);
+      else zero8(vx[vs]);
+    }
+  }
+  float beta = 0.f;
+  if (live) {
+    beta = to_f<IT>(static_cast<const IT*>(a.beta)[(tok0 + i) * a.Hv + h]);
+    if (a.flags & F_SIGMOID) beta = 1.f / (1.f + expf(-beta));
+  }
+
+  // ---- gate activation (log2 units), in-wave row prefix sums, norms
+  {
+    const bool gik = a.flags & F_GATE, safe = a.flags & F_SAFE;
+    const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float bias[8];
+      if (gik && a.dt_bias) load8(a.dt_bias + h * KD + 32 * ks + 8 * quad, bias);
+      else zero8(bias);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float gn = gl[ks][e];
         if (gik) {
-          float z = x + bias;
-          float sp = fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
-          gn = -Aexp * sp;
-        } else {
-          gn = x;
+          const float z = gn + bias[e];
+          // softplus(z) = max(z, 0) + ln(1 + e^-|z|)
+          gn = -Aexp * (fmaxf(z, 0.f) + LN2 * flog2(1.f + fexp2(-LOG2E * fabsf(z))));
         }
         if (safe) gn = fmaxf(gn, a.lower_bound);
-        gl = gn * LOG2E;
+        gl[ks][e] = row_scan16(live ? gn * LOG2E : 0.f);
       }
-      run += gl;
-      sG[i * PG + c] = run;
     }
-    sTot[grp * KD + c] = run;
   }
-
-  // ---- q, k rows (raw) + squared norms + q.k dot; beta
+  float rq, rk, dqk;
   {
-    constexpr int CPR = KD / EI, TOT = 64 * CPR;
-    const IT* qp = static_cast<const IT*>(a.q);
-    const IT* kp = static_cast<const IT*>(a.k);
-    const int64_t qstride = (int64_t)a.Hk * KD;
+    float sqq = 0.f, skk = 0.f, sqk = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sqq += qx[ks][e] * qx[ks][e];
+        skk += kx[ks][e] * kx[ks][e];
+        sqk += qx[ks][e] * kx[ks][e];
+      }
+    sqq += __shfl_xor(sqq, 16); sqq += __shfl_xor(sqq, 32);
+    skk += __shfl_xor(skk, 16); skk += __shfl_xor(skk, 32);
+    sqk += __shfl_xor(sqk, 16); sqk += __shfl_xor(sqk, 32);
     const bool l2 = a.flags & F_L2;
-    for (int id = tid; id < TOT; id += NTH) {
-      const int row = id / CPR, part = id % CPR;
-      u32x4 uq = u32x4{0u, 0u, 0u, 0u}, uk = u32x4{0u, 0u, 0u, 0u};
-      if (row < C) {
-        const int64_t off = (tok0 + row) * qstride + hk * KD + part * EI;
-        if (has_q) uq = *reinterpret_cast<const u32x4*>(qp + off);
-        uk = *reinterpret_cast<const u32x4*>(kp + off);
-      }
-      *reinterpret_cast<u32x4*>(sQV + row * PQ + part * EI) = uq;
-      *reinterpret_cast<u32x4*>(sK + row * PQ + part * EI) = uk;
-      const IT* eq = reinterpret_cast<const IT*>(&uq);
-      const IT* ek = reinterpret_cast<const IT*>(&uk);
-      float sqq = 0.f, skk = 0.f, sqk = 0.f;
+    rq = l2 ? 1.f / sqrtf(sqq + a.eps) : 1.f;
+    rk = l2 ? 1.f / sqrtf(skk + a.eps) : 1.f;
+    dqk = sqk;
+  }
+  if (r16 == 15) {
 #pragma unroll
-      for (int e = 0; e < EI; ++e) {
-        float xq = to_f<IT>(eq[e]), xk = to_f<IT>(ek[e]);
-        sqq += xq * xq;
-        skk += xk * xk;
-        sqk += xq * xk;
-      }
+    for (int ks = 0; ks < NKS; ++ks) store8(&sTot[wave][32 * ks + 8 * quad], gl[ks]);
+  }
+  if (quad == 0) sBeta[i] = beta;
+  __syncthreads();
+
+  // ---- finish the chunk cumsum; publish reference rows and the chunk decay
+  float gC[NKS][8];
 #pragma unroll
-      for (int o = CPR / 2; o >= 1; o >>= 1) {
-        sqq += __shfl_xor(sqq, o);
-        skk += __shfl_xor(skk, o);
-        sqk += __shfl_xor(sqk, o);
-      }
-      if (part == 0) {
-        sRq[row] = l2 ? 1.f / sqrtf(sqq + a.eps) : 1.f;
-        sRk[row] = l2 ? 1.f / sqrtf(skk + a.eps) : 1.f;
-        sDg[row] = sqk;
-      }
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int c0 = 32 * ks + 8 * quad;
+    float t0[8], t1[8], t2[8], t3[8];
+    load8(&sTot[0][c0], t0);
+    load8(&sTot[1][c0], t1);
+    load8(&sTot[2][c0], t2);
+    load8(&sTot[3][c0], t3);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float off = (wave > 0 ? t0[e] : 0.f) + (wave > 1 ? t1[e] : 0.f) + (wave > 2 ? t2[e] : 0.f);
+      gl[ks][e] += off;
+      gC[ks][e] = t0[e] + t1[e] + t2[e] + t3[e];
     }
-    if (tid < 64) {
-      float b = 0.f;
-      if (tid < C) {
-        b = to_f<IT>(static_cast<const IT*>(a.beta)[(tok0 + tid) * a.Hv + h]);
-        if (a.flags & F_SIGMOID) b = 1.f / (1.f + expf(-b));
-      }
-      sBeta[tid] = b;
+    if (r16 == 0 && wave >= 1) store8(&sRef[wave - 1][c0], gl[ks]);
+    if (wave == 0 && r16 == 0) {
+      float d[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[e] = fexp2(gC[ks][e]);
+      store8(a.gdec + ch * KD + c0, d);
     }
   }
+  // normalised rows
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kx[ks][e] *= rk;
+      qx[ks][e] *= rq;
+    }
   __syncthreads();
-  {  // add the totals of the preceding row groups to finish the cumsum
-    constexpr int G = NTH / KD, RPG = BT / G;
-    const int c = tid % KD, grp = tid / KD;
-    float off = 0.f;
-    for (int g2 = 0; g2 < grp; ++g2) off += sTot[g2 * KD + c];
-    if (grp > 0)
-      for (int r = 0; r < RPG; ++r) sG[(grp * RPG + r) * PG + c] += off;
+
+  // ---- column operands of levels 64 / 32 (LDS), qg and kg^T (global)
+  {
+    auto put_col = [&](const float* gref, bf16_t* hi, bf16_t* lo, int row) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int c0 = 32 * ks + 8 * quad;
+        float gr[8], x[8];
+        load8(gref + c0, gr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = kx[ks][e] * fexp2(gr[e] - gl[ks][e]);
+        Frag f = split8(x);
+        *reinterpret_cast<bf16x8*>(hi + row * PB + c0) = f.hi;
+        *reinterpret_cast<bf16x8*>(lo + row * PB + c0) = f.lo;
+      }
+    };
+    if (wave <= 1) put_col(sRef[1], b64hi, b64lo, i);
+    if (wave == 0) put_col(sRef[0], b32ahi, b32alo, i);
+    if (wave == 2) put_col(sRef[2], b32bhi, b32blo, i - 32);
+    if (has_q) {
+      ST* qg = static_cast<ST*>(a.qg) + ch * (BT * KD) + i * KD;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = a.scale * qx[ks][e] * fexp2(gl[ks][e]);
+        store8(qg + 32 * ks + 8 * quad, x);
+      }
+    }
+    float* kgT = static_cast<float*>(a.kgT) + ch * (KD * BT);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        kgT[(32 * ks + 8 * quad + e) * BT + i] = kx[ks][e] * fexp2(gC[ks][e] - gl[ks][e]);
   }
   __syncthreads();
 
   // ---- Akk (L) and Aqk tiles on the matrix cores
   ST* Aqk_out = static_cast<ST*>(a.Aqk) + ch * (BT * BT);
   {
-    const int r16 = lane & 15, quad = lane >> 4;
-    // acc_kk/acc_qk += (row operand at level L) x (col operand at level L)^T
-    auto tile_level = [&](int I, int J, int L, f32x4& akk, f32x4& aqk) {
-      const int i = 16 * I + r16, j = 16 * J + r16;
-      const bool irow = (i % L) >= (L >> 1), jcol = (j % L) < (L >> 1);
-      const int ri = (i / L) * L + (L >> 1), rj = (j / L) * L + (L >> 1);
-      const float rki = sRk[i], rqi = sRq[i], rkj = sRk[j];
+    // diagonal tile of this wave: levels L = 2 << b for b = 0..3 (blocks of 2, 4, 8, 16 rows)
+    f32x4 dk[4], dq[4];
 #pragma unroll
-      for (int ks = 0; ks < KD / 32; ++ks) {
-        const int c0 = ks * 32 + 8 * quad;
-        float ka[8], qa[8], kb[8];
-        if (irow) {
-          float x[8], gi[8], gr[8];
-          load8(&sK[i * PQ + c0], x);
-          load8(&sG[i * PG + c0], gi);
-          load8(&sG[ri * PG + c0], gr);
-          float xq[8];
-          if (has_q) load8(&sQV[i * PQ + c0], xq);
+    for (int b = 0; b < 4; ++b) {
+      dk[b] = zero4();
+      dq[b] = zero4();
+      const int L = 2 << b;
+      const bool isrow = (r16 & (L - 1)) >= (L >> 1);
+      const int src = 16 * quad + (r16 & ~(L - 1)) + (L >> 1);   // lane holding the reference row
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float f = exp2f(gi[e] - gr[e]);
-            ka[e] = x[e] * rki * f;
-            qa[e] = has_q ? xq[e] * rqi * f : 0.f;
-          }
-        } else {
+      for (int ks = 0; ks < NKS; ++ks) {
+        float ra[8], rb[8], rq8[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) { ka[e] = 0.f; qa[e] = 0.f; }
+        for (int e = 0; e < 8; ++e) {
+          const float gr = __shfl(gl[ks][e], src);
+          const float f = fexp2(isrow ? gl[ks][e] - gr : gr - gl[ks][e]);
+          const float kv = kx[ks][e] * f;
+          ra[e] = isrow ? kv : 0.f;
+          rb[e] = isrow ? 0.f : kv;
+          rq8[e] = isrow ? qx[ks][e] * f : 0.f;
         }
-        if (jcol) {
-          float x[8], gj[8], gr[8];
-          load8(&sK[j * PQ + c0], x);
-          load8(&sG[j * PG + c0], gj);
-          load8(&sG[rj * PG + c0], gr);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kb[e] = x[e] * rkj * exp2f(gr[e] - gj[e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kb[e] = 0.f;
-        }
-        Frag fa = split8(ka), fb = split8(kb);
-        akk = mfma(fa.hi, fb.hi, akk);
-        akk = mfma(fa.lo, fb.hi, akk);
-        akk = mfma(fa.hi, fb.lo, akk);
+        Frag A = split8(ra), B = split8(rb);
+        dk[b] = mma3(A, B, dk[b]);
         if (has_q) {
-          if (F32) {
-            Frag fq = split8(qa);
-            aqk = mfma(fq.hi, fb.hi, aqk);
-            aqk = mfma(fq.lo, fb.hi, aqk);
-            aqk = mfma(fq.hi, fb.lo, aqk);
-          } else {
-            aqk = mfma(round8(qa), fb.hi, aqk);
-          }
+          if (F32) dq[b] = mma3(split8(rq8), B, dq[b]);
+          else dq[b] = mfma(round8(rq8), B.hi, dq[b]);
         }
       }
-    };
-    // full tile at one level: every entry valid
-    auto full_tile = [&](int I, int J, int L) {
+    }
+    // diagonal tile output; the lane with r16 == row owns that row's norms and dot
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int il = 4 * quad + e, jl = r16;
+      const int row = 16 * wave + il, col = 16 * wave + jl;
+      float vk = 0.f, vq = 0.f;
+      if (il > jl) {
+        const int b = 31 - __clz(il ^ jl);
+        vk = b == 0 ? dk[0][e] : b == 1 ? dk[1][e] : b == 2 ? dk[2][e] : dk[3][e];
+        vq = b == 0 ? dq[0][e] : b == 1 ? dq[1][e] : b == 2 ? dq[2][e] : dq[3][e];
+        vk *= sBeta[row];
+        vq *= a.scale;
+      } else if (il == jl) {
+        vq = a.scale * rq * rk * dqk;
+      }
+      sL[row * P64 + col] = vk;
+      if (has_q) store_val(Aqk_out + row * BT + col, vq);
+    }
+    // off-diagonal tiles: row operand from this wave's rows, column operand from LDS
+    auto off_tile = [&](const float* gref, int J, const bf16_t* bhi, const bf16_t* blo, int brow0)
+        __attribute__((always_inline)) {
       f32x4 akk = zero4(), aqk = zero4();
-      tile_level(I, J, L, akk, aqk);
-      const int j = 16 * J + r16;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int c0 = 32 * ks + 8 * quad;
+        float gr[8], ra[8], rq8[8];
+        load8(gref + c0, gr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = fexp2(gl[ks][e] - gr[e]);
+          ra[e] = kx[ks][e] * f;
+          rq8[e] = qx[ks][e] * f;
+        }
+        Frag A = split8(ra), B;
+        B.hi = load_bf16x8(bhi + (brow0 + r16) * PB + c0);
+        B.lo = load_bf16x8(blo + (brow0 + r16) * PB + c0);
+        akk = mma3(A, B, akk);
+        if (has_q) {
+          if (F32) aqk = mma3(split8(rq8), B, aqk);
+          else aqk = mfma(round8(rq8), B.hi, aqk);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * I + 4 * quad + e;
-        sL[i * P64 + j] = sBeta[i] * akk[e];
-        if (has_q) Aqk_out[i * BT + j] = from_f<ST>(a.scale * aqk[e]);
+        const int row = 16 * wave + 4 * quad + e, col = 16 * J + r16;
+        sL[row * P64 + col] = sBeta[row] * akk[e];
+        if (has_q) store_val(Aqk_out + row * BT + col, a.scale * aqk[e]);
       }
     };
-    if (wave < 4) {
-      // diagonal tile I = wave: levels 16, 8, 4, 2 (index b: L = 2 << b)
-      const int I = wave;
-      f32x4 kk[4], qk[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        kk[b] = zero4();
-        qk[b] = zero4();
-        tile_level(I, I, 2 << b, kk[b], qk[b]);
-      }
-      const int j = 16 * I + r16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * I + 4 * quad + e;
-        float vk = 0.f, vq = 0.f;
-        if (i > j) {
-          const int b = 31 - __clz(i ^ j);
-          vk = b == 0 ? kk[0][e] : b == 1 ? kk[1][e] : b == 2 ? kk[2][e] : kk[3][e];
-          vq = b == 0 ? qk[0][e] : b == 1 ? qk[1][e] : b == 2 ? qk[2][e] : qk[3][e];
-          vk *= sBeta[i];
-          vq *= a.scale;
-        } else if (i == j) {
-          vq = a.scale * sRq[i] * sRk[i] * sDg[i];
-        }
-        sL[i * P64 + j] = vk;
-        if (has_q) Aqk_out[i * BT + j] = from_f<ST>(vq);
-      }
-    } else {
-      const int w4 = wave - 4;
-      full_tile(2 + (w4 >> 1), w4 & 1, 64);
-      if (w4 == 0) full_tile(1, 0, 32);
-      if (w4 == 1) full_tile(3, 2, 32);
-      if (w4 >= 2 && has_q) {  // upper-triangle tiles of Aqk are zero
-        for (int idx = (w4 - 2) * 64 + lane; idx < 6 * 256; idx += 128) {
-          const int t = idx >> 8, e = idx & 255;
-          const int I = t < 3 ? 0 : (t < 5 ? 1 : 2);
-          const int J = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
-          Aqk_out[(16 * I + (e >> 4)) * BT + 16 * J + (e & 15)] = from_f<ST>(0.f);
-        }
-      }
+    if (wave == 1) off_tile(sRef[0], 0, b32ahi, b32alo, 0);
+    if (wave >= 2) {
+      off_tile(sRef[1], 0, b64hi, b64lo, 0);
+      off_tile(sRef[1], 1, b64hi, b64lo, 16);
     }
-  }
-
-  // ---- elementwise outputs: qg, kgT, X^T (LDS), gdec
-  {
-    constexpr int CG = KD / 8;
-    if (has_q) {
-      ST* qg = static_cast<ST*>(a.qg) + ch * (BT * KD);
-      for (int idx = tid; idx < BT * CG; idx += NTH) {
-        const int i = idx / CG, c0 = (idx % CG) * 8;
-        float x[8], gi[8];
-        load8(&sQV[i * PQ + c0], x);
-        load8(&sG[i * PG + c0], gi);
-        const float s = a.scale * sRq[i];
-        float outv[8];
+    if (wave == 3) off_tile(sRef[2], 2, b32bhi, b32blo, 0);
+    if (has_q) {  // upper-triangle tiles of this row tile are zero
+      for (int J = wave + 1; J < 4; ++J)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) outv[e] = x[e] * s * exp2f(gi[e]);
-        store8(qg + i * KD + c0, outv);
-      }
+        for (int e = 0; e < 4; ++e)
+          store_val(Aqk_out + (16 * wave + 4 * quad + e) * BT + 16 * J + r16, 0.f);
     }
-    float* kgT = static_cast<float*>(a.kgT) + ch * (KD * BT);
-    for (int idx = tid; idx < KD * 8; idx += NTH) {
-      const int c = idx >> 3, t0 = (idx & 7) * 8;
-      const float gC = sG[63 * PG + c];
-      float kv[8], xv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = t0 + e;
-        const float kn = to_f<IT>(sK[t * PQ + c]) * sRk[t];
-        const float gt = sG[t * PG + c];
-        kv[e] = kn * exp2f(gC - gt);
-        xv[e] = kn * exp2f(gt);
-      }
-      store8(kgT + c * BT + t0, kv);
-      store8(sXT + c * PT + t0, xv);
-    }
-    if (tid < KD) a.gdec[ch * KD + tid] = exp2f(sG[63 * PG + tid]);
   }
   __syncthreads();
 
-  // ---- diagonal 16x16 inverses (wave 0) | v^T into LDS (waves 1..7)
-  if (wave == 0) {
-    const int b = lane >> 4, jj = lane & 15;
+  // ---- v^T and X^T = (k * 2^gamma)^T into LDS; diagonal 16x16 inverses
+#pragma unroll
+  for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sVT[(32 * vs + 8 * quad + e) * PT + i] = from_f<ST>(vx[vs][e]);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sXT[(32 * ks + 8 * quad + e) * PT + i] = from_f<ST>(kx[ks][e] * fexp2(gl[ks][e]));
+  if (quad == 0) {
+    const int b = wave, jj = r16;
     float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float s = (i == jj) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      float s = (r == jj) ? 1.f : 0.f;
 #pragma unroll
-      for (int kq = 0; kq < i; ++kq) s -= sL[(16 * b + i) * P64 + 16 * b + kq] * x[kq];
-      x[i] = s;
+      for (int kq = 0; kq < r; ++kq) s -= sL[(16 * b + r) * P64 + 16 * b + kq] * x[kq];
+      x[r] = s;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sA[(16 * b + i) * P64 + 16 * b + jj] = x[i];
-  } else {
-    constexpr int CPRV = VD / EI, TOTV = 64 * CPRV;
-    const IT* vp = static_cast<const IT*>(a.v);
-    const int64_t vstride = (int64_t)a.Hv * VD;
-    for (int id = tid - 64; id < TOTV; id += NTH - 64) {
-      const int row = id / CPRV, part = id % CPRV;
-      u32x4 uv = u32x4{0u, 0u, 0u, 0u};
-      if (row < C) uv = *reinterpret_cast<const u32x4*>(vp + (tok0 + row) * vstride + h * VD + part * EI);
-      const IT* ev = reinterpret_cast<const IT*>(&uv);
-#pragma unroll
-      for (int e = 0; e < EI; ++e) sQV[(part * EI + e) * PT + row] = ev[e];
-    }
+    for (int r = 0; r < 16; ++r) sA[(16 * b + r) * P64 + 16 * b + jj] = x[r];
+  }
+  // zero the strictly upper blocks of A (read by the u/w products)
+  for (int idx = tid; idx < 6 * 256; idx += 256) {
+    const int t = idx >> 8, e = idx & 255;
+    const int I = t < 3 ? 0 : (t < 5 ? 1 : 2);
+    const int J = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
+    sA[(16 * I + (e >> 4)) * P64 + 16 * J + (e & 15)] = 0.f;
   }
   __syncthreads();
 
@@ -348,6 +402,7 @@ __global__ __launch_bounds__(512) void intra_kernel(IntraArgs a) {
         const int I = wave + d, J = wave;
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int m = J; m < I; ++m) {
+#pragma unroll 4
           for (int kq = 0; kq < 16; ++kq) {
             const float av = sA[(16 * m + kq) * P64 + 16 * J + jj];
 #pragma unroll
@@ -361,6 +416,7 @@ __global__ __launch_bounds__(512) void intra_kernel(IntraArgs a) {
       if (wave <= 3 - d) {
         const int I = wave + d, J = wave;
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
         for (int kq = 0; kq < 16; ++kq) {
           const float xv = sX[wave * 256 + kq * 16 + jj];
 #pragma unroll
@@ -373,39 +429,29 @@ __global__ __launch_bounds__(512) void intra_kernel(IntraArgs a) {
     }
   }
 
-  // ---- u = A diag(beta) v,  w = A diag(beta) X   (X = k * 2^gamma)
+  // ---- u^T = (A diag(beta) v)^T (fp32),  w = A diag(beta) X (token dtype)
   {
-    const int I = wave & 3, isw = wave >> 2;
-    const int r16 = lane & 15, quad = lane >> 4;
+    const int I = wave;
     const int nks = I >= 2 ? 2 : 1;                // A is lower triangular
     Frag fa[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      if (ks < nks) {
-        const int j0 = ks * 32 + 8 * quad;
-        float x[8];
+      float x[8];
+      const int j0 = 32 * ks + 8 * quad;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = sA[(16 * I + r16) * P64 + j0 + e] * sBeta[j0 + e];
-        fa[ks] = split8(x);
-      }
+      for (int e = 0; e < 8; ++e) x[e] = ks < nks ? sA[(16 * I + r16) * P64 + j0 + e] * sBeta[j0 + e] : 0.f;
+      fa[ks] = split8(x);
     }
-    const int ND = isw ? KD : VD;
-    const ST* Bsrc = isw ? sXT : sQV;
-    ST* dstw = static_cast<ST*>(a.w) + ch * (BT * KD);       // w in the token dtype
-    float* dstu = static_cast<float*>(a.u) + ch * (BT * VD);  // u in fp32
-    for (int ct = 0; ct < ND / 16; ++ct) {
+    auto tile = [&](const ST* bsrc, int ct) __attribute__((always_inline)) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         if (ks < nks) {
-          const ST* bp = Bsrc + (16 * ct + r16) * PT + ks * 32 + 8 * quad;
+          const ST* bp = bsrc + (16 * ct + r16) * PT + 32 * ks + 8 * quad;
           if (F32) {
             float xb[8];
             load8(reinterpret_cast<const float*>(bp), xb);
-            Frag fb = split8(xb);
-            acc = mfma(fa[ks].hi, fb.hi, acc);
-            acc = mfma(fa[ks].lo, fb.hi, acc);
-            acc = mfma(fa[ks].hi, fb.lo, acc);
+            acc = mma3(fa[ks], split8(xb), acc);
           } else {
             bf16x8 b = load_bf16x8(reinterpret_cast<const bf16_t*>(bp));
             acc = mfma(fa[ks].hi, b, acc);
@@ -413,12 +459,18 @@ __global__ __launch_bounds__(512) void intra_kernel(IntraArgs a) {
           }
         }
       }
+      return acc;
+    };
+    float* uT = static_cast<float*>(a.u) + ch * (VD * BT);
+    for (int ct = 0; ct < VD / 16; ++ct) {
+      f32x4 acc = tile(sVT, ct);
+      *reinterpret_cast<f32x4*>(uT + (16 * ct + r16) * BT + 16 * I + 4 * quad) = acc;
+    }
+    ST* wout = static_cast<ST*>(a.w) + ch * (BT * KD);
+    for (int ct = 0; ct < KD / 16; ++ct) {
+      f32x4 acc = tile(sXT, ct);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int idx = (16 * I + 4 * quad + e) * ND + 16 * ct + r16;
-        if (isw) dstw[idx] = from_f<ST>(acc[e]);
-        else dstu[idx] = acc[e];
-      }
+      for (int e = 0; e < 4; ++e) store_val(wout + (16 * I + 4 * quad + e) * KD + 16 * ct + r16, acc[e]);
     }
   }
 }
@@ -427,7 +479,7 @@ __global__ __launch_bounds__(512) void intra_kernel(IntraArgs a) {
 
 hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t s) {
   if (a.nchunks == 0 || a.Hv == 0) return hipSuccess;
-  dim3 grid(a.nchunks, a.Hv), block(512);
+  dim3 grid(a.nchunks, a.Hv), block(256);
 #define KDA_INTRA_CASE(KK, VV, TT)                                          \
   if (K == KK && V == VV) {                                                 \
     hipLaunchKernelGGL((intra_kernel<KK, VV, TT>), grid, block, 0, s, a);   \

@@ -9,10 +9,17 @@
 //   o     = qg h + tril(Aqk) v_new               (forward mode only)
 //   h     = Diag(gdec) h + kg^T v_new
 // The state stays in the matrix-core accumulators (fp32) for the whole
-// sequence; it is rounded to a bf16 hi/lo pair only as an operand, and u,
-// kg^T and v_new enter the state update as fp32 (hi/lo pairs), so each
-// state-feeding product carries ~16 significant bits.  The next chunk's
-// inputs are prefetched into registers while the current chunk computes.
+// sequence.  It is rounded to a bf16 hi/lo pair as an operand, and u, kg^T and
+// v_new enter the state update as fp32 (hi/lo pairs), so each state-feeding
+// product carries ~16 significant bits.  Every per-chunk operand is read from
+// the workspace straight into registers in the matrix-core layout, one chunk
+// ahead of its use; only h^T and v_new^T, which the workgroup produces itself,
+// pass through LDS.
+//
+// Each workgroup has 4 state waves, which carry the recurrence, and in forward
+// mode 4 output waves, which form o from the same h^T and v_new^T off the
+// critical path.  Two workgroup barriers per chunk order the roles: h^T is
+// published before the first, v_new^T before the second.
 //
 // Summary mode scans the augmented state [S~ | M] (K x (V + K)) from [0 | I]
 // with u = [u | 0] and writes S~ and M ("KDA Context Parallelism (KCP)",
@@ -24,32 +31,76 @@ namespace kda {
 
 namespace {
 
-constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
-constexpr int imax(int a, int b) { return a > b ? a : b; }
+// One 8-element matrix-core operand fragment as stored in the workspace.
+template <typename ST> struct Op;
+template <> struct Op<bf16_t> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+};
+template <> struct Op<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ Frag split() const {
+    float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return split8(x);
+  }
+};
 
+// acc += op * (bhi + blo)
+__device__ __forceinline__ f32x4 mma_bsplit(const Op<bf16_t>& op, const bf16x8& bhi, const bf16x8& blo,
+                                            f32x4 acc) {
+  acc = mfma(op.v, bhi, acc);
+  return mfma(op.v, blo, acc);
+}
+__device__ __forceinline__ f32x4 mma_bsplit(const Op<float>& op, const bf16x8& bhi, const bf16x8& blo,
+                                            f32x4 acc) {
+  Frag f = op.split();
+  acc = mfma(f.hi, bhi, acc);
+  acc = mfma(f.hi, blo, acc);
+  return mfma(f.lo, bhi, acc);
+}
+// acc += op * b for the output terms: bf16 operands use the hi part of b only;
+// fp32 operands keep full precision.
+__device__ __forceinline__ f32x4 mma_out(const Op<bf16_t>& op, const bf16x8& bhi, const bf16x8&, f32x4 acc) {
+  return mfma(op.v, bhi, acc);
+}
+__device__ __forceinline__ f32x4 mma_out(const Op<float>& op, const bf16x8& bhi, const bf16x8& blo, f32x4 acc) {
+  return mma_bsplit(op, bhi, blo, acc);
+}
+
+// Per-chunk operands of a state wave (v_new and the state update).
+template <int KD, int BV, typename ST>
+struct StateFrags {
+  static constexpr int NKS = KD / 32, RT = KD / 64, CT = BV / 16;
+  Op<ST> w[NKS];          // w rows 16*sw + r16, channels 32*ks + 8*quad
+  Op<float> kg[RT][2];    // kg^T rows 16*(RT*sw + rt) + r16, tokens 32*ks + 8*quad
+  f32x4 u[CT];            // u^T row (value column) v0 + 16*ct + r16, tokens 16*sw + 4*quad .. +3
+  f32x4 gd[RT];           // gdec for channels 16*(RT*sw + rt) + 4*quad .. +3
+};
+// Per-chunk operands of an output wave.
+template <int KD, typename ST>
+struct OutFrags {
+  static constexpr int NKS = KD / 32;
+  Op<ST> q[NKS];          // qg rows 16*ow + r16, channels 32*ks + 8*quad
+  Op<ST> aq[2];           // Aqk rows 16*ow + r16, tokens 32*ks + 8*quad
+};
+
+// Workgroup: 4 state waves (v_new and the state update: the recurrence's
+// critical path) and, in forward mode, 4 output waves that compute o from the
+// same h^T and v_new^T while the state waves move on.
 template <int KD, int VD, int BV, typename ST, bool SUM>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
-  constexpr int NTH = 256;
-  constexpr bool F32 = sizeof(ST) == 4;
-  constexpr int ES = sizeof(ST);
-  constexpr int EI = 16 / ES;
-  constexpr int PK = KD + EI;          // rows of K elements (w, qg), ST
-  constexpr int PT = 64 + EI;          // rows of 64 elements (Aqk), ST
-  constexpr int PKG = 64 + 4;          // kg^T rows (fp32)
-  constexpr int PU = BV + 4;           // u tile rows (fp32)
+__global__ __launch_bounds__(SUM ? 256 : 512) void scan_kernel(ScanArgs a) {
+  using SF = StateFrags<KD, BV, ST>;
+  using OF = OutFrags<KD, ST>;
+  constexpr int NKS = SF::NKS, RT = SF::RT, CT = SF::CT;
   constexpr int PH = KD + 8;           // h^T rows (bf16)
   constexpr int PV = 64 + 8;           // v_new^T rows (bf16)
   constexpr int VA = SUM ? VD + KD : VD;
   constexpr int NTILE = VA / BV;
-  constexpr int RT = KD / 64;          // h row tiles per wave
-  constexpr int CT = BV / 16;          // column tiles
 
-  __shared__ __attribute__((aligned(16))) ST sW[64 * PK];
-  __shared__ __attribute__((aligned(16))) float sKg[KD * PKG];
-  __shared__ __attribute__((aligned(16))) ST sQg[SUM ? 8 : 64 * PK];
-  __shared__ __attribute__((aligned(16))) ST sAq[SUM ? 8 : 64 * PT];
-  __shared__ __attribute__((aligned(16))) float sU[64 * PU];
-  __shared__ __attribute__((aligned(16))) float sGd[KD];
   __shared__ __attribute__((aligned(16))) bf16_t sHhi[BV * PH];
   __shared__ __attribute__((aligned(16))) bf16_t sHlo[BV * PH];
   __shared__ __attribute__((aligned(16))) bf16_t sVhi[BV * PV];
@@ -64,6 +115,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int n = lid / (NTILE * a.Hv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, quad = lane >> 4;
+  const int rw = wave & 3;                              // wave index within its role
 
   int64_t tok0s;
   int len;
@@ -73,242 +125,214 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const bool mtile = SUM && tv * BV >= VD;              // columns of M
   const int v0 = mtile ? tv * BV - VD : tv * BV;        // first column inside S~ or M
 
-  // ---- register staging of one chunk's inputs (16-byte pieces)
-  constexpr int NWp = 64 * KD * ES / 16, NKp = KD * 64 * 4 / 16;
-  constexpr int NQp = SUM ? 0 : 64 * KD * ES / 16, NAp = SUM ? 0 : 64 * 64 * ES / 16;
-  constexpr int NUp = 64 * BV * 4 / 16, NGp = KD * 4 / 16;
-  constexpr int CW = cdiv(NWp, NTH), CK = cdiv(NKp, NTH), CQ = imax(1, cdiv(NQp, NTH));
-  constexpr int CA = imax(1, cdiv(NAp, NTH)), CU = cdiv(NUp, NTH), CG = cdiv(NGp, NTH);
-  u32x4 rW[CW], rK[CK], rQ[CQ], rA[CA], rU[CU], rG[CG];
+  if (wave < 4) {
+    // =========================== state waves ===========================
+    auto load = [&](SF& f, int c) __attribute__((always_inline)) {
+      const int64_t ch = (int64_t)h * a.nchunks + cb + c;
+      const ST* w = static_cast<const ST*>(a.w) + ch * (64 * KD) + (16 * rw + r16) * KD + 8 * quad;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) f.w[ks].load(w + 32 * ks);
+      const float* kg = static_cast<const float*>(a.kgT) + ch * (KD * 64) + 8 * quad;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) f.kg[rt][ks].load(kg + (16 * (RT * rw + rt) + r16) * 64 + 32 * ks);
+      const float* u = static_cast<const float*>(a.u) + ch * (VD * 64) + 16 * rw + 4 * quad;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        f.u[ct] = mtile ? zero4() : *reinterpret_cast<const f32x4*>(u + (v0 + 16 * ct + r16) * 64);
+      const float* gd = a.gdec + ch * KD + 4 * quad;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) f.gd[rt] = *reinterpret_cast<const f32x4*>(gd + 16 * (RT * rw + rt));
+    };
 
-  auto load_chunk = [&](int c) __attribute__((always_inline)) {
-    const int64_t ch = (int64_t)h * a.nchunks + cb + c;
-    const u32x4* gw = reinterpret_cast<const u32x4*>(static_cast<const ST*>(a.w) + ch * (64 * KD));
-    const u32x4* gk = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.kgT) + ch * (64 * KD));
-#pragma unroll
-    for (int i = 0; i < CW; ++i) { int p = tid + i * NTH; if (p < NWp) rW[i] = gw[p]; }
-#pragma unroll
-    for (int i = 0; i < CK; ++i) { int p = tid + i * NTH; if (p < NKp) rK[i] = gk[p]; }
+    // state tile in accumulators: rows 16*(RT*rw+rt) + 4*quad + e, col 16*ct + r16
+    f32x4 hs[RT][CT];
+    const float* h0p = nullptr;
+    bool valid_row = true;
+    int64_t srow = n;
     if (!SUM) {
-      const u32x4* gq = reinterpret_cast<const u32x4*>(static_cast<const ST*>(a.qg) + ch * (64 * KD));
-      const u32x4* ga = reinterpret_cast<const u32x4*>(static_cast<const ST*>(a.Aqk) + ch * (64 * 64));
-#pragma unroll
-      for (int i = 0; i < CQ; ++i) { int p = tid + i * NTH; if (p < NQp) rQ[i] = gq[p]; }
-#pragma unroll
-      for (int i = 0; i < CA; ++i) { int p = tid + i * NTH; if (p < NAp) rA[i] = ga[p]; }
-    }
-    const float* gu = static_cast<const float*>(a.u) + ch * (64 * VD) + v0;
-    constexpr int UPR = BV / 4;           // pieces per u row
-#pragma unroll
-    for (int i = 0; i < CU; ++i) {
-      int p = tid + i * NTH;
-      if (p < NUp) {
-        if (mtile) rU[i] = u32x4{0u, 0u, 0u, 0u};
-        else rU[i] = *reinterpret_cast<const u32x4*>(gu + (p / UPR) * VD + (p % UPR) * 4);
+      if (a.state_rows > 0) {
+        const int r = a.state_idx[n];
+        valid_row = r >= 0 && r < a.state_rows;
+        srow = r;
+        if (valid_row && a.h0) h0p = a.h0 + (srow * a.Hv + h) * (int64_t)(KD * VD);
+      } else if (a.h0) {
+        h0p = a.h0 + ((int64_t)n * a.Hv + h) * (int64_t)(KD * VD);
       }
     }
-    const u32x4* gg = reinterpret_cast<const u32x4*>(a.gdec + ch * KD);
-#pragma unroll
-    for (int i = 0; i < CG; ++i) { int p = tid + i * NTH; if (p < NGp) rG[i] = gg[p]; }
-  };
-  auto stage_chunk = [&]() __attribute__((always_inline)) {
-    constexpr int WPR = KD * ES / 16, KPR = 64 * ES / 16, KGPR = 64 / 4, UPR = BV / 4;
-#pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      int p = tid + i * NTH;
-      if (p < NWp) *reinterpret_cast<u32x4*>(sW + (p / WPR) * PK + (p % WPR) * EI) = rW[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CK; ++i) {
-      int p = tid + i * NTH;
-      if (p < NKp) *reinterpret_cast<u32x4*>(sKg + (p / KGPR) * PKG + (p % KGPR) * 4) = rK[i];
-    }
-    if (!SUM) {
-#pragma unroll
-      for (int i = 0; i < CQ; ++i) {
-        int p = tid + i * NTH;
-        if (p < NQp) *reinterpret_cast<u32x4*>(sQg + (p / WPR) * PK + (p % WPR) * EI) = rQ[i];
-      }
-#pragma unroll
-      for (int i = 0; i < CA; ++i) {
-        int p = tid + i * NTH;
-        if (p < NAp) *reinterpret_cast<u32x4*>(sAq + (p / KPR) * PT + (p % KPR) * EI) = rA[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < CU; ++i) {
-      int p = tid + i * NTH;
-      if (p < NUp) *reinterpret_cast<u32x4*>(sU + (p / UPR) * PU + (p % UPR) * 4) = rU[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CG; ++i) {
-      int p = tid + i * NTH;
-      if (p < NGp) *reinterpret_cast<u32x4*>(sGd + p * 4) = rG[i];
-    }
-  };
-
-  // ---- state tile in accumulators: rows 16*(RT*wave+rt) + 4*quad + e, col 16*ct + r16
-  f32x4 hs[RT][CT];
-  const float* h0p = nullptr;
-  bool valid_row = true;
-  int64_t srow = n;
-  if (!SUM) {
-    if (a.state_rows > 0) {
-      const int r = a.state_idx[n];
-      valid_row = r >= 0 && r < a.state_rows;
-      srow = r;
-      if (valid_row && a.h0) h0p = a.h0 + (srow * a.Hv + h) * (int64_t)(KD * VD);
-    } else if (a.h0) {
-      h0p = a.h0 + ((int64_t)n * a.Hv + h) * (int64_t)(KD * VD);
-    }
-  }
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * (RT * wave + rt) + 4 * quad + e, col = 16 * ct + r16;
-        float x = 0.f;
-        if (mtile) x = (row == v0 + col) ? 1.f : 0.f;
-        else if (h0p) x = h0p[(int64_t)row * VD + v0 + col];
-        hs[rt][ct][e] = x;
-      }
-
-  if (nck > 0) load_chunk(0);
-  for (int c = 0; c < nck; ++c) {
-    stage_chunk();
-    // h^T as bf16 hi/lo operand
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int row0 = 16 * (RT * wave + rt) + 4 * quad, col = 16 * ct + r16;
-        uint32_t hi01, hi23, lo01, lo23;
-        float hv[4], lv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hv[e] = hs[rt][ct][e];
-          lv[e] = hv[e] - bf2f(f2bf(hv[e]));
-        }
-        hi01 = pack_bf16x2(hv[0], hv[1]);
-        hi23 = pack_bf16x2(hv[2], hv[3]);
-        lo01 = pack_bf16x2(lv[0], lv[1]);
-        lo23 = pack_bf16x2(lv[2], lv[3]);
-        *reinterpret_cast<u32x2*>(sHhi + col * PH + row0) = u32x2{hi01, hi23};
-        *reinterpret_cast<u32x2*>(sHlo + col * PH + row0) = u32x2{lo01, lo23};
-      }
-    __syncthreads();
-    if (c + 1 < nck) load_chunk(c + 1);
-
-    // ---- v_new = u - w h   (wave: token rows 16*wave .. +15)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < KD / 32; ++ks) {
-        const int k0 = ks * 32 + 8 * quad;
-        acc = mma_a_bsplit(sW + (16 * wave + r16) * PK + k0, sHhi + (16 * ct + r16) * PH + k0,
-                           sHlo + (16 * ct + r16) * PH + k0, acc);
-      }
-      const int t0 = 16 * wave + 4 * quad, col = 16 * ct + r16;
-      float vn[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vn[e] = sU[(t0 + e) * PU + col] - acc[e];
-      float lv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) lv[e] = vn[e] - bf2f(f2bf(vn[e]));
-      *reinterpret_cast<u32x2*>(sVhi + col * PV + t0) =
-          u32x2{pack_bf16x2(vn[0], vn[1]), pack_bf16x2(vn[2], vn[3])};
-      *reinterpret_cast<u32x2*>(sVlo + col * PV + t0) =
-          u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
-    }
-    __syncthreads();
-
-    // ---- o = qg h + tril(Aqk) v_new
-    if (!SUM) {
-      const int Cn = min(BT, len - c * BT);
-      const int64_t tokc = tok0s + (int64_t)c * BT;
-      ST* op = static_cast<ST*>(a.o);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KD / 32; ++ks) {
-          const int k0 = ks * 32 + 8 * quad;
-          if (F32)
-            acc = mma_a_bsplit(sQg + (16 * wave + r16) * PK + k0, sHhi + (16 * ct + r16) * PH + k0,
-                               sHlo + (16 * ct + r16) * PH + k0, acc);
-          else
-            acc = mma_a_bhi(sQg + (16 * wave + r16) * PK + k0, sHhi + (16 * ct + r16) * PH + k0, acc);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (ks * 2 <= wave) {     // Aqk is lower triangular
-            const int k0 = ks * 32 + 8 * quad;
-            if (F32)
-              acc = mma_a_bsplit(sAq + (16 * wave + r16) * PT + k0, sVhi + (16 * ct + r16) * PV + k0,
-                                 sVlo + (16 * ct + r16) * PV + k0, acc);
-            else
-              acc = mma_a_bhi(sAq + (16 * wave + r16) * PT + k0, sVhi + (16 * ct + r16) * PV + k0, acc);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * wave + 4 * quad + e;
-          if (t < Cn)
-            op[(tokc + t) * (int64_t)(a.Hv * VD) + (int64_t)h * VD + v0 + 16 * ct + r16] = from_f<ST>(acc[e]);
-        }
-      }
-    }
-
-    // ---- h = Diag(gdec) h + kg^T v_new
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int R = RT * wave + rt;
-      float gd[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) gd[e] = sGd[16 * R + 4 * quad + e];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        f32x4 acc = hs[rt][ct];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] *= gd[e];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int k0 = ks * 32 + 8 * quad;
-          acc = mma_a_bsplit(sKg + (16 * R + r16) * PKG + k0, sVhi + (16 * ct + r16) * PV + k0,
-                             sVlo + (16 * ct + r16) * PV + k0, acc);
-        }
-        hs[rt][ct] = acc;
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- final state
-  float* dst = nullptr;
-  int64_t ld = VD;
-  if (SUM) {
-    if (mtile) { dst = a.M + ((int64_t)n * a.Hv + h) * (int64_t)(KD * KD); ld = KD; }
-    else dst = a.hT + ((int64_t)n * a.Hv + h) * (int64_t)(KD * VD);
-  } else if (a.hT) {
-    if (a.state_rows > 0) {
-      if (valid_row) dst = a.hT + (srow * a.Hv + h) * (int64_t)(KD * VD);
-    } else {
-      dst = a.hT + ((int64_t)n * a.Hv + h) * (int64_t)(KD * VD);
-    }
-  }
-  if (dst) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = 16 * (RT * wave + rt) + 4 * quad + e, col = 16 * ct + r16;
-          dst[(int64_t)row * ld + v0 + col] = hs[rt][ct][e];
+          const int row = 16 * (RT * rw + rt) + 4 * quad + e, col = 16 * ct + r16;
+          float x = 0.f;
+          if (mtile) x = (row == v0 + col) ? 1.f : 0.f;
+          else if (h0p) x = h0p[(int64_t)row * VD + v0 + col];
+          hs[rt][ct][e] = x;
         }
+
+    auto step = [&](const SF& cur, SF& nxt, int c) __attribute__((always_inline)) {
+      if (c + 1 < nck) load(nxt, c + 1);
+      // h^T as a bf16 hi/lo operand
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int row0 = 16 * (RT * rw + rt) + 4 * quad, col = 16 * ct + r16;
+          float hv[4], lv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hv[e] = hs[rt][ct][e];
+            lv[e] = hv[e] - bf2f(f2bf(hv[e]));
+          }
+          *reinterpret_cast<u32x2*>(sHhi + col * PH + row0) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+          *reinterpret_cast<u32x2*>(sHlo + col * PH + row0) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+        }
+      __syncthreads();
+
+      // ---- v_new = u - w h   (token rows 16*rw .. +15)
+      bf16x8 bh[CT][NKS], bl[CT][NKS];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int off = (16 * ct + r16) * PH + 32 * ks + 8 * quad;
+          bh[ct][ks] = load_bf16x8(sHhi + off);
+          bl[ct][ks] = load_bf16x8(sHlo + off);
+        }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc = mma_bsplit(cur.w[ks], bh[ct][ks], bl[ct][ks], acc);
+        const int t0 = 16 * rw + 4 * quad, col = 16 * ct + r16;
+        float vn[4], lv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vn[e] = cur.u[ct][e] - acc[e];
+          lv[e] = vn[e] - bf2f(f2bf(vn[e]));
+        }
+        *reinterpret_cast<u32x2*>(sVhi + col * PV + t0) = u32x2{pack_bf16x2(vn[0], vn[1]), pack_bf16x2(vn[2], vn[3])};
+        *reinterpret_cast<u32x2*>(sVlo + col * PV + t0) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+      }
+      __syncthreads();
+
+      // ---- h = Diag(gdec) h + kg^T v_new
+      bf16x8 vh[CT][2], vl[CT][2];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int off = (16 * ct + r16) * PV + 32 * ks + 8 * quad;
+          vh[ct][ks] = load_bf16x8(sVhi + off);
+          vl[ct][ks] = load_bf16x8(sVlo + off);
+        }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const Frag kf[2] = {cur.kg[rt][0].split(), cur.kg[rt][1].split()};
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          f32x4 acc = hs[rt][ct];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] *= cur.gd[rt][e];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            acc = mfma(kf[ks].hi, vh[ct][ks], acc);
+            acc = mfma(kf[ks].hi, vl[ct][ks], acc);
+            acc = mfma(kf[ks].lo, vh[ct][ks], acc);
+          }
+          hs[rt][ct] = acc;
+        }
+      }
+    };
+
+    SF fa, fb;
+    if (nck > 0) load(fa, 0);
+    for (int c = 0; c < nck; c += 2) {
+      step(fa, fb, c);
+      if (c + 1 < nck) step(fb, fa, c + 1);
+    }
+
+    // ---- final state
+    float* dst = nullptr;
+    int64_t ld = VD;
+    if (SUM) {
+      if (mtile) { dst = a.M + ((int64_t)n * a.Hv + h) * (int64_t)(KD * KD); ld = KD; }
+      else dst = a.hT + ((int64_t)n * a.Hv + h) * (int64_t)(KD * VD);
+    } else if (a.hT) {
+      if (a.state_rows > 0) {
+        if (valid_row) dst = a.hT + (srow * a.Hv + h) * (int64_t)(KD * VD);
+      } else {
+        dst = a.hT + ((int64_t)n * a.Hv + h) * (int64_t)(KD * VD);
+      }
+    }
+    if (dst) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * (RT * rw + rt) + 4 * quad + e, col = 16 * ct + r16;
+            dst[(int64_t)row * ld + v0 + col] = hs[rt][ct][e];
+          }
+    }
+  } else if constexpr (!SUM) {
+    // =========================== output waves ==========================
+    auto load = [&](OF& f, int c) __attribute__((always_inline)) {
+      const int64_t ch = (int64_t)h * a.nchunks + cb + c;
+      const ST* q = static_cast<const ST*>(a.qg) + ch * (64 * KD) + (16 * rw + r16) * KD + 8 * quad;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) f.q[ks].load(q + 32 * ks);
+      const ST* aq = static_cast<const ST*>(a.Aqk) + ch * (64 * 64) + (16 * rw + r16) * 64 + 8 * quad;
+      f.aq[0].load(aq);
+      if (rw >= 2) f.aq[1].load(aq + 32);
+    };
+    ST* op = static_cast<ST*>(a.o);
+    auto step = [&](const OF& cur, OF& nxt, int c) __attribute__((always_inline)) {
+      if (c + 1 < nck) load(nxt, c + 1);
+      __syncthreads();
+      // o = qg h (needs only h^T, overlaps the state waves' v_new)
+      f32x4 acc[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        acc[ct] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int off = (16 * ct + r16) * PH + 32 * ks + 8 * quad;
+          acc[ct] = mma_out(cur.q[ks], load_bf16x8(sHhi + off), load_bf16x8(sHlo + off), acc[ct]);
+        }
+      }
+      __syncthreads();
+      // o += tril(Aqk) v_new
+      const int Cn = min(BT, len - c * BT);
+      const int64_t tokc = tok0s + (int64_t)c * BT;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks * 2 <= rw) {     // Aqk is lower triangular
+            const int off = (16 * ct + r16) * PV + 32 * ks + 8 * quad;
+            acc[ct] = mma_out(cur.aq[ks], load_bf16x8(sVhi + off), load_bf16x8(sVlo + off), acc[ct]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * rw + 4 * quad + e;
+          if (t < Cn)
+            op[(tokc + t) * (int64_t)(a.Hv * VD) + (int64_t)h * VD + v0 + 16 * ct + r16] = from_f<ST>(acc[ct][e]);
+        }
+      }
+    };
+    OF fa, fb;
+    if (nck > 0) load(fa, 0);
+    for (int c = 0; c < nck; c += 2) {
+      step(fa, fb, c);
+      if (c + 1 < nck) step(fb, fa, c + 1);
+    }
   }
 }
 
@@ -349,7 +373,7 @@ hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s
   const int VA = a.summary ? V + K : V;
   const long nb = (long)(VA / BV) * a.Hv * a.seq.N;
   if (nb > 0x7fffffffL) return hipErrorInvalidValue;
-  dim3 grid((unsigned)nb), block(256);
+  dim3 grid((unsigned)nb), block(a.summary ? 256 : 512);
 #define KDA_SCAN_CASE(KK, VV, TT)                                                    \
   if (K == KK && V == VV) {                                                          \
     if (a.summary) hipLaunchKernelGGL((scan_kernel<KK, VV, BV, TT, true>), grid, block, 0, s, a); \
