@@ -109,6 +109,44 @@ def traffic_for(kernel):
     return e["bytes_per_launch"]
 
 
+def summarize_pmc(fetch_csv, write_csv, copy_bytes, out_json):
+    """Per-launch HBM bytes of each KDA kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs, scaled by what the same counters read for the calibration copy of
+    `copy_bytes` bytes (read once, written once).  Writes `out_json` and
+    returns a text summary."""
+    import csv
+    import statistics
+
+    def per_kernel(path):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    copy_name = max((k for k in fetch if "copy" in k.lower()), key=lambda k: max(fetch[k]))
+    cf = copy_bytes / (max(fetch[copy_name]) * 1024.0)
+    cw = copy_bytes / (max(write[copy_name]) * 1024.0)
+    out = {"calibration": {"kernel": copy_name, "bytes": copy_bytes, "fetch_factor": cf,
+                           "write_factor": cw}}
+    lines = [f"calibration copy {copy_name}: {copy_bytes / 1e6:.1f} MB read + written; "
+             f"FETCH_SIZE factor {cf:.4f}, WRITE_SIZE factor {cw:.4f} (bytes per counted byte)"]
+    for short, key in (("intra_kernel", "intra_kernel"), ("scan_kernel", "scan_kernel")):
+        names = [k for k in fetch if key in k]
+        if not names:
+            continue
+        k = names[0]
+        fb = statistics.mean(fetch[k]) * 1024.0 * cf
+        wb = statistics.mean(write[k]) * 1024.0 * cw
+        out[short] = {"kernel": k, "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                      "source_sha256": source_hash()}
+        lines.append(f"{short}: fetch {fb / 1e6:.1f} MB + write {wb / 1e6:.1f} MB = "
+                     f"{(fb + wb) / 1e6:.1f} MB per launch ({len(fetch[k])} launches)")
+    with open(out_json, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,7 +154,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mb", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MB (PMC calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
+                            args.calibration_copy_mb * 1024 * 1024,
+                            os.path.join(ROOT, "profiles", "pmc_traffic.json")))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -166,6 +213,14 @@ def main():
     intra = [hev.elapsed_ms(evs[3 * i], evs[3 * i + 1]) for i in range(args.steps)]
     scan = [hev.elapsed_ms(evs[3 * i + 1], evs[3 * i + 2]) for i in range(args.steps)]
     hev.destroy(evs)
+
+    if args.calibration_copy_mb:
+        src = torch.empty(args.calibration_copy_mb * 1024 * 1024, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms = total_ms / args.steps
     flop, nbytes = algorithmic(B, T, H, K, V)

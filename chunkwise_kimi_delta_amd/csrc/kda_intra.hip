@@ -70,8 +70,11 @@ __device__ __forceinline__ f32x4 mma3(const Frag& A, const Frag& B, f32x4 acc) {
   return acc;
 }
 
-template <typename ST>
-__device__ __forceinline__ void store_val(ST* p, float v) { *p = from_f<ST>(v); }
+// Store 4 consecutive values (8 bytes as bf16, 16 bytes as fp32).
+__device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
 
 template <int KD, int VD, typename IT>
 __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
@@ -291,31 +294,37 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
           rb[e] = isrow ? 0.f : kv;
           rq8[e] = isrow ? qx[ks][e] * f : 0.f;
         }
-        Frag A = split8(ra), B = split8(rb);
-        dk[b] = mma3(A, B, dk[b]);
+        // transposed tile: column-side rows are the A operand, row-side rows the B operand
+        Frag R = split8(ra), Cs = split8(rb);
+        dk[b] = mma3(Cs, R, dk[b]);
         if (has_q) {
-          if (F32) dq[b] = mma3(split8(rq8), B, dq[b]);
-          else dq[b] = mfma(round8(rq8), B.hi, dq[b]);
+          if (F32) dq[b] = mma3(Cs, split8(rq8), dq[b]);
+          else dq[b] = mfma(Cs.hi, round8(rq8), dq[b]);
         }
       }
     }
-    // diagonal tile output; the lane with r16 == row owns that row's norms and dot
+    // diagonal tile output: this lane holds row i = r16, columns 4*quad .. +3,
+    // and owns row i's beta, norms and q.k dot
+    {
+      f32x4 vk4, vq4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int il = 4 * quad + e, jl = r16;
-      const int row = 16 * wave + il, col = 16 * wave + jl;
-      float vk = 0.f, vq = 0.f;
-      if (il > jl) {
-        const int b = 31 - __clz(il ^ jl);
-        vk = b == 0 ? dk[0][e] : b == 1 ? dk[1][e] : b == 2 ? dk[2][e] : dk[3][e];
-        vq = b == 0 ? dq[0][e] : b == 1 ? dq[1][e] : b == 2 ? dq[2][e] : dq[3][e];
-        vk *= sBeta[row];
-        vq *= a.scale;
-      } else if (il == jl) {
-        vq = a.scale * rq * rk * dqk;
+      for (int e = 0; e < 4; ++e) {
+        const int il = r16, jl = 4 * quad + e;
+        float vk = 0.f, vq = 0.f;
+        if (il > jl) {
+          const int b = 31 - __clz(il ^ jl);
+          vk = b == 0 ? dk[0][e] : b == 1 ? dk[1][e] : b == 2 ? dk[2][e] : dk[3][e];
+          vq = b == 0 ? dq[0][e] : b == 1 ? dq[1][e] : b == 2 ? dq[2][e] : dq[3][e];
+          vk *= beta;
+          vq *= a.scale;
+        } else if (il == jl) {
+          vq = a.scale * rq * rk * dqk;
+        }
+        vk4[e] = vk;
+        vq4[e] = vq;
       }
-      sL[row * P64 + col] = vk;
-      if (has_q) store_val(Aqk_out + row * BT + col, vq);
+      *reinterpret_cast<f32x4*>(&sL[i * P64 + 16 * wave + 4 * quad]) = vk4;
+      if (has_q) store4(Aqk_out + i * BT + 16 * wave + 4 * quad, vq4);
     }
     // off-diagonal tiles: row operand from this wave's rows, column operand from LDS
     auto off_tile = [&](const float* gref, int J, const bf16_t* bhi, const bf16_t* blo, int brow0)
@@ -332,21 +341,23 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
           ra[e] = kx[ks][e] * f;
           rq8[e] = qx[ks][e] * f;
         }
-        Frag A = split8(ra), B;
-        B.hi = load_bf16x8(bhi + (brow0 + r16) * PB + c0);
-        B.lo = load_bf16x8(blo + (brow0 + r16) * PB + c0);
-        akk = mma3(A, B, akk);
+        Frag R = split8(ra), Cs;
+        Cs.hi = load_bf16x8(bhi + (brow0 + r16) * PB + c0);
+        Cs.lo = load_bf16x8(blo + (brow0 + r16) * PB + c0);
+        akk = mma3(Cs, R, akk);          // transposed tile: row i = r16, columns 4*quad .. +3
         if (has_q) {
-          if (F32) aqk = mma3(split8(rq8), B, aqk);
-          else aqk = mfma(round8(rq8), B.hi, aqk);
+          if (F32) aqk = mma3(Cs, split8(rq8), aqk);
+          else aqk = mfma(Cs.hi, round8(rq8), aqk);
         }
       }
+      f32x4 vk4, vq4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = 16 * wave + 4 * quad + e, col = 16 * J + r16;
-        sL[row * P64 + col] = sBeta[row] * akk[e];
-        if (has_q) store_val(Aqk_out + row * BT + col, a.scale * aqk[e]);
+        vk4[e] = beta * akk[e];
+        vq4[e] = a.scale * aqk[e];
       }
+      *reinterpret_cast<f32x4*>(&sL[i * P64 + 16 * J + 4 * quad]) = vk4;
+      if (has_q) store4(Aqk_out + i * BT + 16 * J + 4 * quad, vq4);
     };
     if (wave == 1) off_tile(sRef[0], 0, b32ahi, b32alo, 0);
     if (wave >= 2) {
@@ -355,10 +366,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     }
     if (wave == 3) off_tile(sRef[2], 2, b32bhi, b32blo, 0);
     if (has_q) {  // upper-triangle tiles of this row tile are zero
-      for (int J = wave + 1; J < 4; ++J)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          store_val(Aqk_out + (16 * wave + 4 * quad + e) * BT + 16 * J + r16, 0.f);
+      for (int J = wave + 1; J < 4; ++J) store4(Aqk_out + i * BT + 16 * J + 4 * quad, zero4());
     }
   }
   __syncthreads();
@@ -466,11 +474,27 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
       f32x4 acc = tile(sVT, ct);
       *reinterpret_cast<f32x4*>(uT + (16 * ct + r16) * BT + 16 * I + 4 * quad) = acc;
     }
-    ST* wout = static_cast<ST*>(a.w) + ch * (BT * KD);
+    // w^T tiles (X^T rows as the A operand): this lane holds token 16*I + r16,
+    // channels 16*ct + 4*quad .. +3 -> one vector store
+    ST* wrow = static_cast<ST*>(a.w) + ch * (BT * KD) + (16 * I + r16) * KD + 4 * quad;
     for (int ct = 0; ct < KD / 16; ++ct) {
-      f32x4 acc = tile(sXT, ct);
+      f32x4 acc = zero4();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_val(wout + (16 * I + 4 * quad + e) * KD + 16 * ct + r16, acc[e]);
+      for (int ks = 0; ks < 2; ++ks) {
+        if (ks < nks) {
+          const ST* xp = sXT + (16 * ct + r16) * PT + 32 * ks + 8 * quad;
+          if (F32) {
+            float xb[8];
+            load8(reinterpret_cast<const float*>(xp), xb);
+            acc = mma3(split8(xb), fa[ks], acc);
+          } else {
+            bf16x8 x = load_bf16x8(reinterpret_cast<const bf16_t*>(xp));
+            acc = mfma(x, fa[ks].hi, acc);
+            acc = mfma(x, fa[ks].lo, acc);
+          }
+        }
+      }
+      store4(wrow + 16 * ct, acc);
     }
   }
 }

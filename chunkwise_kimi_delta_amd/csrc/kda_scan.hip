@@ -62,16 +62,23 @@ __device__ __forceinline__ f32x4 mma_bsplit(const Op<float>& op, const bf16x8& b
   acc = mfma(f.hi, blo, acc);
   return mfma(f.lo, bhi, acc);
 }
-// acc += op * b for the output terms: bf16 operands use the hi part of b only;
-// fp32 operands keep full precision.
-__device__ __forceinline__ f32x4 mma_out(const Op<bf16_t>& op, const bf16x8& bhi, const bf16x8&, f32x4 acc) {
-  return mfma(op.v, bhi, acc);
+// acc += (ahi [+ alo]) * op for the output terms: bf16 operands use the hi
+// part of the LDS operand only, fp32 operands keep full precision.
+__device__ __forceinline__ f32x4 mma_out_t(const bf16x8& ahi, const bf16x8&, const Op<bf16_t>& op, f32x4 acc) {
+  return mfma(ahi, op.v, acc);
 }
-__device__ __forceinline__ f32x4 mma_out(const Op<float>& op, const bf16x8& bhi, const bf16x8& blo, f32x4 acc) {
-  return mma_bsplit(op, bhi, blo, acc);
+__device__ __forceinline__ f32x4 mma_out_t(const bf16x8& ahi, const bf16x8& alo, const Op<float>& op, f32x4 acc) {
+  Frag f = op.split();
+  acc = mfma(ahi, f.hi, acc);
+  acc = mfma(alo, f.hi, acc);
+  return mfma(ahi, f.lo, acc);
 }
+// Store 4 consecutive values.
+__device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-// Per-chunk operands of a state wave (v_new and the state update).
 template <int KD, int BV, typename ST>
 struct StateFrags {
   static constexpr int NKS = KD / 32, RT = KD / 64, CT = BV / 16;
@@ -175,7 +182,9 @@ __global__ __launch_bounds__(SUM ? 256 : 512) void scan_kernel(ScanArgs a) {
         }
 
     auto step = [&](const SF& cur, SF& nxt, int c) __attribute__((always_inline)) {
-      if (c + 1 < nck) load(nxt, c + 1);
+      // Unconditional prefetch (the last chunk reloads itself) so that the
+      // compiler's wait counters stay exact across the loop back-edge.
+      load(nxt, min(c + 1, nck - 1));
       // h^T as a bf16 hi/lo operand
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
@@ -289,13 +298,17 @@ __global__ __launch_bounds__(SUM ? 256 : 512) void scan_kernel(ScanArgs a) {
       for (int ks = 0; ks < NKS; ++ks) f.q[ks].load(q + 32 * ks);
       const ST* aq = static_cast<const ST*>(a.Aqk) + ch * (64 * 64) + (16 * rw + r16) * 64 + 8 * quad;
       f.aq[0].load(aq);
-      if (rw >= 2) f.aq[1].load(aq + 32);
+      f.aq[1].load(aq + 32);
     };
     ST* op = static_cast<ST*>(a.o);
     auto step = [&](const OF& cur, OF& nxt, int c) __attribute__((always_inline)) {
-      if (c + 1 < nck) load(nxt, c + 1);
+      // Unconditional prefetch (the last chunk reloads itself) so that the
+      // compiler's wait counters stay exact across the loop back-edge.
+      load(nxt, min(c + 1, nck - 1));
       __syncthreads();
-      // o = qg h (needs only h^T, overlaps the state waves' v_new)
+      // o^T = h^T qg^T (needs only h^T; overlaps the state waves' v_new).  The
+      // transposed tile gives each lane 4 consecutive value columns of one
+      // token, stored as one 8-byte (bf16) or 16-byte (fp32) write.
       f32x4 acc[CT];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -303,28 +316,24 @@ __global__ __launch_bounds__(SUM ? 256 : 512) void scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const int off = (16 * ct + r16) * PH + 32 * ks + 8 * quad;
-          acc[ct] = mma_out(cur.q[ks], load_bf16x8(sHhi + off), load_bf16x8(sHlo + off), acc[ct]);
+          acc[ct] = mma_out_t(load_bf16x8(sHhi + off), load_bf16x8(sHlo + off), cur.q[ks], acc[ct]);
         }
       }
       __syncthreads();
-      // o += tril(Aqk) v_new
-      const int Cn = min(BT, len - c * BT);
-      const int64_t tokc = tok0s + (int64_t)c * BT;
+      // o^T += v_new^T tril(Aqk)^T
+      const int t = 16 * rw + r16;                       // this lane's token
+      const bool tok_ok = t < min(BT, len - c * BT);
+      ST* orow = op + (tok0s + (int64_t)c * BT + t) * (int64_t)(a.Hv * VD) + (int64_t)h * VD + v0 + 4 * quad;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (ks * 2 <= rw) {     // Aqk is lower triangular
             const int off = (16 * ct + r16) * PV + 32 * ks + 8 * quad;
-            acc[ct] = mma_out(cur.aq[ks], load_bf16x8(sVhi + off), load_bf16x8(sVlo + off), acc[ct]);
+            acc[ct] = mma_out_t(load_bf16x8(sVhi + off), load_bf16x8(sVlo + off), cur.aq[ks], acc[ct]);
           }
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * rw + 4 * quad + e;
-          if (t < Cn)
-            op[(tokc + t) * (int64_t)(a.Hv * VD) + (int64_t)h * VD + v0 + 16 * ct + r16] = from_f<ST>(acc[ct][e]);
-        }
+        if (tok_ok) store4(orow + 16 * ct, acc[ct]);
       }
     };
     OF fa, fb;
