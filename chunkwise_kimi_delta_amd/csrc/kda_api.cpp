@@ -48,7 +48,7 @@ struct Plan {
   int N = 0;
   size_t es = 0;          // element size of token tensors
   // workspace offsets
-  size_t off_chunk = 0, off_w = 0, off_u = 0, off_kg = 0, off_qg = 0, off_aqk = 0, off_gd = 0;
+  size_t off_chunk = 0, off_rec = 0;
   size_t bytes = 0;
 };
 
@@ -106,20 +106,13 @@ kda_status_t plan_problem(const kda_problem_t* p, bool forward, Plan& pl) {
   }
   if (pl.nchunks > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many chunks (%lld)", (long long)pl.nchunks);
   const int VA = forward ? p->V : p->V + p->K;
-  if ((int64_t)(VA / 32) * p->Hv * pl.N > 0x7fffffffLL)
+  if ((int64_t)(VA / 16) * p->Hv * pl.N > 0x7fffffffLL)
     return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head, tile) workgroups");
 
   const size_t slots = (size_t)p->Hv * (size_t)pl.nchunks;
   size_t off = 0;
   pl.off_chunk = off;  off = align256(off + sizeof(int32_t) * (size_t)(pl.N + 1));
-  pl.off_w = off;      off = align256(off + slots * kBT * p->K * pl.es);
-  pl.off_u = off;      off = align256(off + slots * kBT * p->V * sizeof(float));
-  pl.off_kg = off;     off = align256(off + slots * kBT * p->K * sizeof(float));
-  if (forward) {
-    pl.off_qg = off;   off = align256(off + slots * kBT * p->K * pl.es);
-    pl.off_aqk = off;  off = align256(off + slots * kBT * kBT * pl.es);
-  }
-  pl.off_gd = off;     off = align256(off + slots * p->K * sizeof(float));
+  pl.off_rec = off;    off += slots * kda::rec_layout(p->K, p->V, (int)pl.es, forward).bytes;
   pl.bytes = off;
   return KDA_OK;
 }
@@ -161,10 +154,7 @@ kda_status_t run_intra(const kda_problem_t* p, const Plan& pl, const kda::SeqInf
   a.A_log = A_log; a.dt_bias = dt_bias;
   a.Hk = p->Hk; a.Hv = p->Hv; a.nchunks = (int)pl.nchunks;
   a.flags = p->flags; a.scale = p->scale; a.eps = p->eps; a.lower_bound = p->lower_bound;
-  a.w = ws + pl.off_w; a.u = ws + pl.off_u; a.kgT = ws + pl.off_kg;
-  a.qg = q ? ws + pl.off_qg : nullptr;
-  a.Aqk = q ? ws + pl.off_aqk : nullptr;
-  a.gdec = reinterpret_cast<float*>(ws + pl.off_gd);
+  a.ws = reinterpret_cast<unsigned char*>(ws + pl.off_rec);
   return hip_status(kda::launch_intra(p->K, p->V, p->dtype, a, s), "intra-chunk kernel launch");
 }
 
@@ -277,9 +267,7 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
   kda::ScanArgs a{};
   a.seq = si;
   a.Hv = p->Hv; a.nchunks = (int)pl.nchunks; a.state_rows = p->state_rows; a.summary = 0;
-  a.w = ws + pl.off_w; a.u = ws + pl.off_u; a.kgT = ws + pl.off_kg;
-  a.qg = ws + pl.off_qg; a.Aqk = ws + pl.off_aqk;
-  a.gdec = reinterpret_cast<const float*>(ws + pl.off_gd);
+  a.ws = reinterpret_cast<const unsigned char*>(ws + pl.off_rec);
   a.h0 = initial_state; a.state_idx = state_indices; a.hT = final_state; a.M = nullptr; a.o = o;
   if ((st = hip_status(kda::launch_scan(p->K, p->V, p->dtype, a, s), "state-scan kernel launch")) != KDA_OK)
     return st;
@@ -314,8 +302,7 @@ kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const vo
   kda::ScanArgs a{};
   a.seq = si;
   a.Hv = p->Hv; a.nchunks = (int)pl.nchunks; a.state_rows = 0; a.summary = 1;
-  a.w = ws + pl.off_w; a.u = ws + pl.off_u; a.kgT = ws + pl.off_kg;
-  a.gdec = reinterpret_cast<const float*>(ws + pl.off_gd);
+  a.ws = reinterpret_cast<const unsigned char*>(ws + pl.off_rec);
   a.hT = S_tilde; a.M = M;
   if ((st = hip_status(kda::launch_scan(p->K, p->V, p->dtype, a, s), "summary scan kernel launch")) != KDA_OK)
     return st;

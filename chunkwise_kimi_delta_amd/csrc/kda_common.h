@@ -42,19 +42,36 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
-// Eight values -> bf16 fragment (hi) and the rounding remainder (lo), so that
-// hi + lo carries ~16 significant bits of each fp32 value.
+// fp32 -> bf16 hi/lo pairs: hi = RNE(x), lo = RNE(x - hi), so that hi + lo
+// carries ~16 significant bits of x (x - hi is exact in fp32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const bf16x2_t h = {(__bf16)a, (__bf16)b};
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  const bf16x2_t l = {(__bf16)(a - __uint_as_float(hb << 16)), (__bf16)(b - __uint_as_float(hb & 0xffff0000u))};
+  hi = hb;
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// Eight values -> bf16 fragment (hi) and the rounding remainder (lo).
 struct Frag { bf16x8 hi, lo; };
 
 __device__ __forceinline__ Frag split8(const float (&x)[8]) {
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split2(x[0], x[1], h0, l0);
+  split2(x[2], x[3], h1, l1);
+  split2(x[4], x[5], h2, l2);
+  split2(x[6], x[7], h3, l3);
   Frag f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __bf16 h = (__bf16)x[i];
-    f.hi[i] = h;
-    f.lo[i] = (__bf16)(x[i] - (float)h);
-  }
+  f.hi = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
+  f.lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
   return f;
+}
+// Two accumulator tiles (rows 4g..4g+3 and 16+4g..16+4g+3 of a 32-row block)
+// as one hi/lo operand fragment.
+__device__ __forceinline__ Frag split_pair(const f32x4& x, const f32x4& y) {
+  const float v[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return split8(v);
 }
 __device__ __forceinline__ bf16x8 round8(const float (&x)[8]) {
   bf16x8 r;
@@ -95,6 +112,20 @@ __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
 }
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Raw buffer loads: a resource descriptor for a byte range (base in SGPRs,
+// bounds checked by the hardware: reads past num_bytes return zeros) and a
+// 32-bit per-lane byte offset, so that per-lane addresses are computed once.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)num_bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
 // acc += A * B where the operands are stored as T (bf16: exact single pass;

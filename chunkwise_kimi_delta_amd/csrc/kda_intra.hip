@@ -117,6 +117,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   const int C = min(BT, len - cidx * BT);
   const int hk = h / (a.Hv / a.Hk);
   const int64_t ch = (int64_t)h * a.nchunks + gc;      // head-major chunk slot
+  const RecLayout RL = rec_layout(KD, VD, (int)sizeof(IT), a.q != nullptr);
+  unsigned char* rec = a.ws + ch * RL.bytes;
   const bool has_q = a.q != nullptr;
   const int i = 16 * wave + r16;                       // this lane's token row
   const bool live = i < C;
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
       float d[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) d[e] = fexp2(gC[ks][e]);
-      store8(a.gdec + ch * KD + c0, d);
+      store8(reinterpret_cast<float*>(rec + RL.gd) + c0, d);
     }
   }
   // normalised rows
@@ -252,26 +254,36 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     if (wave == 0) put_col(sRef[0], b32ahi, b32alo, i);
     if (wave == 2) put_col(sRef[2], b32bhi, b32blo, i - 32);
     if (has_q) {
-      ST* qg = static_cast<ST*>(a.qg) + ch * (BT * KD) + i * KD;
+      ST* qg = reinterpret_cast<ST*>(rec + RL.qg);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        float x[8];
+        f32x4 x0, x1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = a.scale * qx[ks][e] * fexp2(gl[ks][e]);
-        store8(qg + 32 * ks + 8 * quad, x);
+        for (int e = 0; e < 4; ++e) {
+          x0[e] = a.scale * qx[ks][e] * fexp2(gl[ks][e]);
+          x1[e] = a.scale * qx[ks][e + 4] * fexp2(gl[ks][e + 4]);
+        }
+        store4(qg + frag_off(i, 32 * ks + 8 * quad, NKS), x0);
+        store4(qg + frag_off(i, 32 * ks + 8 * quad + 4, NKS), x1);
       }
     }
-    float* kgT = static_cast<float*>(a.kgT) + ch * (KD * BT);
+    bf16_t* kgh = reinterpret_cast<bf16_t*>(rec + RL.kgh);
+    bf16_t* kgl = reinterpret_cast<bf16_t*>(rec + RL.kgl);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        kgT[(32 * ks + 8 * quad + e) * BT + i] = kx[ks][e] * fexp2(gC[ks][e] - gl[ks][e]);
+      for (int e = 0; e < 8; ++e) {
+        const float x = kx[ks][e] * fexp2(gC[ks][e] - gl[ks][e]);
+        const bf16_t hb = f2bf(x);
+        const int off = frag_off(32 * ks + 8 * quad + e, i, 2);
+        kgh[off] = hb;
+        kgl[off] = f2bf(x - bf2f(hb));
+      }
   }
   __syncthreads();
 
   // ---- Akk (L) and Aqk tiles on the matrix cores
-  ST* Aqk_out = static_cast<ST*>(a.Aqk) + ch * (BT * BT);
+  ST* Aqk_out = reinterpret_cast<ST*>(rec + RL.aqk);
   {
     // diagonal tile of this wave: levels L = 2 << b for b = 0..3 (blocks of 2, 4, 8, 16 rows)
     f32x4 dk[4], dq[4];
@@ -324,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         vq4[e] = vq;
       }
       *reinterpret_cast<f32x4*>(&sL[i * P64 + 16 * wave + 4 * quad]) = vk4;
-      if (has_q) store4(Aqk_out + i * BT + 16 * wave + 4 * quad, vq4);
+      if (has_q) store4(Aqk_out + frag_off(i, 16 * wave + 4 * quad, 2), vq4);
     }
     // off-diagonal tiles: row operand from this wave's rows, column operand from LDS
     auto off_tile = [&](const float* gref, int J, const bf16_t* bhi, const bf16_t* blo, int brow0)
@@ -357,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         vq4[e] = a.scale * aqk[e];
       }
       *reinterpret_cast<f32x4*>(&sL[i * P64 + 16 * J + 4 * quad]) = vk4;
-      if (has_q) store4(Aqk_out + i * BT + 16 * J + 4 * quad, vq4);
+      if (has_q) store4(Aqk_out + frag_off(i, 16 * J + 4 * quad, 2), vq4);
     };
     if (wave == 1) off_tile(sRef[0], 0, b32ahi, b32alo, 0);
     if (wave >= 2) {
@@ -366,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     }
     if (wave == 3) off_tile(sRef[2], 2, b32bhi, b32blo, 0);
     if (has_q) {  // upper-triangle tiles of this row tile are zero
-      for (int J = wave + 1; J < 4; ++J) store4(Aqk_out + i * BT + 16 * J + 4 * quad, zero4());
+      for (int J = wave + 1; J < 4; ++J) store4(Aqk_out + frag_off(i, 16 * J + 4 * quad, 2), zero4());
     }
   }
   __syncthreads();
@@ -469,14 +481,14 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
       }
       return acc;
     };
-    float* uT = static_cast<float*>(a.u) + ch * (VD * BT);
+    float* uT = reinterpret_cast<float*>(rec + RL.ut);
     for (int ct = 0; ct < VD / 16; ++ct) {
       f32x4 acc = tile(sVT, ct);
-      *reinterpret_cast<f32x4*>(uT + (16 * ct + r16) * BT + 16 * I + 4 * quad) = acc;
+      *reinterpret_cast<f32x4*>(uT + cfrag_off(16 * I + 4 * quad, 16 * ct + r16, VD / 16)) = acc;
     }
     // w^T tiles (X^T rows as the A operand): this lane holds token 16*I + r16,
     // channels 16*ct + 4*quad .. +3 -> one vector store
-    ST* wrow = static_cast<ST*>(a.w) + ch * (BT * KD) + (16 * I + r16) * KD + 4 * quad;
+    ST* wbase = reinterpret_cast<ST*>(rec + RL.w);
     for (int ct = 0; ct < KD / 16; ++ct) {
       f32x4 acc = zero4();
 #pragma unroll
@@ -494,7 +506,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
           }
         }
       }
-      store4(wrow + 16 * ct, acc);
+      store4(wbase + frag_off(16 * I + r16, 16 * ct + 4 * quad, NKS), acc);
     }
   }
 }

@@ -10,6 +10,54 @@ namespace kda {
 
 enum : uint32_t { F_GATE = 1u, F_SAFE = 2u, F_L2 = 4u, F_SIGMOID = 8u };
 
+// Per-(value head, chunk) workspace record written by the chunk-local kernel
+// and read by the state scan.  Sections are 256-byte aligned; a record is one
+// contiguous span so that a whole chunk can be prefetched as a byte range.
+// Matrices are stored as matrix-core fragments in lane order, so that every
+// operand load of the scan is one contiguous 1 KiB (2 KiB for fp32) block:
+//   w   [64][K]  token dtype   operand fragments, rows = tokens, reduction = channels
+//   kgh [K][64]  bf16          hi part of kg^T, rows = channels, reduction = tokens
+//   kgl [K][64]  bf16          lo part (kg^T - hi rounded to bf16)
+//   qg  [64][K]  token dtype   scale * q * 2^gamma, like w (forward only)
+//   aqk [64][64] token dtype   tril(Aqk), rows = tokens, reduction = tokens (forward only)
+//   gd  [K]      fp32          2^gamma_C, the chunk decay (plain vector)
+//   ut  [64][V]  fp32          u as accumulator tiles (16 x 16, four values per lane)
+// Inside an operand fragment the reduction index is permuted by sigma: within
+// each aligned block of 32, index x sits in slot sig32(x), so that reduction
+// slot 8*g + i (g = lane / 16, i = 0..7) holds index 4*g + i for i < 4 and
+// 16 + 4*g + (i - 4) for i >= 4 -- the rows of two stacked accumulator tiles
+// as one lane holds them.
+struct RecLayout {
+  size_t w, kgh, kgl, qg, aqk, gd, ut, bytes;
+};
+__host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+__host__ __device__ constexpr RecLayout rec_layout(int K, int V, int es, bool fwd) {
+  RecLayout r{};
+  r.w = 0;
+  r.kgh = al256(r.w + (size_t)64 * K * es);
+  r.kgl = al256(r.kgh + (size_t)K * 64 * 2);
+  r.qg = al256(r.kgl + (size_t)K * 64 * 2);
+  r.aqk = al256(r.qg + (fwd ? (size_t)64 * K * es : 0));
+  r.gd = al256(r.aqk + (fwd ? (size_t)64 * 64 * es : 0));
+  r.ut = al256(r.gd + (size_t)K * 4);
+  r.bytes = al256(r.ut + (size_t)V * 64 * 4);
+  return r;
+}
+__host__ __device__ constexpr int sig32(int x) { return 8 * ((x & 15) >> 2) + 4 * (x >> 4) + (x & 3); }
+// Element offset of (row, red) in a matrix stored as 16 x 32 operand fragments
+// (nrb fragments along the reduction index): 512 elements per fragment, eight
+// per lane, lane = row % 16 + 16 * (slot / 8).
+__host__ __device__ constexpr int frag_off(int row, int red, int nrb) {
+  return (((row >> 4) * nrb + (red >> 5)) << 9) + (((row & 15) + 16 * (sig32(red & 31) >> 3)) << 3) +
+         (sig32(red & 31) & 7);
+}
+// Element offset of (row, col) in a matrix stored as 16 x 16 accumulator tiles
+// (ncb tiles along col): 256 elements per tile, lane = col % 16 + 16 * (row % 16 / 4),
+// four consecutive rows per lane.
+__host__ __device__ constexpr int cfrag_off(int row, int col, int ncb) {
+  return (((row >> 4) * ncb + (col >> 4)) << 8) + (((col & 15) + 16 * ((row & 15) >> 2)) << 2) + (row & 3);
+}
+
 // Chunk-local ("intra") kernel: gate + cumsum, L2Norm, beta, Akk/Aqk,
 // (I+L)^-1, WY factors.  One workgroup per (chunk, value head).
 struct IntraArgs {
@@ -19,17 +67,15 @@ struct IntraArgs {
   int Hk, Hv, nchunks;
   uint32_t flags;
   float scale, eps, lower_bound;
-  // outputs, head-major [Hv][nchunks][...]; element type = token dtype
-  void *w, *u, *kgT, *qg, *Aqk;       // qg/Aqk unused when q is null
-  float* gdec;                        // [Hv][nchunks][K]  2^(chunk log2 decay)
+  unsigned char* ws;                  // records, [Hv][nchunks]
 };
 
-// Inter-chunk state scan + output.  One workgroup per (dv tile, head, sequence).
+// Inter-chunk state scan + output.  One workgroup per (16-column value tile,
+// head, sequence).
 struct ScanArgs {
   SeqInfo seq;
   int Hv, nchunks, state_rows, summary;
-  const void *w, *u, *kgT, *qg, *Aqk;
-  const float* gdec;
+  const unsigned char* ws;            // records, [Hv][nchunks]
   const float* h0;                    // [N,Hv,K,V] | cache | null
   const int32_t* state_idx;           // cache mode
   float* hT;                          // final [N,Hv,K,V] | cache | null ; summary: S~

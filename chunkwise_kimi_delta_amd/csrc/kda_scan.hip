@@ -1,25 +1,31 @@
-// Inter-chunk KDA state scan with the fused chunk output, one workgroup
-// (4 waves) per (value tile of BV columns, value head, sequence).
+// Inter-chunk KDA state scan with the fused chunk output.  One workgroup per
+// (16-column value tile, value head, sequence).
 //
 // Follows "KDA Chunk Backward — TPU/Pallas Kernel Design", sections 1 and 1.2
 // (the forward output, v_new = u - w h, the inter-chunk recurrence) and the
 // state / finalize stages of "Hyper-Parallel Chunk KDA" section 5.1.  For
-// each chunk in order, with h the K x BV state tile at the chunk entry:
+// each chunk in order, with h the K x 16 state tile at the chunk entry:
 //   v_new = u - w h
 //   o     = qg h + tril(Aqk) v_new               (forward mode only)
 //   h     = Diag(gdec) h + kg^T v_new
-// The state stays in the matrix-core accumulators (fp32) for the whole
-// sequence.  It is rounded to a bf16 hi/lo pair as an operand, and u, kg^T and
-// v_new enter the state update as fp32 (hi/lo pairs), so each state-feeding
-// product carries ~16 significant bits.  Every per-chunk operand is read from
-// the workspace straight into registers in the matrix-core layout, one chunk
-// ahead of its use; only h^T and v_new^T, which the workgroup produces itself,
-// pass through LDS.
 //
-// Each workgroup has 4 state waves, which carry the recurrence, and in forward
-// mode 4 output waves, which form o from the same h^T and v_new^T off the
-// critical path.  Two workgroup barriers per chunk order the roles: h^T is
-// published before the first, v_new^T before the second.
+// Work split.  K/32 state waves each own 32 rows of the state (fp32, in
+// matrix-core accumulators for the whole sequence).  Per chunk:
+//   1. each state wave forms its 32-row share of w h straight from its
+//      accumulators (two stacked accumulator tiles are one reduction slice of
+//      the next product; the workspace stores w, kg^T, qg and Aqk with the
+//      matching index permutation) and leaves it in LDS;       -- barrier A
+//   2. each state wave sums the shares of its own token tile(s), subtracts
+//      from u and leaves v_new as a bf16 hi/lo fragment in LDS; -- barrier B
+//   3. every state wave updates its rows with the whole v_new, while two
+//      output waves form o from the same h and v_new fragments.
+// The output waves run their loads two chunks ahead and touch the workspace
+// four chunks ahead, so the state waves' own loads (one chunk ahead) are
+// served from L2.
+//
+// Precision.  h and v_new enter the state products as bf16 hi/lo pairs and
+// kg^T comes in hi/lo from the workspace, so each state-feeding product
+// carries ~16 significant bits; the bf16 output uses the hi parts only.
 //
 // Summary mode scans the augmented state [S~ | M] (K x (V + K)) from [0 | I]
 // with u = [u | 0] and writes S~ and M ("KDA Context Parallelism (KCP)",
@@ -35,13 +41,13 @@ namespace {
 template <typename ST> struct Op;
 template <> struct Op<bf16_t> {
   bf16x8 v;
-  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = __builtin_bit_cast(bf16x8, buf_load16(r, off)); }
 };
 template <> struct Op<float> {
   f32x4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const f32x4*>(p);
-    b = *reinterpret_cast<const f32x4*>(p + 4);
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
+    a = __builtin_bit_cast(f32x4, buf_load16(r, off));
+    b = __builtin_bit_cast(f32x4, buf_load16(r, off + 16));
   }
   __device__ __forceinline__ Frag split() const {
     float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -49,69 +55,65 @@ template <> struct Op<float> {
   }
 };
 
-// acc += op * (bhi + blo)
-__device__ __forceinline__ f32x4 mma_bsplit(const Op<bf16_t>& op, const bf16x8& bhi, const bf16x8& blo,
-                                            f32x4 acc) {
-  acc = mfma(op.v, bhi, acc);
-  return mfma(op.v, blo, acc);
+// acc += A * (B.hi + B.lo) with A stored in the workspace
+__device__ __forceinline__ f32x4 mma_sb(const Op<bf16_t>& A, const Frag& B, f32x4 acc) {
+  acc = mfma(A.v, B.hi, acc);
+  return mfma(A.v, B.lo, acc);
 }
-__device__ __forceinline__ f32x4 mma_bsplit(const Op<float>& op, const bf16x8& bhi, const bf16x8& blo,
-                                            f32x4 acc) {
-  Frag f = op.split();
-  acc = mfma(f.hi, bhi, acc);
-  acc = mfma(f.hi, blo, acc);
-  return mfma(f.lo, bhi, acc);
+__device__ __forceinline__ f32x4 mma_sb(const Op<float>& A, const Frag& B, f32x4 acc) {
+  const Frag f = A.split();
+  acc = mfma(f.hi, B.hi, acc);
+  acc = mfma(f.lo, B.hi, acc);
+  return mfma(f.hi, B.lo, acc);
 }
-// acc += (ahi [+ alo]) * op for the output terms: bf16 operands use the hi
-// part of the LDS operand only, fp32 operands keep full precision.
-__device__ __forceinline__ f32x4 mma_out_t(const bf16x8& ahi, const bf16x8&, const Op<bf16_t>& op, f32x4 acc) {
-  return mfma(ahi, op.v, acc);
+// Output products, A from LDS (hi [, lo]) and B stored: bf16 tokens use the
+// hi part only, fp32 tokens keep ~16 bits on both sides.
+__device__ __forceinline__ f32x4 mma_out(const bf16x8& ahi, const bf16x8&, const Op<bf16_t>& B, f32x4 acc) {
+  return mfma(ahi, B.v, acc);
 }
-__device__ __forceinline__ f32x4 mma_out_t(const bf16x8& ahi, const bf16x8& alo, const Op<float>& op, f32x4 acc) {
-  Frag f = op.split();
+__device__ __forceinline__ f32x4 mma_out(const bf16x8& ahi, const bf16x8& alo, const Op<float>& B, f32x4 acc) {
+  const Frag f = B.split();
   acc = mfma(ahi, f.hi, acc);
   acc = mfma(alo, f.hi, acc);
   return mfma(ahi, f.lo, acc);
 }
-// Store 4 consecutive values.
+
 __device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-template <int KD, int BV, typename ST>
-struct StateFrags {
-  static constexpr int NKS = KD / 32, RT = KD / 64, CT = BV / 16;
-  Op<ST> w[NKS];          // w rows 16*sw + r16, channels 32*ks + 8*quad
-  Op<float> kg[RT][2];    // kg^T rows 16*(RT*sw + rt) + r16, tokens 32*ks + 8*quad
-  f32x4 u[CT];            // u^T row (value column) v0 + 16*ct + r16, tokens 16*sw + 4*quad .. +3
-  f32x4 gd[RT];           // gdec for channels 16*(RT*sw + rt) + 4*quad .. +3
-};
-// Per-chunk operands of an output wave.
-template <int KD, typename ST>
-struct OutFrags {
-  static constexpr int NKS = KD / 32;
-  Op<ST> q[NKS];          // qg rows 16*ow + r16, channels 32*ks + 8*quad
-  Op<ST> aq[2];           // Aqk rows 16*ow + r16, tokens 32*ks + 8*quad
-};
+// Half of a v_new fragment: one accumulator tile (4 values per lane) as bf16
+// hi (x, y) and lo (z, w).
+__device__ __forceinline__ u32x4 half_frag(const f32x4& v) {
+  uint32_t h0, l0, h1, l1;
+  split2(v[0], v[1], h0, l0);
+  split2(v[2], v[3], h1, l1);
+  return u32x4{h0, h1, l0, l1};
+}
+__device__ __forceinline__ Frag join_halves(const u32x4& a, const u32x4& b) {
+  Frag f;
+  f.hi = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+  f.lo = __builtin_bit_cast(bf16x8, u32x4{a.z, a.w, b.z, b.w});
+  return f;
+}
 
-// Workgroup: 4 state waves (v_new and the state update: the recurrence's
-// critical path) and, in forward mode, 4 output waves that compute o from the
-// same h^T and v_new^T while the state waves move on.
-template <int KD, int VD, int BV, typename ST, bool SUM>
-__global__ __launch_bounds__(SUM ? 256 : 512) void scan_kernel(ScanArgs a) {
-  using SF = StateFrags<KD, BV, ST>;
-  using OF = OutFrags<KD, ST>;
-  constexpr int NKS = SF::NKS, RT = SF::RT, CT = SF::CT;
-  constexpr int PH = KD + 8;           // h^T rows (bf16)
-  constexpr int PV = 64 + 8;           // v_new^T rows (bf16)
+template <int KD, int VD, typename ST, bool SUM, int CT>
+__global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanArgs a) {
+  constexpr RecLayout L = rec_layout(KD, VD, (int)sizeof(ST), !SUM);
+  constexpr bool F32 = sizeof(ST) == 4;
+  constexpr int ES = (int)sizeof(ST);
+  constexpr int NS = KD / 32;         // state waves, 32 state rows each
+  constexpr int TPW = 4 / NS;         // token tiles each state wave reduces
+  constexpr int BV = 16 * CT;         // state columns per workgroup
   constexpr int VA = SUM ? VD + KD : VD;
   constexpr int NTILE = VA / BV;
+  static_assert(VD % BV == 0, "a workgroup's columns lie in one of S~ and M");
 
-  __shared__ __attribute__((aligned(16))) bf16_t sHhi[BV * PH];
-  __shared__ __attribute__((aligned(16))) bf16_t sHlo[BV * PH];
-  __shared__ __attribute__((aligned(16))) bf16_t sVhi[BV * PV];
-  __shared__ __attribute__((aligned(16))) bf16_t sVlo[BV * PV];
+  __shared__ f32x4 sP[NS][4][CT][64];                       // per-wave shares of w h
+  __shared__ u32x4 sV[2][4][CT][64];                        // v_new half fragments, by chunk parity
+  __shared__ bf16x8 sHh[SUM ? 1 : 2][NS][CT][64];           // h fragments (hi) for the output
+  __shared__ bf16x8 sHl[(F32 && !SUM) ? 2 : 1][NS][CT][64]; // h fragments (lo), fp32 tokens
 
   // ---- block -> (tile, head, sequence); tiles of one (head, sequence) share an XCD
   int lid = blockIdx.x;
@@ -122,7 +124,6 @@ __global__ __launch_bounds__(SUM ? 256 : 512) void scan_kernel(ScanArgs a) {
   const int n = lid / (NTILE * a.Hv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, quad = lane >> 4;
-  const int rw = wave & 3;                              // wave index within its role
 
   int64_t tok0s;
   int len;
@@ -131,30 +132,50 @@ __global__ __launch_bounds__(SUM ? 256 : 512) void scan_kernel(ScanArgs a) {
   const int cb = chunk_base(a.seq, n);
   const bool mtile = SUM && tv * BV >= VD;              // columns of M
   const int v0 = mtile ? tv * BV - VD : tv * BV;        // first column inside S~ or M
+  const unsigned char* recs = a.ws + ((size_t)h * a.nchunks + cb) * L.bytes;
 
-  if (wave < 4) {
+  if (wave < NS) {
     // =========================== state waves ===========================
-    auto load = [&](SF& f, int c) __attribute__((always_inline)) {
-      const int64_t ch = (int64_t)h * a.nchunks + cb + c;
-      const ST* w = static_cast<const ST*>(a.w) + ch * (64 * KD) + (16 * rw + r16) * KD + 8 * quad;
+    const int s = wave;
+    const int row0 = 32 * s;
+    struct Ops {
+      Op<ST> w[4];                    // w rows 16*tt + r16, channels row0 + (slots of lane / 16)
+      f32x4 u[TPW][CT];               // u rows 16*(TPW*s + j) + 4*quad .. +3, column v0 + 16*ct + r16
+      bf16x8 kh[2][2], kl[2][2];      // kg^T rows row0 + 16*kt + r16, tokens 32*ks + (slots)
+      f32x4 gd[2];                    // gdec rows row0 + 16*kt + 4*quad .. +3
+    };
+    // fragment (tt, K-block s) of w; fragments (2s + kt, ks) of kg^T; u tiles
+    // (TPW*s + j, v0/16 + ct).  M columns (summary mode) see u = 0: their
+    // offset lies past the record, where the buffer load returns zeros.
+    constexpr uint32_t FW = 512 * ES;                     // bytes per operand fragment
+    const uint32_t o_w = L.w + (uint32_t)(s * 512 + lane * 8) * ES;
+    const uint32_t o_u = mtile ? (uint32_t)L.bytes
+                               : L.ut + (uint32_t)((TPW * s * (VD / 16) + v0 / 16) * 256 + lane * 4) * 4;
+    const uint32_t o_kg = (uint32_t)(2 * s * 2 * 512 + lane * 8) * 2;
+    const uint32_t o_gd = L.gd + (uint32_t)(row0 + 4 * quad) * 4;
+    auto load = [&](Ops& f, int c) __attribute__((always_inline)) {
+      const rsrc_t r = make_rsrc(recs + (size_t)c * L.bytes, (uint32_t)L.bytes);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) f.w[ks].load(w + 32 * ks);
-      const float* kg = static_cast<const float*>(a.kgT) + ch * (KD * 64) + 8 * quad;
+      for (int tt = 0; tt < 4; ++tt) f.w[tt].load(r, o_w + FW * NS * tt);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int j = 0; j < TPW; ++j)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) f.kg[rt][ks].load(kg + (16 * (RT * rw + rt) + r16) * 64 + 32 * ks);
-      const float* u = static_cast<const float*>(a.u) + ch * (VD * 64) + 16 * rw + 4 * quad;
+        for (int ct = 0; ct < CT; ++ct)
+          f.u[j][ct] = __builtin_bit_cast(f32x4, buf_load16(r, o_u + (mtile ? 0 : 1024 * ((VD / 16) * j + ct))));
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        f.u[ct] = mtile ? zero4() : *reinterpret_cast<const f32x4*>(u + (v0 + 16 * ct + r16) * 64);
-      const float* gd = a.gdec + ch * KD + 4 * quad;
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) f.gd[rt] = *reinterpret_cast<const f32x4*>(gd + 16 * (RT * rw + rt));
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint32_t off = o_kg + 1024 * (2 * kt + ks);
+          f.kh[kt][ks] = __builtin_bit_cast(bf16x8, buf_load16(r, L.kgh + off));
+          f.kl[kt][ks] = __builtin_bit_cast(bf16x8, buf_load16(r, L.kgl + off));
+        }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) f.gd[kt] = __builtin_bit_cast(f32x4, buf_load16(r, o_gd + 64 * kt));
     };
 
-    // state tile in accumulators: rows 16*(RT*rw+rt) + 4*quad + e, col 16*ct + r16
-    f32x4 hs[RT][CT];
+    // state rows row0 + 16*kt + 4*quad + e, column v0 + 16*ct + r16
+    f32x4 hs[2][CT];
     const float* h0p = nullptr;
     bool valid_row = true;
     int64_t srow = n;
@@ -169,100 +190,86 @@ __global__ __launch_bounds__(SUM ? 256 : 512) void scan_kernel(ScanArgs a) {
       }
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = 16 * (RT * rw + rt) + 4 * quad + e, col = 16 * ct + r16;
+          const int row = row0 + 16 * kt + 4 * quad + e, col = v0 + 16 * ct + r16;
           float x = 0.f;
-          if (mtile) x = (row == v0 + col) ? 1.f : 0.f;
-          else if (h0p) x = h0p[(int64_t)row * VD + v0 + col];
-          hs[rt][ct][e] = x;
+          if (mtile) x = (row == col) ? 1.f : 0.f;
+          else if (h0p) x = h0p[(int64_t)row * VD + col];
+          hs[kt][ct][e] = x;
         }
 
-    auto step = [&](const SF& cur, SF& nxt, int c) __attribute__((always_inline)) {
+    auto step = [&](const Ops& cur, Ops& nxt, int c) __attribute__((always_inline)) {
       // Unconditional prefetch (the last chunk reloads itself) so that the
-      // compiler's wait counters stay exact across the loop back-edge.
+      // compiler's wait counters stay exact across the loop back-edge; the
+      // scheduling barrier keeps the loads at the top of the step.
       load(nxt, min(c + 1, nck - 1));
-      // h^T as a bf16 hi/lo operand
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const int row0 = 16 * (RT * rw + rt) + 4 * quad, col = 16 * ct + r16;
-          float hv[4], lv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hv[e] = hs[rt][ct][e];
-            lv[e] = hv[e] - bf2f(f2bf(hv[e]));
-          }
-          *reinterpret_cast<u32x2*>(sHhi + col * PH + row0) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-          *reinterpret_cast<u32x2*>(sHlo + col * PH + row0) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
-        }
-      __syncthreads();
-
-      // ---- v_new = u - w h   (token rows 16*rw .. +15)
-      bf16x8 bh[CT][NKS], bl[CT][NKS];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const int off = (16 * ct + r16) * PH + 32 * ks + 8 * quad;
-          bh[ct][ks] = load_bf16x8(sHhi + off);
-          bl[ct][ks] = load_bf16x8(sHlo + off);
-        }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- 1. this wave's share of w h
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) acc = mma_bsplit(cur.w[ks], bh[ct][ks], bl[ct][ks], acc);
-        const int t0 = 16 * rw + 4 * quad, col = 16 * ct + r16;
-        float vn[4], lv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vn[e] = cur.u[ct][e] - acc[e];
-          lv[e] = vn[e] - bf2f(f2bf(vn[e]));
+        const Frag hb = split_pair(hs[0][ct], hs[1][ct]);
+        if constexpr (!SUM) {
+          sHh[c & 1][s][ct][lane] = hb.hi;
+          if constexpr (F32) sHl[c & 1][s][ct][lane] = hb.lo;
         }
-        *reinterpret_cast<u32x2*>(sVhi + col * PV + t0) = u32x2{pack_bf16x2(vn[0], vn[1]), pack_bf16x2(vn[2], vn[3])};
-        *reinterpret_cast<u32x2*>(sVlo + col * PV + t0) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) sP[s][tt][ct][lane] = mma_sb(cur.w[tt], hb, zero4());
       }
-      __syncthreads();
-
-      // ---- h = Diag(gdec) h + kg^T v_new
-      bf16x8 vh[CT][2], vl[CT][2];
+      __syncthreads();                                           // A
+      // ---- 2. v_new of this wave's token tiles (shares summed in wave order)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int off = (16 * ct + r16) * PV + 32 * ks + 8 * quad;
-          vh[ct][ks] = load_bf16x8(sVhi + off);
-          vl[ct][ks] = load_bf16x8(sVlo + off);
-        }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const Frag kf[2] = {cur.kg[rt][0].split(), cur.kg[rt][1].split()};
+      for (int j = 0; j < TPW; ++j) {
+        const int tt = TPW * s + j;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          f32x4 acc = hs[rt][ct];
+          f32x4 sum = sP[0][tt][ct][lane];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] *= cur.gd[rt][e];
+          for (int w2 = 1; w2 < NS; ++w2) {
+            const f32x4 x = sP[w2][tt][ct][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum[e] += x[e];
+          }
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = cur.u[j][ct][e] - sum[e];
+          sV[c & 1][tt][ct][lane] = half_frag(v);
+        }
+      }
+      __syncthreads();                                           // B
+      // ---- 3. h = Diag(gdec) h + kg^T v_new
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        Frag vb[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          vb[ks] = join_halves(sV[c & 1][2 * ks][ct][lane], sV[c & 1][2 * ks + 1][ct][lane]);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          f32x4 acc = hs[kt][ct];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] *= cur.gd[kt][e];
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            acc = mfma(kf[ks].hi, vh[ct][ks], acc);
-            acc = mfma(kf[ks].hi, vl[ct][ks], acc);
-            acc = mfma(kf[ks].lo, vh[ct][ks], acc);
+            acc = mfma(cur.kh[kt][ks], vb[ks].hi, acc);
+            acc = mfma(cur.kl[kt][ks], vb[ks].hi, acc);
+            acc = mfma(cur.kh[kt][ks], vb[ks].lo, acc);
           }
-          hs[rt][ct] = acc;
+          hs[kt][ct] = acc;
         }
       }
     };
 
-    SF fa, fb;
-    if (nck > 0) load(fa, 0);
-    for (int c = 0; c < nck; c += 2) {
-      step(fa, fb, c);
-      if (c + 1 < nck) step(fb, fa, c + 1);
+    if (nck > 0) {
+      Ops fa, fb;
+      load(fa, 0);
+      for (int c = 0; c < nck; c += 2) {
+        step(fa, fb, c);
+        if (c + 1 < nck) step(fb, fa, c + 1);
+      }
     }
 
     // ---- final state
@@ -280,67 +287,101 @@ __global__ __launch_bounds__(SUM ? 256 : 512) void scan_kernel(ScanArgs a) {
     }
     if (dst) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int row = 16 * (RT * rw + rt) + 4 * quad + e, col = 16 * ct + r16;
-            dst[(int64_t)row * ld + v0 + col] = hs[rt][ct][e];
+            const int row = row0 + 16 * kt + 4 * quad + e;
+            dst[(int64_t)row * ld + v0 + 16 * ct + r16] = hs[kt][ct][e];
           }
     }
   } else if constexpr (!SUM) {
     // =========================== output waves ==========================
+    // first output wave: token tiles 0, 1; second: token tiles 2, 3.  Chunk
+    // c's output is formed between the state waves' barriers B(c) and A(c+1).
+    const int ow = wave - NS;
+    struct OF {
+      Op<ST> q[2][NS];    // qg rows 16*(2*ow + j) + r16, channels 32*kb + (slots of lane / 16)
+      Op<ST> aq[2][2];    // Aqk rows 16*(2*ow + j) + r16, tokens 32*ks + (slots)
+    };
+    // fragments (2*ow + j, kb) of qg and (2*ow + j, ks) of Aqk
+    constexpr uint32_t FW = 512 * ES;
+    const uint32_t o_q = L.qg + (uint32_t)(2 * ow * NS * 512 + lane * 8) * ES;
+    const uint32_t o_a = L.aqk + (uint32_t)(2 * ow * 2 * 512 + lane * 8) * ES;
     auto load = [&](OF& f, int c) __attribute__((always_inline)) {
-      const int64_t ch = (int64_t)h * a.nchunks + cb + c;
-      const ST* q = static_cast<const ST*>(a.qg) + ch * (64 * KD) + (16 * rw + r16) * KD + 8 * quad;
+      const rsrc_t r = make_rsrc(recs + (size_t)c * L.bytes, (uint32_t)L.bytes);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) f.q[ks].load(q + 32 * ks);
-      const ST* aq = static_cast<const ST*>(a.Aqk) + ch * (64 * 64) + (16 * rw + r16) * 64 + 8 * quad;
-      f.aq[0].load(aq);
-      f.aq[1].load(aq + 32);
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int kb = 0; kb < NS; ++kb) f.q[j][kb].load(r, o_q + FW * (NS * j + kb));
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) f.aq[j][ks].load(r, o_a + FW * (2 * j + ks));
+      }
+    };
+    // L2 warm-up: this tile touches its share of the 128-byte lines of the
+    // record four chunks ahead (one line per lane; the sibling tiles of the
+    // head cover the rest).  The loaded word is consumed three steps later,
+    // so the touch never makes this wave wait.
+    constexpr int NL = (int)(L.bytes / 128);
+    const int l0 = tv * NL / NTILE, l1 = (tv + 1) * NL / NTILE;
+    const int tline = l0 + ow * 64 + lane;
+    const uint32_t toff = tline < l1 ? (uint32_t)tline * 128 : (uint32_t)L.bytes;   // past the end: no access
+    auto touch = [&](int c) __attribute__((always_inline)) -> uint32_t {
+      return buf_load4(make_rsrc(recs + (size_t)min(c, nck - 1) * L.bytes, (uint32_t)L.bytes), toff);
     };
     ST* op = static_cast<ST*>(a.o);
-    auto step = [&](const OF& cur, OF& nxt, int c) __attribute__((always_inline)) {
-      // Unconditional prefetch (the last chunk reloads itself) so that the
-      // compiler's wait counters stay exact across the loop back-edge.
-      load(nxt, min(c + 1, nck - 1));
-      __syncthreads();
-      // o^T = h^T qg^T (needs only h^T; overlaps the state waves' v_new).  The
-      // transposed tile gives each lane 4 consecutive value columns of one
-      // token, stored as one 8-byte (bf16) or 16-byte (fp32) write.
-      f32x4 acc[CT];
+    // Each step loads chunk c + 2 into `ld` and forms chunk c from `use`.
+    uint32_t pf0 = touch(1), pf1 = touch(2), pf2 = touch(3);
+    auto ostep = [&](OF& ld, const OF& use, int c) __attribute__((always_inline)) {
+      load(ld, min(c + 2, nck - 1));
+      asm volatile("; prefetch sink %0" ::"v"(pf0));
+      pf0 = pf1;
+      pf1 = pf2;
+      pf2 = touch(c + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();                                           // A(c)
+      __syncthreads();                                           // B(c)
+      const int b = c & 1;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        acc[ct] = zero4();
+        bf16x8 hh[NS], hl[NS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const int off = (16 * ct + r16) * PH + 32 * ks + 8 * quad;
-          acc[ct] = mma_out_t(load_bf16x8(sHhi + off), load_bf16x8(sHlo + off), cur.q[ks], acc[ct]);
+        for (int kb = 0; kb < NS; ++kb) {
+          hh[kb] = sHh[b][kb][ct][lane];
+          if constexpr (F32) hl[kb] = sHl[b][kb][ct][lane];
+          else hl[kb] = hh[kb];
         }
-      }
-      __syncthreads();
-      // o^T += v_new^T tril(Aqk)^T
-      const int t = 16 * rw + r16;                       // this lane's token
-      const bool tok_ok = t < min(BT, len - c * BT);
-      ST* orow = op + (tok0s + (int64_t)c * BT + t) * (int64_t)(a.Hv * VD) + (int64_t)h * VD + v0 + 4 * quad;
+        Frag vf[2];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
+        for (int ks = 0; ks < 2; ++ks) vf[ks] = join_halves(sV[b][2 * ks][ct][lane], sV[b][2 * ks + 1][ct][lane]);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (ks * 2 <= rw) {     // Aqk is lower triangular
-            const int off = (16 * ct + r16) * PV + 32 * ks + 8 * quad;
-            acc[ct] = mma_out_t(load_bf16x8(sVhi + off), load_bf16x8(sVlo + off), cur.aq[ks], acc[ct]);
-          }
+        for (int j = 0; j < 2; ++j) {
+          // o^T tile: this lane holds token 16*tt + r16, columns v0 + 16*ct + 4*quad .. +3
+          const int tt = 2 * ow + j;
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < NS; ++kb) acc = mma_out(hh[kb], hl[kb], use.q[j][kb], acc);
+          // (the strictly upper blocks of Aqk are stored as zeros)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) acc = mma_out(vf[ks].hi, F32 ? vf[ks].lo : vf[ks].hi, use.aq[j][ks], acc);
+          const int t = 16 * tt + r16;
+          if (t < len - c * BT)
+            store4(op + (tok0s + (int64_t)c * BT + t) * (int64_t)(a.Hv * VD) + (int64_t)h * VD + v0 + 16 * ct + 4 * quad,
+                   acc);
         }
-        if (tok_ok) store4(orow + 16 * ct, acc[ct]);
       }
     };
-    OF fa, fb;
-    if (nck > 0) load(fa, 0);
-    for (int c = 0; c < nck; c += 2) {
-      step(fa, fb, c);
-      if (c + 1 < nck) step(fb, fa, c + 1);
+    if (nck > 0) {
+      OF f0, f1, f2;
+      load(f0, 0);
+      load(f1, min(1, nck - 1));
+      for (int c = 0; c < nck; c += 3) {
+        ostep(f2, f0, c);
+        if (c + 1 < nck) ostep(f0, f1, c + 1);
+        if (c + 2 < nck) ostep(f1, f2, c + 2);
+      }
+      asm volatile("; prefetch sink %0 %1 %2" ::"v"(pf0), "v"(pf1), "v"(pf2));
     }
   }
 }
@@ -377,26 +418,35 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
 }
 
 hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s) {
-  constexpr int BV = 32;
   if (a.seq.N == 0 || a.Hv == 0) return hipSuccess;
   const int VA = a.summary ? V + K : V;
-  const long nb = (long)(VA / BV) * a.Hv * a.seq.N;
+#ifdef KDA_SCAN_CT
+  const int CTsel = dtype == 1 ? KDA_SCAN_CT : 1;
+#else
+  const int CTsel = 1;
+#endif
+  const long nb = (long)(VA / (16 * CTsel)) * a.Hv * a.seq.N;
   if (nb > 0x7fffffffL) return hipErrorInvalidValue;
-  dim3 grid((unsigned)nb), block(a.summary ? 256 : 512);
-#define KDA_SCAN_CASE(KK, VV, TT)                                                    \
-  if (K == KK && V == VV) {                                                          \
-    if (a.summary) hipLaunchKernelGGL((scan_kernel<KK, VV, BV, TT, true>), grid, block, 0, s, a); \
-    else hipLaunchKernelGGL((scan_kernel<KK, VV, BV, TT, false>), grid, block, 0, s, a);          \
-    return hipGetLastError();                                                        \
+  // K/32 state waves, plus two output waves in forward mode
+  dim3 grid((unsigned)nb), block(K * 2 + (a.summary ? 0 : 128));
+#define KDA_SCAN_CASE(KK, VV, TT, CC)                                                             \
+  if (K == KK && V == VV && CTsel == CC) {                                                        \
+    if (a.summary) hipLaunchKernelGGL((scan_kernel<KK, VV, TT, true, CC>), grid, block, 0, s, a); \
+    else hipLaunchKernelGGL((scan_kernel<KK, VV, TT, false, CC>), grid, block, 0, s, a);          \
+    return hipGetLastError();                                                                     \
   }
   if (dtype == 1) {
-    KDA_SCAN_CASE(128, 128, bf16_t)
-    KDA_SCAN_CASE(64, 64, bf16_t)
-    KDA_SCAN_CASE(128, 64, bf16_t)
-    KDA_SCAN_CASE(64, 128, bf16_t)
+    KDA_SCAN_CASE(128, 128, bf16_t, 1)
+    KDA_SCAN_CASE(64, 64, bf16_t, 1)
+    KDA_SCAN_CASE(128, 64, bf16_t, 1)
+    KDA_SCAN_CASE(64, 128, bf16_t, 1)
+#ifdef KDA_SCAN_CT
+    KDA_SCAN_CASE(128, 128, bf16_t, 2)
+    KDA_SCAN_CASE(128, 128, bf16_t, 4)
+#endif
   } else {
-    KDA_SCAN_CASE(64, 64, float)
-    KDA_SCAN_CASE(64, 128, float)
+    KDA_SCAN_CASE(64, 64, float, 1)
+    KDA_SCAN_CASE(64, 128, float, 1)
   }
 #undef KDA_SCAN_CASE
   return hipErrorInvalidValue;

@@ -50,8 +50,9 @@ def _ws(lib, p, summary=False):
 def test_workspace_size_layer_and_monotone(lib):
     st, b = _ws(lib, _problem())
     assert st == 0
-    # w, qg, Aqk (bf16), u, kgT and the chunk decay (fp32) per (head, chunk), 256-byte aligned regions.
-    per = 64 * 128 * (2 + 4 + 4 + 2) + 64 * 64 * 2 + 128 * 4
+    # One record per (head, chunk): w, qg (bf16 64x128), kg^T hi and lo (bf16 128x64 each),
+    # Aqk (bf16 64x64), the chunk decay (fp32 128) and u^T (fp32 128x64).
+    per = 64 * 128 * 2 * 2 + 128 * 64 * 2 * 2 + 64 * 64 * 2 + 128 * 4 + 128 * 64 * 4
     assert b >= 32 * 128 * per and b < 32 * 128 * per + 8 * 256
     prev = 0
     for T in (0, 1, 64, 65, 1000, 8192):
