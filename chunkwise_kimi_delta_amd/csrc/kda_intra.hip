@@ -51,6 +51,17 @@ __device__ __forceinline__ float row_scan16(float x) {
   return x;
 }
 
+// Value of x in another lane: a DPP move with control CTRL (row_shl, quad_perm)
+// or a swizzle with bit-mode PATTERN (and/or masks within 32-lane groups).
+template <int CTRL>
+__device__ __forceinline__ float lane_from(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+template <int PATTERN>
+__device__ __forceinline__ float swizzle(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), PATTERN));
+}
+
 // 2^x and log2(x) on the transcendental unit (v_exp_f32 / v_log_f32).  Every
 // exponent used here is <= 0; results below the normal range flush towards
 // zero, where the products they scale are negligible.
@@ -90,8 +101,13 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
 
   __shared__ __attribute__((aligned(16))) float sTot[4][KD];   // per-wave gate totals
   __shared__ __attribute__((aligned(16))) float sRef[3][KD];   // gamma of rows 16, 32, 48
-  __shared__ __attribute__((aligned(16))) float sL[64 * P64];
-  __shared__ __attribute__((aligned(16))) float sA[64 * P64];
+  // sL (Akk) and sA ((I+L)^-1); before the Akk phase the same span holds kg^T
+  // as (hi | lo << 16) words, [KD][P64]
+  __shared__ __attribute__((aligned(16))) float sLA[2 * 64 * P64];
+  float* sL = sLA;
+  float* sA = sLA + 64 * P64;
+  uint32_t* sKG = reinterpret_cast<uint32_t*>(sLA);
+  static_assert(KD * P64 <= 2 * 64 * P64, "kg^T staging fits in sL and sA");
   __shared__ float sX[3 * 256];
   __shared__ float sBeta[64];
   // column operands of the off-diagonal levels, later reused for v^T and X^T
@@ -267,54 +283,87 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         store4(qg + frag_off(i, 32 * ks + 8 * quad + 4, NKS), x1);
       }
     }
-    bf16_t* kgh = reinterpret_cast<bf16_t*>(rec + RL.kgh);
-    bf16_t* kgl = reinterpret_cast<bf16_t*>(rec + RL.kgl);
+    // kg = k * 2^(gamma_C - gamma) as hi/lo pairs, transposed through LDS
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = kx[ks][e] * fexp2(gC[ks][e] - gl[ks][e]);
-        const bf16_t hb = f2bf(x);
-        const int off = frag_off(32 * ks + 8 * quad + e, i, 2);
-        kgh[off] = hb;
-        kgl[off] = f2bf(x - bf2f(hb));
+      for (int e = 0; e < 8; e += 2) {
+        uint32_t hi, lo;
+        split2(kx[ks][e] * fexp2(gC[ks][e] - gl[ks][e]), kx[ks][e + 1] * fexp2(gC[ks][e + 1] - gl[ks][e + 1]), hi, lo);
+        const int c = 32 * ks + 8 * quad + e;
+        sKG[c * P64 + i] = (hi & 0xffffu) | (lo << 16);
+        sKG[(c + 1) * P64 + i] = (hi >> 16) | (lo & 0xffff0000u);
       }
   }
   __syncthreads();
 
+  // ---- kg^T fragments to the workspace: 16 channel rows x 32 tokens each,
+  // lane l holds channel 16*kt + l%16 and tokens 32*ks + slots of l/16
+  {
+    u32x4* kgh = reinterpret_cast<u32x4*>(rec + RL.kgh);
+    u32x4* kgl = reinterpret_cast<u32x4*>(rec + RL.kgl);
+    for (int f = wave; f < KD / 8; f += 4) {
+      const int kt = f >> 1, ks = f & 1;
+      const uint32_t* src = sKG + (16 * kt + r16) * P64 + 32 * ks + 4 * quad;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src);        // tokens 4g .. 4g+3
+      const u32x4 y = *reinterpret_cast<const u32x4*>(src + 16);   // tokens 16+4g .. +3
+      const u32x4 hi = {__builtin_amdgcn_perm(x.y, x.x, 0x05040100u), __builtin_amdgcn_perm(x.w, x.z, 0x05040100u),
+                        __builtin_amdgcn_perm(y.y, y.x, 0x05040100u), __builtin_amdgcn_perm(y.w, y.z, 0x05040100u)};
+      const u32x4 lo = {__builtin_amdgcn_perm(x.y, x.x, 0x07060302u), __builtin_amdgcn_perm(x.w, x.z, 0x07060302u),
+                        __builtin_amdgcn_perm(y.y, y.x, 0x07060302u), __builtin_amdgcn_perm(y.w, y.z, 0x07060302u)};
+      kgh[f * 64 + lane] = hi;
+      kgl[f * 64 + lane] = lo;
+    }
+  }
+
   // ---- Akk (L) and Aqk tiles on the matrix cores
   ST* Aqk_out = reinterpret_cast<ST*>(rec + RL.aqk);
   {
-    // diagonal tile of this wave: levels L = 2 << b for b = 0..3 (blocks of 2, 4, 8, 16 rows)
+    // Diagonal tile of this wave: levels L = 2 << b for b = 0..3 (blocks of 2,
+    // 4, 8, 16 rows).  At level b every row carries one factor, relative to the
+    // first row of the upper half of its block: 2^(gamma_r - gamma_ref) in the
+    // upper half, 2^(gamma_ref - gamma_r) in the lower half.  The operand built
+    // from these rows serves as both matrix-core operands: the entries (i, j)
+    // with i in the upper and j in the lower half are exactly the wanted ones;
+    // the rest of the tile is ignored.  The reference gamma comes from the lane
+    // of the reference row by a DPP move (b = 0, 1) or a swizzle (b = 2, 3);
+    // the 16 lanes of a DPP row are the 16 rows of the tile.
     f32x4 dk[4], dq[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       dk[b] = zero4();
       dq[b] = zero4();
-      const int L = 2 << b;
-      const bool isrow = (r16 & (L - 1)) >= (L >> 1);
-      const int src = 16 * quad + (r16 & ~(L - 1)) + (L >> 1);   // lane holding the reference row
+    }
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        float ra[8], rb[8], rq8[8];
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const bool up = (r16 >> b) & 1;
+        // lane-uniform arithmetic only: a cross-lane move under a lane-dependent
+        // branch would read from disabled lanes
+        const float sgn = up ? 1.f : -1.f;
+        float kv[8], qv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float gr = __shfl(gl[ks][e], src);
-          const float f = fexp2(isrow ? gl[ks][e] - gr : gr - gl[ks][e]);
-          const float kv = kx[ks][e] * f;
-          ra[e] = isrow ? kv : 0.f;
-          rb[e] = isrow ? 0.f : kv;
-          rq8[e] = isrow ? qx[ks][e] * f : 0.f;
+          const float g = gl[ks][e];
+          float ex;
+          if (b == 0) ex = (up ? 0.f : 1.f) * (lane_from<0x101>(g) - g);   // lower rows: row r + 1 (row_shl:1)
+          else if (b == 1) ex = sgn * (g - lane_from<0xAA>(g));           // row (r & ~3) | 2 (quad_perm 2,2,2,2)
+          else if (b == 2) ex = sgn * (g - swizzle<0x98>(g));             // row (r & ~7) | 4
+          else ex = sgn * (g - swizzle<0x110>(g));                        // row 8
+          const float f = fexp2(ex);
+          kv[e] = kx[ks][e] * f;
+          qv[e] = qx[ks][e] * f;
         }
-        // transposed tile: column-side rows are the A operand, row-side rows the B operand
-        Frag R = split8(ra), Cs = split8(rb);
-        dk[b] = mma3(Cs, R, dk[b]);
+        const Frag F = split8(kv);
+        dk[b] = mma3(F, F, dk[b]);
         if (has_q) {
-          if (F32) dq[b] = mma3(Cs, split8(rq8), dq[b]);
-          else dq[b] = mfma(Cs.hi, round8(rq8), dq[b]);
+          if (F32) dq[b] = mma3(F, split8(qv), dq[b]);
+          else dq[b] = mfma(F.hi, round8(qv), dq[b]);
         }
       }
     }
+    __syncthreads();   // kg^T staging (sL, sA) fully read
     // diagonal tile output: this lane holds row i = r16, columns 4*quad .. +3,
     // and owns row i's beta, norms and q.k dot
     {
@@ -338,45 +387,77 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
       *reinterpret_cast<f32x4*>(&sL[i * P64 + 16 * wave + 4 * quad]) = vk4;
       if (has_q) store4(Aqk_out + frag_off(i, 16 * wave + 4 * quad, 2), vq4);
     }
-    // off-diagonal tiles: row operand from this wave's rows, column operand from LDS
-    auto off_tile = [&](const float* gref, int J, const bf16_t* bhi, const bf16_t* blo, int brow0)
-        __attribute__((always_inline)) {
-      f32x4 akk = zero4(), aqk = zero4();
+    // Off-diagonal tiles: this wave's rows (one row operand per reference,
+    // shared by the column tiles it meets) against column operands in LDS.
+    // Level 64: tiles 2, 3 against 0, 1 (reference row 32) -> acc[0], acc[1];
+    // level 32: tile 1 against 0 (row 16), tile 3 against 2 (row 48) -> acc[2].
+    if (wave >= 1) {
+      f32x4 ak[3], aq[3];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int j = 0; j < 3; ++j) {
+        ak[j] = zero4();
+        aq[j] = zero4();
+      }
+      const bool l64 = wave >= 2, l32 = (wave & 1) != 0;
+      const float* gref32 = wave == 1 ? sRef[0] : sRef[2];
+      const bf16_t* c32hi = wave == 1 ? b32ahi : b32bhi;
+      const bf16_t* c32lo = wave == 1 ? b32alo : b32blo;
+      auto row_op = [&](const float* gref, int ks, Frag& R, bf16x8& Rq, Frag& Rqf) __attribute__((always_inline)) {
         const int c0 = 32 * ks + 8 * quad;
-        float gr[8], ra[8], rq8[8];
+        float gr[8], kv[8], qv[8];
         load8(gref + c0, gr);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float f = fexp2(gl[ks][e] - gr[e]);
-          ra[e] = kx[ks][e] * f;
-          rq8[e] = qx[ks][e] * f;
+          kv[e] = kx[ks][e] * f;
+          qv[e] = qx[ks][e] * f;
         }
-        Frag R = split8(ra), Cs;
+        R = split8(kv);
+        if (F32) Rqf = split8(qv);
+        else Rq = round8(qv);
+      };
+      auto tile = [&](const Frag& R, const bf16x8& Rq, const Frag& Rqf, const bf16_t* bhi, const bf16_t* blo,
+                      int brow0, int ks, f32x4& akk, f32x4& aqk) __attribute__((always_inline)) {
+        const int c0 = 32 * ks + 8 * quad;
+        Frag Cs;
         Cs.hi = load_bf16x8(bhi + (brow0 + r16) * PB + c0);
         Cs.lo = load_bf16x8(blo + (brow0 + r16) * PB + c0);
         akk = mma3(Cs, R, akk);          // transposed tile: row i = r16, columns 4*quad .. +3
         if (has_q) {
-          if (F32) aqk = mma3(Cs, split8(rq8), aqk);
-          else aqk = mfma(Cs.hi, round8(rq8), aqk);
+          if (F32) aqk = mma3(Cs, Rqf, aqk);
+          else aqk = mfma(Cs.hi, Rq, aqk);
+        }
+      };
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        Frag R, Rqf;
+        bf16x8 Rq;
+        if (l64) {
+          row_op(sRef[1], ks, R, Rq, Rqf);
+          tile(R, Rq, Rqf, b64hi, b64lo, 0, ks, ak[0], aq[0]);
+          tile(R, Rq, Rqf, b64hi, b64lo, 16, ks, ak[1], aq[1]);
+        }
+        if (l32) {
+          row_op(gref32, ks, R, Rq, Rqf);
+          tile(R, Rq, Rqf, c32hi, c32lo, 0, ks, ak[2], aq[2]);
         }
       }
-      f32x4 vk4, vq4;
+      auto put = [&](int J, const f32x4& akk, const f32x4& aqk) __attribute__((always_inline)) {
+        f32x4 vk4, vq4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vk4[e] = beta * akk[e];
-        vq4[e] = a.scale * aqk[e];
+        for (int e = 0; e < 4; ++e) {
+          vk4[e] = beta * akk[e];
+          vq4[e] = a.scale * aqk[e];
+        }
+        *reinterpret_cast<f32x4*>(&sL[i * P64 + 16 * J + 4 * quad]) = vk4;
+        if (has_q) store4(Aqk_out + frag_off(i, 16 * J + 4 * quad, 2), vq4);
+      };
+      if (l64) {
+        put(0, ak[0], aq[0]);
+        put(1, ak[1], aq[1]);
       }
-      *reinterpret_cast<f32x4*>(&sL[i * P64 + 16 * J + 4 * quad]) = vk4;
-      if (has_q) store4(Aqk_out + frag_off(i, 16 * J + 4 * quad, 2), vq4);
-    };
-    if (wave == 1) off_tile(sRef[0], 0, b32ahi, b32alo, 0);
-    if (wave >= 2) {
-      off_tile(sRef[1], 0, b64hi, b64lo, 0);
-      off_tile(sRef[1], 1, b64hi, b64lo, 16);
+      if (l32) put(wave - 1, ak[2], aq[2]);
     }
-    if (wave == 3) off_tile(sRef[2], 2, b32bhi, b32blo, 0);
     if (has_q) {  // upper-triangle tiles of this row tile are zero
       for (int J = wave + 1; J < 4; ++J) store4(Aqk_out + frag_off(i, 16 * J + 4 * quad, 2), zero4());
     }

@@ -98,6 +98,10 @@ __device__ __forceinline__ Frag join_halves(const u32x4& a, const u32x4& b) {
   return f;
 }
 
+constexpr int TOUCH_AHEAD = 4;   // chunks between an L2 touch and its chunk's loads
+constexpr int SPF = 1;           // state waves: chunks between an operand load and its use
+constexpr int OPF = 2;           // output waves: the same
+
 template <int KD, int VD, typename ST, bool SUM, int CT>
 __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanArgs a) {
   constexpr RecLayout L = rec_layout(KD, VD, (int)sizeof(ST), !SUM);
@@ -153,7 +157,8 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanA
                                : L.ut + (uint32_t)((TPW * s * (VD / 16) + v0 / 16) * 256 + lane * 4) * 4;
     const uint32_t o_kg = (uint32_t)(2 * s * 2 * 512 + lane * 8) * 2;
     const uint32_t o_gd = L.gd + (uint32_t)(row0 + 4 * quad) * 4;
-    auto load = [&](Ops& f, int c) __attribute__((always_inline)) {
+    // operands of the first half of a step (w h and v_new) ...
+    auto load_a = [&](Ops& f, int c) __attribute__((always_inline)) {
       const rsrc_t r = make_rsrc(recs + (size_t)c * L.bytes, (uint32_t)L.bytes);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) f.w[tt].load(r, o_w + FW * NS * tt);
@@ -162,6 +167,10 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanA
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
           f.u[j][ct] = __builtin_bit_cast(f32x4, buf_load16(r, o_u + (mtile ? 0 : 1024 * ((VD / 16) * j + ct))));
+    };
+    // ... and of the state update
+    auto load_b = [&](Ops& f, int c) __attribute__((always_inline)) {
+      const rsrc_t r = make_rsrc(recs + (size_t)c * L.bytes, (uint32_t)L.bytes);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -172,6 +181,10 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanA
         }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) f.gd[kt] = __builtin_bit_cast(f32x4, buf_load16(r, o_gd + 64 * kt));
+    };
+    auto load = [&](Ops& f, int c) __attribute__((always_inline)) {
+      load_a(f, c);
+      load_b(f, c);
     };
 
     // state rows row0 + 16*kt + 4*quad + e, column v0 + 16*ct + r16
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanA
       // Unconditional prefetch (the last chunk reloads itself) so that the
       // compiler's wait counters stay exact across the loop back-edge; the
       // scheduling barrier keeps the loads at the top of the step.
-      load(nxt, min(c + 1, nck - 1));
+      load(nxt, min(c + SPF, nck - 1));
       __builtin_amdgcn_sched_barrier(0);
       // ---- 1. this wave's share of w h
 #pragma unroll
@@ -264,11 +277,14 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanA
     };
 
     if (nck > 0) {
-      Ops fa, fb;
-      load(fa, 0);
-      for (int c = 0; c < nck; c += 2) {
-        step(fa, fb, c);
-        if (c + 1 < nck) step(fb, fa, c + 1);
+      // operands of chunk c live in f[c % (SPF + 1)], loaded SPF steps ahead
+      Ops f[SPF + 1];
+#pragma unroll
+      for (int i = 0; i < SPF; ++i) load(f[i], min(i, nck - 1));
+      for (int c = 0; c < nck; c += SPF + 1) {
+#pragma unroll
+        for (int i = 0; i <= SPF; ++i)
+          if (c + i < nck) step(f[i], f[(i + SPF) % (SPF + 1)], c + i);
       }
     }
 
@@ -332,13 +348,15 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanA
     };
     ST* op = static_cast<ST*>(a.o);
     // Each step loads chunk c + 2 into `ld` and forms chunk c from `use`.
-    uint32_t pf0 = touch(1), pf1 = touch(2), pf2 = touch(3);
+    uint32_t pf[TOUCH_AHEAD - 1];
+#pragma unroll
+    for (int i = 0; i < TOUCH_AHEAD - 1; ++i) pf[i] = touch(i + 1);
     auto ostep = [&](OF& ld, const OF& use, int c) __attribute__((always_inline)) {
-      load(ld, min(c + 2, nck - 1));
-      asm volatile("; prefetch sink %0" ::"v"(pf0));
-      pf0 = pf1;
-      pf1 = pf2;
-      pf2 = touch(c + 4);
+      load(ld, min(c + OPF, nck - 1));
+      asm volatile("; prefetch sink %0" ::"v"(pf[0]));
+#pragma unroll
+      for (int i = 0; i + 1 < TOUCH_AHEAD - 1; ++i) pf[i] = pf[i + 1];
+      pf[TOUCH_AHEAD - 2] = touch(c + TOUCH_AHEAD);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();                                           // A(c)
       __syncthreads();                                           // B(c)
@@ -373,15 +391,17 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanA
       }
     };
     if (nck > 0) {
-      OF f0, f1, f2;
-      load(f0, 0);
-      load(f1, min(1, nck - 1));
-      for (int c = 0; c < nck; c += 3) {
-        ostep(f2, f0, c);
-        if (c + 1 < nck) ostep(f0, f1, c + 1);
-        if (c + 2 < nck) ostep(f1, f2, c + 2);
+      // operands of chunk c live in f[c % (OPF + 1)], loaded OPF steps ahead
+      OF f[OPF + 1];
+#pragma unroll
+      for (int i = 0; i < OPF; ++i) load(f[i], min(i, nck - 1));
+      for (int c = 0; c < nck; c += OPF + 1) {
+#pragma unroll
+        for (int i = 0; i <= OPF; ++i)
+          if (c + i < nck) ostep(f[(i + OPF) % (OPF + 1)], f[i], c + i);
       }
-      asm volatile("; prefetch sink %0 %1 %2" ::"v"(pf0), "v"(pf1), "v"(pf2));
+#pragma unroll
+      for (int i = 0; i < TOUCH_AHEAD - 1; ++i) asm volatile("; prefetch sink %0" ::"v"(pf[i]));
     }
   }
 }
