@@ -106,7 +106,7 @@ kda_status_t plan_problem(const kda_problem_t* p, bool forward, Plan& pl) {
   }
   if (pl.nchunks > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many chunks (%lld)", (long long)pl.nchunks);
   const int VA = forward ? p->V : p->V + p->K;
-  if ((int64_t)(VA / 16) * p->Hv * pl.N > 0x7fffffffLL)
+  if ((int64_t)(VA / 16) * p->Hv * pl.N > 0x7fffffffLL || pl.nchunks * (int64_t)p->Hv > 0x7fffffffLL)
     return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head, tile) workgroups");
 
   const size_t slots = (size_t)p->Hv * (size_t)pl.nchunks;

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   ST* sVT = reinterpret_cast<ST*>(sU8);            // [VD][PT]
   ST* sXT = sVT + VD * PT;                         // [KD][PT]
 
-  const int gc = blockIdx.x, h = blockIdx.y;
+  const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, quad = lane >> 4;
   const int n = seq_of_chunk(a.seq, gc);
@@ -596,7 +596,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
 
 hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t s) {
   if (a.nchunks == 0 || a.Hv == 0) return hipSuccess;
-  dim3 grid(a.nchunks, a.Hv), block(256);
+  const long nb = (long)a.nchunks * a.Hv;
+  if (nb > 0x7fffffffL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nb), block(256);
 #define KDA_INTRA_CASE(KK, VV, TT)                                          \
   if (K == KK && V == VV) {                                                 \
     hipLaunchKernelGGL((intra_kernel<KK, VV, TT>), grid, block, 0, s, a);   \
