@@ -87,7 +87,7 @@ __device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-template <int KD, int VD, typename IT>
+template <int KD, int VD, typename IT, bool FWD>
 __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   using ST = IT;                                   // workspace type of w, qg, Aqk
   constexpr bool F32 = sizeof(IT) == 4;
@@ -133,9 +133,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   const int C = min(BT, len - cidx * BT);
   const int hk = h / (a.Hv / a.Hk);
   const int64_t ch = (int64_t)h * a.nchunks + gc;      // head-major chunk slot
-  const RecLayout RL = rec_layout(KD, VD, (int)sizeof(IT), a.q != nullptr);
+  constexpr RecLayout RL = rec_layout(KD, VD, (int)sizeof(IT), FWD);
   unsigned char* rec = a.ws + ch * RL.bytes;
-  const bool has_q = a.q != nullptr;
+  constexpr bool has_q = FWD;                          // q (and the output terms) present
   const int i = 16 * wave + r16;                       // this lane's token row
   const bool live = i < C;
 
@@ -171,25 +171,34 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
 
   // ---- gate activation (log2 units), in-wave row prefix sums, norms
   {
-    const bool gik = a.flags & F_GATE, safe = a.flags & F_SAFE;
-    const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
+    // The flag tests sit outside the element loops (one uniform branch), so
+    // that the per-element work forms one straight-line block.
+    const bool gik = a.flags & F_GATE;
+    const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;   // max(g, -inf) = g
+    if (gik) {
+      const float Aexp = expf(a.A_log[h]);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      float bias[8];
-      if (gik && a.dt_bias) load8(a.dt_bias + h * KD + 32 * ks + 8 * quad, bias);
-      else zero8(bias);
+      for (int ks = 0; ks < NKS; ++ks) {
+        float bias[8];
+        if (a.dt_bias) load8(a.dt_bias + h * KD + 32 * ks + 8 * quad, bias);
+        else zero8(bias);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float gn = gl[ks][e];
-        if (gik) {
-          const float z = gn + bias[e];
+        for (int e = 0; e < 8; ++e) {
+          const float z = gl[ks][e] + bias[e];
           // softplus(z) = max(z, 0) + ln(1 + e^-|z|)
-          gn = -Aexp * (fmaxf(z, 0.f) + LN2 * flog2(1.f + fexp2(-LOG2E * fabsf(z))));
+          gl[ks][e] = fmaxf(-Aexp * (fmaxf(z, 0.f) + LN2 * flog2(1.f + fexp2(-LOG2E * fabsf(z)))), lb);
         }
-        if (safe) gn = fmaxf(gn, a.lower_bound);
-        gl[ks][e] = row_scan16(live ? gn * LOG2E : 0.f);
       }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gl[ks][e] = fmaxf(gl[ks][e], lb);
     }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gl[ks][e] = row_scan16(live ? gl[ks][e] * LOG2E : 0.f);
   }
   float rq, rk, dqk;
   {
@@ -601,7 +610,8 @@ hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t
   dim3 grid((unsigned)nb), block(256);
 #define KDA_INTRA_CASE(KK, VV, TT)                                          \
   if (K == KK && V == VV) {                                                 \
-    hipLaunchKernelGGL((intra_kernel<KK, VV, TT>), grid, block, 0, s, a);   \
+    if (a.q) hipLaunchKernelGGL((intra_kernel<KK, VV, TT, true>), grid, block, 0, s, a);  \
+    else hipLaunchKernelGGL((intra_kernel<KK, VV, TT, false>), grid, block, 0, s, a);     \
     return hipGetLastError();                                               \
   }
   if (dtype == 1) {

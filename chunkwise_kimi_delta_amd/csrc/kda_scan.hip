@@ -101,9 +101,14 @@ __device__ __forceinline__ Frag join_halves(const u32x4& a, const u32x4& b) {
 constexpr int TOUCH_AHEAD = 4;   // chunks between an L2 touch and its chunk's loads
 constexpr int SPF = 1;           // state waves: chunks between an operand load and its use
 constexpr int OPF = 2;           // output waves: the same
+#ifndef KDA_SCAN_NOW
+#define KDA_SCAN_NOW 2
+#endif
+constexpr int NOW = KDA_SCAN_NOW;  // output waves (forward mode)
+constexpr int TPO = 4 / NOW;       // token tiles per output wave
 
 template <int KD, int VD, typename ST, bool SUM, int CT>
-__global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(ScanArgs a) {
   constexpr RecLayout L = rec_layout(KD, VD, (int)sizeof(ST), !SUM);
   constexpr bool F32 = sizeof(ST) == 4;
   constexpr int ES = (int)sizeof(ST);
@@ -314,21 +319,21 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanA
     }
   } else if constexpr (!SUM) {
     // =========================== output waves ==========================
-    // first output wave: token tiles 0, 1; second: token tiles 2, 3.  Chunk
-    // c's output is formed between the state waves' barriers B(c) and A(c+1).
+    // output wave ow forms token tiles TPO*ow .. TPO*ow + TPO - 1.  Chunk c's
+    // output is formed between the state waves' barriers B(c) and A(c+1).
     const int ow = wave - NS;
     struct OF {
-      Op<ST> q[2][NS];    // qg rows 16*(2*ow + j) + r16, channels 32*kb + (slots of lane / 16)
-      Op<ST> aq[2][2];    // Aqk rows 16*(2*ow + j) + r16, tokens 32*ks + (slots)
+      Op<ST> q[TPO][NS];    // qg rows 16*(TPO*ow + j) + r16, channels 32*kb + (slots of lane / 16)
+      Op<ST> aq[TPO][2];    // Aqk rows 16*(TPO*ow + j) + r16, tokens 32*ks + (slots)
     };
-    // fragments (2*ow + j, kb) of qg and (2*ow + j, ks) of Aqk
+    // fragments (TPO*ow + j, kb) of qg and (TPO*ow + j, ks) of Aqk
     constexpr uint32_t FW = 512 * ES;
-    const uint32_t o_q = L.qg + (uint32_t)(2 * ow * NS * 512 + lane * 8) * ES;
-    const uint32_t o_a = L.aqk + (uint32_t)(2 * ow * 2 * 512 + lane * 8) * ES;
+    const uint32_t o_q = L.qg + (uint32_t)(TPO * ow * NS * 512 + lane * 8) * ES;
+    const uint32_t o_a = L.aqk + (uint32_t)(TPO * ow * 2 * 512 + lane * 8) * ES;
     auto load = [&](OF& f, int c) __attribute__((always_inline)) {
       const rsrc_t r = make_rsrc(recs + (size_t)c * L.bytes, (uint32_t)L.bytes);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < TPO; ++j) {
 #pragma unroll
         for (int kb = 0; kb < NS; ++kb) f.q[j][kb].load(r, o_q + FW * (NS * j + kb));
 #pragma unroll
@@ -341,7 +346,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanA
     // so the touch never makes this wave wait.
     constexpr int NL = (int)(L.bytes / 128);
     const int l0 = tv * NL / NTILE, l1 = (tv + 1) * NL / NTILE;
-    const int tline = l0 + ow * 64 + lane;
+    const int tline = l0 + ow * 64 + lane;   // NOW*64 lanes cover a tile's share
     const uint32_t toff = tline < l1 ? (uint32_t)tline * 128 : (uint32_t)L.bytes;   // past the end: no access
     auto touch = [&](int c) __attribute__((always_inline)) -> uint32_t {
       return buf_load4(make_rsrc(recs + (size_t)min(c, nck - 1) * L.bytes, (uint32_t)L.bytes), toff);
@@ -374,9 +379,9 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 128) void scan_kernel(ScanA
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) vf[ks] = join_halves(sV[b][2 * ks][ct][lane], sV[b][2 * ks + 1][ct][lane]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TPO; ++j) {
           // o^T tile: this lane holds token 16*tt + r16, columns v0 + 16*ct + 4*quad .. +3
-          const int tt = 2 * ow + j;
+          const int tt = TPO * ow + j;
           f32x4 acc = zero4();
 #pragma unroll
           for (int kb = 0; kb < NS; ++kb) acc = mma_out(hh[kb], hl[kb], use.q[j][kb], acc);
@@ -447,8 +452,8 @@ hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s
 #endif
   const long nb = (long)(VA / (16 * CTsel)) * a.Hv * a.seq.N;
   if (nb > 0x7fffffffL) return hipErrorInvalidValue;
-  // K/32 state waves, plus two output waves in forward mode
-  dim3 grid((unsigned)nb), block(K * 2 + (a.summary ? 0 : 128));
+  // K/32 state waves, plus the output waves in forward mode
+  dim3 grid((unsigned)nb), block(K * 2 + (a.summary ? 0 : 64 * NOW));
 #define KDA_SCAN_CASE(KK, VV, TT, CC)                                                             \
   if (K == KK && V == VV && CTsel == CC) {                                                        \
     if (a.summary) hipLaunchKernelGGL((scan_kernel<KK, VV, TT, true, CC>), grid, block, 0, s, a); \
