@@ -81,6 +81,31 @@ __device__ __forceinline__ f32x4 mma3(const Frag& A, const Frag& B, f32x4 acc) {
   return acc;
 }
 
+// Eight consecutive elements through a buffer descriptor (zeros past its end).
+template <typename T> __device__ __forceinline__ void load8b(rsrc_t r, uint32_t off, float (&x)[8]);
+template <> __device__ __forceinline__ void load8b<bf16_t>(rsrc_t r, uint32_t off, float (&x)[8]) {
+  const u32x4 u = buf_load16(r, off);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = __uint_as_float(w[j] << 16);
+    x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
+template <> __device__ __forceinline__ void load8b<float>(rsrc_t r, uint32_t off, float (&x)[8]) {
+  const f32x4 a = __builtin_bit_cast(f32x4, buf_load16(r, off));
+  const f32x4 b = __builtin_bit_cast(f32x4, buf_load16(r, off + 16));
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+template <typename T> __device__ __forceinline__ float load1b(rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ float load1b<bf16_t>(rsrc_t r, uint32_t off) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0) << 16);
+}
+template <> __device__ __forceinline__ float load1b<float>(rsrc_t r, uint32_t off) {
+  return __uint_as_float(buf_load4(r, off));
+}
+
 // Store 4 consecutive values (8 bytes as bf16, 16 bytes as fp32).
 __device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -139,52 +164,55 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   const int i = 16 * wave + r16;                       // this lane's token row
   const bool live = i < C;
 
-  // ---- loads: gate, k, q, v rows of this lane; beta
-  float gl[NKS][8], kx[NKS][8], qx[NKS][8], vx[NVS][8];
+  // ---- loads, in the order of use (loads complete in order): gate bias and
+  // gate rows first, then k, q, v rows of this lane; beta.  Buffer loads with
+  // per-tensor descriptors bounded at the chunk's last valid row: rows past the
+  // sequence end read as zeros without a branch, so all loads issue back to
+  // back (a conditional load would make the compiler wait for each one).
+  const bool gik = a.flags & F_GATE;
+  constexpr int ES = (int)sizeof(IT);
+  float bias[NKS][8];
   {
-    const int64_t tok = tok0 + i;
+    const rsrc_t rb = make_rsrc(a.dt_bias ? a.dt_bias + h * KD : a.A_log, (gik && a.dt_bias) ? KD * 4 : 0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) load8b<float>(rb, (uint32_t)(32 * ks + 8 * quad) * 4, bias[ks]);
+  }
+  const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
+  float gl[NKS][8], kx[NKS][8], qx[NKS][8], vx[NVS][8];
+  float beta;
+  {
+    const rsrc_t rg = make_rsrc(static_cast<const IT*>(a.g) + (tok0 * a.Hv + h) * KD, (uint32_t)(C * a.Hv * KD * ES));
+    const rsrc_t rk = make_rsrc(static_cast<const IT*>(a.k) + (tok0 * a.Hk + hk) * KD, (uint32_t)(C * a.Hk * KD * ES));
+    const rsrc_t rq = make_rsrc(has_q ? static_cast<const IT*>(a.q) + (tok0 * a.Hk + hk) * KD : nullptr,
+                                has_q ? (uint32_t)(C * a.Hk * KD * ES) : 0u);
+    const rsrc_t rv = make_rsrc(static_cast<const IT*>(a.v) + (tok0 * a.Hv + h) * VD, (uint32_t)(C * a.Hv * VD * ES));
+    const rsrc_t rbeta = make_rsrc(static_cast<const IT*>(a.beta) + tok0 * a.Hv + h, (uint32_t)(C * a.Hv * ES));
+    const uint32_t ok = (uint32_t)(i * a.Hk * KD) * ES, og = (uint32_t)(i * a.Hv * KD) * ES;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) load8b<IT>(rg, og + (32 * ks + 8 * quad) * ES, gl[ks]);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const int c0 = 32 * ks + 8 * quad;
-      if (live) {
-        load8(static_cast<const IT*>(a.g) + tok * (int64_t)(a.Hv * KD) + h * KD + c0, gl[ks]);
-        load8(static_cast<const IT*>(a.k) + tok * (int64_t)(a.Hk * KD) + hk * KD + c0, kx[ks]);
-        if (has_q) load8(static_cast<const IT*>(a.q) + tok * (int64_t)(a.Hk * KD) + hk * KD + c0, qx[ks]);
-        else zero8(qx[ks]);
-      } else {
-        zero8(gl[ks]);
-        zero8(kx[ks]);
-        zero8(qx[ks]);
-      }
+      load8b<IT>(rk, ok + (32 * ks + 8 * quad) * ES, kx[ks]);
+      load8b<IT>(rq, ok + (32 * ks + 8 * quad) * ES, qx[ks]);
     }
+    const uint32_t ov = (uint32_t)(i * a.Hv * VD) * ES;
 #pragma unroll
-    for (int vs = 0; vs < NVS; ++vs) {
-      if (live) load8(static_cast<const IT*>(a.v) + tok * (int64_t)(a.Hv * VD) + h * VD + 32 * vs + 8 * quad, vx[vs]);
-      else zero8(vx[vs]);
-    }
+    for (int vs = 0; vs < NVS; ++vs) load8b<IT>(rv, ov + (32 * vs + 8 * quad) * ES, vx[vs]);
+    beta = load1b<IT>(rbeta, (uint32_t)(i * a.Hv) * ES);
   }
-  float beta = 0.f;
-  if (live) {
-    beta = to_f<IT>(static_cast<const IT*>(a.beta)[(tok0 + i) * a.Hv + h]);
-    if (a.flags & F_SIGMOID) beta = 1.f / (1.f + expf(-beta));
-  }
+  if (a.flags & F_SIGMOID) beta = live ? 1.f / (1.f + expf(-beta)) : 0.f;
 
   // ---- gate activation (log2 units), in-wave row prefix sums, norms
   {
     // The flag tests sit outside the element loops (one uniform branch), so
     // that the per-element work forms one straight-line block.
-    const bool gik = a.flags & F_GATE;
     const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;   // max(g, -inf) = g
     if (gik) {
-      const float Aexp = expf(a.A_log[h]);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        float bias[8];
-        if (a.dt_bias) load8(a.dt_bias + h * KD + 32 * ks + 8 * quad, bias);
-        else zero8(bias);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float z = gl[ks][e] + bias[e];
+          const float z = gl[ks][e] + bias[ks][e];
           // softplus(z) = max(z, 0) + ln(1 + e^-|z|)
           gl[ks][e] = fmaxf(-Aexp * (fmaxf(z, 0.f) + LN2 * flog2(1.f + fexp2(-LOG2E * fabsf(z)))), lb);
         }
