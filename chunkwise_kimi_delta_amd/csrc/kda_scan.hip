@@ -354,8 +354,6 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     ST* op = static_cast<ST*>(a.o);
     // Each step loads chunk c + 2 into `ld` and forms chunk c from `use`.
     uint32_t pf[TOUCH_AHEAD - 1];
-#pragma unroll
-    for (int i = 0; i < TOUCH_AHEAD - 1; ++i) pf[i] = touch(i + 1);
     auto ostep = [&](OF& ld, const OF& use, int c) __attribute__((always_inline)) {
       load(ld, min(c + OPF, nck - 1));
       asm volatile("; prefetch sink %0" ::"v"(pf[0]));
@@ -396,6 +394,10 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
       }
     };
     if (nck > 0) {
+      // (the first touches, like every load here, only for a sequence with chunks:
+      // for an empty one the clamped chunk index would be -1)
+#pragma unroll
+      for (int i = 0; i < TOUCH_AHEAD - 1; ++i) pf[i] = touch(i + 1);
       // operands of chunk c live in f[c % (OPF + 1)], loaded OPF steps ahead
       OF f[OPF + 1];
 #pragma unroll

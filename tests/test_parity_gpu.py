@@ -130,6 +130,17 @@ def test_varlen_small_with_cache(gpu_lib):
             assert np.array_equal(got[r], cache_before[r]), f"row {r} changed"
 
 
+def test_varlen_leading_and_trailing_empty_sequences(gpu_lib):
+    """Empty sequences first and last: they own no chunks, so no workgroup of
+    theirs may address a record (the first one's would lie before the workspace)."""
+    p = ks.make("varlen", lens=[0, 70, 0, 129, 0], H=2, cache_rows=6, n_invalid=0)
+    t = to_torch(p)
+    o, cache = run_fwd(gpu_lib, p, t)
+    ro, rcache = orc.forward(p)
+    check("o", np64(o), ro, TOL_BF16_OUT)
+    check("cache", np64(cache), rcache, TOL_STATE)
+
+
 def test_varlen_cache_out_of_range_index_reads_zero(gpu_lib):
     p = ks.make("varlen", lens=[40, 90], H=2, cache_rows=4, n_invalid=0)
     p.state_indices = np.array([7, 2], dtype=np.int32)     # 7 >= rows: invalid
