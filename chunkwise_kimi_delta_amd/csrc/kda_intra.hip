@@ -30,6 +30,12 @@
 // both factors <= 1.  Levels 64 and 32 are full 16x16 tiles; levels 16, 8, 4
 // and 2 live inside the diagonal tiles and are masked per entry.  The diagonal
 // of Aqk (factor 1) is a plain dot product.
+//
+// Precision of the matrix-core products.  With bf16 token tensors every
+// factor of Akk and Aqk enters as one bf16 rounding (single pass): an
+// error of 2^-9 relative per entry of L moves (I + L)^-1, u and w by far less
+// than the state tolerance, since L only reaches the state through them.
+// With fp32 token tensors Akk and Aqk use bf16 hi/lo pairs (three passes).
 #include "kda_launch.h"
 
 namespace kda {
@@ -120,7 +126,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   constexpr int P64 = 64 + 4;                      // row stride of sL / sA (floats)
   constexpr int PB = KD + 8;                       // row stride of bf16 column operands
   constexpr int PT = 64 + 16 / (int)sizeof(ST);    // row stride of v^T / X^T
-  constexpr int BOP_BYTES = (32 + 16 + 16) * PB * 2 * 2;
+  constexpr int NP = F32 ? 2 : 1;                  // bf16 parts of a column operand (hi [, lo])
+  constexpr int BOP_BYTES = (32 + 16 + 16) * PB * 2 * NP;
   constexpr int VX_BYTES = (VD + KD) * PT * (int)sizeof(ST);
   constexpr int UB = BOP_BYTES > VX_BYTES ? BOP_BYTES : VX_BYTES;
 
@@ -138,10 +145,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   // column operands of the off-diagonal levels, later reused for v^T and X^T
   __shared__ __attribute__((aligned(16))) unsigned char sU8[UB];
   bf16_t* b64hi = reinterpret_cast<bf16_t*>(sU8);  // rows 0..31, reference row 32
-  bf16_t* b64lo = b64hi + 32 * PB;
-  bf16_t* b32ahi = b64lo + 32 * PB;                // rows 0..15, reference row 16
+  bf16_t* b64lo = b64hi + 32 * PB;                 // (lo parts: fp32 tokens only)
+  bf16_t* b32ahi = b64hi + NP * 32 * PB;           // rows 0..15, reference row 16
   bf16_t* b32alo = b32ahi + 16 * PB;
-  bf16_t* b32bhi = b32alo + 16 * PB;               // rows 32..47, reference row 48
+  bf16_t* b32bhi = b32ahi + NP * 16 * PB;          // rows 32..47, reference row 48
   bf16_t* b32blo = b32bhi + 16 * PB;
   ST* sVT = reinterpret_cast<ST*>(sU8);            // [VD][PT]
   ST* sXT = sVT + VD * PT;                         // [KD][PT]
@@ -298,9 +305,13 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         load8(gref + c0, gr);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = kx[ks][e] * fexp2(gr[e] - gl[ks][e]);
-        Frag f = split8(x);
-        *reinterpret_cast<bf16x8*>(hi + row * PB + c0) = f.hi;
-        *reinterpret_cast<bf16x8*>(lo + row * PB + c0) = f.lo;
+        if constexpr (F32) {
+          Frag f = split8(x);
+          *reinterpret_cast<bf16x8*>(hi + row * PB + c0) = f.hi;
+          *reinterpret_cast<bf16x8*>(lo + row * PB + c0) = f.lo;
+        } else {
+          *reinterpret_cast<bf16x8*>(hi + row * PB + c0) = round8(x);
+        }
       }
     };
     if (wave <= 1) put_col(sRef[1], b64hi, b64lo, i);
@@ -392,11 +403,14 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
           kv[e] = kx[ks][e] * f;
           qv[e] = qx[ks][e] * f;
         }
-        const Frag F = split8(kv);
-        dk[b] = mma3(F, F, dk[b]);
-        if (has_q) {
-          if (F32) dq[b] = mma3(F, split8(qv), dq[b]);
-          else dq[b] = mfma(F.hi, round8(qv), dq[b]);
+        if constexpr (F32) {
+          const Frag F = split8(kv);
+          dk[b] = mma3(F, F, dk[b]);
+          if (has_q) dq[b] = mma3(F, split8(qv), dq[b]);
+        } else {
+          const bf16x8 F = round8(kv);
+          dk[b] = mfma(F, F, dk[b]);
+          if (has_q) dq[b] = mfma(F, round8(qv), dq[b]);
         }
       }
     }
@@ -449,20 +463,28 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
           kv[e] = kx[ks][e] * f;
           qv[e] = qx[ks][e] * f;
         }
-        R = split8(kv);
-        if (F32) Rqf = split8(qv);
-        else Rq = round8(qv);
+        if constexpr (F32) {
+          R = split8(kv);
+          Rqf = split8(qv);
+        } else {
+          R.hi = round8(kv);
+          Rq = round8(qv);
+        }
       };
       auto tile = [&](const Frag& R, const bf16x8& Rq, const Frag& Rqf, const bf16_t* bhi, const bf16_t* blo,
                       int brow0, int ks, f32x4& akk, f32x4& aqk) __attribute__((always_inline)) {
         const int c0 = 32 * ks + 8 * quad;
-        Frag Cs;
-        Cs.hi = load_bf16x8(bhi + (brow0 + r16) * PB + c0);
-        Cs.lo = load_bf16x8(blo + (brow0 + r16) * PB + c0);
-        akk = mma3(Cs, R, akk);          // transposed tile: row i = r16, columns 4*quad .. +3
-        if (has_q) {
-          if (F32) aqk = mma3(Cs, Rqf, aqk);
-          else aqk = mfma(Cs.hi, Rq, aqk);
+        // transposed tiles: row i = r16, columns 4*quad .. +3
+        if constexpr (F32) {
+          Frag Cs;
+          Cs.hi = load_bf16x8(bhi + (brow0 + r16) * PB + c0);
+          Cs.lo = load_bf16x8(blo + (brow0 + r16) * PB + c0);
+          akk = mma3(Cs, R, akk);
+          if (has_q) aqk = mma3(Cs, Rqf, aqk);
+        } else {
+          const bf16x8 Ch = load_bf16x8(bhi + (brow0 + r16) * PB + c0);
+          akk = mfma(Ch, R.hi, akk);
+          if (has_q) aqk = mfma(Ch, Rq, aqk);
         }
       };
 #pragma unroll
