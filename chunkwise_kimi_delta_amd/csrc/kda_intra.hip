@@ -154,7 +154,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   ST* sXT = sVT + VD * PT;                         // [KD][PT]
 
   const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave branches are scalar
   const int r16 = lane & 15, quad = lane >> 4;
   const int n = seq_of_chunk(a.seq, gc);
   int64_t tok0s;
@@ -590,62 +591,55 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   }
 
   // ---- u^T = (A diag(beta) v)^T (fp32),  w = A diag(beta) X (token dtype)
+  // Both reduction slices are used by every wave: the strictly upper blocks
+  // of A are zero in LDS, so the products need no per-wave bounds.
   {
     const int I = wave;
-    const int nks = I >= 2 ? 2 : 1;                // A is lower triangular
     Frag fa[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      float x[8];
       const int j0 = 32 * ks + 8 * quad;
+      float ar[8], bt[8], x[8];
+      load8(&sA[(16 * I + r16) * P64 + j0], ar);
+      load8(&sBeta[j0], bt);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = ks < nks ? sA[(16 * I + r16) * P64 + j0 + e] * sBeta[j0 + e] : 0.f;
+      for (int e = 0; e < 8; ++e) x[e] = ar[e] * bt[e];
       fa[ks] = split8(x);
     }
-    auto tile = [&](const ST* bsrc, int ct) __attribute__((always_inline)) {
+    auto tile = [&](const ST* bsrc, int ct, bool a_left) __attribute__((always_inline)) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        if (ks < nks) {
-          const ST* bp = bsrc + (16 * ct + r16) * PT + 32 * ks + 8 * quad;
-          if (F32) {
-            float xb[8];
-            load8(reinterpret_cast<const float*>(bp), xb);
-            acc = mma3(fa[ks], split8(xb), acc);
-          } else {
-            bf16x8 b = load_bf16x8(reinterpret_cast<const bf16_t*>(bp));
+        const ST* bp = bsrc + (16 * ct + r16) * PT + 32 * ks + 8 * quad;
+        if constexpr (F32) {
+          float xb[8];
+          load8(reinterpret_cast<const float*>(bp), xb);
+          acc = a_left ? mma3(fa[ks], split8(xb), acc) : mma3(split8(xb), fa[ks], acc);
+        } else {
+          const bf16x8 b = load_bf16x8(reinterpret_cast<const bf16_t*>(bp));
+          if (a_left) {
             acc = mfma(fa[ks].hi, b, acc);
             acc = mfma(fa[ks].lo, b, acc);
+          } else {
+            acc = mfma(b, fa[ks].hi, acc);
+            acc = mfma(b, fa[ks].lo, acc);
           }
         }
       }
       return acc;
     };
     float* uT = reinterpret_cast<float*>(rec + RL.ut);
+#pragma unroll
     for (int ct = 0; ct < VD / 16; ++ct) {
-      f32x4 acc = tile(sVT, ct);
+      const f32x4 acc = tile(sVT, ct, true);
       *reinterpret_cast<f32x4*>(uT + cfrag_off(16 * I + 4 * quad, 16 * ct + r16, VD / 16)) = acc;
     }
     // w^T tiles (X^T rows as the A operand): this lane holds token 16*I + r16,
     // channels 16*ct + 4*quad .. +3 -> one vector store
     ST* wbase = reinterpret_cast<ST*>(rec + RL.w);
-    for (int ct = 0; ct < KD / 16; ++ct) {
-      f32x4 acc = zero4();
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks < nks) {
-          const ST* xp = sXT + (16 * ct + r16) * PT + 32 * ks + 8 * quad;
-          if (F32) {
-            float xb[8];
-            load8(reinterpret_cast<const float*>(xp), xb);
-            acc = mma3(split8(xb), fa[ks], acc);
-          } else {
-            bf16x8 x = load_bf16x8(reinterpret_cast<const bf16_t*>(xp));
-            acc = mfma(x, fa[ks].hi, acc);
-            acc = mfma(x, fa[ks].lo, acc);
-          }
-        }
-      }
+    for (int ct = 0; ct < KD / 16; ++ct) {
+      const f32x4 acc = tile(sXT, ct, false);
       store4(wbase + frag_off(16 * I + r16, 16 * ct + 4 * quad, NKS), acc);
     }
   }
