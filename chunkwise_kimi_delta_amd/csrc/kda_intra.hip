@@ -140,7 +140,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   float* sA = sLA + 64 * P64;
   uint32_t* sKG = reinterpret_cast<uint32_t*>(sLA);
   static_assert(KD * P64 <= 2 * 64 * P64, "kg^T staging fits in sL and sA");
-  __shared__ float sX[3 * 256];
   __shared__ float sBeta[64];
   // column operands of the off-diagonal levels, later reused for v^T and X^T
   __shared__ __attribute__((aligned(16))) unsigned char sU8[UB];
@@ -555,40 +554,45 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   }
   __syncthreads();
 
-  // ---- off-diagonal blocks of (I+L)^-1, by block distance d
-  {
-    const int jj = lane & 15, i0 = 4 * (lane >> 4);
-    for (int d = 1; d <= 3; ++d) {
-      if (wave <= 3 - d) {
-        const int I = wave + d, J = wave;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int m = J; m < I; ++m) {
-#pragma unroll 4
-          for (int kq = 0; kq < 16; ++kq) {
-            const float av = sA[(16 * m + kq) * P64 + 16 * J + jj];
+  // ---- off-diagonal blocks of (I+L)^-1: A_IJ = -A_II sum_{J<=m<I} L_Im A_mJ.
+  // Wave J forms the blocks of its own block column J (I = J+1 .. 3) in order,
+  // on the fp32 matrix cores (16x16x4 per pass, four passes per 16-wide
+  // reduction).  Pass p of a product gives lane l the reduction index
+  // 4*(l/16) + p, so an accumulator tile (lane l: rows 4*(l/16) .. +3, column
+  // l%16) is, element p, exactly the B operand of pass p: the column blocks
+  // stay in registers and only the diagonal inverses (other waves) and L come
+  // from LDS.
+  if (wave < 3) {
+    const int J = wave;
+    f32x4 col[4];   // col[m] = A_mJ as an accumulator tile (m >= J)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += sL[(16 * I + i0 + e) * P64 + 16 * m + kq] * av;
-          }
-        }
+    for (int m = 0; m < 3; ++m)
+      if (m == J)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sX[wave * 256 + (i0 + e) * 16 + jj] = acc[e];
+        for (int e = 0; e < 4; ++e) col[m][e] = sA[(16 * J + 4 * quad + e) * P64 + 16 * J + r16];
+#pragma unroll
+    for (int I = 1; I < 4; ++I) {
+      if (I <= J) continue;
+      f32x4 x = zero4();
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        if (m < J || m >= I) continue;
+        const f32x4 lrow = *reinterpret_cast<const f32x4*>(&sL[(16 * I + r16) * P64 + 16 * m + 4 * quad]);
+#pragma unroll
+        for (int pss = 0; pss < 4; ++pss) x = __builtin_amdgcn_mfma_f32_16x16x4f32(lrow[pss], col[m][pss], x, 0, 0, 0);
       }
-      __syncthreads();
-      if (wave <= 3 - d) {
-        const int I = wave + d, J = wave;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int kq = 0; kq < 16; ++kq) {
-          const float xv = sX[wave * 256 + kq * 16 + jj];
+      const f32x4 arow = *reinterpret_cast<const f32x4*>(&sA[(16 * I + r16) * P64 + 16 * I + 4 * quad]);
+      f32x4 y = zero4();
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] -= sA[(16 * I + i0 + e) * P64 + 16 * I + kq] * xv;
-        }
+      for (int pss = 0; pss < 4; ++pss) y = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[pss], x[pss], y, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sA[(16 * I + i0 + e) * P64 + 16 * J + jj] = acc[e];
+      for (int e = 0; e < 4; ++e) {
+        col[I][e] = -y[e];
+        sA[(16 * I + 4 * quad + e) * P64 + 16 * J + r16] = -y[e];
       }
-      __syncthreads();
     }
   }
+  __syncthreads();
 
   // ---- u^T = (A diag(beta) v)^T (fp32),  w = A diag(beta) X (token dtype)
   // Both reduction slices are used by every wave: the strictly upper blocks
