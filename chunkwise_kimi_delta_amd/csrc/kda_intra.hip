@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   const bool live = i < C;
 
   // ---- loads, in the order of use (loads complete in order): gate bias and
-  // gate rows first, then k, q, v rows of this lane; beta.  Buffer loads with
+  // gate rows first, then k, q rows of this lane, beta, v rows.  Buffer loads with
   // per-tensor descriptors bounded at the chunk's last valid row: rows past the
   // sequence end read as zeros without a branch, so all loads issue back to
   // back (a conditional load would make the compiler wait for each one).
@@ -185,7 +185,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     for (int ks = 0; ks < NKS; ++ks) load8b<float>(rb, (uint32_t)(32 * ks + 8 * quad) * 4, bias[ks]);
   }
   const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
-  float gl[NKS][8], kx[NKS][8], qx[NKS][8], vx[NVS][8];
+  float gl[NKS][8], kx[NKS][8], qx[NKS][8];
+  // v rows stay as loaded (8 values of the token dtype per slice) until their
+  // transpose: unpacking them here would make the first phase wait for them
+  u32x4 vr[NVS][ES / 2];
   float beta;
   {
     const rsrc_t rg = make_rsrc(static_cast<const IT*>(a.g) + (tok0 * a.Hv + h) * KD, (uint32_t)(C * a.Hv * KD * ES));
@@ -202,12 +205,14 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
       load8b<IT>(rk, ok + (32 * ks + 8 * quad) * ES, kx[ks]);
       load8b<IT>(rq, ok + (32 * ks + 8 * quad) * ES, qx[ks]);
     }
+    beta = load1b<IT>(rbeta, (uint32_t)(i * a.Hv) * ES);
+    __builtin_amdgcn_sched_barrier(0);   // keep beta ahead of the v rows in the queue
     const uint32_t ov = (uint32_t)(i * a.Hv * VD) * ES;
 #pragma unroll
-    for (int vs = 0; vs < NVS; ++vs) load8b<IT>(rv, ov + (32 * vs + 8 * quad) * ES, vx[vs]);
-    beta = load1b<IT>(rbeta, (uint32_t)(i * a.Hv) * ES);
+    for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+      for (int j = 0; j < ES / 2; ++j) vr[vs][j] = buf_load16(rv, ov + (32 * vs + 8 * quad) * ES + 16 * j);
   }
-  if (a.flags & F_SIGMOID) beta = live ? 1.f / (1.f + expf(-beta)) : 0.f;
 
   // ---- gate activation (log2 units), in-wave row prefix sums, norms
   {
@@ -258,6 +263,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) store8(&sTot[wave][32 * ks + 8 * quad], gl[ks]);
   }
+  // beta activation here, not at its load: the gate work above needs only the
+  // gate rows, and waiting on beta means waiting on every load before it
+  if (a.flags & F_SIGMOID) beta = live ? 1.f / (1.f + expf(-beta)) : 0.f;
   if (quad == 0) sBeta[i] = beta;
   __syncthreads();
 
@@ -527,7 +535,15 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
 #pragma unroll
   for (int vs = 0; vs < NVS; ++vs)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sVT[(32 * vs + 8 * quad + e) * PT + i] = from_f<ST>(vx[vs][e]);
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (F32) {
+        sVT[(32 * vs + 8 * quad + e) * PT + i] = from_f<ST>(__uint_as_float(vr[vs][e >> 2][e & 3]));
+      } else {
+        // the stored value is the token's own bf16 (v enters u unscaled)
+        const uint32_t w = vr[vs][0][e >> 1];
+        reinterpret_cast<uint16_t*>(sVT)[(32 * vs + 8 * quad + e) * PT + i] = (uint16_t)((e & 1) ? (w >> 16) : w);
+      }
+    }
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
