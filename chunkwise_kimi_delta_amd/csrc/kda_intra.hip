@@ -217,28 +217,33 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   // ---- gate activation (log2 units), in-wave row prefix sums, norms
   {
     // The flag tests sit outside the element loops (one uniform branch), so
-    // that the per-element work forms one straight-line block.
-    const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;   // max(g, -inf) = g
+    // that the per-element work forms one straight-line block.  Results are in
+    // log2 units: log2(e) * max(g, lb) = max(log2(e) * g, log2(e) * lb), with
+    // the unit change and the zero of rows past the sequence end folded into
+    // one per-row coefficient (lb = -inf without the clamp: max(x, -inf) = x).
+    const float lb2 = !live ? 0.f : (a.flags & F_SAFE) ? a.lower_bound * LOG2E : -INFINITY;
     if (gik) {
+      const float cA = live ? -Aexp * LOG2E : 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float z = gl[ks][e] + bias[ks][e];
           // softplus(z) = max(z, 0) + ln(1 + e^-|z|)
-          gl[ks][e] = fmaxf(-Aexp * (fmaxf(z, 0.f) + LN2 * flog2(1.f + fexp2(-LOG2E * fabsf(z)))), lb);
+          gl[ks][e] = fmaxf(cA * (fmaxf(z, 0.f) + LN2 * flog2(1.f + fexp2(-LOG2E * fabsf(z)))), lb2);
         }
       }
     } else {
+      const float cL = live ? LOG2E : 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gl[ks][e] = fmaxf(gl[ks][e], lb);
+        for (int e = 0; e < 8; ++e) gl[ks][e] = fmaxf(cL * gl[ks][e], lb2);
     }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gl[ks][e] = row_scan16(live ? gl[ks][e] * LOG2E : 0.f);
+      for (int e = 0; e < 8; ++e) gl[ks][e] = row_scan16(gl[ks][e]);
   }
   float rq, rk, dqk;
   {
@@ -274,17 +279,22 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int c0 = 32 * ks + 8 * quad;
-    float t0[8], t1[8], t2[8], t3[8];
-    load8(&sTot[0][c0], t0);
-    load8(&sTot[1][c0], t1);
-    load8(&sTot[2][c0], t2);
-    load8(&sTot[3][c0], t3);
+    // running sum over the waves' totals: the part before this wave is its
+    // offset, the whole is the chunk total
+    float off[8];
+    zero8(off);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float off = (wave > 0 ? t0[e] : 0.f) + (wave > 1 ? t1[e] : 0.f) + (wave > 2 ? t2[e] : 0.f);
-      gl[ks][e] += off;
-      gC[ks][e] = t0[e] + t1[e] + t2[e] + t3[e];
+    for (int w = 0; w < 4; ++w) {
+      float t[8];
+      load8(&sTot[w][c0], t);
+      if (w > 0 && w == wave)   // (wave 0: offset zero)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) off[e] = gC[ks][e];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gC[ks][e] = w == 0 ? t[e] : gC[ks][e] + t[e];
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gl[ks][e] += off[e];
     if (r16 == 0 && wave >= 1) store8(&sRef[wave - 1][c0], gl[ks]);
     if (wave == 0 && r16 == 0) {
       float d[8];
