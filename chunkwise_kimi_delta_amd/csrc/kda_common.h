@@ -45,6 +45,12 @@ __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; retur
 // fp32 -> bf16 hi/lo pairs: hi = RNE(x), lo = RNE(x - hi), so that hi + lo
 // carries ~16 significant bits of x (x - hi is exact in fp32).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two floats -> two bf16 (round to nearest even) in one word, a in the low
+// half: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
   const bf16x2_t h = {(__bf16)a, (__bf16)b};
   const uint32_t hb = __builtin_bit_cast(uint32_t, h);
@@ -95,9 +101,6 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
 }
 // Store 8 floats as 8 consecutive elements of type bf16 (16-byte aligned) or fp32.
 __device__ __forceinline__ void store8(bf16_t* p, const float (&x)[8]) {

@@ -87,6 +87,26 @@ __device__ __forceinline__ f32x4 mma3(const Frag& A, const Frag& B, f32x4 acc) {
   return acc;
 }
 
+// Transposes on the matrix cores.  With B = S_half (32 x 16, one where the
+// reduction index equals 16*half + column), the product A S_half of a row
+// tile A (16 rows x 32 reduction, bf16) is A's columns 16*half .. +15 as an
+// accumulator tile: lane l gets column 16*half + l%16 of rows 4*(l/16) .. +3.
+// Every product term is one bf16 value times 1, so the result is exact.  Two
+// such tiles of consecutive 16-row tiles are the two halves of one operand
+// fragment in the stored lane order (slots 8g .. 8g+3 and 8g+4 .. 8g+7 hold
+// rows 4g .. 4g+3 of the first and of the second tile).
+__device__ __forceinline__ bf16x8 select_operand(int half, int lane) {
+  const int col = 16 * half + (lane & 15), k0 = 8 * (lane >> 4);
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = (k0 + 2 * j == col ? 0x3f80u : 0u) | (k0 + 2 * j + 1 == col ? 0x3f800000u : 0u);
+  return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
+__device__ __forceinline__ u32x2 pack4(const f32x4& v) {
+  return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
 // Eight consecutive elements through a buffer descriptor (zeros past its end).
 template <typename T> __device__ __forceinline__ void load8b(rsrc_t r, uint32_t off, float (&x)[8]);
 template <> __device__ __forceinline__ void load8b<bf16_t>(rsrc_t r, uint32_t off, float (&x)[8]) {
@@ -125,21 +145,20 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   constexpr int NKS = KD / 32, NVS = VD / 32;
   constexpr int P64 = 64 + 4;                      // row stride of sL / sA (floats)
   constexpr int PB = KD + 8;                       // row stride of bf16 column operands
-  constexpr int PT = 64 + 16 / (int)sizeof(ST);    // row stride of v^T / X^T
+  constexpr int PT = 64 + 16 / (int)sizeof(ST);    // row stride of v^T / X^T (fp32 tokens)
   constexpr int NP = F32 ? 2 : 1;                  // bf16 parts of a column operand (hi [, lo])
   constexpr int BOP_BYTES = (32 + 16 + 16) * PB * 2 * NP;
-  constexpr int VX_BYTES = (VD + KD) * PT * (int)sizeof(ST);
+  // v^T / X^T: fp32 tokens as [channel][token] rows; bf16 tokens as operand
+  // fragments (16 channels x 32 tokens, 1 KiB each, stored lane order)
+  constexpr int VX_BYTES = F32 ? (VD + KD) * PT * 4 : (VD + KD) / 16 * 2 * 1024;
   constexpr int UB = BOP_BYTES > VX_BYTES ? BOP_BYTES : VX_BYTES;
 
   __shared__ __attribute__((aligned(16))) float sTot[4][KD];   // per-wave gate totals
   __shared__ __attribute__((aligned(16))) float sRef[3][KD];   // gamma of rows 16, 32, 48
-  // sL (Akk) and sA ((I+L)^-1); before the Akk phase the same span holds kg^T
-  // as (hi | lo << 16) words, [KD][P64]
+  // sL (Akk) and sA ((I+L)^-1)
   __shared__ __attribute__((aligned(16))) float sLA[2 * 64 * P64];
   float* sL = sLA;
   float* sA = sLA + 64 * P64;
-  uint32_t* sKG = reinterpret_cast<uint32_t*>(sLA);
-  static_assert(KD * P64 <= 2 * 64 * P64, "kg^T staging fits in sL and sA");
   __shared__ float sBeta[64];
   // column operands of the off-diagonal levels, later reused for v^T and X^T
   __shared__ __attribute__((aligned(16))) unsigned char sU8[UB];
@@ -149,8 +168,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   bf16_t* b32alo = b32ahi + 16 * PB;
   bf16_t* b32bhi = b32ahi + NP * 16 * PB;          // rows 32..47, reference row 48
   bf16_t* b32blo = b32bhi + 16 * PB;
-  ST* sVT = reinterpret_cast<ST*>(sU8);            // [VD][PT]
-  ST* sXT = sVT + VD * PT;                         // [KD][PT]
+  ST* sVT = reinterpret_cast<ST*>(sU8);            // fp32 tokens: [VD][PT]
+  ST* sXT = sVT + VD * PT;                         //              [KD][PT]
+  u32x4* sVF = reinterpret_cast<u32x4*>(sU8);      // bf16 tokens: fragment (ct, ks) at [(2ct + ks) * 64]
+  u32x4* sXF = sVF + (VD / 16) * 2 * 64;
 
   const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -314,6 +335,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   __syncthreads();
 
   // ---- column operands of levels 64 / 32 (LDS), qg and kg^T (global)
+  const bf16x8 sel[2] = {select_operand(0, lane), select_operand(1, lane)};
   {
     auto put_col = [&](const float* gref, bf16_t* hi, bf16_t* lo, int row) __attribute__((always_inline)) {
 #pragma unroll
@@ -349,38 +371,29 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         store4(qg + frag_off(i, 32 * ks + 8 * quad + 4, NKS), x1);
       }
     }
-    // kg = k * 2^(gamma_C - gamma) as hi/lo pairs, transposed through LDS
+    // kg = k * 2^(gamma_C - gamma) as bf16 hi/lo rows, transposed on the
+    // matrix cores into kg^T fragments (16 channels x 32 tokens): this wave's
+    // 16 tokens are half of fragment (kt, wave / 2), 8 bytes of each lane
+    unsigned char* kgh = rec + RL.kgh;
+    unsigned char* kgl = rec + RL.kgl;
+    const uint32_t kg_off = (uint32_t)((wave >> 1) * 64 + lane) * 16 + (wave & 1) * 8;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+    for (int ks = 0; ks < NKS; ++ks) {
+      float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        uint32_t hi, lo;
-        split2(kx[ks][e] * fexp2(gC[ks][e] - gl[ks][e]), kx[ks][e + 1] * fexp2(gC[ks][e + 1] - gl[ks][e + 1]), hi, lo);
-        const int c = 32 * ks + 8 * quad + e;
-        sKG[c * P64 + i] = (hi & 0xffffu) | (lo << 16);
-        sKG[(c + 1) * P64 + i] = (hi >> 16) | (lo & 0xffff0000u);
+      for (int e = 0; e < 8; ++e) x[e] = kx[ks][e] * fexp2(gC[ks][e] - gl[ks][e]);
+      const Frag f = split8(x);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int kt = 2 * ks + half;
+        const f32x4 th = mfma(f.hi, sel[half], zero4());
+        const f32x4 tl = mfma(f.lo, sel[half], zero4());
+        *reinterpret_cast<u32x2*>(kgh + kt * 2 * 1024 + kg_off) = pack4(th);
+        *reinterpret_cast<u32x2*>(kgl + kt * 2 * 1024 + kg_off) = pack4(tl);
       }
-  }
-  __syncthreads();
-
-  // ---- kg^T fragments to the workspace: 16 channel rows x 32 tokens each,
-  // lane l holds channel 16*kt + l%16 and tokens 32*ks + slots of l/16
-  {
-    u32x4* kgh = reinterpret_cast<u32x4*>(rec + RL.kgh);
-    u32x4* kgl = reinterpret_cast<u32x4*>(rec + RL.kgl);
-    for (int f = wave; f < KD / 8; f += 4) {
-      const int kt = f >> 1, ks = f & 1;
-      const uint32_t* src = sKG + (16 * kt + r16) * P64 + 32 * ks + 4 * quad;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(src);        // tokens 4g .. 4g+3
-      const u32x4 y = *reinterpret_cast<const u32x4*>(src + 16);   // tokens 16+4g .. +3
-      const u32x4 hi = {__builtin_amdgcn_perm(x.y, x.x, 0x05040100u), __builtin_amdgcn_perm(x.w, x.z, 0x05040100u),
-                        __builtin_amdgcn_perm(y.y, y.x, 0x05040100u), __builtin_amdgcn_perm(y.w, y.z, 0x05040100u)};
-      const u32x4 lo = {__builtin_amdgcn_perm(x.y, x.x, 0x07060302u), __builtin_amdgcn_perm(x.w, x.z, 0x07060302u),
-                        __builtin_amdgcn_perm(y.y, y.x, 0x07060302u), __builtin_amdgcn_perm(y.w, y.z, 0x07060302u)};
-      kgh[f * 64 + lane] = hi;
-      kgl[f * 64 + lane] = lo;
     }
   }
+  __syncthreads();
 
   // ---- Akk (L) and Aqk tiles on the matrix cores
   ST* Aqk_out = reinterpret_cast<ST*>(rec + RL.aqk);
@@ -432,7 +445,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         }
       }
     }
-    __syncthreads();   // kg^T staging (sL, sA) fully read
     // diagonal tile output: this lane holds row i = r16, columns 4*quad .. +3,
     // and owns row i's beta, norms and q.k dot
     {
@@ -542,22 +554,43 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   __syncthreads();
 
   // ---- v^T and X^T = (k * 2^gamma)^T into LDS; diagonal 16x16 inverses
+  if constexpr (F32) {
 #pragma unroll
-  for (int vs = 0; vs < NVS; ++vs)
+    for (int vs = 0; vs < NVS; ++vs)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (F32) {
-        sVT[(32 * vs + 8 * quad + e) * PT + i] = from_f<ST>(__uint_as_float(vr[vs][e >> 2][e & 3]));
-      } else {
-        // the stored value is the token's own bf16 (v enters u unscaled)
-        const uint32_t w = vr[vs][0][e >> 1];
-        reinterpret_cast<uint16_t*>(sVT)[(32 * vs + 8 * quad + e) * PT + i] = (uint16_t)((e & 1) ? (w >> 16) : w);
+      for (int e = 0; e < 8; ++e) sVT[(32 * vs + 8 * quad + e) * PT + i] = __uint_as_float(vr[vs][e >> 2][e & 3]);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sXT[(32 * ks + 8 * quad + e) * PT + i] = kx[ks][e] * fexp2(gl[ks][e]);
+  } else {
+    // transposed on the matrix cores into operand fragments (16 channels x 32
+    // tokens); v enters as the token's own bf16 values
+    const uint32_t f_off = (uint32_t)(wave >> 1) * 64 + lane;   // fragment (ct, wave / 2), in u32x4
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs) {
+      const bf16x8 vrow = __builtin_bit_cast(bf16x8, vr[vs][0]);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ct = 2 * vs + half;
+        *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(sVF + ct * 2 * 64 + f_off) + (wave & 1) * 8) =
+            pack4(mfma(vrow, sel[half], zero4()));
       }
     }
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
+    for (int ks = 0; ks < NKS; ++ks) {
+      float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sXT[(32 * ks + 8 * quad + e) * PT + i] = from_f<ST>(kx[ks][e] * fexp2(gl[ks][e]));
+      for (int e = 0; e < 8; ++e) x[e] = kx[ks][e] * fexp2(gl[ks][e]);
+      const bf16x8 xrow = round8(x);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ct = 2 * ks + half;
+        *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(sXF + ct * 2 * 64 + f_off) + (wave & 1) * 8) =
+            pack4(mfma(xrow, sel[half], zero4()));
+      }
+    }
+  }
   if (quad == 0) {
     const int b = wave, jj = r16;
     float x[16];
@@ -625,28 +658,34 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   // of A are zero in LDS, so the products need no per-wave bounds.
   {
     const int I = wave;
+    // rows of A diag(beta): reduction slots in the stored fragment order for
+    // bf16 tokens (slots 8g .. 8g+3: tokens 4g .. 4g+3, 8g+4 .. 8g+7: tokens
+    // 16+4g .. 16+4g+3 of each 32), in natural order for fp32 tokens
     Frag fa[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int j0 = 32 * ks + 8 * quad;
+      const int j0 = F32 ? 32 * ks + 8 * quad : 32 * ks + 4 * quad;
+      const int j1 = F32 ? j0 + 4 : j0 + 16;
       float ar[8], bt[8], x[8];
-      load8(&sA[(16 * I + r16) * P64 + j0], ar);
-      load8(&sBeta[j0], bt);
+      *reinterpret_cast<f32x4*>(&ar[0]) = *reinterpret_cast<const f32x4*>(&sA[(16 * I + r16) * P64 + j0]);
+      *reinterpret_cast<f32x4*>(&ar[4]) = *reinterpret_cast<const f32x4*>(&sA[(16 * I + r16) * P64 + j1]);
+      *reinterpret_cast<f32x4*>(&bt[0]) = *reinterpret_cast<const f32x4*>(&sBeta[j0]);
+      *reinterpret_cast<f32x4*>(&bt[4]) = *reinterpret_cast<const f32x4*>(&sBeta[j1]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = ar[e] * bt[e];
       fa[ks] = split8(x);
     }
-    auto tile = [&](const ST* bsrc, int ct, bool a_left) __attribute__((always_inline)) {
+    auto tile = [&](const ST* bsrc, const u32x4* fsrc, int ct, bool a_left) __attribute__((always_inline)) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const ST* bp = bsrc + (16 * ct + r16) * PT + 32 * ks + 8 * quad;
         if constexpr (F32) {
+          const ST* bp = bsrc + (16 * ct + r16) * PT + 32 * ks + 8 * quad;
           float xb[8];
           load8(reinterpret_cast<const float*>(bp), xb);
           acc = a_left ? mma3(fa[ks], split8(xb), acc) : mma3(split8(xb), fa[ks], acc);
         } else {
-          const bf16x8 b = load_bf16x8(reinterpret_cast<const bf16_t*>(bp));
+          const bf16x8 b = __builtin_bit_cast(bf16x8, fsrc[(2 * ct + ks) * 64 + lane]);
           if (a_left) {
             acc = mfma(fa[ks].hi, b, acc);
             acc = mfma(fa[ks].lo, b, acc);
@@ -661,7 +700,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     float* uT = reinterpret_cast<float*>(rec + RL.ut);
 #pragma unroll
     for (int ct = 0; ct < VD / 16; ++ct) {
-      const f32x4 acc = tile(sVT, ct, true);
+      const f32x4 acc = tile(sVT, sVF, ct, true);
       *reinterpret_cast<f32x4*>(uT + cfrag_off(16 * I + 4 * quad, 16 * ct + r16, VD / 16)) = acc;
     }
     // w^T tiles (X^T rows as the A operand): this lane holds token 16*I + r16,
@@ -669,7 +708,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     ST* wbase = reinterpret_cast<ST*>(rec + RL.w);
 #pragma unroll
     for (int ct = 0; ct < KD / 16; ++ct) {
-      const f32x4 acc = tile(sXT, ct, false);
+      const f32x4 acc = tile(sXT, sXF, ct, false);
       store4(wbase + frag_off(16 * I + r16, 16 * ct + 4 * quad, NKS), acc);
     }
   }
