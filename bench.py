@@ -68,22 +68,25 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def cpu_baseline(p, sample_tokens):
-    """The fp64 oracle on the first `sample_tokens` tokens of every head."""
+def cpu_baseline(p, sample_tokens, repeats):
+    """The fp64 oracle on the first `sample_tokens` tokens of every head, run
+    `repeats` times (the rate is over all runs)."""
     from threadpoolctl import threadpool_limits
 
     import dataclasses
 
     from oracle import kda_oracle as orc
+    sample_tokens = min(sample_tokens, p.T)
     sl = slice(0, sample_tokens)
     sub = dataclasses.replace(p, T=sample_tokens, q=p.q[:, sl], k=p.k[:, sl], v=p.v[:, sl],
                               g=p.g[:, sl], beta=p.beta[:, sl])
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        orc.forward(sub)
+        for _ in range(repeats):
+            orc.forward(sub)
         dt = time.perf_counter() - t0
-    return {"value": sample_tokens * p.B / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {sample_tokens} tokens x all {p.Hv} heads of the workload "
+    return {"value": repeats * sample_tokens * p.B / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens x all {p.Hv} heads of the workload, {repeats} runs "
                       f"({dt:.1f} s, numpy fp64 token recurrence, 1 thread)",
             "host_cpu": platform.processor() or platform.machine(),
             "host_cores_available": len(os.sched_getaffinity(0))}
@@ -152,7 +155,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-repeats", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MB (PMC calibration)")
@@ -247,8 +251,8 @@ def main():
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
     }
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_sample_tokens} tokens ...")
-        res["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_tokens)
+        log(f"cpu baseline: oracle on {args.cpu_sample_tokens} tokens x {args.cpu_repeats} ...")
+        res["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_tokens, args.cpu_repeats)
     print(json.dumps(res), flush=True)
 
 
