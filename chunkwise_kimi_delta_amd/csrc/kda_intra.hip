@@ -407,12 +407,59 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     // the rest of the tile is ignored.  The reference gamma comes from the lane
     // of the reference row by a DPP move (b = 0, 1) or a swizzle (b = 2, 3);
     // the 16 lanes of a DPP row are the 16 rows of the tile.
+    //
+    // Small-decay form.  With the in-kernel gate every g is <= 0, so within
+    // the tile |gamma_r - gamma_8| never exceeds the tile's total decay D.
+    // When D < 112 (log2 units) one reference serves every pair: with
+    // F_i = k_i 2^(gamma_i - gamma_8) and G_j = k_j 2^(gamma_8 - gamma_j), both
+    // below 2^112 in scale, L_ij = beta_i F_i . G_j exactly as at the split
+    // levels (entries with i <= j may overflow and are never read).  Decided
+    // per wave from the tile totals kept for the cumsum.
+    bool one_ref = false;
+    if (gik) {
+      float span = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        float t[8];
+        load8(&sTot[wave][32 * ks + 8 * quad], t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) span = fmaxf(span, -t[e]);
+      }
+      span = fmaxf(span, __shfl_xor(span, 16));
+      span = fmaxf(span, __shfl_xor(span, 32));
+      one_ref = __builtin_amdgcn_readfirstlane(span < 112.f ? 1 : 0) != 0;
+    }
     f32x4 dk[4], dq[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       dk[b] = zero4();
       dq[b] = zero4();
     }
+    if (one_ref) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        float kf[8], kb[8], qf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float g = gl[ks][e];
+          const float d = g - swizzle<0x110>(g);   // gamma_r - gamma_8 (row 8 of the tile)
+          const float f = fexp2(d), fb = fexp2(-d);
+          kf[e] = kx[ks][e] * f;
+          kb[e] = kx[ks][e] * fb;
+          qf[e] = qx[ks][e] * f;
+        }
+        // A = G (rows j), B = F (columns i): this lane gets (i = r16, j = 4*quad + e)
+        if constexpr (F32) {
+          const Frag F = split8(kf), G = split8(kb);
+          dk[0] = mma3(G, F, dk[0]);
+          if (has_q) dq[0] = mma3(G, split8(qf), dq[0]);
+        } else {
+          const bf16x8 F = round8(kf), G = round8(kb);
+          dk[0] = mfma(G, F, dk[0]);
+          if (has_q) dq[0] = mfma(G, round8(qf), dq[0]);
+        }
+      }
+    } else {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -445,6 +492,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         }
       }
     }
+    }
     // diagonal tile output: this lane holds row i = r16, columns 4*quad .. +3,
     // and owns row i's beta, norms and q.k dot
     {
@@ -454,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         const int il = r16, jl = 4 * quad + e;
         float vk = 0.f, vq = 0.f;
         if (il > jl) {
-          const int b = 31 - __clz(il ^ jl);
+          const int b = one_ref ? 0 : 31 - __clz(il ^ jl);   // (small-decay form: all in dk[0], dq[0])
           vk = b == 0 ? dk[0][e] : b == 1 ? dk[1][e] : b == 2 ? dk[2][e] : dk[3][e];
           vq = b == 0 ? dq[0][e] : b == 1 ? dq[1][e] : b == 2 ? dq[2][e] : dq[3][e];
           vk *= beta;

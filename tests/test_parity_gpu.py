@@ -115,6 +115,16 @@ def test_beta_zero_is_pure_decay(gpu_lib):
     fwd_case(gpu_lib, p)
 
 
+def test_small_and_large_decay_heads(gpu_lib):
+    """Head 0 decays slowly (every 16-token tile within the single-reference
+    range of the diagonal tiles), head 1 fast (per-token decays of tens in log2
+    units: the binary split everywhere); both against the oracle."""
+    p = ks.make("layer", T=300, H=2)
+    p.A_log = np.array([math.log(0.05), math.log(64.0)], dtype=np.float32)
+    o, f = fwd_case(gpu_lib, p)
+    assert np.isfinite(np64(o)).all() and np.isfinite(np64(f)).all()
+
+
 def test_varlen_small_with_cache(gpu_lib):
     p = ks.make("varlen", lens=[70, 0, 1, 130, 64, 5], H=3, cache_rows=9, n_invalid=2)
     cache_before = p.h0.copy()
