@@ -42,6 +42,20 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// Four floats -> four e4m3 bytes (round to nearest even), clamped to +-448 so
+// that no value converts to NaN.
+__device__ __forceinline__ uint32_t pack4_fp8(const f32x4& v) {
+  f32x4 c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c[e] = fminf(fmaxf(v[e], -448.f), 448.f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+}
+// acc += A * B on 8-bit e4m3 operands (eight per lane, same lane layout as bf16)
+__device__ __forceinline__ f32x4 mfma_fp8(uint64_t a, uint64_t b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
+}
+
 // fp32 -> bf16 hi/lo pairs: hi = RNE(x), lo = RNE(x - hi), so that hi + lo
 // carries ~16 significant bits of x (x - hi is exact in fp32).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -13,7 +13,8 @@
 //   u = A (beta * v),  w = A (beta * k * 2^gamma)
 //   kg = k * 2^(gamma_C - gamma),  qg = scale * q * 2^gamma,  gdec = 2^gamma_C
 // Workspace per (head, chunk): w, qg [64][K] and Aqk [64][64] in the token
-// dtype; kg^T [K][64], u^T [V][64] and gdec [K] in fp32 (they feed the state
+// dtype; kg^T [K][64] as a bf16 hi part and an e4m3 lo part (together ~13
+// significant bits); u [64][V] and gdec [K] in fp32 (they feed the state
 // update directly).
 //
 // Each wave owns 16 token rows and keeps them in registers in the matrix-core
@@ -373,10 +374,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     }
     // kg = k * 2^(gamma_C - gamma) as bf16 hi/lo rows, transposed on the
     // matrix cores into kg^T fragments (16 channels x 32 tokens): this wave's
-    // 16 tokens are half of fragment (kt, wave / 2), 8 bytes of each lane
+    // 16 tokens are half of fragment (kt, wave / 2), 8 bytes of each lane (hi)
+    // and 4 bytes (lo, stored as e4m3 after scaling by 2^10, clamped to its range)
     unsigned char* kgh = rec + RL.kgh;
     unsigned char* kgl = rec + RL.kgl;
     const uint32_t kg_off = (uint32_t)((wave >> 1) * 64 + lane) * 16 + (wave & 1) * 8;
+    const uint32_t kl_off = (uint32_t)((wave >> 1) * 64 + lane) * 8 + (wave & 1) * 4;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       float x[8];
@@ -389,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         const f32x4 th = mfma(f.hi, sel[half], zero4());
         const f32x4 tl = mfma(f.lo, sel[half], zero4());
         *reinterpret_cast<u32x2*>(kgh + kt * 2 * 1024 + kg_off) = pack4(th);
-        *reinterpret_cast<u32x2*>(kgl + kt * 2 * 1024 + kg_off) = pack4(tl);
+        *reinterpret_cast<uint32_t*>(kgl + kt * 2 * 512 + kl_off) = pack4_fp8(tl * KGL_SCALE);
       }
     }
   }

@@ -14,10 +14,11 @@ enum : uint32_t { F_GATE = 1u, F_SAFE = 2u, F_L2 = 4u, F_SIGMOID = 8u };
 // and read by the state scan.  Sections are 256-byte aligned; a record is one
 // contiguous span so that a whole chunk can be prefetched as a byte range.
 // Matrices are stored as matrix-core fragments in lane order, so that every
-// operand load of the scan is one contiguous 1 KiB (2 KiB for fp32) block:
+// operand load of the scan is one contiguous 1 KiB (2 KiB for fp32, 512 B for
+// the fp8 kgl) block:
 //   w   [64][K]  token dtype   operand fragments, rows = tokens, reduction = channels
 //   kgh [K][64]  bf16          hi part of kg^T, rows = channels, reduction = tokens
-//   kgl [K][64]  bf16          lo part (kg^T - hi rounded to bf16)
+//   kgl [K][64]  fp8 e4m3      lo part, 2^10 (kg^T - hi) (one byte per element)
 //   qg  [64][K]  token dtype   scale * q * 2^gamma, like w (forward only)
 //   aqk [64][64] token dtype   tril(Aqk), rows = tokens, reduction = tokens (forward only)
 //   gd  [K]      fp32          2^gamma_C, the chunk decay (plain vector)
@@ -36,13 +37,16 @@ __host__ __device__ constexpr RecLayout rec_layout(int K, int V, int es, bool fw
   r.w = 0;
   r.kgh = al256(r.w + (size_t)64 * K * es);
   r.kgl = al256(r.kgh + (size_t)K * 64 * 2);
-  r.qg = al256(r.kgl + (size_t)K * 64 * 2);
+  r.qg = al256(r.kgl + (size_t)K * 64);
   r.aqk = al256(r.qg + (fwd ? (size_t)64 * K * es : 0));
   r.gd = al256(r.aqk + (fwd ? (size_t)64 * 64 * es : 0));
   r.ut = al256(r.gd + (size_t)K * 4);
   r.bytes = al256(r.ut + (size_t)V * 64 * 4);
   return r;
 }
+// Scale of the fp8 kgl values (2^10): kg^T - hi is below 2^-8 |kg| <= 2^-8
+// for unit-norm keys, well inside e4m3's range after scaling.
+constexpr float KGL_SCALE = 1024.f;
 __host__ __device__ constexpr int sig32(int x) { return 8 * ((x & 15) >> 2) + 4 * (x >> 4) + (x & 3); }
 // Element offset of (row, red) in a matrix stored as 16 x 32 operand fragments
 // (nrb fragments along the reduction index): 512 elements per fragment, eight

@@ -23,9 +23,10 @@
 // four chunks ahead, so the state waves' own loads (one chunk ahead) are
 // served from L2.
 //
-// Precision.  h and v_new enter the state products as bf16 hi/lo pairs and
-// kg^T comes in hi/lo from the workspace, so each state-feeding product
-// carries ~16 significant bits; the bf16 output uses the hi parts only.
+// Precision.  h and v_new enter the state products as bf16 hi/lo pairs; kg^T
+// comes as a bf16 hi part and an e4m3 lo part (scaled by 2^10), the lo part
+// meeting v_new in e4m3 in an accumulator of its own: kg^T is carried to ~13
+// significant bits, v_new and h to ~16; the bf16 output uses the hi parts only.
 //
 // Summary mode scans the augmented state [S~ | M] (K x (V + K)) from [0 | I]
 // with u = [u | 0] and writes S~ and M ("KDA Context Parallelism (KCP)",
@@ -121,6 +122,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
 
   __shared__ f32x4 sP[NS][4][CT][64];                       // per-wave shares of w h
   __shared__ u32x4 sV[2][4][CT][64];                        // v_new half fragments, by chunk parity
+  __shared__ uint32_t sV8[2][4][CT][64];                    // v_new as e4m3 (for the kg^T lo pass)
   __shared__ bf16x8 sHh[SUM ? 1 : 2][NS][CT][64];           // h fragments (hi) for the output
   __shared__ bf16x8 sHl[(F32 && !SUM) ? 2 : 1][NS][CT][64]; // h fragments (lo), fp32 tokens
 
@@ -150,7 +152,8 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     struct Ops {
       Op<ST> w[4];                    // w rows 16*tt + r16, channels row0 + (slots of lane / 16)
       f32x4 u[TPW][CT];               // u rows 16*(TPW*s + j) + 4*quad .. +3, column v0 + 16*ct + r16
-      bf16x8 kh[2][2], kl[2][2];      // kg^T rows row0 + 16*kt + r16, tokens 32*ks + (slots)
+      bf16x8 kh[2][2];                // kg^T rows row0 + 16*kt + r16, tokens 32*ks + (slots): hi
+      uint64_t kl[2][2];              // the same, lo (e4m3, scaled by 2^10)
       f32x4 gd[2];                    // gdec rows row0 + 16*kt + 4*quad .. +3
     };
     // fragment (tt, K-block s) of w; fragments (2s + kt, ks) of kg^T; u tiles
@@ -161,6 +164,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     const uint32_t o_u = mtile ? (uint32_t)L.bytes
                                : L.ut + (uint32_t)((TPW * s * (VD / 16) + v0 / 16) * 256 + lane * 4) * 4;
     const uint32_t o_kg = (uint32_t)(2 * s * 2 * 512 + lane * 8) * 2;
+    const uint32_t o_kl = (uint32_t)(2 * s * 2 * 512 + lane * 8);   // e4m3 fragments: 512 B
     const uint32_t o_gd = L.gd + (uint32_t)(row0 + 4 * quad) * 4;
     // operands of the first half of a step (w h and v_new) ...
     auto load_a = [&](Ops& f, int c) __attribute__((always_inline)) {
@@ -182,7 +186,8 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
         for (int ks = 0; ks < 2; ++ks) {
           const uint32_t off = o_kg + 1024 * (2 * kt + ks);
           f.kh[kt][ks] = __builtin_bit_cast(bf16x8, buf_load16(r, L.kgh + off));
-          f.kl[kt][ks] = __builtin_bit_cast(bf16x8, buf_load16(r, L.kgl + off));
+          f.kl[kt][ks] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                          r, (int)(L.kgl + o_kl + 512 * (2 * kt + ks)), 0, 0));
         }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) f.gd[kt] = __builtin_bit_cast(f32x4, buf_load16(r, o_gd + 64 * kt));
@@ -255,6 +260,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = cur.u[j][ct][e] - sum[e];
           sV[c & 1][tt][ct][lane] = half_frag(v);
+          sV8[c & 1][tt][ct][lane] = pack4_fp8(v);
         }
       }
       __syncthreads();                                           // B
@@ -262,20 +268,25 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         Frag vb[2];
+        uint64_t v8[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks) {
           vb[ks] = join_halves(sV[c & 1][2 * ks][ct][lane], sV[c & 1][2 * ks + 1][ct][lane]);
+          v8[ks] = (uint64_t)sV8[c & 1][2 * ks][ct][lane] | ((uint64_t)sV8[c & 1][2 * ks + 1][ct][lane] << 32);
+        }
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          f32x4 acc = hs[kt][ct];
+          f32x4 acc = hs[kt][ct], acc8 = zero4();
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[e] *= cur.gd[kt][e];
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             acc = mfma(cur.kh[kt][ks], vb[ks].hi, acc);
-            acc = mfma(cur.kl[kt][ks], vb[ks].hi, acc);
             acc = mfma(cur.kh[kt][ks], vb[ks].lo, acc);
+            acc8 = mfma_fp8(cur.kl[kt][ks], v8[ks], acc8);
           }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += acc8[e] * (1.f / KGL_SCALE);
           hs[kt][ct] = acc;
         }
       }

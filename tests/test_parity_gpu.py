@@ -115,6 +115,14 @@ def test_beta_zero_is_pure_decay(gpu_lib):
     fwd_case(gpu_lib, p)
 
 
+def test_state_keeps_the_kg_lo_part(gpu_lib):
+    """kg^T reaches the state as a bf16 hi part plus an e4m3 lo part (scaled by
+    2^10).  A CPU emulation of exactly that arithmetic puts this case's final
+    state 1.4e-4 from the oracle, and 2.4e-3 with the lo part dropped (or
+    wired wrongly); the bound sits between, well inside the 5e-3 bar."""
+    fwd_case(gpu_lib, ks.make("layer", T=1280, H=2), f_tol=8e-4)
+
+
 def test_small_and_large_decay_heads(gpu_lib):
     """Head 0 decays slowly (every 16-token tile within the single-reference
     range of the diagonal tiles), head 1 fast (per-token decays of tens in log2
