@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   constexpr int PB = KD + 8;                       // row stride of bf16 column operands
   constexpr int PT = 64 + 16 / (int)sizeof(ST);    // row stride of v^T / X^T (fp32 tokens)
   constexpr int NP = F32 ? 2 : 1;                  // bf16 parts of a column operand (hi [, lo])
-  constexpr int BOP_BYTES = (32 + 16 + 16) * PB * 2 * NP;
+  constexpr int BOP_BYTES = (32 + 16 + 16 + 32) * PB * 2 * NP;   // + rows 48..63 as row operand (k, q)
   // v^T / X^T: fp32 tokens as [channel][token] rows; bf16 tokens as operand
   // fragments (16 channels x 32 tokens, 1 KiB each, stored lane order)
   constexpr int VX_BYTES = F32 ? (VD + KD) * PT * 4 : (VD + KD) / 16 * 2 * 1024;
@@ -169,6 +169,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
   bf16_t* b32alo = b32ahi + 16 * PB;
   bf16_t* b32bhi = b32ahi + NP * 16 * PB;          // rows 32..47, reference row 48
   bf16_t* b32blo = b32bhi + 16 * PB;
+  bf16_t* r32khi = b32bhi + NP * 16 * PB;          // rows 48..63 against reference row 48 (row operand)
+  bf16_t* r32klo = r32khi + 16 * PB;
+  bf16_t* r32qhi = r32khi + NP * 16 * PB;          // the same rows of q
+  bf16_t* r32qlo = r32qhi + 16 * PB;
   ST* sVT = reinterpret_cast<ST*>(sU8);            // fp32 tokens: [VD][PT]
   ST* sXT = sVT + VD * PT;                         //              [KD][PT]
   u32x4* sVF = reinterpret_cast<u32x4*>(sU8);      // bf16 tokens: fragment (ct, ks) at [(2ct + ks) * 64]
@@ -282,7 +286,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     skk += __shfl_xor(skk, 16); skk += __shfl_xor(skk, 32);
     sqk += __shfl_xor(sqk, 16); sqk += __shfl_xor(sqk, 32);
     const bool l2 = a.flags & F_L2;
-    rq = l2 ? 1.f / sqrtf(sqq + a.eps) : 1.f;
+    // the attention scale rides on q's normalisation (q enters only Aqk and qg)
+    rq = a.scale * (l2 ? 1.f / sqrtf(sqq + a.eps) : 1.f);
     rk = l2 ? 1.f / sqrtf(skk + a.eps) : 1.f;
     dqk = sqk;
   }
@@ -318,12 +323,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) gl[ks][e] += off[e];
     if (r16 == 0 && wave >= 1) store8(&sRef[wave - 1][c0], gl[ks]);
-    if (wave == 0 && r16 == 0) {
-      float d[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) d[e] = fexp2(gC[ks][e]);
-      store8(reinterpret_cast<float*>(rec + RL.gd) + c0, d);
-    }
   }
   // normalised rows
 #pragma unroll
@@ -355,9 +354,46 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         }
       }
     };
+    if (wave == 3 && r16 == 0) {   // the chunk decay 2^gamma_C (wave 3 builds no column operand)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        float d[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e] = fexp2(gC[ks][e]);
+        store8(reinterpret_cast<float*>(rec + RL.gd) + 32 * ks + 8 * quad, d);
+      }
+    }
     if (wave <= 1) put_col(sRef[1], b64hi, b64lo, i);
     if (wave == 0) put_col(sRef[0], b32ahi, b32alo, i);
     if (wave == 2) put_col(sRef[2], b32bhi, b32blo, i - 32);
+    if (wave == 3) {
+      // rows 48..63 against reference row 48 (factor 2^(gamma_i - gamma_48) <= 1),
+      // k and q: the level-32 tile (3, 2) is formed by wave 0, idle there
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int c0 = 32 * ks + 8 * quad;
+        float gr[8], kv[8], qv[8];
+        load8(sRef[2] + c0, gr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = fexp2(gl[ks][e] - gr[e]);
+          kv[e] = kx[ks][e] * f;
+          qv[e] = qx[ks][e] * f;
+        }
+        if constexpr (F32) {
+          const Frag fk = split8(kv), fq = split8(qv);
+          *reinterpret_cast<bf16x8*>(r32khi + r16 * PB + c0) = fk.hi;
+          *reinterpret_cast<bf16x8*>(r32klo + r16 * PB + c0) = fk.lo;
+          if (has_q) {
+            *reinterpret_cast<bf16x8*>(r32qhi + r16 * PB + c0) = fq.hi;
+            *reinterpret_cast<bf16x8*>(r32qlo + r16 * PB + c0) = fq.lo;
+          }
+        } else {
+          *reinterpret_cast<bf16x8*>(r32khi + r16 * PB + c0) = round8(kv);
+          if (has_q) *reinterpret_cast<bf16x8*>(r32qhi + r16 * PB + c0) = round8(qv);
+        }
+      }
+    }
     if (has_q) {
       ST* qg = reinterpret_cast<ST*>(rec + RL.qg);
 #pragma unroll
@@ -365,8 +401,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         f32x4 x0, x1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x0[e] = a.scale * qx[ks][e] * fexp2(gl[ks][e]);
-          x1[e] = a.scale * qx[ks][e + 4] * fexp2(gl[ks][e + 4]);
+          x0[e] = qx[ks][e] * fexp2(gl[ks][e]);
+          x1[e] = qx[ks][e + 4] * fexp2(gl[ks][e + 4]);
         }
         store4(qg + frag_off(i, 32 * ks + 8 * quad, NKS), x0);
         store4(qg + frag_off(i, 32 * ks + 8 * quad + 4, NKS), x1);
@@ -509,9 +545,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
           vk = b == 0 ? dk[0][e] : b == 1 ? dk[1][e] : b == 2 ? dk[2][e] : dk[3][e];
           vq = b == 0 ? dq[0][e] : b == 1 ? dq[1][e] : b == 2 ? dq[2][e] : dq[3][e];
           vk *= beta;
-          vq *= a.scale;
         } else if (il == jl) {
-          vq = a.scale * rq * rk * dqk;
+          vq = rq * rk * dqk;
         }
         vk4[e] = vk;
         vq4[e] = vq;
@@ -519,21 +554,22 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
       *reinterpret_cast<f32x4*>(&sL[i * P64 + 16 * wave + 4 * quad]) = vk4;
       if (has_q) store4(Aqk_out + frag_off(i, 16 * wave + 4 * quad, 2), vq4);
     }
-    // Off-diagonal tiles: this wave's rows (one row operand per reference,
-    // shared by the column tiles it meets) against column operands in LDS.
-    // Level 64: tiles 2, 3 against 0, 1 (reference row 32) -> acc[0], acc[1];
-    // level 32: tile 1 against 0 (row 16), tile 3 against 2 (row 48) -> acc[2].
-    if (wave >= 1) {
+    // Off-diagonal tiles: row operands (one per reference, shared by the column
+    // tiles it meets) against column operands in LDS.  Level 64: tiles 2, 3
+    // against 0, 1 (reference row 32) -> acc[0], acc[1], waves 2 and 3; level 32:
+    // tile 1 against 0 (row 16) -> acc[2], wave 1, and tile 3 against 2 (row 48)
+    // by wave 0 from the row operand wave 3 left in LDS.
+    {
       f32x4 ak[3], aq[3];
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         ak[j] = zero4();
         aq[j] = zero4();
       }
-      const bool l64 = wave >= 2, l32 = (wave & 1) != 0;
-      const float* gref32 = wave == 1 ? sRef[0] : sRef[2];
-      const bf16_t* c32hi = wave == 1 ? b32ahi : b32bhi;
-      const bf16_t* c32lo = wave == 1 ? b32alo : b32blo;
+      const bool l64 = wave >= 2, l32 = wave == 1;
+      const float* gref32 = sRef[0];
+      const bf16_t* c32hi = b32ahi;
+      const bf16_t* c32lo = b32alo;
       auto row_op = [&](const float* gref, int ks, Frag& R, bf16x8& Rq, Frag& Rqf) __attribute__((always_inline)) {
         const int c0 = 32 * ks + 8 * quad;
         float gr[8], kv[8], qv[8];
@@ -581,22 +617,38 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
           row_op(gref32, ks, R, Rq, Rqf);
           tile(R, Rq, Rqf, c32hi, c32lo, 0, ks, ak[2], aq[2]);
         }
+        if (wave == 0) {
+          const int c0 = 32 * ks + 8 * quad;
+          R.hi = load_bf16x8(r32khi + r16 * PB + c0);
+          if constexpr (F32) {
+            R.lo = load_bf16x8(r32klo + r16 * PB + c0);
+            if (has_q) {
+              Rqf.hi = load_bf16x8(r32qhi + r16 * PB + c0);
+              Rqf.lo = load_bf16x8(r32qlo + r16 * PB + c0);
+            }
+          } else if (has_q) {
+            Rq = load_bf16x8(r32qhi + r16 * PB + c0);
+          }
+          tile(R, Rq, Rqf, b32bhi, b32blo, 0, ks, ak[2], aq[2]);
+        }
       }
-      auto put = [&](int J, const f32x4& akk, const f32x4& aqk) __attribute__((always_inline)) {
+      // tile J of row tile `row / 16` (row = this lane's row of it), scaled
+      auto put = [&](int J, int row, float brow, const f32x4& akk, const f32x4& aqk) __attribute__((always_inline)) {
         f32x4 vk4, vq4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          vk4[e] = beta * akk[e];
-          vq4[e] = a.scale * aqk[e];
+          vk4[e] = brow * akk[e];
+          vq4[e] = aqk[e];
         }
-        *reinterpret_cast<f32x4*>(&sL[i * P64 + 16 * J + 4 * quad]) = vk4;
-        if (has_q) store4(Aqk_out + frag_off(i, 16 * J + 4 * quad, 2), vq4);
+        *reinterpret_cast<f32x4*>(&sL[row * P64 + 16 * J + 4 * quad]) = vk4;
+        if (has_q) store4(Aqk_out + frag_off(row, 16 * J + 4 * quad, 2), vq4);
       };
       if (l64) {
-        put(0, ak[0], aq[0]);
-        put(1, ak[1], aq[1]);
+        put(0, i, beta, ak[0], aq[0]);
+        put(1, i, beta, ak[1], aq[1]);
       }
-      if (l32) put(wave - 1, ak[2], aq[2]);
+      if (l32) put(0, i, beta, ak[2], aq[2]);
+      if (wave == 0) put(2, 48 + r16, sBeta[48 + r16], ak[2], aq[2]);
     }
     if (has_q) {  // upper-triangle tiles of this row tile are zero
       for (int J = wave + 1; J < 4; ++J) store4(Aqk_out + frag_off(i, 16 * J + 4 * quad, 2), zero4());
