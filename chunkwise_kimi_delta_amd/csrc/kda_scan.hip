@@ -21,7 +21,8 @@
 //      output waves form o from the same h and v_new fragments.
 // The output waves run their loads two chunks ahead and touch the workspace
 // four chunks ahead, so the state waves' own loads (one chunk ahead) are
-// served from L2.
+// served from L2; they store chunk c's output one step later, between the
+// barriers of chunk c + 1, where they would otherwise wait.
 //
 // Precision.  h and v_new enter the state products as bf16 hi/lo pairs; kg^T
 // comes as a bf16 hi part and an e4m3 lo part (scaled by 2^10), the lo part
@@ -363,7 +364,24 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
       return buf_load4(make_rsrc(recs + (size_t)min(c, nck - 1) * L.bytes, (uint32_t)L.bytes), toff);
     };
     ST* op = static_cast<ST*>(a.o);
-    // Each step loads chunk c + 2 into `ld` and forms chunk c from `use`.
+    // Chunk c's output tiles wait in registers and are stored between the
+    // barriers A(c+1) and B(c+1), where this wave would otherwise sit idle for
+    // the state waves' reduction: a store that waits for a slot in the memory
+    // queue then delays no barrier.
+    f32x4 pend[TPO][CT];
+    auto flush = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < TPO; ++j)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int t = 16 * (TPO * ow + j) + r16;
+          if (t < len - c * BT)
+            store4(op + (tok0s + (int64_t)c * BT + t) * (int64_t)(a.Hv * VD) + (int64_t)h * VD + v0 + 16 * ct + 4 * quad,
+                   pend[j][ct]);
+        }
+    };
+    // Each step loads chunk c + 2 into `ld`, stores chunk c - 1 and forms
+    // chunk c from `use`.
     uint32_t pf[TOUCH_AHEAD - 1];
     auto ostep = [&](OF& ld, const OF& use, int c) __attribute__((always_inline)) {
       load(ld, min(c + OPF, nck - 1));
@@ -373,6 +391,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
       pf[TOUCH_AHEAD - 2] = touch(c + TOUCH_AHEAD);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();                                           // A(c)
+      if (c > 0) flush(c - 1);
       __syncthreads();                                           // B(c)
       const int b = c & 1;
 #pragma unroll
@@ -397,10 +416,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
           // (the strictly upper blocks of Aqk are stored as zeros)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) acc = mma_out(vf[ks].hi, F32 ? vf[ks].lo : vf[ks].hi, use.aq[j][ks], acc);
-          const int t = 16 * tt + r16;
-          if (t < len - c * BT)
-            store4(op + (tok0s + (int64_t)c * BT + t) * (int64_t)(a.Hv * VD) + (int64_t)h * VD + v0 + 16 * ct + 4 * quad,
-                   acc);
+          pend[j][ct] = acc;
         }
       }
     };
@@ -418,6 +434,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
         for (int i = 0; i <= OPF; ++i)
           if (c + i < nck) ostep(f[(i + OPF) % (OPF + 1)], f[i], c + i);
       }
+      flush(nck - 1);
 #pragma unroll
       for (int i = 0; i < TOUCH_AHEAD - 1; ++i) asm volatile("; prefetch sink %0" ::"v"(pf[i]));
     }
