@@ -411,11 +411,14 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     // kg = k * 2^(gamma_C - gamma) as bf16 hi/lo rows, transposed on the
     // matrix cores into kg^T fragments (16 channels x 32 tokens): this wave's
     // 16 tokens are half of fragment (kt, wave / 2), 8 bytes of each lane (hi)
-    // and 4 bytes (lo, stored as e4m3 after scaling by 2^10, clamped to its range)
+    // and 4 bytes (lo, as e4m3 after scaling by 2^10, clamped to its range).
+    // The lo bytes of the four waves are gathered in LDS (the inverse's space,
+    // unused until then) and stored as whole 16-byte lane words after the barrier.
     unsigned char* kgh = rec + RL.kgh;
-    unsigned char* kgl = rec + RL.kgl;
     const uint32_t kg_off = (uint32_t)((wave >> 1) * 64 + lane) * 16 + (wave & 1) * 8;
-    const uint32_t kl_off = (uint32_t)((wave >> 1) * 64 + lane) * 8 + (wave & 1) * 4;
+    static_assert(KD * 64 <= 64 * P64 * 4, "the staged kg^T lo bytes fit the inverse's LDS");
+    unsigned char* kstage = reinterpret_cast<unsigned char*>(sA);
+    const uint32_t kl_off = (uint32_t)lane * 16 + (wave >> 1) * 8 + (wave & 1) * 4;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       float x[8];
@@ -428,11 +431,20 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
         const f32x4 th = mfma(f.hi, sel[half], zero4());
         const f32x4 tl = mfma(f.lo, sel[half], zero4());
         *reinterpret_cast<u32x2*>(kgh + kt * 2 * 1024 + kg_off) = pack4(th);
-        *reinterpret_cast<uint32_t*>(kgl + kt * 2 * 512 + kl_off) = pack4_fp8(tl * KGL_SCALE);
+        *reinterpret_cast<uint32_t*>(kstage + kt * 1024 + kl_off) = pack4_fp8(tl * KGL_SCALE);
       }
     }
   }
   __syncthreads();
+
+  // kg^T lo part: channel tiles KD / 64 * wave .. of the staged bytes, one
+  // contiguous 1 KiB store each
+#pragma unroll
+  for (int j = 0; j < KD / 64; ++j) {
+    const int kt = KD / 64 * wave + j;
+    *reinterpret_cast<u32x4*>(rec + RL.kgl + kt * 1024 + lane * 16) =
+        *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(sA) + kt * 1024 + lane * 16);
+  }
 
   // ---- Akk (L) and Aqk tiles on the matrix cores
   ST* Aqk_out = reinterpret_cast<ST*>(rec + RL.aqk);

@@ -14,11 +14,14 @@ enum : uint32_t { F_GATE = 1u, F_SAFE = 2u, F_L2 = 4u, F_SIGMOID = 8u };
 // and read by the state scan.  Sections are 256-byte aligned; a record is one
 // contiguous span so that a whole chunk can be prefetched as a byte range.
 // Matrices are stored as matrix-core fragments in lane order, so that every
-// operand load of the scan is one contiguous 1 KiB (2 KiB for fp32, 512 B for
-// the fp8 kgl) block:
+// operand load of the scan is one contiguous 1 KiB (2 KiB for fp32) block; the
+// fp8 kgl keeps the two token blocks of a channel tile side by side per lane
+// (8 bytes each), so one 1 KiB load fetches both:
 //   w   [64][K]  token dtype   operand fragments, rows = tokens, reduction = channels
 //   kgh [K][64]  bf16          hi part of kg^T, rows = channels, reduction = tokens
-//   kgl [K][64]  fp8 e4m3      lo part, 2^10 (kg^T - hi) (one byte per element)
+//   kgl [K][64]  fp8 e4m3      lo part, 2^10 (kg^T - hi) (one byte per element;
+//                              channel tile kt, lane l, token block tb at
+//                              1024 kt + 16 l + 8 tb)
 //   qg  [64][K]  token dtype   scale * q * 2^gamma, like w (forward only)
 //   aqk [64][64] token dtype   tril(Aqk), rows = tokens, reduction = tokens (forward only)
 //   gd  [K]      fp32          2^gamma_C, the chunk decay (plain vector)

@@ -165,7 +165,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     const uint32_t o_u = mtile ? (uint32_t)L.bytes
                                : L.ut + (uint32_t)((TPW * s * (VD / 16) + v0 / 16) * 256 + lane * 4) * 4;
     const uint32_t o_kg = (uint32_t)(2 * s * 2 * 512 + lane * 8) * 2;
-    const uint32_t o_kl = (uint32_t)(2 * s * 2 * 512 + lane * 8);   // e4m3 fragments: 512 B
+    const uint32_t o_kl = (uint32_t)(2 * s * 1024 + lane * 16);     // e4m3: both token blocks per lane
     const uint32_t o_gd = L.gd + (uint32_t)(row0 + 4 * quad) * 4;
     // operands of the first half of a step (w h and v_new) ...
     auto load_a = [&](Ops& f, int c) __attribute__((always_inline)) {
@@ -182,14 +182,14 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     auto load_b = [&](Ops& f, int c) __attribute__((always_inline)) {
       const rsrc_t r = make_rsrc(recs + (size_t)c * L.bytes, (uint32_t)L.bytes);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const uint32_t off = o_kg + 1024 * (2 * kt + ks);
-          f.kh[kt][ks] = __builtin_bit_cast(bf16x8, buf_load16(r, L.kgh + off));
-          f.kl[kt][ks] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                                          r, (int)(L.kgl + o_kl + 512 * (2 * kt + ks)), 0, 0));
-        }
+        for (int ks = 0; ks < 2; ++ks)
+          f.kh[kt][ks] = __builtin_bit_cast(bf16x8, buf_load16(r, L.kgh + o_kg + 1024 * (2 * kt + ks)));
+        const u32x4 l = buf_load16(r, L.kgl + o_kl + 1024 * kt);
+        f.kl[kt][0] = (uint64_t)l.y << 32 | l.x;
+        f.kl[kt][1] = (uint64_t)l.w << 32 | l.z;
+      }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) f.gd[kt] = __builtin_bit_cast(f32x4, buf_load16(r, o_gd + 64 * kt));
     };
