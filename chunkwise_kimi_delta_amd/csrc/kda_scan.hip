@@ -100,6 +100,13 @@ __device__ __forceinline__ Frag join_halves(const u32x4& a, const u32x4& b) {
   return f;
 }
 
+// Lane K of each 16-lane row, broadcast to the row (DPP row_newbcast; every
+// lane active).
+template <int K>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + K, 0xf, 0xf, false));
+}
+
 constexpr int TOUCH_AHEAD = 4;   // chunks between an L2 touch and its chunk's loads
 constexpr int SPF = 1;           // state waves: chunks between an operand load and its use
 constexpr int OPF = 2;           // output waves: the same
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
       f32x4 u[TPW][CT];               // u rows 16*(TPW*s + j) + 4*quad .. +3, column v0 + 16*ct + r16
       bf16x8 kh[2][2];                // kg^T rows row0 + 16*kt + r16, tokens 32*ks + (slots): hi
       uint64_t kl[2][2];              // the same, lo (e4m3, scaled by 2^10)
-      f32x4 gd[2];                    // gdec rows row0 + 16*kt + 4*quad .. +3
+      float gd;                       // gdec row row0 + 16*((r16 >> 2) & 1) + 4*quad + (r16 & 3)
     };
     // fragment (tt, K-block s) of w; fragments (2s + kt, ks) of kg^T; u tiles
     // (TPW*s + j, v0/16 + ct).  M columns (summary mode) see u = 0: their
@@ -166,7 +173,9 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
                                : L.ut + (uint32_t)((TPW * s * (VD / 16) + v0 / 16) * 256 + lane * 4) * 4;
     const uint32_t o_kg = (uint32_t)(2 * s * 2 * 512 + lane * 8) * 2;
     const uint32_t o_kl = (uint32_t)(2 * s * 1024 + lane * 16);     // e4m3: both token blocks per lane
-    const uint32_t o_gd = L.gd + (uint32_t)(row0 + 4 * quad) * 4;
+    // (one gdec row per lane: lanes 0..7 of each 16-lane row hold the eight
+    // rows that row's accumulator tiles need, handed out by DPP broadcasts)
+    const uint32_t o_gd = L.gd + (uint32_t)(row0 + 16 * ((r16 >> 2) & 1) + 4 * quad + (r16 & 3)) * 4;
     // operands of the first half of a step (w h and v_new) ...
     auto load_a = [&](Ops& f, int c) __attribute__((always_inline)) {
       const rsrc_t r = make_rsrc(recs + (size_t)c * L.bytes, (uint32_t)L.bytes);
@@ -190,8 +199,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
         f.kl[kt][0] = (uint64_t)l.y << 32 | l.x;
         f.kl[kt][1] = (uint64_t)l.w << 32 | l.z;
       }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) f.gd[kt] = __builtin_bit_cast(f32x4, buf_load16(r, o_gd + 64 * kt));
+      f.gd = __uint_as_float(buf_load4(r, o_gd));
     };
     auto load = [&](Ops& f, int c) __attribute__((always_inline)) {
       load_a(f, c);
@@ -278,8 +286,10 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           f32x4 acc = hs[kt][ct], acc8 = zero4();
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] *= cur.gd[kt][e];
+          acc[0] *= kt ? row_bcast<4>(cur.gd) : row_bcast<0>(cur.gd);
+          acc[1] *= kt ? row_bcast<5>(cur.gd) : row_bcast<1>(cur.gd);
+          acc[2] *= kt ? row_bcast<6>(cur.gd) : row_bcast<2>(cur.gd);
+          acc[3] *= kt ? row_bcast<7>(cur.gd) : row_bcast<3>(cur.gd);
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             acc = mfma(cur.kh[kt][ks], vb[ks].hi, acc);
@@ -334,6 +344,8 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     // output wave ow forms token tiles TPO*ow .. TPO*ow + TPO - 1.  Chunk c's
     // output is formed between the state waves' barriers B(c) and A(c+1).
     const int ow = wave - NS;
+    const int owu = __builtin_amdgcn_readfirstlane(ow);   // uniform: the Aqk block tests are scalar branches
+    auto aqk_live = [](int tt, int ks) { return 32 * ks <= 16 * tt + 15; };
     struct OF {
       Op<ST> q[TPO][NS];    // qg rows 16*(TPO*ow + j) + r16, channels 32*kb + (slots of lane / 16)
       Op<ST> aq[TPO][2];    // Aqk rows 16*(TPO*ow + j) + r16, tokens 32*ks + (slots)
@@ -349,7 +361,12 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
 #pragma unroll
         for (int kb = 0; kb < NS; ++kb) f.q[j][kb].load(r, o_q + FW * (NS * j + kb));
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) f.aq[j][ks].load(r, o_a + FW * (2 * j + ks));
+        for (int ks = 0; ks < 2; ++ks) {
+          // token block ks of Aqk rows 16*tt .. +15 is zero when it lies wholly
+          // above the diagonal: not loaded, and its product skipped
+          if (aqk_live(TPO * owu + j, ks)) f.aq[j][ks].load(r, o_a + FW * (2 * j + ks));
+          else f.aq[j][ks] = Op<ST>{};
+        }
       }
     };
     // L2 warm-up: this tile touches its share of the 128-byte lines of the
@@ -408,14 +425,16 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
         for (int ks = 0; ks < 2; ++ks) vf[ks] = join_halves(sV[b][2 * ks][ct][lane], sV[b][2 * ks + 1][ct][lane]);
 #pragma unroll
         for (int j = 0; j < TPO; ++j) {
-          // o^T tile: this lane holds token 16*tt + r16, columns v0 + 16*ct + 4*quad .. +3
-          const int tt = TPO * ow + j;
+          // o^T tile tt = TPO*ow + j: this lane holds token 16*tt + r16, columns
+          // v0 + 16*ct + 4*quad .. +3
           f32x4 acc = zero4();
 #pragma unroll
           for (int kb = 0; kb < NS; ++kb) acc = mma_out(hh[kb], hl[kb], use.q[j][kb], acc);
-          // (the strictly upper blocks of Aqk are stored as zeros)
+          // (the strictly upper 16 x 16 blocks of Aqk are stored as zeros; whole
+          // zero 32-token blocks are skipped)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) acc = mma_out(vf[ks].hi, F32 ? vf[ks].lo : vf[ks].hi, use.aq[j][ks], acc);
+          for (int ks = 0; ks < 2; ++ks)
+            if (aqk_live(TPO * owu + j, ks)) acc = mma_out(vf[ks].hi, F32 ? vf[ks].lo : vf[ks].hi, use.aq[j][ks], acc);
           pend[j][ct] = acc;
         }
       }
