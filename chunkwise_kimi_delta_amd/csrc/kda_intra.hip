@@ -210,7 +210,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) load8b<float>(rb, (uint32_t)(32 * ks + 8 * quad) * 4, bias[ks]);
   }
-  const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
   float gl[NKS][8], kx[NKS][8], qx[NKS][8];
   // v rows stay as loaded (8 values of the token dtype per slice) until their
   // transpose: unpacking them here would make the first phase wait for them
@@ -239,6 +238,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
 #pragma unroll
       for (int j = 0; j < ES / 2; ++j) vr[vs][j] = buf_load16(rv, ov + (32 * vs + 8 * quad) * ES + 16 * j);
   }
+  // (after the row loads: its scalar read and exponential would hold them back)
+  __builtin_amdgcn_sched_barrier(0);
+  const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
 
   // ---- gate activation (log2 units), in-wave row prefix sums, norms
   {
