@@ -110,10 +110,7 @@ __device__ __forceinline__ float row_bcast(float x) {
 constexpr int TOUCH_AHEAD = 4;   // chunks between an L2 touch and its chunk's loads
 constexpr int SPF = 1;           // state waves: chunks between an operand load and its use
 constexpr int OPF = 2;           // output waves: the same
-#ifndef KDA_SCAN_NOW
-#define KDA_SCAN_NOW 2
-#endif
-constexpr int NOW = KDA_SCAN_NOW;  // output waves (forward mode)
+constexpr int NOW = 2;             // output waves (forward mode)
 constexpr int TPO = 4 / NOW;       // token tiles per output wave
 
 template <int KD, int VD, typename ST, bool SUM, int CT>
@@ -494,11 +491,7 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
 hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s) {
   if (a.seq.N == 0 || a.Hv == 0) return hipSuccess;
   const int VA = a.summary ? V + K : V;
-#ifdef KDA_SCAN_CT
-  const int CTsel = dtype == 1 ? KDA_SCAN_CT : 1;
-#else
-  const int CTsel = 1;
-#endif
+  constexpr int CTsel = 1;   // 16-column tiles (wider tiles leave CUs idle at the layer)
   const long nb = (long)(VA / (16 * CTsel)) * a.Hv * a.seq.N;
   if (nb > 0x7fffffffL) return hipErrorInvalidValue;
   // K/32 state waves, plus the output waves in forward mode
@@ -514,10 +507,6 @@ hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s
     KDA_SCAN_CASE(64, 64, bf16_t, 1)
     KDA_SCAN_CASE(128, 64, bf16_t, 1)
     KDA_SCAN_CASE(64, 128, bf16_t, 1)
-#ifdef KDA_SCAN_CT
-    KDA_SCAN_CASE(128, 128, bf16_t, 2)
-    KDA_SCAN_CASE(128, 128, bf16_t, 4)
-#endif
   } else {
     KDA_SCAN_CASE(64, 64, float, 1)
     KDA_SCAN_CASE(64, 128, float, 1)
