@@ -43,8 +43,12 @@ to themselves) live in ``tests/test_oracle_pins.py``: closed forms for beta=0
 and for linear attention with orthonormal keys, last-write-wins, a scalar
 closed form, brute-force matrix products at tiny sizes, linearity, L2Norm
 scale invariance, gate closed forms, packed == separate runs, grouped heads ==
-repeated heads, and the summary identities (affinity, split invariance,
-non-commutativity, M not droppable).  No function here is "parity unpinned".
+repeated heads, the summary identities (affinity, split invariance,
+non-commutativity, M not droppable); the in-kernel preprocessing route of
+``forward`` and ``segment_summary`` (gate, safe-gate clamp, sigmoid, L2Norm,
+per-head parameters, grouped heads) against the bare recurrence fed inputs
+prepared element by element with the scalar math library; and the ``heads=``
+and ``t_max=`` subsets against slices of the full run.
 """
 from __future__ import annotations
 

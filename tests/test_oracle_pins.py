@@ -315,3 +315,166 @@ def test_merge_order_matters_and_transition_cannot_be_dropped():
 def test_compare_metric():
     c = orc.compare(np.array([1.0, 2.1]), np.array([1.0, 2.0]))
     assert abs(c["err_max"] - 0.05) < 1e-12 and c["nonfinite"] == 0
+
+
+# ------------------------------------------- in-kernel preprocessing routes
+def _hand_gate(g_raw, A_log, dt_bias, safe, lb):
+    """-exp(A_log[h]) * softplus(g_raw + dt_bias[h, c]) element by element with
+    the scalar math library (softplus(x) = log(1 + e^x)), then the optional
+    clamp at lb ("Hyper-Parallel Chunk KDA", section 4: use_gate_in_kernel,
+    a_log, dt_bias, safe_gate, lower_bound)."""
+    out = np.empty(g_raw.shape)
+    for idx in np.ndindex(*g_raw.shape):
+        h, c = idx[-2], idx[-1]
+        x = float(g_raw[idx]) + (0.0 if dt_bias is None else float(dt_bias[h, c]))
+        sp = x + math.log1p(math.exp(-x)) if x > 0 else math.log1p(math.exp(x))
+        val = -math.exp(float(A_log[h])) * sp
+        out[idx] = max(val, lb) if safe else val
+    return out
+
+
+def _hand_sigmoid(b):
+    return np.vectorize(lambda x: 1.0 / (1.0 + math.exp(-float(x))))(b)
+
+
+def _hand_l2(x, eps):
+    out = np.empty(x.shape)
+    for idx in np.ndindex(*x.shape[:-1]):
+        row = [float(e) for e in x[idx]]
+        r = 1.0 / math.sqrt(sum(e * e for e in row) + eps)
+        out[idx] = [e * r for e in row]
+    return out
+
+
+def _gate_prob(safe, seed=30, H=3, Hk=None, T=11, K=4, V=3, layout="bsnd", **kw):
+    """A problem on the in-kernel route: raw gate, raw beta logits, raw q/k.
+    Every head has its own A_log and dt_bias, so a mis-indexed head fails."""
+    r = RNG(seed)
+    Hk = Hk or H
+    shp = (1, T) if layout == "bsnd" else (T,)
+    return _prob(T=T, H=H, K=K, V=V, seed=seed, layout=layout,
+                 Hk=Hk, q=r.standard_normal(shp + (Hk, K)) * 2.0,
+                 k=r.standard_normal(shp + (Hk, K)) * 0.7,
+                 g=r.standard_normal(shp + (H, K)) * 1.5,
+                 beta=r.standard_normal(shp + (H,)) * 2.0,
+                 A_log=np.log(np.array([0.3, 1.7, 9.0, 2.2, 5.5, 0.8][:H])),
+                 dt_bias=r.standard_normal((H, K)) * 0.5,
+                 gate_in_kernel=True, safe_gate=safe, lower_bound=-1.2, l2norm=True,
+                 beta_sigmoid=True, eps=1e-6, **kw)
+
+
+@pytest.mark.parametrize("safe", [False, True])
+def test_forward_in_kernel_route_equals_hand_prepared_recurrence(safe):
+    """forward() on raw inputs with the gate, sigmoid, L2Norm (and clamp) flags
+    equals the bare recurrence fed inputs prepared by hand, head by head."""
+    p = _gate_prob(safe)
+    X = RNG(31).standard_normal((1, p.Hv, p.K, p.V))
+    p.h0 = X
+    o, f = orc.forward(p)
+    g = _hand_gate(p.g[0], p.A_log, p.dt_bias, safe, p.lower_bound)
+    if safe:
+        assert (g == p.lower_bound).any() and (g > p.lower_bound).any()
+    b = _hand_sigmoid(p.beta[0])
+    q = _hand_l2(p.q[0], p.eps)
+    k = _hand_l2(p.k[0], p.eps)
+    for h in range(p.Hv):
+        oh, sh = orc.recurrence(k[:, [h]], p.v[0][:, [h]], g[:, [h]], b[:, [h]], X[0][[h]],
+                                q=q[:, [h]], scale=p.scale)
+        np.testing.assert_allclose(o[0, :, h], oh[:, 0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(f[0, h], sh[0], rtol=1e-12, atol=1e-13)
+
+
+def test_precomputed_gate_clamp_and_sigmoid_route():
+    """Without the in-kernel gate, the safe gate still clamps the given
+    natural-log decay, and the sigmoid flag still activates beta."""
+    p = _prob(T=9, H=2, seed=32, safe_gate=True, lower_bound=-0.2, beta_sigmoid=True,
+              g=-np.abs(RNG(33).standard_normal((1, 9, 2, 4))) * 0.5,
+              beta=RNG(34).standard_normal((1, 9, 2)))
+    o, f = orc.forward(p)
+    g = np.maximum(p.g[0], -0.2)
+    assert (p.g[0] < -0.2).any()
+    b = _hand_sigmoid(p.beta[0])
+    oh, sh = orc.recurrence(p.k[0], p.v[0], g, b, np.zeros((2, 4, 3)), q=p.q[0], scale=p.scale)
+    np.testing.assert_allclose(o[0], oh, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(f[0], sh, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("safe", [False, True])
+def test_summary_in_kernel_route_equals_hand_prepared_recurrence(safe):
+    p = _gate_prob(safe, seed=35)
+    M, St = orc.segment_summary(p)
+    g = _hand_gate(p.g[0], p.A_log, p.dt_bias, safe, p.lower_bound)
+    b = _hand_sigmoid(p.beta[0])
+    k = _hand_l2(p.k[0], p.eps)
+    for h in range(p.Hv):
+        _, sh = orc.recurrence(k[:, [h]], p.v[0][:, [h]], g[:, [h]], b[:, [h]],
+                               np.zeros((1, p.K, p.V)))
+        P = np.eye(p.K)
+        for t in range(p.T):
+            P = (np.eye(p.K) - b[t, h] * np.outer(k[t, h], k[t, h])) @ np.diag(np.exp(g[t, h])) @ P
+        np.testing.assert_allclose(St[0, h], sh[0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(M[0, h], P, rtol=1e-11, atol=1e-13)
+
+
+def test_grouped_heads_on_the_in_kernel_route():
+    """Hv = 4 over Hk = 2 with the gate/sigmoid/L2Norm flags: value head h
+    reads q/k head h // 2 but its own A_log[h], dt_bias[h] and beta."""
+    p = _gate_prob(False, seed=36, H=4, Hk=2)
+    o, f = orc.forward(p)
+    g = _hand_gate(p.g[0], p.A_log, p.dt_bias, False, 0.0)
+    b = _hand_sigmoid(p.beta[0])
+    q = _hand_l2(p.q[0], p.eps)
+    k = _hand_l2(p.k[0], p.eps)
+    for h in range(4):
+        oh, sh = orc.recurrence(k[:, [h // 2]], p.v[0][:, [h]], g[:, [h]], b[:, [h]],
+                                np.zeros((1, p.K, p.V)), q=q[:, [h // 2]], scale=p.scale)
+        np.testing.assert_allclose(o[0, :, h], oh[:, 0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(f[0, h], sh[0], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("heads", [[2], [3, 0], [1, 2, 3]])
+def test_head_subset_equals_slice_of_full_run(heads):
+    """forward(heads=...) and segment_summary(heads=...) reproduce the full
+    run on those heads (grouped heads, in-kernel route) and leave the rest zero."""
+    p = _gate_prob(True, seed=37, H=4, Hk=2)
+    p.h0 = RNG(38).standard_normal((1, 4, p.K, p.V))
+    o, f = orc.forward(p)
+    os_, fs = orc.forward(p, heads=heads)
+    rest = [h for h in range(4) if h not in heads]
+    np.testing.assert_array_equal(os_[..., heads, :], o[..., heads, :])
+    np.testing.assert_array_equal(fs[:, heads], f[:, heads])
+    assert not os_[..., rest, :].any() and not fs[:, rest].any()
+    M, S = orc.segment_summary(p)
+    Ms, Ss = orc.segment_summary(p, heads=heads)
+    np.testing.assert_array_equal(Ms[:, heads], M[:, heads])
+    np.testing.assert_array_equal(Ss[:, heads], S[:, heads])
+
+
+def test_head_subset_in_cache_mode_keeps_other_heads():
+    lens = [4, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cache = RNG(39).standard_normal((3, 3, 4, 3))
+    p = _gate_prob(False, seed=40, T=int(cu[-1]), layout="tnd", cu_seqlens=cu, h0=cache,
+                   state_indices=np.array([2, 0], dtype=np.int32))
+    _, full = orc.forward(p)
+    _, part = orc.forward(p, heads=[1])
+    np.testing.assert_array_equal(part[:, 1], full[:, 1])
+    np.testing.assert_array_equal(part[:, [0, 2]], cache[:, [0, 2]])
+
+
+def test_token_limit_equals_truncated_problem():
+    """forward(t_max=n) equals the run of each sequence's first n tokens."""
+    lens = [9, 3, 12]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    p = _gate_prob(True, seed=41, T=int(cu[-1]), layout="tnd", cu_seqlens=cu,
+                   h0=RNG(42).standard_normal((3, 3, 4, 3)))
+    o, f = orc.forward(p, t_max=5)
+    keep = np.concatenate([np.arange(cu[n], min(cu[n + 1], cu[n] + 5)) for n in range(3)])
+    cut = np.concatenate([[0], np.cumsum([min(L, 5) for L in lens])]).astype(np.int32)
+    sub = SimpleNamespace(**{**vars(p), "T": int(cut[-1]), "cu_seqlens": cut, "q": p.q[keep],
+                             "k": p.k[keep], "v": p.v[keep], "g": p.g[keep], "beta": p.beta[keep]})
+    os_, fs = orc.forward(sub)
+    np.testing.assert_array_equal(o[keep], os_)
+    np.testing.assert_array_equal(f, fs)
+    drop = np.setdiff1d(np.arange(p.T), keep)
+    assert not o[drop].any()
