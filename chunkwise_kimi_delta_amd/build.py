@@ -63,5 +63,43 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     return LIB_PATH
 
 
+# Host-only sanitizer build of the C ABI (kda_api.cpp with stand-in launchers):
+# the validation, planning and error paths under AddressSanitizer and
+# UndefinedBehaviorSanitizer, for CPU tests on a machine without a GPU.  Each
+# -fsanitize applies to the host pass only; no device code is built.
+SAN_LIB_PATH = os.path.join(HERE, "_build", "libkda_host_asan.so")
+_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+        "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized() -> str:
+    hipcc = _hipcc()
+    out_dir = os.path.join(HERE, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    objs = []
+    for src in ("kda_api.cpp", "kda_host_stubs.cpp"):
+        obj = os.path.join(out_dir, src + ".san.o")
+        cmd = [hipcc, "--cuda-host-only", "-x", "hip", "-O1", "-g", "-std=c++17", "-fPIC", "-I", INCLUDE,
+               "-I", CSRC] + _SAN + ["-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitizer build of {src} failed:\n{r.stdout}{r.stderr}")
+        objs.append(obj)
+    r = subprocess.run([hipcc, "-shared", "-fPIC"] + _SAN + objs + ["-o", SAN_LIB_PATH],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking the sanitizer build failed:\n{r.stdout}{r.stderr}")
+    return SAN_LIB_PATH
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that the sanitizer build links against."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("the clang AddressSanitizer runtime was not found under /opt/rocm/llvm")
+    return hits[-1]
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -15,10 +15,10 @@
 namespace {
 
 thread_local std::string g_last_error;
-thread_local hipEvent_t g_stage_ev[3] = {nullptr, nullptr, nullptr};
 
-hipError_t record_stage(int i, hipStream_t s) {
-  return g_stage_ev[i] ? hipEventRecord(g_stage_ev[i], s) : hipSuccess;
+// Stage events of one call (caller-owned, recorded on the call's stream).
+hipError_t record_stage(void* const* ev, int i, hipStream_t s) {
+  return (ev && ev[i]) ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
 }
 
 kda_status_t fail(kda_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -66,13 +66,11 @@ kda_status_t plan_problem(const kda_problem_t* p, bool forward, Plan& pl) {
   if (p->Hv > 65535) return fail(KDA_ERR_UNSUPPORTED, "Hv=%d exceeds 65535", p->Hv);
   if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128))
     return fail(KDA_ERR_UNSUPPORTED, "head dims K=%d V=%d: each must be 64 or 128", p->K, p->V);
-  if (p->dtype == KDA_F32 && p->K != 64)
-    return fail(KDA_ERR_UNSUPPORTED, "fp32 token tensors are built for K=64 only (got K=%d)", p->K);
   if (p->flags & ~kAllFlags) return fail(KDA_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", p->flags & ~kAllFlags);
   if (!std::isfinite(p->scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(KDA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
-  if ((p->flags & KDA_SAFE_GATE) && !std::isfinite(p->lower_bound))
-    return fail(KDA_ERR_INVALID_ARGUMENT, "lower_bound is not finite");
+  if ((p->flags & KDA_SAFE_GATE) && !(std::isfinite(p->lower_bound) && p->lower_bound <= 0.f))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "lower_bound must be finite and <= 0 (a decay, in natural log)");
   if (p->B < 0 || p->T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative B=%d or T=%d", p->B, p->T);
   if (p->state_rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative state_rows");
   if (!forward && p->state_rows != 0)
@@ -192,15 +190,6 @@ const char* kda_status_string(kda_status_t s) {
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
-kda_status_t kda_set_stage_events(void* begin, void* after_chunk_local, void* end) {
-  const bool all = begin && after_chunk_local && end, none = !begin && !after_chunk_local && !end;
-  if (!all && !none) return fail(KDA_ERR_INVALID_ARGUMENT, "pass three events or none");
-  g_stage_ev[0] = static_cast<hipEvent_t>(begin);
-  g_stage_ev[1] = static_cast<hipEvent_t>(after_chunk_local);
-  g_stage_ev[2] = static_cast<hipEvent_t>(end);
-  return ok();
-}
-
 kda_status_t kda_chunk_offsets_host(const int32_t* cu, int32_t N, int32_t chunk, int32_t* out) {
   if (!cu || !out || N < 0 || chunk < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "bad chunk-offset arguments");
   if (cu[0] != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] must be 0");
@@ -237,7 +226,8 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
                            const void* g, const void* beta, const float* A_log, const float* dt_bias,
                            const float* initial_state, const int32_t* cu_seqlens,
                            const int32_t* state_indices, void* o, float* final_state,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           void* const* stage_events) {
   Plan pl;
   kda_status_t st = plan_problem(p, true, pl);
   if (st != KDA_OK) return st;
@@ -261,9 +251,9 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   kda::SeqInfo si = seq_info(p, pl, cu_seqlens, ws);
-  if ((st = hip_status(record_stage(0, s), "stage event")) != KDA_OK) return st;
+  if ((st = hip_status(record_stage(stage_events, 0, s), "stage event")) != KDA_OK) return st;
   if ((st = run_intra(p, pl, si, cu_seqlens, q, k, v, g, beta, A_log, dt_bias, ws, s)) != KDA_OK) return st;
-  if ((st = hip_status(record_stage(1, s), "stage event")) != KDA_OK) return st;
+  if ((st = hip_status(record_stage(stage_events, 1, s), "stage event")) != KDA_OK) return st;
   kda::ScanArgs a{};
   a.seq = si;
   a.Hv = p->Hv; a.nchunks = (int)pl.nchunks; a.state_rows = p->state_rows; a.summary = 0;
@@ -271,14 +261,14 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
   a.h0 = initial_state; a.state_idx = state_indices; a.hT = final_state; a.M = nullptr; a.o = o;
   if ((st = hip_status(kda::launch_scan(p->K, p->V, p->dtype, a, s), "state-scan kernel launch")) != KDA_OK)
     return st;
-  if ((st = hip_status(record_stage(2, s), "stage event")) != KDA_OK) return st;
+  if ((st = hip_status(record_stage(stage_events, 2, s), "stage event")) != KDA_OK) return st;
   return ok();
 }
 
 kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const void* v, const void* g,
                                  const void* beta, const float* A_log, const float* dt_bias,
                                  const int32_t* cu_seqlens, float* M, float* S_tilde, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 size_t workspace_bytes, void* stream, void* const* stage_events) {
   Plan pl;
   kda_status_t st = plan_problem(p, false, pl);
   if (st != KDA_OK) return st;
@@ -295,10 +285,10 @@ kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   kda::SeqInfo si = seq_info(p, pl, cu_seqlens, ws);
-  if ((st = hip_status(record_stage(0, s), "stage event")) != KDA_OK) return st;
+  if ((st = hip_status(record_stage(stage_events, 0, s), "stage event")) != KDA_OK) return st;
   if ((st = run_intra(p, pl, si, cu_seqlens, nullptr, k, v, g, beta, A_log, dt_bias, ws, s)) != KDA_OK)
     return st;
-  if ((st = hip_status(record_stage(1, s), "stage event")) != KDA_OK) return st;
+  if ((st = hip_status(record_stage(stage_events, 1, s), "stage event")) != KDA_OK) return st;
   kda::ScanArgs a{};
   a.seq = si;
   a.Hv = p->Hv; a.nchunks = (int)pl.nchunks; a.state_rows = 0; a.summary = 1;
@@ -306,7 +296,7 @@ kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const vo
   a.hT = S_tilde; a.M = M;
   if ((st = hip_status(kda::launch_scan(p->K, p->V, p->dtype, a, s), "summary scan kernel launch")) != KDA_OK)
     return st;
-  if ((st = hip_status(record_stage(2, s), "stage event")) != KDA_OK) return st;
+  if ((st = hip_status(record_stage(stage_events, 2, s), "stage event")) != KDA_OK) return st;
   return ok();
 }
 

@@ -1,0 +1,12 @@
+// Host-only stand-ins for the kernel launchers, linked into the sanitizer
+// build of the C ABI (kda_api.cpp) so that its validation, workspace planning
+// and error paths run under AddressSanitizer and UndefinedBehaviorSanitizer
+// on a machine without a GPU.  They launch nothing and report success.
+#include "kda_launch.h"
+
+namespace kda {
+hipError_t launch_chunk_offsets(const int32_t*, int, int32_t*, hipStream_t) { return hipSuccess; }
+hipError_t launch_intra(int, int, int, const IntraArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_scan(int, int, int, const ScanArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_merge(int, int, const MergeArgs&, hipStream_t) { return hipSuccess; }
+}  // namespace kda

@@ -139,8 +139,12 @@ __device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
 
+// Two workgroups per CU, except fp32 tokens with K = 128, whose LDS (about
+// 108 KB) leaves room for one.
+template <int KD, typename IT> constexpr int intra_min_blocks() { return (sizeof(IT) == 4 && KD == 128) ? 1 : 2; }
+
 template <int KD, int VD, typename IT, bool FWD>
-__global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
+__global__ __launch_bounds__(256, (intra_min_blocks<KD, IT>())) void intra_kernel(IntraArgs a) {
   using ST = IT;                                   // workspace type of w, qg, Aqk
   constexpr bool F32 = sizeof(IT) == 4;
   constexpr int NKS = KD / 32, NVS = VD / 32;
@@ -289,8 +293,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs a) {
     sqk += __shfl_xor(sqk, 16); sqk += __shfl_xor(sqk, 32);
     const bool l2 = a.flags & F_L2;
     // the attention scale rides on q's normalisation (q enters only Aqk and qg)
-    rq = a.scale * (l2 ? 1.f / sqrtf(sqq + a.eps) : 1.f);
-    rk = l2 ? 1.f / sqrtf(skk + a.eps) : 1.f;
+    // (rows past the sequence end get zero factors: with eps = 0 their zero
+    // norms would otherwise turn into 0 * inf = NaN)
+    rq = live ? a.scale * (l2 ? 1.f / sqrtf(sqq + a.eps) : 1.f) : 0.f;
+    rk = live ? (l2 ? 1.f / sqrtf(skk + a.eps) : 1.f) : 0.f;
     dqk = sqk;
   }
   if (r16 == 15) {
@@ -840,9 +846,8 @@ hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t
   dim3 grid((unsigned)nb), block(256);
 #define KDA_INTRA_CASE(KK, VV, TT)                                          \
   if (K == KK && V == VV) {                                                 \
-    if (a.q) hipLaunchKernelGGL((intra_kernel<KK, VV, TT, true>), grid, block, 0, s, a);  \
-    else hipLaunchKernelGGL((intra_kernel<KK, VV, TT, false>), grid, block, 0, s, a);     \
-    return hipGetLastError();                                               \
+    return a.q ? launch(intra_kernel<KK, VV, TT, true>, grid, block, s, a)  \
+               : launch(intra_kernel<KK, VV, TT, false>, grid, block, s, a); \
   }
   if (dtype == 1) {
     KDA_INTRA_CASE(128, 128, bf16_t)
@@ -850,7 +855,9 @@ hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t
     KDA_INTRA_CASE(128, 64, bf16_t)
     KDA_INTRA_CASE(64, 128, bf16_t)
   } else {
+    KDA_INTRA_CASE(128, 128, float)
     KDA_INTRA_CASE(64, 64, float)
+    KDA_INTRA_CASE(128, 64, float)
     KDA_INTRA_CASE(64, 128, float)
   }
 #undef KDA_INTRA_CASE

@@ -96,6 +96,15 @@ struct MergeArgs {
   float* state;
 };
 
+// Launch a kernel and return the status of this launch alone (hipLaunchKernel
+// reports its own failure; hipGetLastError would also return an error left
+// behind by the caller's earlier work).
+template <typename... A>
+inline hipError_t launch(void (*kern)(A...), dim3 grid, dim3 block, hipStream_t s, A... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, 0, s);
+}
+
 // dtype: 0 = fp32, 1 = bf16
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);
 hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t s);

@@ -54,8 +54,7 @@ hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s) {
   if (a.P == 0 || a.Hv == 0) return hipSuccess;
 #define KDA_MERGE_CASE(KK, VV)                                                          \
   if (K == KK && V == VV) {                                                             \
-    hipLaunchKernelGGL((merge_kernel<KK, VV>), dim3(a.Hv * (VV / 32)), dim3(256), 0, s, a); \
-    return hipGetLastError();                                                           \
+    return launch(merge_kernel<KK, VV>, dim3(a.Hv * (VV / 32)), dim3(256), s, a);     \
   }
   KDA_MERGE_CASE(128, 128)
   KDA_MERGE_CASE(64, 64)

@@ -484,8 +484,7 @@ __global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t* cu, i
 }  // namespace
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s) {
-  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, s, cu, N, chunk_off);
-  return hipGetLastError();
+  return launch(chunk_offsets_kernel, dim3(1), dim3(256), s, cu, N, chunk_off);
 }
 
 hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s) {
@@ -498,9 +497,8 @@ hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s
   dim3 grid((unsigned)nb), block(K * 2 + (a.summary ? 0 : 64 * NOW));
 #define KDA_SCAN_CASE(KK, VV, TT, CC)                                                             \
   if (K == KK && V == VV && CTsel == CC) {                                                        \
-    if (a.summary) hipLaunchKernelGGL((scan_kernel<KK, VV, TT, true, CC>), grid, block, 0, s, a); \
-    else hipLaunchKernelGGL((scan_kernel<KK, VV, TT, false, CC>), grid, block, 0, s, a);          \
-    return hipGetLastError();                                                                     \
+    return a.summary ? launch(scan_kernel<KK, VV, TT, true, CC>, grid, block, s, a)              \
+                     : launch(scan_kernel<KK, VV, TT, false, CC>, grid, block, s, a);            \
   }
   if (dtype == 1) {
     KDA_SCAN_CASE(128, 128, bf16_t, 1)
@@ -508,7 +506,9 @@ hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s
     KDA_SCAN_CASE(128, 64, bf16_t, 1)
     KDA_SCAN_CASE(64, 128, bf16_t, 1)
   } else {
+    KDA_SCAN_CASE(128, 128, float, 1)
     KDA_SCAN_CASE(64, 64, float, 1)
+    KDA_SCAN_CASE(128, 64, float, 1)
     KDA_SCAN_CASE(64, 128, float, 1)
   }
 #undef KDA_SCAN_CASE

@@ -13,7 +13,10 @@ from typing import Optional, Tuple
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda_mi355x.so")
+# KDA_LIBRARY selects another build of the same ABI (the host sanitizer build
+# of the validation code is one).
+LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libkda_mi355x.so")
 
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
@@ -43,7 +46,9 @@ class KdaProblem(ctypes.Structure):
 _lib = None
 EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_segment_summary_workspace_size",
            "kda_segment_summary", "kda_summary_merge", "kda_chunk_offsets_host",
-           "kda_set_stage_events", "kda_status_string", "kda_last_error", "kda_abi_version")
+           "kda_status_string", "kda_last_error", "kda_abi_version")
+ABI_VERSION = 2
+STAGE_EVENTS = 3
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -57,19 +62,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, VP, SZ, I32 = ctypes.POINTER(KdaProblem), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
     lib.kda_chunk_fwd_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.kda_segment_summary_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
-    lib.kda_chunk_fwd.argtypes = [P] + [VP] * 13 + [SZ, VP]
-    lib.kda_segment_summary.argtypes = [P] + [VP] * 10 + [SZ, VP]
+    lib.kda_chunk_fwd.argtypes = [P] + [VP] * 13 + [SZ, VP, VP]
+    lib.kda_segment_summary.argtypes = [P] + [VP] * 10 + [SZ, VP, VP]
     lib.kda_summary_merge.argtypes = [I32, I32, I32, I32, VP, VP, VP, VP]
     lib.kda_chunk_offsets_host.argtypes = [VP, I32, I32, VP]
-    lib.kda_set_stage_events.argtypes = [VP, VP, VP]
     lib.kda_status_string.argtypes = [I32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_abi_version.restype = I32
     for name in ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_segment_summary_workspace_size",
-                 "kda_segment_summary", "kda_summary_merge", "kda_chunk_offsets_host",
-                 "kda_set_stage_events"):
+                 "kda_segment_summary", "kda_summary_merge", "kda_chunk_offsets_host"):
         getattr(lib, name).restype = I32
+    if lib.kda_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.kda_abi_version()}, expected {ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 
@@ -96,13 +101,34 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _need(t: Optional[torch.Tensor], name: str, dtype=None):
+def _need(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, device=None):
+    """Shape, dtype, layout and device of one tensor argument: the C ABI sees
+    only pointers, so a wrong size here would become an out-of-bounds access."""
     if t is None:
         return
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _gpu_device(v: torch.Tensor) -> torch.device:
+    if v.device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {v.device}")
+    return v.device
+
+
+def _events(stage_events):
+    if stage_events is None:
+        return None
+    ev = list(stage_events)
+    if len(ev) != STAGE_EVENTS:
+        raise ValueError(f"stage_events needs {STAGE_EVENTS} entries")
+    return (ctypes.c_void_p * STAGE_EVENTS)(*ev)
 
 
 def make_problem(q_or_k: torch.Tensor, v: torch.Tensor, *, scale: float, flags: int, eps: float,
@@ -125,12 +151,22 @@ def make_problem(q_or_k: torch.Tensor, v: torch.Tensor, *, scale: float, flags: 
     return p, N
 
 
-def _cu_pair(cu_seqlens, cu_seqlens_host, device):
-    if cu_seqlens is None:
+def _cu_pair(cu_seqlens, cu_seqlens_host, device, tokens: torch.Tensor):
+    """Device and host copies of cu_seqlens (int32); only 3-D (TND) token
+    tensors take them."""
+    if tokens.dim() == 4:
+        if cu_seqlens is not None or cu_seqlens_host is not None:
+            raise ValueError("4-D (BSND) token tensors take no cu_seqlens")
         return None, None
+    if cu_seqlens is None:
+        raise ValueError("3-D (TND) token tensors need cu_seqlens")
     cu_h = cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens.detach().to("cpu")
     cu_h = cu_h.to(torch.int32).contiguous()
-    cu_d = cu_seqlens if cu_seqlens.is_cuda else cu_h.to(device)
+    if cu_h.device.type != "cpu":
+        raise ValueError("cu_seqlens_host must be a CPU tensor")
+    if cu_seqlens.dim() != 1 or cu_h.dim() != 1 or cu_seqlens.numel() != cu_h.numel() or cu_h.numel() < 1:
+        raise ValueError("cu_seqlens and its host copy must be 1-D of the same length N+1 >= 1")
+    cu_d = cu_seqlens if cu_seqlens.device == device else cu_h.to(device)
     cu_d = cu_d.to(torch.int32).contiguous()
     return cu_d, cu_h
 
@@ -140,26 +176,61 @@ def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None
                   output_final_state: bool = True, gate_in_kernel: bool = False,
                   safe_gate: bool = False, lower_bound: float = -5.0, qk_l2norm: bool = False,
                   beta_sigmoid: bool = False, eps: float = 1e-6, o=None, final_state=None,
-                  workspace=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  workspace=None, stage_events=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA forward.  Returns (o, final_state).
 
     With ``state_indices`` the ``initial_state`` is a state cache
     [rows,Hv,K,V]; final states are scattered into ``final_state`` (default:
-    the same cache, in place) and that cache is returned.
+    the same cache, in place) and that cache is returned.  ``stage_events``:
+    three raw hipEvent_t handles the call records at its stage boundaries.
     """
     lib = load()
-    dev = v.device
+    if q.dim() not in (3, 4) or v.dim() != q.dim():
+        raise ValueError("token tensors are [B,T,H,D] or [T,H,D], q and v alike")
+    lead, Hk, K = tuple(q.shape[:-2]), q.shape[-2], q.shape[-1]
+    Hv, V = v.shape[-2], v.shape[-1]
+    cache = state_indices is not None
+    _need(k, "k", None, q.shape)
+    _need(v, "v", None, lead + (Hv, V))
+    _need(g, "g", None, lead + (Hv, K))
+    _need(beta, "beta", None, lead + (Hv,))
+    _need(A_log, "A_log", torch.float32, (Hv,))
+    _need(dt_bias, "dt_bias", torch.float32, (Hv, K))
+    if gate_in_kernel and A_log is None:
+        raise ValueError("gate_in_kernel needs A_log")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta")):
         _need(t, n, v.dtype)
-    _need(A_log, "A_log", torch.float32)
-    _need(dt_bias, "dt_bias", torch.float32)
-    _need(initial_state, "initial_state", torch.float32)
-    cu_d, cu_h = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    if q.dim() == 4:
+        if cu_seqlens is not None or cu_seqlens_host is not None:
+            raise ValueError("4-D (BSND) token tensors take no cu_seqlens")
+        N = q.shape[0]
+    else:
+        if cu_seqlens is None:
+            raise ValueError("3-D (TND) token tensors need cu_seqlens")
+        if cu_seqlens_host is not None and cu_seqlens_host.numel() != cu_seqlens.numel():
+            raise ValueError("cu_seqlens and its host copy must be 1-D of the same length N+1 >= 1")
+        N = cu_seqlens.numel() - 1
+    if cache:
+        if initial_state is None or initial_state.dim() != 4 or initial_state.shape[0] < 1:
+            raise ValueError("state_indices needs the state cache [rows,Hv,K,V] as initial_state")
+        rows = initial_state.shape[0]
+        _need(initial_state, "initial_state", torch.float32, (rows, Hv, K, V))
+        _need(state_indices, "state_indices", None, (N,))
+        _need(final_state, "final_state", torch.float32, (rows, Hv, K, V))
+    else:
+        _need(initial_state, "initial_state", torch.float32, (N, Hv, K, V))
+        _need(final_state, "final_state", torch.float32, (N, Hv, K, V))
+    _need(o, "o", v.dtype, v.shape)
+    dev = _gpu_device(v)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (A_log, "A_log"),
+                 (dt_bias, "dt_bias"), (initial_state, "initial_state"), (final_state, "final_state")):
+        _need(t, n, device=dev)
+    cu_d, cu_h = _cu_pair(cu_seqlens, cu_seqlens_host, dev, q)
+    _need(o, "o", device=dev)
     if scale is None:
         scale = q.shape[-1] ** -0.5
     flags = ((KDA_GATE_IN_KERNEL if gate_in_kernel else 0) | (KDA_SAFE_GATE if safe_gate else 0)
              | (KDA_QK_L2NORM if qk_l2norm else 0) | (KDA_BETA_SIGMOID if beta_sigmoid else 0))
-    cache = state_indices is not None
     rows = initial_state.shape[0] if cache else 0
     p, N = make_problem(q, v, scale=scale, flags=flags, eps=eps, lower_bound=lower_bound,
                         cu_host=cu_h, state_rows=rows)
@@ -176,12 +247,13 @@ def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None
             final_state = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev)
     ws_bytes = ctypes.c_size_t()
     _check(lib.kda_chunk_fwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
-    if workspace is None or workspace.numel() < ws_bytes.value:
+    if workspace is None:
         workspace = torch.empty(max(ws_bytes.value, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
     _check(lib.kda_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_d), _ptr(si),
                              _ptr(o), _ptr(final_state), _ptr(workspace), workspace.numel(),
-                             _stream(dev)))
+                             _stream(dev), _events(stage_events)))
     return o, final_state
 
 
@@ -189,39 +261,62 @@ def kda_segment_summary(k, v, g, beta, *, A_log=None, dt_bias=None, cu_seqlens=N
                         cu_seqlens_host=None, gate_in_kernel: bool = False, safe_gate: bool = False,
                         lower_bound: float = -5.0, qk_l2norm: bool = False,
                         beta_sigmoid: bool = False, eps: float = 1e-6, M=None, S_tilde=None,
-                        workspace=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                        workspace=None, stage_events=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-sequence affine summary (M [N,Hv,K,K], S~ [N,Hv,K,V]), fp32."""
     lib = load()
-    dev = v.device
+    if k.dim() not in (3, 4) or v.dim() != k.dim():
+        raise ValueError("token tensors are [B,T,H,D] or [T,H,D], k and v alike")
+    lead, K = tuple(k.shape[:-2]), k.shape[-1]
+    Hv, V = v.shape[-2], v.shape[-1]
+    _need(v, "v", None, lead + (Hv, V))
+    _need(g, "g", None, lead + (Hv, K))
+    _need(beta, "beta", None, lead + (Hv,))
+    _need(A_log, "A_log", torch.float32, (Hv,))
+    _need(dt_bias, "dt_bias", torch.float32, (Hv, K))
+    if gate_in_kernel and A_log is None:
+        raise ValueError("gate_in_kernel needs A_log")
     for t, n in ((k, "k"), (v, "v"), (g, "g"), (beta, "beta")):
         _need(t, n, v.dtype)
-    _need(A_log, "A_log", torch.float32)
-    _need(dt_bias, "dt_bias", torch.float32)
-    cu_d, cu_h = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    dev = _gpu_device(v)
+    for t, n in ((k, "k"), (v, "v"), (g, "g"), (beta, "beta")):
+        _need(t, n, device=dev)
+    _need(A_log, "A_log", device=dev)
+    _need(dt_bias, "dt_bias", device=dev)
+    cu_d, cu_h = _cu_pair(cu_seqlens, cu_seqlens_host, dev, k)
     flags = ((KDA_GATE_IN_KERNEL if gate_in_kernel else 0) | (KDA_SAFE_GATE if safe_gate else 0)
              | (KDA_QK_L2NORM if qk_l2norm else 0) | (KDA_BETA_SIGMOID if beta_sigmoid else 0))
     p, N = make_problem(k, v, scale=1.0, flags=flags, eps=eps, lower_bound=lower_bound, cu_host=cu_h)
     K, V, Hv = k.shape[-1], v.shape[-1], v.shape[-2]
+    _need(M, "M", torch.float32, (N, Hv, K, K), dev)
+    _need(S_tilde, "S_tilde", torch.float32, (N, Hv, K, V), dev)
     if M is None:
         M = torch.empty((N, Hv, K, K), dtype=torch.float32, device=dev)
     if S_tilde is None:
         S_tilde = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev)
     ws_bytes = ctypes.c_size_t()
     _check(lib.kda_segment_summary_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
-    if workspace is None or workspace.numel() < ws_bytes.value:
+    if workspace is None:
         workspace = torch.empty(max(ws_bytes.value, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
     _check(lib.kda_segment_summary(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                    _ptr(A_log), _ptr(dt_bias), _ptr(cu_d), _ptr(M), _ptr(S_tilde),
-                                   _ptr(workspace), workspace.numel(), _stream(dev)))
+                                   _ptr(workspace), workspace.numel(), _stream(dev),
+                                   _events(stage_events)))
     return M, S_tilde
 
 
 def kda_summary_merge(M: torch.Tensor, S_tilde: torch.Tensor, state: torch.Tensor) -> torch.Tensor:
     """In place: state <- M[j] state + S_tilde[j] for j in order.  Returns ``state``."""
     lib = load()
+    if state.dim() != 3 or S_tilde.dim() != 4:
+        raise ValueError("state is [Hv,K,V] and S_tilde [P,Hv,K,V]")
+    Hv, K, V = state.shape
+    P = S_tilde.shape[0]
+    _need(S_tilde, "S_tilde", torch.float32, (P, Hv, K, V))
+    _need(M, "M", torch.float32, (P, Hv, K, K))
+    dev = _gpu_device(state)
     for t, n in ((M, "M"), (S_tilde, "S_tilde"), (state, "state")):
-        _need(t, n, torch.float32)
-    P, Hv, K, V = S_tilde.shape if S_tilde.dim() == 4 else (0,) + tuple(state.shape)
+        _need(t, n, torch.float32, device=dev)
     _check(lib.kda_summary_merge(P, Hv, K, V, _ptr(M), _ptr(S_tilde), _ptr(state),
                                  _stream(state.device)))
     return state
@@ -234,11 +329,6 @@ def kda_chunk_offsets_host(cu_seqlens_host: torch.Tensor, chunk: int = CHUNK) ->
     out = torch.empty(cu.numel(), dtype=torch.int32)
     _check(lib.kda_chunk_offsets_host(cu.data_ptr(), cu.numel() - 1, chunk, out.data_ptr()))
     return out
-
-
-def kda_set_stage_events(begin: Optional[int], after_chunk_local: Optional[int], end: Optional[int]):
-    """Register raw hipEvent_t handles recorded at the stage boundaries of later calls."""
-    _check(load().kda_set_stage_events(begin, after_chunk_local, end))
 
 
 def workspace_bytes(q_or_k: torch.Tensor, v: torch.Tensor, cu_seqlens_host=None, summary: bool = False) -> int:

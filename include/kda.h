@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
   KDA_OK = 0,
@@ -73,18 +73,21 @@ enum {
   KDA_BETA_SIGMOID = 8u
 };
 
+/* Number of stage events a token-level call records (see kda_chunk_fwd). */
+#define KDA_STAGE_EVENTS 3
+
 /* Problem description, passed by pointer to every token-level call. */
 typedef struct kda_problem {
   int32_t layout;       /* kda_layout_t */
   int32_t dtype;        /* kda_dtype_t of q, k, v, g, beta and o */
   int32_t B, T;         /* BSND: batch and tokens per sequence.  TND: B = 1, T = packed tokens */
   int32_t Hk, Hv;       /* query/key heads and value heads; Hv % Hk == 0 */
-  int32_t K, V;         /* key and value head dims; each 64 or 128 */
+  int32_t K, V;         /* key and value head dims; each 64 or 128 (bf16 or fp32 tokens) */
   int32_t chunk_size;   /* must be 64 */
   uint32_t flags;       /* KDA_* flags above */
   float scale;          /* output scale, usually K^-1/2 */
   float eps;            /* L2Norm epsilon (inside the square root), e.g. 1e-6 */
-  float lower_bound;    /* safe-gate floor for the natural-log decay, e.g. -5 */
+  float lower_bound;    /* safe-gate floor for the natural-log decay, finite and <= 0, e.g. -5 */
   int32_t num_seqs;     /* N: BSND must equal B; TND = number of packed sequences */
   const int32_t* cu_seqlens_host; /* TND: HOST copy of cu_seqlens [N+1]; NULL for BSND */
   int32_t state_rows;   /* 0: states are [N,Hv,K,V]; > 0: state cache rows, see kda_chunk_fwd */
@@ -113,6 +116,10 @@ kda_status_t kda_chunk_fwd_workspace_size(const kda_problem_t* p, size_t* bytes)
  *                     state of sequence n is written to row state_indices[n] when that
  *                     index is valid, other rows are untouched.  May equal initial_state.
  *  workspace        : device buffer of at least kda_chunk_fwd_workspace_size bytes.
+ *  stage_events     : NULL, or KDA_STAGE_EVENTS hipEvent_t handles (as void*, any may be
+ *                     NULL) recorded on `stream` before the first kernel, after the
+ *                     chunk-local kernel and after the last kernel of this call; a
+ *                     caller times each kernel with them.  Not kept after the call.
  * Inputs are not modified (except the cache when final_state == initial_state).
  */
 kda_status_t kda_chunk_fwd(const kda_problem_t* p,
@@ -122,7 +129,8 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p,
                            const float* initial_state, const int32_t* cu_seqlens,
                            const int32_t* state_indices,
                            void* o, float* final_state,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           void* const* stage_events);
 
 /* Bytes of device workspace kda_segment_summary needs for this problem. */
 kda_status_t kda_segment_summary_workspace_size(const kda_problem_t* p, size_t* bytes);
@@ -136,6 +144,7 @@ kda_status_t kda_segment_summary_workspace_size(const kda_problem_t* p, size_t* 
  * later tokens on the left; S_tilde[n] = the state reached from a zero state.
  *  k, v, g, beta, A_log, dt_bias, cu_seqlens : as in kda_chunk_fwd (no q is needed).
  *  M       : fp32 [N,Hv,K,K] output.   S_tilde : fp32 [N,Hv,K,V] output.
+ *  stage_events : as in kda_chunk_fwd.
  * p->state_rows must be 0.
  */
 kda_status_t kda_segment_summary(const kda_problem_t* p,
@@ -143,7 +152,8 @@ kda_status_t kda_segment_summary(const kda_problem_t* p,
                                  const float* A_log, const float* dt_bias,
                                  const int32_t* cu_seqlens,
                                  float* M, float* S_tilde,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* stage_events);
 
 /*
  * Prefix merge of preceding summaries ("KDA Context Parallelism (KCP)",
@@ -166,13 +176,6 @@ kda_status_t kda_summary_merge(int32_t P, int32_t Hv, int32_t K, int32_t V,
  * 3.8, chunk-to-segment map). */
 kda_status_t kda_chunk_offsets_host(const int32_t* cu_seqlens_host, int32_t N,
                                     int32_t chunk_size, int32_t* chunk_offsets_host);
-
-/* Profiling aid.  Registers three hipEvent_t handles (passed as void*) that
- * later kda_chunk_fwd / kda_segment_summary calls on the calling thread record
- * on their stream: at the start, after the chunk-local kernel and at the end,
- * so a caller can time each kernel of the call.  All NULL disables it.  The
- * caller owns the events and keeps them alive while registered. */
-kda_status_t kda_set_stage_events(void* begin, void* after_chunk_local, void* end);
 
 /* Static description of a status code. */
 const char* kda_status_string(kda_status_t s);

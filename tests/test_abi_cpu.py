@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(kda.EXPORTS)
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == kda.ABI_VERSION == 2
 
 
 def _problem(**kw):
@@ -38,6 +38,13 @@ def _problem(**kw):
              state_rows=0)
     d.update(kw)
     return kda.KdaProblem(*[d[f] for f, _ in kda.KdaProblem._fields_])
+
+
+def test_fp32_tokens_at_k128_are_in_the_envelope(lib):
+    st, b = _ws(lib, _problem(dtype=0))
+    assert st == 0 and b > 0
+    st, _ = _ws(lib, _problem(dtype=0, flags=15 | 2, lower_bound=0.0))   # floor 0 is allowed
+    assert st == 0
 
 
 def _ws(lib, p, summary=False):
@@ -67,7 +74,9 @@ def test_workspace_size_layer_and_monotone(lib):
     (dict(chunk_size=32), kda.KDA_ERR_UNSUPPORTED),
     (dict(K=96), kda.KDA_ERR_UNSUPPORTED),
     (dict(V=256), kda.KDA_ERR_UNSUPPORTED),
-    (dict(dtype=0), kda.KDA_ERR_UNSUPPORTED),            # fp32 with K=128
+    (dict(dtype=0, K=96), kda.KDA_ERR_UNSUPPORTED),      # fp32 with an unbuilt K
+    (dict(flags=15 | 2, lower_bound=0.5), kda.KDA_ERR_INVALID_ARGUMENT),   # safe-gate floor > 0
+    (dict(flags=15 | 2, lower_bound=float("-inf")), kda.KDA_ERR_INVALID_ARGUMENT),
     (dict(dtype=7), kda.KDA_ERR_INVALID_ARGUMENT),
     (dict(layout=3), kda.KDA_ERR_INVALID_ARGUMENT),
     (dict(Hk=3), kda.KDA_ERR_INVALID_ARGUMENT),          # 32 % 3 != 0
@@ -119,18 +128,91 @@ def test_chunk_map_matches_worked_example():
 
 def test_calls_fail_closed_without_launching(lib):
     p = _problem(T=128)
-    st = lib.kda_chunk_fwd(ctypes.byref(p), *([None] * 13), 0, None)
+    st = lib.kda_chunk_fwd(ctypes.byref(p), *([None] * 13), 0, None, None)
     assert st == kda.KDA_ERR_INVALID_ARGUMENT            # q/k/v... are NULL
     # misaligned pointers are rejected before any device access
     fake = 0x1000
     st = lib.kda_chunk_fwd(ctypes.byref(p), fake + 2, fake, fake, fake, fake, fake, None, None,
-                           None, None, fake, None, fake, 1 << 40, None)
+                           None, None, fake, None, fake, 1 << 40, None, None)
     assert st == kda.KDA_ERR_INVALID_ARGUMENT and b"aligned" in lib.kda_last_error()
     st = lib.kda_chunk_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None,
-                           None, None, fake, None, fake, 10, None)
+                           None, None, fake, None, fake, 10, None, None)
     assert st == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    # an empty selection (N = 0) launches nothing and succeeds
+    p0, keep = _tnd([0])
+    sz = ctypes.c_size_t()
+    assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(p0), ctypes.byref(sz)) == 0
+    st = lib.kda_chunk_fwd(ctypes.byref(p0), None, None, None, None, None, fake, None, None,
+                           fake, None, None, None, fake, sz.value, None, None)
+    assert st == 0, lib.kda_last_error()
     assert lib.kda_summary_merge(1, 32, 128, 96, fake, fake, fake, None) == kda.KDA_ERR_UNSUPPORTED
     assert lib.kda_summary_merge(-1, 32, 128, 128, fake, fake, fake, None) == kda.KDA_ERR_INVALID_ARGUMENT
     assert lib.kda_summary_merge(0, 32, 128, 128, None, None, fake, None) == 0   # P = 0: nothing to do
     for s in range(5):
         assert lib.kda_status_string(s)
+
+
+# ------------------------------------------------- binding argument checks
+def _cpu_layer(B=1, T=70, Hk=2, Hv=4, K=64, V=64, dtype=torch.bfloat16):
+    z = lambda *s: torch.zeros(*s, dtype=dtype)
+    return dict(q=z(B, T, Hk, K), k=z(B, T, Hk, K), v=z(B, T, Hv, V), g=z(B, T, Hv, K),
+                beta=z(B, T, Hv), A_log=torch.zeros(Hv), dt_bias=torch.zeros(Hv, K))
+
+
+def _fwd(t, **kw):
+    return kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], A_log=t["A_log"],
+                             dt_bias=t["dt_bias"], gate_in_kernel=True, **kw)
+
+
+@pytest.mark.parametrize("name,bad,err", [
+    ("k", torch.zeros(1, 70, 1, 64, dtype=torch.bfloat16), ValueError),    # fewer q/k heads than q
+    ("v", torch.zeros(1, 70, 4, 64, dtype=torch.bfloat16)[:, :69], ValueError),
+    ("g", torch.zeros(1, 70, 4, 32, dtype=torch.bfloat16), ValueError),
+    ("beta", torch.zeros(1, 70, 2, dtype=torch.bfloat16), ValueError),
+    ("A_log", torch.zeros(3), ValueError),
+    ("dt_bias", torch.zeros(4, 64, dtype=torch.float64), TypeError),
+    ("g", torch.zeros(1, 70, 4, 64, dtype=torch.float32), TypeError),       # dtype differs from v
+])
+def test_binding_rejects_wrong_shapes_and_dtypes(lib, name, bad, err):
+    t = _cpu_layer()
+    t[name] = bad
+    with pytest.raises(err):
+        _fwd(t)
+
+
+def test_binding_rejects_wrong_state_shapes(lib):
+    t = _cpu_layer()
+    with pytest.raises(ValueError, match="initial_state"):
+        _fwd(t, initial_state=torch.zeros(2, 4, 64, 64))                    # N = 1, not 2
+    with pytest.raises(ValueError, match="final_state"):
+        _fwd(t, final_state=torch.zeros(1, 2, 64, 64))
+    with pytest.raises(ValueError, match="o has shape"):
+        _fwd(t, o=torch.zeros(1, 70, 4, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="state_indices"):
+        _fwd(t, initial_state=torch.zeros(5, 4, 64, 64), state_indices=torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        _fwd(t, cu_seqlens=torch.tensor([0, 70], dtype=torch.int32))         # BSND takes none
+
+
+def test_binding_rejects_host_tensors_before_the_library_call(lib):
+    """Well-shaped CPU tensors fail on the device check: no pointer reaches the library."""
+    t = _cpu_layer()
+    with pytest.raises(ValueError, match="GPU device"):
+        _fwd(t)
+    with pytest.raises(ValueError, match="GPU device"):
+        kda.kda_segment_summary(t["k"], t["v"], t["g"], t["beta"], A_log=t["A_log"], gate_in_kernel=True)
+    with pytest.raises(ValueError, match="GPU device"):
+        kda.kda_summary_merge(torch.zeros(2, 4, 64, 64), torch.zeros(2, 4, 64, 64), torch.zeros(4, 64, 64))
+    with pytest.raises(ValueError, match="M has shape"):
+        kda.kda_summary_merge(torch.zeros(2, 4, 64, 32), torch.zeros(2, 4, 64, 64), torch.zeros(4, 64, 64))
+
+
+def test_binding_tnd_needs_matching_cu_seqlens(lib):
+    z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    t = dict(q=z(70, 2, 64), k=z(70, 2, 64), v=z(70, 2, 64), g=z(70, 2, 64), beta=z(70, 2),
+             A_log=torch.zeros(2), dt_bias=None)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        _fwd(t)
+    with pytest.raises(ValueError, match="same length"):
+        _fwd(t, cu_seqlens=torch.tensor([0, 70], dtype=torch.int32),
+             cu_seqlens_host=torch.tensor([0, 30, 70], dtype=torch.int32))

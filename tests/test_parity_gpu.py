@@ -5,6 +5,7 @@ Bars: bf16 outputs err_max <= 2e-2; fp32 states, summaries and merged states
 Small cases span several 64-token chunks with a ragged tail; full-size cases
 compare sampled heads (every token and state entry of those heads).
 """
+import dataclasses
 import math
 import sys
 
@@ -169,6 +170,86 @@ def test_varlen_cache_out_of_range_index_reads_zero(gpu_lib):
     check("cache", np64(cache), rcache, TOL_STATE)
 
 
+def test_eps_zero_ragged_tail(gpu_lib):
+    """eps = 0 with the in-kernel L2Norm and T % 64 != 0: the rows past the
+    sequence end carry zero norms and must stay inert (no 0 * inf)."""
+    p = ks.make("layer", T=65, H=2)
+    p.eps = 0.0
+    fwd_case(gpu_lib, p)
+
+
+def test_fp32_k128(gpu_lib):
+    fwd_case(gpu_lib, ks.make("layer", T=150, H=2, K=128, V=128, dtype="f32"))
+
+
+def test_varlen_duplicate_gather_indices(gpu_lib):
+    """Two sequences may start from the same cache row when nothing is written
+    back (vllm-ascend KDA prefill state copy page, numeric contract)."""
+    p = ks.make("varlen", lens=[70, 33, 130], H=2, cache_rows=4, n_invalid=0)
+    p.state_indices = np.array([1, 3, 1], dtype=np.int32)
+    t = to_torch(p)
+    before = t["h0"].clone()
+    o, fin = gpu_lib.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=p.scale,
+                                   A_log=t["A_log"], dt_bias=t["dt_bias"], initial_state=t["h0"],
+                                   cu_seqlens=t["cu"], cu_seqlens_host=t["cu_host"],
+                                   state_indices=t["state_indices"], output_final_state=False,
+                                   **flag_kwargs(p))
+    torch.cuda.synchronize()
+    assert fin is None and torch.equal(t["h0"], before)
+    ro, _ = orc.forward(p)
+    check("o", np64(o), ro, TOL_BF16_OUT)
+
+
+def test_nan_input_propagates(gpu_lib):
+    """A NaN in one value row: every output the oracle makes NaN is NaN on the
+    GPU too, the chunks before it are unaffected and nothing faults."""
+    p = ks.make("layer", T=200, H=2)
+    p.v = p.v.copy()
+    p.v[0, 100, 1, 7] = np.nan
+    o, f = run_fwd(gpu_lib, p)
+    ro, rf = orc.forward(p)
+    go, gf = np64(o), np64(f)
+    assert np.isnan(go[np.isnan(ro)]).all() and np.isnan(gf[np.isnan(rf)]).all()
+    assert np.isnan(rf).any()
+    check("o before the NaN chunk", go[:, :64], ro[:, :64], TOL_BF16_OUT)
+    check("head 0", go[:, :, 0], ro[:, :, 0], TOL_BF16_OUT)
+
+
+def test_empty_selection(gpu_lib):
+    """N = 0 sequences: nothing is launched and nothing is written."""
+    z = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o, f = gpu_lib.kda_chunk_fwd(z, z, z, z, torch.zeros((0, 2), dtype=torch.bfloat16, device="cuda"),
+                                 cu_seqlens=cu, cu_seqlens_host=cu.cpu())
+    torch.cuda.synchronize()
+    assert o.shape == (0, 2, 128) and f.shape == (0, 2, 128, 128)
+
+
+def test_state_cache_beyond_4GiB(gpu_lib):
+    """Cache rows whose byte offsets exceed 2^32: gather and scatter use 64-bit
+    addresses (a 32-bit offset would touch row r - 32768 instead)."""
+    p = ks.make("varlen", lens=[90, 40], H=2, cache_rows=2, n_invalid=0)
+    rows = 33000                                        # 128 KiB per row: 4.3 GB
+    cache = torch.zeros((rows, 2, 128, 128), dtype=torch.float32, device="cuda")
+    cache[32990] = torch.from_numpy(p.h0[0]).cuda()
+    t = to_torch(p)
+    si = torch.tensor([32990, 32999], dtype=torch.int32, device="cuda")
+    o, cache = gpu_lib.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=p.scale,
+                                     A_log=t["A_log"], dt_bias=t["dt_bias"], initial_state=cache,
+                                     cu_seqlens=t["cu"], cu_seqlens_host=t["cu_host"],
+                                     state_indices=si, **flag_kwargs(p))
+    torch.cuda.synchronize()
+    # the same problem on a two-row cache [row 32990, zeros] with indices [0, 1]
+    ref = dataclasses.replace(p, h0=np.stack([p.h0[0], np.zeros_like(p.h0[0])]),
+                              state_indices=np.array([0, 1], dtype=np.int32))
+    ro, rcache = orc.forward(ref)
+    check("o", np64(o), ro, TOL_BF16_OUT)
+    check("row 32990", np64(cache[32990]), rcache[0], TOL_STATE)
+    check("row 32999", np64(cache[32999]), rcache[1], TOL_STATE)
+    assert not cache[32990 - 32768].any() and not cache[32999 - 32768].any()
+    del cache
+
+
 def test_gqa_small_safe_gate(gpu_lib):
     fwd_case(gpu_lib, ks.make("gqa", B=2, T=150, Hk=2, Hv=8))
 
@@ -265,6 +346,29 @@ def test_summary_small_matches_oracle(gpu_lib):
     check("S~", np64(S), rS, TOL_STATE)
 
 
+@pytest.mark.parametrize("route", ["precomputed", "in_kernel"])
+def test_summary_deep_transition(gpu_lib, route):
+    """M over 64 chunks in a regime where it stays O(0.1-1): a near-zero
+    precomputed gate with small beta, or the in-kernel gate with small A_log
+    (every chunk's transition passes the kg^T lo part of the scan)."""
+    p = ks.make("layer", T=4096, H=4, h0_std=0.0)
+    rng = np.random.default_rng(11)
+    if route == "precomputed":
+        p.gate_in_kernel = False
+        p.g = ks.bf16_round((-2e-4 * rng.random(p.g.shape)).astype(np.float32))
+        p.beta = ks.bf16_round((rng.standard_normal(p.beta.shape) - 5.0).astype(np.float32))
+    else:
+        p.A_log = np.log(np.array([1e-4, 3e-4, 1e-3, 2e-4], dtype=np.float32))
+        p.dt_bias = np.full_like(p.dt_bias, -6.0)
+        p.beta = ks.bf16_round((rng.standard_normal(p.beta.shape) - 5.0).astype(np.float32))
+    M, S = _summary_gpu(gpu_lib, p)
+    rM, rS = orc.segment_summary(p)
+    say(f"  max|M| = {np.abs(rM).max():.3f}, max|M - I| = {np.abs(rM - np.eye(p.K)).max():.3f}")
+    assert 0.1 < np.abs(rM).max() and np.abs(rM - np.eye(p.K)).max() > 0.05
+    check("M", np64(M), rM, TOL_STATE)
+    check("S~", np64(S), rS, TOL_STATE)
+
+
 def test_summary_varlen_matches_oracle(gpu_lib):
     p = ks.make("varlen", lens=[20, 0, 129], H=2, cache_rows=3, n_invalid=0)
     p.state_indices, p.h0 = None, None
@@ -302,7 +406,15 @@ def _segment_case(kda, p, heads):
     t = to_torch(p)
     M, S = _summary_gpu(kda, p, t)
     rM, rS = orc.segment_summary(p, heads=heads)
-    check("segment M", np64(M)[:, heads], rM[:, heads], TOL_STATE)
+    if np.abs(rM[:, heads]).max() == 0.0:
+        # The layer gate (A_log up to ln 16) decays the transition to exact
+        # zeros over a segment of this length: the check is then that the GPU
+        # returns exact zeros too.  Non-trivial M over many chunks is checked
+        # by test_summary_deep_transition.
+        say("  segment M: the oracle's transition is exactly zero; GPU must match it exactly")
+        assert np.abs(np64(M)[:, heads]).max() == 0.0
+    else:
+        check("segment M", np64(M)[:, heads], rM[:, heads], TOL_STATE)
     check("segment S~", np64(S)[:, heads], rS[:, heads], TOL_STATE)
     p.h0 = state.cpu().numpy()[None]
     t["h0"] = state[None].contiguous()
