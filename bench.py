@@ -262,14 +262,15 @@ def traffic_for(kernels):
     return sum(d[k]["bytes_per_launch"] for k in kernels)
 
 
-def _per_kernel_counters(path):
+def _per_dispatch_counters(path):
+    """{kernel: {counter: [value per dispatch]}} from a rocprofv3 counter CSV
+    (one row per dispatch and counter, already summed over the chip)."""
     import csv
     vals = {}
     for r in csv.DictReader(open(path)):
-        name = r["Kernel_Name"]
-        vals.setdefault(name, {}).setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
-        vals[name][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
-    return {k: {c: statistics.mean(d.values()) for c, d in cs.items()} for k, cs in vals.items()}
+        d = vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], {})
+        d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {k: {c: list(d.values()) for c, d in cs.items()} for k, cs in vals.items()}
 
 
 SHORT = (("intra_kernel", "intra_kernel"), ("scan_kernel", "scan_kernel"))
@@ -278,11 +279,11 @@ SHORT = (("intra_kernel", "intra_kernel"), ("scan_kernel", "scan_kernel"))
 def summarize_pmc(fetch_csv, write_csv, copy_bytes, out_json):
     """Per-launch HBM bytes of each KDA kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
     runs, scaled by what the same counters read for the calibration copy of
-    ``copy_bytes`` bytes (read once, written once)."""
-    fetch, write = _per_kernel_counters(fetch_csv), _per_kernel_counters(write_csv)
-    copy_name = max((k for k in fetch if "copy" in k.lower()), key=lambda k: fetch[k]["FETCH_SIZE"])
-    cf = copy_bytes / (fetch[copy_name]["FETCH_SIZE"] * 1024.0)
-    cw = copy_bytes / (write[copy_name]["WRITE_SIZE"] * 1024.0)
+    ``copy_bytes`` bytes (read once, written once: its largest dispatch)."""
+    fetch, write = _per_dispatch_counters(fetch_csv), _per_dispatch_counters(write_csv)
+    copy_name = max((k for k in fetch if "copy" in k.lower()), key=lambda k: max(fetch[k]["FETCH_SIZE"]))
+    cf = copy_bytes / (max(fetch[copy_name]["FETCH_SIZE"]) * 1024.0)
+    cw = copy_bytes / (max(write[copy_name]["WRITE_SIZE"]) * 1024.0)
     out = {"source_sha256": source_hash(),
            "calibration": {"kernel": copy_name, "bytes": copy_bytes, "fetch_factor": cf, "write_factor": cw}}
     lines = [f"calibration copy {copy_name}: {copy_bytes / 1e6:.1f} MB read + written; "
@@ -292,44 +293,50 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes, out_json):
         if not names:
             continue
         k = names[0]
-        fb = fetch[k]["FETCH_SIZE"] * 1024.0 * cf
-        wb = write[k]["WRITE_SIZE"] * 1024.0 * cw
-        out[short] = {"kernel": k, "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+        fb = statistics.mean(fetch[k]["FETCH_SIZE"]) * 1024.0 * cf
+        wb = statistics.mean(write[k]["WRITE_SIZE"]) * 1024.0 * cw
+        out[short] = {"kernel": k, "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                      "launches": len(fetch[k]["FETCH_SIZE"])}
         lines.append(f"{short}: fetch {fb / 1e6:.1f} MB + write {wb / 1e6:.1f} MB = "
-                     f"{(fb + wb) / 1e6:.1f} MB per launch")
+                     f"{(fb + wb) / 1e6:.1f} MB per launch ({len(fetch[k]['FETCH_SIZE'])} launches)")
     with open(out_json, "w") as fh:
         json.dump(out, fh, indent=1)
     return "\n".join(lines)
 
 
-CU_NUM, SIMD_PER_CU, CLOCK_GHZ = 256, 4, 2.4
+CU_NUM, SIMD_NUM, XCD_NUM, CLOCK_GHZ = 256, 1024, 8, 2.4
 
 
 def summarize_mfma(csv_path, out_json):
     """Matrix-core and vector-ALU activity per kernel from one rocprofv3 --pmc
     run of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_{BF16,F32,F8},
     SQ_INSTS_VALU, SQ_ACTIVE_INST_VALU, SQ_BUSY_CU_CYCLES and GRBM_GUI_ACTIVE.
-    MFMA util = busy cycles / (GUI-active cycles x SIMDs); MOPS count 512 flop each."""
-    data = _per_kernel_counters(csv_path)
+    GRBM_GUI_ACTIVE is summed over the XCDs: one XCD's count is the kernel's
+    cycles.  MFMA util = busy cycles / (kernel cycles x SIMDs); VALU active =
+    4 x SQ_ACTIVE_INST_VALU (quad-cycles) / (kernel cycles x SIMDs); each
+    MOPS counts 512 flop."""
+    data = _per_dispatch_counters(csv_path)
     out = {"source_sha256": source_hash()}
     lines = []
     for short, key in SHORT:
         names = [k for k in data if key in k]
         if not names:
             continue
-        c = data[names[0]]
-        gui = c.get("GRBM_GUI_ACTIVE", 0.0)
-        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
-        util = busy / (gui * CU_NUM * SIMD_PER_CU) if gui else None
+        c = {n: statistics.mean(v) for n, v in data[names[0]].items()}
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / XCD_NUM
+        us = cyc / (CLOCK_GHZ * 1e3)
+        util = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * SIMD_NUM) if cyc else None
         flops = {d: c.get(f"SQ_INSTS_VALU_MFMA_MOPS_{d}", 0.0) * 512 for d in ("BF16", "F32", "F8")}
-        valu_busy = (c.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (gui * CU_NUM * SIMD_PER_CU)) if gui else None
-        out[short] = {"kernel": names[0], "counters": c, "mfma_util": util, "mfma_flop": flops,
-                      "valu_insts": c.get("SQ_INSTS_VALU"), "valu_active_frac": valu_busy,
-                      "gui_active_cycles": gui}
-        lines.append(f"{short}: MFMA busy {100 * util:.1f}% of SIMD cycles; MFMA flop bf16 "
-                     f"{flops['BF16'] / 1e9:.2f} G, f32 {flops['F32'] / 1e9:.3f} G, f8 "
-                     f"{flops['F8'] / 1e9:.3f} G; VALU insts {c.get('SQ_INSTS_VALU', 0) / 1e6:.1f} M, "
-                     f"VALU active {100 * valu_busy:.1f}% of SIMD cycles; GUI active {gui:.0f} cycles")
+        valu = c.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (cyc * SIMD_NUM) if cyc else None
+        bf16_frac = flops["BF16"] / (us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12) if us else None
+        out[short] = {"kernel": names[0], "counters_mean_per_dispatch": c, "kernel_cycles": cyc,
+                      "kernel_us_from_counter": us, "mfma_busy_frac": util, "mfma_flop": flops,
+                      "bf16_mfma_flop_frac_of_peak": bf16_frac, "valu_insts": c.get("SQ_INSTS_VALU"),
+                      "valu_active_frac": valu}
+        lines.append(f"{short}: {us:.1f} us; MFMA busy {100 * util:.1f}% of SIMD cycles; MFMA flop bf16 "
+                     f"{flops['BF16'] / 1e9:.2f} G ({100 * bf16_frac:.1f}% of the bf16 peak over the kernel), "
+                     f"f32 {flops['F32'] / 1e9:.3f} G, f8 {flops['F8'] / 1e9:.3f} G; VALU insts "
+                     f"{c.get('SQ_INSTS_VALU', 0) / 1e6:.1f} M, VALU active {100 * valu:.1f}% of SIMD cycles")
     with open(out_json, "w") as fh:
         json.dump(out, fh, indent=1)
     return "\n".join(lines)
@@ -438,8 +445,10 @@ def main():
                      "frac": step_gbs / PEAK_HBM_GBS, "traffic": traffic},
     }
     if mfma:
-        res["mfma_counters"] = {k: {"mfma_util": v["mfma_util"], "valu_active_frac": v["valu_active_frac"]}
-                                for k, v in mfma.items() if isinstance(v, dict) and "mfma_util" in v}
+        res["mfma_counters"] = {k: {"mfma_busy_frac": v["mfma_busy_frac"],
+                                    "bf16_mfma_flop_frac_of_peak": v["bf16_mfma_flop_frac_of_peak"],
+                                    "valu_active_frac": v["valu_active_frac"]}
+                                for k, v in mfma.items() if isinstance(v, dict) and "mfma_busy_frac" in v}
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on about {args.cpu_token_heads} token-heads ...")
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_token_heads)
