@@ -173,6 +173,28 @@ def setup(name, dev, hev):
                     config={"T": p.T, "H": Hv, "dk": K, "dv": V, "preceding_summaries": P})
         return step, meta
 
+    if name == "decode":
+        o = torch.empty_like(t["v"])
+        n_valid = int((p.state_indices >= 0).sum())
+
+        def step(m):
+            if m is not None:
+                hev.record(m[0], stream)
+            kda.kda_recurrent_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=p.scale,
+                                  A_log=t["A_log"], dt_bias=t["dt_bias"], initial_state=t["h0"],
+                                  cu_seqlens=t["cu"], cu_seqlens_host=t["cu_host"],
+                                  state_indices=t["state_indices"], o=o, **kw)
+            if m is not None:
+                hev.record(m[1], stream)
+
+        # per token and head: K*V for the decay, 2*K*V each for S^T k, the write and S^T q
+        meta = dict(p=p, flop=th * 7 * K * V, bytes=token_bytes(p) + 2 * n_valid * state, nmarks=2,
+                    intervals={"recurrent_kernel": (0, 1)},
+                    own_bytes={"recurrent_kernel": token_bytes(p) + 2 * n_valid * state},
+                    config={"seqs": N, "tokens_per_seq": p.T // N, "H": Hv, "dk": K, "dv": V,
+                            "state_cache_rows": int(p.h0.shape[0]), "valid_indices": n_valid})
+        return step, meta
+
     cache = p.state_indices is not None
     o = torch.empty_like(t["v"])
     if cache:
@@ -206,6 +228,7 @@ WORKLOAD_TEXT = {
     "varlen": "packed varlen prefill with a state cache (16 sequences, lengths U[512, 8192])",
     "segment": "one segment of a 1M-token sequence: summary + merge of 7 preceding summaries + forward",
     "gqa": "GQA long batch forward (16 q/k heads shared by 64 value heads, safe gate)",
+    "decode": "decode step: one token for each of 64 sequences, state cache updated in place",
 }
 
 

@@ -300,6 +300,41 @@ kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const vo
   return ok();
 }
 
+kda_status_t kda_recurrent_fwd(const kda_problem_t* p, const void* q, const void* k, const void* v,
+                               const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                               const float* initial_state, const int32_t* cu_seqlens,
+                               const int32_t* state_indices, void* o, float* final_state, void* stream) {
+  Plan pl;
+  kda_status_t st = plan_problem(p, true, pl);
+  if (st != KDA_OK) return st;
+  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, cu_seqlens)) != KDA_OK) return st;
+  if (pl.tokens > 0) {
+    if ((st = check_token_ptr(q, "q", 16)) != KDA_OK) return st;
+    if ((st = check_token_ptr(o, "o", 16)) != KDA_OK) return st;
+  }
+  if (p->state_rows > 0 && !state_indices)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "state_rows > 0 needs state_indices");
+  if (p->state_rows == 0 && state_indices)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "state_indices given without a state cache (state_rows == 0)");
+  if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "states must be 16-byte aligned");
+  if (pl.N == 0) return ok();
+  kda::RecurrentArgs a{};
+  a.seq.tnd = p->layout == KDA_LAYOUT_TND;
+  a.seq.T = p->T;
+  a.seq.N = pl.N;
+  a.seq.cu = cu_seqlens;
+  a.seq.chunk_off = nullptr;   // the recurrent kernel walks tokens, not chunks
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.A_log = A_log; a.dt_bias = dt_bias;
+  a.Hk = p->Hk; a.Hv = p->Hv; a.state_rows = p->state_rows;
+  a.flags = p->flags; a.scale = p->scale; a.eps = p->eps; a.lower_bound = p->lower_bound;
+  a.h0 = initial_state; a.state_idx = state_indices; a.hT = final_state; a.o = o;
+  if ((st = hip_status(kda::launch_recurrent(p->K, p->V, p->dtype, a, static_cast<hipStream_t>(stream)),
+                       "recurrent kernel launch")) != KDA_OK)
+    return st;
+  return ok();
+}
+
 kda_status_t kda_summary_merge(int32_t P, int32_t Hv, int32_t K, int32_t V, const float* M,
                                const float* S_tilde, float* state, void* stream) {
   if (P < 0 || Hv < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "need P >= 0 and Hv >= 1 (P=%d Hv=%d)", P, Hv);

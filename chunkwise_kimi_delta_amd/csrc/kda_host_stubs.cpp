@@ -9,4 +9,5 @@ hipError_t launch_chunk_offsets(const int32_t*, int, int32_t*, hipStream_t) { re
 hipError_t launch_intra(int, int, int, const IntraArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_scan(int, int, int, const ScanArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_merge(int, int, const MergeArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_recurrent(int, int, int, const RecurrentArgs&, hipStream_t) { return hipSuccess; }
 }  // namespace kda

@@ -139,12 +139,12 @@ __device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-// Two workgroups per CU, except fp32 tokens with K = 128, whose LDS (about
-// 108 KB) leaves room for one.
-template <int KD, typename IT> constexpr int intra_min_blocks() { return (sizeof(IT) == 4 && KD == 128) ? 1 : 2; }
+// Two workgroups per CU, except fp32 tokens with K or V = 128, whose LDS
+// (89 - 108 KB) leaves room for one.
+template <int KD, int VD, typename IT> constexpr int intra_min_blocks() { return (sizeof(IT) == 4 && (KD == 128 || VD == 128)) ? 1 : 2; }
 
 template <int KD, int VD, typename IT, bool FWD>
-__global__ __launch_bounds__(256, (intra_min_blocks<KD, IT>())) void intra_kernel(IntraArgs a) {
+__global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_kernel(IntraArgs a) {
   using ST = IT;                                   // workspace type of w, qg, Aqk
   constexpr bool F32 = sizeof(IT) == 4;
   constexpr int NKS = KD / 32, NVS = VD / 32;

@@ -90,6 +90,20 @@ struct ScanArgs {
   void* o;                            // [tokens,Hv,V]
 };
 
+// Token-by-token forward (decode).  One wave per (64-column slice, head, sequence).
+struct RecurrentArgs {
+  SeqInfo seq;
+  const void *q, *k, *v, *g, *beta;
+  const float *A_log, *dt_bias;
+  int Hk, Hv, state_rows;
+  uint32_t flags;
+  float scale, eps, lower_bound;
+  const float* h0;                    // [N,Hv,K,V] | cache | null
+  const int32_t* state_idx;           // cache mode
+  float* hT;                          // final [N,Hv,K,V] | cache | null (may equal h0)
+  void* o;                            // [tokens,Hv,V]
+};
+
 struct MergeArgs {
   int P, Hv;
   const float *M, *S;
@@ -110,5 +124,6 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
 hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t s);
 hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s);
 hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s);
+hipError_t launch_recurrent(int K, int V, int dtype, const RecurrentArgs& a, hipStream_t s);
 
 }  // namespace kda

@@ -45,7 +45,7 @@ class KdaProblem(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_segment_summary_workspace_size",
-           "kda_segment_summary", "kda_summary_merge", "kda_chunk_offsets_host",
+           "kda_segment_summary", "kda_summary_merge", "kda_recurrent_fwd", "kda_chunk_offsets_host",
            "kda_status_string", "kda_last_error", "kda_abi_version")
 ABI_VERSION = 2
 STAGE_EVENTS = 3
@@ -65,13 +65,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd.argtypes = [P] + [VP] * 13 + [SZ, VP, VP]
     lib.kda_segment_summary.argtypes = [P] + [VP] * 10 + [SZ, VP, VP]
     lib.kda_summary_merge.argtypes = [I32, I32, I32, I32, VP, VP, VP, VP]
+    lib.kda_recurrent_fwd.argtypes = [P] + [VP] * 12 + [VP]
     lib.kda_chunk_offsets_host.argtypes = [VP, I32, I32, VP]
     lib.kda_status_string.argtypes = [I32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_abi_version.restype = I32
     for name in ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_segment_summary_workspace_size",
-                 "kda_segment_summary", "kda_summary_merge", "kda_chunk_offsets_host"):
+                 "kda_segment_summary", "kda_summary_merge", "kda_recurrent_fwd", "kda_chunk_offsets_host"):
         getattr(lib, name).restype = I32
     if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{path} has ABI version {lib.kda_abi_version()}, expected {ABI_VERSION}: rebuild it")
@@ -171,20 +172,11 @@ def _cu_pair(cu_seqlens, cu_seqlens_host, device, tokens: torch.Tensor):
     return cu_d, cu_h
 
 
-def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None, dt_bias=None,
-                  initial_state=None, cu_seqlens=None, cu_seqlens_host=None, state_indices=None,
-                  output_final_state: bool = True, gate_in_kernel: bool = False,
-                  safe_gate: bool = False, lower_bound: float = -5.0, qk_l2norm: bool = False,
-                  beta_sigmoid: bool = False, eps: float = 1e-6, o=None, final_state=None,
-                  workspace=None, stage_events=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunkwise KDA forward.  Returns (o, final_state).
-
-    With ``state_indices`` the ``initial_state`` is a state cache
-    [rows,Hv,K,V]; final states are scattered into ``final_state`` (default:
-    the same cache, in place) and that cache is returned.  ``stage_events``:
-    three raw hipEvent_t handles the call records at its stage boundaries.
-    """
-    lib = load()
+def _forward_args(q, k, v, g, beta, *, scale, A_log, dt_bias, initial_state, cu_seqlens,
+                  cu_seqlens_host, state_indices, output_final_state, gate_in_kernel, safe_gate,
+                  lower_bound, qk_l2norm, beta_sigmoid, eps, o, final_state):
+    """Checks and marshalling shared by the forward calls: every tensor's shape,
+    dtype, layout and device, then the problem descriptor and the outputs."""
     if q.dim() not in (3, 4) or v.dim() != q.dim():
         raise ValueError("token tensors are [B,T,H,D] or [T,H,D], q and v alike")
     lead, Hk, K = tuple(q.shape[:-2]), q.shape[-2], q.shape[-1]
@@ -218,25 +210,24 @@ def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None
         _need(state_indices, "state_indices", None, (N,))
         _need(final_state, "final_state", torch.float32, (rows, Hv, K, V))
     else:
+        rows = 0
         _need(initial_state, "initial_state", torch.float32, (N, Hv, K, V))
         _need(final_state, "final_state", torch.float32, (N, Hv, K, V))
     _need(o, "o", v.dtype, v.shape)
     dev = _gpu_device(v)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (A_log, "A_log"),
-                 (dt_bias, "dt_bias"), (initial_state, "initial_state"), (final_state, "final_state")):
+                 (dt_bias, "dt_bias"), (initial_state, "initial_state"), (final_state, "final_state"),
+                 (o, "o")):
         _need(t, n, device=dev)
     cu_d, cu_h = _cu_pair(cu_seqlens, cu_seqlens_host, dev, q)
-    _need(o, "o", device=dev)
     if scale is None:
-        scale = q.shape[-1] ** -0.5
+        scale = K ** -0.5
     flags = ((KDA_GATE_IN_KERNEL if gate_in_kernel else 0) | (KDA_SAFE_GATE if safe_gate else 0)
              | (KDA_QK_L2NORM if qk_l2norm else 0) | (KDA_BETA_SIGMOID if beta_sigmoid else 0))
-    rows = initial_state.shape[0] if cache else 0
     p, N = make_problem(q, v, scale=scale, flags=flags, eps=eps, lower_bound=lower_bound,
                         cu_host=cu_h, state_rows=rows)
     if o is None:
         o = torch.empty(v.shape, dtype=v.dtype, device=dev)
-    K, V, Hv = q.shape[-1], v.shape[-1], v.shape[-2]
     if cache:
         si = state_indices.to(device=dev, dtype=torch.int32).contiguous()
         if final_state is None and output_final_state:
@@ -245,6 +236,29 @@ def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None
         si = None
         if final_state is None and output_final_state:
             final_state = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev)
+    return p, dev, cu_d, si, o, final_state
+
+
+def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None, dt_bias=None,
+                  initial_state=None, cu_seqlens=None, cu_seqlens_host=None, state_indices=None,
+                  output_final_state: bool = True, gate_in_kernel: bool = False,
+                  safe_gate: bool = False, lower_bound: float = -5.0, qk_l2norm: bool = False,
+                  beta_sigmoid: bool = False, eps: float = 1e-6, o=None, final_state=None,
+                  workspace=None, stage_events=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA forward.  Returns (o, final_state).
+
+    With ``state_indices`` the ``initial_state`` is a state cache
+    [rows,Hv,K,V]; final states are scattered into ``final_state`` (default:
+    the same cache, in place) and that cache is returned.  ``stage_events``:
+    three raw hipEvent_t handles the call records at its stage boundaries.
+    """
+    lib = load()
+    p, dev, cu_d, si, o, final_state = _forward_args(
+        q, k, v, g, beta, scale=scale, A_log=A_log, dt_bias=dt_bias, initial_state=initial_state,
+        cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, state_indices=state_indices,
+        output_final_state=output_final_state, gate_in_kernel=gate_in_kernel, safe_gate=safe_gate,
+        lower_bound=lower_bound, qk_l2norm=qk_l2norm, beta_sigmoid=beta_sigmoid, eps=eps, o=o,
+        final_state=final_state)
     ws_bytes = ctypes.c_size_t()
     _check(lib.kda_chunk_fwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
     if workspace is None:
@@ -254,6 +268,28 @@ def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None
                              _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_d), _ptr(si),
                              _ptr(o), _ptr(final_state), _ptr(workspace), workspace.numel(),
                              _stream(dev), _events(stage_events)))
+    return o, final_state
+
+
+def kda_recurrent_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None, dt_bias=None,
+                      initial_state=None, cu_seqlens=None, cu_seqlens_host=None, state_indices=None,
+                      output_final_state: bool = True, gate_in_kernel: bool = False,
+                      safe_gate: bool = False, lower_bound: float = -5.0, qk_l2norm: bool = False,
+                      beta_sigmoid: bool = False, eps: float = 1e-6, o=None, final_state=None
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Token-by-token KDA forward (decode: a few tokens per sequence, the state
+    cache updated in place).  Same arguments and results as ``kda_chunk_fwd``;
+    no workspace."""
+    lib = load()
+    p, dev, cu_d, si, o, final_state = _forward_args(
+        q, k, v, g, beta, scale=scale, A_log=A_log, dt_bias=dt_bias, initial_state=initial_state,
+        cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, state_indices=state_indices,
+        output_final_state=output_final_state, gate_in_kernel=gate_in_kernel, safe_gate=safe_gate,
+        lower_bound=lower_bound, qk_l2norm=qk_l2norm, beta_sigmoid=beta_sigmoid, eps=eps, o=o,
+        final_state=final_state)
+    _check(lib.kda_recurrent_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_d), _ptr(si),
+                                 _ptr(o), _ptr(final_state), _stream(dev)))
     return o, final_state
 
 

@@ -168,6 +168,25 @@ kda_status_t kda_summary_merge(int32_t P, int32_t Hv, int32_t K, int32_t V,
                                const float* M, const float* S_tilde, float* state,
                                void* stream);
 
+/*
+ * Token-by-token KDA forward for decode ("vllm-ascend KDA prefill state copy"
+ * page, background section: the recurrent step that follows a prefill, one
+ * token per sequence with the state cache updated in place).  Same problem
+ * descriptor, tensors and state conventions as kda_chunk_fwd, any sequence
+ * length (each sequence's tokens are applied in order, the state kept in
+ * registers), no workspace.  It is meant for a few tokens per sequence: its
+ * cost is the state's round trip through HBM plus K*V*8 flop per token and
+ * head; longer sequences belong to kda_chunk_fwd.  With a state cache,
+ * initial_state and final_state may be the same buffer (in place).
+ */
+kda_status_t kda_recurrent_fwd(const kda_problem_t* p,
+                               const void* q, const void* k, const void* v,
+                               const void* g, const void* beta,
+                               const float* A_log, const float* dt_bias,
+                               const float* initial_state, const int32_t* cu_seqlens,
+                               const int32_t* state_indices,
+                               void* o, float* final_state, void* stream);
+
 /* Chunk map of packed sequences (host only, no device work): given host
  * cu_seqlens [N+1] and a chunk size, writes chunk_offsets_host [N+1] with the
  * index of each sequence's first chunk (a chunk never spans two sequences and

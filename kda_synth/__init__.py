@@ -253,12 +253,42 @@ def make_gqa(seed=1004, B=4, T=16384, Hk=16, Hv=64, K=128, V=128, dtype="bf16") 
                    A_log=A_log, dt_bias=dt_bias, h0=h0)
 
 
+def make_decode(seed=1005, n_seqs=64, tokens=1, H=32, K=128, V=128, dtype="bf16", cache_rows=128,
+                n_invalid=2, lens=None) -> Problem:
+    """Decode step after a prefill: ``tokens`` new tokens for each of ``n_seqs``
+    sequences (TND), initial states gathered from a state cache by index and
+    final states scattered back in place; the layer's gate, L2Norm and sigmoid.
+    ``lens`` overrides the per-sequence token counts."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = np.full(n_seqs, tokens, dtype=np.int64) if lens is None else np.asarray(lens, dtype=np.int64)
+    n_seqs = len(lens)
+    cu = np.zeros(n_seqs + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    T = int(cu[-1])
+    q = _store(_normal(rng, (T, H, K)), dtype)
+    k = _store(_normal(rng, (T, H, K)), dtype)
+    v = _store(_normal(rng, (T, H, V)), dtype)
+    g = _store(_normal(rng, (T, H, K)), dtype)
+    b = _store(_normal(rng, (T, H)), dtype)
+    A_log, dt_bias = _kimi_gate_params(rng, H, K)
+    cache = _normal(rng, (cache_rows, H, K, V), 0.02)
+    idx = rng.permutation(cache_rows)[:n_seqs].astype(np.int32)
+    if n_invalid:
+        bad = rng.choice(n_seqs, size=n_invalid, replace=False)
+        idx[bad] = -1
+    return Problem(name="decode", layout="tnd", dtype=dtype, B=1, T=T, Hk=H, Hv=H, K=K, V=V,
+                   q=q, k=k, v=v, g=g, beta=b, scale=1.0 / math.sqrt(K),
+                   gate_in_kernel=True, l2norm=True, beta_sigmoid=True,
+                   A_log=A_log, dt_bias=dt_bias, h0=cache, cu_seqlens=cu, state_indices=idx)
+
+
 WORKLOADS = {
     "tiny": make_tiny,
     "layer": make_layer,
     "varlen": make_varlen,
     "segment": make_segment,
     "gqa": make_gqa,
+    "decode": make_decode,
 }
 
 

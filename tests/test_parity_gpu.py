@@ -323,6 +323,67 @@ def test_graph_capture_replays_match_eager(gpu_lib):
         assert not torch.equal(og, torch.zeros_like(og))
 
 
+# ------------------------------------------------------ recurrent (decode)
+def run_rec(kda, p, t=None, **over):
+    t = t or to_torch(p)
+    kw = flag_kwargs(p)
+    kw.update(over)
+    o, f = kda.kda_recurrent_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=p.scale,
+                                 A_log=t["A_log"], dt_bias=t["dt_bias"],
+                                 initial_state=None if p.h0 is None else t["h0"],
+                                 cu_seqlens=t["cu"], cu_seqlens_host=t["cu_host"],
+                                 state_indices=t["state_indices"], **kw)
+    torch.cuda.synchronize()
+    return o, f
+
+
+def test_recurrent_decode_step(gpu_lib):
+    """One token for each of 64 sequences, states gathered from and scattered
+    back into the cache in place; rows no valid index selects stay untouched."""
+    p = ks.make("decode")
+    before = p.h0.copy()
+    o, cache = run_rec(gpu_lib, p)
+    ro, rcache = orc.forward(p)
+    check("o", np64(o), ro, TOL_BF16_OUT)
+    check("cache", np64(cache), rcache, 1e-5)
+    got = cache.cpu().numpy()
+    touched = set(int(i) for i in p.state_indices if i >= 0)
+    for r in range(p.h0.shape[0]):
+        if r not in touched:
+            assert np.array_equal(got[r], before[r]), f"row {r} changed"
+
+
+def test_recurrent_multi_token_and_empty_sequences(gpu_lib):
+    p = ks.make("decode", lens=[1, 3, 0, 7, 2, 0], H=3, cache_rows=9, n_invalid=1)
+    o, cache = run_rec(gpu_lib, p)
+    ro, rcache = orc.forward(p)
+    check("o", np64(o), ro, TOL_BF16_OUT)
+    check("cache", np64(cache), rcache, 1e-5)
+
+
+@pytest.mark.parametrize("K,V", [(64, 64), (64, 128), (128, 64)])
+def test_recurrent_head_dims_fp32_dense_states(gpu_lib, K, V):
+    """fp32 tokens, dense initial/final states, BSND, grouped heads, safe gate."""
+    p = ks.make("gqa", B=2, T=5, Hk=2, Hv=4, K=K, V=V, dtype="f32")
+    o, f = run_rec(gpu_lib, p)
+    ro, rf = orc.forward(p)
+    check("o", np64(o), ro, 1e-5)
+    check("final_state", np64(f), rf, 1e-5)
+
+
+def test_recurrent_equals_chunked_forward(gpu_lib):
+    """Both forms of the method on the same 200-token layer problem."""
+    p = ks.make("layer", T=200, H=2)
+    t = to_torch(p)
+    oc, fc = run_fwd(gpu_lib, p, t)
+    orr, fr = run_rec(gpu_lib, p, t)
+    check("o recurrent vs chunked", np64(orr), np64(oc), TOL_BF16_OUT)
+    check("final recurrent vs chunked", np64(fr), np64(fc), TOL_STATE)
+    ro, rf = orc.forward(p)
+    check("o recurrent vs oracle", np64(orr), ro, TOL_BF16_OUT)
+    check("final recurrent vs oracle", np64(fr), rf, 1e-5)
+
+
 # ---------------------------------------------------------- summary and merge
 def _summary_gpu(kda, p, t=None):
     t = t or to_torch(p)
