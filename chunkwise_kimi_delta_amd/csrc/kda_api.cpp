@@ -300,6 +300,28 @@ kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const vo
   return ok();
 }
 
+kda_status_t kda_chunk_fwd_noalloc(const kda_problem_t* p, const void* q, const void* k, const void* v,
+                                   const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                                   const float* initial_state, const int32_t* cu_seqlens,
+                                   const int32_t* state_indices, void* o, float* final_state, void* stream) {
+  Plan pl;
+  kda_status_t st = plan_problem(p, true, pl);
+  if (st != KDA_OK) return st;
+  if (pl.bytes > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+    return fail(KDA_ERR_UNSUPPORTED,
+                "this problem needs %zu bytes of workspace; the fixed scratch holds %zu "
+                "(call kda_chunk_fwd with a workspace instead)",
+                pl.bytes, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+  if (pl.N == 0) return kda_chunk_fwd(p, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens,
+                                      state_indices, o, final_state, nullptr, 0, stream, nullptr);
+  void* ws = nullptr;
+  char why[160] = "";
+  const hipError_t e = kda::noalloc_scratch(static_cast<hipStream_t>(stream), &ws, why, sizeof why);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "fixed scratch: %s: %s", why, hipGetErrorString(e));
+  return kda_chunk_fwd(p, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, state_indices, o,
+                       final_state, ws, KDA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}
+
 kda_status_t kda_recurrent_fwd(const kda_problem_t* p, const void* q, const void* k, const void* v,
                                const void* g, const void* beta, const float* A_log, const float* dt_bias,
                                const float* initial_state, const int32_t* cu_seqlens,

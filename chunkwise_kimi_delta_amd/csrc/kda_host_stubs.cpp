@@ -2,6 +2,8 @@
 // build of the C ABI (kda_api.cpp) so that its validation, workspace planning
 // and error paths run under AddressSanitizer and UndefinedBehaviorSanitizer
 // on a machine without a GPU.  They launch nothing and report success.
+#include <cstdio>
+
 #include "kda_launch.h"
 
 namespace kda {
@@ -10,4 +12,9 @@ hipError_t launch_intra(int, int, int, const IntraArgs&, hipStream_t) { return h
 hipError_t launch_scan(int, int, int, const ScanArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_merge(int, int, const MergeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_recurrent(int, int, int, const RecurrentArgs&, hipStream_t) { return hipSuccess; }
+// (no device scratch in a host-only build)
+hipError_t noalloc_scratch(hipStream_t, void**, char* why, size_t why_len) {
+  snprintf(why, why_len, "host-only build");
+  return hipErrorNotSupported;
+}
 }  // namespace kda

@@ -125,5 +125,8 @@ hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t
 hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s);
 hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s);
 hipError_t launch_recurrent(int K, int V, int dtype, const RecurrentArgs& a, hipStream_t s);
+// Device address of the fixed scratch on the stream's device (kda_noalloc.hip);
+// on failure `why` names the step that failed.
+hipError_t noalloc_scratch(hipStream_t stream, void** out, char* why, size_t why_len);
 
 }  // namespace kda

@@ -45,7 +45,8 @@ class KdaProblem(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_segment_summary_workspace_size",
-           "kda_segment_summary", "kda_summary_merge", "kda_recurrent_fwd", "kda_chunk_offsets_host",
+           "kda_segment_summary", "kda_summary_merge", "kda_recurrent_fwd", "kda_chunk_fwd_noalloc",
+           "kda_chunk_offsets_host",
            "kda_status_string", "kda_last_error", "kda_abi_version")
 ABI_VERSION = 2
 STAGE_EVENTS = 3
@@ -66,13 +67,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_segment_summary.argtypes = [P] + [VP] * 10 + [SZ, VP, VP]
     lib.kda_summary_merge.argtypes = [I32, I32, I32, I32, VP, VP, VP, VP]
     lib.kda_recurrent_fwd.argtypes = [P] + [VP] * 12 + [VP]
+    lib.kda_chunk_fwd_noalloc.argtypes = [P] + [VP] * 12 + [VP]
     lib.kda_chunk_offsets_host.argtypes = [VP, I32, I32, VP]
     lib.kda_status_string.argtypes = [I32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_abi_version.restype = I32
     for name in ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_segment_summary_workspace_size",
-                 "kda_segment_summary", "kda_summary_merge", "kda_recurrent_fwd", "kda_chunk_offsets_host"):
+                 "kda_segment_summary", "kda_summary_merge", "kda_recurrent_fwd", "kda_chunk_fwd_noalloc",
+                 "kda_chunk_offsets_host"):
         getattr(lib, name).restype = I32
     if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{path} has ABI version {lib.kda_abi_version()}, expected {ABI_VERSION}: rebuild it")
@@ -268,6 +271,32 @@ def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None
                              _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_d), _ptr(si),
                              _ptr(o), _ptr(final_state), _ptr(workspace), workspace.numel(),
                              _stream(dev), _events(stage_events)))
+    return o, final_state
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, *, o, final_state=None, scale: Optional[float] = None,
+                          A_log=None, dt_bias=None, initial_state=None, cu_seqlens=None,
+                          cu_seqlens_host=None, state_indices=None, gate_in_kernel: bool = False,
+                          safe_gate: bool = False, lower_bound: float = -5.0, qk_l2norm: bool = False,
+                          beta_sigmoid: bool = False, eps: float = 1e-6):
+    """``kda_chunk_fwd`` without a workspace: the library's fixed device scratch
+    serves instead (problems needing more than NOALLOC_SCRATCH_BYTES are
+    rejected).  The outputs are the caller's (``o`` required; ``final_state``
+    optional, or the cache itself in cache mode), so nothing is allocated.
+    Calls that overlap on one GPU share the scratch and race."""
+    lib = load()
+    p, dev, cu_d, si, o, final_state = _forward_args(
+        q, k, v, g, beta, scale=scale, A_log=A_log, dt_bias=dt_bias, initial_state=initial_state,
+        cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, state_indices=state_indices,
+        output_final_state=state_indices is not None, gate_in_kernel=gate_in_kernel,
+        safe_gate=safe_gate, lower_bound=lower_bound, qk_l2norm=qk_l2norm, beta_sigmoid=beta_sigmoid,
+        eps=eps, o=o, final_state=final_state)
+    _check(lib.kda_chunk_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_d),
+                                     _ptr(si), _ptr(o), _ptr(final_state), _stream(dev)))
     return o, final_state
 
 

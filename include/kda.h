@@ -132,6 +132,32 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p,
                            void* workspace, size_t workspace_bytes, void* stream,
                            void* const* stage_events);
 
+/* Bytes of the fixed device scratch behind kda_chunk_fwd_noalloc (64 MiB). */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * kda_chunk_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation, arguments and results as kda_chunk_fwd (no stage events),
+ * with the workspace taken from a fixed KDA_NOALLOC_SCRATCH_BYTES array that
+ * the library holds on each GPU it runs on until the process ends.  It calls
+ * no allocating routine.  Problems whose kda_chunk_fwd_workspace_size exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES are rejected with KDA_ERR_UNSUPPORTED (at K = V =
+ * 128 in bf16 that is about 690 (head, 64-token chunk) pairs, e.g. 32 heads x
+ * 1344 tokens).  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (two streams, two threads) race and must be serialised
+ * by the caller.  The first call on a device looks up the scratch address on
+ * that device (the stream's device is made current for the lookup and then
+ * restored).
+ */
+kda_status_t kda_chunk_fwd_noalloc(const kda_problem_t* p,
+                                   const void* q, const void* k, const void* v,
+                                   const void* g, const void* beta,
+                                   const float* A_log, const float* dt_bias,
+                                   const float* initial_state, const int32_t* cu_seqlens,
+                                   const int32_t* state_indices,
+                                   void* o, float* final_state, void* stream);
+
 /* Bytes of device workspace kda_segment_summary needs for this problem. */
 kda_status_t kda_segment_summary_workspace_size(const kda_problem_t* p, size_t* bytes);
 

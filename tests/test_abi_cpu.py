@@ -40,6 +40,17 @@ def _problem(**kw):
     return kda.KdaProblem(*[d[f] for f, _ in kda.KdaProblem._fields_])
 
 
+def test_noalloc_rejects_problems_beyond_its_scratch_before_any_device_access(lib):
+    """The layer problem needs ~395 MB of workspace, beyond the 64 MiB scratch:
+    the call fails closed on the host (fake pointers are never touched)."""
+    p = _problem()
+    fake = 0x1000
+    st = lib.kda_chunk_fwd_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None,
+                                   None, None, fake, None, None)
+    assert st == kda.KDA_ERR_UNSUPPORTED and b"fixed scratch" in lib.kda_last_error()
+    assert kda.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def test_fp32_tokens_at_k128_are_in_the_envelope(lib):
     st, b = _ws(lib, _problem(dtype=0))
     assert st == 0 and b > 0
