@@ -108,7 +108,7 @@ def stats_us(xs_ms):
 
 
 # ------------------------------------------------------------------ workloads
-def setup(name, dev, hev):
+def setup(name, dev, hev, scan_segments=0):
     """Inputs on the device and a step function for one workload.
 
     Returns (step(marks) -> None, meta).  ``step`` records the events of the
@@ -203,17 +203,20 @@ def setup(name, dev, hev):
     else:
         final = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev)
         n_states = N * (2 if p.h0 is not None else 1)
-    ws = torch.empty(kda.workspace_bytes(t["q"], t["v"], t["cu_host"]), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kda.workspace_bytes(t["q"], t["v"], t["cu_host"], scan_segments=scan_segments),
+                     dtype=torch.uint8, device=dev)
 
     def step(m):
         kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=p.scale, A_log=t["A_log"],
                           dt_bias=t["dt_bias"], initial_state=t["h0"], cu_seqlens=t["cu"],
                           cu_seqlens_host=t["cu_host"], state_indices=t["state_indices"], o=o,
-                          final_state=final, workspace=ws, stage_events=m, **kw)
+                          final_state=final, workspace=ws, stage_events=m, scan_segments=scan_segments,
+                          **kw)
 
     es = 2 if p.dtype == "bf16" else 4
     meta = dict(p=p, flop=fpt * th, bytes=token_bytes(p) + n_states * state, nmarks=3,
                 intervals={"intra_kernel": (0, 1), "scan_kernel": (1, 2)},
+                scan_segments=scan_segments,
                 own_bytes={"intra_kernel": token_bytes(p, with_o=False),
                            "scan_kernel": nbytes(p.v, es) + n_states * state},
                 config={"B": p.B, "T": p.T, "Hk": p.Hk, "H": Hv, "dk": K, "dv": V})
@@ -229,6 +232,7 @@ WORKLOAD_TEXT = {
     "segment": "one segment of a 1M-token sequence: summary + merge of 7 preceding summaries + forward",
     "gqa": "GQA long batch forward (16 q/k heads shared by 64 value heads, safe gate)",
     "decode": "decode step: one token for each of 64 sequences, state cache updated in place",
+    "longseq": "long sequence over few heads (B=1, T=65536, H=4): segment-parallel scan",
 }
 
 
@@ -372,6 +376,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--scan-segments", type=int, default=0,
+                    help="0: the library chooses the segment-parallel scan, 1: off, n > 1: forced")
     ap.add_argument("--cpu-token-heads", type=int, default=524288,
                     help="token-heads of the oracle's CPU-baseline sample (about 10 s at one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -404,7 +410,7 @@ def main():
     torch.cuda.set_device(dev)
     hev = HipEvents()
     log(f"generating inputs ({args.workload}) ...")
-    step, meta = setup(args.workload, dev, hev)
+    step, meta = setup(args.workload, dev, hev, args.scan_segments)
     p = meta["p"]
 
     log(f"warmup {args.warmup} ...")
@@ -457,6 +463,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "chunk": BT, **meta["config"],
+                   "scan_segments": args.scan_segments,
                    "gate": "in-kernel -exp(A_log)*softplus(g+dt_bias)" if p.gate_in_kernel else "precomputed",
                    "safe_gate": p.safe_gate, "l2norm": p.l2norm, "beta_sigmoid": p.beta_sigmoid},
         "step_us": st, "tflops": tflops, "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS,

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 
@@ -47,10 +48,31 @@ struct Plan {
   int64_t nchunks = 0;    // chunks over all sequences
   int N = 0;
   size_t es = 0;          // element size of token tensors
+  int seg_len = 0x7fffffff, seg_max = 1;   // segment-parallel scan (seg_max > 1)
   // workspace offsets
-  size_t off_chunk = 0, off_rec = 0;
+  size_t off_chunk = 0, off_rec = 0, off_mseg = 0, off_sseg = 0, off_hin = 0;
   size_t bytes = 0;
 };
+
+// Segment plan of the forward scan.  Automatic: split when fewer than half the
+// compute units would hold a (sequence, head, 16-column tile) scan, into
+// segments of at least 8 chunks, aiming at about 256 workgroups.
+void plan_segments(const kda_problem_t* p, int64_t max_nck, int N, Plan& pl) {
+  int target = 1;
+  if (p->scan_segments > 1) {
+    target = p->scan_segments;
+  } else if (p->scan_segments == 0) {
+    const int64_t wg = (int64_t)N * p->Hv * (p->V / 16);
+    if (wg > 0 && wg < 128) target = (int)std::min<int64_t>(16, 256 / wg);
+  }
+  if (target < 2 || max_nck < 2) return;
+  int64_t len = (max_nck + target - 1) / target;
+  if (p->scan_segments == 0) len = std::max<int64_t>(len, 8);
+  const int64_t nseg = (max_nck + len - 1) / len;
+  if (nseg < 2) return;
+  pl.seg_len = (int)len;
+  pl.seg_max = (int)nseg;
+}
 
 // Shape / flag validation shared by every token-level call; fills the plan.
 kda_status_t plan_problem(const kda_problem_t* p, bool forward, Plan& pl) {
@@ -73,10 +95,13 @@ kda_status_t plan_problem(const kda_problem_t* p, bool forward, Plan& pl) {
     return fail(KDA_ERR_INVALID_ARGUMENT, "lower_bound must be finite and <= 0 (a decay, in natural log)");
   if (p->B < 0 || p->T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative B=%d or T=%d", p->B, p->T);
   if (p->state_rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative state_rows");
+  if (p->scan_segments < 0 || p->scan_segments > 4096)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "scan_segments %d outside 0 .. 4096", p->scan_segments);
   if (!forward && p->state_rows != 0)
     return fail(KDA_ERR_INVALID_ARGUMENT, "summaries take no state cache (state_rows must be 0)");
 
   pl.es = p->dtype == KDA_BF16 ? 2 : 4;
+  int64_t max_nck = 0;
   if (p->layout == KDA_LAYOUT_BSND) {
     if (p->num_seqs != p->B)
       return fail(KDA_ERR_INVALID_ARGUMENT, "BSND needs num_seqs == B (got %d vs %d)", p->num_seqs, p->B);
@@ -84,6 +109,7 @@ kda_status_t plan_problem(const kda_problem_t* p, bool forward, Plan& pl) {
     pl.N = p->B;
     pl.tokens = (int64_t)p->B * p->T;
     pl.nchunks = (int64_t)p->B * ((p->T + kBT - 1) / kBT);
+    max_nck = (p->T + kBT - 1) / kBT;
   } else {
     if (p->B != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "TND needs B == 1 (got %d)", p->B);
     if (p->num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative num_seqs");
@@ -94,7 +120,9 @@ kda_status_t plan_problem(const kda_problem_t* p, bool forward, Plan& pl) {
     for (int i = 0; i < p->num_seqs; ++i) {
       if (cu[i + 1] < cu[i])
         return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %d (%d -> %d)", i, cu[i], cu[i + 1]);
-      nc += (cu[i + 1] - cu[i] + kBT - 1) / kBT;
+      const int64_t c = (cu[i + 1] - cu[i] + kBT - 1) / kBT;
+      nc += c;
+      max_nck = std::max(max_nck, c);
     }
     if (cu[p->num_seqs] != p->T)
       return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[N] = %d differs from T = %d", cu[p->num_seqs], p->T);
@@ -107,10 +135,20 @@ kda_status_t plan_problem(const kda_problem_t* p, bool forward, Plan& pl) {
   if ((int64_t)(VA / 16) * p->Hv * pl.N > 0x7fffffffLL || pl.nchunks * (int64_t)p->Hv > 0x7fffffffLL)
     return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head, tile) workgroups");
 
+  if (forward) plan_segments(p, max_nck, pl.N, pl);
+  if ((int64_t)(p->V + p->K) / 16 * p->Hv * pl.N * pl.seg_max > 0x7fffffffLL)
+    return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, segment, head, tile) workgroups");
+
   const size_t slots = (size_t)p->Hv * (size_t)pl.nchunks;
   size_t off = 0;
   pl.off_chunk = off;  off = align256(off + sizeof(int32_t) * (size_t)(pl.N + 1));
-  pl.off_rec = off;    off += slots * kda::rec_layout(p->K, p->V, (int)pl.es, forward).bytes;
+  pl.off_rec = off;    off = align256(off + slots * kda::rec_layout(p->K, p->V, (int)pl.es, forward).bytes);
+  if (pl.seg_max > 1) {
+    const size_t segs = (size_t)pl.N * pl.seg_max * p->Hv;
+    pl.off_mseg = off;  off = align256(off + segs * p->K * p->K * sizeof(float));
+    pl.off_sseg = off;  off = align256(off + segs * p->K * p->V * sizeof(float));
+    pl.off_hin = off;   off = align256(off + segs * p->K * p->V * sizeof(float));
+  }
   pl.bytes = off;
   return KDA_OK;
 }
@@ -256,8 +294,29 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
   if ((st = hip_status(record_stage(stage_events, 1, s), "stage event")) != KDA_OK) return st;
   kda::ScanArgs a{};
   a.seq = si;
-  a.Hv = p->Hv; a.nchunks = (int)pl.nchunks; a.state_rows = p->state_rows; a.summary = 0;
+  a.Hv = p->Hv; a.nchunks = (int)pl.nchunks; a.state_rows = p->state_rows;
   a.ws = reinterpret_cast<const unsigned char*>(ws + pl.off_rec);
+  a.seg_len = pl.seg_len; a.seg_max = pl.seg_max;
+  if (pl.seg_max > 1) {
+    // segment-parallel scan: summaries of every segment but each sequence's
+    // last, their prefix merge, then all segments' scans from their incoming states
+    float* Mseg = reinterpret_cast<float*>(ws + pl.off_mseg);
+    float* Sseg = reinterpret_cast<float*>(ws + pl.off_sseg);
+    float* hin = reinterpret_cast<float*>(ws + pl.off_hin);
+    kda::ScanArgs sa = a;
+    sa.summary = 1; sa.fwd_records = 1; sa.skip_last = 1; sa.state_rows = 0;
+    sa.hT = Sseg; sa.M = Mseg;
+    if ((st = hip_status(kda::launch_scan(p->K, p->V, p->dtype, sa, s), "segment summary scan launch")) != KDA_OK)
+      return st;
+    kda::PrefixMergeArgs ma{};
+    ma.seq = si; ma.Hv = p->Hv; ma.seg_len = pl.seg_len; ma.seg_max = pl.seg_max;
+    ma.state_rows = p->state_rows; ma.M = Mseg; ma.S = Sseg; ma.h0 = initial_state;
+    ma.state_idx = state_indices; ma.h_in = hin;
+    if ((st = hip_status(kda::launch_prefix_merge(p->K, p->V, ma, s), "segment prefix merge launch")) != KDA_OK)
+      return st;
+    a.h_in = hin;
+  }
+  a.summary = 0;
   a.h0 = initial_state; a.state_idx = state_indices; a.hT = final_state; a.M = nullptr; a.o = o;
   if ((st = hip_status(kda::launch_scan(p->K, p->V, p->dtype, a, s), "state-scan kernel launch")) != KDA_OK)
     return st;
@@ -292,6 +351,7 @@ kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const vo
   kda::ScanArgs a{};
   a.seq = si;
   a.Hv = p->Hv; a.nchunks = (int)pl.nchunks; a.state_rows = 0; a.summary = 1;
+  a.seg_len = 0x7fffffff; a.seg_max = 1;
   a.ws = reinterpret_cast<const unsigned char*>(ws + pl.off_rec);
   a.hT = S_tilde; a.M = M;
   if ((st = hip_status(kda::launch_scan(p->K, p->V, p->dtype, a, s), "summary scan kernel launch")) != KDA_OK)

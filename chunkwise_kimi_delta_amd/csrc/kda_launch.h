@@ -82,11 +82,15 @@ struct IntraArgs {
 struct ScanArgs {
   SeqInfo seq;
   int Hv, nchunks, state_rows, summary;
+  int fwd_records;                    // summary mode on records written in forward mode
+  int seg_len, seg_max;               // chunks per segment (>= 1), segments per sequence in the grid
+  int skip_last;                      // summary mode: no workgroup for a sequence's last segment
+  const float* h_in;                  // forward, segment s > 0: [N*seg_max][Hv][K][V] incoming state
   const unsigned char* ws;            // records, [Hv][nchunks]
   const float* h0;                    // [N,Hv,K,V] | cache | null
   const int32_t* state_idx;           // cache mode
   float* hT;                          // final [N,Hv,K,V] | cache | null ; summary: S~
-  float* M;                           // summary only: [N,Hv,K,K]
+  float* M;                           // summary only: [N*seg_max,Hv,K,K] (S~ in hT alike)
   void* o;                            // [tokens,Hv,V]
 };
 
@@ -110,6 +114,17 @@ struct MergeArgs {
   float* state;
 };
 
+// Prefix merge over the segments of each sequence: h_in[n*seg_max + s + 1] =
+// M[..s] h_in[..s] + S~[..s], from the sequence's initial state.
+struct PrefixMergeArgs {
+  SeqInfo seq;
+  int Hv, seg_len, seg_max, state_rows;
+  const float *M, *S;                 // [N*seg_max][Hv][K][K], [..][K][V]
+  const float* h0;                    // [N,Hv,K,V] | cache | null
+  const int32_t* state_idx;
+  float* h_in;                        // [N*seg_max][Hv][K][V]
+};
+
 // Launch a kernel and return the status of this launch alone (hipLaunchKernel
 // reports its own failure; hipGetLastError would also return an error left
 // behind by the caller's earlier work).
@@ -124,6 +139,7 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
 hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t s);
 hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s);
 hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s);
+hipError_t launch_prefix_merge(int K, int V, const PrefixMergeArgs& a, hipStream_t s);
 hipError_t launch_recurrent(int K, int V, int dtype, const RecurrentArgs& a, hipStream_t s);
 // Device address of the fixed scratch on the stream's device (kda_noalloc.hip);
 // on failure `why` names the step that failed.

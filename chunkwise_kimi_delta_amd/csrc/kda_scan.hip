@@ -33,6 +33,15 @@
 // with u = [u | 0] and writes S~ and M ("KDA Context Parallelism (KCP)",
 // notation and algorithm steps 1-2): the M columns see zero values, so they
 // accumulate the product of the per-token transitions.
+//
+// Segments.  A sequence of nck chunks may be cut into segments of seg_len
+// chunks, one workgroup per (tile, head, sequence, segment) -- the same
+// decomposition applied across CUs ("KDA Context Parallelism (KCP)",
+// algorithm): the summary mode writes each segment's (M, S~) at index
+// n * seg_max + s (optionally skipping last segments, whose summary nobody
+// needs); the forward mode starts segment s > 0 from h_in[n * seg_max + s]
+// (the prefix merge of the earlier segments' summaries) and only the last
+// segment writes the sequence's final state.
 #include "kda_launch.h"
 
 namespace kda {
@@ -113,9 +122,12 @@ constexpr int OPF = 2;           // output waves: the same
 constexpr int NOW = 2;             // output waves (forward mode)
 constexpr int TPO = 4 / NOW;       // token tiles per output wave
 
-template <int KD, int VD, typename ST, bool SUM, int CT>
+// RF: the records hold the forward sections (qg, Aqk), i.e. the chunk-local
+// kernel ran in forward mode; a summary scan inside a forward call reads them.
+template <int KD, int VD, typename ST, bool SUM, int CT, bool RF>
 __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(ScanArgs a) {
-  constexpr RecLayout L = rec_layout(KD, VD, (int)sizeof(ST), !SUM);
+  static_assert(SUM || RF, "the forward scan reads forward records");
+  constexpr RecLayout L = rec_layout(KD, VD, (int)sizeof(ST), RF);
   constexpr bool F32 = sizeof(ST) == 4;
   constexpr int ES = (int)sizeof(ST);
   constexpr int NS = KD / 32;         // state waves, 32 state rows each
@@ -137,15 +149,27 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
   if ((NB & 7) == 0) lid = (lid & 7) * (NB >> 3) + (lid >> 3);
   const int tv = lid % NTILE;
   const int h = (lid / NTILE) % a.Hv;
-  const int n = lid / (NTILE * a.Hv);
+  const int ns = lid / (NTILE * a.Hv);                  // (sequence, segment)
+  const int n = ns / a.seg_max, seg = ns % a.seg_max;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, quad = lane >> 4;
 
   int64_t tok0s;
   int len;
   seq_range(a.seq, n, tok0s, len);
-  const int nck = (len + BT - 1) / BT;
-  const int cb = chunk_base(a.seq, n);
+  // this segment's chunks [c_lo, c_hi) of the sequence; segment 0 always runs
+  // (an empty sequence still passes its initial state through)
+  const int nck_seq = (len + BT - 1) / BT;
+  const int c_lo = (int)min((int64_t)seg * a.seg_len, (int64_t)nck_seq);
+  const int c_hi = (int)min((int64_t)c_lo + a.seg_len, (int64_t)nck_seq);
+  const bool last_seg = c_hi == nck_seq;
+  if (seg > 0 && c_lo >= nck_seq) return;               // past the sequence: no work
+  if (SUM && a.skip_last && last_seg) return;           // summary not needed
+  tok0s += (int64_t)c_lo * BT;
+  len = min(len - c_lo * BT, (c_hi - c_lo) * BT);
+  const int nck = c_hi - c_lo;
+  const int64_t sidx = (int64_t)n * a.seg_max + seg;    // summary output / h_in index
+  const int cb = chunk_base(a.seq, n) + c_lo;
   const bool mtile = SUM && tv * BV >= VD;              // columns of M
   const int v0 = mtile ? tv * BV - VD : tv * BV;        // first column inside S~ or M
   const unsigned char* recs = a.ws + ((size_t)h * a.nchunks + cb) * L.bytes;
@@ -217,6 +241,8 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
       } else if (a.h0) {
         h0p = a.h0 + ((int64_t)n * a.Hv + h) * (int64_t)(KD * VD);
       }
+      // a later segment starts from the prefix merge of the earlier ones
+      if (seg > 0) h0p = a.h_in + (sidx * a.Hv + h) * (int64_t)(KD * VD);
     }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -316,9 +342,9 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     float* dst = nullptr;
     int64_t ld = VD;
     if (SUM) {
-      if (mtile) { dst = a.M + ((int64_t)n * a.Hv + h) * (int64_t)(KD * KD); ld = KD; }
-      else dst = a.hT + ((int64_t)n * a.Hv + h) * (int64_t)(KD * VD);
-    } else if (a.hT) {
+      if (mtile) { dst = a.M + (sidx * a.Hv + h) * (int64_t)(KD * KD); ld = KD; }
+      else dst = a.hT + (sidx * a.Hv + h) * (int64_t)(KD * VD);
+    } else if (a.hT && last_seg) {
       if (a.state_rows > 0) {
         if (valid_row) dst = a.hT + (srow * a.Hv + h) * (int64_t)(KD * VD);
       } else {
@@ -489,16 +515,18 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
 
 hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s) {
   if (a.seq.N == 0 || a.Hv == 0) return hipSuccess;
+  if (a.seg_max < 1 || a.seg_len < 1) return hipErrorInvalidValue;
   const int VA = a.summary ? V + K : V;
   constexpr int CTsel = 1;   // 16-column tiles (wider tiles leave CUs idle at the layer)
-  const long nb = (long)(VA / (16 * CTsel)) * a.Hv * a.seq.N;
+  const long nb = (long)(VA / (16 * CTsel)) * a.Hv * a.seq.N * a.seg_max;
   if (nb > 0x7fffffffL) return hipErrorInvalidValue;
   // K/32 state waves, plus the output waves in forward mode
   dim3 grid((unsigned)nb), block(K * 2 + (a.summary ? 0 : 64 * NOW));
 #define KDA_SCAN_CASE(KK, VV, TT, CC)                                                             \
   if (K == KK && V == VV && CTsel == CC) {                                                        \
-    return a.summary ? launch(scan_kernel<KK, VV, TT, true, CC>, grid, block, s, a)              \
-                     : launch(scan_kernel<KK, VV, TT, false, CC>, grid, block, s, a);            \
+    if (!a.summary) return launch(scan_kernel<KK, VV, TT, false, CC, true>, grid, block, s, a);   \
+    return a.fwd_records ? launch(scan_kernel<KK, VV, TT, true, CC, true>, grid, block, s, a)     \
+                         : launch(scan_kernel<KK, VV, TT, true, CC, false>, grid, block, s, a);   \
   }
   if (dtype == 1) {
     KDA_SCAN_CASE(128, 128, bf16_t, 1)

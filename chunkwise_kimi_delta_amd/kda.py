@@ -40,7 +40,7 @@ class KdaProblem(ctypes.Structure):
                 ("scale", ctypes.c_float), ("eps", ctypes.c_float), ("lower_bound", ctypes.c_float),
                 ("num_seqs", ctypes.c_int32),
                 ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
-                ("state_rows", ctypes.c_int32)]
+                ("state_rows", ctypes.c_int32), ("scan_segments", ctypes.c_int32)]
 
 
 _lib = None
@@ -136,7 +136,8 @@ def _events(stage_events):
 
 
 def make_problem(q_or_k: torch.Tensor, v: torch.Tensor, *, scale: float, flags: int, eps: float,
-                 lower_bound: float, cu_host: Optional[torch.Tensor], state_rows: int = 0):
+                 lower_bound: float, cu_host: Optional[torch.Tensor], state_rows: int = 0,
+                 scan_segments: int = 0):
     """Fill the C problem descriptor from tensor shapes (BSND if 4-D, TND if 3-D)."""
     if q_or_k.dim() == 4:
         B, T, Hk, K = q_or_k.shape
@@ -151,7 +152,7 @@ def make_problem(q_or_k: torch.Tensor, v: torch.Tensor, *, scale: float, flags: 
         raise ValueError("token tensors are [B,T,H,D] or [T,H,D]")
     Hv, V = v.shape[-2], v.shape[-1]
     p = KdaProblem(layout, _dtype_code(v), B, T, Hk, Hv, K, V, CHUNK, flags, scale, eps, lower_bound,
-                   N, cu_ptr, state_rows)
+                   N, cu_ptr, state_rows, scan_segments)
     return p, N
 
 
@@ -177,7 +178,7 @@ def _cu_pair(cu_seqlens, cu_seqlens_host, device, tokens: torch.Tensor):
 
 def _forward_args(q, k, v, g, beta, *, scale, A_log, dt_bias, initial_state, cu_seqlens,
                   cu_seqlens_host, state_indices, output_final_state, gate_in_kernel, safe_gate,
-                  lower_bound, qk_l2norm, beta_sigmoid, eps, o, final_state):
+                  lower_bound, qk_l2norm, beta_sigmoid, eps, o, final_state, scan_segments=0):
     """Checks and marshalling shared by the forward calls: every tensor's shape,
     dtype, layout and device, then the problem descriptor and the outputs."""
     if q.dim() not in (3, 4) or v.dim() != q.dim():
@@ -228,7 +229,7 @@ def _forward_args(q, k, v, g, beta, *, scale, A_log, dt_bias, initial_state, cu_
     flags = ((KDA_GATE_IN_KERNEL if gate_in_kernel else 0) | (KDA_SAFE_GATE if safe_gate else 0)
              | (KDA_QK_L2NORM if qk_l2norm else 0) | (KDA_BETA_SIGMOID if beta_sigmoid else 0))
     p, N = make_problem(q, v, scale=scale, flags=flags, eps=eps, lower_bound=lower_bound,
-                        cu_host=cu_h, state_rows=rows)
+                        cu_host=cu_h, state_rows=rows, scan_segments=scan_segments)
     if o is None:
         o = torch.empty(v.shape, dtype=v.dtype, device=dev)
     if cache:
@@ -247,13 +248,16 @@ def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None
                   output_final_state: bool = True, gate_in_kernel: bool = False,
                   safe_gate: bool = False, lower_bound: float = -5.0, qk_l2norm: bool = False,
                   beta_sigmoid: bool = False, eps: float = 1e-6, o=None, final_state=None,
-                  workspace=None, stage_events=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  workspace=None, stage_events=None, scan_segments: int = 0
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA forward.  Returns (o, final_state).
 
     With ``state_indices`` the ``initial_state`` is a state cache
     [rows,Hv,K,V]; final states are scattered into ``final_state`` (default:
     the same cache, in place) and that cache is returned.  ``stage_events``:
     three raw hipEvent_t handles the call records at its stage boundaries.
+    ``scan_segments``: 0 lets the library choose the segment-parallel scan,
+    1 turns it off, n > 1 cuts each sequence into at most n segments.
     """
     lib = load()
     p, dev, cu_d, si, o, final_state = _forward_args(
@@ -261,7 +265,7 @@ def kda_chunk_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None
         cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, state_indices=state_indices,
         output_final_state=output_final_state, gate_in_kernel=gate_in_kernel, safe_gate=safe_gate,
         lower_bound=lower_bound, qk_l2norm=qk_l2norm, beta_sigmoid=beta_sigmoid, eps=eps, o=o,
-        final_state=final_state)
+        final_state=final_state, scan_segments=scan_segments)
     ws_bytes = ctypes.c_size_t()
     _check(lib.kda_chunk_fwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
     if workspace is None:
@@ -281,7 +285,7 @@ def kda_chunk_fwd_noalloc(q, k, v, g, beta, *, o, final_state=None, scale: Optio
                           A_log=None, dt_bias=None, initial_state=None, cu_seqlens=None,
                           cu_seqlens_host=None, state_indices=None, gate_in_kernel: bool = False,
                           safe_gate: bool = False, lower_bound: float = -5.0, qk_l2norm: bool = False,
-                          beta_sigmoid: bool = False, eps: float = 1e-6):
+                          beta_sigmoid: bool = False, eps: float = 1e-6, scan_segments: int = 0):
     """``kda_chunk_fwd`` without a workspace: the library's fixed device scratch
     serves instead (problems needing more than NOALLOC_SCRATCH_BYTES are
     rejected).  The outputs are the caller's (``o`` required; ``final_state``
@@ -293,7 +297,7 @@ def kda_chunk_fwd_noalloc(q, k, v, g, beta, *, o, final_state=None, scale: Optio
         cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, state_indices=state_indices,
         output_final_state=state_indices is not None, gate_in_kernel=gate_in_kernel,
         safe_gate=safe_gate, lower_bound=lower_bound, qk_l2norm=qk_l2norm, beta_sigmoid=beta_sigmoid,
-        eps=eps, o=o, final_state=final_state)
+        eps=eps, o=o, final_state=final_state, scan_segments=scan_segments)
     _check(lib.kda_chunk_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                      _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_d),
                                      _ptr(si), _ptr(o), _ptr(final_state), _stream(dev)))
@@ -396,11 +400,13 @@ def kda_chunk_offsets_host(cu_seqlens_host: torch.Tensor, chunk: int = CHUNK) ->
     return out
 
 
-def workspace_bytes(q_or_k: torch.Tensor, v: torch.Tensor, cu_seqlens_host=None, summary: bool = False) -> int:
+def workspace_bytes(q_or_k: torch.Tensor, v: torch.Tensor, cu_seqlens_host=None, summary: bool = False,
+                    scan_segments: int = 0) -> int:
     """Device workspace bytes a forward (or summary) call needs for these shapes."""
     lib = load()
     cu = None if cu_seqlens_host is None else cu_seqlens_host.to(torch.int32).contiguous()
-    p, _ = make_problem(q_or_k, v, scale=1.0, flags=0, eps=0.0, lower_bound=0.0, cu_host=cu)
+    p, _ = make_problem(q_or_k, v, scale=1.0, flags=0, eps=0.0, lower_bound=0.0, cu_host=cu,
+                        scan_segments=scan_segments)
     sz = ctypes.c_size_t()
     fn = lib.kda_segment_summary_workspace_size if summary else lib.kda_chunk_fwd_workspace_size
     _check(fn(ctypes.byref(p), ctypes.byref(sz)))

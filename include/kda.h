@@ -91,6 +91,14 @@ typedef struct kda_problem {
   int32_t num_seqs;     /* N: BSND must equal B; TND = number of packed sequences */
   const int32_t* cu_seqlens_host; /* TND: HOST copy of cu_seqlens [N+1]; NULL for BSND */
   int32_t state_rows;   /* 0: states are [N,Hv,K,V]; > 0: state cache rows, see kda_chunk_fwd */
+  /* Segment-parallel state scan of kda_chunk_fwd / kda_chunk_fwd_noalloc
+   * ("KDA Context Parallelism (KCP)", algorithm, applied across the GPU's
+   * compute units): 0 = the library decides (it splits long sequences when too
+   * few (sequence, head) scans would occupy the GPU), 1 = one sequential scan
+   * per sequence, n > 1 = cut each sequence's chunks into at most n segments
+   * that are summarised in parallel, merged in order and rescanned in
+   * parallel.  The result is the same computation; other calls ignore it. */
+  int32_t scan_segments;
 } kda_problem_t;
 
 /* Bytes of device workspace kda_chunk_fwd needs for this problem. */

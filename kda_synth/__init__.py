@@ -282,6 +282,14 @@ def make_decode(seed=1005, n_seqs=64, tokens=1, H=32, K=128, V=128, dtype="bf16"
                    A_log=A_log, dt_bias=dt_bias, h0=cache, cu_seqlens=cu, state_indices=idx)
 
 
+def make_longseq(seed=1006, T=65536, H=4, **kw) -> Problem:
+    """A long sequence over few heads (the layer's recipe): too few (head,
+    column-tile) scans to occupy the GPU, the case for the segment-parallel scan."""
+    p = make_layer(seed=seed, T=T, H=H, **kw)
+    p.name = "longseq"
+    return p
+
+
 WORKLOADS = {
     "tiny": make_tiny,
     "layer": make_layer,
@@ -289,6 +297,7 @@ WORKLOADS = {
     "segment": make_segment,
     "gqa": make_gqa,
     "decode": make_decode,
+    "longseq": make_longseq,
 }
 
 

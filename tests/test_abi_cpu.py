@@ -35,9 +35,25 @@ def test_every_declared_symbol_is_exported(lib):
 def _problem(**kw):
     d = dict(layout=0, dtype=1, B=1, T=8192, Hk=32, Hv=32, K=128, V=128, chunk_size=64, flags=15,
              scale=128 ** -0.5, eps=1e-6, lower_bound=-5.0, num_seqs=1, cu_seqlens_host=None,
-             state_rows=0)
+             state_rows=0, scan_segments=0)
     d.update(kw)
     return kda.KdaProblem(*[d[f] for f, _ in kda.KdaProblem._fields_])
+
+
+def test_segment_plan_grows_the_workspace_only_when_it_splits(lib):
+    """The layer (32 heads x 8 tiles = 256 scans) fills the GPU: no split, the
+    plain workspace.  Few heads on a long sequence: the library splits (the
+    summaries, their prefixes and the incoming states join the workspace);
+    scan_segments = 1 turns that off and n > 1 forces it."""
+    _, plain = _ws(lib, _problem())
+    assert _ws(lib, _problem(scan_segments=1))[1] == plain
+    _, few = _ws(lib, _problem(Hk=2, Hv=2, T=65536))
+    _, few_off = _ws(lib, _problem(Hk=2, Hv=2, T=65536, scan_segments=1))
+    assert few > few_off
+    seg_bytes = 2 * 16 * 128 * (128 + 2 * 128) * 4          # 16 segments x 2 heads
+    assert few - few_off >= seg_bytes
+    _, forced = _ws(lib, _problem(scan_segments=3))
+    assert forced > plain
 
 
 def test_noalloc_rejects_problems_beyond_its_scratch_before_any_device_access(lib):
@@ -98,6 +114,7 @@ def test_workspace_size_layer_and_monotone(lib):
     (dict(num_seqs=2), kda.KDA_ERR_INVALID_ARGUMENT),    # BSND needs num_seqs == B
     (dict(T=-1), kda.KDA_ERR_INVALID_ARGUMENT),
     (dict(state_rows=-2), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(scan_segments=-1), kda.KDA_ERR_INVALID_ARGUMENT),
 ])
 def test_bad_descriptors_are_rejected(lib, kw, status):
     st, _ = _ws(lib, _problem(**kw))

@@ -323,6 +323,65 @@ def test_graph_capture_replays_match_eager(gpu_lib):
         assert not torch.equal(og, torch.zeros_like(og))
 
 
+# ------------------------------------------- segment-parallel state scan
+@pytest.mark.parametrize("S", [2, 3, 5, 16])
+def test_segmented_scan_matches_oracle(gpu_lib, S):
+    """The forward with each sequence cut into S segments (summaries in
+    parallel, prefix merge, rescans in parallel) against the oracle and
+    against the one-scan forward."""
+    p = ks.make("layer", T=1000, H=2)
+    t = to_torch(p)
+    o1, f1 = run_fwd(gpu_lib, p, t, scan_segments=1)
+    oS, fS = run_fwd(gpu_lib, p, t, scan_segments=S)
+    ro, rf = orc.forward(p)
+    check("o", np64(oS), ro, TOL_BF16_OUT)
+    check("final_state", np64(fS), rf, TOL_STATE)
+    check("o vs one scan", np64(oS), np64(o1), TOL_BF16_OUT)
+    check("final vs one scan", np64(fS), np64(f1), TOL_STATE)
+
+
+def test_segmented_scan_carries_state_across_segments(gpu_lib):
+    """Slow decay (small A_log): the state entering each segment matters, so a
+    wrong transition product or merge order shows in o and the final state."""
+    p = ks.make("layer", T=2048, H=2)
+    p.A_log = np.log(np.array([1e-3, 3e-3], dtype=np.float32))
+    p.dt_bias = np.full_like(p.dt_bias, -4.0)
+    t = to_torch(p)
+    o, f = run_fwd(gpu_lib, p, t, scan_segments=4)
+    ro, rf = orc.forward(p)
+    say(f"  max|final| = {np.abs(rf).max():.3f}")
+    check("o", np64(o), ro, TOL_BF16_OUT)
+    check("final_state", np64(f), rf, TOL_STATE)
+    # dropping the incoming states (zero start per segment) must be far off
+    pz = ks.make("layer", T=512, H=2)
+    pz.A_log, pz.dt_bias, pz.h0 = p.A_log, p.dt_bias, None
+    for name in ("q", "k", "v", "g", "beta"):
+        setattr(pz, name, getattr(p, name)[:, 1536:])
+    roz, _ = orc.forward(pz)
+    assert np.abs(roz - ro[:, 1536:]).max() > 10 * TOL_BF16_OUT * np.abs(ro).max()
+
+
+def test_segmented_scan_varlen_with_cache(gpu_lib):
+    p = ks.make("varlen", lens=[300, 70, 513, 1, 0, 260], H=3, cache_rows=9, n_invalid=1)
+    before = p.h0.copy()
+    o, cache = run_fwd(gpu_lib, p, scan_segments=4)
+    ro, rcache = orc.forward(p)
+    check("o", np64(o), ro, TOL_BF16_OUT)
+    check("cache", np64(cache), rcache, TOL_STATE)
+    got = cache.cpu().numpy()
+    touched = set(int(i) for i in p.state_indices if i >= 0)
+    for r in range(p.h0.shape[0]):
+        if r not in touched:
+            assert np.array_equal(got[r], before[r]), f"row {r} changed"
+
+
+def test_segmented_scan_automatic_on_few_heads(gpu_lib):
+    """Two heads over 16,384 tokens: 16 column-tile scans, so the library splits
+    each sequence by itself; every token and state entry against the oracle."""
+    p = ks.make("longseq", T=16384, H=2)
+    fwd_case(gpu_lib, p)
+
+
 # ------------------------------------------------------ recurrent (decode)
 def run_rec(kda, p, t=None, **over):
     t = t or to_torch(p)
