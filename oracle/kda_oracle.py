@@ -264,3 +264,154 @@ def compare(x: np.ndarray, ref: np.ndarray) -> dict:
     return dict(err_max=float(np.max(d)) / den if d.size else 0.0,
                 rel_l2=float(np.linalg.norm(x - ref)) / max(nrm, 1e-30),
                 nonfinite=int((~np.isfinite(x)).sum()))
+
+
+# ------------------------------------------------------------------ backward
+def recurrence_bwd(k, v, g, beta, S0, q, scale, do, dST, ckpt=64):
+    """Adjoint of ``recurrence`` for one sequence, all heads at once, fp64.
+
+    Forward per token (decay, correct the decayed state's prediction, write,
+    read):  S' = Diag(alpha) S;  e = v - S'^T k;  S = S' + beta k e^T;
+    o = scale S^T q,  alpha = exp(g).  Given do [T,H,V] = dL/do and
+    dST [H,K,V] = dL/dS_T (None = 0), walks the tokens backwards and returns
+    (dq [T,H,K], dk [T,H,K], dv [T,H,V], dg [T,H,K], dbeta [T,H], dS0 [H,K,V]),
+    the gradients with respect to the recurrence's own inputs (g natural-log
+    decay, beta the write strength, q and k as used).  States are kept every
+    ``ckpt`` tokens and the ones in between recomputed ("KDA Chunk Backward —
+    TPU/Pallas Kernel Design", section 1.1: the backward recomputes forward
+    quantities instead of storing them).
+    """
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    q = np.asarray(q, F64)
+    g = np.asarray(g, F64)
+    alpha = np.exp(g)
+    beta = np.asarray(beta, F64)
+    do = np.asarray(do, F64)
+    T, H, K = k.shape
+    V = v.shape[-1]
+    # forward pass keeping the state at every checkpoint
+    marks = {}
+    S = np.array(S0, dtype=F64, copy=True)
+    for t in range(T):
+        if t % ckpt == 0:
+            marks[t] = S.copy()
+        S = _step(S, k[t], v[t], alpha[t], beta[t])
+    dS = np.zeros((H, K, V), F64) if dST is None else np.array(dST, dtype=F64, copy=True)
+    dq = np.zeros((T, H, K), F64)
+    dk = np.zeros((T, H, K), F64)
+    dv = np.zeros((T, H, V), F64)
+    dg = np.zeros((T, H, K), F64)
+    db = np.zeros((T, H), F64)
+    for c0 in reversed(range(0, T, ckpt)):
+        c1 = min(T, c0 + ckpt)
+        states = [marks[c0]]                         # states[i] = S before token c0 + i
+        for t in range(c0, c1):
+            states.append(_step(states[-1], k[t], v[t], alpha[t], beta[t]))
+        for t in reversed(range(c0, c1)):
+            Sp = states[t - c0]                       # S_{t-1}
+            Sd = alpha[t][:, :, None] * Sp            # S' = Diag(alpha) S_{t-1}
+            pred = np.einsum("hkv,hk->hv", Sd, k[t])
+            e = v[t] - pred
+            St = states[t - c0 + 1]
+            # o_t = scale S_t^T q_t
+            dq[t] = scale * np.einsum("hkv,hv->hk", St, do[t])
+            dS = dS + scale * q[t][:, :, None] * do[t][:, None, :]
+            # S_t = S' + beta k e^T
+            db[t] = np.einsum("hk,hkv,hv->h", k[t], dS, e)
+            de = beta[t][:, None] * np.einsum("hkv,hk->hv", dS, k[t])
+            dk[t] = beta[t][:, None] * np.einsum("hkv,hv->hk", dS, e)
+            # e = v - S'^T k
+            dv[t] = de
+            dSd = dS - k[t][:, :, None] * de[:, None, :]
+            dk[t] -= np.einsum("hkv,hv->hk", Sd, de)
+            # S' = Diag(alpha) S_{t-1}, alpha = exp(g)
+            dg[t] = np.einsum("hkv,hkv->hk", dSd, Sp) * alpha[t]
+            dS = alpha[t][:, :, None] * dSd
+    return dq, dk, dv, dg, db, dS
+
+
+def _step(S, k, v, alpha, beta):
+    Sd = alpha[:, :, None] * S
+    e = v - np.einsum("hkv,hk->hv", Sd, k)
+    return Sd + beta[:, None, None] * k[:, :, None] * e[:, None, :]
+
+
+def _l2norm_bwd(x, dy, eps):
+    """Gradient of x / sqrt(sum x^2 + eps) (last axis) given dy."""
+    x = np.asarray(x, F64)
+    r = 1.0 / np.sqrt((x * x).sum(-1, keepdims=True) + eps)
+    y = x * r
+    return r * (dy - y * (y * dy).sum(-1, keepdims=True))
+
+
+def backward(p, do, dht=None, heads: Optional[Sequence[int]] = None):
+    """Gradients of a whole problem's forward (dense initial states; BSND or
+    TND), fp64: dict with dq, dk (shape of p.q / p.k: grouped heads summed over
+    their value heads), dv, dg (w.r.t. p.g: the raw gate with the in-kernel
+    gate, else the natural-log decay), dbeta (w.r.t. p.beta: the logit with the
+    in-kernel sigmoid), dA_log [Hv], ddt_bias [Hv, K] (in-kernel gate), dh0
+    [N, Hv, K, V].  The loss is sum(do * o) + sum(dht * final_state).
+
+    Per token the adjoint of the recurrence (``recurrence_bwd``); then the
+    preprocessing of "Hyper-Parallel Chunk KDA", section 4: sigmoid'(b) =
+    s(1 - s); the gate -exp(A_log) softplus(g + dt_bias) has derivative
+    -exp(A_log) sigmoid(g + dt_bias) in g and dt_bias and itself in A_log, zero
+    where the safe-gate clamp is active; L2Norm's derivative is
+    r (dy - y (y . dy)).  ``heads`` restricts the work to those value heads
+    (the other heads' gradients stay zero, and dq/dk receive only their share).
+    """
+    if p.state_indices is not None:
+        raise ValueError("the backward takes dense initial states")
+    Hv, K, V = p.Hv, p.K, p.V
+    hs = list(range(Hv)) if heads is None else list(heads)
+    rep = Hv // p.Hk
+    kh_idx = [h // rep for h in hs]
+    do = np.asarray(do, F64)
+    seqs = _seq_slices(p.layout, p.B, p.T, p.cu_seqlens)
+    out = dict(dq=np.zeros(p.q.shape, F64), dk=np.zeros(p.k.shape, F64), dv=np.zeros(p.v.shape, F64),
+               dg=np.zeros(p.g.shape, F64), dbeta=np.zeros(p.beta.shape, F64),
+               dA_log=np.zeros(Hv, F64), ddt_bias=np.zeros((Hv, K), F64),
+               dh0=np.zeros((len(seqs), Hv, K, V), F64))
+    for n, (b, t0, t1) in enumerate(seqs):
+        sl = (b, slice(t0, t1)) if b is not None else (slice(t0, t1),)
+        qr = np.asarray(p.q[sl][:, kh_idx], F64)
+        kr = np.asarray(p.k[sl][:, kh_idx], F64)
+        v = p.v[sl][:, hs]
+        graw = np.asarray(p.g[sl][:, hs], F64)
+        braw = np.asarray(p.beta[sl][:, hs], F64)
+        qq = l2norm(qr, p.eps) if p.l2norm else qr
+        kk = l2norm(kr, p.eps) if p.l2norm else kr
+        bb = sigmoid(braw) if p.beta_sigmoid else braw
+        if p.gate_in_kernel:
+            z = graw + (0.0 if p.dt_bias is None else np.asarray(p.dt_bias, F64)[hs])
+            g_act = -np.exp(np.asarray(p.A_log, F64)[hs])[:, None] * softplus(z)
+        else:
+            g_act = graw
+        clamped = (g_act < p.lower_bound) if p.safe_gate else np.zeros(g_act.shape, bool)
+        gg = np.where(clamped, p.lower_bound, g_act)
+        S0 = np.zeros((len(hs), K, V), F64) if p.h0 is None else np.array(p.h0[n][hs], F64)
+        dST = None if dht is None else np.asarray(dht, F64)[n][hs]
+        dq, dk, dv, dgg, db, dS0 = recurrence_bwd(kk, v, gg, bb, S0, qq, p.scale, do[sl][:, hs], dST)
+        if p.l2norm:
+            dq = _l2norm_bwd(qr, dq, p.eps)
+            dk = _l2norm_bwd(kr, dk, p.eps)
+        dgg = np.where(clamped, 0.0, dgg)
+        if p.gate_in_kernel:
+            dz = dgg * -np.exp(np.asarray(p.A_log, F64)[hs])[:, None] * sigmoid(z)
+            out["dA_log"][hs] += (dgg * g_act).sum(axis=(0, 2))
+            if p.dt_bias is not None:
+                out["ddt_bias"][hs] += dz.sum(axis=0)
+            dgraw = dz
+        else:
+            dgraw = dgg
+        dbraw = db * bb * (1.0 - bb) if p.beta_sigmoid else db
+        tgt = (lambda name: out[name][b]) if b is not None else (lambda name: out[name])
+        for j, h in enumerate(hs):
+            tgt("dq")[t0:t1, kh_idx[j]] += dq[:, j]
+            tgt("dk")[t0:t1, kh_idx[j]] += dk[:, j]
+            tgt("dv")[t0:t1, h] = dv[:, j]
+            tgt("dg")[t0:t1, h] = dgraw[:, j]
+            tgt("dbeta")[t0:t1, h] = dbraw[:, j]
+        out["dh0"][n][hs] = dS0
+    return out
