@@ -17,7 +17,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_NAME = "libkda_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["kda_api.cpp", "kda_intra.hip", "kda_scan.hip", "kda_merge.hip", "kda_recurrent.hip",
-           "kda_noalloc.hip"]
+           "kda_noalloc.hip", "kda_bwd.hip"]
 ARCH = "gfx950"
 
 

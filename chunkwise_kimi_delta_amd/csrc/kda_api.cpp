@@ -360,6 +360,122 @@ kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const vo
   return ok();
 }
 
+namespace {
+
+// Workspace of the backward: the chunk map, then the backward records, the
+// chunk-entry states, the chunk-exit state
+// gradients, the per-value-head q/k gradients, beta and decay gradients and
+// the gate's block partial sums.
+struct BwdPlan {
+  Plan fwd;
+  size_t off_rec = 0, off_h = 0, off_dh = 0, off_dqn = 0, off_dkn = 0, off_db = 0, off_dg = 0, off_part = 0;
+  size_t bytes = 0;
+  int64_t tokens = 0;
+};
+
+kda_status_t plan_bwd(const kda_problem_t* p, BwdPlan& bp) {
+  kda_problem_t q = *p;
+  q.scan_segments = 1;                       // (the forward's segment plan plays no part here)
+  kda_status_t st = plan_problem(&q, true, bp.fwd);
+  if (st != KDA_OK) return st;
+  if (p->state_rows != 0)
+    return fail(KDA_ERR_UNSUPPORTED, "the backward takes dense initial states (state_rows must be 0)");
+  const Plan& f = bp.fwd;
+  bp.tokens = f.tokens;
+  const size_t slots = (size_t)p->Hv * (size_t)f.nchunks;
+  const size_t th = (size_t)f.tokens * p->Hv;
+  const size_t nblk = (size_t)((f.tokens + kda::BWD_GATE_TOKENS - 1) / kda::BWD_GATE_TOKENS);
+  size_t off = align256(f.off_rec);            // the chunk map only; no forward records
+  bp.off_rec = off;  off = align256(off + slots * kda::bwd_rec(p->K, p->V).bytes);
+  bp.off_h = off;    off = align256(off + slots * p->K * p->V * sizeof(float));
+  bp.off_dh = off;   off = align256(off + slots * p->K * p->V * sizeof(float));
+  bp.off_dqn = off;  off = align256(off + th * p->K * sizeof(float));
+  bp.off_dkn = off;  off = align256(off + th * p->K * sizeof(float));
+  bp.off_db = off;   off = align256(off + th * sizeof(float));
+  bp.off_dg = off;   off = align256(off + th * p->K * sizeof(float));
+  bp.off_part = off; off = align256(off + nblk * p->Hv * (p->K + 1) * sizeof(float));
+  bp.bytes = off;
+  return KDA_OK;
+}
+
+}  // namespace
+
+kda_status_t kda_chunk_bwd_workspace_size(const kda_problem_t* p, size_t* bytes) {
+  if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  BwdPlan bp;
+  kda_status_t st = plan_bwd(p, bp);
+  if (st != KDA_OK) return st;
+  *bytes = bp.bytes;
+  return ok();
+}
+
+kda_status_t kda_chunk_bwd(const kda_problem_t* p, const void* q, const void* k, const void* v,
+                           const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                           const float* initial_state, const int32_t* cu_seqlens, const void* dout,
+                           const float* dht, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                           float* dA_log, float* ddt_bias, float* dh0, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  BwdPlan bp;
+  kda_status_t st = plan_bwd(p, bp);
+  if (st != KDA_OK) return st;
+  const Plan& pl = bp.fwd;
+  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, cu_seqlens)) != KDA_OK) return st;
+  if (pl.tokens > 0) {
+    if ((st = check_token_ptr(q, "q", 16)) != KDA_OK) return st;
+    if ((st = check_token_ptr(dout, "do", 16)) != KDA_OK) return st;
+    const struct { const void* ptr; const char* name; } outs[] = {
+        {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {dg, "dg"}, {dbeta, "dbeta"}};
+    for (const auto& o : outs)
+      if ((st = check_token_ptr(o.ptr, o.name, 4)) != KDA_OK) return st;
+  }
+  for (const float* s : {initial_state, dht, (const float*)dh0, (const float*)dA_log, (const float*)ddt_bias})
+    if (s && !aligned(s, 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "fp32 arguments must be 4-byte aligned");
+  if (workspace_bytes < bp.bytes)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, bp.bytes);
+  if (bp.bytes && !workspace) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (pl.N == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  kda::SeqInfo si = seq_info(p, pl, cu_seqlens, ws);
+  if (si.tnd) {   // chunk map of the packed sequences
+    if ((st = hip_status(kda::launch_chunk_offsets(cu_seqlens, pl.N, reinterpret_cast<int32_t*>(ws + pl.off_chunk), s),
+                         "chunk offsets launch")) != KDA_OK)
+      return st;
+  }
+  // 2. - 6. backward stages
+  kda::BwdArgs a{};
+  a.seq = si;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.dout = dout;
+  a.A_log = A_log; a.dt_bias = dt_bias; a.dht = dht;
+  a.Hk = p->Hk; a.Hv = p->Hv; a.nchunks = (int)pl.nchunks;
+  a.flags = p->flags; a.scale = p->scale; a.eps = p->eps; a.lower_bound = p->lower_bound;
+  a.rec = reinterpret_cast<float*>(ws + bp.off_rec);
+  a.h0 = initial_state;
+  a.h_store = reinterpret_cast<const float*>(ws + bp.off_h);
+  a.h_store_w = reinterpret_cast<float*>(ws + bp.off_h);
+  a.dh_store = reinterpret_cast<float*>(ws + bp.off_dh);
+  a.dh0 = dh0;
+  a.dqn = reinterpret_cast<float*>(ws + bp.off_dqn);
+  a.dkn = reinterpret_cast<float*>(ws + bp.off_dkn);
+  a.dbeta_act = reinterpret_cast<float*>(ws + bp.off_db);
+  a.dg_nat = reinterpret_cast<float*>(ws + bp.off_dg);
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta;
+  a.dA_log = (p->flags & KDA_GATE_IN_KERNEL) ? dA_log : nullptr;
+  a.ddt_bias = ((p->flags & KDA_GATE_IN_KERNEL) && dt_bias) ? ddt_bias : nullptr;
+  float* part = reinterpret_cast<float*>(ws + bp.off_part);
+  // prep (records), forward states, reverse state scan, chunk backward, q/k, gate, gate sums
+  static const int order[] = {0, 6, 1, 2, 3, 4, 5};
+  static const char* what[] = {"backward prep launch", "backward reverse scan launch", "backward chunk launch",
+                               "backward q/k launch", "backward gate launch", "backward gate sum launch",
+                               "backward state scan launch"};
+  for (int stage : order)
+    if ((st = hip_status(kda::launch_bwd(p->K, p->V, p->dtype, a, stage, bp.tokens, part, s), what[stage])) != KDA_OK)
+      return st;
+  return ok();
+}
+
 kda_status_t kda_chunk_fwd_noalloc(const kda_problem_t* p, const void* q, const void* k, const void* v,
                                    const void* g, const void* beta, const float* A_log, const float* dt_bias,
                                    const float* initial_state, const int32_t* cu_seqlens,

@@ -1,0 +1,814 @@
+// Chunkwise KDA backward: gradients of the forward with respect to q, k, v,
+// the gate input, beta, A_log, dt_bias and the initial state.
+//
+// Follows "KDA Chunk Backward — TPU/Pallas Kernel Design": section 1.1 (what
+// the backward recomputes instead of storing), 2.2 (dAv: the output's
+// gradient into the intra-chunk attention and v_new), 2.3 (the reverse
+// inter-chunk recurrence of the state gradient, the WY / intra-chunk
+// backward and the reverse cumsum of the gate gradient) and 2.5 (the gate
+// backward), and "Hyper-Parallel Chunk KDA" section 5.2 (backward stages).
+// All arithmetic is fp32; the decay ratios exp(G_i - G_j) of a chunk are
+// formed pair by pair with non-positive exponents (G is the in-chunk
+// natural-log cumsum, non-increasing), so no range split is needed.
+//
+// Per chunk (rows i < C, h the chunk-entry state, h' its exit state):
+//   v_new = u - w h,   o = qg h + Aqk v_new,   h' = D h + kg^T v_new
+// with u = A (b v), w = A (b k e^G), A = (I + L)^-1, L_ij = b_i sum_c
+// k_ic k_jc e^(G_ic - G_jc) (i > j), Aqk_ij = s sum_c q_ic k_jc e^(G_ic -
+// G_jc) (i >= j), qg = s q e^G, kg = k e^(G_C - G), D = diag(e^G_C).  Given
+// dh' and do:
+//   dv_new = Aqk^T do + kg dh',   dh = qg^T do + D dh' - w^T dv_new
+//   dAqk = tril(do v_new^T),  dqg = do h^T,  dkg = v_new dh'^T,  dD = rowsum(h . dh')
+//   dw = -dv_new h^T,  d(b v) = A^T dv_new,  d(b k e^G) = A^T dw
+//   dA = tril(dv_new (b v)^T + dw (b k e^G)^T),  dL = -strict_tril(A^T dA A^T)
+// and the pair sums of dL and dAqk back into k, q, b and G.
+//
+// Kernels:
+//   bwd_prep_kernel   (chunk, head): gate, norms, sigmoid, G, L, Aqk, A, u, w -> fp32 record
+//   bwd_state_kernel  (sequence, head, 32 columns): the forward state recurrence in
+//                     fp32, storing every chunk-entry state
+//   bwd_scan_kernel   (sequence, head, 32 columns): the reverse recurrence of dh,
+//                     storing each chunk's exit gradient; dh0 at the end
+//   bwd_chunk_kernel  (chunk, head): everything chunk-local
+//   bwd_qk_kernel     (token, q/k head): grouped-head sum and L2Norm backward
+//   bwd_gate_kernel / bwd_gate_sum_kernel: gate and sigmoid backward, dA_log and
+//                     dt_bias sums (two passes, fixed order: deterministic)
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+template <typename T> __device__ __forceinline__ float ldf(const T* p);
+template <> __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ldf<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+
+// acc[a][b] += sum_{k < kr} A(tm + 16a, k) * B(k, tn + 16b): a 256-thread
+// register-blocked product, thread t = 16 tm + tn.
+template <int MR, int NR, typename FA, typename FB>
+__device__ __forceinline__ void mm(float (&acc)[MR][NR], int kr, int tm, int tn, FA A, FB B) {
+  for (int k = 0; k < kr; ++k) {
+    float a[MR], b[NR];
+#pragma unroll
+    for (int i = 0; i < MR; ++i) a[i] = A(tm + 16 * i, k);
+#pragma unroll
+    for (int j = 0; j < NR; ++j) b[j] = B(k, tn + 16 * j);
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[i][j] += a[i] * b[j];
+  }
+}
+template <int MR, int NR>
+__device__ __forceinline__ void zero(float (&acc)[MR][NR]) {
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[i][j] = 0.f;
+}
+
+struct ChunkPos {
+  int n, C;
+  int64_t tok0;     // first token of the chunk
+  int64_t slot;     // head-major (head, global chunk) slot
+  int gc;
+};
+__device__ __forceinline__ ChunkPos chunk_pos(const SeqInfo& s, int gc, int h, int nchunks) {
+  ChunkPos p;
+  p.gc = gc;
+  p.n = seq_of_chunk(s, gc);
+  int64_t t0;
+  int len;
+  seq_range(s, p.n, t0, len);
+  const int cidx = gc - chunk_base(s, p.n);
+  p.tok0 = t0 + (int64_t)cidx * BT;
+  p.C = min(BT, len - cidx * BT);
+  p.slot = (int64_t)h * nchunks + gc;
+  return p;
+}
+
+// ------------------------------------------------------------------ prep
+template <int KD, int VD, typename IT>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int LK = KD + 1, LX = (KD > VD ? KD : VD) + 1;
+  __shared__ float sG[BT * LK], sK[BT * LK], sX[BT * LX];
+  __shared__ float sL[BT * 65], sA[BT * 65];
+  __shared__ float sB[BT];
+  constexpr BwdRec R = bwd_rec(KD, VD);
+  const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
+  const ChunkPos P = chunk_pos(a.seq, gc, h, a.nchunks);
+  const int hk = h / (a.Hv / a.Hk);
+  const int tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
+  float* rec = a.rec + P.slot * (int64_t)(R.bytes / 4);
+  const IT* q = static_cast<const IT*>(a.q);
+  const IT* k = static_cast<const IT*>(a.k);
+  const IT* g = static_cast<const IT*>(a.g);
+  const IT* bt = static_cast<const IT*>(a.beta);
+  const IT* v = static_cast<const IT*>(a.v);
+  const bool gik = a.flags & F_GATE, l2 = a.flags & F_L2;
+  const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;
+  const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
+
+  // rows r = tid / 4, channels 32 * (tid % 4) .. +31 (K = 128; K = 64: 16 each)
+  {
+    const int r = tid >> 2, part = tid & 3;
+    constexpr int CPT = KD / 4;
+    const bool live = r < P.C;
+    float kr[CPT], qr[CPT];
+    float skk = 0.f, sqq = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      const int c = part * CPT + e;
+      kr[e] = live ? ldf(k + ((P.tok0 + r) * a.Hk + hk) * KD + c) : 0.f;
+      qr[e] = live ? ldf(q + ((P.tok0 + r) * a.Hk + hk) * KD + c) : 0.f;
+      skk += kr[e] * kr[e];
+      sqq += qr[e] * qr[e];
+      float gv = live ? ldf(g + ((P.tok0 + r) * a.Hv + h) * KD + c) : 0.f;
+      if (live && gik) gv = -Aexp * softplus_f(gv + (a.dt_bias ? a.dt_bias[h * KD + c] : 0.f));
+      if (live && gv < lb) gv = lb;
+      sG[r * LK + c] = gv;
+    }
+    skk += __shfl_xor(skk, 1);
+    skk += __shfl_xor(skk, 2);
+    sqq += __shfl_xor(sqq, 1);
+    sqq += __shfl_xor(sqq, 2);
+    const float rk = live ? (l2 ? 1.f / sqrtf(skk + a.eps) : 1.f) : 0.f;
+    const float rq = live ? (l2 ? 1.f / sqrtf(sqq + a.eps) : 1.f) : 0.f;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      const int c = part * CPT + e;
+      sK[r * LK + c] = kr[e] * rk;
+      sX[r * LX + c] = qr[e] * rq;
+    }
+    if (part == 0) {
+      float b = live ? ldf(bt + (P.tok0 + r) * a.Hv + h) : 0.f;
+      if (live && (a.flags & F_SIGMOID)) b = sigmoid_f(b);
+      sB[r] = b;
+    }
+  }
+  __syncthreads();
+  // in-chunk cumsum of the decay (natural log); rows past the end keep the last value
+  if (tid < KD) {
+    float run = 0.f;
+    for (int r = 0; r < BT; ++r) {
+      run += sG[r * LK + tid];
+      sG[r * LK + tid] = run;
+    }
+  }
+  __syncthreads();
+  // store G, normalised k and q, beta
+  for (int i = tid; i < BT * KD; i += 256) {
+    const int r = i / KD, c = i % KD;
+    rec[R.G + i] = sG[r * LK + c];
+    rec[R.kn + i] = sK[r * LK + c];
+    rec[R.qn + i] = sX[r * LX + c];
+  }
+  if (tid < BT) rec[R.beta + tid] = sB[tid];
+  // L (strict lower, beta-scaled) and Aqk (lower with diagonal, scaled): pair by pair
+  for (int p = tid; p < BT * (BT + 1) / 2; p += 256) {
+    int i = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+    while (i * (i + 1) / 2 > p) --i;
+    while ((i + 1) * (i + 2) / 2 <= p) ++i;
+    const int j = p - i * (i + 1) / 2;
+    float kd = 0.f, aq = 0.f;
+    for (int c = 0; c < KD; ++c) {
+      const float f = expf(sG[i * LK + c] - sG[j * LK + c]);
+      const float kj = sK[j * LK + c] * f;
+      kd += sK[i * LK + c] * kj;
+      aq += sX[i * LX + c] * kj;
+    }
+    sL[i * 65 + j] = i > j ? sB[i] * kd : 0.f;
+    rec[R.aqk + i * BT + j] = a.scale * aq;
+    if (i != j) {
+      sL[j * 65 + i] = 0.f;
+      rec[R.aqk + j * BT + i] = 0.f;
+    }
+  }
+  __syncthreads();
+  // A = (I + L)^-1 by forward substitution, one column per thread
+  if (tid < BT) {
+    const int j = tid;
+    for (int i = 0; i < BT; ++i) {
+      float s = i == j ? 1.f : 0.f;
+      for (int m = j; m < i; ++m) s -= sL[i * 65 + m] * sA[m * 65 + j];
+      sA[i * 65 + j] = i >= j ? s : 0.f;
+    }
+  }
+  // beta v into sX (q is stored already)
+  __syncthreads();
+  for (int i = tid; i < BT * VD; i += 256) {
+    const int r = i / VD, c = i % VD;
+    sX[r * LX + c] = r < P.C ? sB[r] * ldf(v + ((P.tok0 + r) * a.Hv + h) * VD + c) : 0.f;
+  }
+  for (int i = tid; i < BT * BT; i += 256) rec[R.A + i] = sA[(i / BT) * 65 + i % BT];
+  __syncthreads();
+  {  // u = A (beta v)
+    float acc[4][VD / 16];
+    zero(acc);
+    mm(acc, BT, tm, tn, [&](int i, int j) { return sA[i * 65 + j]; },
+       [&](int j, int c) { return sX[j * LX + c]; });
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < VD / 16; ++y) rec[R.u + (tm + 16 * x) * VD + tn + 16 * y] = acc[x][y];
+  }
+  __syncthreads();
+  for (int i = tid; i < BT * KD; i += 256) {
+    const int r = i / KD, c = i % KD;
+    sX[r * LX + c] = sB[r] * sK[r * LK + c] * expf(sG[r * LK + c]);
+  }
+  __syncthreads();
+  {  // w = A (beta k e^G)
+    float acc[4][KD / 16];
+    zero(acc);
+    mm(acc, BT, tm, tn, [&](int i, int j) { return sA[i * 65 + j]; },
+       [&](int j, int c) { return sX[j * LX + c]; });
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < KD / 16; ++y) rec[R.w + (tm + 16 * x) * KD + tn + 16 * y] = acc[x][y];
+  }
+}
+
+// ------------------------------------------------------ forward state scan
+// The chunk-entry states for the backward, in fp32 from the fp32 records:
+// h <- D h + kg^T (u - w h), every entry state stored.  One workgroup per
+// (sequence, head, 32 columns).
+template <int KD, int VD>
+__global__ __launch_bounds__(256) void bwd_state_kernel(BwdArgs a) {
+  constexpr int TW = 32, LT = TW + 1, LK = KD + 1;
+  __shared__ float sH[KD * LT], sVN[BT * LT], sW[BT * LK], sKG[BT * LK];
+  __shared__ float sGC[KD];
+  constexpr BwdRec R = bwd_rec(KD, VD);
+  constexpr int NT = VD / TW;
+  const int tile = blockIdx.x % NT, h = (blockIdx.x / NT) % a.Hv, n = blockIdx.x / (NT * a.Hv);
+  const int v0 = tile * TW, tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
+  int64_t tok0s;
+  int len;
+  seq_range(a.seq, n, tok0s, len);
+  const int nck = (len + BT - 1) / BT;
+  const int cb = chunk_base(a.seq, n);
+  for (int i = tid; i < KD * TW; i += 256) {
+    const int r = i / TW, c = i % TW;
+    sH[r * LT + c] = a.h0 ? a.h0[(((int64_t)n * a.Hv + h) * KD + r) * VD + v0 + c] : 0.f;
+  }
+  __syncthreads();
+  for (int c = 0; c < nck; ++c) {
+    const int64_t slot = (int64_t)h * a.nchunks + cb + c;
+    const float* rec = a.rec + slot * (int64_t)(R.bytes / 4);
+    const int C = min(BT, len - c * BT);
+    float* dst = a.h_store_w + slot * (int64_t)(KD * VD);
+    for (int i = tid; i < KD * TW; i += 256) dst[(i / TW) * VD + v0 + i % TW] = sH[(i / TW) * LT + i % TW];
+    if (tid < KD) sGC[tid] = rec[R.G + (C - 1) * KD + tid];
+    __syncthreads();
+    for (int i = tid; i < BT * KD; i += 256) {
+      const int r = i / KD, cc = i % KD;
+      sW[r * LK + cc] = rec[R.w + i];
+      sKG[r * LK + cc] = rec[R.kn + i] * expf(sGC[cc] - rec[R.G + i]);
+    }
+    __syncthreads();
+    {  // v_new = u - w h
+      float acc[4][2];
+      zero(acc);
+      mm(acc, KD, tm, tn, [&](int i, int kk) { return sW[i * LK + kk]; }, [&](int kk, int j) { return sH[kk * LT + j]; });
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const int i = tm + 16 * x, j = tn + 16 * y;
+          sVN[i * LT + j] = rec[R.u + i * VD + v0 + j] - acc[x][y];
+        }
+    }
+    __syncthreads();
+    {  // h = D h + kg^T v_new
+      float acc[KD / 16][2];
+      zero(acc);
+      mm(acc, BT, tm, tn, [&](int kk, int r) { return sKG[r * LK + kk]; }, [&](int r, int j) { return sVN[r * LT + j]; });
+#pragma unroll
+      for (int x = 0; x < KD / 16; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const int kk = tm + 16 * x, j = tn + 16 * y;
+          sH[kk * LT + j] = expf(sGC[kk]) * sH[kk * LT + j] + acc[x][y];
+        }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------ reverse state scan
+template <int KD, int VD, typename IT>
+__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
+  constexpr int TW = 32, LT = TW + 1, LK = KD + 1;
+  __shared__ float sDH[KD * LT], sDo[BT * LT], sDV[BT * LT];
+  __shared__ float sM1[BT * LK], sM2[BT * LK], sAq[BT * 65];
+  __shared__ float sGC[KD];
+  constexpr BwdRec R = bwd_rec(KD, VD);
+  constexpr int NT = VD / TW;
+  const int tile = blockIdx.x % NT, h = (blockIdx.x / NT) % a.Hv, n = blockIdx.x / (NT * a.Hv);
+  const int v0 = tile * TW, tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
+  int64_t tok0s;
+  int len;
+  seq_range(a.seq, n, tok0s, len);
+  const int nck = (len + BT - 1) / BT;
+  const int cb = chunk_base(a.seq, n);
+  const IT* dout = static_cast<const IT*>(a.dout);
+  // dh' of the last chunk: the final state's gradient
+  for (int i = tid; i < KD * TW; i += 256) {
+    const int r = i / TW, c = i % TW;
+    sDH[r * LT + c] = a.dht ? a.dht[(((int64_t)n * a.Hv + h) * KD + r) * VD + v0 + c] : 0.f;
+  }
+  __syncthreads();
+  for (int c = nck - 1; c >= 0; --c) {
+    const int64_t slot = (int64_t)h * a.nchunks + cb + c;
+    const float* rec = a.rec + slot * (int64_t)(R.bytes / 4);
+    const int C = min(BT, len - c * BT);
+    const int64_t tok0 = tok0s + (int64_t)c * BT;
+    float* dst = a.dh_store + slot * (int64_t)(KD * VD);
+    for (int i = tid; i < KD * TW; i += 256) dst[(i / TW) * VD + v0 + i % TW] = sDH[(i / TW) * LT + i % TW];
+    if (tid < KD) sGC[tid] = rec[R.G + (C - 1) * KD + tid];
+    __syncthreads();
+    // kg = k e^(G_C - G), Aqk, do
+    for (int i = tid; i < BT * KD; i += 256) {
+      const int r = i / KD, cc = i % KD;
+      sM1[r * LK + cc] = rec[R.kn + i] * expf(sGC[cc] - rec[R.G + i]);
+    }
+    for (int i = tid; i < BT * BT; i += 256) sAq[(i / BT) * 65 + i % BT] = rec[R.aqk + i];
+    for (int i = tid; i < BT * TW; i += 256) {
+      const int r = i / TW, cc = i % TW;
+      sDo[r * LT + cc] = r < C ? ldf(dout + ((tok0 + r) * a.Hv + h) * VD + v0 + cc) : 0.f;
+    }
+    __syncthreads();
+    {  // dv_new = Aqk^T do + kg dh'
+      float acc[4][2];
+      zero(acc);
+      mm(acc, BT, tm, tn, [&](int i, int r) { return sAq[r * 65 + i]; }, [&](int r, int j) { return sDo[r * LT + j]; });
+      mm(acc, KD, tm, tn, [&](int i, int kk) { return sM1[i * LK + kk]; }, [&](int kk, int j) { return sDH[kk * LT + j]; });
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) sDV[(tm + 16 * x) * LT + tn + 16 * y] = acc[x][y];
+    }
+    __syncthreads();
+    // qg = s q e^G and w
+    for (int i = tid; i < BT * KD; i += 256) {
+      const int r = i / KD, cc = i % KD;
+      sM1[r * LK + cc] = a.scale * rec[R.qn + i] * expf(rec[R.G + i]);
+      sM2[r * LK + cc] = rec[R.w + i];
+    }
+    __syncthreads();
+    {  // dh = qg^T do + D dh' - w^T dv_new
+      float acc[KD / 16][2];
+      zero(acc);
+      mm(acc, BT, tm, tn, [&](int kk, int r) { return sM1[r * LK + kk]; }, [&](int r, int j) { return sDo[r * LT + j]; });
+#pragma unroll
+      for (int x = 0; x < KD / 16; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = -acc[x][y];
+      mm(acc, BT, tm, tn, [&](int kk, int r) { return sM2[r * LK + kk]; }, [&](int r, int j) { return sDV[r * LT + j]; });
+      __syncthreads();
+#pragma unroll
+      for (int x = 0; x < KD / 16; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const int kk = tm + 16 * x, j = tn + 16 * y;
+          sDH[kk * LT + j] = expf(sGC[kk]) * sDH[kk * LT + j] - acc[x][y];
+        }
+    }
+    __syncthreads();
+  }
+  if (a.dh0)
+    for (int i = tid; i < KD * TW; i += 256)
+      a.dh0[(((int64_t)n * a.Hv + h) * KD + i / TW) * VD + v0 + i % TW] = sDH[(i / TW) * LT + i % TW];
+}
+
+// --------------------------------------------------------- chunk backward
+template <int KD, int VD, typename IT>
+__global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
+  static_assert(KD == 128 || KD == 64, "K");
+  constexpr int LX = (KD > VD ? KD : VD) + 1;
+  constexpr int MRK = 4, NRK = KD / 16, NRV = VD / 16;
+  __shared__ float sB1[BT * LX], sB2[BT * LX], sB3[BT * LX];
+  __shared__ float sS1[BT * 65], sS2[BT * 65], sS3[BT * 65];
+  __shared__ float sBeta[BT], sGC[KD];
+  static_assert(BT * 17 <= BT * 65 && 16 * KD <= BT * 65, "reduction buffers fit the small matrices");
+  float* sRed = sS1;    // (after the pair sums)
+  float* sRedK = sS2;
+  constexpr BwdRec R = bwd_rec(KD, VD);
+  const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
+  const ChunkPos P = chunk_pos(a.seq, gc, h, a.nchunks);
+  const int tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
+  const float* rec = a.rec + P.slot * (int64_t)(R.bytes / 4);
+  const float* hc = a.h_store + P.slot * (int64_t)(KD * VD);
+  const float* dh = a.dh_store + P.slot * (int64_t)(KD * VD);
+  const IT* dout = static_cast<const IT*>(a.dout);
+  const IT* vin = static_cast<const IT*>(a.v);
+  const float* G = rec + R.G;
+  const float* kn = rec + R.kn;
+  const float* qn = rec + R.qn;
+  auto DO = [&](int i, int c) { return i < P.C ? ldf(dout + ((P.tok0 + i) * a.Hv + h) * VD + c) : 0.f; };
+  auto VV = [&](int i, int c) { return i < P.C ? ldf(vin + ((P.tok0 + i) * a.Hv + h) * VD + c) : 0.f; };
+  if (tid < BT) sBeta[tid] = rec[R.beta + tid];
+  if (tid < KD) sGC[tid] = G[(P.C - 1) * KD + tid];
+  __syncthreads();
+
+  // gradient accumulators of q, k and G, rows tm + 16x, channels tn + 16y
+  float dq[MRK][NRK], dk[MRK][NRK], dG[MRK][NRK];
+  zero(dq);
+  zero(dk);
+  zero(dG);
+  float dbeta[MRK];   // partial sums over this thread's columns
+#pragma unroll
+  for (int x = 0; x < MRK; ++x) dbeta[x] = 0.f;
+  float dGCp[NRK];    // partial sums over this thread's rows
+#pragma unroll
+  for (int y = 0; y < NRK; ++y) dGCp[y] = 0.f;
+
+  {  // v_new = u - w h  -> B1
+    float acc[MRK][NRV];
+    zero(acc);
+    mm(acc, KD, tm, tn, [&](int i, int kk) { return rec[R.w + i * KD + kk]; },
+       [&](int kk, int j) { return hc[kk * VD + j]; });
+#pragma unroll
+    for (int x = 0; x < MRK; ++x)
+#pragma unroll
+      for (int y = 0; y < NRV; ++y) {
+        const int i = tm + 16 * x, j = tn + 16 * y;
+        sB1[i * LX + j] = rec[R.u + i * VD + j] - acc[x][y];
+      }
+  }
+  {  // dv_new = Aqk^T do + kg dh'  -> B2
+    float acc[MRK][NRV];
+    zero(acc);
+    mm(acc, BT, tm, tn, [&](int i, int r) { return rec[R.aqk + r * BT + i]; }, [&](int r, int j) { return DO(r, j); });
+    mm(acc, KD, tm, tn, [&](int i, int kk) { return kn[i * KD + kk] * expf(sGC[kk] - G[i * KD + kk]); },
+       [&](int kk, int j) { return dh[kk * VD + j]; });
+#pragma unroll
+    for (int x = 0; x < MRK; ++x)
+#pragma unroll
+      for (int y = 0; y < NRV; ++y) sB2[(tm + 16 * x) * LX + tn + 16 * y] = acc[x][y];
+  }
+  __syncthreads();
+  {  // dAqk = tril(do v_new^T)  -> S1
+    float acc[MRK][4];
+    zero(acc);
+    mm(acc, VD, tm, tn, [&](int i, int c) { return DO(i, c); }, [&](int c, int j) { return sB1[j * LX + c]; });
+#pragma unroll
+    for (int x = 0; x < MRK; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int i = tm + 16 * x, j = tn + 16 * y;
+        sS1[i * 65 + j] = i >= j ? acc[x][y] : 0.f;
+      }
+  }
+  {  // dqg = do h^T: q and G
+    float acc[MRK][NRK];
+    zero(acc);
+    mm(acc, VD, tm, tn, [&](int i, int c) { return DO(i, c); }, [&](int c, int kk) { return hc[kk * VD + c]; });
+#pragma unroll
+    for (int x = 0; x < MRK; ++x)
+#pragma unroll
+      for (int y = 0; y < NRK; ++y) {
+        const int i = tm + 16 * x, kk = tn + 16 * y;
+        const float e = a.scale * expf(G[i * KD + kk]);
+        dq[x][y] += e * acc[x][y];
+        dG[x][y] += e * qn[i * KD + kk] * acc[x][y];
+      }
+  }
+  {  // dkg = v_new dh'^T: k, G and G_C
+    float acc[MRK][NRK];
+    zero(acc);
+    mm(acc, VD, tm, tn, [&](int i, int c) { return sB1[i * LX + c]; }, [&](int c, int kk) { return dh[kk * VD + c]; });
+#pragma unroll
+    for (int x = 0; x < MRK; ++x)
+#pragma unroll
+      for (int y = 0; y < NRK; ++y) {
+        const int i = tm + 16 * x, kk = tn + 16 * y;
+        const float e = expf(sGC[kk] - G[i * KD + kk]);
+        const float kgv = kn[i * KD + kk] * e;
+        dk[x][y] += e * acc[x][y];
+        dG[x][y] -= kgv * acc[x][y];
+        dGCp[y] += kgv * acc[x][y];
+      }
+  }
+  __syncthreads();
+  {  // dw = -dv_new h^T  -> B1 (v_new no longer needed)
+    float acc[MRK][NRK];
+    zero(acc);
+    mm(acc, VD, tm, tn, [&](int i, int c) { return sB2[i * LX + c]; }, [&](int c, int kk) { return hc[kk * VD + c]; });
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < MRK; ++x)
+#pragma unroll
+      for (int y = 0; y < NRK; ++y) sB1[(tm + 16 * x) * LX + tn + 16 * y] = -acc[x][y];
+  }
+  for (int i = tid; i < BT * BT; i += 256) sS2[(i / BT) * 65 + i % BT] = rec[R.A + i];
+  __syncthreads();
+  {  // d(b k e^G) = A^T dw: k, b, G
+    float acc[MRK][NRK];
+    zero(acc);
+    mm(acc, BT, tm, tn, [&](int j, int i) { return sS2[i * 65 + j]; }, [&](int i, int kk) { return sB1[i * LX + kk]; });
+#pragma unroll
+    for (int x = 0; x < MRK; ++x)
+#pragma unroll
+      for (int y = 0; y < NRK; ++y) {
+        const int j = tm + 16 * x, kk = tn + 16 * y;
+        const float e = expf(G[j * KD + kk]), X = kn[j * KD + kk] * e;
+        const float dX = sBeta[j] * acc[x][y];
+        dbeta[x] += X * acc[x][y];
+        dk[x][y] += e * dX;
+        dG[x][y] += X * dX;
+      }
+  }
+  {  // d(b v) = A^T dv_new: dv and b
+    float acc[MRK][NRV];
+    zero(acc);
+    mm(acc, BT, tm, tn, [&](int j, int i) { return sS2[i * 65 + j]; }, [&](int i, int c) { return sB2[i * LX + c]; });
+#pragma unroll
+    for (int x = 0; x < MRK; ++x) {
+      const int j = tm + 16 * x;
+#pragma unroll
+      for (int y = 0; y < NRV; ++y) {
+        const int c = tn + 16 * y;
+        dbeta[x] += VV(j, c) * acc[x][y];
+        if (j < P.C) a.dv[((P.tok0 + j) * a.Hv + h) * VD + c] = sBeta[j] * acc[x][y];
+      }
+    }
+  }
+  {  // dA = tril(dv_new (b v)^T + dw (b k e^G)^T)  -> S3
+    float acc[MRK][4];
+    zero(acc);
+    mm(acc, VD, tm, tn, [&](int i, int c) { return sB2[i * LX + c]; }, [&](int c, int j) { return sBeta[j] * VV(j, c); });
+    mm(acc, KD, tm, tn, [&](int i, int c) { return sB1[i * LX + c]; },
+       [&](int c, int j) { return sBeta[j] * kn[j * KD + c] * expf(G[j * KD + c]); });
+#pragma unroll
+    for (int x = 0; x < MRK; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int i = tm + 16 * x, j = tn + 16 * y;
+        sS3[i * 65 + j] = i >= j ? acc[x][y] : 0.f;
+      }
+  }
+  __syncthreads();
+  {  // dL = -strict_tril(A^T (dA A^T))  -> S3
+    float acc[MRK][4];
+    zero(acc);
+    mm(acc, BT, tm, tn, [&](int i, int j) { return sS3[i * 65 + j]; }, [&](int j, int m) { return sS2[m * 65 + j]; });
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < MRK; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) sS3[(tm + 16 * x) * 65 + tn + 16 * y] = acc[x][y];
+    __syncthreads();
+    zero(acc);
+    mm(acc, BT, tm, tn, [&](int l, int i) { return sS2[i * 65 + l]; }, [&](int i, int m) { return sS3[i * 65 + m]; });
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < MRK; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int l = tm + 16 * x, m = tn + 16 * y;
+        sS3[l * 65 + m] = l > m ? -acc[x][y] : 0.f;
+      }
+  }
+  // stage G, k, q for the pair sums
+  for (int i = tid; i < BT * KD; i += 256) {
+    const int r = i / KD, c = i % KD;
+    sB1[r * LX + c] = G[i];
+    sB2[r * LX + c] = kn[i];
+    sB3[r * LX + c] = qn[i];
+  }
+  __syncthreads();
+  // pair sums, row side: row i gathers over its columns j
+#pragma unroll
+  for (int x = 0; x < MRK; ++x) {
+    const int i = tm + 16 * x;
+#pragma unroll
+    for (int y = 0; y < NRK; ++y) {
+      const int c = tn + 16 * y;
+      const float gi = sB1[i * LX + c];
+      float rL = 0.f, rA = 0.f;
+      for (int j = 0; j <= i; ++j) {
+        const float kf = sB2[j * LX + c] * expf(gi - sB1[j * LX + c]);
+        rL += sS3[i * 65 + j] * kf;
+        rA += sS1[i * 65 + j] * kf;
+      }
+      const float ki = sB2[i * LX + c], qi = sB3[i * LX + c];
+      dk[x][y] += sBeta[i] * rL;
+      dq[x][y] += a.scale * rA;
+      dG[x][y] += sBeta[i] * ki * rL + a.scale * qi * rA;
+      dbeta[x] += ki * rL;
+    }
+  }
+  // column side: column j gathers over its rows i
+#pragma unroll
+  for (int x = 0; x < MRK; ++x) {
+    const int j = tm + 16 * x;
+#pragma unroll
+    for (int y = 0; y < NRK; ++y) {
+      const int c = tn + 16 * y;
+      const float gj = sB1[j * LX + c];
+      float cL = 0.f, cA = 0.f;
+      for (int i = j; i < BT; ++i) {
+        const float f = expf(sB1[i * LX + c] - gj);
+        cL += sS3[i * 65 + j] * sBeta[i] * sB2[i * LX + c] * f;
+        cA += sS1[i * 65 + j] * sB3[i * LX + c] * f;
+      }
+      const float s = cL + a.scale * cA;
+      dk[x][y] += s;
+      dG[x][y] -= sB2[j * LX + c] * s;
+    }
+  }
+  // reductions: dbeta over columns, dG_C over rows
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < MRK; ++x) sRed[(tm + 16 * x) * 17 + tn] = dbeta[x];
+#pragma unroll
+  for (int y = 0; y < NRK; ++y) sRedK[tm * KD + tn + 16 * y] = dGCp[y];
+  __syncthreads();
+  if (tid < BT) {
+    float s = 0.f;
+    for (int t = 0; t < 16; ++t) s += sRed[tid * 17 + t];
+    if (tid < P.C) a.dbeta_act[(P.tok0 + tid) * a.Hv + h] = s;
+  }
+  if (tid < KD) {
+    float s = 0.f;
+    for (int t = 0; t < 16; ++t) s += sRedK[t * KD + tid];
+    float dd = 0.f;   // dD = rowsum(h . dh')
+    for (int c = 0; c < VD; ++c) dd += hc[tid * VD + c] * dh[tid * VD + c];
+    sGC[tid] = s + expf(sGC[tid]) * dd;   // dG_C
+  }
+  // dG -> dg: reverse cumsum over the chunk's rows plus dG_C
+#pragma unroll
+  for (int x = 0; x < MRK; ++x)
+#pragma unroll
+    for (int y = 0; y < NRK; ++y) sB1[(tm + 16 * x) * LX + tn + 16 * y] = dG[x][y];
+  __syncthreads();
+  if (tid < KD) {
+    float run = sGC[tid];
+    for (int r = P.C - 1; r >= 0; --r) {
+      run += sB1[r * LX + tid];
+      a.dg_nat[((P.tok0 + r) * a.Hv + h) * KD + tid] = run;
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < MRK; ++x) {
+    const int i = tm + 16 * x;
+    if (i >= P.C) continue;
+#pragma unroll
+    for (int y = 0; y < NRK; ++y) {
+      const int c = tn + 16 * y;
+      a.dqn[((P.tok0 + i) * a.Hv + h) * KD + c] = dq[x][y];
+      a.dkn[((P.tok0 + i) * a.Hv + h) * KD + c] = dk[x][y];
+    }
+  }
+}
+
+// ------------------------------------------- grouped heads and L2Norm
+template <int KD, typename IT>
+__global__ __launch_bounds__(64) void bwd_qk_kernel(BwdArgs a, int64_t tokens) {
+  const int64_t tok = blockIdx.x / a.Hk;
+  const int hk = blockIdx.x % a.Hk, lane = threadIdx.x;
+  const int rep = a.Hv / a.Hk;
+  const bool l2 = a.flags & F_L2;
+  const IT* q = static_cast<const IT*>(a.q);
+  const IT* k = static_cast<const IT*>(a.k);
+  for (int which = 0; which < 2; ++which) {
+    const IT* x = which ? k : q;
+    const float* d = which ? a.dkn : a.dqn;
+    float* out = which ? a.dk : a.dq;
+    float xs[2] = {0.f, 0.f}, ds[2] = {0.f, 0.f};
+    float sxx = 0.f, sxd = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = lane + 64 * j;
+      if (c < KD) {
+        xs[j] = ldf(x + (tok * a.Hk + hk) * KD + c);
+        for (int r = 0; r < rep; ++r) ds[j] += d[(tok * a.Hv + hk * rep + r) * KD + c];
+      }
+      sxx += xs[j] * xs[j];
+    }
+    for (int m = 1; m < 64; m <<= 1) sxx += __shfl_xor(sxx, m);
+    const float rr = l2 ? 1.f / sqrtf(sxx + a.eps) : 1.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sxd += xs[j] * rr * ds[j];
+    for (int m = 1; m < 64; m <<= 1) sxd += __shfl_xor(sxd, m);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = lane + 64 * j;
+      if (c < KD) out[(tok * a.Hk + hk) * KD + c] = l2 ? rr * (ds[j] - xs[j] * rr * sxd) : ds[j];
+    }
+  }
+  (void)tokens;
+}
+
+// -------------------------------------------------- gate and sigmoid
+// One workgroup per (value head, block of tokens), one thread per channel:
+// the gate input's gradient, and this block's partial sums of dA_log and
+// dt_bias (summed in block order by bwd_gate_sum_kernel).
+constexpr int GATE_TOKENS = BWD_GATE_TOKENS;
+
+template <int KD, typename IT>
+__global__ __launch_bounds__(KD) void bwd_gate_kernel(BwdArgs a, int64_t tokens, float* part) {
+  const int h = blockIdx.x % a.Hv, blk = blockIdx.x / a.Hv, c = threadIdx.x;
+  const IT* g = static_cast<const IT*>(a.g);
+  const IT* bt = static_cast<const IT*>(a.beta);
+  const bool gik = a.flags & F_GATE;
+  const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;
+  const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
+  const float bias = (gik && a.dt_bias) ? a.dt_bias[h * KD + c] : 0.f;
+  float sA = 0.f, sB = 0.f;
+  const int64_t t0 = (int64_t)blk * GATE_TOKENS, t1 = min(tokens, t0 + GATE_TOKENS);
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t i = (t * a.Hv + h) * KD + c;
+    const float dgn = a.dg_nat[i];
+    const float x = ldf(g + i);
+    float gact = x, dz = dgn;
+    if (gik) {
+      const float z = x + bias;
+      gact = -Aexp * softplus_f(z);
+      dz = dgn * -Aexp * sigmoid_f(z);
+    }
+    const bool clamped = gact < lb;
+    if (clamped) dz = 0.f;
+    a.dg[i] = dz;
+    sB += dz;
+    sA += clamped ? 0.f : dgn * gact;
+    if (c == 0) {
+      const int64_t j = t * a.Hv + h;
+      float db = a.dbeta_act[j];
+      if (a.flags & F_SIGMOID) {
+        const float s = sigmoid_f(ldf(bt + j));
+        db *= s * (1.f - s);
+      }
+      a.dbeta[j] = db;
+    }
+  }
+  // partial sums: [blk][Hv][KD + 1] (dt_bias per channel, then A_log)
+  float* pp = part + ((int64_t)blk * a.Hv + h) * (KD + 1);
+  pp[c] = sB;
+  __shared__ float red[KD];
+  red[c] = sA;
+  __syncthreads();
+  if (c == 0) {
+    float s = 0.f;
+    for (int i = 0; i < KD; ++i) s += red[i];
+    pp[KD] = s;
+  }
+}
+
+template <int KD>
+__global__ __launch_bounds__(KD) void bwd_gate_sum_kernel(BwdArgs a, int nblk, const float* part) {
+  const int h = blockIdx.x, c = threadIdx.x;
+  float sB = 0.f, sA = 0.f;
+  for (int b = 0; b < nblk; ++b) {
+    const float* pp = part + ((int64_t)b * a.Hv + h) * (KD + 1);
+    sB += pp[c];
+    if (c == 0) sA += pp[KD];
+  }
+  if (a.ddt_bias) a.ddt_bias[h * KD + c] = sB;
+  if (c == 0 && a.dA_log) a.dA_log[h] = sA;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int64_t tokens, float* part,
+                      hipStream_t s) {
+  const long nb_chunk = (long)a.nchunks * a.Hv;
+  const long nb_scan = (long)a.seq.N * a.Hv * (V / 32);
+  const long nb_qk = (long)tokens * a.Hk;
+  const int nblk = (int)((tokens + GATE_TOKENS - 1) / GATE_TOKENS);
+  if (nb_chunk > 0x7fffffffL || nb_qk > 0x7fffffffL || (long)nblk * a.Hv > 0x7fffffffL) return hipErrorInvalidValue;
+#define KDA_BWD_CASE(KK, VV, TT)                                                                        \
+  if (K == KK && V == VV) {                                                                             \
+    switch (stage) {                                                                                    \
+      case 0: return nb_chunk ? launch(bwd_prep_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(256), s, a) : hipSuccess; \
+      case 1: return nb_scan ? launch(bwd_scan_kernel<KK, VV, TT>, dim3(nb_scan), dim3(256), s, a) : hipSuccess;   \
+      case 2: return nb_chunk ? launch(bwd_chunk_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(256), s, a) : hipSuccess; \
+      case 3: return nb_qk ? launch(bwd_qk_kernel<KK, TT>, dim3(nb_qk), dim3(64), s, a, tokens) : hipSuccess;       \
+      case 4: return nblk ? launch(bwd_gate_kernel<KK, TT>, dim3(nblk * a.Hv), dim3(KK), s, a, tokens, part)        \
+                          : hipSuccess;                                                                 \
+      case 5: return launch(bwd_gate_sum_kernel<KK>, dim3(a.Hv), dim3(KK), s, a, nblk, (const float*)part);       \
+      case 6: return nb_scan ? launch(bwd_state_kernel<KK, VV>, dim3(nb_scan), dim3(256), s, a) : hipSuccess;       \
+    }                                                                                                   \
+    return hipErrorInvalidValue;                                                                        \
+  }
+  if (dtype == 1) {
+    KDA_BWD_CASE(128, 128, bf16_t)
+    KDA_BWD_CASE(64, 64, bf16_t)
+    KDA_BWD_CASE(128, 64, bf16_t)
+    KDA_BWD_CASE(64, 128, bf16_t)
+  } else {
+    KDA_BWD_CASE(128, 128, float)
+    KDA_BWD_CASE(64, 64, float)
+    KDA_BWD_CASE(128, 64, float)
+    KDA_BWD_CASE(64, 128, float)
+  }
+#undef KDA_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -13,6 +13,7 @@ hipError_t launch_scan(int, int, int, const ScanArgs&, hipStream_t) { return hip
 hipError_t launch_merge(int, int, const MergeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_prefix_merge(int, int, const PrefixMergeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_recurrent(int, int, int, const RecurrentArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_bwd(int, int, int, const BwdArgs&, int, int64_t, float*, hipStream_t) { return hipSuccess; }
 // (no device scratch in a host-only build)
 hipError_t noalloc_scratch(hipStream_t, void**, char* why, size_t why_len) {
   snprintf(why, why_len, "host-only build");

@@ -91,7 +91,7 @@ struct ScanArgs {
   const int32_t* state_idx;           // cache mode
   float* hT;                          // final [N,Hv,K,V] | cache | null ; summary: S~
   float* M;                           // summary only: [N*seg_max,Hv,K,K] (S~ in hT alike)
-  void* o;                            // [tokens,Hv,V]
+  void* o;                            // [tokens,Hv,V] (null: not written)
 };
 
 // Token-by-token forward (decode).  One wave per (64-column slice, head, sequence).
@@ -134,6 +134,48 @@ inline hipError_t launch(void (*kern)(A...), dim3 grid, dim3 block, hipStream_t 
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, 0, s);
 }
 
+// Backward record per (head, chunk), fp32 row-major, offsets in floats:
+//   G [64][K] in-chunk natural-log cumsum of the decay (rows past the end keep
+//   the last value), kn / qn [64][K] normalised k and q, beta [64] (activated),
+//   A [64][64] = (I + L)^-1, aqk [64][64] (scaled, zero above the diagonal),
+//   w [64][K], u [64][V].
+struct BwdRec {
+  size_t G, kn, qn, beta, A, aqk, w, u, bytes;
+};
+__host__ __device__ constexpr BwdRec bwd_rec(int K, int V) {
+  BwdRec r{};
+  r.G = 0;
+  r.kn = r.G + 64 * (size_t)K;
+  r.qn = r.kn + 64 * (size_t)K;
+  r.beta = r.qn + 64 * (size_t)K;
+  r.A = r.beta + 64;
+  r.aqk = r.A + 64 * 64;
+  r.w = r.aqk + 64 * 64;
+  r.u = r.w + 64 * (size_t)K;
+  r.bytes = al256((r.u + 64 * (size_t)V) * 4);
+  return r;
+}
+
+struct BwdArgs {
+  SeqInfo seq;
+  const void *q, *k, *v, *g, *beta, *dout;   // token tensors (dtype of q)
+  const float *A_log, *dt_bias, *dht;        // dht [N][Hv][K][V] or null
+  int Hk, Hv, nchunks;
+  uint32_t flags;
+  float scale, eps, lower_bound;
+  float* rec;                 // [Hv * nchunks] backward records
+  const float* h0;            // [N][Hv][K][V] or null (zero)
+  const float* h_store;       // [Hv * nchunks][K][V] chunk-entry states
+  float* h_store_w;           // the same buffer, written by the state kernel
+  float* dh_store;            // [Hv * nchunks][K][V] gradients of the chunk-exit states
+  float* dh0;                 // [N][Hv][K][V] or null
+  float *dqn, *dkn;           // [tokens][Hv][K]: per value head, w.r.t. normalised q / k
+  float *dbeta_act, *dg_nat;  // [tokens][Hv] w.r.t. activated beta, [tokens][Hv][K] w.r.t. the decay
+  float *dq, *dk;             // [tokens][Hk][K]
+  float *dv, *dg, *dbeta;     // [tokens][Hv][V], [tokens][Hv][K], [tokens][Hv]
+  float *dA_log, *ddt_bias;   // [Hv], [Hv][K] or null
+};
+
 // dtype: 0 = fp32, 1 = bf16
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);
 hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t s);
@@ -141,6 +183,12 @@ hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s
 hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s);
 hipError_t launch_prefix_merge(int K, int V, const PrefixMergeArgs& a, hipStream_t s);
 hipError_t launch_recurrent(int K, int V, int dtype, const RecurrentArgs& a, hipStream_t s);
+// Backward stage: 0 prep, 6 forward state scan (fp32), 1 reverse state scan,
+// 2 chunk-local backward, 3 grouped heads + L2Norm, 4 gate/sigmoid with block
+// partial sums (into `part`), 5 the sums of those partials.
+hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int64_t tokens, float* part,
+                      hipStream_t s);
+constexpr int BWD_GATE_TOKENS = 512;   // tokens per gate workgroup (one partial each)
 // Device address of the fixed scratch on the stream's device (kda_noalloc.hip);
 // on failure `why` names the step that failed.
 hipError_t noalloc_scratch(hipStream_t stream, void** out, char* why, size_t why_len);

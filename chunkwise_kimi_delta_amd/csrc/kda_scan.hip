@@ -415,7 +415,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int t = 16 * (TPO * ow + j) + r16;
-          if (t < len - c * BT)
+          if (op && t < len - c * BT)
             store4(op + (tok0s + (int64_t)c * BT + t) * (int64_t)(a.Hv * VD) + (int64_t)h * VD + v0 + 16 * ct + 4 * quad,
                    pend[j][ct]);
         }

@@ -44,7 +44,8 @@ class KdaProblem(ctypes.Structure):
 
 
 _lib = None
-EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_segment_summary_workspace_size",
+EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
+           "kda_segment_summary_workspace_size",
            "kda_segment_summary", "kda_summary_merge", "kda_recurrent_fwd", "kda_chunk_fwd_noalloc",
            "kda_chunk_offsets_host",
            "kda_status_string", "kda_last_error", "kda_abi_version")
@@ -68,12 +69,17 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_summary_merge.argtypes = [I32, I32, I32, I32, VP, VP, VP, VP]
     lib.kda_recurrent_fwd.argtypes = [P] + [VP] * 12 + [VP]
     lib.kda_chunk_fwd_noalloc.argtypes = [P] + [VP] * 12 + [VP]
+    lib.kda_chunk_bwd_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
+    lib.kda_chunk_bwd.argtypes = [P] + [VP] * 20 + [SZ, VP]
     lib.kda_chunk_offsets_host.argtypes = [VP, I32, I32, VP]
     lib.kda_status_string.argtypes = [I32]
     lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_abi_version.argtypes = []
     lib.kda_abi_version.restype = I32
-    for name in ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_segment_summary_workspace_size",
+    for name in ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_bwd_workspace_size",
+                 "kda_chunk_bwd", "kda_segment_summary_workspace_size",
                  "kda_segment_summary", "kda_summary_merge", "kda_recurrent_fwd", "kda_chunk_fwd_noalloc",
                  "kda_chunk_offsets_host"):
         getattr(lib, name).restype = I32
@@ -178,7 +184,8 @@ def _cu_pair(cu_seqlens, cu_seqlens_host, device, tokens: torch.Tensor):
 
 def _forward_args(q, k, v, g, beta, *, scale, A_log, dt_bias, initial_state, cu_seqlens,
                   cu_seqlens_host, state_indices, output_final_state, gate_in_kernel, safe_gate,
-                  lower_bound, qk_l2norm, beta_sigmoid, eps, o, final_state, scan_segments=0):
+                  lower_bound, qk_l2norm, beta_sigmoid, eps, o, final_state, scan_segments=0,
+                  alloc_o=True):
     """Checks and marshalling shared by the forward calls: every tensor's shape,
     dtype, layout and device, then the problem descriptor and the outputs."""
     if q.dim() not in (3, 4) or v.dim() != q.dim():
@@ -230,7 +237,7 @@ def _forward_args(q, k, v, g, beta, *, scale, A_log, dt_bias, initial_state, cu_
              | (KDA_QK_L2NORM if qk_l2norm else 0) | (KDA_BETA_SIGMOID if beta_sigmoid else 0))
     p, N = make_problem(q, v, scale=scale, flags=flags, eps=eps, lower_bound=lower_bound,
                         cu_host=cu_h, state_rows=rows, scan_segments=scan_segments)
-    if o is None:
+    if o is None and alloc_o:
         o = torch.empty(v.shape, dtype=v.dtype, device=dev)
     if cache:
         si = state_indices.to(device=dev, dtype=torch.int32).contiguous()
@@ -302,6 +309,48 @@ def kda_chunk_fwd_noalloc(q, k, v, g, beta, *, o, final_state=None, scale: Optio
                                      _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_d),
                                      _ptr(si), _ptr(o), _ptr(final_state), _stream(dev)))
     return o, final_state
+
+
+def kda_chunk_bwd(q, k, v, g, beta, do, *, dht=None, scale: Optional[float] = None, A_log=None,
+                  dt_bias=None, initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
+                  gate_in_kernel: bool = False, safe_gate: bool = False, lower_bound: float = -5.0,
+                  qk_l2norm: bool = False, beta_sigmoid: bool = False, eps: float = 1e-6,
+                  workspace=None) -> dict:
+    """Gradients of sum(do * o) + sum(dht * final_state) for the forward with
+    the same arguments (dense initial states).  Returns fp32 tensors: dq, dk
+    (shape of q / k), dv, dg (w.r.t. g as passed), dbeta (w.r.t. beta as
+    passed), and dA_log / ddt_bias (with the in-kernel gate) and dh0 (with an
+    initial state)."""
+    lib = load()
+    p, dev, cu_d, _, _, _ = _forward_args(
+        q, k, v, g, beta, scale=scale, A_log=A_log, dt_bias=dt_bias, initial_state=initial_state,
+        cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, state_indices=None,
+        output_final_state=False, gate_in_kernel=gate_in_kernel, safe_gate=safe_gate,
+        lower_bound=lower_bound, qk_l2norm=qk_l2norm, beta_sigmoid=beta_sigmoid, eps=eps, o=None,
+        final_state=None, alloc_o=False)
+    N, Hv, K, V = p.num_seqs, v.shape[-2], q.shape[-1], v.shape[-1]
+    _need(do, "do", v.dtype, v.shape, dev)
+    _need(dht, "dht", torch.float32, (N, Hv, K, V), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty(q.shape, **f32), dk=torch.empty(k.shape, **f32), dv=torch.empty(v.shape, **f32),
+               dg=torch.empty(g.shape, **f32), dbeta=torch.empty(beta.shape, **f32))
+    if gate_in_kernel:
+        out["dA_log"] = torch.empty((Hv,), **f32)
+        if dt_bias is not None:
+            out["ddt_bias"] = torch.empty((Hv, K), **f32)
+    if initial_state is not None:
+        out["dh0"] = torch.empty((N, Hv, K, V), **f32)
+    ws_bytes = ctypes.c_size_t()
+    _check(lib.kda_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes.value, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    _check(lib.kda_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                             _ptr(dt_bias), _ptr(initial_state), _ptr(cu_d), _ptr(do), _ptr(dht),
+                             _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                             _ptr(out["dbeta"]), _ptr(out.get("dA_log")), _ptr(out.get("ddt_bias")),
+                             _ptr(out.get("dh0")), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
 
 
 def kda_recurrent_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None, dt_bias=None,

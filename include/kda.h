@@ -140,6 +140,43 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p,
                            void* workspace, size_t workspace_bytes, void* stream,
                            void* const* stage_events);
 
+/* Bytes of device workspace kda_chunk_bwd needs for this problem. */
+kda_status_t kda_chunk_bwd_workspace_size(const kda_problem_t* p, size_t* bytes);
+
+/*
+ * Chunkwise KDA backward ("KDA Chunk Backward — TPU/Pallas Kernel Design",
+ * sections 1.1, 2.2, 2.3 and 2.5; "Hyper-Parallel Chunk KDA" section 5.2):
+ * the gradients of L = sum(do * o) + sum(dht * final_state) for the forward
+ * kda_chunk_fwd computes with the same arguments.  The forward quantities are
+ * recomputed (the call runs the forward's kernels first, keeping every
+ * chunk-entry state in the workspace), then the state gradient is carried
+ * backwards over the chunks and every chunk's local backward runs in
+ * parallel.  All gradients are fp32, computed in fp32.
+ *  q ... cu_seqlens : as in kda_chunk_fwd; p->state_rows must be 0 (dense states).
+ *  dout  : dL/do, [.., Hv, V] in p->dtype.   dht : fp32 [N,Hv,K,V] or NULL (zero).
+ *  dq, dk : fp32 [.., Hk, K] (grouped heads summed over their value heads; with
+ *           KDA_QK_L2NORM, with respect to the raw q and k).
+ *  dv     : fp32 [.., Hv, V].
+ *  dg     : fp32 [.., Hv, K], with respect to g as passed (the raw gate with
+ *           KDA_GATE_IN_KERNEL, else the natural-log decay); zero where the
+ *           safe-gate clamp is active.
+ *  dbeta  : fp32 [.., Hv], with respect to beta as passed (the logit with
+ *           KDA_BETA_SIGMOID).
+ *  dA_log : fp32 [Hv] or NULL; ddt_bias : fp32 [Hv,K] or NULL (KDA_GATE_IN_KERNEL;
+ *           ddt_bias needs dt_bias).  dh0 : fp32 [N,Hv,K,V] or NULL.
+ *  workspace : at least kda_chunk_bwd_workspace_size bytes.
+ * Every output is overwritten; nothing is accumulated into.
+ */
+kda_status_t kda_chunk_bwd(const kda_problem_t* p,
+                           const void* q, const void* k, const void* v,
+                           const void* g, const void* beta,
+                           const float* A_log, const float* dt_bias,
+                           const float* initial_state, const int32_t* cu_seqlens,
+                           const void* dout, const float* dht,
+                           float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                           float* dA_log, float* ddt_bias, float* dh0,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of the fixed device scratch behind kda_chunk_fwd_noalloc (64 MiB). */
 #define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
 

@@ -32,6 +32,21 @@ def test_every_declared_symbol_is_exported(lib):
     assert lib.kda_abi_version() == kda.ABI_VERSION == 2
 
 
+def test_binding_argument_counts_match_the_header(lib):
+    """Every function the header declares is bound with exactly as many
+    argument types as it has parameters (a missing one makes ctypes pass the
+    trailing arguments with the wrong width)."""
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    decls = re.findall(r"\b(kda_[a-z_]+)\s*\(([^;{]*?)\)\s*;", src, flags=re.S)
+    assert len(decls) == len(kda.EXPORTS)
+    for name, params in decls:
+        params = params.strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        bound = getattr(lib, name).argtypes
+        assert bound is not None and len(bound) == n, (name, n, bound)
+
+
 def _problem(**kw):
     d = dict(layout=0, dtype=1, B=1, T=8192, Hk=32, Hv=32, K=128, V=128, chunk_size=64, flags=15,
              scale=128 ** -0.5, eps=1e-6, lower_bound=-5.0, num_seqs=1, cu_seqlens_host=None,

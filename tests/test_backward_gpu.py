@@ -1,0 +1,153 @@
+"""GPU parity of the backward (kda_chunk_bwd, through the C ABI) against the
+fp64 oracle's adjoint.
+
+The gradients are fp32 outputs computed in fp32: bar err_max <= 5e-3 (max
+|x - ref| / max |ref| per tensor), the bar for fp32 results.  The loss is
+sum(do * o) + sum(dht * final_state) with seeded do ~ N(0, 1) (token dtype)
+and dht ~ N(0, 0.01^2).
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kda_synth as ks
+from kda_synth.torch_io import flag_kwargs, to_torch
+from oracle import kda_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL_GRAD = 5e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(name, x, ref, tol=TOL_GRAD):
+    c = orc.compare(x, ref)
+    say(f"  {name}: err_max={c['err_max']:.3e} rel_l2={c['rel_l2']:.3e} nonfinite={c['nonfinite']}")
+    assert c["nonfinite"] == 0, name
+    assert c["err_max"] <= tol, (name, c)
+    return c
+
+
+def cotangents(p, seed=77, dht_std=0.01, do_scale=1.0):
+    rng = np.random.default_rng(seed)
+    do = rng.standard_normal(p.v.shape).astype(np.float32) * np.float32(do_scale)
+    do = ks.bf16_round(do) if p.dtype == "bf16" else do
+    N = p.num_seqs
+    dht = (rng.standard_normal((N, p.Hv, p.K, p.V)) * dht_std).astype(np.float32)
+    return do, dht
+
+
+def gpu_bwd(kda, p, do, dht, t=None):
+    t = t or to_torch(p)
+    dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+    out = kda.kda_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], torch.from_numpy(do).to("cuda", dt),
+                            dht=torch.from_numpy(dht).cuda(), scale=p.scale, A_log=t["A_log"],
+                            dt_bias=t["dt_bias"], initial_state=None if p.h0 is None else t["h0"],
+                            cu_seqlens=t["cu"], cu_seqlens_host=t["cu_host"], **flag_kwargs(p))
+    torch.cuda.synchronize()
+    return out
+
+
+def bwd_case(kda, p, seed=77, **cot):
+    say(f"case {p.name}: layout={p.layout} dtype={p.dtype} B={p.B} T={p.T} Hk={p.Hk} Hv={p.Hv} "
+        f"K={p.K} V={p.V}")
+    do, dht = cotangents(p, seed, **cot)
+    got = gpu_bwd(kda, p, do, dht)
+    ref = orc.backward(p, do, dht)
+    names = ["dq", "dk", "dv", "dg", "dbeta"]
+    if p.h0 is not None:
+        names.append("dh0")
+    if p.gate_in_kernel:
+        names.append("dA_log")
+        if p.dt_bias is not None:
+            names.append("ddt_bias")
+    for n in names:
+        check(n, np64(got[n]), ref[n])
+    return got, ref
+
+
+def test_bwd_layer_small(gpu_lib):
+    bwd_case(gpu_lib, ks.make("layer", T=150, H=2))
+
+
+@pytest.mark.parametrize("T", [1, 64, 200])
+def test_bwd_layer_ragged(gpu_lib, T):
+    bwd_case(gpu_lib, ks.make("layer", T=T, H=2))
+
+
+def test_bwd_gqa_small_safe_gate(gpu_lib):
+    """Grouped heads (dq, dk summed over the group) and the safe-gate clamp."""
+    p = ks.make("gqa", B=2, T=130, Hk=2, Hv=4)
+    got, ref = bwd_case(gpu_lib, p)
+
+
+def test_bwd_varlen_dense_states(gpu_lib):
+    p = ks.make("varlen", lens=[70, 1, 130, 0, 64], H=2, cache_rows=5, n_invalid=0)
+    p = dataclasses.replace(p, state_indices=None)       # dense [N, H, K, V] initial states
+    bwd_case(gpu_lib, p)
+
+
+def test_bwd_fp32_tiny(gpu_lib):
+    """fp32 tokens, K = V = 64, precomputed gate, pre-normalised q/k, beta given."""
+    bwd_case(gpu_lib, ks.make("tiny"))
+
+
+@pytest.mark.parametrize("K,V", [(64, 128), (128, 64)])
+def test_bwd_head_dims(gpu_lib, K, V):
+    bwd_case(gpu_lib, ks.make("layer", T=100, H=2, K=K, V=V))
+
+
+def test_bwd_T65_strong_decay_final_state_loss(gpu_lib):
+    """The known hard case: T = 65 (one full chunk and one token), strong decay,
+    a loss on the final state only (do = 0).  The pages' acceptance gate for dk
+    is a relative L2 error below 4%; here every gradient is held to the fp32 bar."""
+    p = ks.make("layer", T=65, H=2)
+    p.A_log = np.array([np.log(16.0), np.log(40.0)], dtype=np.float32)
+    got, ref = bwd_case(gpu_lib, p, do_scale=0.0, dht_std=1.0)
+    c = orc.compare(np64(got["dk"]), ref["dk"])
+    assert c["rel_l2"] < 0.04
+
+
+def test_bwd_slow_decay(gpu_lib):
+    """Slow decay: the state gradient reaches back over all chunks."""
+    p = ks.make("layer", T=640, H=2)
+    p.A_log = np.log(np.array([1e-3, 3e-3], dtype=np.float32))
+    p.dt_bias = np.full_like(p.dt_bias, -4.0)
+    bwd_case(gpu_lib, p)
+
+
+def test_bwd_deterministic(gpu_lib):
+    p = ks.make("gqa", B=1, T=200, Hk=2, Hv=4)
+    do, dht = cotangents(p)
+    t = to_torch(p)
+    a = gpu_bwd(gpu_lib, p, do, dht, t)
+    b = gpu_bwd(gpu_lib, p, do, dht, t)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_bwd_gqa_full_size_sampled(gpu_lib):
+    """The GQA long batch (B=4, T=16384, 16 q/k heads over 64 value heads, safe
+    gate) at full size on the GPU; batch 0's first head group (q/k head 0, value
+    heads 0-3) against the oracle run on batch 0 alone (batches are independent)."""
+    p = ks.make("gqa")
+    do, dht = cotangents(p)
+    got = gpu_bwd(gpu_lib, p, do, dht)
+    b0 = dataclasses.replace(p, B=1, q=p.q[:1], k=p.k[:1], v=p.v[:1], g=p.g[:1], beta=p.beta[:1], h0=p.h0[:1])
+    ref = orc.backward(b0, do[:1], dht[:1], heads=[0, 1, 2, 3])
+    check("dq (q/k head 0)", np64(got["dq"])[0, :, 0], ref["dq"][0, :, 0])
+    check("dk (q/k head 0)", np64(got["dk"])[0, :, 0], ref["dk"][0, :, 0])
+    for n in ("dv", "dg", "dbeta"):
+        check(n, np64(got[n])[0][:, :4], ref[n][0][:, :4])
+    check("dh0", np64(got["dh0"])[0, :4], ref["dh0"][0, :4])
