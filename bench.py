@@ -122,7 +122,7 @@ def setup(name, dev, hev, scan_segments=0):
     from chunkwise_kimi_delta_amd import kda
     from kda_synth.torch_io import flag_kwargs, to_torch
 
-    p = ks.make(name)
+    p = ks.make("gqa" if name == "gqa_train" else name)
     t = to_torch(p, dev)
     kw = flag_kwargs(p)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -171,6 +171,41 @@ def setup(name, dev, hev, scan_segments=0):
                                "fwd_chunk_local": token_bytes(p, with_o=False),
                                "fwd_scan": nbytes(p.v, 2 if p.dtype == "bf16" else 4) + 2 * state},
                     config={"T": p.T, "H": Hv, "dk": K, "dv": V, "preceding_summaries": P})
+        return step, meta
+
+    if name == "gqa_train":
+        # forward, then the backward given seeded do ~ N(0, 1) and dht ~ N(0, 0.01^2)
+        rng = np.random.default_rng(2024)
+        do = torch.from_numpy(ks.bf16_round(rng.standard_normal(p.v.shape).astype(np.float32))).to(
+            dev, torch.bfloat16)
+        dht = torch.from_numpy((rng.standard_normal((N, Hv, K, V)) * 0.01).astype(np.float32)).to(dev)
+        o = torch.empty_like(t["v"])
+        final = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev)
+        ws = torch.empty(kda.workspace_bytes(t["q"], t["v"]), dtype=torch.uint8, device=dev)
+        bws = torch.empty(kda_bwd_ws_bytes(kda, p, t), dtype=torch.uint8, device=dev)
+
+        def step(m):
+            kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=p.scale, A_log=t["A_log"],
+                              dt_bias=t["dt_bias"], initial_state=t["h0"], o=o, final_state=final,
+                              workspace=ws, stage_events=None if m is None else m[0:3], **kw)
+            g = kda.kda_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], do, dht=dht, scale=p.scale,
+                                  A_log=t["A_log"], dt_bias=t["dt_bias"], initial_state=t["h0"],
+                                  workspace=bws, **kw)
+            if m is not None:
+                hev.record(m[3], stream)
+            del g
+
+        es = 2
+        fwd_b = token_bytes(p) + 2 * N * state
+        # backward: q, k, v, g, beta, do read; dq, dk, dv, dg, dbeta written in fp32; h0, dht read, dh0 written
+        bwd_b = (token_bytes(p, with_o=False) + nbytes(p.v, es) + nbytes(p.q, 4) + nbytes(p.k, 4)
+                 + nbytes(p.v, 4) + nbytes(p.g, 4) + nbytes(p.beta, 4) + 3 * N * state)
+        meta = dict(p=p, flop=3 * fpt * th, bytes=fwd_b + bwd_b, nmarks=4,
+                    intervals={"fwd_intra_kernel": (0, 1), "fwd_scan_kernel": (1, 2), "backward": (2, 3)},
+                    own_bytes={"fwd_intra_kernel": token_bytes(p, with_o=False),
+                               "fwd_scan_kernel": nbytes(p.v, es) + 2 * N * state, "backward": bwd_b},
+                    config={"B": p.B, "T": p.T, "Hk": p.Hk, "H": Hv, "dk": K, "dv": V,
+                            "step": "forward + backward (flop counted as 3x the forward's)"})
         return step, meta
 
     if name == "decode":
@@ -225,6 +260,21 @@ def setup(name, dev, hev, scan_segments=0):
     return step, meta
 
 
+def kda_bwd_ws_bytes(kda, p, t):
+    """Backward workspace bytes for a problem's shapes (through the C ABI)."""
+    import ctypes
+    lib = kda.load()
+    from kda_synth.torch_io import flag_kwargs
+    fl = flag_kwargs(p)
+    flags = ((kda.KDA_GATE_IN_KERNEL if fl["gate_in_kernel"] else 0) | (kda.KDA_SAFE_GATE if fl["safe_gate"] else 0)
+             | (kda.KDA_QK_L2NORM if fl["qk_l2norm"] else 0) | (kda.KDA_BETA_SIGMOID if fl["beta_sigmoid"] else 0))
+    pr, _ = kda.make_problem(t["q"], t["v"], scale=p.scale, flags=flags, eps=p.eps, lower_bound=p.lower_bound,
+                             cu_host=t["cu_host"])
+    sz = ctypes.c_size_t()
+    kda._check(lib.kda_chunk_bwd_workspace_size(ctypes.byref(pr), ctypes.byref(sz)))
+    return sz.value
+
+
 WORKLOAD_TEXT = {
     "tiny": "tiny KDA forward (fp32, precomputed gate, pre-normalised q/k)",
     "layer": "Kimi-Linear-shaped KDA layer forward",
@@ -233,6 +283,7 @@ WORKLOAD_TEXT = {
     "gqa": "GQA long batch forward (16 q/k heads shared by 64 value heads, safe gate)",
     "decode": "decode step: one token for each of 64 sequences, state cache updated in place",
     "longseq": "long sequence over few heads (B=1, T=65536, H=4): segment-parallel scan",
+    "gqa_train": "GQA long batch forward + backward (dq, dk, dv, dbeta, dg, dA_log, ddt_bias, dh0)",
 }
 
 
@@ -259,6 +310,32 @@ def cpu_baseline(p, target_token_heads):
     return {"value": per_run * repeats / dt / p.Hv, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {t_max} tokens of each of {N} sequence(s) x all {p.Hv} value heads, "
                       f"{repeats} run(s) ({dt:.1f} s, numpy fp64 token recurrence, 1 thread)",
+            "host_cpu": platform.processor() or platform.machine(),
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline_train(p, target_token_heads):
+    """The fp64 oracle's forward and backward on the first t tokens of batch 0
+    over all value heads (t sized to about ``target_token_heads``), scaled to
+    tokens/s of the whole workload like ``cpu_baseline``."""
+    import dataclasses
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kda_oracle as orc
+    t = min(p.T, max(1, target_token_heads // (2 * p.Hv)))
+    sub = dataclasses.replace(p, B=1, T=t, q=p.q[:1, :t], k=p.k[:1, :t], v=p.v[:1, :t], g=p.g[:1, :t],
+                              beta=p.beta[:1, :t], h0=p.h0[:1])
+    do = np.random.default_rng(0).standard_normal(sub.v.shape)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        orc.forward(sub)
+        orc.backward(sub, do, None)
+        dt = time.perf_counter() - t0
+    return {"value": t / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"forward + backward on the first {t} tokens of batch 0 x all {p.Hv} value heads "
+                      f"({dt:.1f} s, numpy fp64, 1 thread)",
             "host_cpu": platform.processor() or platform.machine(),
             "host_cores_available": len(os.sched_getaffinity(0))}
 
@@ -481,7 +558,8 @@ def main():
                                 for k, v in mfma.items() if isinstance(v, dict) and "mfma_busy_frac" in v}
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on about {args.cpu_token_heads} token-heads ...")
-        res["cpu_baseline"] = cpu_baseline(p, args.cpu_token_heads)
+        res["cpu_baseline"] = (cpu_baseline_train(p, args.cpu_token_heads) if args.workload == "gqa_train"
+                               else cpu_baseline(p, args.cpu_token_heads))
     print(json.dumps(res), flush=True)
 
 

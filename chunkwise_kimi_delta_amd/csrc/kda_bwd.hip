@@ -44,22 +44,69 @@ template <> __device__ __forceinline__ float ldf<float>(const float* p) { return
 template <> __device__ __forceinline__ float ldf<bf16_t>(const bf16_t* p) { return bf2f(*p); }
 
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+// 2^x on the transcendental unit; every decay exponent here is <= 0
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float LOG2E_F = 1.4426950408889634f;
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
 
-// acc[a][b] += sum_{k < kr} A(tm + 16a, k) * B(k, tn + 16b): a 256-thread
-// register-blocked product, thread t = 16 tm + tn.
+// Workgroups of NTH threads (8 waves: two per SIMD, so that LDS and memory
+// latency is hidden while the other wave computes); thread t = 16 tm + tn owns
+// rows tm + RS a and columns tn + 16 b of a product.
+constexpr int NTH = 512, RS = NTH / 16;
+
+// acc[a][b] += sum_{k < kr} A(tm + RS a, k) * B(k, tn + 16 b): register-blocked.
 template <int MR, int NR, typename FA, typename FB>
 __device__ __forceinline__ void mm(float (&acc)[MR][NR], int kr, int tm, int tn, FA A, FB B) {
+#pragma unroll 4
   for (int k = 0; k < kr; ++k) {
     float a[MR], b[NR];
 #pragma unroll
-    for (int i = 0; i < MR; ++i) a[i] = A(tm + 16 * i, k);
+    for (int i = 0; i < MR; ++i) a[i] = A(tm + RS * i, k);
 #pragma unroll
     for (int j = 0; j < NR; ++j) b[j] = B(k, tn + 16 * j);
 #pragma unroll
     for (int i = 0; i < MR; ++i)
 #pragma unroll
       for (int j = 0; j < NR; ++j) acc[i][j] += a[i] * b[j];
+  }
+}
+// The same product with both operands read from global memory through an
+// LDS staging buffer, KB reduction indices at a time: every thread loads its
+// share of the A block (RS MR x KB) and the B block (KB x 16 NR) back to back,
+// consecutive threads on the operand's contiguous index (CKA / CKB: the source
+// is contiguous along the reduction index; else along rows of A / columns of B).
+template <int MR, int NR, int KB, bool CKA, bool CKB, int CAP, typename FA, typename FB>
+__device__ __forceinline__ void mm_staged(float (&acc)[MR][NR], int kr, int tid, FA A, FB B, float* stage) {
+  constexpr int M = RS * MR, N = 16 * NR, LA = KB + 1, LB = N + 1;
+  static_assert(M * LA + KB * LB <= CAP, "the staged blocks fit the staging buffer");
+  float* sa = stage;
+  float* sb = stage + M * LA;
+  const int tm = tid >> 4, tn = tid & 15;
+  for (int k0 = 0; k0 < kr; k0 += KB) {
+#pragma unroll
+    for (int e = tid; e < M * KB; e += NTH) {
+      const int m = CKA ? e / KB : e % M, kk = CKA ? e % KB : e / M;
+      sa[m * LA + kk] = A(m, k0 + kk);
+    }
+#pragma unroll
+    for (int e = tid; e < KB * N; e += NTH) {
+      const int n = CKB ? e / KB : e % N, kk = CKB ? e % KB : e / N;
+      sb[kk * LB + n] = B(k0 + kk, n);
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < KB; ++kk) {
+      float a[MR], b[NR];
+#pragma unroll
+      for (int i = 0; i < MR; ++i) a[i] = sa[(tm + RS * i) * LA + kk];
+#pragma unroll
+      for (int j = 0; j < NR; ++j) b[j] = sb[kk * LB + tn + 16 * j];
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int j = 0; j < NR; ++j) acc[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
   }
 }
 template <int MR, int NR>
@@ -92,7 +139,7 @@ __device__ __forceinline__ ChunkPos chunk_pos(const SeqInfo& s, int gc, int h, i
 
 // ------------------------------------------------------------------ prep
 template <int KD, int VD, typename IT>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
   constexpr int LK = KD + 1, LX = (KD > VD ? KD : VD) + 1;
   __shared__ float sG[BT * LK], sK[BT * LK], sX[BT * LX];
   __shared__ float sL[BT * 65], sA[BT * 65];
@@ -112,10 +159,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;
   const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
 
-  // rows r = tid / 4, channels 32 * (tid % 4) .. +31 (K = 128; K = 64: 16 each)
+  // rows r = tid / 8, channels CPT * (tid % 8) .. +CPT-1
   {
-    const int r = tid >> 2, part = tid & 3;
-    constexpr int CPT = KD / 4;
+    const int r = tid >> 3, part = tid & 7;
+    constexpr int CPT = KD / 8;
     const bool live = r < P.C;
     float kr[CPT], qr[CPT];
     float skk = 0.f, sqq = 0.f;
@@ -129,12 +176,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
       float gv = live ? ldf(g + ((P.tok0 + r) * a.Hv + h) * KD + c) : 0.f;
       if (live && gik) gv = -Aexp * softplus_f(gv + (a.dt_bias ? a.dt_bias[h * KD + c] : 0.f));
       if (live && gv < lb) gv = lb;
-      sG[r * LK + c] = gv;
+      sG[r * LK + c] = gv * LOG2E_F;          // log2 units
     }
-    skk += __shfl_xor(skk, 1);
-    skk += __shfl_xor(skk, 2);
-    sqq += __shfl_xor(sqq, 1);
-    sqq += __shfl_xor(sqq, 2);
+    for (int m = 1; m < 8; m <<= 1) {
+      skk += __shfl_xor(skk, m);
+      sqq += __shfl_xor(sqq, m);
+    }
     const float rk = live ? (l2 ? 1.f / sqrtf(skk + a.eps) : 1.f) : 0.f;
     const float rq = live ? (l2 ? 1.f / sqrtf(sqq + a.eps) : 1.f) : 0.f;
 #pragma unroll
@@ -150,7 +197,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // in-chunk cumsum of the decay (natural log); rows past the end keep the last value
+  // in-chunk cumsum of the decay (log2 units); rows past the end keep the last value
   if (tid < KD) {
     float run = 0.f;
     for (int r = 0; r < BT; ++r) {
@@ -160,7 +207,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   }
   __syncthreads();
   // store G, normalised k and q, beta
-  for (int i = tid; i < BT * KD; i += 256) {
+#pragma unroll 8
+  for (int i = tid; i < BT * KD; i += NTH) {
     const int r = i / KD, c = i % KD;
     rec[R.G + i] = sG[r * LK + c];
     rec[R.kn + i] = sK[r * LK + c];
@@ -168,14 +216,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   }
   if (tid < BT) rec[R.beta + tid] = sB[tid];
   // L (strict lower, beta-scaled) and Aqk (lower with diagonal, scaled): pair by pair
-  for (int p = tid; p < BT * (BT + 1) / 2; p += 256) {
+  for (int p = tid; p < BT * (BT + 1) / 2; p += NTH) {
     int i = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
     while (i * (i + 1) / 2 > p) --i;
     while ((i + 1) * (i + 2) / 2 <= p) ++i;
     const int j = p - i * (i + 1) / 2;
     float kd = 0.f, aq = 0.f;
     for (int c = 0; c < KD; ++c) {
-      const float f = expf(sG[i * LK + c] - sG[j * LK + c]);
+      const float f = ex2(sG[i * LK + c] - sG[j * LK + c]);
       const float kj = sK[j * LK + c] * f;
       kd += sK[i * LK + c] * kj;
       aq += sX[i * LX + c] * kj;
@@ -188,48 +236,56 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // A = (I + L)^-1 by forward substitution, one column per thread
-  if (tid < BT) {
-    const int j = tid;
+  // A = (I + L)^-1 by forward substitution: eight lanes per column (each sums
+  // every eighth term; the lanes of a column are adjacent in one wave, so the
+  // row just written is visible to them without a barrier)
+  {
+    const int j = tid >> 3, part = tid & 7;
     for (int i = 0; i < BT; ++i) {
-      float s = i == j ? 1.f : 0.f;
-      for (int m = j; m < i; ++m) s -= sL[i * 65 + m] * sA[m * 65 + j];
-      sA[i * 65 + j] = i >= j ? s : 0.f;
+      float s = 0.f;
+      for (int m = j + part; m < i; m += 8) s += sL[i * 65 + m] * sA[m * 65 + j];
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      if (part == 0) sA[i * 65 + j] = i > j ? -s : (i == j ? 1.f : 0.f);
     }
   }
   // beta v into sX (q is stored already)
   __syncthreads();
-  for (int i = tid; i < BT * VD; i += 256) {
+#pragma unroll 8
+  for (int i = tid; i < BT * VD; i += NTH) {
     const int r = i / VD, c = i % VD;
     sX[r * LX + c] = r < P.C ? sB[r] * ldf(v + ((P.tok0 + r) * a.Hv + h) * VD + c) : 0.f;
   }
-  for (int i = tid; i < BT * BT; i += 256) rec[R.A + i] = sA[(i / BT) * 65 + i % BT];
+#pragma unroll 8
+  for (int i = tid; i < BT * BT; i += NTH) rec[R.A + i] = sA[(i / BT) * 65 + i % BT];
   __syncthreads();
   {  // u = A (beta v)
-    float acc[4][VD / 16];
+    float acc[BT / RS][VD / 16];
     zero(acc);
     mm(acc, BT, tm, tn, [&](int i, int j) { return sA[i * 65 + j]; },
        [&](int j, int c) { return sX[j * LX + c]; });
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < BT / RS; ++x)
 #pragma unroll
-      for (int y = 0; y < VD / 16; ++y) rec[R.u + (tm + 16 * x) * VD + tn + 16 * y] = acc[x][y];
+      for (int y = 0; y < VD / 16; ++y) rec[R.u + (tm + RS * x) * VD + tn + 16 * y] = acc[x][y];
   }
   __syncthreads();
-  for (int i = tid; i < BT * KD; i += 256) {
+#pragma unroll 8
+  for (int i = tid; i < BT * KD; i += NTH) {
     const int r = i / KD, c = i % KD;
-    sX[r * LX + c] = sB[r] * sK[r * LK + c] * expf(sG[r * LK + c]);
+    sX[r * LX + c] = sB[r] * sK[r * LK + c] * ex2(sG[r * LK + c]);
   }
   __syncthreads();
   {  // w = A (beta k e^G)
-    float acc[4][KD / 16];
+    float acc[BT / RS][KD / 16];
     zero(acc);
     mm(acc, BT, tm, tn, [&](int i, int j) { return sA[i * 65 + j]; },
        [&](int j, int c) { return sX[j * LX + c]; });
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < BT / RS; ++x)
 #pragma unroll
-      for (int y = 0; y < KD / 16; ++y) rec[R.w + (tm + 16 * x) * KD + tn + 16 * y] = acc[x][y];
+      for (int y = 0; y < KD / 16; ++y) rec[R.w + (tm + RS * x) * KD + tn + 16 * y] = acc[x][y];
   }
 }
 
@@ -238,7 +294,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 // h <- D h + kg^T (u - w h), every entry state stored.  One workgroup per
 // (sequence, head, 32 columns).
 template <int KD, int VD>
-__global__ __launch_bounds__(256) void bwd_state_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTH) void bwd_state_kernel(BwdArgs a) {
   constexpr int TW = 32, LT = TW + 1, LK = KD + 1;
   __shared__ float sH[KD * LT], sVN[BT * LT], sW[BT * LK], sKG[BT * LK];
   __shared__ float sGC[KD];
@@ -251,7 +307,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdArgs a) {
   seq_range(a.seq, n, tok0s, len);
   const int nck = (len + BT - 1) / BT;
   const int cb = chunk_base(a.seq, n);
-  for (int i = tid; i < KD * TW; i += 256) {
+  for (int i = tid; i < KD * TW; i += NTH) {
     const int r = i / TW, c = i % TW;
     sH[r * LT + c] = a.h0 ? a.h0[(((int64_t)n * a.Hv + h) * KD + r) * VD + v0 + c] : 0.f;
   }
@@ -261,38 +317,40 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdArgs a) {
     const float* rec = a.rec + slot * (int64_t)(R.bytes / 4);
     const int C = min(BT, len - c * BT);
     float* dst = a.h_store_w + slot * (int64_t)(KD * VD);
-    for (int i = tid; i < KD * TW; i += 256) dst[(i / TW) * VD + v0 + i % TW] = sH[(i / TW) * LT + i % TW];
+#pragma unroll
+    for (int i = tid; i < KD * TW; i += NTH) dst[(i / TW) * VD + v0 + i % TW] = sH[(i / TW) * LT + i % TW];
     if (tid < KD) sGC[tid] = rec[R.G + (C - 1) * KD + tid];
     __syncthreads();
-    for (int i = tid; i < BT * KD; i += 256) {
+#pragma unroll 8
+    for (int i = tid; i < BT * KD; i += NTH) {
       const int r = i / KD, cc = i % KD;
       sW[r * LK + cc] = rec[R.w + i];
-      sKG[r * LK + cc] = rec[R.kn + i] * expf(sGC[cc] - rec[R.G + i]);
+      sKG[r * LK + cc] = rec[R.kn + i] * ex2(sGC[cc] - rec[R.G + i]);
     }
     __syncthreads();
     {  // v_new = u - w h
-      float acc[4][2];
+      float acc[BT / RS][2];
       zero(acc);
       mm(acc, KD, tm, tn, [&](int i, int kk) { return sW[i * LK + kk]; }, [&](int kk, int j) { return sH[kk * LT + j]; });
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < BT / RS; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) {
-          const int i = tm + 16 * x, j = tn + 16 * y;
+          const int i = tm + RS * x, j = tn + 16 * y;
           sVN[i * LT + j] = rec[R.u + i * VD + v0 + j] - acc[x][y];
         }
     }
     __syncthreads();
     {  // h = D h + kg^T v_new
-      float acc[KD / 16][2];
+      float acc[KD / RS][2];
       zero(acc);
       mm(acc, BT, tm, tn, [&](int kk, int r) { return sKG[r * LK + kk]; }, [&](int r, int j) { return sVN[r * LT + j]; });
 #pragma unroll
-      for (int x = 0; x < KD / 16; ++x)
+      for (int x = 0; x < KD / RS; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) {
-          const int kk = tm + 16 * x, j = tn + 16 * y;
-          sH[kk * LT + j] = expf(sGC[kk]) * sH[kk * LT + j] + acc[x][y];
+          const int kk = tm + RS * x, j = tn + 16 * y;
+          sH[kk * LT + j] = ex2(sGC[kk]) * sH[kk * LT + j] + acc[x][y];
         }
     }
     __syncthreads();
@@ -301,7 +359,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdArgs a) {
 
 // ------------------------------------------------------ reverse state scan
 template <int KD, int VD, typename IT>
-__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTH) void bwd_scan_kernel(BwdArgs a) {
   constexpr int TW = 32, LT = TW + 1, LK = KD + 1;
   __shared__ float sDH[KD * LT], sDo[BT * LT], sDV[BT * LT];
   __shared__ float sM1[BT * LK], sM2[BT * LK], sAq[BT * 65];
@@ -317,7 +375,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
   const int cb = chunk_base(a.seq, n);
   const IT* dout = static_cast<const IT*>(a.dout);
   // dh' of the last chunk: the final state's gradient
-  for (int i = tid; i < KD * TW; i += 256) {
+  for (int i = tid; i < KD * TW; i += NTH) {
     const int r = i / TW, c = i % TW;
     sDH[r * LT + c] = a.dht ? a.dht[(((int64_t)n * a.Hv + h) * KD + r) * VD + v0 + c] : 0.f;
   }
@@ -328,73 +386,81 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
     const int C = min(BT, len - c * BT);
     const int64_t tok0 = tok0s + (int64_t)c * BT;
     float* dst = a.dh_store + slot * (int64_t)(KD * VD);
-    for (int i = tid; i < KD * TW; i += 256) dst[(i / TW) * VD + v0 + i % TW] = sDH[(i / TW) * LT + i % TW];
+#pragma unroll
+    for (int i = tid; i < KD * TW; i += NTH) dst[(i / TW) * VD + v0 + i % TW] = sDH[(i / TW) * LT + i % TW];
     if (tid < KD) sGC[tid] = rec[R.G + (C - 1) * KD + tid];
     __syncthreads();
     // kg = k e^(G_C - G), Aqk, do
-    for (int i = tid; i < BT * KD; i += 256) {
+#pragma unroll 8
+    for (int i = tid; i < BT * KD; i += NTH) {
       const int r = i / KD, cc = i % KD;
-      sM1[r * LK + cc] = rec[R.kn + i] * expf(sGC[cc] - rec[R.G + i]);
+      sM1[r * LK + cc] = rec[R.kn + i] * ex2(sGC[cc] - rec[R.G + i]);
     }
-    for (int i = tid; i < BT * BT; i += 256) sAq[(i / BT) * 65 + i % BT] = rec[R.aqk + i];
-    for (int i = tid; i < BT * TW; i += 256) {
+#pragma unroll 8
+    for (int i = tid; i < BT * BT; i += NTH) sAq[(i / BT) * 65 + i % BT] = rec[R.aqk + i];
+#pragma unroll
+    for (int i = tid; i < BT * TW; i += NTH) {
       const int r = i / TW, cc = i % TW;
       sDo[r * LT + cc] = r < C ? ldf(dout + ((tok0 + r) * a.Hv + h) * VD + v0 + cc) : 0.f;
     }
     __syncthreads();
     {  // dv_new = Aqk^T do + kg dh'
-      float acc[4][2];
+      float acc[BT / RS][2];
       zero(acc);
       mm(acc, BT, tm, tn, [&](int i, int r) { return sAq[r * 65 + i]; }, [&](int r, int j) { return sDo[r * LT + j]; });
       mm(acc, KD, tm, tn, [&](int i, int kk) { return sM1[i * LK + kk]; }, [&](int kk, int j) { return sDH[kk * LT + j]; });
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < BT / RS; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) sDV[(tm + 16 * x) * LT + tn + 16 * y] = acc[x][y];
+        for (int y = 0; y < 2; ++y) sDV[(tm + RS * x) * LT + tn + 16 * y] = acc[x][y];
     }
     __syncthreads();
     // qg = s q e^G and w
-    for (int i = tid; i < BT * KD; i += 256) {
+#pragma unroll 8
+    for (int i = tid; i < BT * KD; i += NTH) {
       const int r = i / KD, cc = i % KD;
-      sM1[r * LK + cc] = a.scale * rec[R.qn + i] * expf(rec[R.G + i]);
+      sM1[r * LK + cc] = a.scale * rec[R.qn + i] * ex2(rec[R.G + i]);
       sM2[r * LK + cc] = rec[R.w + i];
     }
     __syncthreads();
     {  // dh = qg^T do + D dh' - w^T dv_new
-      float acc[KD / 16][2];
+      float acc[KD / RS][2];
       zero(acc);
       mm(acc, BT, tm, tn, [&](int kk, int r) { return sM1[r * LK + kk]; }, [&](int r, int j) { return sDo[r * LT + j]; });
 #pragma unroll
-      for (int x = 0; x < KD / 16; ++x)
+      for (int x = 0; x < KD / RS; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) acc[x][y] = -acc[x][y];
       mm(acc, BT, tm, tn, [&](int kk, int r) { return sM2[r * LK + kk]; }, [&](int r, int j) { return sDV[r * LT + j]; });
       __syncthreads();
 #pragma unroll
-      for (int x = 0; x < KD / 16; ++x)
+      for (int x = 0; x < KD / RS; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) {
-          const int kk = tm + 16 * x, j = tn + 16 * y;
-          sDH[kk * LT + j] = expf(sGC[kk]) * sDH[kk * LT + j] - acc[x][y];
+          const int kk = tm + RS * x, j = tn + 16 * y;
+          sDH[kk * LT + j] = ex2(sGC[kk]) * sDH[kk * LT + j] - acc[x][y];
         }
     }
     __syncthreads();
   }
   if (a.dh0)
-    for (int i = tid; i < KD * TW; i += 256)
+    for (int i = tid; i < KD * TW; i += NTH)
       a.dh0[(((int64_t)n * a.Hv + h) * KD + i / TW) * VD + v0 + i % TW] = sDH[(i / TW) * LT + i % TW];
 }
 
 // --------------------------------------------------------- chunk backward
 template <int KD, int VD, typename IT>
-__global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   static_assert(KD == 128 || KD == 64, "K");
   constexpr int LX = (KD > VD ? KD : VD) + 1;
-  constexpr int MRK = 4, NRK = KD / 16, NRV = VD / 16;
-  __shared__ float sB1[BT * LX], sB2[BT * LX], sB3[BT * LX];
+  constexpr int MRK = BT / RS, NRK = KD / 16, NRV = VD / 16;
+  // sB3 doubles as the staging buffer of the products (A block 64 x 33, B block 32 x (N + 1))
+  constexpr int STAGE = BT * 33 + 32 * ((KD > VD ? KD : VD) + 1);
+  constexpr int NB3 = BT * LX > STAGE ? BT * LX : STAGE;
+  __shared__ float sB1[BT * LX], sB2[BT * LX], sB3[NB3];
   __shared__ float sS1[BT * 65], sS2[BT * 65], sS3[BT * 65];
   __shared__ float sBeta[BT], sGC[KD];
-  static_assert(BT * 17 <= BT * 65 && 16 * KD <= BT * 65, "reduction buffers fit the small matrices");
+  static_assert(BT * 17 <= BT * 65 && RS * KD <= BT * 65, "reduction buffers fit the small matrices");
   float* sRed = sS1;    // (after the pair sums)
   float* sRedK = sS2;
   constexpr BwdRec R = bwd_rec(KD, VD);
@@ -415,7 +481,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   if (tid < KD) sGC[tid] = G[(P.C - 1) * KD + tid];
   __syncthreads();
 
-  // gradient accumulators of q, k and G, rows tm + 16x, channels tn + 16y
+  // gradient accumulators of q, k and G, rows tm + RS x, channels tn + 16 y
   float dq[MRK][NRK], dk[MRK][NRK], dG[MRK][NRK];
   zero(dq);
   zero(dk);
@@ -427,53 +493,60 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
   for (int y = 0; y < NRK; ++y) dGCp[y] = 0.f;
 
+  float* stage = sB3;   // staging buffer of the products until the pair sums
+  const float* wr = rec + R.w;
+  const float* aq = rec + R.aqk;
   {  // v_new = u - w h  -> B1
     float acc[MRK][NRV];
     zero(acc);
-    mm(acc, KD, tm, tn, [&](int i, int kk) { return rec[R.w + i * KD + kk]; },
-       [&](int kk, int j) { return hc[kk * VD + j]; });
+    mm_staged<MRK, NRV, 32, true, false, NB3>(acc, KD, tid, [&](int i, int kk) { return wr[i * KD + kk]; },
+                                         [&](int kk, int j) { return hc[kk * VD + j]; }, stage);
 #pragma unroll
     for (int x = 0; x < MRK; ++x)
 #pragma unroll
       for (int y = 0; y < NRV; ++y) {
-        const int i = tm + 16 * x, j = tn + 16 * y;
+        const int i = tm + RS * x, j = tn + 16 * y;
         sB1[i * LX + j] = rec[R.u + i * VD + j] - acc[x][y];
       }
   }
   {  // dv_new = Aqk^T do + kg dh'  -> B2
     float acc[MRK][NRV];
     zero(acc);
-    mm(acc, BT, tm, tn, [&](int i, int r) { return rec[R.aqk + r * BT + i]; }, [&](int r, int j) { return DO(r, j); });
-    mm(acc, KD, tm, tn, [&](int i, int kk) { return kn[i * KD + kk] * expf(sGC[kk] - G[i * KD + kk]); },
-       [&](int kk, int j) { return dh[kk * VD + j]; });
+    mm_staged<MRK, NRV, 32, false, false, NB3>(acc, BT, tid, [&](int i, int r) { return aq[r * BT + i]; },
+                                          [&](int r, int j) { return DO(r, j); }, stage);
+    mm_staged<MRK, NRV, 32, true, false, NB3>(
+        acc, KD, tid, [&](int i, int kk) { return kn[i * KD + kk] * ex2(sGC[kk] - G[i * KD + kk]); },
+        [&](int kk, int j) { return dh[kk * VD + j]; }, stage);
 #pragma unroll
     for (int x = 0; x < MRK; ++x)
 #pragma unroll
-      for (int y = 0; y < NRV; ++y) sB2[(tm + 16 * x) * LX + tn + 16 * y] = acc[x][y];
+      for (int y = 0; y < NRV; ++y) sB2[(tm + RS * x) * LX + tn + 16 * y] = acc[x][y];
   }
   __syncthreads();
   {  // dAqk = tril(do v_new^T)  -> S1
     float acc[MRK][4];
     zero(acc);
-    mm(acc, VD, tm, tn, [&](int i, int c) { return DO(i, c); }, [&](int c, int j) { return sB1[j * LX + c]; });
+    mm_staged<MRK, 4, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return DO(i, c); },
+                                      [&](int c, int j) { return sB1[j * LX + c]; }, stage);
 #pragma unroll
     for (int x = 0; x < MRK; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
-        const int i = tm + 16 * x, j = tn + 16 * y;
+        const int i = tm + RS * x, j = tn + 16 * y;
         sS1[i * 65 + j] = i >= j ? acc[x][y] : 0.f;
       }
   }
   {  // dqg = do h^T: q and G
     float acc[MRK][NRK];
     zero(acc);
-    mm(acc, VD, tm, tn, [&](int i, int c) { return DO(i, c); }, [&](int c, int kk) { return hc[kk * VD + c]; });
+    mm_staged<MRK, NRK, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return DO(i, c); },
+                                        [&](int c, int kk) { return hc[kk * VD + c]; }, stage);
 #pragma unroll
     for (int x = 0; x < MRK; ++x)
 #pragma unroll
       for (int y = 0; y < NRK; ++y) {
-        const int i = tm + 16 * x, kk = tn + 16 * y;
-        const float e = a.scale * expf(G[i * KD + kk]);
+        const int i = tm + RS * x, kk = tn + 16 * y;
+        const float e = a.scale * ex2(G[i * KD + kk]);
         dq[x][y] += e * acc[x][y];
         dG[x][y] += e * qn[i * KD + kk] * acc[x][y];
       }
@@ -481,31 +554,32 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   {  // dkg = v_new dh'^T: k, G and G_C
     float acc[MRK][NRK];
     zero(acc);
-    mm(acc, VD, tm, tn, [&](int i, int c) { return sB1[i * LX + c]; }, [&](int c, int kk) { return dh[kk * VD + c]; });
+    mm_staged<MRK, NRK, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB1[i * LX + c]; },
+                                        [&](int c, int kk) { return dh[kk * VD + c]; }, stage);
 #pragma unroll
     for (int x = 0; x < MRK; ++x)
 #pragma unroll
       for (int y = 0; y < NRK; ++y) {
-        const int i = tm + 16 * x, kk = tn + 16 * y;
-        const float e = expf(sGC[kk] - G[i * KD + kk]);
+        const int i = tm + RS * x, kk = tn + 16 * y;
+        const float e = ex2(sGC[kk] - G[i * KD + kk]);
         const float kgv = kn[i * KD + kk] * e;
         dk[x][y] += e * acc[x][y];
         dG[x][y] -= kgv * acc[x][y];
         dGCp[y] += kgv * acc[x][y];
       }
   }
-  __syncthreads();
   {  // dw = -dv_new h^T  -> B1 (v_new no longer needed)
     float acc[MRK][NRK];
     zero(acc);
-    mm(acc, VD, tm, tn, [&](int i, int c) { return sB2[i * LX + c]; }, [&](int c, int kk) { return hc[kk * VD + c]; });
-    __syncthreads();
+    mm_staged<MRK, NRK, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB2[i * LX + c]; },
+                                        [&](int c, int kk) { return hc[kk * VD + c]; }, stage);
 #pragma unroll
     for (int x = 0; x < MRK; ++x)
 #pragma unroll
-      for (int y = 0; y < NRK; ++y) sB1[(tm + 16 * x) * LX + tn + 16 * y] = -acc[x][y];
+      for (int y = 0; y < NRK; ++y) sB1[(tm + RS * x) * LX + tn + 16 * y] = -acc[x][y];
   }
-  for (int i = tid; i < BT * BT; i += 256) sS2[(i / BT) * 65 + i % BT] = rec[R.A + i];
+#pragma unroll 8
+  for (int i = tid; i < BT * BT; i += NTH) sS2[(i / BT) * 65 + i % BT] = rec[R.A + i];
   __syncthreads();
   {  // d(b k e^G) = A^T dw: k, b, G
     float acc[MRK][NRK];
@@ -515,8 +589,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     for (int x = 0; x < MRK; ++x)
 #pragma unroll
       for (int y = 0; y < NRK; ++y) {
-        const int j = tm + 16 * x, kk = tn + 16 * y;
-        const float e = expf(G[j * KD + kk]), X = kn[j * KD + kk] * e;
+        const int j = tm + RS * x, kk = tn + 16 * y;
+        const float e = ex2(G[j * KD + kk]), X = kn[j * KD + kk] * e;
         const float dX = sBeta[j] * acc[x][y];
         dbeta[x] += X * acc[x][y];
         dk[x][y] += e * dX;
@@ -529,7 +603,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     mm(acc, BT, tm, tn, [&](int j, int i) { return sS2[i * 65 + j]; }, [&](int i, int c) { return sB2[i * LX + c]; });
 #pragma unroll
     for (int x = 0; x < MRK; ++x) {
-      const int j = tm + 16 * x;
+      const int j = tm + RS * x;
 #pragma unroll
       for (int y = 0; y < NRV; ++y) {
         const int c = tn + 16 * y;
@@ -541,14 +615,16 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   {  // dA = tril(dv_new (b v)^T + dw (b k e^G)^T)  -> S3
     float acc[MRK][4];
     zero(acc);
-    mm(acc, VD, tm, tn, [&](int i, int c) { return sB2[i * LX + c]; }, [&](int c, int j) { return sBeta[j] * VV(j, c); });
-    mm(acc, KD, tm, tn, [&](int i, int c) { return sB1[i * LX + c]; },
-       [&](int c, int j) { return sBeta[j] * kn[j * KD + c] * expf(G[j * KD + c]); });
+    mm_staged<MRK, 4, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB2[i * LX + c]; },
+                                      [&](int c, int j) { return sBeta[j] * VV(j, c); }, stage);
+    mm_staged<MRK, 4, 32, true, true, NB3>(acc, KD, tid, [&](int i, int c) { return sB1[i * LX + c]; },
+                                      [&](int c, int j) { return sBeta[j] * kn[j * KD + c] * ex2(G[j * KD + c]); },
+                                      stage);
 #pragma unroll
     for (int x = 0; x < MRK; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
-        const int i = tm + 16 * x, j = tn + 16 * y;
+        const int i = tm + RS * x, j = tn + 16 * y;
         sS3[i * 65 + j] = i >= j ? acc[x][y] : 0.f;
       }
   }
@@ -561,7 +637,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int x = 0; x < MRK; ++x)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) sS3[(tm + 16 * x) * 65 + tn + 16 * y] = acc[x][y];
+      for (int y = 0; y < 4; ++y) sS3[(tm + RS * x) * 65 + tn + 16 * y] = acc[x][y];
     __syncthreads();
     zero(acc);
     mm(acc, BT, tm, tn, [&](int l, int i) { return sS2[i * 65 + l]; }, [&](int i, int m) { return sS3[i * 65 + m]; });
@@ -570,12 +646,13 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     for (int x = 0; x < MRK; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
-        const int l = tm + 16 * x, m = tn + 16 * y;
+        const int l = tm + RS * x, m = tn + 16 * y;
         sS3[l * 65 + m] = l > m ? -acc[x][y] : 0.f;
       }
   }
   // stage G, k, q for the pair sums
-  for (int i = tid; i < BT * KD; i += 256) {
+#pragma unroll 8
+  for (int i = tid; i < BT * KD; i += NTH) {
     const int r = i / KD, c = i % KD;
     sB1[r * LX + c] = G[i];
     sB2[r * LX + c] = kn[i];
@@ -585,14 +662,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   // pair sums, row side: row i gathers over its columns j
 #pragma unroll
   for (int x = 0; x < MRK; ++x) {
-    const int i = tm + 16 * x;
+    const int i = tm + RS * x;
 #pragma unroll
     for (int y = 0; y < NRK; ++y) {
       const int c = tn + 16 * y;
       const float gi = sB1[i * LX + c];
       float rL = 0.f, rA = 0.f;
       for (int j = 0; j <= i; ++j) {
-        const float kf = sB2[j * LX + c] * expf(gi - sB1[j * LX + c]);
+        const float kf = sB2[j * LX + c] * ex2(gi - sB1[j * LX + c]);
         rL += sS3[i * 65 + j] * kf;
         rA += sS1[i * 65 + j] * kf;
       }
@@ -606,14 +683,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   // column side: column j gathers over its rows i
 #pragma unroll
   for (int x = 0; x < MRK; ++x) {
-    const int j = tm + 16 * x;
+    const int j = tm + RS * x;
 #pragma unroll
     for (int y = 0; y < NRK; ++y) {
       const int c = tn + 16 * y;
       const float gj = sB1[j * LX + c];
       float cL = 0.f, cA = 0.f;
       for (int i = j; i < BT; ++i) {
-        const float f = expf(sB1[i * LX + c] - gj);
+        const float f = ex2(sB1[i * LX + c] - gj);
         cL += sS3[i * 65 + j] * sBeta[i] * sB2[i * LX + c] * f;
         cA += sS1[i * 65 + j] * sB3[i * LX + c] * f;
       }
@@ -625,7 +702,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   // reductions: dbeta over columns, dG_C over rows
   __syncthreads();
 #pragma unroll
-  for (int x = 0; x < MRK; ++x) sRed[(tm + 16 * x) * 17 + tn] = dbeta[x];
+  for (int x = 0; x < MRK; ++x) sRed[(tm + RS * x) * 17 + tn] = dbeta[x];
 #pragma unroll
   for (int y = 0; y < NRK; ++y) sRedK[tm * KD + tn + 16 * y] = dGCp[y];
   __syncthreads();
@@ -636,16 +713,16 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   }
   if (tid < KD) {
     float s = 0.f;
-    for (int t = 0; t < 16; ++t) s += sRedK[t * KD + tid];
+    for (int t = 0; t < RS; ++t) s += sRedK[t * KD + tid];
     float dd = 0.f;   // dD = rowsum(h . dh')
     for (int c = 0; c < VD; ++c) dd += hc[tid * VD + c] * dh[tid * VD + c];
-    sGC[tid] = s + expf(sGC[tid]) * dd;   // dG_C
+    sGC[tid] = s + ex2(sGC[tid]) * dd;   // dG_C
   }
   // dG -> dg: reverse cumsum over the chunk's rows plus dG_C
 #pragma unroll
   for (int x = 0; x < MRK; ++x)
 #pragma unroll
-    for (int y = 0; y < NRK; ++y) sB1[(tm + 16 * x) * LX + tn + 16 * y] = dG[x][y];
+    for (int y = 0; y < NRK; ++y) sB1[(tm + RS * x) * LX + tn + 16 * y] = dG[x][y];
   __syncthreads();
   if (tid < KD) {
     float run = sGC[tid];
@@ -656,7 +733,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int x = 0; x < MRK; ++x) {
-    const int i = tm + 16 * x;
+    const int i = tm + RS * x;
     if (i >= P.C) continue;
 #pragma unroll
     for (int y = 0; y < NRK; ++y) {
@@ -785,14 +862,14 @@ hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int6
 #define KDA_BWD_CASE(KK, VV, TT)                                                                        \
   if (K == KK && V == VV) {                                                                             \
     switch (stage) {                                                                                    \
-      case 0: return nb_chunk ? launch(bwd_prep_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(256), s, a) : hipSuccess; \
-      case 1: return nb_scan ? launch(bwd_scan_kernel<KK, VV, TT>, dim3(nb_scan), dim3(256), s, a) : hipSuccess;   \
-      case 2: return nb_chunk ? launch(bwd_chunk_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(256), s, a) : hipSuccess; \
+      case 0: return nb_chunk ? launch(bwd_prep_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
+      case 1: return nb_scan ? launch(bwd_scan_kernel<KK, VV, TT>, dim3(nb_scan), dim3(NTH), s, a) : hipSuccess;   \
+      case 2: return nb_chunk ? launch(bwd_chunk_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
       case 3: return nb_qk ? launch(bwd_qk_kernel<KK, TT>, dim3(nb_qk), dim3(64), s, a, tokens) : hipSuccess;       \
       case 4: return nblk ? launch(bwd_gate_kernel<KK, TT>, dim3(nblk * a.Hv), dim3(KK), s, a, tokens, part)        \
                           : hipSuccess;                                                                 \
       case 5: return launch(bwd_gate_sum_kernel<KK>, dim3(a.Hv), dim3(KK), s, a, nblk, (const float*)part);       \
-      case 6: return nb_scan ? launch(bwd_state_kernel<KK, VV>, dim3(nb_scan), dim3(256), s, a) : hipSuccess;       \
+      case 6: return nb_scan ? launch(bwd_state_kernel<KK, VV>, dim3(nb_scan), dim3(NTH), s, a) : hipSuccess;       \
     }                                                                                                   \
     return hipErrorInvalidValue;                                                                        \
   }
