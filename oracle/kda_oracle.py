@@ -415,3 +415,31 @@ def backward(p, do, dht=None, heads: Optional[Sequence[int]] = None):
             tgt("dbeta")[t0:t1, h] = dbraw[:, j]
         out["dh0"][n][hs] = dS0
     return out
+
+
+def segment_summary_bwd(p, do, heads: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Backward summary of each sequence: ``local`` [N, Hv, K, V], the gradient
+    of sum(do * o) with respect to the sequence's initial state when nothing
+    flows in from its final state.  The state gradient's recursion does not
+    involve the states themselves, so the full gradient with respect to the
+    initial state is affine in the final state's gradient dS_T:
+        dS_0 = M^T dS_T + local,
+    with M the forward summary's transition ("Hyper-Parallel Chunk KDA",
+    sections 5.2 and 6.4: the backward pre-process and the reverse merge;
+    "KDA Chunk Backward — TPU/Pallas Kernel Design", section 2.4)."""
+    return backward(p, do, None, heads=heads)["dh0"]
+
+
+def summary_merge_bwd(M: np.ndarray, local: np.ndarray, dstate: Optional[np.ndarray] = None
+                      ) -> np.ndarray:
+    """Reverse merge: S <- M_j^T S + local_j for j = P-1 down to 0, from the
+    gradient of the last segment's final state (zero if None); the result is
+    the gradient with respect to the first segment's initial state, and each
+    intermediate value is the gradient a preceding segment receives for its
+    final state (M [P,H,K,K], local [P,H,K,V])."""
+    M = np.asarray(M, F64)
+    local = np.asarray(local, F64)
+    S = np.zeros(local.shape[1:], F64) if dstate is None else np.array(dstate, F64)
+    for j in reversed(range(M.shape[0])):
+        S = np.matmul(np.swapaxes(M[j], -1, -2), S) + local[j]
+    return S

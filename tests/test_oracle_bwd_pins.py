@@ -124,3 +124,54 @@ def test_backward_head_subset_equals_slice():
     # and 1 share q/k head 0, so the two partial runs add up to the full one
     np.testing.assert_allclose(part["dq"][..., 0, :] + orc.backward(p, do, dht, heads=[0])["dq"][..., 0, :],
                                full["dq"][..., 0, :], rtol=1e-12, atol=1e-13)
+
+
+def test_initial_state_gradient_is_affine_in_the_final_one():
+    """dS_0 = M^T dS_T + local, with M the forward summary's transition: the
+    backward's state gradient is the forward transition transposed."""
+    p = _problem("bsnd", seed=64)
+    p = SimpleNamespace(**{**vars(p), "B": 1, "q": p.q[:1], "k": p.k[:1], "v": p.v[:1], "g": p.g[:1],
+                           "beta": p.beta[:1], "h0": p.h0[:1]})
+    r = RNG(65)
+    do = r.standard_normal(p.v.shape)
+    dht = r.standard_normal(p.h0.shape)
+    M, _ = orc.segment_summary(p)
+    local = orc.segment_summary_bwd(p, do)
+    full = orc.backward(p, do, dht)["dh0"]
+    np.testing.assert_allclose(full[0], np.matmul(np.swapaxes(M[0], -1, -2), dht[0]) + local[0],
+                               rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("cuts", [[4], [2, 7], [1, 3, 6]])
+def test_reverse_merge_of_split_summaries_equals_full_backward(cuts):
+    """A sequence cut into segments: the reverse merge of the segments'
+    (M, local) from dS_T equals the full backward's dS_0, and its intermediate
+    values equal the full backward's gradient at each cut (the backward's
+    composition order is the reverse of the forward's)."""
+    p = _problem("bsnd", seed=66)
+    p = SimpleNamespace(**{**vars(p), "B": 1, "q": p.q[:1], "k": p.k[:1], "v": p.v[:1], "g": p.g[:1],
+                           "beta": p.beta[:1], "h0": p.h0[:1]})
+    r = RNG(67)
+    do = r.standard_normal(p.v.shape)
+    dht = r.standard_normal(p.h0.shape)
+    bounds = [0] + cuts + [p.T]
+    Ms, locs = [], []
+    for t0, t1 in zip(bounds[:-1], bounds[1:]):
+        seg = SimpleNamespace(**{**vars(p), "T": t1 - t0, "q": p.q[:, t0:t1], "k": p.k[:, t0:t1],
+                                 "v": p.v[:, t0:t1], "g": p.g[:, t0:t1], "beta": p.beta[:, t0:t1]})
+        Ms.append(orc.segment_summary(seg)[0][0])
+        locs.append(orc.segment_summary_bwd(seg, do[:, t0:t1])[0])
+    full = orc.backward(p, do, dht)["dh0"][0]
+    np.testing.assert_allclose(orc.summary_merge_bwd(np.stack(Ms), np.stack(locs), dht[0]), full,
+                               rtol=1e-10, atol=1e-11)
+    # gradient arriving at the first cut = backward of the tail from dht
+    tail = SimpleNamespace(**{**vars(p), "T": p.T - cuts[0], "q": p.q[:, cuts[0]:], "k": p.k[:, cuts[0]:],
+                              "v": p.v[:, cuts[0]:], "g": p.g[:, cuts[0]:], "beta": p.beta[:, cuts[0]:]})
+    at_cut = orc.backward(tail, do[:, cuts[0]:], dht)["dh0"][0]
+    np.testing.assert_allclose(orc.summary_merge_bwd(np.stack(Ms[1:]), np.stack(locs[1:]), dht[0]), at_cut,
+                               rtol=1e-10, atol=1e-11)
+    # the forward order gives something else
+    S = dht[0].copy()
+    for j in range(len(Ms)):
+        S = np.matmul(np.swapaxes(Ms[j], -1, -2), S) + locs[j]
+    assert np.abs(S - full).max() > 1e-3
