@@ -476,6 +476,77 @@ kda_status_t kda_chunk_bwd(const kda_problem_t* p, const void* q, const void* k,
   return ok();
 }
 
+kda_status_t kda_segment_summary_bwd_workspace_size(const kda_problem_t* p, size_t* bytes) {
+  if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  BwdPlan bp;
+  kda_status_t st = plan_bwd(p, bp);
+  if (st != KDA_OK) return st;
+  *bytes = bp.off_h;     // the chunk map and the backward records
+  return ok();
+}
+
+kda_status_t kda_segment_summary_bwd(const kda_problem_t* p, const void* q, const void* k, const void* v,
+                                     const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                                     const int32_t* cu_seqlens, const void* dout, float* local, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  BwdPlan bp;
+  kda_status_t st = plan_bwd(p, bp);
+  if (st != KDA_OK) return st;
+  const Plan& pl = bp.fwd;
+  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, cu_seqlens)) != KDA_OK) return st;
+  if (pl.tokens > 0) {
+    if ((st = check_token_ptr(q, "q", 16)) != KDA_OK) return st;
+    if ((st = check_token_ptr(dout, "do", 16)) != KDA_OK) return st;
+  }
+  if (pl.N > 0 && (!local || !aligned(local, 4)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "local is NULL or misaligned");
+  if (workspace_bytes < bp.off_h)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, bp.off_h);
+  if (bp.off_h && !workspace) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (pl.N == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  kda::SeqInfo si = seq_info(p, pl, cu_seqlens, ws);
+  if (si.tnd) {
+    if ((st = hip_status(kda::launch_chunk_offsets(cu_seqlens, pl.N, reinterpret_cast<int32_t*>(ws + pl.off_chunk), s),
+                         "chunk offsets launch")) != KDA_OK)
+      return st;
+  }
+  kda::BwdArgs a{};
+  a.seq = si;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.dout = dout;
+  a.A_log = A_log; a.dt_bias = dt_bias; a.dht = nullptr;
+  a.Hk = p->Hk; a.Hv = p->Hv; a.nchunks = (int)pl.nchunks;
+  a.flags = p->flags; a.scale = p->scale; a.eps = p->eps; a.lower_bound = p->lower_bound;
+  a.rec = reinterpret_cast<float*>(ws + bp.off_rec);
+  a.dh_store = nullptr;
+  a.dh0 = local;
+  if ((st = hip_status(kda::launch_bwd(p->K, p->V, p->dtype, a, 0, bp.tokens, nullptr, s), "backward prep launch")) != KDA_OK)
+    return st;
+  if ((st = hip_status(kda::launch_bwd(p->K, p->V, p->dtype, a, 1, bp.tokens, nullptr, s),
+                       "backward reverse scan launch")) != KDA_OK)
+    return st;
+  return ok();
+}
+
+kda_status_t kda_summary_merge_bwd(int32_t P, int32_t Hv, int32_t K, int32_t V, const float* M,
+                                   const float* local, float* state, void* stream) {
+  if (P < 0 || Hv < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "need P >= 0 and Hv >= 1 (P=%d Hv=%d)", P, Hv);
+  if ((K != 64 && K != 128) || (V != 64 && V != 128))
+    return fail(KDA_ERR_UNSUPPORTED, "head dims K=%d V=%d: each must be 64 or 128", K, V);
+  if ((int64_t)Hv * (V / 32) > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many heads");
+  if (!state || !aligned(state, 16)) return fail(KDA_ERR_INVALID_ARGUMENT, "state is NULL or misaligned");
+  if (P == 0) return ok();
+  if (!M || !local || !aligned(M, 16) || !aligned(local, 16))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "M and local must be non-NULL and 16-byte aligned");
+  kda::MergeArgs a{P, Hv, M, local, state};
+  kda_status_t st = hip_status(kda::launch_merge(K, V, a, static_cast<hipStream_t>(stream), true),
+                               "reverse merge kernel launch");
+  if (st != KDA_OK) return st;
+  return ok();
+}
+
 kda_status_t kda_chunk_fwd_noalloc(const kda_problem_t* p, const void* q, const void* k, const void* v,
                                    const void* g, const void* beta, const float* A_log, const float* dt_bias,
                                    const float* initial_state, const int32_t* cu_seqlens,

@@ -385,9 +385,11 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(BwdArgs a) {
     const float* rec = a.rec + slot * (int64_t)(R.bytes / 4);
     const int C = min(BT, len - c * BT);
     const int64_t tok0 = tok0s + (int64_t)c * BT;
-    float* dst = a.dh_store + slot * (int64_t)(KD * VD);
+    if (a.dh_store) {   // (the backward summary keeps none)
+      float* dst = a.dh_store + slot * (int64_t)(KD * VD);
 #pragma unroll
-    for (int i = tid; i < KD * TW; i += NTH) dst[(i / TW) * VD + v0 + i % TW] = sDH[(i / TW) * LT + i % TW];
+      for (int i = tid; i < KD * TW; i += NTH) dst[(i / TW) * VD + v0 + i % TW] = sDH[(i / TW) * LT + i % TW];
+    }
     if (tid < KD) sGC[tid] = rec[R.G + (C - 1) * KD + tid];
     __syncthreads();
     // kg = k e^(G_C - G), Aqk, do

@@ -10,7 +10,7 @@ namespace kda {
 hipError_t launch_chunk_offsets(const int32_t*, int, int32_t*, hipStream_t) { return hipSuccess; }
 hipError_t launch_intra(int, int, int, const IntraArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_scan(int, int, int, const ScanArgs&, hipStream_t) { return hipSuccess; }
-hipError_t launch_merge(int, int, const MergeArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_merge(int, int, const MergeArgs&, hipStream_t, bool) { return hipSuccess; }
 hipError_t launch_prefix_merge(int, int, const PrefixMergeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_recurrent(int, int, int, const RecurrentArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd(int, int, int, const BwdArgs&, int, int64_t, float*, hipStream_t) { return hipSuccess; }

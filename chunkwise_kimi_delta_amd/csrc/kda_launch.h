@@ -167,7 +167,7 @@ struct BwdArgs {
   const float* h0;            // [N][Hv][K][V] or null (zero)
   const float* h_store;       // [Hv * nchunks][K][V] chunk-entry states
   float* h_store_w;           // the same buffer, written by the state kernel
-  float* dh_store;            // [Hv * nchunks][K][V] gradients of the chunk-exit states
+  float* dh_store;            // [Hv * nchunks][K][V] gradients of the chunk-exit states (or null)
   float* dh0;                 // [N][Hv][K][V] or null
   float *dqn, *dkn;           // [tokens][Hv][K]: per value head, w.r.t. normalised q / k
   float *dbeta_act, *dg_nat;  // [tokens][Hv] w.r.t. activated beta, [tokens][Hv][K] w.r.t. the decay
@@ -180,7 +180,7 @@ struct BwdArgs {
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);
 hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t s);
 hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s);
-hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s);
+hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s, bool backward = false);
 hipError_t launch_prefix_merge(int K, int V, const PrefixMergeArgs& a, hipStream_t s);
 hipError_t launch_recurrent(int K, int V, int dtype, const RecurrentArgs& a, hipStream_t s);
 // Backward stage: 0 prep, 6 forward state scan (fp32), 1 reverse state scan,

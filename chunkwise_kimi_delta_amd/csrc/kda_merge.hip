@@ -9,7 +9,10 @@ namespace kda {
 
 namespace {
 
-template <int KD, int VD>
+// BWD: the reverse merge of the backward, state <- M_j^T state + S_j for
+// j = P-1 down to 0 ("Hyper-Parallel Chunk KDA" section 6.4; "KDA Chunk
+// Backward — TPU/Pallas Kernel Design" section 2.4): M_j is staged transposed.
+template <int KD, int VD, bool BWD>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int BVm = 32, PS = BVm + 4, PM = KD + 4;
   constexpr int RPT = KD * BVm / 256;            // outputs per thread
@@ -20,12 +23,18 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int col = tid % BVm, rg = tid / BVm;     // rows rg, rg + 8, ...
   float* st = a.state + (int64_t)h * KD * VD;
   for (int i = tid; i < KD * BVm; i += 256) sS[(i / BVm) * PS + i % BVm] = st[(i / BVm) * VD + v0 + i % BVm];
-  for (int j = 0; j < a.P; ++j) {
+  for (int jj = 0; jj < a.P; ++jj) {
+    const int j = BWD ? a.P - 1 - jj : jj;
     const float* Mj = a.M + ((int64_t)j * a.Hv + h) * KD * KD;
     const float* Sj = a.S + ((int64_t)j * a.Hv + h) * KD * VD;
     for (int i = tid * 4; i < KD * KD; i += 256 * 4) {
       f32x4 x = *reinterpret_cast<const f32x4*>(Mj + i);
-      *reinterpret_cast<f32x4*>(sM + (i / KD) * PM + i % KD) = x;
+      if (BWD) {   // row r of M^T is column r of M
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sM[((i + e) % KD) * PM + (i + e) / KD] = x[e];
+      } else {
+        *reinterpret_cast<f32x4*>(sM + (i / KD) * PM + i % KD) = x;
+      }
     }
     __syncthreads();
     float acc[RPT];
@@ -127,11 +136,12 @@ hipError_t launch_prefix_merge(int K, int V, const PrefixMergeArgs& a, hipStream
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s) {
+hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s, bool backward) {
   if (a.P == 0 || a.Hv == 0) return hipSuccess;
-#define KDA_MERGE_CASE(KK, VV)                                                          \
-  if (K == KK && V == VV) {                                                             \
-    return launch(merge_kernel<KK, VV>, dim3(a.Hv * (VV / 32)), dim3(256), s, a);     \
+#define KDA_MERGE_CASE(KK, VV)                                                                       \
+  if (K == KK && V == VV) {                                                                          \
+    return backward ? launch(merge_kernel<KK, VV, true>, dim3(a.Hv * (VV / 32)), dim3(256), s, a)    \
+                    : launch(merge_kernel<KK, VV, false>, dim3(a.Hv * (VV / 32)), dim3(256), s, a);  \
   }
   KDA_MERGE_CASE(128, 128)
   KDA_MERGE_CASE(64, 64)

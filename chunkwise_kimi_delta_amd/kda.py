@@ -45,6 +45,7 @@ class KdaProblem(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
+           "kda_segment_summary_bwd_workspace_size", "kda_segment_summary_bwd", "kda_summary_merge_bwd",
            "kda_segment_summary_workspace_size",
            "kda_segment_summary", "kda_summary_merge", "kda_recurrent_fwd", "kda_chunk_fwd_noalloc",
            "kda_chunk_offsets_host",
@@ -71,6 +72,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd_noalloc.argtypes = [P] + [VP] * 12 + [VP]
     lib.kda_chunk_bwd_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.kda_chunk_bwd.argtypes = [P] + [VP] * 20 + [SZ, VP]
+    lib.kda_segment_summary_bwd_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
+    lib.kda_segment_summary_bwd.argtypes = [P] + [VP] * 11 + [SZ, VP]
+    lib.kda_summary_merge_bwd.argtypes = [I32, I32, I32, I32, VP, VP, VP, VP]
     lib.kda_chunk_offsets_host.argtypes = [VP, I32, I32, VP]
     lib.kda_status_string.argtypes = [I32]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -79,7 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_abi_version.argtypes = []
     lib.kda_abi_version.restype = I32
     for name in ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_bwd_workspace_size",
-                 "kda_chunk_bwd", "kda_segment_summary_workspace_size",
+                 "kda_chunk_bwd", "kda_segment_summary_bwd_workspace_size", "kda_segment_summary_bwd",
+                 "kda_summary_merge_bwd", "kda_segment_summary_workspace_size",
                  "kda_segment_summary", "kda_summary_merge", "kda_recurrent_fwd", "kda_chunk_fwd_noalloc",
                  "kda_chunk_offsets_host"):
         getattr(lib, name).restype = I32
@@ -351,6 +356,53 @@ def kda_chunk_bwd(q, k, v, g, beta, do, *, dht=None, scale: Optional[float] = No
                              _ptr(out["dbeta"]), _ptr(out.get("dA_log")), _ptr(out.get("ddt_bias")),
                              _ptr(out.get("dh0")), _ptr(workspace), workspace.numel(), _stream(dev)))
     return out
+
+
+def kda_segment_summary_bwd(q, k, v, g, beta, do, *, scale: Optional[float] = None, A_log=None,
+                            dt_bias=None, cu_seqlens=None, cu_seqlens_host=None,
+                            gate_in_kernel: bool = False, safe_gate: bool = False, lower_bound: float = -5.0,
+                            qk_l2norm: bool = False, beta_sigmoid: bool = False, eps: float = 1e-6,
+                            local=None, workspace=None) -> torch.Tensor:
+    """Backward summary: the gradient of sum(do * o) with respect to each
+    sequence's initial state when nothing flows in from its final state
+    (fp32 [N,Hv,K,V])."""
+    lib = load()
+    p, dev, cu_d, _, _, _ = _forward_args(
+        q, k, v, g, beta, scale=scale, A_log=A_log, dt_bias=dt_bias, initial_state=None,
+        cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, state_indices=None,
+        output_final_state=False, gate_in_kernel=gate_in_kernel, safe_gate=safe_gate,
+        lower_bound=lower_bound, qk_l2norm=qk_l2norm, beta_sigmoid=beta_sigmoid, eps=eps, o=None,
+        final_state=None, alloc_o=False)
+    N, Hv, K, V = p.num_seqs, v.shape[-2], q.shape[-1], v.shape[-1]
+    _need(do, "do", v.dtype, v.shape, dev)
+    _need(local, "local", torch.float32, (N, Hv, K, V), dev)
+    if local is None:
+        local = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev)
+    ws_bytes = ctypes.c_size_t()
+    _check(lib.kda_segment_summary_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes.value, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    _check(lib.kda_segment_summary_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(A_log), _ptr(dt_bias), _ptr(cu_d), _ptr(do), _ptr(local),
+                                       _ptr(workspace), workspace.numel(), _stream(dev)))
+    return local
+
+
+def kda_summary_merge_bwd(M: torch.Tensor, local: torch.Tensor, state: torch.Tensor) -> torch.Tensor:
+    """In place: state <- M[j]^T state + local[j] for j from the last to the first.  Returns ``state``."""
+    lib = load()
+    if state.dim() != 3 or local.dim() != 4:
+        raise ValueError("state is [Hv,K,V] and local [P,Hv,K,V]")
+    Hv, K, V = state.shape
+    P = local.shape[0]
+    _need(local, "local", torch.float32, (P, Hv, K, V))
+    _need(M, "M", torch.float32, (P, Hv, K, K))
+    dev = _gpu_device(state)
+    for t, n in ((M, "M"), (local, "local"), (state, "state")):
+        _need(t, n, torch.float32, device=dev)
+    _check(lib.kda_summary_merge_bwd(P, Hv, K, V, _ptr(M), _ptr(local), _ptr(state), _stream(state.device)))
+    return state
 
 
 def kda_recurrent_fwd(q, k, v, g, beta, *, scale: Optional[float] = None, A_log=None, dt_bias=None,

@@ -177,6 +177,45 @@ kda_status_t kda_chunk_bwd(const kda_problem_t* p,
                            float* dA_log, float* ddt_bias, float* dh0,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace kda_segment_summary_bwd needs for this problem. */
+kda_status_t kda_segment_summary_bwd_workspace_size(const kda_problem_t* p, size_t* bytes);
+
+/*
+ * Backward summary of each sequence ("Hyper-Parallel Chunk KDA" sections 5.2
+ * and 6.4, the backward pre-process; "KDA Chunk Backward — TPU/Pallas Kernel
+ * Design" section 2.4): local[n] = the gradient of sum(do * o) over sequence n
+ * with respect to its initial state when no gradient flows in from its final
+ * state.  The state gradient's recursion does not involve the states, so for
+ * any gradient dS_T of the final state the initial state's gradient is
+ *     M[n]^T dS_T + local[n]
+ * with M the forward summary's transition (kda_segment_summary).  Sequence
+ * parallelism: each segment computes its (M, local) independently, then
+ * kda_summary_merge_bwd hands each segment the gradient of its final state.
+ *  q ... cu_seqlens : as in kda_chunk_fwd (p->state_rows must be 0; no state).
+ *  dout  : dL/do, [.., Hv, V] in p->dtype.   local : fp32 [N,Hv,K,V] output.
+ */
+kda_status_t kda_segment_summary_bwd(const kda_problem_t* p,
+                                     const void* q, const void* k, const void* v,
+                                     const void* g, const void* beta,
+                                     const float* A_log, const float* dt_bias,
+                                     const int32_t* cu_seqlens, const void* dout,
+                                     float* local, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/*
+ * Reverse merge of backward summaries ("Hyper-Parallel Chunk KDA" section 6.4;
+ * "KDA Chunk Backward — TPU/Pallas Kernel Design" section 2.4), in place on
+ * state [Hv,K,V] (fp32), in reverse time order:
+ *     for j = P-1 down to 0:  state <- M[j]^T state + local[j]
+ * with M fp32 [P,Hv,K,K] (the forward summaries' transitions) and local fp32
+ * [P,Hv,K,V].  Start from the gradient of the last segment's final state
+ * (zero if none); after the step for segment j the state is the gradient of
+ * segment j-1's final state.  P = 0 launches nothing.
+ */
+kda_status_t kda_summary_merge_bwd(int32_t P, int32_t Hv, int32_t K, int32_t V,
+                                   const float* M, const float* local, float* state,
+                                   void* stream);
+
 /* Bytes of the fixed device scratch behind kda_chunk_fwd_noalloc (64 MiB). */
 #define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
 

@@ -151,3 +151,74 @@ def test_bwd_gqa_full_size_sampled(gpu_lib):
     for n in ("dv", "dg", "dbeta"):
         check(n, np64(got[n])[0][:, :4], ref[n][0][:, :4])
     check("dh0", np64(got["dh0"])[0, :4], ref["dh0"][0, :4])
+
+
+# ------------------------------------- backward summary and reverse merge
+def _slow(T, H=2, seed=0):
+    p = ks.make("layer", T=T, H=H)
+    p.A_log = np.log(np.array([1e-3, 3e-3, 2e-3, 5e-4][:H], dtype=np.float32))
+    p.dt_bias = np.full_like(p.dt_bias, -4.0)
+    return p
+
+
+def _gpu_local(kda, p, do, t=None):
+    t = t or to_torch(p)
+    dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+    loc = kda.kda_segment_summary_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                      torch.from_numpy(do).to("cuda", dt), scale=p.scale, A_log=t["A_log"],
+                                      dt_bias=t["dt_bias"], cu_seqlens=t["cu"], cu_seqlens_host=t["cu_host"],
+                                      **flag_kwargs(p))
+    torch.cuda.synchronize()
+    return loc
+
+
+@pytest.mark.parametrize("name", ["layer", "slow", "varlen"])
+def test_bwd_summary_matches_oracle(gpu_lib, name):
+    if name == "slow":
+        p = _slow(300)
+    elif name == "varlen":
+        p = dataclasses.replace(ks.make("varlen", lens=[70, 0, 130], H=2, cache_rows=3, n_invalid=0),
+                                state_indices=None, h0=None)
+    else:
+        p = ks.make("layer", T=300, H=2)
+    do, _ = cotangents(p)
+    loc = _gpu_local(gpu_lib, p, do)
+    check("local", np64(loc), orc.segment_summary_bwd(p, do))
+
+
+def test_reverse_merge_matches_oracle(gpu_lib):
+    rng = np.random.default_rng(9)
+    P, H, K, V = 5, 3, 128, 128
+    M = (rng.standard_normal((P, H, K, K)) / np.sqrt(K)).astype(np.float32)
+    L = (rng.standard_normal((P, H, K, V)) * 0.02).astype(np.float32)
+    X = (rng.standard_normal((H, K, V)) * 0.02).astype(np.float32)
+    st = torch.from_numpy(X.copy()).cuda()
+    gpu_lib.kda_summary_merge_bwd(torch.from_numpy(M).cuda(), torch.from_numpy(L).cuda(), st)
+    torch.cuda.synchronize()
+    check("reverse merged", np64(st), orc.summary_merge_bwd(M, L, X), 1e-5)
+
+
+def test_segment_chain_backward_equals_full_backward(gpu_lib):
+    """A 960-token sequence (slow decay) cut into three segments: the forward
+    summaries' M and the backward summaries' local, reverse-merged from dht,
+    give the full backward's dh0 (GPU and oracle)."""
+    p = _slow(960)
+    do, dht = cotangents(p)
+    full = gpu_bwd(gpu_lib, p, do, dht)["dh0"]
+    ref = orc.backward(p, do, dht)["dh0"]
+    cuts = [0, 320, 704, 960]
+    Ms, locs = [], []
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        seg = dataclasses.replace(p, T=t1 - t0, q=p.q[:, t0:t1], k=p.k[:, t0:t1], v=p.v[:, t0:t1],
+                                  g=p.g[:, t0:t1], beta=p.beta[:, t0:t1], h0=None)
+        ts = to_torch(seg)
+        M, _ = gpu_lib.kda_segment_summary(ts["k"], ts["v"], ts["g"], ts["beta"], A_log=ts["A_log"],
+                                           dt_bias=ts["dt_bias"], **flag_kwargs(seg))
+        Ms.append(M[0])
+        locs.append(_gpu_local(gpu_lib, seg, do[:, t0:t1], ts)[0])
+    state = torch.from_numpy(dht[0]).cuda()
+    gpu_lib.kda_summary_merge_bwd(torch.stack(Ms), torch.stack(locs), state)
+    torch.cuda.synchronize()
+    say(f"  max|M| = {float(torch.stack(Ms).abs().max()):.3f}")
+    check("merged vs oracle dh0", np64(state), ref[0])
+    check("merged vs full GPU backward", np64(state), np64(full)[0])
