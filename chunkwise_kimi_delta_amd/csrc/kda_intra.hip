@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
   constexpr int UB = BOP_BYTES > VX_BYTES ? BOP_BYTES : VX_BYTES;
 
   __shared__ __attribute__((aligned(16))) float sTot[4][KD];   // per-wave gate totals
-  __shared__ __attribute__((aligned(16))) float sRef[3][KD];   // gamma of rows 16, 32, 48
+  __shared__ __attribute__((aligned(16))) float sRef[4][KD];   // gamma of rows 16, 32, 48 and the chunk total
   // sL (Akk) and sA ((I+L)^-1)
   __shared__ __attribute__((aligned(16))) float sLA[2 * 64 * P64];
   float* sL = sLA;
@@ -310,27 +310,25 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
   __syncthreads();
 
   // ---- finish the chunk cumsum; publish reference rows and the chunk decay
-  float gC[NKS][8];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int c0 = 32 * ks + 8 * quad;
-    // running sum over the waves' totals: the part before this wave is its
-    // offset, the whole is the chunk total
+    // offset of this wave's rows: the sum of the earlier waves' totals
     float off[8];
     zero8(off);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < 3; ++w) {
+      if (w >= wave) break;
       float t[8];
       load8(&sTot[w][c0], t);
-      if (w > 0 && w == wave)   // (wave 0: offset zero)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) off[e] = gC[ks][e];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gC[ks][e] = w == 0 ? t[e] : gC[ks][e] + t[e];
+      for (int e = 0; e < 8; ++e) off[e] += t[e];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) gl[ks][e] += off[e];
+    // reference rows 16, 32, 48 and row 63 (the chunk total gamma_C)
     if (r16 == 0 && wave >= 1) store8(&sRef[wave - 1][c0], gl[ks]);
+    if (r16 == 15 && wave == 3) store8(&sRef[3][c0], gl[ks]);
   }
   // normalised rows
 #pragma unroll
@@ -366,8 +364,9 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         float d[8];
+        load8(sRef[3] + 32 * ks + 8 * quad, d);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d[e] = fexp2(gC[ks][e]);
+        for (int e = 0; e < 8; ++e) d[e] = fexp2(d[e]);
         store8(reinterpret_cast<float*>(rec + RL.gd) + 32 * ks + 8 * quad, d);
       }
     }
@@ -429,9 +428,10 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
     const uint32_t kl_off = (uint32_t)lane * 16 + (wave >> 1) * 8 + (wave & 1) * 4;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      float x[8];
+      float x[8], gc[8];
+      load8(sRef[3] + 32 * ks + 8 * quad, gc);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = kx[ks][e] * fexp2(gC[ks][e] - gl[ks][e]);
+      for (int e = 0; e < 8; ++e) x[e] = kx[ks][e] * fexp2(gc[e] - gl[ks][e]);
       const Frag f = split8(x);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
