@@ -363,12 +363,13 @@ kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const vo
 namespace {
 
 // Workspace of the backward: the chunk map, then the backward records, the
-// chunk-entry states, the chunk-exit state
-// gradients, the per-value-head q/k gradients, beta and decay gradients and
-// the gate's block partial sums.
+// chunk-entry states, the chunk-exit state gradients, the per-value-head q/k
+// gradients, beta and decay gradients, the gate's block partial sums and
+// each chunk's dL / dAqk for the pair sums.
 struct BwdPlan {
   Plan fwd;
   size_t off_rec = 0, off_h = 0, off_dh = 0, off_dqn = 0, off_dkn = 0, off_db = 0, off_dg = 0, off_part = 0;
+  size_t off_pairs = 0;
   size_t bytes = 0;
   int64_t tokens = 0;
 };
@@ -394,6 +395,7 @@ kda_status_t plan_bwd(const kda_problem_t* p, BwdPlan& bp) {
   bp.off_db = off;   off = align256(off + th * sizeof(float));
   bp.off_dg = off;   off = align256(off + th * p->K * sizeof(float));
   bp.off_part = off; off = align256(off + nblk * p->Hv * (p->K + 1) * sizeof(float));
+  bp.off_pairs = off; off = align256(off + slots * 2 * kda::BT * kda::BT * sizeof(float));
   bp.bytes = off;
   return KDA_OK;
 }
@@ -464,12 +466,14 @@ kda_status_t kda_chunk_bwd(const kda_problem_t* p, const void* q, const void* k,
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta;
   a.dA_log = (p->flags & KDA_GATE_IN_KERNEL) ? dA_log : nullptr;
   a.ddt_bias = ((p->flags & KDA_GATE_IN_KERNEL) && dt_bias) ? ddt_bias : nullptr;
+  a.pairs = reinterpret_cast<float*>(ws + bp.off_pairs);
   float* part = reinterpret_cast<float*>(ws + bp.off_part);
-  // prep (records), forward states, reverse state scan, chunk backward, q/k, gate, gate sums
-  static const int order[] = {0, 6, 1, 2, 3, 4, 5};
+  // prep (records), forward states, reverse state scan, chunk backward and its
+  // pair sums, q/k, gate, gate sums
+  static const int order[] = {0, 6, 1, 2, 7, 3, 4, 5};
   static const char* what[] = {"backward prep launch", "backward reverse scan launch", "backward chunk launch",
                                "backward q/k launch", "backward gate launch", "backward gate sum launch",
-                               "backward state scan launch"};
+                               "backward state scan launch", "backward pair sums launch"};
   for (int stage : order)
     if ((st = hip_status(kda::launch_bwd(p->K, p->V, p->dtype, a, stage, bp.tokens, part, s), what[stage])) != KDA_OK)
       return st;

@@ -451,24 +451,141 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------- chunk backward
+// fp32 matrix-core products (v_mfma_f32_16x16x4_f32, exact fp32 products)
+// for 64-row outputs.  A 64 x N output is cut into 16 x 16 tiles; wave w owns
+// tiles w + 8 t (t < TPW), all in tile column w % (N / 16), at tile rows
+// (w + 8 t) / (N / 16).  In a tile, lane l holds rows 4 (l / 16) + e (e =
+// 0..3) of column l % 16.  Pass p of a 16-wide reduction step gives lane l the
+// reduction index 4 (l / 16) + p, so each operand is read as four
+// consecutive reduction values per lane.
+template <int N>
+struct Own {
+  static constexpr int NT = N / 16, TPW = 4 * NT / (NTH / 64);
+  int w, r16, q;
+  __device__ explicit Own(int tid) : w(tid >> 6), r16(tid & 15), q((tid >> 4) & 3) {}
+  __device__ int ti(int t) const { return (w + (NTH / 64) * t) / NT; }
+  __device__ int col() const { return 16 * (w % NT) + r16; }
+  __device__ int row(int t, int e) const { return 16 * ti(t) + 4 * q + e; }
+};
+static_assert(Own<64>::TPW == 2 && Own<128>::TPW == 4, "eight waves cover a 64-row output");
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc += A (64 x kr) * B (kr x N), both read through an LDS staging buffer KB
+// reduction indices at a time (A as [row][k], B as [col][k], so that a lane
+// reads four consecutive reduction values with one 16-byte access).  The next
+// block's values are fetched into registers while the current block is
+// multiplied.  CKA / CKB: the source is contiguous along the reduction index
+// (else along A's rows / B's columns), so consecutive threads fetch
+// consecutive addresses.  kr must be a multiple of KB.
+template <int N, int KB, bool CKA, bool CKB, int CAP, typename FA, typename FB>
+__device__ __forceinline__ void mf_staged(f32x4 (&acc)[Own<N>::TPW], int kr, int tid, FA A, FB B,
+                                          float* stage) {
+  constexpr int L = KB + 4, NA = BT * KB / NTH, NB = N * KB / NTH;
+  static_assert(BT * L + N * L <= CAP, "the staged blocks fit the staging buffer");
+  static_assert(BT * KB % NTH == 0 && N * KB % NTH == 0 && KB % 16 == 0, "whole blocks per thread");
+  float* sa = stage;
+  float* sb = stage + BT * L;
+  const Own<N> o(tid);
+  float ra[NA], rb[NB];
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const int e = tid + NTH * s, m = CKA ? e / KB : e % BT, kk = CKA ? e % KB : e / BT;
+      ra[s] = A(m, k0 + kk);
+    }
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      const int e = tid + NTH * s, n = CKB ? e / KB : e % N, kk = CKB ? e % KB : e / N;
+      rb[s] = B(k0 + kk, n);
+    }
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < kr; k0 += KB) {
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const int e = tid + NTH * s, m = CKA ? e / KB : e % BT, kk = CKA ? e % KB : e / BT;
+      sa[m * L + kk] = ra[s];
+    }
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      const int e = tid + NTH * s, n = CKB ? e / KB : e % N, kk = CKB ? e % KB : e / N;
+      sb[n * L + kk] = rb[s];
+    }
+    __syncthreads();
+    if (k0 + KB < kr) fetch(k0 + KB);
+#pragma unroll
+    for (int kk = 0; kk < KB; kk += 16) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(&sb[o.col() * L + kk + 4 * o.q]);
+#pragma unroll
+      for (int t = 0; t < Own<N>::TPW; ++t) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(&sa[(16 * o.ti(t) + o.r16) * L + kk + 4 * o.q]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], b[p], acc[t]);
+      }
+    }
+    __syncthreads();
+  }
+}
+// acc += A (64 x kr) * B (kr x N) with both operands read element by element
+// (from LDS) through accessors.
+template <int N, typename FA, typename FB>
+__device__ __forceinline__ void mf_lds(f32x4 (&acc)[Own<N>::TPW], int kr, int tid, FA A, FB B) {
+  const Own<N> o(tid);
+  for (int kk = 0; kk < kr; kk += 16) {
+    float b[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) b[p] = B(kk + 4 * o.q + p, o.col());
+#pragma unroll
+    for (int t = 0; t < Own<N>::TPW; ++t)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) acc[t] = mfma4(A(16 * o.ti(t) + o.r16, kk + 4 * o.q + p), b[p], acc[t]);
+  }
+}
+template <int T>
+__device__ __forceinline__ void zero(f32x4 (&x)[T]) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) x[t] = zero4();
+}
+// Sum over the 16 lanes of a DPP row (lanes sharing l / 16).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+
 template <int KD, int VD, typename IT>
 __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   static_assert(KD == 128 || KD == 64, "K");
-  constexpr int LX = (KD > VD ? KD : VD) + 1;
-  constexpr int MRK = BT / RS, NRK = KD / 16, NRV = VD / 16;
-  // sB3 doubles as the staging buffer of the products (A block 64 x 33, B block 32 x (N + 1))
-  constexpr int STAGE = BT * 33 + 32 * ((KD > VD ? KD : VD) + 1);
+  constexpr int MX = KD > VD ? KD : VD;
+  constexpr int LX = MX + 4;        // row stride of the 64-row matrices (16-byte aligned rows)
+  constexpr int LS = BT + 4;        // row stride of the 64 x 64 matrices
+  constexpr int STAGE = (BT + MX) * (32 + 4);
   constexpr int NB3 = BT * LX > STAGE ? BT * LX : STAGE;
-  __shared__ float sB1[BT * LX], sB2[BT * LX], sB3[NB3];
-  __shared__ float sS1[BT * 65], sS2[BT * 65], sS3[BT * 65];
+  // sB3 doubles as the staging buffer of the products until the pair sums
+  __shared__ __attribute__((aligned(16))) float sB1[BT * LX];
+  __shared__ __attribute__((aligned(16))) float sB2[BT * LX];
+  __shared__ __attribute__((aligned(16))) float sB3[NB3];
+  __shared__ __attribute__((aligned(16))) float sS1[BT * LS];
+  __shared__ __attribute__((aligned(16))) float sS2[BT * LS];
+  __shared__ __attribute__((aligned(16))) float sS3[BT * LS];
   __shared__ float sBeta[BT], sGC[KD];
-  static_assert(BT * 17 <= BT * 65 && RS * KD <= BT * 65, "reduction buffers fit the small matrices");
-  float* sRed = sS1;    // (after the pair sums)
-  float* sRedK = sS2;
+  using OK = Own<KD>;
+  using OV = Own<VD>;
+  using OS = Own<BT>;
+  static_assert((OK::NT + OV::NT) * BT <= BT * LS && (NTH / 64 / OK::NT) * KD <= BT * LS,
+                "reduction buffers fit the small matrices");
   constexpr BwdRec R = bwd_rec(KD, VD);
   const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
   const ChunkPos P = chunk_pos(a.seq, gc, h, a.nchunks);
-  const int tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
+  const int tid = threadIdx.x;
+  const OK ok(tid);
+  const OV ov(tid);
+  const OS os(tid);
   const float* rec = a.rec + P.slot * (int64_t)(R.bytes / 4);
   const float* hc = a.h_store + P.slot * (int64_t)(KD * VD);
   const float* dh = a.dh_store + P.slot * (int64_t)(KD * VD);
@@ -483,266 +600,517 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   if (tid < KD) sGC[tid] = G[(P.C - 1) * KD + tid];
   __syncthreads();
 
-  // gradient accumulators of q, k and G, rows tm + RS x, channels tn + 16 y
-  float dq[MRK][NRK], dk[MRK][NRK], dG[MRK][NRK];
+  // gradients of q, k and G in the 64 x K ownership; partial sums of dbeta
+  // (64 x K and 64 x V ownership) and of dG_C (this lane's column)
+  f32x4 dq[OK::TPW], dk[OK::TPW], dG[OK::TPW], dbK[OK::TPW], dbV[OV::TPW];
   zero(dq);
   zero(dk);
   zero(dG);
-  float dbeta[MRK];   // partial sums over this thread's columns
-#pragma unroll
-  for (int x = 0; x < MRK; ++x) dbeta[x] = 0.f;
-  float dGCp[NRK];    // partial sums over this thread's rows
-#pragma unroll
-  for (int y = 0; y < NRK; ++y) dGCp[y] = 0.f;
+  zero(dbK);
+  zero(dbV);
+  float dGCp = 0.f;
 
-  float* stage = sB3;   // staging buffer of the products until the pair sums
+  float* stage = sB3;
   const float* wr = rec + R.w;
   const float* aq = rec + R.aqk;
   {  // v_new = u - w h  -> B1
-    float acc[MRK][NRV];
+    f32x4 acc[OV::TPW];
     zero(acc);
-    mm_staged<MRK, NRV, 32, true, false, NB3>(acc, KD, tid, [&](int i, int kk) { return wr[i * KD + kk]; },
-                                         [&](int kk, int j) { return hc[kk * VD + j]; }, stage);
+    mf_staged<VD, 32, true, false, NB3>(acc, KD, tid, [&](int i, int kk) { return wr[i * KD + kk]; },
+                                        [&](int kk, int j) { return hc[kk * VD + j]; }, stage);
 #pragma unroll
-    for (int x = 0; x < MRK; ++x)
+    for (int t = 0; t < OV::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < NRV; ++y) {
-        const int i = tm + RS * x, j = tn + 16 * y;
-        sB1[i * LX + j] = rec[R.u + i * VD + j] - acc[x][y];
+      for (int e = 0; e < 4; ++e) {
+        const int i = ov.row(t, e), j = ov.col();
+        sB1[i * LX + j] = rec[R.u + i * VD + j] - acc[t][e];
       }
   }
   {  // dv_new = Aqk^T do + kg dh'  -> B2
-    float acc[MRK][NRV];
+    f32x4 acc[OV::TPW];
     zero(acc);
-    mm_staged<MRK, NRV, 32, false, false, NB3>(acc, BT, tid, [&](int i, int r) { return aq[r * BT + i]; },
-                                          [&](int r, int j) { return DO(r, j); }, stage);
-    mm_staged<MRK, NRV, 32, true, false, NB3>(
+    mf_staged<VD, 32, false, false, NB3>(acc, BT, tid, [&](int i, int r) { return aq[r * BT + i]; },
+                                         [&](int r, int j) { return DO(r, j); }, stage);
+    mf_staged<VD, 32, true, false, NB3>(
         acc, KD, tid, [&](int i, int kk) { return kn[i * KD + kk] * ex2(sGC[kk] - G[i * KD + kk]); },
         [&](int kk, int j) { return dh[kk * VD + j]; }, stage);
 #pragma unroll
-    for (int x = 0; x < MRK; ++x)
+    for (int t = 0; t < OV::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < NRV; ++y) sB2[(tm + RS * x) * LX + tn + 16 * y] = acc[x][y];
+      for (int e = 0; e < 4; ++e) sB2[ov.row(t, e) * LX + ov.col()] = acc[t][e];
   }
   __syncthreads();
   {  // dAqk = tril(do v_new^T)  -> S1
-    float acc[MRK][4];
+    f32x4 acc[OS::TPW];
     zero(acc);
-    mm_staged<MRK, 4, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return DO(i, c); },
-                                      [&](int c, int j) { return sB1[j * LX + c]; }, stage);
+    mf_staged<BT, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return DO(i, c); },
+                                       [&](int c, int j) { return sB1[j * LX + c]; }, stage);
 #pragma unroll
-    for (int x = 0; x < MRK; ++x)
+    for (int t = 0; t < OS::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int i = tm + RS * x, j = tn + 16 * y;
-        sS1[i * 65 + j] = i >= j ? acc[x][y] : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const int i = os.row(t, e), j = os.col();
+        sS1[i * LS + j] = i >= j ? acc[t][e] : 0.f;
       }
   }
   {  // dqg = do h^T: q and G
-    float acc[MRK][NRK];
+    f32x4 acc[OK::TPW];
     zero(acc);
-    mm_staged<MRK, NRK, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return DO(i, c); },
-                                        [&](int c, int kk) { return hc[kk * VD + c]; }, stage);
+    mf_staged<KD, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return DO(i, c); },
+                                       [&](int c, int kk) { return hc[kk * VD + c]; }, stage);
 #pragma unroll
-    for (int x = 0; x < MRK; ++x)
+    for (int t = 0; t < OK::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < NRK; ++y) {
-        const int i = tm + RS * x, kk = tn + 16 * y;
-        const float e = a.scale * ex2(G[i * KD + kk]);
-        dq[x][y] += e * acc[x][y];
-        dG[x][y] += e * qn[i * KD + kk] * acc[x][y];
+      for (int e = 0; e < 4; ++e) {
+        const int i = ok.row(t, e), kk = ok.col();
+        const float ex = a.scale * ex2(G[i * KD + kk]);
+        dq[t][e] += ex * acc[t][e];
+        dG[t][e] += ex * qn[i * KD + kk] * acc[t][e];
       }
   }
   {  // dkg = v_new dh'^T: k, G and G_C
-    float acc[MRK][NRK];
+    f32x4 acc[OK::TPW];
     zero(acc);
-    mm_staged<MRK, NRK, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB1[i * LX + c]; },
-                                        [&](int c, int kk) { return dh[kk * VD + c]; }, stage);
+    mf_staged<KD, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB1[i * LX + c]; },
+                                       [&](int c, int kk) { return dh[kk * VD + c]; }, stage);
 #pragma unroll
-    for (int x = 0; x < MRK; ++x)
+    for (int t = 0; t < OK::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < NRK; ++y) {
-        const int i = tm + RS * x, kk = tn + 16 * y;
-        const float e = ex2(sGC[kk] - G[i * KD + kk]);
-        const float kgv = kn[i * KD + kk] * e;
-        dk[x][y] += e * acc[x][y];
-        dG[x][y] -= kgv * acc[x][y];
-        dGCp[y] += kgv * acc[x][y];
+      for (int e = 0; e < 4; ++e) {
+        const int i = ok.row(t, e), kk = ok.col();
+        const float ex = ex2(sGC[kk] - G[i * KD + kk]);
+        const float kgv = kn[i * KD + kk] * ex;
+        dk[t][e] += ex * acc[t][e];
+        dG[t][e] -= kgv * acc[t][e];
+        dGCp += kgv * acc[t][e];
       }
   }
   {  // dw = -dv_new h^T  -> B1 (v_new no longer needed)
-    float acc[MRK][NRK];
+    f32x4 acc[OK::TPW];
     zero(acc);
-    mm_staged<MRK, NRK, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB2[i * LX + c]; },
-                                        [&](int c, int kk) { return hc[kk * VD + c]; }, stage);
+    mf_staged<KD, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB2[i * LX + c]; },
+                                       [&](int c, int kk) { return hc[kk * VD + c]; }, stage);
 #pragma unroll
-    for (int x = 0; x < MRK; ++x)
+    for (int t = 0; t < OK::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < NRK; ++y) sB1[(tm + RS * x) * LX + tn + 16 * y] = -acc[x][y];
+      for (int e = 0; e < 4; ++e) sB1[ok.row(t, e) * LX + ok.col()] = -acc[t][e];
   }
 #pragma unroll 8
-  for (int i = tid; i < BT * BT; i += NTH) sS2[(i / BT) * 65 + i % BT] = rec[R.A + i];
+  for (int i = tid; i < BT * BT; i += NTH) sS2[(i / BT) * LS + i % BT] = rec[R.A + i];
   __syncthreads();
   {  // d(b k e^G) = A^T dw: k, b, G
-    float acc[MRK][NRK];
+    f32x4 acc[OK::TPW];
     zero(acc);
-    mm(acc, BT, tm, tn, [&](int j, int i) { return sS2[i * 65 + j]; }, [&](int i, int kk) { return sB1[i * LX + kk]; });
+    mf_lds<KD>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
+               [&](int i, int kk) { return sB1[i * LX + kk]; });
 #pragma unroll
-    for (int x = 0; x < MRK; ++x)
+    for (int t = 0; t < OK::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < NRK; ++y) {
-        const int j = tm + RS * x, kk = tn + 16 * y;
-        const float e = ex2(G[j * KD + kk]), X = kn[j * KD + kk] * e;
-        const float dX = sBeta[j] * acc[x][y];
-        dbeta[x] += X * acc[x][y];
-        dk[x][y] += e * dX;
-        dG[x][y] += X * dX;
+      for (int e = 0; e < 4; ++e) {
+        const int j = ok.row(t, e), kk = ok.col();
+        const float ex = ex2(G[j * KD + kk]), X = kn[j * KD + kk] * ex;
+        const float dX = sBeta[j] * acc[t][e];
+        dbK[t][e] += X * acc[t][e];
+        dk[t][e] += ex * dX;
+        dG[t][e] += X * dX;
       }
   }
   {  // d(b v) = A^T dv_new: dv and b
-    float acc[MRK][NRV];
+    f32x4 acc[OV::TPW];
     zero(acc);
-    mm(acc, BT, tm, tn, [&](int j, int i) { return sS2[i * 65 + j]; }, [&](int i, int c) { return sB2[i * LX + c]; });
+    mf_lds<VD>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
+               [&](int i, int c) { return sB2[i * LX + c]; });
 #pragma unroll
-    for (int x = 0; x < MRK; ++x) {
-      const int j = tm + RS * x;
+    for (int t = 0; t < OV::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < NRV; ++y) {
-        const int c = tn + 16 * y;
-        dbeta[x] += VV(j, c) * acc[x][y];
-        if (j < P.C) a.dv[((P.tok0 + j) * a.Hv + h) * VD + c] = sBeta[j] * acc[x][y];
+      for (int e = 0; e < 4; ++e) {
+        const int j = ov.row(t, e), c = ov.col();
+        dbV[t][e] += VV(j, c) * acc[t][e];
+        if (j < P.C) a.dv[((P.tok0 + j) * a.Hv + h) * VD + c] = sBeta[j] * acc[t][e];
       }
-    }
   }
   {  // dA = tril(dv_new (b v)^T + dw (b k e^G)^T)  -> S3
-    float acc[MRK][4];
+    f32x4 acc[OS::TPW];
     zero(acc);
-    mm_staged<MRK, 4, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB2[i * LX + c]; },
-                                      [&](int c, int j) { return sBeta[j] * VV(j, c); }, stage);
-    mm_staged<MRK, 4, 32, true, true, NB3>(acc, KD, tid, [&](int i, int c) { return sB1[i * LX + c]; },
-                                      [&](int c, int j) { return sBeta[j] * kn[j * KD + c] * ex2(G[j * KD + c]); },
-                                      stage);
+    mf_staged<BT, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB2[i * LX + c]; },
+                                       [&](int c, int j) { return sBeta[j] * VV(j, c); }, stage);
+    mf_staged<BT, 32, true, true, NB3>(acc, KD, tid, [&](int i, int c) { return sB1[i * LX + c]; },
+                                       [&](int c, int j) { return sBeta[j] * kn[j * KD + c] * ex2(G[j * KD + c]); },
+                                       stage);
 #pragma unroll
-    for (int x = 0; x < MRK; ++x)
+    for (int t = 0; t < OS::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int i = tm + RS * x, j = tn + 16 * y;
-        sS3[i * 65 + j] = i >= j ? acc[x][y] : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const int i = os.row(t, e), j = os.col();
+        sS3[i * LS + j] = i >= j ? acc[t][e] : 0.f;
       }
   }
   __syncthreads();
   {  // dL = -strict_tril(A^T (dA A^T))  -> S3
-    float acc[MRK][4];
+    f32x4 acc[OS::TPW];
     zero(acc);
-    mm(acc, BT, tm, tn, [&](int i, int j) { return sS3[i * 65 + j]; }, [&](int j, int m) { return sS2[m * 65 + j]; });
+    mf_lds<BT>(acc, BT, tid, [&](int i, int j) { return sS3[i * LS + j]; },
+               [&](int j, int m) { return sS2[m * LS + j]; });
     __syncthreads();
 #pragma unroll
-    for (int x = 0; x < MRK; ++x)
+    for (int t = 0; t < OS::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) sS3[(tm + RS * x) * 65 + tn + 16 * y] = acc[x][y];
+      for (int e = 0; e < 4; ++e) sS3[os.row(t, e) * LS + os.col()] = acc[t][e];
     __syncthreads();
     zero(acc);
-    mm(acc, BT, tm, tn, [&](int l, int i) { return sS2[i * 65 + l]; }, [&](int i, int m) { return sS3[i * 65 + m]; });
+    mf_lds<BT>(acc, BT, tid, [&](int l, int i) { return sS2[i * LS + l]; },
+               [&](int i, int m) { return sS3[i * LS + m]; });
     __syncthreads();
 #pragma unroll
-    for (int x = 0; x < MRK; ++x)
+    for (int t = 0; t < OS::TPW; ++t)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int l = tm + RS * x, m = tn + 16 * y;
-        sS3[l * 65 + m] = l > m ? -acc[x][y] : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const int l = os.row(t, e), m = os.col();
+        sS3[l * LS + m] = l > m ? -acc[t][e] : 0.f;
       }
-  }
-  // stage G, k, q for the pair sums
-#pragma unroll 8
-  for (int i = tid; i < BT * KD; i += NTH) {
-    const int r = i / KD, c = i % KD;
-    sB1[r * LX + c] = G[i];
-    sB2[r * LX + c] = kn[i];
-    sB3[r * LX + c] = qn[i];
   }
   __syncthreads();
-  // pair sums, row side: row i gathers over its columns j
+  {  // dL and dAqk to the workspace for the pair sums
+    float* pr = a.pairs + P.slot * (int64_t)(2 * BT * BT);
 #pragma unroll
-  for (int x = 0; x < MRK; ++x) {
-    const int i = tm + RS * x;
-#pragma unroll
-    for (int y = 0; y < NRK; ++y) {
-      const int c = tn + 16 * y;
-      const float gi = sB1[i * LX + c];
-      float rL = 0.f, rA = 0.f;
-      for (int j = 0; j <= i; ++j) {
-        const float kf = sB2[j * LX + c] * ex2(gi - sB1[j * LX + c]);
-        rL += sS3[i * 65 + j] * kf;
-        rA += sS1[i * 65 + j] * kf;
-      }
-      const float ki = sB2[i * LX + c], qi = sB3[i * LX + c];
-      dk[x][y] += sBeta[i] * rL;
-      dq[x][y] += a.scale * rA;
-      dG[x][y] += sBeta[i] * ki * rL + a.scale * qi * rA;
-      dbeta[x] += ki * rL;
+    for (int s = 0; s < BT * BT / 4 / NTH; ++s) {
+      const int i = 4 * (tid + NTH * s), r = i / BT, cc = i % BT;
+      *reinterpret_cast<f32x4*>(pr + i) = *reinterpret_cast<const f32x4*>(&sS3[r * LS + cc]);
+      *reinterpret_cast<f32x4*>(pr + BT * BT + i) = *reinterpret_cast<const f32x4*>(&sS1[r * LS + cc]);
     }
   }
-  // column side: column j gathers over its rows i
+  // dD = rowsum(h . dh'), four threads per row of the states, 16-byte loads
+  float* sDD = sS2 + 4 * KD;   // [KD] (after sRedK)
+  {
+    constexpr int TPR = NTH / KD > 4 ? 4 : NTH / KD, SEG = VD / TPR;
+    const int r = tid / TPR, part = tid % TPR;
+    float s = 0.f;
+    if (r < KD) {
 #pragma unroll
-  for (int x = 0; x < MRK; ++x) {
-    const int j = tm + RS * x;
-#pragma unroll
-    for (int y = 0; y < NRK; ++y) {
-      const int c = tn + 16 * y;
-      const float gj = sB1[j * LX + c];
-      float cL = 0.f, cA = 0.f;
-      for (int i = j; i < BT; ++i) {
-        const float f = ex2(sB1[i * LX + c] - gj);
-        cL += sS3[i * 65 + j] * sBeta[i] * sB2[i * LX + c] * f;
-        cA += sS1[i * 65 + j] * sB3[i * LX + c] * f;
+      for (int cc = part * SEG; cc < (part + 1) * SEG; cc += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(hc + r * VD + cc);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(dh + r * VD + cc);
+        s += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
       }
-      const float s = cL + a.scale * cA;
-      dk[x][y] += s;
-      dG[x][y] -= sB2[j * LX + c] * s;
     }
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) s += __shfl_xor(s, m);
+    if (r < KD && part == 0) sDD[r] = s;
   }
-  // reductions: dbeta over columns, dG_C over rows
+  // dbeta partial sums in a fixed order (per ownership, the 16 lanes of a row
+  // first), dG_C over rows (the four lane groups first)
   __syncthreads();
+  float* sRedB = sS1;   // [OK::NT + OV::NT][BT]
+  float* sRedK = sS2;   // [waves per column block][KD]
 #pragma unroll
-  for (int x = 0; x < MRK; ++x) sRed[(tm + RS * x) * 17 + tn] = dbeta[x];
+  for (int t = 0; t < OK::TPW; ++t)
 #pragma unroll
-  for (int y = 0; y < NRK; ++y) sRedK[tm * KD + tn + 16 * y] = dGCp[y];
+    for (int e = 0; e < 4; ++e) {
+      const float s = sum16(dbK[t][e]);
+      if (ok.r16 == 0) sRedB[(ok.w % OK::NT) * BT + ok.row(t, e)] = s;
+    }
+#pragma unroll
+  for (int t = 0; t < OV::TPW; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float s = sum16(dbV[t][e]);
+      if (ov.r16 == 0) sRedB[(OK::NT + ov.w % OV::NT) * BT + ov.row(t, e)] = s;
+    }
+  {
+    float s = dGCp;
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (ok.q == 0) sRedK[(ok.w / OK::NT) * KD + ok.col()] = s;
+  }
+  // dG into LDS (v_new / dw no longer needed)
+#pragma unroll
+  for (int t = 0; t < OK::TPW; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sB1[ok.row(t, e) * LX + ok.col()] = dG[t][e];
   __syncthreads();
   if (tid < BT) {
     float s = 0.f;
-    for (int t = 0; t < 16; ++t) s += sRed[tid * 17 + t];
+    for (int r = 0; r < OK::NT + OV::NT; ++r) s += sRedB[r * BT + tid];
     if (tid < P.C) a.dbeta_act[(P.tok0 + tid) * a.Hv + h] = s;
   }
   if (tid < KD) {
+    // dG_C (the chunk decay's gradient) joins the last row: the reverse cumsum
+    // over the rows then hands it to every row
     float s = 0.f;
-    for (int t = 0; t < RS; ++t) s += sRedK[t * KD + tid];
-    float dd = 0.f;   // dD = rowsum(h . dh')
-    for (int c = 0; c < VD; ++c) dd += hc[tid * VD + c] * dh[tid * VD + c];
-    sGC[tid] = s + ex2(sGC[tid]) * dd;   // dG_C
+    for (int r = 0; r < NTH / 64 / OK::NT; ++r) s += sRedK[r * KD + tid];
+    sB1[(P.C - 1) * LX + tid] += s + ex2(sGC[tid]) * sDD[tid];
   }
-  // dG -> dg: reverse cumsum over the chunk's rows plus dG_C
-#pragma unroll
-  for (int x = 0; x < MRK; ++x)
-#pragma unroll
-    for (int y = 0; y < NRK; ++y) sB1[(tm + RS * x) * LX + tn + 16 * y] = dG[x][y];
   __syncthreads();
-  if (tid < KD) {
-    float run = sGC[tid];
-    for (int r = P.C - 1; r >= 0; --r) {
-      run += sB1[r * LX + tid];
-      a.dg_nat[((P.tok0 + r) * a.Hv + h) * KD + tid] = run;
-    }
+  // partial gradients (the pair sums add to them): dG rows, dq, dk
+#pragma unroll 4
+  for (int i = tid; i < BT * KD; i += NTH) {
+    const int r = i / KD, cc = i % KD;
+    if (r < P.C) a.dg_nat[((P.tok0 + r) * a.Hv + h) * KD + cc] = sB1[r * LX + cc];
   }
 #pragma unroll
-  for (int x = 0; x < MRK; ++x) {
-    const int i = tm + RS * x;
-    if (i >= P.C) continue;
+  for (int t = 0; t < OK::TPW; ++t)
 #pragma unroll
-    for (int y = 0; y < NRK; ++y) {
-      const int c = tn + 16 * y;
-      a.dqn[((P.tok0 + i) * a.Hv + h) * KD + c] = dq[x][y];
-      a.dkn[((P.tok0 + i) * a.Hv + h) * KD + c] = dk[x][y];
+    for (int e = 0; e < 4; ++e) {
+      const int i = ok.row(t, e);
+      if (i >= P.C) continue;
+      a.dqn[((P.tok0 + i) * a.Hv + h) * KD + ok.col()] = dq[t][e];
+      a.dkn[((P.tok0 + i) * a.Hv + h) * KD + ok.col()] = dk[t][e];
     }
+}
+
+// Pair sums of the chunk backward: the gradients dL and dAqk of the decayed
+// key-key and query-key products, back into k, q, beta and the gate cumsum,
+// added to the partial gradients the chunk kernel left; then the reverse
+// cumsum of the gate gradient over the chunk's rows.
+template <int KD, int VD, typename IT>
+__global__ __launch_bounds__(NTH) void bwd_pairs_kernel(BwdArgs a) {
+  static_assert(KD == 128 || KD == 64, "K");
+  constexpr int LX = KD + 4;        // row stride of the 64 x K matrices
+  constexpr int LS = BT + 4;        // row stride of the 64 x 64 matrices
+  __shared__ __attribute__((aligned(16))) float sB1[BT * LX];
+  __shared__ __attribute__((aligned(16))) float sB2[BT * LX];
+  __shared__ __attribute__((aligned(16))) float sB3[BT * LX];
+  __shared__ __attribute__((aligned(16))) float sS1[BT * LS];
+  __shared__ __attribute__((aligned(16))) float sS3[BT * LS];
+  __shared__ float sBeta[BT];
+  using OK = Own<KD>;
+  static_assert(OK::NT * BT <= BT * LS && (NTH / KD) * KD <= BT * LS, "reduction buffers fit");
+  constexpr BwdRec R = bwd_rec(KD, VD);
+  const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
+  const ChunkPos P = chunk_pos(a.seq, gc, h, a.nchunks);
+  const int tid = threadIdx.x;
+  const OK ok(tid);
+  const float* rec = a.rec + P.slot * (int64_t)(R.bytes / 4);
+  const float* G = rec + R.G;
+  const float* kn = rec + R.kn;
+  const float* qn = rec + R.qn;
+  if (tid < BT) sBeta[tid] = rec[R.beta + tid];
+  {  // dL and dAqk
+    const float* pr = a.pairs + P.slot * (int64_t)(2 * BT * BT);
+#pragma unroll
+    for (int s = 0; s < BT * BT / 4 / NTH; ++s) {
+      const int i = 4 * (tid + NTH * s), r = i / BT, cc = i % BT;
+      *reinterpret_cast<f32x4*>(&sS3[r * LS + cc]) = *reinterpret_cast<const f32x4*>(pr + i);
+      *reinterpret_cast<f32x4*>(&sS1[r * LS + cc]) = *reinterpret_cast<const f32x4*>(pr + BT * BT + i);
+    }
+  }
+  // stage G, k, q for the pair sums (16-byte pieces, all issued at once)
+  {
+    constexpr int NP4 = BT * KD / 4 / NTH;
+    f32x4 xg[NP4], xk[NP4], xq[NP4];
+#pragma unroll
+    for (int s = 0; s < NP4; ++s) {
+      const int i = 4 * (tid + NTH * s);
+      xg[s] = *reinterpret_cast<const f32x4*>(G + i);
+      xk[s] = *reinterpret_cast<const f32x4*>(kn + i);
+      xq[s] = *reinterpret_cast<const f32x4*>(qn + i);
+    }
+#pragma unroll
+    for (int s = 0; s < NP4; ++s) {
+      const int i = 4 * (tid + NTH * s), r = i / KD, cc = i % KD;
+      *reinterpret_cast<f32x4*>(&sB1[r * LX + cc]) = xg[s];
+      *reinterpret_cast<f32x4*>(&sB2[r * LX + cc]) = xk[s];
+      *reinterpret_cast<f32x4*>(&sB3[r * LX + cc]) = xq[s];
+    }
+  }
+  __syncthreads();
+  f32x4 dq[OK::TPW], dk[OK::TPW], dG[OK::TPW], dbK[OK::TPW];
+  zero(dq);
+  zero(dk);
+  zero(dG);
+  zero(dbK);
+  // Pair sums of dL (S3) and dAqk (S1) back into k, q, b and G in this lane's
+  // channel c, on the matrix cores.  For a pair i >= j the decay factor
+  // 2^(G_ic - G_jc) splits at a reference row r with j <= r <= i into
+  // 2^(G_ic - G_rc) 2^(G_rc - G_jc), both <= 1 (G is non-increasing), so a
+  // block of rows against another block is a plain product of prescaled
+  // operands.  Off-diagonal blocks use the first row of the later block as r;
+  // the diagonal blocks split further (below).
+  const int c = ok.col();
+#pragma unroll
+  for (int t = 0; t < OK::TPW; ++t) {
+    const int I = ok.ti(t), i0 = 16 * I, iq = i0 + 4 * ok.q;   // rows iq .. iq + 3 of block I
+    float gq[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gq[e] = sB1[(iq + e) * LX + c];
+    f32x4 rL = zero4(), rA = zero4(), cL = zero4(), cA = zero4();
+    // row side, earlier blocks: sum over j < i0 against reference row i0
+    if (I > 0) {
+      const float gr = sB1[i0 * LX + c];
+      f32x4 pL = zero4(), pA = zero4();
+      for (int kk = 0; kk < i0; kk += 16) {
+        float b[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int j = kk + 4 * ok.q + p;
+          b[p] = sB2[j * LX + c] * ex2(gr - sB1[j * LX + c]);
+        }
+        const f32x4 aL = *reinterpret_cast<const f32x4*>(&sS3[(i0 + ok.r16) * LS + kk + 4 * ok.q]);
+        const f32x4 aA = *reinterpret_cast<const f32x4*>(&sS1[(i0 + ok.r16) * LS + kk + 4 * ok.q]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          pL = mfma4(aL[p], b[p], pL);
+          pA = mfma4(aA[p], b[p], pA);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = ex2(gq[e] - gr);
+        rL[e] += f * pL[e];
+        rA[e] += f * pA[e];
+      }
+    }
+    // column side, later blocks: sum over i >= i0 + 16 against reference row i0 + 16
+    if (I < 3) {
+      const int r = i0 + 16;
+      const float gr = sB1[r * LX + c];
+      f32x4 pL = zero4(), pA = zero4();
+      for (int kk = r; kk < BT; kk += 16) {
+        float bL[4], bA[4], aL[4], aA[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int i = kk + 4 * ok.q + p;
+          const float ex = ex2(sB1[i * LX + c] - gr);
+          bL[p] = sBeta[i] * sB2[i * LX + c] * ex;
+          bA[p] = sB3[i * LX + c] * ex;
+          aL[p] = sS3[i * LS + i0 + ok.r16];
+          aA[p] = sS1[i * LS + i0 + ok.r16];
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          pL = mfma4(aL[p], bL[p], pL);
+          pA = mfma4(aA[p], bA[p], pA);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = ex2(gr - gq[e]);
+        cL[e] += f * pL[e];
+        cA[e] += f * pA[e];
+      }
+    }
+    // the diagonal block: binary split levels b = 3 .. 0 (blocks of 16, 8, 4
+    // and 2 rows).  At level b the pairs (i, j) with i in the upper and j in
+    // the lower half of one block use that upper half's first row as the
+    // reference; every pair i > j of the block meets exactly one level, and
+    // both factors are <= 1, whatever the decay.  Rows on the other side get
+    // a zero operand before any product (their factor may overflow).
+    {
+      const int xr = 4 * ok.q;   // this lane's reduction rows x = i0 + xr + p
+#pragma unroll 1
+      for (int lv = 3; lv >= 0; --lv) {
+        const int hb = 1 << lv;
+        f32x4 pL = zero4(), pA = zero4(), qL = zero4(), qA = zero4();
+        float bR[4], bL[4], bA[4], aL[4], aA[4], aC[4], aD[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int x = xr + p, xg = i0 + x;
+          const bool lo = !((x >> lv) & 1);                       // x in a lower half
+          const float gref = sB1[(i0 + ((x >> (lv + 1)) << (lv + 1)) + hb) * LX + c];
+          const float gx = sB1[xg * LX + c], kx = sB2[xg * LX + c];
+          bR[p] = lo ? kx * ex2(gref - gx) : 0.f;                   // row side: j = x (lower)
+          const float eu = !lo ? ex2(gx - gref) : 0.f;              // column side: i = x (upper)
+          bL[p] = sBeta[xg] * kx * eu;
+          bA[p] = sB3[xg * LX + c] * eu;
+          // A operands, row i0 + r16 against reduction row x (same block, opposite halves)
+          const int y = ok.r16;
+          const bool pair_rows = (y >> (lv + 1)) == (x >> (lv + 1));
+          const bool row_up = pair_rows && ((y >> lv) & 1) && lo;    // i = y upper, j = x lower
+          const bool col_lo = pair_rows && !((y >> lv) & 1) && !lo;  // j = y lower, i = x upper
+          aL[p] = row_up ? sS3[(i0 + y) * LS + xg] : 0.f;
+          aA[p] = row_up ? sS1[(i0 + y) * LS + xg] : 0.f;
+          aC[p] = col_lo ? sS3[xg * LS + i0 + y] : 0.f;
+          aD[p] = col_lo ? sS1[xg * LS + i0 + y] : 0.f;
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          pL = mfma4(aL[p], bR[p], pL);
+          pA = mfma4(aA[p], bR[p], pA);
+          qL = mfma4(aC[p], bL[p], qL);
+          qA = mfma4(aD[p], bA[p], qA);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int y = 4 * ok.q + e;   // output row iq + e
+          const bool up = (y >> lv) & 1;
+          const float gref = sB1[(i0 + ((y >> (lv + 1)) << (lv + 1)) + hb) * LX + c];
+          const float fr = up ? ex2(gq[e] - gref) : 0.f;      // row side: i upper
+          const float fc = !up ? ex2(gref - gq[e]) : 0.f;     // column side: j lower
+          rL[e] += fr * pL[e];
+          rA[e] += fr * pA[e];
+          cL[e] += fc * qL[e];
+          cA[e] += fc * qA[e];
+        }
+      }
+      // the diagonal of dAqk (factor 1): row side j = i, column side i = j
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = iq + e;
+        const float d = sS1[i * LS + i];
+        rA[e] += d * sB2[i * LX + c];
+        cA[e] += d * sB3[i * LX + c];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = iq + e;
+      const float ki = sB2[i * LX + c], qi = sB3[i * LX + c];
+      const float s = cL[e] + a.scale * cA[e];
+      dk[t][e] += sBeta[i] * rL[e] + s;
+      dq[t][e] += a.scale * rA[e];
+      dG[t][e] += sBeta[i] * ki * rL[e] + a.scale * qi * rA[e] - ki * s;
+      dbK[t][e] += ki * rL[e];
+    }
+  }
+  __syncthreads();   // (the pair sums read sB3 and sS3, reused below)
+  // dbeta: this kernel's share, added to the chunk kernel's partial sums
+  float* sRedB = sS1;   // [OK::NT][BT]
+#pragma unroll
+  for (int t = 0; t < OK::TPW; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float s = sum16(dbK[t][e]);
+      if (ok.r16 == 0) sRedB[(ok.w % OK::NT) * BT + ok.row(t, e)] = s;
+    }
+  // dq, dk: added to the partial gradients; dG: the whole row into LDS
+#pragma unroll
+  for (int t = 0; t < OK::TPW; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = ok.row(t, e);
+      float gpart = 0.f;
+      if (i < P.C) {
+        const int64_t o = ((P.tok0 + i) * a.Hv + h) * KD + c;
+        a.dqn[o] += dq[t][e];
+        a.dkn[o] += dk[t][e];
+        gpart = a.dg_nat[o];
+      }
+      sB3[i * LX + c] = gpart + dG[t][e];
+    }
+  __syncthreads();
+  if (tid < BT && tid < P.C) {
+    float s = 0.f;
+    for (int r = 0; r < OK::NT; ++r) s += sRedB[r * BT + tid];
+    a.dbeta_act[(P.tok0 + tid) * a.Hv + h] += s;
+  }
+  {  // dG -> dg: reverse cumsum over the chunk's rows (dG_C is in the last
+     // row); NTH / KD threads per channel, each a segment of SR rows
+    constexpr int NSG = NTH / KD, SR = BT / NSG;
+    float* sSeg = sS3;   // [NSG][KD] segment totals
+    const int cc = tid % KD, sg = tid / KD, r0 = sg * SR;
+    float x[SR], run = 0.f;
+#pragma unroll
+    for (int r = SR - 1; r >= 0; --r) {
+      run += r0 + r < P.C ? sB3[(r0 + r) * LX + cc] : 0.f;
+      x[r] = run;
+    }
+    sSeg[sg * KD + cc] = run;
+    __syncthreads();
+    float off = 0.f;
+    for (int g = sg + 1; g < NSG; ++g) off += sSeg[g * KD + cc];
+#pragma unroll
+    for (int r = 0; r < SR; ++r)
+      if (r0 + r < P.C) a.dg_nat[((P.tok0 + r0 + r) * a.Hv + h) * KD + cc] = x[r] + off;
   }
 }
 
@@ -872,6 +1240,7 @@ hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int6
                           : hipSuccess;                                                                 \
       case 5: return launch(bwd_gate_sum_kernel<KK>, dim3(a.Hv), dim3(KK), s, a, nblk, (const float*)part);       \
       case 6: return nb_scan ? launch(bwd_state_kernel<KK, VV>, dim3(nb_scan), dim3(NTH), s, a) : hipSuccess;       \
+      case 7: return nb_chunk ? launch(bwd_pairs_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
     }                                                                                                   \
     return hipErrorInvalidValue;                                                                        \
   }

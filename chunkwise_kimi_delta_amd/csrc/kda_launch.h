@@ -174,6 +174,7 @@ struct BwdArgs {
   float *dq, *dk;             // [tokens][Hk][K]
   float *dv, *dg, *dbeta;     // [tokens][Hv][V], [tokens][Hv][K], [tokens][Hv]
   float *dA_log, *ddt_bias;   // [Hv], [Hv][K] or null
+  float* pairs;               // [Hv * nchunks][2][64][64]: dL and dAqk of each chunk
 };
 
 // dtype: 0 = fp32, 1 = bf16
@@ -184,8 +185,9 @@ hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s, bool ba
 hipError_t launch_prefix_merge(int K, int V, const PrefixMergeArgs& a, hipStream_t s);
 hipError_t launch_recurrent(int K, int V, int dtype, const RecurrentArgs& a, hipStream_t s);
 // Backward stage: 0 prep, 6 forward state scan (fp32), 1 reverse state scan,
-// 2 chunk-local backward, 3 grouped heads + L2Norm, 4 gate/sigmoid with block
-// partial sums (into `part`), 5 the sums of those partials.
+// 2 chunk-local backward (products), 7 its pair sums, 3 grouped heads +
+// L2Norm, 4 gate/sigmoid with block partial sums (into `part`), 5 the sums of
+// those partials.
 hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int64_t tokens, float* part,
                       hipStream_t s);
 constexpr int BWD_GATE_TOKENS = 512;   // tokens per gate workgroup (one partial each)
