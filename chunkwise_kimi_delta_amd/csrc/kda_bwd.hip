@@ -289,68 +289,117 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
   }
 }
 
+// acc += a * b on the fp32 matrix cores (16 x 16 x 4 per instruction)
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // ------------------------------------------------------ forward state scan
+// Tiles of a R x V state-shaped output (R = 64 or K rows, V columns), eight
+// waves: wave w owns tiles w * TPW + t (t < TPW), so that all its tiles lie in
+// one block of 16 rows (rb) and consecutive column blocks (cb).
+template <int R, int V>
+struct STiles {
+  static constexpr int NCB = V / 16, NT = (R / 16) * NCB, TPW = NT / (NTH / 64);
+  static_assert(NCB % TPW == 0 || TPW % NCB == 0, "a wave's tiles share one row block");
+  int rb, cb0, r16, q;
+  __device__ explicit STiles(int tid) : r16(tid & 15), q((tid >> 4) & 3) {
+    const int T0 = (tid >> 6) * TPW;
+    rb = T0 / NCB;
+    cb0 = T0 % NCB;
+  }
+};
+static_assert(STiles<128, 128>::TPW == 8 && STiles<64, 128>::TPW == 4 && STiles<64, 64>::TPW == 2,
+              "tile counts per wave");
+
 // The chunk-entry states for the backward, in fp32 from the fp32 records:
 // h <- D h + kg^T (u - w h), every entry state stored.  One workgroup per
-// (sequence, head, 32 columns).
+// (sequence, head); h lives in LDS, the products run on the fp32 matrix cores
+// (wave w: row block w of the update, v_new tiles of row block w / 2).
 template <int KD, int VD>
 __global__ __launch_bounds__(NTH) void bwd_state_kernel(BwdArgs a) {
-  constexpr int TW = 32, LT = TW + 1, LK = KD + 1;
-  __shared__ float sH[KD * LT], sVN[BT * LT], sW[BT * LK], sKG[BT * LK];
+  constexpr int LH = VD + 4;
+  __shared__ __attribute__((aligned(16))) float sH[KD * LH];
+  __shared__ __attribute__((aligned(16))) float sVN[BT * LH];
   __shared__ float sGC[KD];
+  using TV = STiles<BT, VD>;   // v_new
+  using TH = STiles<KD, VD>;   // h
+  static_assert(TH::TPW <= TH::NCB && TV::TPW <= TV::NCB, "one row block per wave");
   constexpr BwdRec R = bwd_rec(KD, VD);
-  constexpr int NT = VD / TW;
-  const int tile = blockIdx.x % NT, h = (blockIdx.x / NT) % a.Hv, n = blockIdx.x / (NT * a.Hv);
-  const int v0 = tile * TW, tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
+  const int h = blockIdx.x % a.Hv, n = blockIdx.x / a.Hv, tid = threadIdx.x;
+  const TV tv(tid);
+  const TH th(tid);
   int64_t tok0s;
   int len;
   seq_range(a.seq, n, tok0s, len);
   const int nck = (len + BT - 1) / BT;
   const int cb = chunk_base(a.seq, n);
-  for (int i = tid; i < KD * TW; i += NTH) {
-    const int r = i / TW, c = i % TW;
-    sH[r * LT + c] = a.h0 ? a.h0[(((int64_t)n * a.Hv + h) * KD + r) * VD + v0 + c] : 0.f;
-  }
+  for (int i = tid; i < KD * VD; i += NTH)
+    sH[(i / VD) * LH + i % VD] = a.h0 ? a.h0[((int64_t)n * a.Hv + h) * (KD * VD) + i] : 0.f;
   __syncthreads();
   for (int c = 0; c < nck; ++c) {
     const int64_t slot = (int64_t)h * a.nchunks + cb + c;
     const float* rec = a.rec + slot * (int64_t)(R.bytes / 4);
     const int C = min(BT, len - c * BT);
     float* dst = a.h_store_w + slot * (int64_t)(KD * VD);
+    // this wave's h tiles: kept for the update, stored as the chunk-entry state
+    f32x4 hold[TH::TPW];
 #pragma unroll
-    for (int i = tid; i < KD * TW; i += NTH) dst[(i / TW) * VD + v0 + i % TW] = sH[(i / TW) * LT + i % TW];
+    for (int t = 0; t < TH::TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = 16 * th.rb + 4 * th.q + e, j = 16 * (th.cb0 + t) + th.r16;
+        hold[t][e] = sH[kk * LH + j];
+        dst[kk * VD + j] = hold[t][e];
+      }
     if (tid < KD) sGC[tid] = rec[R.G + (C - 1) * KD + tid];
-    __syncthreads();
-#pragma unroll 8
-    for (int i = tid; i < BT * KD; i += NTH) {
-      const int r = i / KD, cc = i % KD;
-      sW[r * LK + cc] = rec[R.w + i];
-      sKG[r * LK + cc] = rec[R.kn + i] * ex2(sGC[cc] - rec[R.G + i]);
-    }
-    __syncthreads();
-    {  // v_new = u - w h
-      float acc[BT / RS][2];
-      zero(acc);
-      mm(acc, KD, tm, tn, [&](int i, int kk) { return sW[i * LK + kk]; }, [&](int kk, int j) { return sH[kk * LT + j]; });
+    {  // v_new = u - w h  -> sVN
+      f32x4 acc[TV::TPW];
 #pragma unroll
-      for (int x = 0; x < BT / RS; ++x)
+      for (int t = 0; t < TV::TPW; ++t) acc[t] = zero4();
+      const float* wrow = rec + R.w + (16 * tv.rb + tv.r16) * KD + 4 * tv.q;
+      for (int kk = 0; kk < KD; kk += 16) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(wrow + kk);
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const int i = tm + RS * x, j = tn + 16 * y;
-          sVN[i * LT + j] = rec[R.u + i * VD + v0 + j] - acc[x][y];
+        for (int t = 0; t < TV::TPW; ++t)
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            acc[t] = mfma4(av[p], sH[(kk + 4 * tv.q + p) * LH + 16 * (tv.cb0 + t) + tv.r16], acc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < TV::TPW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * tv.rb + 4 * tv.q + e, j = 16 * (tv.cb0 + t) + tv.r16;
+          sVN[i * LH + j] = rec[R.u + i * VD + j] - acc[t][e];
         }
     }
     __syncthreads();
-    {  // h = D h + kg^T v_new
-      float acc[KD / RS][2];
-      zero(acc);
-      mm(acc, BT, tm, tn, [&](int kk, int r) { return sKG[r * LK + kk]; }, [&](int r, int j) { return sVN[r * LT + j]; });
+    {  // h = D h + kg^T v_new, kg = k e^(G_C - G) (A operand: kg^T rows of this wave's block)
+      f32x4 acc[TH::TPW];
 #pragma unroll
-      for (int x = 0; x < KD / RS; ++x)
+      for (int t = 0; t < TH::TPW; ++t) acc[t] = zero4();
+      const int kk = 16 * th.rb + th.r16;
+      const float gck = sGC[kk];
+      for (int r0 = 0; r0 < BT; r0 += 16) {
+        float av[4];
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const int kk = tm + RS * x, j = tn + 16 * y;
-          sH[kk * LT + j] = ex2(sGC[kk]) * sH[kk * LT + j] + acc[x][y];
+        for (int p = 0; p < 4; ++p) {
+          const int r = r0 + 4 * th.q + p;
+          av[p] = rec[R.kn + r * KD + kk] * ex2(gck - rec[R.G + r * KD + kk]);
+        }
+#pragma unroll
+        for (int t = 0; t < TH::TPW; ++t)
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            acc[t] = mfma4(av[p], sVN[(r0 + 4 * th.q + p) * LH + 16 * (th.cb0 + t) + th.r16], acc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < TH::TPW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k2 = 16 * th.rb + 4 * th.q + e, j = 16 * (th.cb0 + t) + th.r16;
+          sH[k2 * LH + j] = ex2(sGC[k2]) * hold[t][e] + acc[t][e];
         }
     }
     __syncthreads();
@@ -358,96 +407,124 @@ __global__ __launch_bounds__(NTH) void bwd_state_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------ reverse state scan
+// dh over the chunks in reverse: dv_new = Aqk^T do + kg dh',
+// dh = qg^T do + D dh' - w^T dv_new, every chunk's exit gradient stored.  One
+// workgroup per (sequence, head), dh in LDS, fp32 matrix cores as above.
 template <int KD, int VD, typename IT>
 __global__ __launch_bounds__(NTH) void bwd_scan_kernel(BwdArgs a) {
-  constexpr int TW = 32, LT = TW + 1, LK = KD + 1;
-  __shared__ float sDH[KD * LT], sDo[BT * LT], sDV[BT * LT];
-  __shared__ float sM1[BT * LK], sM2[BT * LK], sAq[BT * 65];
+  constexpr int LH = VD + 4;
+  __shared__ __attribute__((aligned(16))) float sDH[KD * LH];
+  __shared__ __attribute__((aligned(16))) float sDV[BT * LH];
+  __shared__ __attribute__((aligned(16))) float sDo[BT * LH];
   __shared__ float sGC[KD];
+  using TV = STiles<BT, VD>;
+  using TH = STiles<KD, VD>;
+  static_assert(TH::TPW <= TH::NCB && TV::TPW <= TV::NCB, "one row block per wave");
   constexpr BwdRec R = bwd_rec(KD, VD);
-  constexpr int NT = VD / TW;
-  const int tile = blockIdx.x % NT, h = (blockIdx.x / NT) % a.Hv, n = blockIdx.x / (NT * a.Hv);
-  const int v0 = tile * TW, tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
+  const int h = blockIdx.x % a.Hv, n = blockIdx.x / a.Hv, tid = threadIdx.x;
+  const TV tv(tid);
+  const TH th(tid);
   int64_t tok0s;
   int len;
   seq_range(a.seq, n, tok0s, len);
   const int nck = (len + BT - 1) / BT;
   const int cb = chunk_base(a.seq, n);
   const IT* dout = static_cast<const IT*>(a.dout);
-  // dh' of the last chunk: the final state's gradient
-  for (int i = tid; i < KD * TW; i += NTH) {
-    const int r = i / TW, c = i % TW;
-    sDH[r * LT + c] = a.dht ? a.dht[(((int64_t)n * a.Hv + h) * KD + r) * VD + v0 + c] : 0.f;
-  }
+  for (int i = tid; i < KD * VD; i += NTH)   // dh' of the last chunk: the final state's gradient
+    sDH[(i / VD) * LH + i % VD] = a.dht ? a.dht[((int64_t)n * a.Hv + h) * (KD * VD) + i] : 0.f;
   __syncthreads();
   for (int c = nck - 1; c >= 0; --c) {
     const int64_t slot = (int64_t)h * a.nchunks + cb + c;
     const float* rec = a.rec + slot * (int64_t)(R.bytes / 4);
     const int C = min(BT, len - c * BT);
     const int64_t tok0 = tok0s + (int64_t)c * BT;
-    if (a.dh_store) {   // (the backward summary keeps none)
-      float* dst = a.dh_store + slot * (int64_t)(KD * VD);
+    f32x4 dold[TH::TPW];
 #pragma unroll
-      for (int i = tid; i < KD * TW; i += NTH) dst[(i / TW) * VD + v0 + i % TW] = sDH[(i / TW) * LT + i % TW];
-    }
+    for (int t = 0; t < TH::TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = 16 * th.rb + 4 * th.q + e, j = 16 * (th.cb0 + t) + th.r16;
+        dold[t][e] = sDH[kk * LH + j];
+        if (a.dh_store) a.dh_store[slot * (int64_t)(KD * VD) + kk * VD + j] = dold[t][e];
+      }
     if (tid < KD) sGC[tid] = rec[R.G + (C - 1) * KD + tid];
-    __syncthreads();
-    // kg = k e^(G_C - G), Aqk, do
-#pragma unroll 8
-    for (int i = tid; i < BT * KD; i += NTH) {
-      const int r = i / KD, cc = i % KD;
-      sM1[r * LK + cc] = rec[R.kn + i] * ex2(sGC[cc] - rec[R.G + i]);
-    }
-#pragma unroll 8
-    for (int i = tid; i < BT * BT; i += NTH) sAq[(i / BT) * 65 + i % BT] = rec[R.aqk + i];
-#pragma unroll
-    for (int i = tid; i < BT * TW; i += NTH) {
-      const int r = i / TW, cc = i % TW;
-      sDo[r * LT + cc] = r < C ? ldf(dout + ((tok0 + r) * a.Hv + h) * VD + v0 + cc) : 0.f;
+    for (int i = tid; i < BT * VD; i += NTH) {
+      const int r = i / VD, cc = i % VD;
+      sDo[r * LH + cc] = r < C ? ldf(dout + ((tok0 + r) * a.Hv + h) * VD + cc) : 0.f;
     }
     __syncthreads();
-    {  // dv_new = Aqk^T do + kg dh'
-      float acc[BT / RS][2];
-      zero(acc);
-      mm(acc, BT, tm, tn, [&](int i, int r) { return sAq[r * 65 + i]; }, [&](int r, int j) { return sDo[r * LT + j]; });
-      mm(acc, KD, tm, tn, [&](int i, int kk) { return sM1[i * LK + kk]; }, [&](int kk, int j) { return sDH[kk * LT + j]; });
+    {  // dv_new = Aqk^T do + kg dh'  -> sDV
+      f32x4 acc[TV::TPW];
 #pragma unroll
-      for (int x = 0; x < BT / RS; ++x)
+      for (int t = 0; t < TV::TPW; ++t) acc[t] = zero4();
+      const int i = 16 * tv.rb + tv.r16;
+      for (int r0 = 0; r0 < BT; r0 += 16) {
+        float av[4];
 #pragma unroll
-        for (int y = 0; y < 2; ++y) sDV[(tm + RS * x) * LT + tn + 16 * y] = acc[x][y];
+        for (int p = 0; p < 4; ++p) av[p] = rec[R.aqk + (r0 + 4 * tv.q + p) * BT + i];
+#pragma unroll
+        for (int t = 0; t < TV::TPW; ++t)
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            acc[t] = mfma4(av[p], sDo[(r0 + 4 * tv.q + p) * LH + 16 * (tv.cb0 + t) + tv.r16], acc[t]);
+      }
+      const float* knr = rec + R.kn + i * KD + 4 * tv.q;
+      const float* gr = rec + R.G + i * KD + 4 * tv.q;
+      for (int kk = 0; kk < KD; kk += 16) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(knr + kk);
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(gr + kk);
+        float av[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) av[p] = kv[p] * ex2(sGC[kk + 4 * tv.q + p] - gv[p]);
+#pragma unroll
+        for (int t = 0; t < TV::TPW; ++t)
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            acc[t] = mfma4(av[p], sDH[(kk + 4 * tv.q + p) * LH + 16 * (tv.cb0 + t) + tv.r16], acc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < TV::TPW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sDV[(16 * tv.rb + 4 * tv.q + e) * LH + 16 * (tv.cb0 + t) + tv.r16] = acc[t][e];
     }
     __syncthreads();
-    // qg = s q e^G and w
-#pragma unroll 8
-    for (int i = tid; i < BT * KD; i += NTH) {
-      const int r = i / KD, cc = i % KD;
-      sM1[r * LK + cc] = a.scale * rec[R.qn + i] * ex2(rec[R.G + i]);
-      sM2[r * LK + cc] = rec[R.w + i];
-    }
-    __syncthreads();
-    {  // dh = qg^T do + D dh' - w^T dv_new
-      float acc[KD / RS][2];
-      zero(acc);
-      mm(acc, BT, tm, tn, [&](int kk, int r) { return sM1[r * LK + kk]; }, [&](int r, int j) { return sDo[r * LT + j]; });
+    {  // dh = qg^T do + D dh' - w^T dv_new (A operands: qg^T and w^T rows of this wave's block)
+      f32x4 acc[TH::TPW];
 #pragma unroll
-      for (int x = 0; x < KD / RS; ++x)
+      for (int t = 0; t < TH::TPW; ++t) acc[t] = zero4();
+      const int kk = 16 * th.rb + th.r16;
+      for (int r0 = 0; r0 < BT; r0 += 16) {
+        float aq[4], aw[4];
 #pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = -acc[x][y];
-      mm(acc, BT, tm, tn, [&](int kk, int r) { return sM2[r * LK + kk]; }, [&](int r, int j) { return sDV[r * LT + j]; });
-      __syncthreads();
+        for (int p = 0; p < 4; ++p) {
+          const int r = r0 + 4 * th.q + p;
+          aq[p] = a.scale * rec[R.qn + r * KD + kk] * ex2(rec[R.G + r * KD + kk]);
+          aw[p] = -rec[R.w + r * KD + kk];
+        }
 #pragma unroll
-      for (int x = 0; x < KD / RS; ++x)
+        for (int t = 0; t < TH::TPW; ++t)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const int kk = tm + RS * x, j = tn + 16 * y;
-          sDH[kk * LT + j] = ex2(sGC[kk]) * sDH[kk * LT + j] - acc[x][y];
+          for (int p = 0; p < 4; ++p) {
+            const int r = r0 + 4 * th.q + p, j = 16 * (th.cb0 + t) + th.r16;
+            acc[t] = mfma4(aq[p], sDo[r * LH + j], acc[t]);
+            acc[t] = mfma4(aw[p], sDV[r * LH + j], acc[t]);
+          }
+      }
+      // (every wave finished reading dh' before the barrier above)
+#pragma unroll
+      for (int t = 0; t < TH::TPW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k2 = 16 * th.rb + 4 * th.q + e, j = 16 * (th.cb0 + t) + th.r16;
+          sDH[k2 * LH + j] = ex2(sGC[k2]) * dold[t][e] + acc[t][e];
         }
     }
     __syncthreads();
   }
   if (a.dh0)
-    for (int i = tid; i < KD * TW; i += NTH)
-      a.dh0[(((int64_t)n * a.Hv + h) * KD + i / TW) * VD + v0 + i % TW] = sDH[(i / TW) * LT + i % TW];
+    for (int i = tid; i < KD * VD; i += NTH)
+      a.dh0[((int64_t)n * a.Hv + h) * (KD * VD) + i] = sDH[(i / VD) * LH + i % VD];
 }
 
 // --------------------------------------------------------- chunk backward
@@ -469,9 +546,6 @@ struct Own {
 };
 static_assert(Own<64>::TPW == 2 && Own<128>::TPW == 4, "eight waves cover a 64-row output");
 
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 // acc += A (64 x kr) * B (kr x N), both read through an LDS staging buffer KB
 // reduction indices at a time (A as [row][k], B as [col][k], so that a lane
@@ -1225,7 +1299,7 @@ __global__ __launch_bounds__(KD) void bwd_gate_sum_kernel(BwdArgs a, int nblk, c
 hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int64_t tokens, float* part,
                       hipStream_t s) {
   const long nb_chunk = (long)a.nchunks * a.Hv;
-  const long nb_scan = (long)a.seq.N * a.Hv * (V / 32);
+  const long nb_scan = (long)a.seq.N * a.Hv;
   const long nb_qk = (long)tokens * a.Hk;
   const int nblk = (int)((tokens + GATE_TOKENS - 1) / GATE_TOKENS);
   if (nb_chunk > 0x7fffffffL || nb_qk > 0x7fffffffL || (long)nblk * a.Hv > 0x7fffffffL) return hipErrorInvalidValue;
