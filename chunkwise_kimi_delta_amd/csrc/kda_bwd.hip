@@ -137,158 +137,6 @@ __device__ __forceinline__ ChunkPos chunk_pos(const SeqInfo& s, int gc, int h, i
   return p;
 }
 
-// ------------------------------------------------------------------ prep
-template <int KD, int VD, typename IT>
-__global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
-  constexpr int LK = KD + 1, LX = (KD > VD ? KD : VD) + 1;
-  __shared__ float sG[BT * LK], sK[BT * LK], sX[BT * LX];
-  __shared__ float sL[BT * 65], sA[BT * 65];
-  __shared__ float sB[BT];
-  constexpr BwdRec R = bwd_rec(KD, VD);
-  const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
-  const ChunkPos P = chunk_pos(a.seq, gc, h, a.nchunks);
-  const int hk = h / (a.Hv / a.Hk);
-  const int tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
-  float* rec = a.rec + P.slot * (int64_t)(R.bytes / 4);
-  const IT* q = static_cast<const IT*>(a.q);
-  const IT* k = static_cast<const IT*>(a.k);
-  const IT* g = static_cast<const IT*>(a.g);
-  const IT* bt = static_cast<const IT*>(a.beta);
-  const IT* v = static_cast<const IT*>(a.v);
-  const bool gik = a.flags & F_GATE, l2 = a.flags & F_L2;
-  const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;
-  const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
-
-  // rows r = tid / 8, channels CPT * (tid % 8) .. +CPT-1
-  {
-    const int r = tid >> 3, part = tid & 7;
-    constexpr int CPT = KD / 8;
-    const bool live = r < P.C;
-    float kr[CPT], qr[CPT];
-    float skk = 0.f, sqq = 0.f;
-#pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      const int c = part * CPT + e;
-      kr[e] = live ? ldf(k + ((P.tok0 + r) * a.Hk + hk) * KD + c) : 0.f;
-      qr[e] = live ? ldf(q + ((P.tok0 + r) * a.Hk + hk) * KD + c) : 0.f;
-      skk += kr[e] * kr[e];
-      sqq += qr[e] * qr[e];
-      float gv = live ? ldf(g + ((P.tok0 + r) * a.Hv + h) * KD + c) : 0.f;
-      if (live && gik) gv = -Aexp * softplus_f(gv + (a.dt_bias ? a.dt_bias[h * KD + c] : 0.f));
-      if (live && gv < lb) gv = lb;
-      sG[r * LK + c] = gv * LOG2E_F;          // log2 units
-    }
-    for (int m = 1; m < 8; m <<= 1) {
-      skk += __shfl_xor(skk, m);
-      sqq += __shfl_xor(sqq, m);
-    }
-    const float rk = live ? (l2 ? 1.f / sqrtf(skk + a.eps) : 1.f) : 0.f;
-    const float rq = live ? (l2 ? 1.f / sqrtf(sqq + a.eps) : 1.f) : 0.f;
-#pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      const int c = part * CPT + e;
-      sK[r * LK + c] = kr[e] * rk;
-      sX[r * LX + c] = qr[e] * rq;
-    }
-    if (part == 0) {
-      float b = live ? ldf(bt + (P.tok0 + r) * a.Hv + h) : 0.f;
-      if (live && (a.flags & F_SIGMOID)) b = sigmoid_f(b);
-      sB[r] = b;
-    }
-  }
-  __syncthreads();
-  // in-chunk cumsum of the decay (log2 units); rows past the end keep the last value
-  if (tid < KD) {
-    float run = 0.f;
-    for (int r = 0; r < BT; ++r) {
-      run += sG[r * LK + tid];
-      sG[r * LK + tid] = run;
-    }
-  }
-  __syncthreads();
-  // store G, normalised k and q, beta
-#pragma unroll 8
-  for (int i = tid; i < BT * KD; i += NTH) {
-    const int r = i / KD, c = i % KD;
-    rec[R.G + i] = sG[r * LK + c];
-    rec[R.kn + i] = sK[r * LK + c];
-    rec[R.qn + i] = sX[r * LX + c];
-  }
-  if (tid < BT) rec[R.beta + tid] = sB[tid];
-  // L (strict lower, beta-scaled) and Aqk (lower with diagonal, scaled): pair by pair
-  for (int p = tid; p < BT * (BT + 1) / 2; p += NTH) {
-    int i = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-    while (i * (i + 1) / 2 > p) --i;
-    while ((i + 1) * (i + 2) / 2 <= p) ++i;
-    const int j = p - i * (i + 1) / 2;
-    float kd = 0.f, aq = 0.f;
-    for (int c = 0; c < KD; ++c) {
-      const float f = ex2(sG[i * LK + c] - sG[j * LK + c]);
-      const float kj = sK[j * LK + c] * f;
-      kd += sK[i * LK + c] * kj;
-      aq += sX[i * LX + c] * kj;
-    }
-    sL[i * 65 + j] = i > j ? sB[i] * kd : 0.f;
-    rec[R.aqk + i * BT + j] = a.scale * aq;
-    if (i != j) {
-      sL[j * 65 + i] = 0.f;
-      rec[R.aqk + j * BT + i] = 0.f;
-    }
-  }
-  __syncthreads();
-  // A = (I + L)^-1 by forward substitution: eight lanes per column (each sums
-  // every eighth term; the lanes of a column are adjacent in one wave, so the
-  // row just written is visible to them without a barrier)
-  {
-    const int j = tid >> 3, part = tid & 7;
-    for (int i = 0; i < BT; ++i) {
-      float s = 0.f;
-      for (int m = j + part; m < i; m += 8) s += sL[i * 65 + m] * sA[m * 65 + j];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      if (part == 0) sA[i * 65 + j] = i > j ? -s : (i == j ? 1.f : 0.f);
-    }
-  }
-  // beta v into sX (q is stored already)
-  __syncthreads();
-#pragma unroll 8
-  for (int i = tid; i < BT * VD; i += NTH) {
-    const int r = i / VD, c = i % VD;
-    sX[r * LX + c] = r < P.C ? sB[r] * ldf(v + ((P.tok0 + r) * a.Hv + h) * VD + c) : 0.f;
-  }
-#pragma unroll 8
-  for (int i = tid; i < BT * BT; i += NTH) rec[R.A + i] = sA[(i / BT) * 65 + i % BT];
-  __syncthreads();
-  {  // u = A (beta v)
-    float acc[BT / RS][VD / 16];
-    zero(acc);
-    mm(acc, BT, tm, tn, [&](int i, int j) { return sA[i * 65 + j]; },
-       [&](int j, int c) { return sX[j * LX + c]; });
-#pragma unroll
-    for (int x = 0; x < BT / RS; ++x)
-#pragma unroll
-      for (int y = 0; y < VD / 16; ++y) rec[R.u + (tm + RS * x) * VD + tn + 16 * y] = acc[x][y];
-  }
-  __syncthreads();
-#pragma unroll 8
-  for (int i = tid; i < BT * KD; i += NTH) {
-    const int r = i / KD, c = i % KD;
-    sX[r * LX + c] = sB[r] * sK[r * LK + c] * ex2(sG[r * LK + c]);
-  }
-  __syncthreads();
-  {  // w = A (beta k e^G)
-    float acc[BT / RS][KD / 16];
-    zero(acc);
-    mm(acc, BT, tm, tn, [&](int i, int j) { return sA[i * 65 + j]; },
-       [&](int j, int c) { return sX[j * LX + c]; });
-#pragma unroll
-    for (int x = 0; x < BT / RS; ++x)
-#pragma unroll
-      for (int y = 0; y < KD / 16; ++y) rec[R.w + (tm + RS * x) * KD + tn + 16 * y] = acc[x][y];
-  }
-}
-
 // acc += a * b on the fp32 matrix cores (16 x 16 x 4 per instruction)
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -525,6 +373,292 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(BwdArgs a) {
   if (a.dh0)
     for (int i = tid; i < KD * VD; i += NTH)
       a.dh0[((int64_t)n * a.Hv + h) * (KD * VD) + i] = sDH[(i / VD) * LH + i % VD];
+}
+
+// ------------------------------------------------------------------ prep
+// The fp32 record of one (chunk, head): gate, norms, sigmoid, the in-chunk
+// cumsum G (log2 units), L = tril(beta k k^T decayed), Aqk, A = (I + L)^-1,
+// u = A (beta v), w = A (beta k 2^G).  L and Aqk are formed on the fp32 matrix
+// cores in 16 x 16 tiles: a tile below the diagonal blocks against the first
+// row r of its row block (factors 2^(G_i - G_r) and 2^(G_r - G_j), both <= 1);
+// a diagonal tile in four split levels (blocks of 16, 8, 4 and 2 rows: the
+// pairs with i in the upper and j in the lower half of one block, against
+// that upper half's first row), every pair i > j meeting exactly one level.
+template <int KD, int VD, typename IT>
+__global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int MX = KD > VD ? KD : VD;
+  constexpr int LX = MX + 4, LS = BT + 4;
+  __shared__ __attribute__((aligned(16))) float sG[BT * LX];
+  __shared__ __attribute__((aligned(16))) float sK[BT * LX];
+  __shared__ __attribute__((aligned(16))) float sX[BT * LX];   // q, then beta v, then beta k 2^G
+  __shared__ __attribute__((aligned(16))) float sL[BT * LS];
+  __shared__ __attribute__((aligned(16))) float sA[BT * LS];
+  __shared__ float sB[BT], sDiag[BT];
+  constexpr BwdRec R = bwd_rec(KD, VD);
+  const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
+  const ChunkPos P = chunk_pos(a.seq, gc, h, a.nchunks);
+  const int hk = h / (a.Hv / a.Hk);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
+  float* rec = a.rec + P.slot * (int64_t)(R.bytes / 4);
+  const IT* q = static_cast<const IT*>(a.q);
+  const IT* k = static_cast<const IT*>(a.k);
+  const IT* g = static_cast<const IT*>(a.g);
+  const IT* bt = static_cast<const IT*>(a.beta);
+  const IT* v = static_cast<const IT*>(a.v);
+  const bool gik = a.flags & F_GATE, l2 = a.flags & F_L2;
+  const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;
+  const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
+
+  // ---- gate, norms, beta: rows r = tid / 8, channels CPT * (tid % 8) .. +CPT-1
+  {
+    const int r = tid >> 3, part = tid & 7;
+    constexpr int CPT = KD / 8;
+    const bool live = r < P.C;
+    float kr[CPT], qr[CPT];
+    float skk = 0.f, sqq = 0.f, sqk = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      const int c = part * CPT + e;
+      kr[e] = live ? ldf(k + ((P.tok0 + r) * a.Hk + hk) * KD + c) : 0.f;
+      qr[e] = live ? ldf(q + ((P.tok0 + r) * a.Hk + hk) * KD + c) : 0.f;
+      skk += kr[e] * kr[e];
+      sqq += qr[e] * qr[e];
+      sqk += qr[e] * kr[e];
+      float gv = live ? ldf(g + ((P.tok0 + r) * a.Hv + h) * KD + c) : 0.f;
+      if (live && gik) gv = -Aexp * softplus_f(gv + (a.dt_bias ? a.dt_bias[h * KD + c] : 0.f));
+      if (live && gv < lb) gv = lb;
+      sG[r * LX + c] = gv * LOG2E_F;          // log2 units
+    }
+    for (int m = 1; m < 8; m <<= 1) {
+      skk += __shfl_xor(skk, m);
+      sqq += __shfl_xor(sqq, m);
+      sqk += __shfl_xor(sqk, m);
+    }
+    const float rk = live ? (l2 ? 1.f / sqrtf(skk + a.eps) : 1.f) : 0.f;
+    const float rq = live ? (l2 ? 1.f / sqrtf(sqq + a.eps) : 1.f) : 0.f;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      const int c = part * CPT + e;
+      sK[r * LX + c] = kr[e] * rk;
+      sX[r * LX + c] = qr[e] * rq;
+    }
+    if (part == 0) {
+      float b = live ? ldf(bt + (P.tok0 + r) * a.Hv + h) : 0.f;
+      if (live && (a.flags & F_SIGMOID)) b = sigmoid_f(b);
+      sB[r] = b;
+      sDiag[r] = a.scale * rq * rk * sqk;      // Aqk_rr (decay factor 1)
+    }
+  }
+  __syncthreads();
+  {  // in-chunk cumsum of the decay: KD channels x NSG segments of SR rows
+    constexpr int NSG = NTH / KD, SR = BT / NSG;
+    float* sTot = sL;   // [NSG][KD] (sL unused until the tiles)
+    const int cc = tid % KD, sg = tid / KD, r0 = sg * SR;
+    float x[SR], run = 0.f;
+#pragma unroll
+    for (int r = 0; r < SR; ++r) {
+      run += sG[(r0 + r) * LX + cc];
+      x[r] = run;
+    }
+    sTot[sg * KD + cc] = run;
+    __syncthreads();
+    float off = 0.f;
+    for (int s2 = 0; s2 < sg; ++s2) off += sTot[s2 * KD + cc];
+#pragma unroll
+    for (int r = 0; r < SR; ++r) sG[(r0 + r) * LX + cc] = x[r] + off;
+  }
+  __syncthreads();
+  // store G, normalised k and q, beta
+#pragma unroll
+  for (int s2 = 0; s2 < BT * KD / 4 / NTH; ++s2) {
+    const int i = 4 * (tid + NTH * s2), r = i / KD, c = i % KD;
+    *reinterpret_cast<f32x4*>(rec + R.G + i) = *reinterpret_cast<const f32x4*>(&sG[r * LX + c]);
+    *reinterpret_cast<f32x4*>(rec + R.kn + i) = *reinterpret_cast<const f32x4*>(&sK[r * LX + c]);
+    *reinterpret_cast<f32x4*>(rec + R.qn + i) = *reinterpret_cast<const f32x4*>(&sX[r * LX + c]);
+  }
+  if (tid < BT) rec[R.beta + tid] = sB[tid];
+
+  // ---- L (beta-scaled, strict lower) and Aqk (scaled, lower): 6 tiles below
+  // the diagonal blocks and 4 x 4 (diagonal tile, level) jobs, spread over the waves
+  float* aqk = rec + R.aqk;
+  for (int job = wave; job < 22; job += NTH / 64) {
+    f32x4 accL = zero4(), accQ = zero4();
+    if (job < 6) {
+      const int I = job < 1 ? 1 : job < 3 ? 2 : 3, J = job < 1 ? 0 : job < 3 ? job - 1 : job - 3;
+      const int ri = 16 * I + r16, rj = 16 * J + r16, rr = 16 * I;
+      for (int kk = 0; kk < KD; kk += 16) {
+        const int c0 = kk + 4 * quad;
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(&sG[ri * LX + c0]);
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(&sG[rj * LX + c0]);
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(&sG[rr * LX + c0]);
+        const f32x4 ki = *reinterpret_cast<const f32x4*>(&sK[ri * LX + c0]);
+        const f32x4 qi = *reinterpret_cast<const f32x4*>(&sX[ri * LX + c0]);
+        const f32x4 kj = *reinterpret_cast<const f32x4*>(&sK[rj * LX + c0]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float fa = ex2(gi[p] - gr[p]), b = kj[p] * ex2(gr[p] - gj[p]);
+          accL = mfma4(ki[p] * fa, b, accL);
+          accQ = mfma4(qi[p] * fa, b, accQ);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * I + 4 * quad + e, j = 16 * J + r16;
+        sL[i * LS + j] = sB[i] * accL[e];
+        aqk[i * BT + j] = a.scale * accQ[e];
+      }
+    } else {
+      const int I = (job - 6) >> 2, lv = (job - 6) & 3;
+      const int y = r16, ry = 16 * I + y;
+      const bool up = (y >> lv) & 1;
+      const int rref = 16 * I + ((y >> (lv + 1)) << (lv + 1)) + (1 << lv);
+      for (int kk = 0; kk < KD; kk += 16) {
+        const int c0 = kk + 4 * quad;
+        const f32x4 gy = *reinterpret_cast<const f32x4*>(&sG[ry * LX + c0]);
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(&sG[rref * LX + c0]);
+        const f32x4 ky = *reinterpret_cast<const f32x4*>(&sK[ry * LX + c0]);
+        const f32x4 qy = *reinterpret_cast<const f32x4*>(&sX[ry * LX + c0]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float f = ex2(up ? gy[p] - gr[p] : gr[p] - gy[p]);
+          const float fk = ky[p] * f;
+          accL = mfma4(fk, fk, accL);
+          accQ = mfma4(qy[p] * f, fk, accQ);
+        }
+      }
+      // entries (i upper, j lower) of one block at this level
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int il = 4 * quad + e, jl = r16;
+        if ((il >> (lv + 1)) == (jl >> (lv + 1)) && ((il >> lv) & 1) && !((jl >> lv) & 1)) {
+          const int i = 16 * I + il, j = 16 * I + jl;
+          sL[i * LS + j] = sB[i] * accL[e];
+          aqk[i * BT + j] = a.scale * accQ[e];
+        }
+      }
+    }
+  }
+  // diagonal and upper entries: L zero; Aqk its diagonal, zero above
+  for (int idx = tid; idx < BT * BT; idx += NTH) {
+    const int i = idx / BT, j = idx % BT;
+    if (j < i) continue;
+    sL[i * LS + j] = 0.f;
+    aqk[i * BT + j] = i == j ? sDiag[i] : 0.f;
+  }
+  __syncthreads();
+
+  // ---- A = (I + L)^-1: diagonal 16 x 16 blocks by substitution (16 lanes of
+  // waves 0..3, one column each), then the blocks below them column block by
+  // column block, A_IJ = -A_II sum_{J <= m < I} L_Im A_mJ, on the matrix cores
+  if (wave < 4 && quad == 0) {
+    const int b = wave, jj = r16;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = (r == jj) ? 1.f : 0.f;
+#pragma unroll
+      for (int kq = 0; kq < r; ++kq) s -= sL[(16 * b + r) * LS + 16 * b + kq] * x[kq];
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sA[(16 * b + r) * LS + 16 * b + jj] = x[r];
+  }
+  for (int idx = tid; idx < 6 * 256; idx += NTH) {   // the blocks above the diagonal are zero
+    const int t = idx >> 8, e = idx & 255;
+    const int I = t < 3 ? 0 : (t < 5 ? 1 : 2);
+    const int J = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
+    sA[(16 * I + (e >> 4)) * LS + 16 * J + (e & 15)] = 0.f;
+  }
+  __syncthreads();
+  if (wave < 3) {
+    const int J = wave;
+    f32x4 col[4];
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+      if (m == J)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) col[m][e] = sA[(16 * J + 4 * quad + e) * LS + 16 * J + r16];
+#pragma unroll
+    for (int I = 1; I < 4; ++I) {
+      if (I <= J) continue;
+      f32x4 x = zero4();
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        if (m < J || m >= I) continue;
+        const f32x4 lrow = *reinterpret_cast<const f32x4*>(&sL[(16 * I + r16) * LS + 16 * m + 4 * quad]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) x = mfma4(lrow[p], col[m][p], x);
+      }
+      const f32x4 arow = *reinterpret_cast<const f32x4*>(&sA[(16 * I + r16) * LS + 16 * I + 4 * quad]);
+      f32x4 y = zero4();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) y = mfma4(arow[p], x[p], y);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        col[I][e] = -y[e];
+        sA[(16 * I + 4 * quad + e) * LS + 16 * J + r16] = -y[e];
+      }
+    }
+  }
+  // beta v into sX (q is no longer needed)
+#pragma unroll 4
+  for (int i = tid; i < BT * VD; i += NTH) {
+    const int r = i / VD, c = i % VD;
+    sX[r * LX + c] = r < P.C ? sB[r] * ldf(v + ((P.tok0 + r) * a.Hv + h) * VD + c) : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s2 = 0; s2 < BT * BT / 4 / NTH; ++s2) {
+    const int i = 4 * (tid + NTH * s2), r = i / BT, c = i % BT;
+    *reinterpret_cast<f32x4*>(rec + R.A + i) = *reinterpret_cast<const f32x4*>(&sA[r * LS + c]);
+  }
+  {  // u = A (beta v)
+    using TV = STiles<BT, VD>;
+    const TV tv(tid);
+    f32x4 acc[TV::TPW];
+#pragma unroll
+    for (int t = 0; t < TV::TPW; ++t) acc[t] = zero4();
+    for (int kk = 0; kk < BT; kk += 16) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(&sA[(16 * tv.rb + tv.r16) * LS + kk + 4 * tv.q]);
+#pragma unroll
+      for (int t = 0; t < TV::TPW; ++t)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          acc[t] = mfma4(av[p], sX[(kk + 4 * tv.q + p) * LX + 16 * (tv.cb0 + t) + tv.r16], acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < TV::TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        rec[R.u + (16 * tv.rb + 4 * tv.q + e) * VD + 16 * (tv.cb0 + t) + tv.r16] = acc[t][e];
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = tid; i < BT * KD; i += NTH) {
+    const int r = i / KD, c = i % KD;
+    sX[r * LX + c] = sB[r] * sK[r * LX + c] * ex2(sG[r * LX + c]);
+  }
+  __syncthreads();
+  {  // w = A (beta k 2^G)
+    using TK = STiles<BT, KD>;
+    const TK tk(tid);
+    f32x4 acc[TK::TPW];
+#pragma unroll
+    for (int t = 0; t < TK::TPW; ++t) acc[t] = zero4();
+    for (int kk = 0; kk < BT; kk += 16) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(&sA[(16 * tk.rb + tk.r16) * LS + kk + 4 * tk.q]);
+#pragma unroll
+      for (int t = 0; t < TK::TPW; ++t)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          acc[t] = mfma4(av[p], sX[(kk + 4 * tk.q + p) * LX + 16 * (tk.cb0 + t) + tk.r16], acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < TK::TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        rec[R.w + (16 * tk.rb + 4 * tk.q + e) * KD + 16 * (tk.cb0 + t) + tk.r16] = acc[t][e];
+  }
 }
 
 // --------------------------------------------------------- chunk backward
