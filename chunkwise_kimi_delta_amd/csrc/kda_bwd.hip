@@ -42,6 +42,17 @@ namespace {
 template <typename T> __device__ __forceinline__ float ldf(const T* p);
 template <> __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ldf<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+// Four consecutive elements as floats (8 bytes of bf16 or 16 bytes of fp32, aligned).
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4(const bf16_t* p) {
+  const u32x2 u = *reinterpret_cast<const u32x2*>(p);
+  f32x4 r;
+  r[0] = __uint_as_float(u.x << 16);
+  r[1] = __uint_as_float(u.x & 0xffff0000u);
+  r[2] = __uint_as_float(u.y << 16);
+  r[3] = __uint_as_float(u.y & 0xffff0000u);
+  return r;
+}
 
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
 // 2^x on the transcendental unit; every decay exponent here is <= 0
@@ -772,16 +783,18 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   constexpr int MX = KD > VD ? KD : VD;
   constexpr int LX = MX + 4;        // row stride of the 64-row matrices (16-byte aligned rows)
   constexpr int LS = BT + 4;        // row stride of the 64 x 64 matrices
-  constexpr int STAGE = (BT + MX) * (32 + 4);
-  constexpr int NB3 = BT * LX > STAGE ? BT * LX : STAGE;
-  // sB3 doubles as the staging buffer of the products until the pair sums
   __shared__ __attribute__((aligned(16))) float sB1[BT * LX];
   __shared__ __attribute__((aligned(16))) float sB2[BT * LX];
-  __shared__ __attribute__((aligned(16))) float sB3[NB3];
-  __shared__ __attribute__((aligned(16))) float sS1[BT * LS];
-  __shared__ __attribute__((aligned(16))) float sS2[BT * LS];
-  __shared__ __attribute__((aligned(16))) float sS3[BT * LS];
-  __shared__ float sBeta[BT], sGC[KD];
+  __shared__ __attribute__((aligned(16))) float sB3[BT * LX];
+  // the three 64 x 64 matrices; before them the same space holds kg and Aqk
+  __shared__ __attribute__((aligned(16))) float sSm[3 * BT * LS];
+  __shared__ float sBeta[BT], sGC[KD], sDD[KD];
+  float* sS1 = sSm;
+  float* sS2 = sSm + BT * LS;
+  float* sS3 = sSm + 2 * BT * LS;
+  float* sKG = sSm;                 // [64][LX] kg = k 2^(G_C - G) (until dv_new)
+  float* sAq = sSm + BT * LX;       // [64][LS] Aqk (until dv_new)
+  static_assert(BT * LX + BT * LS <= 3 * BT * LS, "kg and Aqk fit the small matrices' space");
   using OK = Own<KD>;
   using OV = Own<VD>;
   using OS = Own<BT>;
@@ -802,11 +815,33 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   const float* G = rec + R.G;
   const float* kn = rec + R.kn;
   const float* qn = rec + R.qn;
-  auto DO = [&](int i, int c) { return i < P.C ? ldf(dout + ((P.tok0 + i) * a.Hv + h) * VD + c) : 0.f; };
   auto VV = [&](int i, int c) { return i < P.C ? ldf(vin + ((P.tok0 + i) * a.Hv + h) * VD + c) : 0.f; };
   if (tid < BT) sBeta[tid] = rec[R.beta + tid];
   if (tid < KD) sGC[tid] = G[(P.C - 1) * KD + tid];
   __syncthreads();
+  // staged once: do (fp32) into B3, kg and Aqk into the small matrices' space
+  float* sDo = sB3;
+#pragma unroll 4
+  for (int i4 = tid; i4 < BT * VD / 4; i4 += NTH) {
+    const int r = 4 * i4 / VD, cc = 4 * i4 % VD;
+    *reinterpret_cast<f32x4*>(&sDo[r * LX + cc]) =
+        r < P.C ? ld4(dout + ((P.tok0 + r) * a.Hv + h) * VD + cc) : zero4();
+  }
+#pragma unroll 4
+  for (int i4 = tid; i4 < BT * KD / 4; i4 += NTH) {
+    const int r = 4 * i4 / KD, cc = 4 * i4 % KD;
+    const f32x4 kv = *reinterpret_cast<const f32x4*>(kn + r * KD + cc);
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(G + r * KD + cc);
+    f32x4 x;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) x[p] = kv[p] * ex2(sGC[cc + p] - gv[p]);
+    *reinterpret_cast<f32x4*>(&sKG[r * LX + cc]) = x;
+  }
+#pragma unroll
+  for (int i4 = tid; i4 < BT * BT / 4; i4 += NTH) {
+    const int r = 4 * i4 / BT, cc = 4 * i4 % BT;
+    *reinterpret_cast<f32x4*>(&sAq[r * LS + cc]) = *reinterpret_cast<const f32x4*>(rec + R.aqk + 4 * i4);
+  }
 
   // gradients of q, k and G in the 64 x K ownership; partial sums of dbeta
   // (64 x K and 64 x V ownership) and of dG_C (this lane's column)
@@ -818,90 +853,159 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   zero(dbV);
   float dGCp = 0.f;
 
-  float* stage = sB3;
-  const float* wr = rec + R.w;
-  const float* aq = rec + R.aqk;
-  {  // v_new = u - w h  -> B1
+  const int vc = ov.col();   // this lane's column in the 64 x V products
+  {  // v_new = u - w h  -> B1 (w rows and h columns straight from global memory)
     f32x4 acc[OV::TPW];
     zero(acc);
-    mf_staged<VD, 32, true, false, NB3>(acc, KD, tid, [&](int i, int kk) { return wr[i * KD + kk]; },
-                                        [&](int kk, int j) { return hc[kk * VD + j]; }, stage);
+    const float* wr = rec + R.w + ov.r16 * KD + 4 * ov.q;
+#pragma unroll 2
+    for (int kk = 0; kk < KD; kk += 16) {
+      float b[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) b[p] = hc[(kk + 4 * ov.q + p) * VD + vc];
+#pragma unroll
+      for (int t = 0; t < OV::TPW; ++t) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(wr + 16 * ov.ti(t) * KD + kk);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], b[p], acc[t]);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < OV::TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = ov.row(t, e), j = ov.col();
-        sB1[i * LX + j] = rec[R.u + i * VD + j] - acc[t][e];
+        const int i = ov.row(t, e);
+        sB1[i * LX + vc] = rec[R.u + i * VD + vc] - acc[t][e];
       }
   }
-  {  // dv_new = Aqk^T do + kg dh'  -> B2
+  __syncthreads();   // do, kg and Aqk staged
+  {  // dv_new = Aqk^T do + kg dh'  -> B2 (dh' columns straight from global memory)
     f32x4 acc[OV::TPW];
     zero(acc);
-    mf_staged<VD, 32, false, false, NB3>(acc, BT, tid, [&](int i, int r) { return aq[r * BT + i]; },
-                                         [&](int r, int j) { return DO(r, j); }, stage);
-    mf_staged<VD, 32, true, false, NB3>(
-        acc, KD, tid, [&](int i, int kk) { return kn[i * KD + kk] * ex2(sGC[kk] - G[i * KD + kk]); },
-        [&](int kk, int j) { return dh[kk * VD + j]; }, stage);
+#pragma unroll 2
+    for (int r0 = 0; r0 < BT; r0 += 16) {
+      float b[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) b[p] = sDo[(r0 + 4 * ov.q + p) * LX + vc];
+#pragma unroll
+      for (int t = 0; t < OV::TPW; ++t)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          acc[t] = mfma4(sAq[(r0 + 4 * ov.q + p) * LS + 16 * ov.ti(t) + ov.r16], b[p], acc[t]);
+    }
+#pragma unroll 2
+    for (int kk = 0; kk < KD; kk += 16) {
+      float b[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) b[p] = dh[(kk + 4 * ov.q + p) * VD + vc];
+#pragma unroll
+      for (int t = 0; t < OV::TPW; ++t) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(&sKG[(16 * ov.ti(t) + ov.r16) * LX + kk + 4 * ov.q]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], b[p], acc[t]);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < OV::TPW; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sB2[ov.row(t, e) * LX + ov.col()] = acc[t][e];
+      for (int e = 0; e < 4; ++e) sB2[ov.row(t, e) * LX + vc] = acc[t][e];
   }
-  __syncthreads();
+  __syncthreads();   // (kg and Aqk give their space to the small matrices)
   {  // dAqk = tril(do v_new^T)  -> S1
     f32x4 acc[OS::TPW];
     zero(acc);
-    mf_staged<BT, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return DO(i, c); },
-                                       [&](int c, int j) { return sB1[j * LX + c]; }, stage);
+    const int j = os.col();
+#pragma unroll 2
+    for (int c0 = 0; c0 < VD; c0 += 16) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(&sB1[j * LX + c0 + 4 * os.q]);
+#pragma unroll
+      for (int t = 0; t < OS::TPW; ++t) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(&sDo[(16 * os.ti(t) + os.r16) * LX + c0 + 4 * os.q]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], b[p], acc[t]);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < OS::TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = os.row(t, e), j = os.col();
+        const int i = os.row(t, e);
         sS1[i * LS + j] = i >= j ? acc[t][e] : 0.f;
       }
   }
-  {  // dqg = do h^T: q and G
+  const int kc = ok.col();   // this lane's channel in the 64 x K products
+  {  // dkg = v_new dh'^T: k, G and G_C (dh' rows straight from global memory)
     f32x4 acc[OK::TPW];
     zero(acc);
-    mf_staged<KD, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return DO(i, c); },
-                                       [&](int c, int kk) { return hc[kk * VD + c]; }, stage);
+    const float* dhr = dh + kc * VD + 4 * ok.q;
+    f32x4 bb[VD / 16];
 #pragma unroll
-    for (int t = 0; t < OK::TPW; ++t)
+    for (int s2 = 0; s2 < VD / 16; ++s2) bb[s2] = *reinterpret_cast<const f32x4*>(dhr + 16 * s2);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = ok.row(t, e), kk = ok.col();
-        const float ex = a.scale * ex2(G[i * KD + kk]);
-        dq[t][e] += ex * acc[t][e];
-        dG[t][e] += ex * qn[i * KD + kk] * acc[t][e];
+    for (int s2 = 0; s2 < VD / 16; ++s2)
+#pragma unroll
+      for (int t = 0; t < OK::TPW; ++t) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(&sB1[(16 * ok.ti(t) + ok.r16) * LX + 16 * s2 + 4 * ok.q]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], bb[s2][p], acc[t]);
       }
-  }
-  {  // dkg = v_new dh'^T: k, G and G_C
-    f32x4 acc[OK::TPW];
-    zero(acc);
-    mf_staged<KD, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB1[i * LX + c]; },
-                                       [&](int c, int kk) { return dh[kk * VD + c]; }, stage);
 #pragma unroll
     for (int t = 0; t < OK::TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = ok.row(t, e), kk = ok.col();
-        const float ex = ex2(sGC[kk] - G[i * KD + kk]);
-        const float kgv = kn[i * KD + kk] * ex;
+        const int i = ok.row(t, e);
+        const float ex = ex2(sGC[kc] - G[i * KD + kc]);
+        const float kgv = kn[i * KD + kc] * ex;
         dk[t][e] += ex * acc[t][e];
         dG[t][e] -= kgv * acc[t][e];
         dGCp += kgv * acc[t][e];
       }
   }
-  {  // dw = -dv_new h^T  -> B1 (v_new no longer needed)
-    f32x4 acc[OK::TPW];
-    zero(acc);
-    mf_staged<KD, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB2[i * LX + c]; },
-                                       [&](int c, int kk) { return hc[kk * VD + c]; }, stage);
+  {  // dqg = do h^T (q and G) and dw = -dv_new h^T (-> B1), sharing h's rows
+    f32x4 aq[OK::TPW], aw[OK::TPW];
+    zero(aq);
+    zero(aw);
+    const float* hr = hc + kc * VD + 4 * ok.q;
+    f32x4 hb[VD / 16];
+#pragma unroll
+    for (int s2 = 0; s2 < VD / 16; ++s2) hb[s2] = *reinterpret_cast<const f32x4*>(hr + 16 * s2);
+    float dd = 0.f;   // dD = rowsum(h . dh') of row kc: this lane's quarter of the columns
+#pragma unroll
+    for (int s2 = 0; s2 < VD / 16; ++s2) {
+      const f32x4 y = *reinterpret_cast<const f32x4*>(dh + kc * VD + 4 * ok.q + 16 * s2);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) dd += hb[s2][p] * y[p];
+    }
+    dd += __shfl_xor(dd, 16);
+    dd += __shfl_xor(dd, 32);
+    if (ok.q == 0 && ok.ti(0) == 0) sDD[kc] = dd;
+#pragma unroll
+    for (int s2 = 0; s2 < VD / 16; ++s2)
+#pragma unroll
+      for (int t = 0; t < OK::TPW; ++t) {
+        const int ro = (16 * ok.ti(t) + ok.r16) * LX + 16 * s2 + 4 * ok.q;
+        const f32x4 d = *reinterpret_cast<const f32x4*>(&sDo[ro]);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sB2[ro]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          aq[t] = mfma4(d[p], hb[s2][p], aq[t]);
+          aw[t] = mfma4(x[p], hb[s2][p], aw[t]);
+        }
+      }
 #pragma unroll
     for (int t = 0; t < OK::TPW; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sB1[ok.row(t, e) * LX + ok.col()] = -acc[t][e];
+      for (int e = 0; e < 4; ++e) {
+        const int i = ok.row(t, e);
+        const float ex = a.scale * ex2(G[i * KD + kc]);
+        dq[t][e] += ex * aq[t][e];
+        dG[t][e] += ex * qn[i * KD + kc] * aq[t][e];
+      }
+    __syncthreads();   // every wave is done with v_new (B1) before dw replaces it
+#pragma unroll
+    for (int t = 0; t < OK::TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sB1[ok.row(t, e) * LX + kc] = -aw[t][e];
   }
 #pragma unroll 8
   for (int i = tid; i < BT * BT; i += NTH) sS2[(i / BT) * LS + i % BT] = rec[R.A + i];
@@ -937,19 +1041,37 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
         if (j < P.C) a.dv[((P.tok0 + j) * a.Hv + h) * VD + c] = sBeta[j] * acc[t][e];
       }
   }
-  {  // dA = tril(dv_new (b v)^T + dw (b k e^G)^T)  -> S3
+  {  // dA = tril(dv_new (b v)^T + dw (b k e^G)^T)  -> S3 (b v, b k e^G straight from global memory)
     f32x4 acc[OS::TPW];
     zero(acc);
-    mf_staged<BT, 32, true, true, NB3>(acc, VD, tid, [&](int i, int c) { return sB2[i * LX + c]; },
-                                       [&](int c, int j) { return sBeta[j] * VV(j, c); }, stage);
-    mf_staged<BT, 32, true, true, NB3>(acc, KD, tid, [&](int i, int c) { return sB1[i * LX + c]; },
-                                       [&](int c, int j) { return sBeta[j] * kn[j * KD + c] * ex2(G[j * KD + c]); },
-                                       stage);
+    const int j = os.col();
+    const float bj = sBeta[j];
+#pragma unroll 4
+    for (int c0 = 0; c0 < VD; c0 += 16) {
+      const f32x4 vv = j < P.C ? ld4(vin + ((P.tok0 + j) * a.Hv + h) * VD + c0 + 4 * os.q) : zero4();
+#pragma unroll
+      for (int t = 0; t < OS::TPW; ++t) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(&sB2[(16 * os.ti(t) + os.r16) * LX + c0 + 4 * os.q]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], bj * vv[p], acc[t]);
+      }
+    }
+#pragma unroll 4
+    for (int c0 = 0; c0 < KD; c0 += 16) {
+      const f32x4 kv = *reinterpret_cast<const f32x4*>(kn + j * KD + c0 + 4 * os.q);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(G + j * KD + c0 + 4 * os.q);
+#pragma unroll
+      for (int t = 0; t < OS::TPW; ++t) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(&sB1[(16 * os.ti(t) + os.r16) * LX + c0 + 4 * os.q]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], bj * kv[p] * ex2(gv[p]), acc[t]);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < OS::TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = os.row(t, e), j = os.col();
+        const int i = os.row(t, e);
         sS3[i * LS + j] = i >= j ? acc[t][e] : 0.f;
       }
   }
@@ -986,24 +1108,6 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
       *reinterpret_cast<f32x4*>(pr + i) = *reinterpret_cast<const f32x4*>(&sS3[r * LS + cc]);
       *reinterpret_cast<f32x4*>(pr + BT * BT + i) = *reinterpret_cast<const f32x4*>(&sS1[r * LS + cc]);
     }
-  }
-  // dD = rowsum(h . dh'), four threads per row of the states, 16-byte loads
-  float* sDD = sS2 + 4 * KD;   // [KD] (after sRedK)
-  {
-    constexpr int TPR = NTH / KD > 4 ? 4 : NTH / KD, SEG = VD / TPR;
-    const int r = tid / TPR, part = tid % TPR;
-    float s = 0.f;
-    if (r < KD) {
-#pragma unroll
-      for (int cc = part * SEG; cc < (part + 1) * SEG; cc += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(hc + r * VD + cc);
-        const f32x4 y = *reinterpret_cast<const f32x4*>(dh + r * VD + cc);
-        s += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < TPR; m <<= 1) s += __shfl_xor(s, m);
-    if (r < KD && part == 0) sDD[r] = s;
   }
   // dbeta partial sums in a fixed order (per ownership, the 16 lanes of a row
   // first), dG_C over rows (the four lane groups first)
