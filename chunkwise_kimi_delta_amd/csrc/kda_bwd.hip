@@ -1384,21 +1384,36 @@ __global__ __launch_bounds__(NTH) void bwd_pairs_kernel(BwdArgs a) {
       const float s = sum16(dbK[t][e]);
       if (ok.r16 == 0) sRedB[(ok.w % OK::NT) * BT + ok.row(t, e)] = s;
     }
-  // dq, dk: added to the partial gradients; dG: the whole row into LDS
+  // dq, dk: added to the partial gradients; dG: the whole row into LDS.  All
+  // partials are loaded before any store (the output buffers may alias as far
+  // as the compiler knows, which would otherwise order every load after the
+  // previous store)
+  {
+    f32x4 pq[OK::TPW], pk[OK::TPW], pg[OK::TPW];
 #pragma unroll
-  for (int t = 0; t < OK::TPW; ++t)
+    for (int t = 0; t < OK::TPW; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = ok.row(t, e);
-      float gpart = 0.f;
-      if (i < P.C) {
+      for (int e = 0; e < 4; ++e) {
+        const int i = ok.row(t, e);
         const int64_t o = ((P.tok0 + i) * a.Hv + h) * KD + c;
-        a.dqn[o] += dq[t][e];
-        a.dkn[o] += dk[t][e];
-        gpart = a.dg_nat[o];
+        const bool in = i < P.C;
+        pq[t][e] = in ? a.dqn[o] : 0.f;
+        pk[t][e] = in ? a.dkn[o] : 0.f;
+        pg[t][e] = in ? a.dg_nat[o] : 0.f;
       }
-      sB3[i * LX + c] = gpart + dG[t][e];
-    }
+#pragma unroll
+    for (int t = 0; t < OK::TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = ok.row(t, e);
+        if (i < P.C) {
+          const int64_t o = ((P.tok0 + i) * a.Hv + h) * KD + c;
+          a.dqn[o] = pq[t][e] + dq[t][e];
+          a.dkn[o] = pk[t][e] + dk[t][e];
+        }
+        sB3[i * LX + c] = pg[t][e] + dG[t][e];
+      }
+  }
   __syncthreads();
   if (tid < BT && tid < P.C) {
     float s = 0.f;
