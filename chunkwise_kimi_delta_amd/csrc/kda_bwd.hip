@@ -821,26 +821,40 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   __syncthreads();
   // staged once: do (fp32) into B3, kg and Aqk into the small matrices' space
   float* sDo = sB3;
-#pragma unroll 4
-  for (int i4 = tid; i4 < BT * VD / 4; i4 += NTH) {
-    const int r = 4 * i4 / VD, cc = 4 * i4 % VD;
-    *reinterpret_cast<f32x4*>(&sDo[r * LX + cc]) =
-        r < P.C ? ld4(dout + ((P.tok0 + r) * a.Hv + h) * VD + cc) : zero4();
-  }
-#pragma unroll 4
-  for (int i4 = tid; i4 < BT * KD / 4; i4 += NTH) {
-    const int r = 4 * i4 / KD, cc = 4 * i4 % KD;
-    const f32x4 kv = *reinterpret_cast<const f32x4*>(kn + r * KD + cc);
-    const f32x4 gv = *reinterpret_cast<const f32x4*>(G + r * KD + cc);
-    f32x4 x;
+  {  // every load issued before any use
+    constexpr int ND = BT * VD / 4 / NTH, NK = BT * KD / 4 / NTH, NQ = BT * BT / 4 / NTH;
+    f32x4 xd[ND], xk[NK], xg[NK], xq[NQ];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) x[p] = kv[p] * ex2(sGC[cc + p] - gv[p]);
-    *reinterpret_cast<f32x4*>(&sKG[r * LX + cc]) = x;
-  }
+    for (int s2 = 0; s2 < ND; ++s2) {
+      const int i4 = tid + NTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
+      xd[s2] = r < P.C ? ld4(dout + ((P.tok0 + r) * a.Hv + h) * VD + cc) : zero4();
+    }
 #pragma unroll
-  for (int i4 = tid; i4 < BT * BT / 4; i4 += NTH) {
-    const int r = 4 * i4 / BT, cc = 4 * i4 % BT;
-    *reinterpret_cast<f32x4*>(&sAq[r * LS + cc]) = *reinterpret_cast<const f32x4*>(rec + R.aqk + 4 * i4);
+    for (int s2 = 0; s2 < NK; ++s2) {
+      const int i4 = tid + NTH * s2;
+      xk[s2] = *reinterpret_cast<const f32x4*>(kn + 4 * i4);
+      xg[s2] = *reinterpret_cast<const f32x4*>(G + 4 * i4);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < NQ; ++s2) xq[s2] = *reinterpret_cast<const f32x4*>(rec + R.aqk + 4 * (tid + NTH * s2));
+#pragma unroll
+    for (int s2 = 0; s2 < ND; ++s2) {
+      const int i4 = tid + NTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
+      *reinterpret_cast<f32x4*>(&sDo[r * LX + cc]) = xd[s2];
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < NK; ++s2) {
+      const int i4 = tid + NTH * s2, r = 4 * i4 / KD, cc = 4 * i4 % KD;
+      f32x4 x;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) x[p] = xk[s2][p] * ex2(sGC[cc + p] - xg[s2][p]);
+      *reinterpret_cast<f32x4*>(&sKG[r * LX + cc]) = x;
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < NQ; ++s2) {
+      const int i4 = tid + NTH * s2, r = 4 * i4 / BT, cc = 4 * i4 % BT;
+      *reinterpret_cast<f32x4*>(&sAq[r * LS + cc]) = xq[s2];
+    }
   }
 
   // gradients of q, k and G in the 64 x K ownership; partial sums of dbeta
@@ -1032,12 +1046,17 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     zero(acc);
     mf_lds<VD>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
                [&](int i, int c) { return sB2[i * LX + c]; });
+    f32x4 vv[OV::TPW];   // (all loads before the stores)
+#pragma unroll
+    for (int t = 0; t < OV::TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[t][e] = VV(ov.row(t, e), ov.col());
 #pragma unroll
     for (int t = 0; t < OV::TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = ov.row(t, e), c = ov.col();
-        dbV[t][e] += VV(j, c) * acc[t][e];
+        dbV[t][e] += vv[t][e] * acc[t][e];
         if (j < P.C) a.dv[((P.tok0 + j) * a.Hv + h) * VD + c] = sBeta[j] * acc[t][e];
       }
   }
