@@ -195,7 +195,8 @@ kda_status_t run_intra(const kda_problem_t* p, const Plan& pl, const kda::SeqInf
 }
 
 kda_status_t common_inputs(const kda_problem_t* p, const Plan& pl, const void* k, const void* v,
-                           const void* g, const void* beta, const float* A_log, const int32_t* cu) {
+                           const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                           const int32_t* cu) {
   if (pl.tokens > 0) {
     kda_status_t st;
     if ((st = check_token_ptr(k, "k", 16)) != KDA_OK) return st;
@@ -204,6 +205,8 @@ kda_status_t common_inputs(const kda_problem_t* p, const Plan& pl, const void* k
     if ((st = check_token_ptr(beta, "beta", pl.es)) != KDA_OK) return st;
     if ((p->flags & KDA_GATE_IN_KERNEL) && !A_log)
       return fail(KDA_ERR_INVALID_ARGUMENT, "KDA_GATE_IN_KERNEL needs A_log");
+    if ((p->flags & KDA_GATE_IN_KERNEL) && dt_bias && !aligned(dt_bias, 16))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "dt_bias must be 16-byte aligned");
   }
   if (p->layout == KDA_LAYOUT_TND && !cu) return fail(KDA_ERR_INVALID_ARGUMENT, "TND needs device cu_seqlens");
   return KDA_OK;
@@ -269,7 +272,7 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
   Plan pl;
   kda_status_t st = plan_problem(p, true, pl);
   if (st != KDA_OK) return st;
-  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, cu_seqlens)) != KDA_OK) return st;
+  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, dt_bias, cu_seqlens)) != KDA_OK) return st;
   if (pl.tokens > 0) {
     if ((st = check_token_ptr(q, "q", 16)) != KDA_OK) return st;
     if ((st = check_token_ptr(o, "o", 16)) != KDA_OK) return st;
@@ -331,7 +334,7 @@ kda_status_t kda_segment_summary(const kda_problem_t* p, const void* k, const vo
   Plan pl;
   kda_status_t st = plan_problem(p, false, pl);
   if (st != KDA_OK) return st;
-  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, cu_seqlens)) != KDA_OK) return st;
+  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, dt_bias, cu_seqlens)) != KDA_OK) return st;
   if (pl.N > 0 && (!M || !S_tilde)) return fail(KDA_ERR_INVALID_ARGUMENT, "M and S_tilde are required");
   if ((M && !aligned(M, 16)) || (S_tilde && !aligned(S_tilde, 16)))
     return fail(KDA_ERR_INVALID_ARGUMENT, "M and S_tilde must be 16-byte aligned");
@@ -421,7 +424,7 @@ kda_status_t kda_chunk_bwd(const kda_problem_t* p, const void* q, const void* k,
   kda_status_t st = plan_bwd(p, bp);
   if (st != KDA_OK) return st;
   const Plan& pl = bp.fwd;
-  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, cu_seqlens)) != KDA_OK) return st;
+  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, dt_bias, cu_seqlens)) != KDA_OK) return st;
   if (pl.tokens > 0) {
     if ((st = check_token_ptr(q, "q", 16)) != KDA_OK) return st;
     if ((st = check_token_ptr(dout, "do", 16)) != KDA_OK) return st;
@@ -497,7 +500,7 @@ kda_status_t kda_segment_summary_bwd(const kda_problem_t* p, const void* q, cons
   kda_status_t st = plan_bwd(p, bp);
   if (st != KDA_OK) return st;
   const Plan& pl = bp.fwd;
-  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, cu_seqlens)) != KDA_OK) return st;
+  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, dt_bias, cu_seqlens)) != KDA_OK) return st;
   if (pl.tokens > 0) {
     if ((st = check_token_ptr(q, "q", 16)) != KDA_OK) return st;
     if ((st = check_token_ptr(dout, "do", 16)) != KDA_OK) return st;
@@ -580,7 +583,7 @@ kda_status_t kda_recurrent_fwd(const kda_problem_t* p, const void* q, const void
   Plan pl;
   kda_status_t st = plan_problem(p, true, pl);
   if (st != KDA_OK) return st;
-  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, cu_seqlens)) != KDA_OK) return st;
+  if ((st = common_inputs(p, pl, k, v, g, beta, A_log, dt_bias, cu_seqlens)) != KDA_OK) return st;
   if (pl.tokens > 0) {
     if ((st = check_token_ptr(q, "q", 16)) != KDA_OK) return st;
     if ((st = check_token_ptr(o, "o", 16)) != KDA_OK) return st;

@@ -420,25 +420,54 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
   const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;
   const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
 
-  // ---- gate, norms, beta: rows r = tid / 8, channels CPT * (tid % 8) .. +CPT-1
+  // ---- gate, norms, beta: rows r = tid / 8, channels CPT * (tid % 8) .. +CPT-1.
+  // softplus in log2 form on the transcendental unit: softplus(z) = max(z, 0)
+  // + ln2 log2(1 + 2^(-|z| log2 e)); the decay is kept in log2 units
   {
     const int r = tid >> 3, part = tid & 7;
     constexpr int CPT = KD / 8;
     const bool live = r < P.C;
-    float kr[CPT], qr[CPT];
+    float kr[CPT], qr[CPT], gr[CPT], br[CPT];
+    if (live) {
+      const IT* kp = k + ((P.tok0 + r) * a.Hk + hk) * KD + part * CPT;
+      const IT* qp = q + ((P.tok0 + r) * a.Hk + hk) * KD + part * CPT;
+      const IT* gp = g + ((P.tok0 + r) * a.Hv + h) * KD + part * CPT;
+#pragma unroll
+      for (int e4 = 0; e4 < CPT; e4 += 4) {
+        const f32x4 kv = ld4(kp + e4), qv = ld4(qp + e4), gv = ld4(gp + e4);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          kr[e4 + p] = kv[p];
+          qr[e4 + p] = qv[p];
+          gr[e4 + p] = gv[p];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) kr[e] = qr[e] = gr[e] = 0.f;
+    }
+#pragma unroll
+    for (int e4 = 0; e4 < CPT; e4 += 4) {
+      const f32x4 bv = (gik && a.dt_bias) ? ld4(a.dt_bias + h * KD + part * CPT + e4) : zero4();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) br[e4 + p] = bv[p];
+    }
     float skk = 0.f, sqq = 0.f, sqk = 0.f;
+    const float lb2 = !live ? 0.f : lb * LOG2E_F;     // (lb = -inf: no clamp)
+    const float cA = live ? -Aexp * LOG2E_F : 0.f;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
-      const int c = part * CPT + e;
-      kr[e] = live ? ldf(k + ((P.tok0 + r) * a.Hk + hk) * KD + c) : 0.f;
-      qr[e] = live ? ldf(q + ((P.tok0 + r) * a.Hk + hk) * KD + c) : 0.f;
       skk += kr[e] * kr[e];
       sqq += qr[e] * qr[e];
       sqk += qr[e] * kr[e];
-      float gv = live ? ldf(g + ((P.tok0 + r) * a.Hv + h) * KD + c) : 0.f;
-      if (live && gik) gv = -Aexp * softplus_f(gv + (a.dt_bias ? a.dt_bias[h * KD + c] : 0.f));
-      if (live && gv < lb) gv = lb;
-      sG[r * LX + c] = gv * LOG2E_F;          // log2 units
+      float gl;
+      if (gik) {
+        const float z = gr[e] + br[e];
+        gl = cA * (fmaxf(z, 0.f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.f + ex2(-LOG2E_F * fabsf(z))));
+      } else {
+        gl = live ? gr[e] * LOG2E_F : 0.f;
+      }
+      sG[r * LX + part * CPT + e] = fmaxf(gl, lb2);    // log2 units
     }
     for (int m = 1; m < 8; m <<= 1) {
       skk += __shfl_xor(skk, m);
@@ -517,6 +546,8 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
         const int i = 16 * I + 4 * quad + e, j = 16 * J + r16;
         sL[i * LS + j] = sB[i] * accL[e];
         aqk[i * BT + j] = a.scale * accQ[e];
+        sL[j * LS + i] = 0.f;          // the mirrored tile above the diagonal
+        aqk[j * BT + i] = 0.f;
       }
     } else {
       const int I = (job - 6) >> 2, lv = (job - 6) & 3;
@@ -541,20 +572,16 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int il = 4 * quad + e, jl = r16;
+        const int i = 16 * I + il, j = 16 * I + jl;
         if ((il >> (lv + 1)) == (jl >> (lv + 1)) && ((il >> lv) & 1) && !((jl >> lv) & 1)) {
-          const int i = 16 * I + il, j = 16 * I + jl;
           sL[i * LS + j] = sB[i] * accL[e];
           aqk[i * BT + j] = a.scale * accQ[e];
+        } else if (lv == 0 && il <= jl) {   // diagonal and upper entries of the tile, once
+          sL[i * LS + j] = 0.f;
+          aqk[i * BT + j] = il == jl ? sDiag[i] : 0.f;
         }
       }
     }
-  }
-  // diagonal and upper entries: L zero; Aqk its diagonal, zero above
-  for (int idx = tid; idx < BT * BT; idx += NTH) {
-    const int i = idx / BT, j = idx % BT;
-    if (j < i) continue;
-    sL[i * LS + j] = 0.f;
-    aqk[i * BT + j] = i == j ? sDiag[i] : 0.f;
   }
   __syncthreads();
 
@@ -611,11 +638,19 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
       }
     }
   }
-  // beta v into sX (q is no longer needed)
-#pragma unroll 4
-  for (int i = tid; i < BT * VD; i += NTH) {
-    const int r = i / VD, c = i % VD;
-    sX[r * LX + c] = r < P.C ? sB[r] * ldf(v + ((P.tok0 + r) * a.Hv + h) * VD + c) : 0.f;
+  {  // beta v into sX (q is no longer needed): every load issued first
+    constexpr int NV = BT * VD / 4 / NTH;
+    f32x4 xv[NV];
+#pragma unroll
+    for (int s2 = 0; s2 < NV; ++s2) {
+      const int i4 = tid + NTH * s2, r = 4 * i4 / VD, c = 4 * i4 % VD;
+      xv[s2] = r < P.C ? ld4(v + ((P.tok0 + r) * a.Hv + h) * VD + c) : zero4();
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < NV; ++s2) {
+      const int i4 = tid + NTH * s2, r = 4 * i4 / VD, c = 4 * i4 % VD;
+      *reinterpret_cast<f32x4*>(&sX[r * LX + c]) = sB[r] * xv[s2];
+    }
   }
   __syncthreads();
 #pragma unroll

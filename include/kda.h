@@ -112,7 +112,8 @@ kda_status_t kda_chunk_fwd_workspace_size(const kda_problem_t* p, size_t* bytes)
  *
  *  q, k, v, g, beta : token tensors in p->layout and p->dtype (see above).
  *  A_log [Hv], dt_bias [Hv,K] : fp32 gate parameters, used with
- *                     KDA_GATE_IN_KERNEL (A_log required, dt_bias may be NULL = 0).
+ *                     KDA_GATE_IN_KERNEL (A_log required, dt_bias may be NULL = 0;
+ *                     dt_bias is read 16 bytes at a time and must be 16-byte aligned).
  *  cu_seqlens       : device int32 [N+1] for TND (must equal cu_seqlens_host); NULL for BSND.
  *  initial_state    : state_rows == 0: fp32 [N,Hv,K,V] or NULL (zero start).
  *                     state_rows  > 0: fp32 state cache [state_rows,Hv,K,V]; sequence n

@@ -181,6 +181,12 @@ def test_calls_fail_closed_without_launching(lib):
     st = lib.kda_chunk_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None,
                            None, None, fake, None, fake, 10, None, None)
     assert st == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    # the gate bias is read 16 bytes at a time: a misaligned one is rejected
+    for fn in (lambda: lib.kda_chunk_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake + 4, None,
+                                         None, None, fake, None, fake, 1 << 40, None, None),
+               lambda: lib.kda_recurrent_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake + 4,
+                                             None, None, None, fake, None, None)):
+        assert fn() == kda.KDA_ERR_INVALID_ARGUMENT and b"dt_bias" in lib.kda_last_error()
     # an empty selection (N = 0) launches nothing and succeeds
     p0, keep = _tnd([0])
     sz = ctypes.c_size_t()
