@@ -1550,29 +1550,54 @@ __global__ __launch_bounds__(KD) void bwd_gate_kernel(BwdArgs a, int64_t tokens,
   const float bias = (gik && a.dt_bias) ? a.dt_bias[h * KD + c] : 0.f;
   float sA = 0.f, sB = 0.f;
   const int64_t t0 = (int64_t)blk * GATE_TOKENS, t1 = min(tokens, t0 + GATE_TOKENS);
-  for (int64_t t = t0; t < t1; ++t) {
-    const int64_t i = (t * a.Hv + h) * KD + c;
-    const float dgn = a.dg_nat[i];
-    const float x = ldf(g + i);
-    float gact = x, dz = dgn;
-    if (gik) {
-      const float z = x + bias;
-      gact = -Aexp * softplus_f(z);
-      dz = dgn * -Aexp * sigmoid_f(z);
+  // batches of GB tokens, every load of a batch issued before its stores (the
+  // output may alias the inputs as far as the compiler knows, which would
+  // otherwise order each token's loads after the previous token's store)
+  constexpr int GB = 8;
+  for (int64_t tb = t0; tb < t1; tb += GB) {
+    float dgn[GB], x[GB];
+#pragma unroll
+    for (int u = 0; u < GB; ++u) {
+      const int64_t t = tb + u;
+      const bool in = t < t1;
+      const int64_t i = (t * a.Hv + h) * KD + c;
+      dgn[u] = in ? a.dg_nat[i] : 0.f;
+      x[u] = in ? ldf(g + i) : 0.f;
     }
-    const bool clamped = gact < lb;
-    if (clamped) dz = 0.f;
-    a.dg[i] = dz;
-    sB += dz;
-    sA += clamped ? 0.f : dgn * gact;
-    if (c == 0) {
-      const int64_t j = t * a.Hv + h;
-      float db = a.dbeta_act[j];
-      if (a.flags & F_SIGMOID) {
-        const float s = sigmoid_f(ldf(bt + j));
-        db *= s * (1.f - s);
+    // beta: thread c < GB of the block takes token tb + c
+    const bool inb = c < GB && tb + c < t1;
+    const int64_t jb = (tb + c) * a.Hv + h;
+    const float db0 = inb ? a.dbeta_act[jb] : 0.f;
+    const float bl0 = (inb && (a.flags & F_SIGMOID)) ? ldf(bt + jb) : 0.f;
+#pragma unroll
+    for (int u = 0; u < GB; ++u) {
+      const int64_t t = tb + u;
+      if (t >= t1) break;
+      const int64_t i = (t * a.Hv + h) * KD + c;
+      float gact = x[u], dz = dgn[u];
+      if (gik) {
+        // softplus(z) = max(z, 0) + ln(1 + e^-|z|) and its derivative sigmoid(z)
+        // from one exponential: e = e^-|z|, sigmoid = 1 / (1 + e) for z >= 0
+        // and e / (1 + e) below
+        const float z = x[u] + bias;
+        const float e = ex2(-LOG2E_F * fabsf(z));
+        const float r = 1.f / (1.f + e);
+        gact = -Aexp * (fmaxf(z, 0.f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.f + e));
+        dz = dgn[u] * -Aexp * (z >= 0.f ? r : e * r);
       }
-      a.dbeta[j] = db;
+      const bool clamped = gact < lb;
+      if (clamped) dz = 0.f;
+      a.dg[i] = dz;
+      sB += dz;
+      sA += clamped ? 0.f : dgn[u] * gact;
+    }
+    if (inb) {
+      float d = db0;
+      if (a.flags & F_SIGMOID) {
+        const float sg = sigmoid_f(bl0);
+        d *= sg * (1.f - sg);
+      }
+      a.dbeta[jb] = d;
     }
   }
   // partial sums: [blk][Hv][KD + 1] (dt_bias per channel, then A_log)
