@@ -340,10 +340,16 @@ def cpu_baseline_train(p, target_token_heads):
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 
+# The sources of the forward step's kernels (the chunk-local kernel, the scan
+# and the layouts they share): counters taken on them stay valid while these
+# files are unchanged.
+FWD_SOURCES = ("kda_common.h", "kda_launch.h", "kda_intra.hip", "kda_scan.hip")
+
+
 def source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "chunkwise_kimi_delta_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in FWD_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()
