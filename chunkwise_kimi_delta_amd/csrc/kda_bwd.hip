@@ -903,34 +903,33 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   float dGCp = 0.f;
 
   const int vc = ov.col();   // this lane's column in the 64 x V products
-  {  // v_new = u - w h  -> B1 (w rows and h columns straight from global memory)
-    f32x4 acc[OV::TPW];
-    zero(acc);
+  __syncthreads();   // do, kg and Aqk staged
+  {  // v_new = u - w h  -> B1 and dv_new = kg dh' + Aqk^T do  -> B2: one pass over K for
+     // both K-reductions (w rows from global memory, kg rows from LDS, h and dh' columns
+     // from global memory), then the Aqk^T do part
+    f32x4 an[OV::TPW], ad[OV::TPW];
+    zero(an);
+    zero(ad);
     const float* wr = rec + R.w + ov.r16 * KD + 4 * ov.q;
 #pragma unroll 2
     for (int kk = 0; kk < KD; kk += 16) {
-      float b[4];
+      float bh[4], bd[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) b[p] = hc[(kk + 4 * ov.q + p) * VD + vc];
+      for (int p = 0; p < 4; ++p) {
+        bh[p] = hc[(kk + 4 * ov.q + p) * VD + vc];
+        bd[p] = dh[(kk + 4 * ov.q + p) * VD + vc];
+      }
 #pragma unroll
       for (int t = 0; t < OV::TPW; ++t) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(wr + 16 * ov.ti(t) * KD + kk);
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(wr + 16 * ov.ti(t) * KD + kk);
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(&sKG[(16 * ov.ti(t) + ov.r16) * LX + kk + 4 * ov.q]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], b[p], acc[t]);
+        for (int p = 0; p < 4; ++p) {
+          an[t] = mfma4(wv[p], bh[p], an[t]);
+          ad[t] = mfma4(kv[p], bd[p], ad[t]);
+        }
       }
     }
-#pragma unroll
-    for (int t = 0; t < OV::TPW; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = ov.row(t, e);
-        sB1[i * LX + vc] = rec[R.u + i * VD + vc] - acc[t][e];
-      }
-  }
-  __syncthreads();   // do, kg and Aqk staged
-  {  // dv_new = Aqk^T do + kg dh'  -> B2 (dh' columns straight from global memory)
-    f32x4 acc[OV::TPW];
-    zero(acc);
 #pragma unroll 2
     for (int r0 = 0; r0 < BT; r0 += 16) {
       float b[4];
@@ -940,24 +939,16 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
       for (int t = 0; t < OV::TPW; ++t)
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-          acc[t] = mfma4(sAq[(r0 + 4 * ov.q + p) * LS + 16 * ov.ti(t) + ov.r16], b[p], acc[t]);
-    }
-#pragma unroll 2
-    for (int kk = 0; kk < KD; kk += 16) {
-      float b[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) b[p] = dh[(kk + 4 * ov.q + p) * VD + vc];
-#pragma unroll
-      for (int t = 0; t < OV::TPW; ++t) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(&sKG[(16 * ov.ti(t) + ov.r16) * LX + kk + 4 * ov.q]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], b[p], acc[t]);
-      }
+          ad[t] = mfma4(sAq[(r0 + 4 * ov.q + p) * LS + 16 * ov.ti(t) + ov.r16], b[p], ad[t]);
     }
 #pragma unroll
     for (int t = 0; t < OV::TPW; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sB2[ov.row(t, e) * LX + vc] = acc[t][e];
+      for (int e = 0; e < 4; ++e) {
+        const int i = ov.row(t, e);
+        sB1[i * LX + vc] = rec[R.u + i * VD + vc] - an[t][e];
+        sB2[i * LX + vc] = ad[t][e];
+      }
   }
   __syncthreads();   // (kg and Aqk give their space to the small matrices)
   {  // dAqk = tril(do v_new^T)  -> S1
@@ -983,72 +974,52 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
       }
   }
   const int kc = ok.col();   // this lane's channel in the 64 x K products
-  {  // dkg = v_new dh'^T: k, G and G_C (dh' rows straight from global memory)
-    f32x4 acc[OK::TPW];
-    zero(acc);
-    const float* dhr = dh + kc * VD + 4 * ok.q;
-    f32x4 bb[VD / 16];
-#pragma unroll
-    for (int s2 = 0; s2 < VD / 16; ++s2) bb[s2] = *reinterpret_cast<const f32x4*>(dhr + 16 * s2);
-#pragma unroll
-    for (int s2 = 0; s2 < VD / 16; ++s2)
-#pragma unroll
-      for (int t = 0; t < OK::TPW; ++t) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(&sB1[(16 * ok.ti(t) + ok.r16) * LX + 16 * s2 + 4 * ok.q]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], bb[s2][p], acc[t]);
-      }
-#pragma unroll
-    for (int t = 0; t < OK::TPW; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = ok.row(t, e);
-        const float ex = ex2(sGC[kc] - G[i * KD + kc]);
-        const float kgv = kn[i * KD + kc] * ex;
-        dk[t][e] += ex * acc[t][e];
-        dG[t][e] -= kgv * acc[t][e];
-        dGCp += kgv * acc[t][e];
-      }
-  }
-  {  // dqg = do h^T (q and G) and dw = -dv_new h^T (-> B1), sharing h's rows
-    f32x4 aq[OK::TPW], aw[OK::TPW];
+  {  // dkg = v_new dh'^T (k, G, G_C), dqg = do h^T (q, G) and dw = -dv_new h^T (-> B1) in
+     // one pass over the V columns: h and dh' rows of this lane's channel straight from
+     // global memory; dD = rowsum(h . dh') on the way
+    f32x4 ak[OK::TPW], aq[OK::TPW], aw[OK::TPW];
+    zero(ak);
     zero(aq);
     zero(aw);
     const float* hr = hc + kc * VD + 4 * ok.q;
-    f32x4 hb[VD / 16];
-#pragma unroll
-    for (int s2 = 0; s2 < VD / 16; ++s2) hb[s2] = *reinterpret_cast<const f32x4*>(hr + 16 * s2);
-    float dd = 0.f;   // dD = rowsum(h . dh') of row kc: this lane's quarter of the columns
-#pragma unroll
+    const float* dhr = dh + kc * VD + 4 * ok.q;
+    float dd = 0.f;   // this lane's quarter of the columns
+#pragma unroll 2
     for (int s2 = 0; s2 < VD / 16; ++s2) {
-      const f32x4 y = *reinterpret_cast<const f32x4*>(dh + kc * VD + 4 * ok.q + 16 * s2);
+      const f32x4 hv = *reinterpret_cast<const f32x4*>(hr + 16 * s2);
+      const f32x4 dv = *reinterpret_cast<const f32x4*>(dhr + 16 * s2);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) dd += hb[s2][p] * y[p];
+      for (int p = 0; p < 4; ++p) dd += hv[p] * dv[p];
+#pragma unroll
+      for (int t = 0; t < OK::TPW; ++t) {
+        const int ro = (16 * ok.ti(t) + ok.r16) * LX + 16 * s2 + 4 * ok.q;
+        const f32x4 vn = *reinterpret_cast<const f32x4*>(&sB1[ro]);
+        const f32x4 d = *reinterpret_cast<const f32x4*>(&sDo[ro]);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sB2[ro]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          ak[t] = mfma4(vn[p], dv[p], ak[t]);
+          aq[t] = mfma4(d[p], hv[p], aq[t]);
+          aw[t] = mfma4(x[p], hv[p], aw[t]);
+        }
+      }
     }
     dd += __shfl_xor(dd, 16);
     dd += __shfl_xor(dd, 32);
     if (ok.q == 0 && ok.ti(0) == 0) sDD[kc] = dd;
 #pragma unroll
-    for (int s2 = 0; s2 < VD / 16; ++s2)
-#pragma unroll
-      for (int t = 0; t < OK::TPW; ++t) {
-        const int ro = (16 * ok.ti(t) + ok.r16) * LX + 16 * s2 + 4 * ok.q;
-        const f32x4 d = *reinterpret_cast<const f32x4*>(&sDo[ro]);
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&sB2[ro]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          aq[t] = mfma4(d[p], hb[s2][p], aq[t]);
-          aw[t] = mfma4(x[p], hb[s2][p], aw[t]);
-        }
-      }
-#pragma unroll
     for (int t = 0; t < OK::TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = ok.row(t, e);
-        const float ex = a.scale * ex2(G[i * KD + kc]);
-        dq[t][e] += ex * aq[t][e];
-        dG[t][e] += ex * qn[i * KD + kc] * aq[t][e];
+        const float gi = G[i * KD + kc];
+        const float ex = ex2(sGC[kc] - gi);
+        const float kgv = kn[i * KD + kc] * ex;
+        const float eq = a.scale * ex2(gi);
+        dk[t][e] += ex * ak[t][e];
+        dG[t][e] += eq * qn[i * KD + kc] * aq[t][e] - kgv * ak[t][e];
+        dGCp += kgv * ak[t][e];
+        dq[t][e] += eq * aq[t][e];
       }
     __syncthreads();   // every wave is done with v_new (B1) before dw replaces it
 #pragma unroll
