@@ -715,12 +715,13 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 // 0..3) of column l % 16.  Pass p of a 16-wide reduction step gives lane l the
 // reduction index 4 (l / 16) + p, so each operand is read as four
 // consecutive reduction values per lane.
-template <int N>
+template <int N, int NW = NTH / 64>
 struct Own {
-  static constexpr int NT = N / 16, TPW = 4 * NT / (NTH / 64);
+  static constexpr int NT = N / 16, TPW = 4 * NT / NW;
+  static_assert(TPW >= 1 && NW % NT == 0, "whole tiles per wave, one column block per wave");
   int w, r16, q;
   __device__ explicit Own(int tid) : w(tid >> 6), r16(tid & 15), q((tid >> 4) & 3) {}
-  __device__ int ti(int t) const { return (w + (NTH / 64) * t) / NT; }
+  __device__ int ti(int t) const { return (w + NW * t) / NT; }
   __device__ int col() const { return 16 * (w % NT) + r16; }
   __device__ int row(int t, int e) const { return 16 * ti(t) + 4 * q + e; }
 };
@@ -785,9 +786,9 @@ __device__ __forceinline__ void mf_staged(f32x4 (&acc)[Own<N>::TPW], int kr, int
 }
 // acc += A (64 x kr) * B (kr x N) with both operands read element by element
 // (from LDS) through accessors.
-template <int N, typename FA, typename FB>
-__device__ __forceinline__ void mf_lds(f32x4 (&acc)[Own<N>::TPW], int kr, int tid, FA A, FB B) {
-  const Own<N> o(tid);
+template <int N, int NW, typename FA, typename FB>
+__device__ __forceinline__ void mf_lds(f32x4 (&acc)[(Own<N, NW>::TPW)], int kr, int tid, FA A, FB B) {
+  const Own<N, NW> o(tid);
   for (int kk = 0; kk < kr; kk += 16) {
     float b[4];
 #pragma unroll
@@ -812,8 +813,12 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
+// The chunk kernel runs 16 waves (four per SIMD): each owns fewer output tiles, so
+// its accumulators fit, and the extra waves hide the load latency of its phases.
+constexpr int CNTH = 1024;
+
 template <int KD, int VD, typename IT>
-__global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
   static_assert(KD == 128 || KD == 64, "K");
   constexpr int MX = KD > VD ? KD : VD;
   constexpr int LX = MX + 4;        // row stride of the 64-row matrices (16-byte aligned rows)
@@ -830,10 +835,10 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   float* sKG = sSm;                 // [64][LX] kg = k 2^(G_C - G) (until dv_new)
   float* sAq = sSm + BT * LX;       // [64][LS] Aqk (until dv_new)
   static_assert(BT * LX + BT * LS <= 3 * BT * LS, "kg and Aqk fit the small matrices' space");
-  using OK = Own<KD>;
-  using OV = Own<VD>;
-  using OS = Own<BT>;
-  static_assert((OK::NT + OV::NT) * BT <= BT * LS && (NTH / 64 / OK::NT) * KD <= BT * LS,
+  using OK = Own<KD, CNTH / 64>;
+  using OV = Own<VD, CNTH / 64>;
+  using OS = Own<BT, CNTH / 64>;
+  static_assert((OK::NT + OV::NT) * BT <= BT * LS && (CNTH / 64 / OK::NT) * KD <= BT * LS,
                 "reduction buffers fit the small matrices");
   constexpr BwdRec R = bwd_rec(KD, VD);
   const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
@@ -857,29 +862,29 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   // staged once: do (fp32) into B3, kg and Aqk into the small matrices' space
   float* sDo = sB3;
   {  // every load issued before any use
-    constexpr int ND = BT * VD / 4 / NTH, NK = BT * KD / 4 / NTH, NQ = BT * BT / 4 / NTH;
+    constexpr int ND = BT * VD / 4 / CNTH, NK = BT * KD / 4 / CNTH, NQ = BT * BT / 4 / CNTH;
     f32x4 xd[ND], xk[NK], xg[NK], xq[NQ];
 #pragma unroll
     for (int s2 = 0; s2 < ND; ++s2) {
-      const int i4 = tid + NTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
+      const int i4 = tid + CNTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
       xd[s2] = r < P.C ? ld4(dout + ((P.tok0 + r) * a.Hv + h) * VD + cc) : zero4();
     }
 #pragma unroll
     for (int s2 = 0; s2 < NK; ++s2) {
-      const int i4 = tid + NTH * s2;
+      const int i4 = tid + CNTH * s2;
       xk[s2] = *reinterpret_cast<const f32x4*>(kn + 4 * i4);
       xg[s2] = *reinterpret_cast<const f32x4*>(G + 4 * i4);
     }
 #pragma unroll
-    for (int s2 = 0; s2 < NQ; ++s2) xq[s2] = *reinterpret_cast<const f32x4*>(rec + R.aqk + 4 * (tid + NTH * s2));
+    for (int s2 = 0; s2 < NQ; ++s2) xq[s2] = *reinterpret_cast<const f32x4*>(rec + R.aqk + 4 * (tid + CNTH * s2));
 #pragma unroll
     for (int s2 = 0; s2 < ND; ++s2) {
-      const int i4 = tid + NTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
+      const int i4 = tid + CNTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
       *reinterpret_cast<f32x4*>(&sDo[r * LX + cc]) = xd[s2];
     }
 #pragma unroll
     for (int s2 = 0; s2 < NK; ++s2) {
-      const int i4 = tid + NTH * s2, r = 4 * i4 / KD, cc = 4 * i4 % KD;
+      const int i4 = tid + CNTH * s2, r = 4 * i4 / KD, cc = 4 * i4 % KD;
       f32x4 x;
 #pragma unroll
       for (int p = 0; p < 4; ++p) x[p] = xk[s2][p] * ex2(sGC[cc + p] - xg[s2][p]);
@@ -887,7 +892,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int s2 = 0; s2 < NQ; ++s2) {
-      const int i4 = tid + NTH * s2, r = 4 * i4 / BT, cc = 4 * i4 % BT;
+      const int i4 = tid + CNTH * s2, r = 4 * i4 / BT, cc = 4 * i4 % BT;
       *reinterpret_cast<f32x4*>(&sAq[r * LS + cc]) = xq[s2];
     }
   }
@@ -1028,12 +1033,12 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) sB1[ok.row(t, e) * LX + kc] = -aw[t][e];
   }
 #pragma unroll 8
-  for (int i = tid; i < BT * BT; i += NTH) sS2[(i / BT) * LS + i % BT] = rec[R.A + i];
+  for (int i = tid; i < BT * BT; i += CNTH) sS2[(i / BT) * LS + i % BT] = rec[R.A + i];
   __syncthreads();
   {  // d(b k e^G) = A^T dw: k, b, G
     f32x4 acc[OK::TPW];
     zero(acc);
-    mf_lds<KD>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
+    mf_lds<KD, CNTH / 64>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
                [&](int i, int kk) { return sB1[i * LX + kk]; });
 #pragma unroll
     for (int t = 0; t < OK::TPW; ++t)
@@ -1050,7 +1055,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   {  // d(b v) = A^T dv_new: dv and b
     f32x4 acc[OV::TPW];
     zero(acc);
-    mf_lds<VD>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
+    mf_lds<VD, CNTH / 64>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
                [&](int i, int c) { return sB2[i * LX + c]; });
     f32x4 vv[OV::TPW];   // (all loads before the stores)
 #pragma unroll
@@ -1104,7 +1109,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   {  // dL = -strict_tril(A^T (dA A^T))  -> S3
     f32x4 acc[OS::TPW];
     zero(acc);
-    mf_lds<BT>(acc, BT, tid, [&](int i, int j) { return sS3[i * LS + j]; },
+    mf_lds<BT, CNTH / 64>(acc, BT, tid, [&](int i, int j) { return sS3[i * LS + j]; },
                [&](int j, int m) { return sS2[m * LS + j]; });
     __syncthreads();
 #pragma unroll
@@ -1113,7 +1118,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) sS3[os.row(t, e) * LS + os.col()] = acc[t][e];
     __syncthreads();
     zero(acc);
-    mf_lds<BT>(acc, BT, tid, [&](int l, int i) { return sS2[i * LS + l]; },
+    mf_lds<BT, CNTH / 64>(acc, BT, tid, [&](int l, int i) { return sS2[i * LS + l]; },
                [&](int i, int m) { return sS3[i * LS + m]; });
     __syncthreads();
 #pragma unroll
@@ -1128,8 +1133,8 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   {  // dL and dAqk to the workspace for the pair sums
     float* pr = a.pairs + P.slot * (int64_t)(2 * BT * BT);
 #pragma unroll
-    for (int s = 0; s < BT * BT / 4 / NTH; ++s) {
-      const int i = 4 * (tid + NTH * s), r = i / BT, cc = i % BT;
+    for (int s = 0; s < BT * BT / 4 / CNTH; ++s) {
+      const int i = 4 * (tid + CNTH * s), r = i / BT, cc = i % BT;
       *reinterpret_cast<f32x4*>(pr + i) = *reinterpret_cast<const f32x4*>(&sS3[r * LS + cc]);
       *reinterpret_cast<f32x4*>(pr + BT * BT + i) = *reinterpret_cast<const f32x4*>(&sS1[r * LS + cc]);
     }
@@ -1174,13 +1179,13 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     // dG_C (the chunk decay's gradient) joins the last row: the reverse cumsum
     // over the rows then hands it to every row
     float s = 0.f;
-    for (int r = 0; r < NTH / 64 / OK::NT; ++r) s += sRedK[r * KD + tid];
+    for (int r = 0; r < CNTH / 64 / OK::NT; ++r) s += sRedK[r * KD + tid];
     sB1[(P.C - 1) * LX + tid] += s + ex2(sGC[tid]) * sDD[tid];
   }
   __syncthreads();
   // partial gradients (the pair sums add to them): dG rows, dq, dk
 #pragma unroll 4
-  for (int i = tid; i < BT * KD; i += NTH) {
+  for (int i = tid; i < BT * KD; i += CNTH) {
     const int r = i / KD, cc = i % KD;
     if (r < P.C) a.dg_nat[((P.tok0 + r) * a.Hv + h) * KD + cc] = sB1[r * LX + cc];
   }
@@ -1611,7 +1616,7 @@ hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int6
     switch (stage) {                                                                                    \
       case 0: return nb_chunk ? launch(bwd_prep_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
       case 1: return nb_scan ? launch(bwd_scan_kernel<KK, VV, TT>, dim3(nb_scan), dim3(NTH), s, a) : hipSuccess;   \
-      case 2: return nb_chunk ? launch(bwd_chunk_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
+      case 2: return nb_chunk ? launch(bwd_chunk_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(CNTH), s, a) : hipSuccess; \
       case 3: return nb_qk ? launch(bwd_qk_kernel<KK, TT>, dim3(nb_qk), dim3(64), s, a, tokens) : hipSuccess;       \
       case 4: return nblk ? launch(bwd_gate_kernel<KK, TT>, dim3(nblk * a.Hv), dim3(KK), s, a, tokens, part)        \
                           : hipSuccess;                                                                 \
