@@ -60,73 +60,11 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 constexpr float LOG2E_F = 1.4426950408889634f;
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
 
-// Workgroups of NTH threads (8 waves: two per SIMD, so that LDS and memory
-// latency is hidden while the other wave computes); thread t = 16 tm + tn owns
-// rows tm + RS a and columns tn + 16 b of a product.
-constexpr int NTH = 512, RS = NTH / 16;
-
-// acc[a][b] += sum_{k < kr} A(tm + RS a, k) * B(k, tn + 16 b): register-blocked.
-template <int MR, int NR, typename FA, typename FB>
-__device__ __forceinline__ void mm(float (&acc)[MR][NR], int kr, int tm, int tn, FA A, FB B) {
-#pragma unroll 4
-  for (int k = 0; k < kr; ++k) {
-    float a[MR], b[NR];
-#pragma unroll
-    for (int i = 0; i < MR; ++i) a[i] = A(tm + RS * i, k);
-#pragma unroll
-    for (int j = 0; j < NR; ++j) b[j] = B(k, tn + 16 * j);
-#pragma unroll
-    for (int i = 0; i < MR; ++i)
-#pragma unroll
-      for (int j = 0; j < NR; ++j) acc[i][j] += a[i] * b[j];
-  }
-}
-// The same product with both operands read from global memory through an
-// LDS staging buffer, KB reduction indices at a time: every thread loads its
-// share of the A block (RS MR x KB) and the B block (KB x 16 NR) back to back,
-// consecutive threads on the operand's contiguous index (CKA / CKB: the source
-// is contiguous along the reduction index; else along rows of A / columns of B).
-template <int MR, int NR, int KB, bool CKA, bool CKB, int CAP, typename FA, typename FB>
-__device__ __forceinline__ void mm_staged(float (&acc)[MR][NR], int kr, int tid, FA A, FB B, float* stage) {
-  constexpr int M = RS * MR, N = 16 * NR, LA = KB + 1, LB = N + 1;
-  static_assert(M * LA + KB * LB <= CAP, "the staged blocks fit the staging buffer");
-  float* sa = stage;
-  float* sb = stage + M * LA;
-  const int tm = tid >> 4, tn = tid & 15;
-  for (int k0 = 0; k0 < kr; k0 += KB) {
-#pragma unroll
-    for (int e = tid; e < M * KB; e += NTH) {
-      const int m = CKA ? e / KB : e % M, kk = CKA ? e % KB : e / M;
-      sa[m * LA + kk] = A(m, k0 + kk);
-    }
-#pragma unroll
-    for (int e = tid; e < KB * N; e += NTH) {
-      const int n = CKB ? e / KB : e % N, kk = CKB ? e % KB : e / N;
-      sb[kk * LB + n] = B(k0 + kk, n);
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < KB; ++kk) {
-      float a[MR], b[NR];
-#pragma unroll
-      for (int i = 0; i < MR; ++i) a[i] = sa[(tm + RS * i) * LA + kk];
-#pragma unroll
-      for (int j = 0; j < NR; ++j) b[j] = sb[kk * LB + tn + 16 * j];
-#pragma unroll
-      for (int i = 0; i < MR; ++i)
-#pragma unroll
-        for (int j = 0; j < NR; ++j) acc[i][j] += a[i] * b[j];
-    }
-    __syncthreads();
-  }
-}
-template <int MR, int NR>
-__device__ __forceinline__ void zero(float (&acc)[MR][NR]) {
-#pragma unroll
-  for (int i = 0; i < MR; ++i)
-#pragma unroll
-    for (int j = 0; j < NR; ++j) acc[i][j] = 0.f;
-}
+// Workgroups of NTH threads: 16 waves, four per SIMD.  The kernels run one
+// workgroup per CU (their LDS is 100 - 160 KB), so the extra waves are what
+// hides the latency of each phase's loads; each wave owns fewer output tiles,
+// which keeps its accumulators within 128 registers.
+constexpr int NTH = 1024;
 
 struct ChunkPos {
   int n, C;
@@ -157,9 +95,9 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 // Tiles of a R x V state-shaped output (R = 64 or K rows, V columns), eight
 // waves: wave w owns tiles w * TPW + t (t < TPW), so that all its tiles lie in
 // one block of 16 rows (rb) and consecutive column blocks (cb).
-template <int R, int V>
+template <int R, int V, int NW = NTH / 64>
 struct STiles {
-  static constexpr int NCB = V / 16, NT = (R / 16) * NCB, TPW = NT / (NTH / 64);
+  static constexpr int NCB = V / 16, NT = (R / 16) * NCB, TPW = NT / NW;
   static_assert(NCB % TPW == 0 || TPW % NCB == 0, "a wave's tiles share one row block");
   int rb, cb0, r16, q;
   __device__ explicit STiles(int tid) : r16(tid & 15), q((tid >> 4) & 3) {
@@ -168,21 +106,26 @@ struct STiles {
     cb0 = T0 % NCB;
   }
 };
-static_assert(STiles<128, 128>::TPW == 8 && STiles<64, 128>::TPW == 4 && STiles<64, 64>::TPW == 2,
+static_assert(STiles<128, 128>::TPW == 4 && STiles<64, 128>::TPW == 2 && STiles<64, 64>::TPW == 1,
               "tile counts per wave");
 
 // The chunk-entry states for the backward, in fp32 from the fp32 records:
 // h <- D h + kg^T (u - w h), every entry state stored.  One workgroup per
 // (sequence, head); h lives in LDS, the products run on the fp32 matrix cores
 // (wave w: row block w of the update, v_new tiles of row block w / 2).
+// The two state scans keep 8 waves (two per SIMD): with 16, the reverse
+// scan's tiles and operands do not fit 128 registers, and the forward one
+// measured slower.
+constexpr int SNTH = 512;
+
 template <int KD, int VD>
-__global__ __launch_bounds__(NTH) void bwd_state_kernel(BwdArgs a) {
+__global__ __launch_bounds__(SNTH) void bwd_state_kernel(BwdArgs a) {
   constexpr int LH = VD + 4;
   __shared__ __attribute__((aligned(16))) float sH[KD * LH];
   __shared__ __attribute__((aligned(16))) float sVN[BT * LH];
   __shared__ float sGC[KD];
-  using TV = STiles<BT, VD>;   // v_new
-  using TH = STiles<KD, VD>;   // h
+  using TV = STiles<BT, VD, SNTH / 64>;   // v_new
+  using TH = STiles<KD, VD, SNTH / 64>;   // h
   static_assert(TH::TPW <= TH::NCB && TV::TPW <= TV::NCB, "one row block per wave");
   constexpr BwdRec R = bwd_rec(KD, VD);
   const int h = blockIdx.x % a.Hv, n = blockIdx.x / a.Hv, tid = threadIdx.x;
@@ -193,7 +136,7 @@ __global__ __launch_bounds__(NTH) void bwd_state_kernel(BwdArgs a) {
   seq_range(a.seq, n, tok0s, len);
   const int nck = (len + BT - 1) / BT;
   const int cb = chunk_base(a.seq, n);
-  for (int i = tid; i < KD * VD; i += NTH)
+  for (int i = tid; i < KD * VD; i += SNTH)
     sH[(i / VD) * LH + i % VD] = a.h0 ? a.h0[((int64_t)n * a.Hv + h) * (KD * VD) + i] : 0.f;
   __syncthreads();
   for (int c = 0; c < nck; ++c) {
@@ -270,14 +213,14 @@ __global__ __launch_bounds__(NTH) void bwd_state_kernel(BwdArgs a) {
 // dh = qg^T do + D dh' - w^T dv_new, every chunk's exit gradient stored.  One
 // workgroup per (sequence, head), dh in LDS, fp32 matrix cores as above.
 template <int KD, int VD, typename IT>
-__global__ __launch_bounds__(NTH) void bwd_scan_kernel(BwdArgs a) {
+__global__ __launch_bounds__(SNTH) void bwd_scan_kernel(BwdArgs a) {
   constexpr int LH = VD + 4;
   __shared__ __attribute__((aligned(16))) float sDH[KD * LH];
   __shared__ __attribute__((aligned(16))) float sDV[BT * LH];
   __shared__ __attribute__((aligned(16))) float sDo[BT * LH];
   __shared__ float sGC[KD];
-  using TV = STiles<BT, VD>;
-  using TH = STiles<KD, VD>;
+  using TV = STiles<BT, VD, SNTH / 64>;
+  using TH = STiles<KD, VD, SNTH / 64>;
   static_assert(TH::TPW <= TH::NCB && TV::TPW <= TV::NCB, "one row block per wave");
   constexpr BwdRec R = bwd_rec(KD, VD);
   const int h = blockIdx.x % a.Hv, n = blockIdx.x / a.Hv, tid = threadIdx.x;
@@ -289,7 +232,7 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(BwdArgs a) {
   const int nck = (len + BT - 1) / BT;
   const int cb = chunk_base(a.seq, n);
   const IT* dout = static_cast<const IT*>(a.dout);
-  for (int i = tid; i < KD * VD; i += NTH)   // dh' of the last chunk: the final state's gradient
+  for (int i = tid; i < KD * VD; i += SNTH)   // dh' of the last chunk: the final state's gradient
     sDH[(i / VD) * LH + i % VD] = a.dht ? a.dht[((int64_t)n * a.Hv + h) * (KD * VD) + i] : 0.f;
   __syncthreads();
   for (int c = nck - 1; c >= 0; --c) {
@@ -307,7 +250,7 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(BwdArgs a) {
         if (a.dh_store) a.dh_store[slot * (int64_t)(KD * VD) + kk * VD + j] = dold[t][e];
       }
     if (tid < KD) sGC[tid] = rec[R.G + (C - 1) * KD + tid];
-    for (int i = tid; i < BT * VD; i += NTH) {
+    for (int i = tid; i < BT * VD; i += SNTH) {
       const int r = i / VD, cc = i % VD;
       sDo[r * LH + cc] = r < C ? ldf(dout + ((tok0 + r) * a.Hv + h) * VD + cc) : 0.f;
     }
@@ -382,7 +325,7 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(BwdArgs a) {
     __syncthreads();
   }
   if (a.dh0)
-    for (int i = tid; i < KD * VD; i += NTH)
+    for (int i = tid; i < KD * VD; i += SNTH)
       a.dh0[((int64_t)n * a.Hv + h) * (KD * VD) + i] = sDH[(i / VD) * LH + i % VD];
 }
 
@@ -420,12 +363,13 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
   const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;
   const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
 
-  // ---- gate, norms, beta: rows r = tid / 8, channels CPT * (tid % 8) .. +CPT-1.
+  // ---- gate, norms, beta: rows r = tid / TPR, channels CPT * (tid % TPR) .. +CPT-1.
   // softplus in log2 form on the transcendental unit: softplus(z) = max(z, 0)
   // + ln2 log2(1 + 2^(-|z| log2 e)); the decay is kept in log2 units
   {
-    const int r = tid >> 3, part = tid & 7;
-    constexpr int CPT = KD / 8;
+    constexpr int TPR = NTH / BT, CPT = KD / TPR;   // threads per row, channels per thread
+    static_assert(CPT % 4 == 0 && (TPR & (TPR - 1)) == 0, "whole 4-channel pieces per thread");
+    const int r = tid / TPR, part = tid % TPR;
     const bool live = r < P.C;
     float kr[CPT], qr[CPT], gr[CPT], br[CPT];
     if (live) {
@@ -469,7 +413,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
       }
       sG[r * LX + part * CPT + e] = fmaxf(gl, lb2);    // log2 units
     }
-    for (int m = 1; m < 8; m <<= 1) {
+    for (int m = 1; m < TPR; m <<= 1) {
       skk += __shfl_xor(skk, m);
       sqq += __shfl_xor(sqq, m);
       sqk += __shfl_xor(sqk, m);
@@ -725,65 +669,9 @@ struct Own {
   __device__ int col() const { return 16 * (w % NT) + r16; }
   __device__ int row(int t, int e) const { return 16 * ti(t) + 4 * q + e; }
 };
-static_assert(Own<64>::TPW == 2 && Own<128>::TPW == 4, "eight waves cover a 64-row output");
+static_assert(Own<64>::TPW == 1 && Own<128>::TPW == 2, "sixteen waves cover a 64-row output");
 
 
-// acc += A (64 x kr) * B (kr x N), both read through an LDS staging buffer KB
-// reduction indices at a time (A as [row][k], B as [col][k], so that a lane
-// reads four consecutive reduction values with one 16-byte access).  The next
-// block's values are fetched into registers while the current block is
-// multiplied.  CKA / CKB: the source is contiguous along the reduction index
-// (else along A's rows / B's columns), so consecutive threads fetch
-// consecutive addresses.  kr must be a multiple of KB.
-template <int N, int KB, bool CKA, bool CKB, int CAP, typename FA, typename FB>
-__device__ __forceinline__ void mf_staged(f32x4 (&acc)[Own<N>::TPW], int kr, int tid, FA A, FB B,
-                                          float* stage) {
-  constexpr int L = KB + 4, NA = BT * KB / NTH, NB = N * KB / NTH;
-  static_assert(BT * L + N * L <= CAP, "the staged blocks fit the staging buffer");
-  static_assert(BT * KB % NTH == 0 && N * KB % NTH == 0 && KB % 16 == 0, "whole blocks per thread");
-  float* sa = stage;
-  float* sb = stage + BT * L;
-  const Own<N> o(tid);
-  float ra[NA], rb[NB];
-  auto fetch = [&](int k0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < NA; ++s) {
-      const int e = tid + NTH * s, m = CKA ? e / KB : e % BT, kk = CKA ? e % KB : e / BT;
-      ra[s] = A(m, k0 + kk);
-    }
-#pragma unroll
-    for (int s = 0; s < NB; ++s) {
-      const int e = tid + NTH * s, n = CKB ? e / KB : e % N, kk = CKB ? e % KB : e / N;
-      rb[s] = B(k0 + kk, n);
-    }
-  };
-  fetch(0);
-  for (int k0 = 0; k0 < kr; k0 += KB) {
-#pragma unroll
-    for (int s = 0; s < NA; ++s) {
-      const int e = tid + NTH * s, m = CKA ? e / KB : e % BT, kk = CKA ? e % KB : e / BT;
-      sa[m * L + kk] = ra[s];
-    }
-#pragma unroll
-    for (int s = 0; s < NB; ++s) {
-      const int e = tid + NTH * s, n = CKB ? e / KB : e % N, kk = CKB ? e % KB : e / N;
-      sb[n * L + kk] = rb[s];
-    }
-    __syncthreads();
-    if (k0 + KB < kr) fetch(k0 + KB);
-#pragma unroll
-    for (int kk = 0; kk < KB; kk += 16) {
-      const f32x4 b = *reinterpret_cast<const f32x4*>(&sb[o.col() * L + kk + 4 * o.q]);
-#pragma unroll
-      for (int t = 0; t < Own<N>::TPW; ++t) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(&sa[(16 * o.ti(t) + o.r16) * L + kk + 4 * o.q]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], b[p], acc[t]);
-      }
-    }
-    __syncthreads();
-  }
-}
 // acc += A (64 x kr) * B (kr x N) with both operands read element by element
 // (from LDS) through accessors.
 template <int N, int NW, typename FA, typename FB>
@@ -813,12 +701,8 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// The chunk kernel runs 16 waves (four per SIMD): each owns fewer output tiles, so
-// its accumulators fit, and the extra waves hide the load latency of its phases.
-constexpr int CNTH = 1024;
-
 template <int KD, int VD, typename IT>
-__global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   static_assert(KD == 128 || KD == 64, "K");
   constexpr int MX = KD > VD ? KD : VD;
   constexpr int LX = MX + 4;        // row stride of the 64-row matrices (16-byte aligned rows)
@@ -835,10 +719,10 @@ __global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
   float* sKG = sSm;                 // [64][LX] kg = k 2^(G_C - G) (until dv_new)
   float* sAq = sSm + BT * LX;       // [64][LS] Aqk (until dv_new)
   static_assert(BT * LX + BT * LS <= 3 * BT * LS, "kg and Aqk fit the small matrices' space");
-  using OK = Own<KD, CNTH / 64>;
-  using OV = Own<VD, CNTH / 64>;
-  using OS = Own<BT, CNTH / 64>;
-  static_assert((OK::NT + OV::NT) * BT <= BT * LS && (CNTH / 64 / OK::NT) * KD <= BT * LS,
+  using OK = Own<KD>;
+  using OV = Own<VD>;
+  using OS = Own<BT>;
+  static_assert((OK::NT + OV::NT) * BT <= BT * LS && (NTH / 64 / OK::NT) * KD <= BT * LS,
                 "reduction buffers fit the small matrices");
   constexpr BwdRec R = bwd_rec(KD, VD);
   const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
@@ -862,29 +746,29 @@ __global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
   // staged once: do (fp32) into B3, kg and Aqk into the small matrices' space
   float* sDo = sB3;
   {  // every load issued before any use
-    constexpr int ND = BT * VD / 4 / CNTH, NK = BT * KD / 4 / CNTH, NQ = BT * BT / 4 / CNTH;
+    constexpr int ND = BT * VD / 4 / NTH, NK = BT * KD / 4 / NTH, NQ = BT * BT / 4 / NTH;
     f32x4 xd[ND], xk[NK], xg[NK], xq[NQ];
 #pragma unroll
     for (int s2 = 0; s2 < ND; ++s2) {
-      const int i4 = tid + CNTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
+      const int i4 = tid + NTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
       xd[s2] = r < P.C ? ld4(dout + ((P.tok0 + r) * a.Hv + h) * VD + cc) : zero4();
     }
 #pragma unroll
     for (int s2 = 0; s2 < NK; ++s2) {
-      const int i4 = tid + CNTH * s2;
+      const int i4 = tid + NTH * s2;
       xk[s2] = *reinterpret_cast<const f32x4*>(kn + 4 * i4);
       xg[s2] = *reinterpret_cast<const f32x4*>(G + 4 * i4);
     }
 #pragma unroll
-    for (int s2 = 0; s2 < NQ; ++s2) xq[s2] = *reinterpret_cast<const f32x4*>(rec + R.aqk + 4 * (tid + CNTH * s2));
+    for (int s2 = 0; s2 < NQ; ++s2) xq[s2] = *reinterpret_cast<const f32x4*>(rec + R.aqk + 4 * (tid + NTH * s2));
 #pragma unroll
     for (int s2 = 0; s2 < ND; ++s2) {
-      const int i4 = tid + CNTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
+      const int i4 = tid + NTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
       *reinterpret_cast<f32x4*>(&sDo[r * LX + cc]) = xd[s2];
     }
 #pragma unroll
     for (int s2 = 0; s2 < NK; ++s2) {
-      const int i4 = tid + CNTH * s2, r = 4 * i4 / KD, cc = 4 * i4 % KD;
+      const int i4 = tid + NTH * s2, r = 4 * i4 / KD, cc = 4 * i4 % KD;
       f32x4 x;
 #pragma unroll
       for (int p = 0; p < 4; ++p) x[p] = xk[s2][p] * ex2(sGC[cc + p] - xg[s2][p]);
@@ -892,7 +776,7 @@ __global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int s2 = 0; s2 < NQ; ++s2) {
-      const int i4 = tid + CNTH * s2, r = 4 * i4 / BT, cc = 4 * i4 % BT;
+      const int i4 = tid + NTH * s2, r = 4 * i4 / BT, cc = 4 * i4 % BT;
       *reinterpret_cast<f32x4*>(&sAq[r * LS + cc]) = xq[s2];
     }
   }
@@ -1033,12 +917,12 @@ __global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) sB1[ok.row(t, e) * LX + kc] = -aw[t][e];
   }
 #pragma unroll 8
-  for (int i = tid; i < BT * BT; i += CNTH) sS2[(i / BT) * LS + i % BT] = rec[R.A + i];
+  for (int i = tid; i < BT * BT; i += NTH) sS2[(i / BT) * LS + i % BT] = rec[R.A + i];
   __syncthreads();
   {  // d(b k e^G) = A^T dw: k, b, G
     f32x4 acc[OK::TPW];
     zero(acc);
-    mf_lds<KD, CNTH / 64>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
+    mf_lds<KD, NTH / 64>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
                [&](int i, int kk) { return sB1[i * LX + kk]; });
 #pragma unroll
     for (int t = 0; t < OK::TPW; ++t)
@@ -1055,7 +939,7 @@ __global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
   {  // d(b v) = A^T dv_new: dv and b
     f32x4 acc[OV::TPW];
     zero(acc);
-    mf_lds<VD, CNTH / 64>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
+    mf_lds<VD, NTH / 64>(acc, BT, tid, [&](int j, int i) { return sS2[i * LS + j]; },
                [&](int i, int c) { return sB2[i * LX + c]; });
     f32x4 vv[OV::TPW];   // (all loads before the stores)
 #pragma unroll
@@ -1109,7 +993,7 @@ __global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
   {  // dL = -strict_tril(A^T (dA A^T))  -> S3
     f32x4 acc[OS::TPW];
     zero(acc);
-    mf_lds<BT, CNTH / 64>(acc, BT, tid, [&](int i, int j) { return sS3[i * LS + j]; },
+    mf_lds<BT, NTH / 64>(acc, BT, tid, [&](int i, int j) { return sS3[i * LS + j]; },
                [&](int j, int m) { return sS2[m * LS + j]; });
     __syncthreads();
 #pragma unroll
@@ -1118,7 +1002,7 @@ __global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) sS3[os.row(t, e) * LS + os.col()] = acc[t][e];
     __syncthreads();
     zero(acc);
-    mf_lds<BT, CNTH / 64>(acc, BT, tid, [&](int l, int i) { return sS2[i * LS + l]; },
+    mf_lds<BT, NTH / 64>(acc, BT, tid, [&](int l, int i) { return sS2[i * LS + l]; },
                [&](int i, int m) { return sS3[i * LS + m]; });
     __syncthreads();
 #pragma unroll
@@ -1133,8 +1017,8 @@ __global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
   {  // dL and dAqk to the workspace for the pair sums
     float* pr = a.pairs + P.slot * (int64_t)(2 * BT * BT);
 #pragma unroll
-    for (int s = 0; s < BT * BT / 4 / CNTH; ++s) {
-      const int i = 4 * (tid + CNTH * s), r = i / BT, cc = i % BT;
+    for (int s = 0; s < BT * BT / 4 / NTH; ++s) {
+      const int i = 4 * (tid + NTH * s), r = i / BT, cc = i % BT;
       *reinterpret_cast<f32x4*>(pr + i) = *reinterpret_cast<const f32x4*>(&sS3[r * LS + cc]);
       *reinterpret_cast<f32x4*>(pr + BT * BT + i) = *reinterpret_cast<const f32x4*>(&sS1[r * LS + cc]);
     }
@@ -1179,13 +1063,13 @@ __global__ __launch_bounds__(CNTH) void bwd_chunk_kernel(BwdArgs a) {
     // dG_C (the chunk decay's gradient) joins the last row: the reverse cumsum
     // over the rows then hands it to every row
     float s = 0.f;
-    for (int r = 0; r < CNTH / 64 / OK::NT; ++r) s += sRedK[r * KD + tid];
+    for (int r = 0; r < NTH / 64 / OK::NT; ++r) s += sRedK[r * KD + tid];
     sB1[(P.C - 1) * LX + tid] += s + ex2(sGC[tid]) * sDD[tid];
   }
   __syncthreads();
   // partial gradients (the pair sums add to them): dG rows, dq, dk
 #pragma unroll 4
-  for (int i = tid; i < BT * KD; i += CNTH) {
+  for (int i = tid; i < BT * KD; i += NTH) {
     const int r = i / KD, cc = i % KD;
     if (r < P.C) a.dg_nat[((P.tok0 + r) * a.Hv + h) * KD + cc] = sB1[r * LX + cc];
   }
@@ -1615,13 +1499,13 @@ hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int6
   if (K == KK && V == VV) {                                                                             \
     switch (stage) {                                                                                    \
       case 0: return nb_chunk ? launch(bwd_prep_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
-      case 1: return nb_scan ? launch(bwd_scan_kernel<KK, VV, TT>, dim3(nb_scan), dim3(NTH), s, a) : hipSuccess;   \
-      case 2: return nb_chunk ? launch(bwd_chunk_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(CNTH), s, a) : hipSuccess; \
+      case 1: return nb_scan ? launch(bwd_scan_kernel<KK, VV, TT>, dim3(nb_scan), dim3(SNTH), s, a) : hipSuccess;  \
+      case 2: return nb_chunk ? launch(bwd_chunk_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
       case 3: return nb_qk ? launch(bwd_qk_kernel<KK, TT>, dim3(nb_qk), dim3(64), s, a, tokens) : hipSuccess;       \
       case 4: return nblk ? launch(bwd_gate_kernel<KK, TT>, dim3(nblk * a.Hv), dim3(KK), s, a, tokens, part)        \
                           : hipSuccess;                                                                 \
       case 5: return launch(bwd_gate_sum_kernel<KK>, dim3(a.Hv), dim3(KK), s, a, nblk, (const float*)part);       \
-      case 6: return nb_scan ? launch(bwd_state_kernel<KK, VV>, dim3(nb_scan), dim3(NTH), s, a) : hipSuccess;       \
+      case 6: return nb_scan ? launch(bwd_state_kernel<KK, VV>, dim3(nb_scan), dim3(SNTH), s, a) : hipSuccess;      \
       case 7: return nb_chunk ? launch(bwd_pairs_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
     }                                                                                                   \
     return hipErrorInvalidValue;                                                                        \
