@@ -103,9 +103,16 @@ def test_bwd_fp32_tiny(gpu_lib):
     bwd_case(gpu_lib, ks.make("tiny"))
 
 
-@pytest.mark.parametrize("K,V", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("K,V", [(64, 128), (128, 64), (64, 64)])
 def test_bwd_head_dims(gpu_lib, K, V):
     bwd_case(gpu_lib, ks.make("layer", T=100, H=2, K=K, V=V))
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 128)])
+def test_bwd_fp32_layer_gate(gpu_lib, K, V):
+    """fp32 token tensors with the in-kernel gate, L2Norm and sigmoid, several
+    chunks and a ragged tail (the fp32 instantiations of every backward kernel)."""
+    bwd_case(gpu_lib, ks.make("layer", T=150, H=2, K=K, V=V, dtype="f32"))
 
 
 def test_bwd_T65_strong_decay_final_state_loss(gpu_lib):
