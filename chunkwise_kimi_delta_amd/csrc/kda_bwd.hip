@@ -7,9 +7,13 @@
 // inter-chunk recurrence of the state gradient, the WY / intra-chunk
 // backward and the reverse cumsum of the gate gradient) and 2.5 (the gate
 // backward), and "Hyper-Parallel Chunk KDA" section 5.2 (backward stages).
-// All arithmetic is fp32; the decay ratios exp(G_i - G_j) of a chunk are
-// formed pair by pair with non-positive exponents (G is the in-chunk
-// natural-log cumsum, non-increasing), so no range split is needed.
+// All arithmetic is fp32 (the products on the fp32 matrix cores).  The decay
+// ratios exp(G_i - G_j) of a chunk are never formed from a positive exponent:
+// a block of rows against an earlier block splits at the later block's first
+// row r into 2^(G_i - G_r) 2^(G_r - G_j), both <= 1 (G is the in-chunk cumsum,
+// non-increasing), and the pairs inside a 16-row block are split further at
+// the levels of a binary split, so prescaled operands turn the pair sums into
+// plain matrix products for any decay.
 //
 // Per chunk (rows i < C, h the chunk-entry state, h' its exit state):
 //   v_new = u - w h,   o = qg h + Aqk v_new,   h' = D h + kg^T v_new
@@ -25,11 +29,14 @@
 //
 // Kernels:
 //   bwd_prep_kernel   (chunk, head): gate, norms, sigmoid, G, L, Aqk, A, u, w -> fp32 record
-//   bwd_state_kernel  (sequence, head, 32 columns): the forward state recurrence in
-//                     fp32, storing every chunk-entry state
-//   bwd_scan_kernel   (sequence, head, 32 columns): the reverse recurrence of dh,
-//                     storing each chunk's exit gradient; dh0 at the end
-//   bwd_chunk_kernel  (chunk, head): everything chunk-local
+//   bwd_state_kernel  (sequence, head): the forward state recurrence in fp32, storing
+//                     every chunk-entry state
+//   bwd_scan_kernel   (sequence, head): the reverse recurrence of dh, storing each
+//                     chunk's exit gradient; dh0 at the end
+//   bwd_chunk_kernel  (chunk, head): the chunk-local products; dL and dAqk out, partial
+//                     gradients of q, k, G and beta
+//   bwd_pairs_kernel  (chunk, head): the pair sums of dL and dAqk into those partials,
+//                     then the reverse cumsum of the gate gradient
 //   bwd_qk_kernel     (token, q/k head): grouped-head sum and L2Norm backward
 //   bwd_gate_kernel / bwd_gate_sum_kernel: gate and sigmoid backward, dA_log and
 //                     dt_bias sums (two passes, fixed order: deterministic)
