@@ -7,7 +7,9 @@
 // inter-chunk recurrence of the state gradient, the WY / intra-chunk
 // backward and the reverse cumsum of the gate gradient) and 2.5 (the gate
 // backward), and "Hyper-Parallel Chunk KDA" section 5.2 (backward stages).
-// All arithmetic is fp32 (the products on the fp32 matrix cores).  The decay
+// All arithmetic is fp32: the chunk-local products on the fp32 matrix cores,
+// the two state scans on bf16 hi/lo operand pairs (~16 significant bits per
+// operand, fp32 accumulation, three passes per product).  The decay
 // ratios exp(G_i - G_j) of a chunk are never formed from a positive exponent:
 // a block of rows against an earlier block splits at the later block's first
 // row r into 2^(G_i - G_r) 2^(G_r - G_j), both <= 1 (G is the in-chunk cumsum,
@@ -29,8 +31,8 @@
 //
 // Kernels:
 //   bwd_prep_kernel   (chunk, head): gate, norms, sigmoid, G, L, Aqk, A, u, w -> fp32 record
-//   bwd_state_kernel  (sequence, head): the forward state recurrence in fp32, storing
-//                     every chunk-entry state
+//   bwd_state_kernel  (sequence, head): the forward state recurrence, storing every
+//                     chunk-entry state
 //   bwd_scan_kernel   (sequence, head): the reverse recurrence of dh, storing each
 //                     chunk's exit gradient; dh0 at the end
 //   bwd_chunk_kernel  (chunk, head): the chunk-local products; dL and dAqk out, partial
@@ -98,9 +100,8 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// ------------------------------------------------------ forward state scan
-// Tiles of a R x V state-shaped output (R = 64 or K rows, V columns), eight
-// waves: wave w owns tiles w * TPW + t (t < TPW), so that all its tiles lie in
+// ------------------------------------------------------ tile ownership
+// Tiles of a R x V output (R = 64 or K rows, V columns) over NW waves: wave w owns tiles w * TPW + t (t < TPW), so that all its tiles lie in
 // one block of 16 rows (rb) and consecutive column blocks (cb).
 template <int R, int V, int NW = NTH / 64>
 struct STiles {
@@ -116,224 +117,422 @@ struct STiles {
 static_assert(STiles<128, 128>::TPW == 4 && STiles<64, 128>::TPW == 2 && STiles<64, 64>::TPW == 1,
               "tile counts per wave");
 
-// The chunk-entry states for the backward, in fp32 from the fp32 records:
-// h <- D h + kg^T (u - w h), every entry state stored.  One workgroup per
-// (sequence, head); h lives in LDS, the products run on the fp32 matrix cores
-// (wave w: row block w of the update, v_new tiles of row block w / 2).
-// The two state scans keep 8 waves (two per SIMD): with 16, the reverse
-// scan's tiles and operands do not fit 128 registers, and the forward one
-// measured slower.
-constexpr int SNTH = 512;
+// ------------------------------------------------------ state scans
+// Both state scans run one workgroup per (sequence, head) with VD / 16 waves
+// and keep the K x V state in registers: wave w owns column block w (16
+// columns), KD / 16 accumulator tiles in which lane l holds rows
+// 16 t + 4 (l / 16) + e of column 16 w + l % 16.  A chunk's operands are
+// staged once in LDS as matrix-core fragments of bf16 hi/lo pairs (hi =
+// bf16(x), lo = bf16(x - hi): ~16 significant bits), and every product is
+// three passes of v_mfma_f32_16x16x32_bf16 (hi.hi + lo.hi + hi.lo) into fp32
+// accumulators.  Inside each aligned block of 32 the reduction index x sits
+// in lane group (x & 15) >> 2, slot 4 (x >> 4) + (x & 3) of a fragment, so
+// that two accumulator tiles of 16 rows are, as they are, the B operand of a
+// product that reduces over those 32 rows: the state and v_new (dv_new) feed
+// the next product without leaving the registers, and nothing but the
+// chunk's operand staging needs a barrier.
+// The stored chunk states and gradients (K x V fp32 per chunk) keep four
+// consecutive rows of a column together: element (k, v) at sq_index(k, v), so
+// that an accumulator tile's four rows of a column are one 16-byte store.
+__host__ __device__ constexpr int sq_index(int k, int v, int V) { return ((k >> 2) * V + v) * 4 + (k & 3); }
+constexpr int FRB = 2048;   // bytes of one fragment in LDS: hi (64 lanes x 16 B), then lo
 
+// reduction index (inside its block of 32) of slot j of lane group g
+__device__ __forceinline__ int sg_index(int g, int j) { return ((j >> 2) << 4) | (g << 2) | (j & 3); }
+
+__device__ __forceinline__ Frag frag_get(const unsigned char* f, int lane) {
+  Frag r;
+  r.hi = *reinterpret_cast<const bf16x8*>(f + 16 * lane);
+  r.lo = *reinterpret_cast<const bf16x8*>(f + 1024 + 16 * lane);
+  return r;
+}
+__device__ __forceinline__ void frag_put(unsigned char* f, int lane, const Frag& x) {
+  *reinterpret_cast<bf16x8*>(f + 16 * lane) = x.hi;
+  *reinterpret_cast<bf16x8*>(f + 1024 + 16 * lane) = x.lo;
+}
+// acc += a b, both operands split (the lo.lo term, below 2^-16 of the
+// product, is dropped)
+__device__ __forceinline__ f32x4 mma3(const Frag& a, const Frag& b, f32x4 acc) {
+  acc = mfma(a.hi, b.hi, acc);
+  acc = mfma(a.lo, b.hi, acc);
+  return mfma(a.hi, b.lo, acc);
+}
+// This wave's LDS writes done before its next LDS reads (a wave's LDS
+// operations complete in order; this also keeps the compiler from moving
+// reads above the writes)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+// Fragments whose reduction runs along the rows of a row-major source S
+// (A[c][t] = S[t][c], or a B operand B[t][c]) for the 16 columns c and 32
+// rows t of one block of S are transposed in their own LDS: the wave first
+// stages the block there (row t at 64 t bytes; lane l holds row l / 2,
+// columns 8 (l % 2) .. +7), then each lane reads its column at its eight
+// rows and overwrites the staging with the split fragment.
+__device__ __forceinline__ void stage_t(unsigned char* f, int lane, const float (&x)[8]) {
+  float* st = reinterpret_cast<float*>(f) + 8 * lane;
+  *reinterpret_cast<f32x4*>(st) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(st + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+__device__ __forceinline__ void gather_t(const unsigned char* f, int lane, float (&y)[8]) {
+  const float* st = reinterpret_cast<const float*>(f);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = st[16 * sg_index(lane >> 4, j) + (lane & 15)];
+}
+// the same for a bf16 source, hi part only (1 KiB: row t at 32 t bytes)
+__device__ __forceinline__ void stage_t16(unsigned char* f, int lane, const u32x4& x) {
+  *reinterpret_cast<u32x4*>(f + 16 * lane) = x;
+}
+__device__ __forceinline__ bf16x8 gather_t16(const unsigned char* f, int lane) {
+  const bf16_t* st = reinterpret_cast<const bf16_t*>(f);
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = (uint32_t)st[16 * sg_index(lane >> 4, 2 * j) + (lane & 15)] |
+           ((uint32_t)st[16 * sg_index(lane >> 4, 2 * j + 1) + (lane & 15)] << 16);
+  return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
+__device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
+  const f32x4 a = ld4(p), b = ld4(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+// eight values at p[0..3] and p[16..19]: the slots of lane group g of a
+// fragment whose reduction index runs along the row (p = row + 32 kb + 4 g)
+__device__ __forceinline__ void ld8s(const float* p, float (&x)[8]) {
+  const f32x4 a = ld4(p), b = ld4(p + 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+
+// The chunk-entry states for the backward, in fp32 from the fp32 records:
+// h <- D h + kg^T (u - w h), every entry state stored.  Operands per chunk:
+// -w as A[token][K] and kg^T = (k 2^(G_C - G))^T as A[K][token].
 template <int KD, int VD>
-__global__ __launch_bounds__(SNTH) void bwd_state_kernel(BwdArgs a) {
-  constexpr int LH = VD + 4;
-  __shared__ __attribute__((aligned(16))) float sH[KD * LH];
-  __shared__ __attribute__((aligned(16))) float sVN[BT * LH];
-  __shared__ float sGC[KD];
-  using TV = STiles<BT, VD, SNTH / 64>;   // v_new
-  using TH = STiles<KD, VD, SNTH / 64>;   // h
-  static_assert(TH::TPW <= TH::NCB && TV::TPW <= TV::NCB, "one row block per wave");
+__global__ __launch_bounds__(VD * 4) void bwd_state_kernel(BwdArgs a) {
+  constexpr int NW = VD / 16, NKT = KD / 16, NKB = KD / 32;
+  constexpr int NFW = 4 * NKB, NFK = 2 * NKT;
+  constexpr int IW = (NFW + NW - 1) / NW, IK = (NFK + NW - 1) / NW;   // fragments per wave
+  __shared__ __attribute__((aligned(16))) unsigned char sF[(NFW + NFK) * FRB];
+  __shared__ __attribute__((aligned(16))) float sD[KD];   // 2^(G_C) per channel
   constexpr BwdRec R = bwd_rec(KD, VD);
   const int h = blockIdx.x % a.Hv, n = blockIdx.x / a.Hv, tid = threadIdx.x;
-  const TV tv(tid);
-  const TH th(tid);
+  // (the wave index is uniform: per-wave branches stay scalar)
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), r16 = lane & 15, g = lane >> 4;
+  const int col = 16 * wave + r16;
+  unsigned char* fW = sF;
+  unsigned char* fK = sF + NFW * FRB;
   int64_t tok0s;
   int len;
   seq_range(a.seq, n, tok0s, len);
   const int nck = (len + BT - 1) / BT;
   const int cb = chunk_base(a.seq, n);
-  for (int i = tid; i < KD * VD; i += SNTH)
-    sH[(i / VD) * LH + i % VD] = a.h0 ? a.h0[((int64_t)n * a.Hv + h) * (KD * VD) + i] : 0.f;
-  __syncthreads();
+  f32x4 H[NKT];
+  {
+    const float* h0 = a.h0 ? a.h0 + ((int64_t)n * a.Hv + h) * (KD * VD) : nullptr;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) H[t][e] = h0 ? h0[(16 * t + 4 * g + e) * VD + col] : 0.f;
+  }
   for (int c = 0; c < nck; ++c) {
     const int64_t slot = (int64_t)h * a.nchunks + cb + c;
     const float* rec = a.rec + slot * (int64_t)(R.bytes / 4);
-    const int C = min(BT, len - c * BT);
-    float* dst = a.h_store_w + slot * (int64_t)(KD * VD);
-    // this wave's h tiles: kept for the update, stored as the chunk-entry state
-    f32x4 hold[TH::TPW];
+    const float* Gc = rec + R.G + (min(BT, len - c * BT) - 1) * KD;
+    {  // the chunk-entry state out
+      float* dst = a.h_store_w + slot * (int64_t)(KD * VD);
 #pragma unroll
-    for (int t = 0; t < TH::TPW; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kk = 16 * th.rb + 4 * th.q + e, j = 16 * (th.cb0 + t) + th.r16;
-        hold[t][e] = sH[kk * LH + j];
-        dst[kk * VD + j] = hold[t][e];
-      }
-    if (tid < KD) sGC[tid] = rec[R.G + (C - 1) * KD + tid];
-    {  // v_new = u - w h  -> sVN
-      f32x4 acc[TV::TPW];
-#pragma unroll
-      for (int t = 0; t < TV::TPW; ++t) acc[t] = zero4();
-      const float* wrow = rec + R.w + (16 * tv.rb + tv.r16) * KD + 4 * tv.q;
-      for (int kk = 0; kk < KD; kk += 16) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(wrow + kk);
-#pragma unroll
-        for (int t = 0; t < TV::TPW; ++t)
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            acc[t] = mfma4(av[p], sH[(kk + 4 * tv.q + p) * LH + 16 * (tv.cb0 + t) + tv.r16], acc[t]);
-      }
-#pragma unroll
-      for (int t = 0; t < TV::TPW; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * tv.rb + 4 * tv.q + e, j = 16 * (tv.cb0 + t) + tv.r16;
-          sVN[i * LH + j] = rec[R.u + i * VD + j] - acc[t][e];
-        }
+      for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4*>(dst + sq_index(16 * t + 4 * g, col, VD)) = H[t];
     }
-    __syncthreads();
-    {  // h = D h + kg^T v_new, kg = k e^(G_C - G) (A operand: kg^T rows of this wave's block)
-      f32x4 acc[TH::TPW];
+    // then the loads: u (v_new starts at u), -w, and k, G, G_C for kg^T
+    f32x4 vn[4];
 #pragma unroll
-      for (int t = 0; t < TH::TPW; ++t) acc[t] = zero4();
-      const int kk = 16 * th.rb + th.r16;
-      const float gck = sGC[kk];
-      for (int r0 = 0; r0 < BT; r0 += 16) {
-        float av[4];
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int r = r0 + 4 * th.q + p;
-          av[p] = rec[R.kn + r * KD + kk] * ex2(gck - rec[R.G + r * KD + kk]);
-        }
+      for (int e = 0; e < 4; ++e) vn[rt][e] = rec[R.u + (16 * rt + 4 * g + e) * VD + col];
+    const float gcv = tid < KD ? Gc[tid] : 0.f;
+    // (a wave past the last fragment loads the last one again and skips its write)
+    float xw[IW][8], xk[IK][8], xg[IK][8], xc[IK][8];
 #pragma unroll
-        for (int t = 0; t < TH::TPW; ++t)
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            acc[t] = mfma4(av[p], sVN[(r0 + 4 * th.q + p) * LH + 16 * (th.cb0 + t) + th.r16], acc[t]);
-      }
-#pragma unroll
-      for (int t = 0; t < TH::TPW; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k2 = 16 * th.rb + 4 * th.q + e, j = 16 * (th.cb0 + t) + th.r16;
-          sH[k2 * LH + j] = ex2(sGC[k2]) * hold[t][e] + acc[t][e];
-        }
+    for (int i = 0; i < IW; ++i) {
+      const int f = min(wave + NW * i, NFW - 1);
+      ld8s(rec + R.w + (16 * (f / NKB) + r16) * KD + 32 * (f % NKB) + 4 * g, xw[i]);
     }
+#pragma unroll
+    for (int i = 0; i < IK; ++i) {
+      const int f = min(wave + NW * i, NFK - 1);
+      const int t = 32 * (f % 2) + (lane >> 1), k0 = 16 * (f / 2) + 8 * (lane & 1);
+      ld8(rec + R.kn + t * KD + k0, xk[i]);
+      ld8(rec + R.G + t * KD + k0, xg[i]);
+      ld8(Gc + k0, xc[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
+#pragma unroll
+    for (int i = 0; i < IW; ++i) {
+      const int f = wave + NW * i;
+      if (f < NFW) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xw[i][j] = -xw[i][j];
+        frag_put(fW + f * FRB, lane, split8(xw[i]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < IK; ++i) {
+      const int f = wave + NW * i;
+      if (f < NFK) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xk[i][j] *= ex2(xc[i][j] - xg[i][j]);
+        stage_t(fK + f * FRB, lane, xk[i]);
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < IK; ++i) {
+      const int f = wave + NW * i;
+      if (f < NFK) gather_t(fK + f * FRB, lane, xk[i]);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < IK; ++i) {
+      const int f = wave + NW * i;
+      if (f < NFK) frag_put(fK + f * FRB, lane, split8(xk[i]));
+    }
+    if (tid < KD) sD[tid] = ex2(gcv);
     __syncthreads();
+    // v_new = u - w h: the state is the B operand as it sits in the accumulators
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const Frag b = split_pair(H[2 * kb], H[2 * kb + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) vn[rt] = mma3(frag_get(fW + (rt * NKB + kb) * FRB, lane), b, vn[rt]);
+    }
+    // h = D h + kg^T v_new
+    const Frag vb0 = split_pair(vn[0], vn[1]), vb1 = split_pair(vn[2], vn[3]);
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) {
+      const f32x4 d = *reinterpret_cast<const f32x4*>(sD + 16 * t + 4 * g);
+      f32x4 acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = d[e] * H[t][e];
+      acc = mma3(frag_get(fK + (2 * t) * FRB, lane), vb0, acc);
+      H[t] = mma3(frag_get(fK + (2 * t + 1) * FRB, lane), vb1, acc);
+    }
+    __syncthreads();   // every wave done with this chunk's fragments
   }
 }
 
 // ------------------------------------------------------ reverse state scan
 // dh over the chunks in reverse: dv_new = Aqk^T do + kg dh',
-// dh = qg^T do + D dh' - w^T dv_new, every chunk's exit gradient stored.  One
-// workgroup per (sequence, head), dh in LDS, fp32 matrix cores as above.
+// dh = qg^T do + D dh' - w^T dv_new, every chunk's exit gradient stored.
+// Operands per chunk: kg as A[token][K], Aqk^T as A[token i][token r], qg^T
+// and -w^T as A[K][token], do as B[token][column] (bf16 tokens are exact in
+// one bf16 part; fp32 tokens are split like the rest).
 template <int KD, int VD, typename IT>
-__global__ __launch_bounds__(SNTH) void bwd_scan_kernel(BwdArgs a) {
-  constexpr int LH = VD + 4;
-  __shared__ __attribute__((aligned(16))) float sDH[KD * LH];
-  __shared__ __attribute__((aligned(16))) float sDV[BT * LH];
-  __shared__ __attribute__((aligned(16))) float sDo[BT * LH];
-  __shared__ float sGC[KD];
-  using TV = STiles<BT, VD, SNTH / 64>;
-  using TH = STiles<KD, VD, SNTH / 64>;
-  static_assert(TH::TPW <= TH::NCB && TV::TPW <= TV::NCB, "one row block per wave");
+__global__ __launch_bounds__(VD * 4) void bwd_scan_kernel(BwdArgs a) {
+  constexpr bool F32 = sizeof(IT) == 4;
+  constexpr int NW = VD / 16, NKT = KD / 16, NKB = KD / 32;
+  constexpr int NFG = 4 * NKB, NFA = 8, NFQ = 2 * NKT, NFD = 2 * NW;
+  constexpr int DOB = F32 ? FRB : FRB / 2;   // bytes of a do fragment
+  constexpr int IG = (NFG + NW - 1) / NW, IA = (NFA + NW - 1) / NW, IQ = (NFQ + NW - 1) / NW;
+  __shared__ __attribute__((aligned(16))) unsigned char sF[(NFG + NFA + 2 * NFQ) * FRB + NFD * DOB];
+  __shared__ __attribute__((aligned(16))) float sD[KD];
   constexpr BwdRec R = bwd_rec(KD, VD);
   const int h = blockIdx.x % a.Hv, n = blockIdx.x / a.Hv, tid = threadIdx.x;
-  const TV tv(tid);
-  const TH th(tid);
+  // (the wave index is uniform: per-wave branches stay scalar)
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), r16 = lane & 15, g = lane >> 4;
+  const int col = 16 * wave + r16;
+  unsigned char* fG = sF;
+  unsigned char* fA = fG + NFG * FRB;
+  unsigned char* fQ = fA + NFA * FRB;
+  unsigned char* fWT = fQ + NFQ * FRB;
+  unsigned char* fD = fWT + NFQ * FRB;
   int64_t tok0s;
   int len;
   seq_range(a.seq, n, tok0s, len);
   const int nck = (len + BT - 1) / BT;
   const int cb = chunk_base(a.seq, n);
   const IT* dout = static_cast<const IT*>(a.dout);
-  for (int i = tid; i < KD * VD; i += SNTH)   // dh' of the last chunk: the final state's gradient
-    sDH[(i / VD) * LH + i % VD] = a.dht ? a.dht[((int64_t)n * a.Hv + h) * (KD * VD) + i] : 0.f;
-  __syncthreads();
+  f32x4 DH[NKT];   // dh' of the last chunk: the final state's gradient
+  {
+    const float* dht = a.dht ? a.dht + ((int64_t)n * a.Hv + h) * (KD * VD) : nullptr;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) DH[t][e] = dht ? dht[(16 * t + 4 * g + e) * VD + col] : 0.f;
+  }
   for (int c = nck - 1; c >= 0; --c) {
     const int64_t slot = (int64_t)h * a.nchunks + cb + c;
     const float* rec = a.rec + slot * (int64_t)(R.bytes / 4);
     const int C = min(BT, len - c * BT);
     const int64_t tok0 = tok0s + (int64_t)c * BT;
-    f32x4 dold[TH::TPW];
+    const float* Gc = rec + R.G + (C - 1) * KD;
+    // the exit gradient of this chunk out
+    if (a.dh_store) {
+      float* dst = a.dh_store + slot * (int64_t)(KD * VD);
 #pragma unroll
-    for (int t = 0; t < TH::TPW; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kk = 16 * th.rb + 4 * th.q + e, j = 16 * (th.cb0 + t) + th.r16;
-        dold[t][e] = sDH[kk * LH + j];
-        if (a.dh_store) a.dh_store[slot * (int64_t)(KD * VD) + kk * VD + j] = dold[t][e];
-      }
-    if (tid < KD) sGC[tid] = rec[R.G + (C - 1) * KD + tid];
-    for (int i = tid; i < BT * VD; i += SNTH) {
-      const int r = i / VD, cc = i % VD;
-      sDo[r * LH + cc] = r < C ? ldf(dout + ((tok0 + r) * a.Hv + h) * VD + cc) : 0.f;
+      for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4*>(dst + sq_index(16 * t + 4 * g, col, VD)) = DH[t];
     }
-    __syncthreads();
-    {  // dv_new = Aqk^T do + kg dh'  -> sDV
-      f32x4 acc[TV::TPW];
+    // then the loads (a wave past the last fragment of a kind loads the last
+    // one again and skips its write)
+    const float gcv = tid < KD ? Gc[tid] : 0.f;
+    float xg[IG][8], xgg[IG][8], xgc[IG][8], xa[IA][8], xq[IQ][8], xqg[IQ][8], xw[IQ][8];
 #pragma unroll
-      for (int t = 0; t < TV::TPW; ++t) acc[t] = zero4();
-      const int i = 16 * tv.rb + tv.r16;
-      for (int r0 = 0; r0 < BT; r0 += 16) {
-        float av[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) av[p] = rec[R.aqk + (r0 + 4 * tv.q + p) * BT + i];
-#pragma unroll
-        for (int t = 0; t < TV::TPW; ++t)
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            acc[t] = mfma4(av[p], sDo[(r0 + 4 * tv.q + p) * LH + 16 * (tv.cb0 + t) + tv.r16], acc[t]);
-      }
-      const float* knr = rec + R.kn + i * KD + 4 * tv.q;
-      const float* gr = rec + R.G + i * KD + 4 * tv.q;
-      for (int kk = 0; kk < KD; kk += 16) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(knr + kk);
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(gr + kk);
-        float av[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) av[p] = kv[p] * ex2(sGC[kk + 4 * tv.q + p] - gv[p]);
-#pragma unroll
-        for (int t = 0; t < TV::TPW; ++t)
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            acc[t] = mfma4(av[p], sDH[(kk + 4 * tv.q + p) * LH + 16 * (tv.cb0 + t) + tv.r16], acc[t]);
-      }
-#pragma unroll
-      for (int t = 0; t < TV::TPW; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sDV[(16 * tv.rb + 4 * tv.q + e) * LH + 16 * (tv.cb0 + t) + tv.r16] = acc[t][e];
+    for (int i = 0; i < IG; ++i) {
+      const int f = min(wave + NW * i, NFG - 1);
+      const int o = (16 * (f / NKB) + r16) * KD + 32 * (f % NKB) + 4 * g;
+      ld8s(rec + R.kn + o, xg[i]);
+      ld8s(rec + R.G + o, xgg[i]);
+      ld8s(Gc + 32 * (f % NKB) + 4 * g, xgc[i]);
     }
-    __syncthreads();
-    {  // dh = qg^T do + D dh' - w^T dv_new (A operands: qg^T and w^T rows of this wave's block)
-      f32x4 acc[TH::TPW];
 #pragma unroll
-      for (int t = 0; t < TH::TPW; ++t) acc[t] = zero4();
-      const int kk = 16 * th.rb + th.r16;
-      for (int r0 = 0; r0 < BT; r0 += 16) {
-        float aq[4], aw[4];
+    for (int i = 0; i < IA; ++i) {
+      const int f = min(wave + NW * i, NFA - 1);   // f = 2 * (block of 16 i) + (block of 32 r)
+      ld8(rec + R.aqk + (32 * (f % 2) + (lane >> 1)) * BT + 16 * (f / 2) + 8 * (lane & 1), xa[i]);
+    }
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int r = r0 + 4 * th.q + p;
-          aq[p] = a.scale * rec[R.qn + r * KD + kk] * ex2(rec[R.G + r * KD + kk]);
-          aw[p] = -rec[R.w + r * KD + kk];
+    for (int i = 0; i < IQ; ++i) {
+      const int f = min(wave + NW * i, NFQ - 1);   // f = 2 * (block of 16 K) + (block of 32 tokens)
+      const int o = (32 * (f % 2) + (lane >> 1)) * KD + 16 * (f / 2) + 8 * (lane & 1);
+      ld8(rec + R.qn + o, xq[i]);
+      ld8(rec + R.G + o, xqg[i]);
+      ld8(rec + R.w + o, xw[i]);
+    }
+    // do: this wave's two fragments (column block = wave), rows past the chunk zero
+    float xd[2][8];
+    u32x4 xd16[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int t = 32 * tb + (lane >> 1);
+      const IT* p = dout + ((tok0 + t) * a.Hv + h) * VD + 16 * wave + 8 * (lane & 1);
+      if constexpr (F32) {
+        if (t < C) ld8(reinterpret_cast<const float*>(p), xd[tb]);
+        else
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xd[tb][j] = 0.f;
+      } else {
+        xd16[tb] = t < C ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
+    // kg fragments (reduction along the row: no transposition)
+#pragma unroll
+    for (int i = 0; i < IG; ++i) {
+      const int f = wave + NW * i;
+      if (f < NFG) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xg[i][j] *= ex2(xgc[i][j] - xgg[i][j]);
+        frag_put(fG + f * FRB, lane, split8(xg[i]));
+      }
+    }
+    // transposed fragments: stage, gather, split
+#pragma unroll
+    for (int i = 0; i < IA; ++i)
+      if (wave + NW * i < NFA) stage_t(fA + (wave + NW * i) * FRB, lane, xa[i]);
+#pragma unroll
+    for (int i = 0; i < IQ; ++i) {
+      const int f = wave + NW * i;
+      if (f < NFQ) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xq[i][j] *= a.scale * ex2(xqg[i][j]);
+          xw[i][j] = -xw[i][j];
         }
-#pragma unroll
-        for (int t = 0; t < TH::TPW; ++t)
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int r = r0 + 4 * th.q + p, j = 16 * (th.cb0 + t) + th.r16;
-            acc[t] = mfma4(aq[p], sDo[r * LH + j], acc[t]);
-            acc[t] = mfma4(aw[p], sDV[r * LH + j], acc[t]);
-          }
+        stage_t(fQ + f * FRB, lane, xq[i]);
+        stage_t(fWT + f * FRB, lane, xw[i]);
       }
-      // (every wave finished reading dh' before the barrier above)
-#pragma unroll
-      for (int t = 0; t < TH::TPW; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k2 = 16 * th.rb + 4 * th.q + e, j = 16 * (th.cb0 + t) + th.r16;
-          sDH[k2 * LH + j] = ex2(sGC[k2]) * dold[t][e] + acc[t][e];
-        }
     }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      if constexpr (F32) stage_t(fD + (2 * wave + tb) * DOB, lane, xd[tb]);
+      else stage_t16(fD + (2 * wave + tb) * DOB, lane, xd16[tb]);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < IA; ++i)
+      if (wave + NW * i < NFA) gather_t(fA + (wave + NW * i) * FRB, lane, xa[i]);
+#pragma unroll
+    for (int i = 0; i < IQ; ++i)
+      if (wave + NW * i < NFQ) {
+        gather_t(fQ + (wave + NW * i) * FRB, lane, xq[i]);
+        gather_t(fWT + (wave + NW * i) * FRB, lane, xw[i]);
+      }
+    bf16x8 dh16[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      if constexpr (F32) gather_t(fD + (2 * wave + tb) * DOB, lane, xd[tb]);
+      else dh16[tb] = gather_t16(fD + (2 * wave + tb) * DOB, lane);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < IA; ++i)
+      if (wave + NW * i < NFA) frag_put(fA + (wave + NW * i) * FRB, lane, split8(xa[i]));
+#pragma unroll
+    for (int i = 0; i < IQ; ++i)
+      if (wave + NW * i < NFQ) {
+        frag_put(fQ + (wave + NW * i) * FRB, lane, split8(xq[i]));
+        frag_put(fWT + (wave + NW * i) * FRB, lane, split8(xw[i]));
+      }
+    // do stays in this wave's registers: its fragments are its own column block
+    Frag dof[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      if constexpr (F32) dof[tb] = split8(xd[tb]);
+      else dof[tb].hi = dh16[tb];
+    }
+    if (tid < KD) sD[tid] = ex2(gcv);
     __syncthreads();
+    // dv_new = Aqk^T do + kg dh' (this wave's columns)
+    f32x4 dv[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) dv[rt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const Frag A = frag_get(fA + (2 * rt + kb) * FRB, lane);
+        if constexpr (F32) dv[rt] = mma3(A, dof[kb], dv[rt]);
+        else dv[rt] = mfma(A.lo, dof[kb].hi, mfma(A.hi, dof[kb].hi, dv[rt]));
+      }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const Frag b = split_pair(DH[2 * kb], DH[2 * kb + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) dv[rt] = mma3(frag_get(fG + (rt * NKB + kb) * FRB, lane), b, dv[rt]);
+    }
+    // dh = D dh' + qg^T do - w^T dv_new
+    const Frag vb0 = split_pair(dv[0], dv[1]), vb1 = split_pair(dv[2], dv[3]);
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) {
+      const f32x4 d = *reinterpret_cast<const f32x4*>(sD + 16 * t + 4 * g);
+      f32x4 acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = d[e] * DH[t][e];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const Frag Q = frag_get(fQ + (2 * t + tb) * FRB, lane);
+        if constexpr (F32) acc = mma3(Q, dof[tb], acc);
+        else acc = mfma(Q.lo, dof[tb].hi, mfma(Q.hi, dof[tb].hi, acc));
+        acc = mma3(frag_get(fWT + (2 * t + tb) * FRB, lane), tb ? vb1 : vb0, acc);
+      }
+      DH[t] = acc;
+    }
+    __syncthreads();   // every wave done with this chunk's fragments
   }
-  if (a.dh0)
-    for (int i = tid; i < KD * VD; i += SNTH)
-      a.dh0[((int64_t)n * a.Hv + h) * (KD * VD) + i] = sDH[(i / VD) * LH + i % VD];
+  if (a.dh0) {
+    float* d0 = a.dh0 + ((int64_t)n * a.Hv + h) * (KD * VD);
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d0[(16 * t + 4 * g + e) * VD + col] = DH[t][e];
+  }
 }
 
 // ------------------------------------------------------------------ prep
@@ -810,10 +1009,14 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll 2
     for (int kk = 0; kk < KD; kk += 16) {
       float bh[4], bd[4];
+      {
+        const f32x4 h4 = *reinterpret_cast<const f32x4*>(hc + sq_index(kk + 4 * ov.q, vc, VD));
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dh + sq_index(kk + 4 * ov.q, vc, VD));
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        bh[p] = hc[(kk + 4 * ov.q + p) * VD + vc];
-        bd[p] = dh[(kk + 4 * ov.q + p) * VD + vc];
+        for (int p = 0; p < 4; ++p) {
+          bh[p] = h4[p];
+          bd[p] = d4[p];
+        }
       }
 #pragma unroll
       for (int t = 0; t < OV::TPW; ++t) {
@@ -877,13 +1080,17 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     zero(ak);
     zero(aq);
     zero(aw);
-    const float* hr = hc + kc * VD + 4 * ok.q;
-    const float* dhr = dh + kc * VD + 4 * ok.q;
+    const float* hr = hc + sq_index(kc, 4 * ok.q, VD);
+    const float* dhr = dh + sq_index(kc, 4 * ok.q, VD);
     float dd = 0.f;   // this lane's quarter of the columns
 #pragma unroll 2
     for (int s2 = 0; s2 < VD / 16; ++s2) {
-      const f32x4 hv = *reinterpret_cast<const f32x4*>(hr + 16 * s2);
-      const f32x4 dv = *reinterpret_cast<const f32x4*>(dhr + 16 * s2);
+      f32x4 hv, dv;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        hv[p] = hr[4 * (16 * s2 + p)];
+        dv[p] = dhr[4 * (16 * s2 + p)];
+      }
 #pragma unroll
       for (int p = 0; p < 4; ++p) dd += hv[p] * dv[p];
 #pragma unroll
@@ -1506,13 +1713,13 @@ hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int6
   if (K == KK && V == VV) {                                                                             \
     switch (stage) {                                                                                    \
       case 0: return nb_chunk ? launch(bwd_prep_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
-      case 1: return nb_scan ? launch(bwd_scan_kernel<KK, VV, TT>, dim3(nb_scan), dim3(SNTH), s, a) : hipSuccess;  \
+      case 1: return nb_scan ? launch(bwd_scan_kernel<KK, VV, TT>, dim3(nb_scan), dim3(VV * 4), s, a) : hipSuccess;  \
       case 2: return nb_chunk ? launch(bwd_chunk_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
       case 3: return nb_qk ? launch(bwd_qk_kernel<KK, TT>, dim3(nb_qk), dim3(64), s, a, tokens) : hipSuccess;       \
       case 4: return nblk ? launch(bwd_gate_kernel<KK, TT>, dim3(nblk * a.Hv), dim3(KK), s, a, tokens, part)        \
                           : hipSuccess;                                                                 \
       case 5: return launch(bwd_gate_sum_kernel<KK>, dim3(a.Hv), dim3(KK), s, a, nblk, (const float*)part);       \
-      case 6: return nb_scan ? launch(bwd_state_kernel<KK, VV>, dim3(nb_scan), dim3(SNTH), s, a) : hipSuccess;      \
+      case 6: return nb_scan ? launch(bwd_state_kernel<KK, VV>, dim3(nb_scan), dim3(VV * 4), s, a) : hipSuccess;      \
       case 7: return nb_chunk ? launch(bwd_pairs_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
     }                                                                                                   \
     return hipErrorInvalidValue;                                                                        \
