@@ -44,6 +44,8 @@
 //                     dt_bias sums (two passes, fixed order: deterministic)
 #include "kda_launch.h"
 
+#include <type_traits>
+
 namespace kda {
 
 namespace {
@@ -669,13 +671,50 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
   if (tid < BT) rec[R.beta + tid] = sB[tid];
 
   // ---- L (beta-scaled, strict lower) and Aqk (scaled, lower): 6 tiles below
-  // the diagonal blocks and 4 x 4 (diagonal tile, level) jobs, spread over the waves
+  // the diagonal blocks and the 4 diagonal tiles, one job each.  A diagonal
+  // tile takes one reference row (its row 8) for every pair when none of the
+  // factors that makes exceeds 2^96 in any channel; otherwise its job runs
+  // the four split levels one after the other.
   float* aqk = rec + R.aqk;
-  for (int job = wave; job < 22; job += NTH / 64) {
+  for (int job = wave; job < 10; job += NTH / 64) {
     f32x4 accL = zero4(), accQ = zero4();
-    if (job < 6) {
+    bool one_ref = false;
+    if (job >= 6) {
+      const int r0 = 16 * (job - 6);
+      bool ok1 = true;
+      for (int cc = lane; cc < KD; cc += 64) {
+        const float gm = sG[(r0 + 8) * LX + cc];
+        ok1 = ok1 && fmaxf(sG[r0 * LX + cc] - gm, gm - sG[(r0 + 15) * LX + cc]) < 96.f;
+      }
+      one_ref = __all(ok1);
+    }
+    if (job >= 6 && one_ref) {
+      const int I = job - 6, ry = 16 * I + r16, rr = 16 * I + 8;
+#pragma unroll 2
+      for (int kk = 0; kk < KD; kk += 16) {
+        const int c0 = kk + 4 * quad;
+        const f32x4 gy = *reinterpret_cast<const f32x4*>(&sG[ry * LX + c0]);
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(&sG[rr * LX + c0]);
+        const f32x4 ky = *reinterpret_cast<const f32x4*>(&sK[ry * LX + c0]);
+        const f32x4 qy = *reinterpret_cast<const f32x4*>(&sX[ry * LX + c0]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float fa = ex2(gy[p] - gr[p]), fb = ky[p] * ex2(gr[p] - gy[p]);
+          accL = mfma4(ky[p] * fa, fb, accL);
+          accQ = mfma4(qy[p] * fa, fb, accQ);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int il = 4 * quad + e, jl = r16;
+        const int i = 16 * I + il, j = 16 * I + jl;
+        sL[i * LS + j] = il > jl ? sB[i] * accL[e] : 0.f;
+        aqk[i * BT + j] = il > jl ? a.scale * accQ[e] : il == jl ? sDiag[i] : 0.f;
+      }
+    } else if (job < 6) {
       const int I = job < 1 ? 1 : job < 3 ? 2 : 3, J = job < 1 ? 0 : job < 3 ? job - 1 : job - 3;
       const int ri = 16 * I + r16, rj = 16 * J + r16, rr = 16 * I;
+#pragma unroll 2
       for (int kk = 0; kk < KD; kk += 16) {
         const int c0 = kk + 4 * quad;
         const f32x4 gi = *reinterpret_cast<const f32x4*>(&sG[ri * LX + c0]);
@@ -700,10 +739,15 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
         aqk[j * BT + i] = 0.f;
       }
     } else {
-      const int I = (job - 6) >> 2, lv = (job - 6) & 3;
+      const int I = job - 6;
+#pragma unroll 1
+      for (int lv = 0; lv < 4; ++lv) {
+      accL = zero4();
+      accQ = zero4();
       const int y = r16, ry = 16 * I + y;
       const bool up = (y >> lv) & 1;
       const int rref = 16 * I + ((y >> (lv + 1)) << (lv + 1)) + (1 << lv);
+#pragma unroll 2
       for (int kk = 0; kk < KD; kk += 16) {
         const int c0 = kk + 4 * quad;
         const f32x4 gy = *reinterpret_cast<const f32x4*>(&sG[ry * LX + c0]);
@@ -730,6 +774,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
           sL[i * LS + j] = 0.f;
           aqk[i * BT + j] = il == jl ? sDiag[i] : 0.f;
         }
+      }
       }
     }
   }
@@ -1367,6 +1412,12 @@ __global__ __launch_bounds__(NTH) void bwd_pairs_kernel(BwdArgs a) {
   // operands.  Off-diagonal blocks use the first row of the later block as r;
   // the diagonal blocks split further (below).
   const int c = ok.col();
+  // The diagonal blocks take one reference row (i0 + 8) for every pair when
+  // none of the factors it makes exceeds 2^96 in any channel of the wave's
+  // tiles (a wave-uniform choice): one product per side instead of four split
+  // levels.  Each choice is its own copy of the loop (separate registers).
+  auto pair_tiles = [&](auto one_ref) __attribute__((always_inline)) {
+    constexpr bool ONE_REF = decltype(one_ref)::value;
 #pragma unroll
   for (int t = 0; t < OK::TPW; ++t) {
     const int I = ok.ti(t), i0 = 16 * I, iq = i0 + 4 * ok.q;   // rows iq .. iq + 3 of block I
@@ -1435,8 +1486,31 @@ __global__ __launch_bounds__(NTH) void bwd_pairs_kernel(BwdArgs a) {
     // reference; every pair i > j of the block meets exactly one level, and
     // both factors are <= 1, whatever the decay.  Rows on the other side get
     // a zero operand before any product (their factor may overflow).
-    {
-      const int xr = 4 * ok.q;   // this lane's reduction rows x = i0 + xr + p
+    const int xr = 4 * ok.q;   // this lane's reduction rows x = i0 + xr + p
+    if constexpr (ONE_REF) {
+      const float gm = sB1[(i0 + 8) * LX + c];
+      f32x4 pL = zero4(), pA = zero4(), qL = zero4(), qA = zero4();
+      const int y = ok.r16;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int x = xr + p, xg = i0 + x;
+        const float gx = sB1[xg * LX + c], kx = sB2[xg * LX + c];
+        const float bR = kx * ex2(gm - gx);         // row side: j = x
+        pL = mfma4(x < y ? sS3[(i0 + y) * LS + xg] : 0.f, bR, pL);   // i = y > j = x
+        pA = mfma4(x < y ? sS1[(i0 + y) * LS + xg] : 0.f, bR, pA);
+        const float eu = ex2(gx - gm);              // column side: i = x > j = y
+        qL = mfma4(x > y ? sS3[xg * LS + i0 + y] : 0.f, sBeta[xg] * kx * eu, qL);
+        qA = mfma4(x > y ? sS1[xg * LS + i0 + y] : 0.f, sB3[xg * LX + c] * eu, qA);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fr = ex2(gq[e] - gm), fc = ex2(gm - gq[e]);
+        rL[e] += fr * pL[e];
+        rA[e] += fr * pA[e];
+        cL[e] += fc * qL[e];
+        cA[e] += fc * qA[e];
+      }
+    } else {
 #pragma unroll 1
       for (int lv = 3; lv >= 0; --lv) {
         const int hb = 1 << lv;
@@ -1482,14 +1556,14 @@ __global__ __launch_bounds__(NTH) void bwd_pairs_kernel(BwdArgs a) {
           cA[e] += fc * qA[e];
         }
       }
-      // the diagonal of dAqk (factor 1): row side j = i, column side i = j
+    }
+    // the diagonal of dAqk (factor 1): row side j = i, column side i = j
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = iq + e;
-        const float d = sS1[i * LS + i];
-        rA[e] += d * sB2[i * LX + c];
-        cA[e] += d * sB3[i * LX + c];
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int i = iq + e;
+      const float d = sS1[i * LS + i];
+      rA[e] += d * sB2[i * LX + c];
+      cA[e] += d * sB3[i * LX + c];
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1502,6 +1576,16 @@ __global__ __launch_bounds__(NTH) void bwd_pairs_kernel(BwdArgs a) {
       dbK[t][e] += ki * rL[e];
     }
   }
+  };
+  bool one_ref = true;
+#pragma unroll
+  for (int t = 0; t < OK::TPW; ++t) {
+    const int i0 = 16 * ok.ti(t);
+    const float gm = sB1[(i0 + 8) * LX + c];
+    one_ref = one_ref && fmaxf(sB1[i0 * LX + c] - gm, gm - sB1[(i0 + 15) * LX + c]) < 96.f;
+  }
+  if (__all(one_ref)) pair_tiles(std::true_type{});
+  else pair_tiles(std::false_type{});
   __syncthreads();   // (the pair sums read sB3 and sS3, reused below)
   // dbeta: this kernel's share, added to the chunk kernel's partial sums
   float* sRedB = sS1;   // [OK::NT][BT]
