@@ -428,10 +428,11 @@ kda_status_t kda_chunk_bwd(const kda_problem_t* p, const void* q, const void* k,
   if (pl.tokens > 0) {
     if ((st = check_token_ptr(q, "q", 16)) != KDA_OK) return st;
     if ((st = check_token_ptr(dout, "do", 16)) != KDA_OK) return st;
-    const struct { const void* ptr; const char* name; } outs[] = {
-        {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {dg, "dg"}, {dbeta, "dbeta"}};
+    // dq, dk and dg are written 16 bytes at a time
+    const struct { const void* ptr; const char* name; size_t align; } outs[] = {
+        {dq, "dq", 16}, {dk, "dk", 16}, {dv, "dv", 4}, {dg, "dg", 16}, {dbeta, "dbeta", 4}};
     for (const auto& o : outs)
-      if ((st = check_token_ptr(o.ptr, o.name, 4)) != KDA_OK) return st;
+      if ((st = check_token_ptr(o.ptr, o.name, o.align)) != KDA_OK) return st;
   }
   for (const float* s : {initial_state, dht, (const float*)dh0, (const float*)dA_log, (const float*)ddt_bias})
     if (s && !aligned(s, 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "fp32 arguments must be 4-byte aligned");

@@ -1654,119 +1654,148 @@ __global__ __launch_bounds__(NTH) void bwd_pairs_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------- grouped heads and L2Norm
+// One wave per (token, q/k head): lanes 0..31 take q, lanes 32..63 take k,
+// KD / 32 consecutive channels per lane (16- or 8-byte accesses); the sum over
+// the group's value heads, then the L2Norm backward.
+constexpr int QK_THREADS = 256;
+
 template <int KD, typename IT>
-__global__ __launch_bounds__(64) void bwd_qk_kernel(BwdArgs a, int64_t tokens) {
-  const int64_t tok = blockIdx.x / a.Hk;
-  const int hk = blockIdx.x % a.Hk, lane = threadIdx.x;
-  const int rep = a.Hv / a.Hk;
+__global__ __launch_bounds__(QK_THREADS) void bwd_qk_kernel(BwdArgs a, int64_t tokens) {
+  constexpr int CPL = KD / 32;
+  const int lane = threadIdx.x & 63, half = lane >> 5, c0 = CPL * (lane & 31);
+  const int64_t item = (int64_t)blockIdx.x * (QK_THREADS / 64) + (threadIdx.x >> 6);
+  if (item >= tokens * a.Hk) return;   // (whole waves: no barrier follows)
+  const int64_t tok = item / a.Hk;
+  const int hk = (int)(item % a.Hk), rep = a.Hv / a.Hk;
   const bool l2 = a.flags & F_L2;
-  const IT* q = static_cast<const IT*>(a.q);
-  const IT* k = static_cast<const IT*>(a.k);
-  for (int which = 0; which < 2; ++which) {
-    const IT* x = which ? k : q;
-    const float* d = which ? a.dkn : a.dqn;
-    float* out = which ? a.dk : a.dq;
-    float xs[2] = {0.f, 0.f}, ds[2] = {0.f, 0.f};
-    float sxx = 0.f, sxd = 0.f;
+  const IT* x = static_cast<const IT*>(half ? a.k : a.q) + (tok * a.Hk + hk) * KD + c0;
+  const float* d = (half ? a.dkn : a.dqn) + (tok * a.Hv + (int64_t)hk * rep) * KD + c0;
+  float* out = (half ? a.dk : a.dq) + (tok * a.Hk + hk) * KD + c0;
+  float xs[CPL], ds[CPL];
+  if constexpr (CPL == 4) {
+    const f32x4 xv = ld4(x);
+    f32x4 dv = ld4(d);
+    for (int r = 1; r < rep; ++r) dv += ld4(d + (int64_t)r * KD);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = lane + 64 * j;
-      if (c < KD) {
-        xs[j] = ldf(x + (tok * a.Hk + hk) * KD + c);
-        for (int r = 0; r < rep; ++r) ds[j] += d[(tok * a.Hv + hk * rep + r) * KD + c];
-      }
-      sxx += xs[j] * xs[j];
+    for (int j = 0; j < 4; ++j) {
+      xs[j] = xv[j];
+      ds[j] = dv[j];
     }
-    for (int m = 1; m < 64; m <<= 1) sxx += __shfl_xor(sxx, m);
-    const float rr = l2 ? 1.f / sqrtf(sxx + a.eps) : 1.f;
+  } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sxd += xs[j] * rr * ds[j];
-    for (int m = 1; m < 64; m <<= 1) sxd += __shfl_xor(sxd, m);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = lane + 64 * j;
-      if (c < KD) out[(tok * a.Hk + hk) * KD + c] = l2 ? rr * (ds[j] - xs[j] * rr * sxd) : ds[j];
+    for (int j = 0; j < CPL; ++j) {
+      xs[j] = ldf(x + j);
+      ds[j] = d[j];
     }
+    for (int r = 1; r < rep; ++r)
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) ds[j] += d[(int64_t)r * KD + j];
   }
-  (void)tokens;
+  float sxx = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) sxx += xs[j] * xs[j];
+  for (int m = 1; m < 32; m <<= 1) sxx += __shfl_xor(sxx, m);
+  const float rr = l2 ? 1.f / sqrtf(sxx + a.eps) : 1.f;
+  float sxd = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) sxd += xs[j] * rr * ds[j];
+  for (int m = 1; m < 32; m <<= 1) sxd += __shfl_xor(sxd, m);
+  float o[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) o[j] = l2 ? rr * (ds[j] - xs[j] * rr * sxd) : ds[j];
+  if constexpr (CPL == 4) *reinterpret_cast<f32x4*>(out) = f32x4{o[0], o[1], o[2], o[3]};
+  else
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) out[j] = o[j];
 }
 
 // -------------------------------------------------- gate and sigmoid
-// One workgroup per (value head, block of tokens), one thread per channel:
-// the gate input's gradient, and this block's partial sums of dA_log and
-// dt_bias (summed in block order by bwd_gate_sum_kernel).
+// One workgroup per (value head, block of tokens): four channels per thread
+// (16-byte accesses), KD / 4 threads per token row and 128 / (KD / 4) rows in
+// flight; the gate input's gradient, and this block's partial sums of dA_log
+// and dt_bias (summed in block order by bwd_gate_sum_kernel).
 constexpr int GATE_TOKENS = BWD_GATE_TOKENS;
+constexpr int GATE_THREADS = 128;
 
 template <int KD, typename IT>
-__global__ __launch_bounds__(KD) void bwd_gate_kernel(BwdArgs a, int64_t tokens, float* part) {
-  const int h = blockIdx.x % a.Hv, blk = blockIdx.x / a.Hv, c = threadIdx.x;
+__global__ __launch_bounds__(GATE_THREADS) void bwd_gate_kernel(BwdArgs a, int64_t tokens, float* part) {
+  constexpr int LPR = KD / 4, RP = GATE_THREADS / LPR;   // threads per token row, rows in flight
+  const int h = blockIdx.x % a.Hv, blk = blockIdx.x / a.Hv, tid = threadIdx.x;
+  const int rg = tid / LPR, c0 = 4 * (tid % LPR);
   const IT* g = static_cast<const IT*>(a.g);
   const IT* bt = static_cast<const IT*>(a.beta);
   const bool gik = a.flags & F_GATE;
   const float lb = (a.flags & F_SAFE) ? a.lower_bound : -INFINITY;
   const float Aexp = gik ? expf(a.A_log[h]) : 0.f;
-  const float bias = (gik && a.dt_bias) ? a.dt_bias[h * KD + c] : 0.f;
-  float sA = 0.f, sB = 0.f;
+  const f32x4 bias = (gik && a.dt_bias) ? ld4(a.dt_bias + h * KD + c0) : zero4();
+  f32x4 sB = zero4();
+  float sA = 0.f;
   const int64_t t0 = (int64_t)blk * GATE_TOKENS, t1 = min(tokens, t0 + GATE_TOKENS);
-  // batches of GB tokens, every load of a batch issued before its stores (the
-  // output may alias the inputs as far as the compiler knows, which would
-  // otherwise order each token's loads after the previous token's store)
-  constexpr int GB = 8;
-  for (int64_t tb = t0; tb < t1; tb += GB) {
-    float dgn[GB], x[GB];
+  // batches of GB tokens per row group, every load of a batch issued before
+  // its stores (the output may alias the inputs as far as the compiler knows)
+  constexpr int GB = 4;
+  for (int64_t tb = t0 + rg; tb < t1; tb += RP * GB) {
+    f32x4 dgn[GB], x[GB];
 #pragma unroll
     for (int u = 0; u < GB; ++u) {
-      const int64_t t = tb + u;
-      const bool in = t < t1;
-      const int64_t i = (t * a.Hv + h) * KD + c;
-      dgn[u] = in ? a.dg_nat[i] : 0.f;
-      x[u] = in ? ldf(g + i) : 0.f;
+      const int64_t t = tb + RP * u;
+      const int64_t i = (t * a.Hv + h) * KD + c0;
+      dgn[u] = t < t1 ? ld4(a.dg_nat + i) : zero4();
+      x[u] = t < t1 ? ld4(g + i) : zero4();
     }
-    // beta: thread c < GB of the block takes token tb + c
-    const bool inb = c < GB && tb + c < t1;
-    const int64_t jb = (tb + c) * a.Hv + h;
-    const float db0 = inb ? a.dbeta_act[jb] : 0.f;
-    const float bl0 = (inb && (a.flags & F_SIGMOID)) ? ldf(bt + jb) : 0.f;
 #pragma unroll
     for (int u = 0; u < GB; ++u) {
-      const int64_t t = tb + u;
+      const int64_t t = tb + RP * u;
       if (t >= t1) break;
-      const int64_t i = (t * a.Hv + h) * KD + c;
-      float gact = x[u], dz = dgn[u];
-      if (gik) {
-        // softplus(z) = max(z, 0) + ln(1 + e^-|z|) and its derivative sigmoid(z)
-        // from one exponential: e = e^-|z|, sigmoid = 1 / (1 + e) for z >= 0
-        // and e / (1 + e) below
-        const float z = x[u] + bias;
-        const float e = ex2(-LOG2E_F * fabsf(z));
-        const float r = 1.f / (1.f + e);
-        gact = -Aexp * (fmaxf(z, 0.f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.f + e));
-        dz = dgn[u] * -Aexp * (z >= 0.f ? r : e * r);
+      f32x4 dz;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float gact = x[u][j], d = dgn[u][j];
+        if (gik) {
+          // softplus(z) = max(z, 0) + ln(1 + e^-|z|) and its derivative sigmoid(z)
+          // from one exponential: e = e^-|z|, sigmoid = 1 / (1 + e) for z >= 0
+          // and e / (1 + e) below
+          const float z = x[u][j] + bias[j];
+          const float e = ex2(-LOG2E_F * fabsf(z));
+          const float r = 1.f / (1.f + e);
+          gact = -Aexp * (fmaxf(z, 0.f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.f + e));
+          d = dgn[u][j] * -Aexp * (z >= 0.f ? r : e * r);
+        }
+        const bool clamped = gact < lb;
+        dz[j] = clamped ? 0.f : d;
+        sA += clamped ? 0.f : dgn[u][j] * gact;
       }
-      const bool clamped = gact < lb;
-      if (clamped) dz = 0.f;
-      a.dg[i] = dz;
       sB += dz;
-      sA += clamped ? 0.f : dgn[u] * gact;
-    }
-    if (inb) {
-      float d = db0;
-      if (a.flags & F_SIGMOID) {
-        const float sg = sigmoid_f(bl0);
-        d *= sg * (1.f - sg);
-      }
-      a.dbeta[jb] = d;
+      *reinterpret_cast<f32x4*>(a.dg + (t * a.Hv + h) * KD + c0) = dz;
     }
   }
-  // partial sums: [blk][Hv][KD + 1] (dt_bias per channel, then A_log)
-  float* pp = part + ((int64_t)blk * a.Hv + h) * (KD + 1);
-  pp[c] = sB;
-  __shared__ float red[KD];
-  red[c] = sA;
+  // beta: one token per thread
+  for (int64_t t = t0 + tid; t < t1; t += GATE_THREADS) {
+    const int64_t jb = t * a.Hv + h;
+    float d = a.dbeta_act[jb];
+    if (a.flags & F_SIGMOID) {
+      const float sg = sigmoid_f(ldf(bt + jb));
+      d *= sg * (1.f - sg);
+    }
+    a.dbeta[jb] = d;
+  }
+  // partial sums: [blk][Hv][KD + 1] (dt_bias per channel, then A_log), each
+  // summed over the row groups / threads in a fixed order
+  __shared__ __attribute__((aligned(16))) f32x4 redB[RP][LPR];
+  __shared__ float redA[GATE_THREADS];
+  redB[rg][tid % LPR] = sB;
+  redA[tid] = sA;
   __syncthreads();
-  if (c == 0) {
+  float* pp = part + ((int64_t)blk * a.Hv + h) * (KD + 1);
+  if (rg == 0) {
+    f32x4 s = redB[0][tid];
+    for (int r = 1; r < RP; ++r) s += redB[r][tid];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pp[c0 + j] = s[j];
+  }
+  if (tid == 0) {
     float s = 0.f;
-    for (int i = 0; i < KD; ++i) s += red[i];
+    for (int i = 0; i < GATE_THREADS; ++i) s += redA[i];
     pp[KD] = s;
   }
 }
@@ -1799,8 +1828,8 @@ hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int6
       case 0: return nb_chunk ? launch(bwd_prep_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
       case 1: return nb_scan ? launch(bwd_scan_kernel<KK, VV, TT>, dim3(nb_scan), dim3(VV * 4), s, a) : hipSuccess;  \
       case 2: return nb_chunk ? launch(bwd_chunk_kernel<KK, VV, TT>, dim3(nb_chunk), dim3(NTH), s, a) : hipSuccess; \
-      case 3: return nb_qk ? launch(bwd_qk_kernel<KK, TT>, dim3(nb_qk), dim3(64), s, a, tokens) : hipSuccess;       \
-      case 4: return nblk ? launch(bwd_gate_kernel<KK, TT>, dim3(nblk * a.Hv), dim3(KK), s, a, tokens, part)        \
+      case 3: return nb_qk ? launch(bwd_qk_kernel<KK, TT>, dim3((nb_qk + 3) / 4), dim3(QK_THREADS), s, a, tokens) : hipSuccess; \
+      case 4: return nblk ? launch(bwd_gate_kernel<KK, TT>, dim3(nblk * a.Hv), dim3(GATE_THREADS), s, a, tokens, part) \
                           : hipSuccess;                                                                 \
       case 5: return launch(bwd_gate_sum_kernel<KK>, dim3(a.Hv), dim3(KK), s, a, nblk, (const float*)part);       \
       case 6: return nb_scan ? launch(bwd_state_kernel<KK, VV>, dim3(nb_scan), dim3(VV * 4), s, a) : hipSuccess;      \

@@ -156,11 +156,11 @@ kda_status_t kda_chunk_bwd_workspace_size(const kda_problem_t* p, size_t* bytes)
  *  q ... cu_seqlens : as in kda_chunk_fwd; p->state_rows must be 0 (dense states).
  *  dout  : dL/do, [.., Hv, V] in p->dtype.   dht : fp32 [N,Hv,K,V] or NULL (zero).
  *  dq, dk : fp32 [.., Hk, K] (grouped heads summed over their value heads; with
- *           KDA_QK_L2NORM, with respect to the raw q and k).
+ *           KDA_QK_L2NORM, with respect to the raw q and k); 16-byte aligned.
  *  dv     : fp32 [.., Hv, V].
  *  dg     : fp32 [.., Hv, K], with respect to g as passed (the raw gate with
  *           KDA_GATE_IN_KERNEL, else the natural-log decay); zero where the
- *           safe-gate clamp is active.
+ *           safe-gate clamp is active; 16-byte aligned.
  *  dbeta  : fp32 [.., Hv], with respect to beta as passed (the logit with
  *           KDA_BETA_SIGMOID).
  *  dA_log : fp32 [Hv] or NULL; ddt_bias : fp32 [Hv,K] or NULL (KDA_GATE_IN_KERNEL;

@@ -187,6 +187,13 @@ def test_calls_fail_closed_without_launching(lib):
                lambda: lib.kda_recurrent_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake + 4,
                                              None, None, None, fake, None, None)):
         assert fn() == kda.KDA_ERR_INVALID_ARGUMENT and b"dt_bias" in lib.kda_last_error()
+    # the backward writes dq, dk and dg 16 bytes at a time: misaligned ones are rejected
+    for bad in range(3):
+        outs = [fake] * 5
+        outs[(0, 1, 3)[bad]] = fake + 4
+        st = lib.kda_chunk_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None, None, fake, None,
+                               *outs, None, None, None, fake, 1 << 40, None)
+        assert st == kda.KDA_ERR_INVALID_ARGUMENT and (b"dq", b"dk", b"dg")[bad] in lib.kda_last_error()
     # an empty selection (N = 0) launches nothing and succeeds
     p0, keep = _tnd([0])
     sz = ctypes.c_size_t()
