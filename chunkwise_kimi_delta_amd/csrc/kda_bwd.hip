@@ -1050,28 +1050,26 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     f32x4 an[OV::TPW], ad[OV::TPW];
     zero(an);
     zero(ad);
-    const float* wr = rec + R.w + ov.r16 * KD + 4 * ov.q;
-#pragma unroll 2
-    for (int kk = 0; kk < KD; kk += 16) {
-      float bh[4], bd[4];
-      {
-        const f32x4 h4 = *reinterpret_cast<const f32x4*>(hc + sq_index(kk + 4 * ov.q, vc, VD));
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dh + sq_index(kk + 4 * ov.q, vc, VD));
+    // the K reductions as bf16 hi/lo products (three passes each): lane group q
+    // takes rows 32 kb + 8 q .. +7 of h and dh' (two 16-byte loads in their
+    // four-row layout) and the same channels of the w and kg rows
+    const float* wr = rec + R.w + ov.r16 * KD + 8 * ov.q;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          bh[p] = h4[p];
-          bd[p] = d4[p];
-        }
-      }
+    for (int kb = 0; kb < KD / 32; ++kb) {
+      const int k0 = 32 * kb + 8 * ov.q;
+      float x[8];
+      *reinterpret_cast<f32x4*>(x) = *reinterpret_cast<const f32x4*>(hc + sq_index(k0, vc, VD));
+      *reinterpret_cast<f32x4*>(x + 4) = *reinterpret_cast<const f32x4*>(hc + sq_index(k0 + 4, vc, VD));
+      const Frag bh = split8(x);
+      *reinterpret_cast<f32x4*>(x) = *reinterpret_cast<const f32x4*>(dh + sq_index(k0, vc, VD));
+      *reinterpret_cast<f32x4*>(x + 4) = *reinterpret_cast<const f32x4*>(dh + sq_index(k0 + 4, vc, VD));
+      const Frag bd = split8(x);
 #pragma unroll
       for (int t = 0; t < OV::TPW; ++t) {
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(wr + 16 * ov.ti(t) * KD + kk);
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(&sKG[(16 * ov.ti(t) + ov.r16) * LX + kk + 4 * ov.q]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          an[t] = mfma4(wv[p], bh[p], an[t]);
-          ad[t] = mfma4(kv[p], bd[p], ad[t]);
-        }
+        ld8(wr + 16 * ov.ti(t) * KD + 32 * kb, x);
+        an[t] = mma3(split8(x), bh, an[t]);
+        ld8(&sKG[(16 * ov.ti(t) + ov.r16) * LX + k0], x);
+        ad[t] = mma3(split8(x), bd, ad[t]);
       }
     }
 #pragma unroll 2
