@@ -215,6 +215,28 @@ __device__ __forceinline__ void ld8s(const float* p, float (&x)[8]) {
   }
 }
 
+// 4 x 4 transpose across the four lanes of a quad (b = lane & 3): lane b's
+// x[j] becomes lane j's x[b].  Two exchanges of 2 x 2 blocks through DPP quad
+// permutations (xor 1, then xor 2), every lane active.
+template <int CTRL> __device__ __forceinline__ float dpp_q(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ void quad_transpose(f32x4& x, int b) {
+  const bool o1 = b & 1, o2 = b & 2;
+  float r = dpp_q<0xB1>(o1 ? x[0] : x[1]);   // quad_perm [1, 0, 3, 2]
+  x[0] = o1 ? r : x[0];
+  x[1] = o1 ? x[1] : r;
+  r = dpp_q<0xB1>(o1 ? x[2] : x[3]);
+  x[2] = o1 ? r : x[2];
+  x[3] = o1 ? x[3] : r;
+  r = dpp_q<0x4E>(o2 ? x[0] : x[2]);         // quad_perm [2, 3, 0, 1]
+  x[0] = o2 ? r : x[0];
+  x[2] = o2 ? x[2] : r;
+  r = dpp_q<0x4E>(o2 ? x[1] : x[3]);
+  x[1] = o2 ? r : x[1];
+  x[3] = o2 ? x[3] : r;
+}
+
 // The chunk-entry states for the backward, in fp32 from the fp32 records:
 // h <- D h + kg^T (u - w h), every entry state stored.  Operands per chunk:
 // -w as A[token][K] and kg^T = (k 2^(G_C - G))^T as A[K][token].
@@ -1123,31 +1145,43 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     zero(ak);
     zero(aq);
     zero(aw);
-    const float* hr = hc + sq_index(kc, 4 * ok.q, VD);
-    const float* dhr = dh + sq_index(kc, 4 * ok.q, VD);
+    // bf16 hi/lo products over the V columns: lane group q takes columns
+    // 32 kb + 8 q .. +7.  h and dh' come in their four-row layout, one 16-byte
+    // load per column for the four channels of the lane's quad, and a 4 x 4
+    // transpose across the quad leaves each lane its own channel's columns.
+    const int qb = ok.r16 & 3;   // this lane's place in its quad (= kc & 3)
+    const float* hq = hc + sq_index(kc & ~3, 8 * ok.q + qb, VD);
+    const float* dhq = dh + sq_index(kc & ~3, 8 * ok.q + qb, VD);
     float dd = 0.f;   // this lane's quarter of the columns
-#pragma unroll 2
-    for (int s2 = 0; s2 < VD / 16; ++s2) {
-      f32x4 hv, dv;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        hv[p] = hr[4 * (16 * s2 + p)];
-        dv[p] = dhr[4 * (16 * s2 + p)];
+    for (int kb = 0; kb < VD / 32; ++kb) {
+      f32x4 h0 = ld4(hq + 4 * (32 * kb)), h1 = ld4(hq + 4 * (32 * kb + 4));
+      f32x4 d0 = ld4(dhq + 4 * (32 * kb)), d1 = ld4(dhq + 4 * (32 * kb + 4));
+      quad_transpose(h0, qb);
+      quad_transpose(h1, qb);
+      quad_transpose(d0, qb);
+      quad_transpose(d1, qb);
+      float xh[8], xd[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xh[j] = h0[j];
+        xh[4 + j] = h1[j];
+        xd[j] = d0[j];
+        xd[4 + j] = d1[j];
       }
 #pragma unroll
-      for (int p = 0; p < 4; ++p) dd += hv[p] * dv[p];
+      for (int j = 0; j < 8; ++j) dd += xh[j] * xd[j];
+      const Frag bh = split8(xh), bd = split8(xd);
 #pragma unroll
       for (int t = 0; t < OK::TPW; ++t) {
-        const int ro = (16 * ok.ti(t) + ok.r16) * LX + 16 * s2 + 4 * ok.q;
-        const f32x4 vn = *reinterpret_cast<const f32x4*>(&sB1[ro]);
-        const f32x4 d = *reinterpret_cast<const f32x4*>(&sDo[ro]);
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&sB2[ro]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          ak[t] = mfma4(vn[p], dv[p], ak[t]);
-          aq[t] = mfma4(d[p], hv[p], aq[t]);
-          aw[t] = mfma4(x[p], hv[p], aw[t]);
-        }
+        const int ro = (16 * ok.ti(t) + ok.r16) * LX + 32 * kb + 8 * ok.q;
+        float x[8];
+        ld8(&sB1[ro], x);
+        ak[t] = mma3(split8(x), bd, ak[t]);
+        ld8(&sDo[ro], x);
+        aq[t] = mma3(split8(x), bh, aq[t]);
+        ld8(&sB2[ro], x);
+        aw[t] = mma3(split8(x), bh, aw[t]);
       }
     }
     dd += __shfl_xor(dd, 16);
