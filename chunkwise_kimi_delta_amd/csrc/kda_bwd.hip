@@ -1018,6 +1018,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   __syncthreads();
   // staged once: do (fp32) into B3, kg and Aqk into the small matrices' space
   float* sDo = sB3;
+  float* sBX = sB3;   // b k 2^G once do is no longer needed
   {  // every load issued before any use
     constexpr int ND = BT * VD / 4 / NTH, NK = BT * KD / 4 / NTH, NQ = BT * BT / 4 / NTH;
     f32x4 xd[ND], xk[NK], xg[NK], xq[NQ];
@@ -1225,6 +1226,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
         dbK[t][e] += X * acc[t][e];
         dk[t][e] += ex * dX;
         dG[t][e] += X * dX;
+        sBX[j * LX + kk] = sBeta[j] * X;   // b k 2^G for dA (do's space is free)
       }
   }
   {  // d(b v) = A^T dv_new: dv and b
@@ -1246,7 +1248,8 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
         if (j < P.C) a.dv[((P.tok0 + j) * a.Hv + h) * VD + c] = sBeta[j] * acc[t][e];
       }
   }
-  {  // dA = tril(dv_new (b v)^T + dw (b k e^G)^T)  -> S3 (b v, b k e^G straight from global memory)
+  __syncthreads();   // b k 2^G staged
+  {  // dA = tril(dv_new (b v)^T + dw (b k e^G)^T)  -> S3 (b v straight from global memory, b k e^G from LDS)
     f32x4 acc[OS::TPW];
     zero(acc);
     const int j = os.col();
@@ -1263,13 +1266,12 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     }
 #pragma unroll 4
     for (int c0 = 0; c0 < KD; c0 += 16) {
-      const f32x4 kv = *reinterpret_cast<const f32x4*>(kn + j * KD + c0 + 4 * os.q);
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(G + j * KD + c0 + 4 * os.q);
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(&sBX[j * LX + c0 + 4 * os.q]);
 #pragma unroll
       for (int t = 0; t < OS::TPW; ++t) {
         const f32x4 av = *reinterpret_cast<const f32x4*>(&sB1[(16 * os.ti(t) + os.r16) * LX + c0 + 4 * os.q]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], bj * kv[p] * ex2(gv[p]), acc[t]);
+        for (int p = 0; p < 4; ++p) acc[t] = mfma4(av[p], xv[p], acc[t]);
       }
     }
 #pragma unroll
