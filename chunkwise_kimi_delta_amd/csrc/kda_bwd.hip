@@ -7,9 +7,10 @@
 // inter-chunk recurrence of the state gradient, the WY / intra-chunk
 // backward and the reverse cumsum of the gate gradient) and 2.5 (the gate
 // backward), and "Hyper-Parallel Chunk KDA" section 5.2 (backward stages).
-// All arithmetic is fp32: the chunk-local products on the fp32 matrix cores,
-// the two state scans on bf16 hi/lo operand pairs (~16 significant bits per
-// operand, fp32 accumulation, three passes per product).  The decay
+// All values are fp32.  The two state scans and the chunk kernel's passes over
+// K and V multiply bf16 hi/lo operand pairs (~16 significant bits per operand,
+// fp32 accumulation, three passes per product); the other chunk-local
+// products run on the fp32 matrix cores.  The decay
 // ratios exp(G_i - G_j) of a chunk are never formed from a positive exponent:
 // a block of rows against an earlier block splits at the later block's first
 // row r into 2^(G_i - G_r) 2^(G_r - G_j), both <= 1 (G is the in-chunk cumsum,
