@@ -280,9 +280,7 @@ __global__ __launch_bounds__(VD * 4) void bwd_state_kernel(BwdArgs a) {
     // then the loads: u (v_new starts at u), -w, and k, G, G_C for kg^T
     f32x4 vn[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vn[rt][e] = rec[R.u + (16 * rt + 4 * g + e) * VD + col];
+    for (int rt = 0; rt < 4; ++rt) vn[rt] = ld4(rec + R.u + sq_index(16 * rt + 4 * g, col, VD));
     const float gcv = tid < KD ? Gc[tid] : 0.f;
     // (a wave past the last fragment loads the last one again and skips its write)
     float xw[IW][8], xk[IK][8], xg[IK][8], xc[IK][8];
@@ -891,10 +889,8 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
           acc[t] = mfma4(av[p], sX[(kk + 4 * tv.q + p) * LX + 16 * (tv.cb0 + t) + tv.r16], acc[t]);
     }
 #pragma unroll
-    for (int t = 0; t < TV::TPW; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        rec[R.u + (16 * tv.rb + 4 * tv.q + e) * VD + 16 * (tv.cb0 + t) + tv.r16] = acc[t][e];
+    for (int t = 0; t < TV::TPW; ++t)   // (u keeps four rows of a column together)
+      *reinterpret_cast<f32x4*>(rec + R.u + sq_index(16 * tv.rb + 4 * tv.q, 16 * (tv.cb0 + t) + tv.r16, VD)) = acc[t];
   }
   __syncthreads();
 #pragma unroll 4
@@ -1108,13 +1104,15 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
           ad[t] = mfma4(sAq[(r0 + 4 * ov.q + p) * LS + 16 * ov.ti(t) + ov.r16], b[p], ad[t]);
     }
 #pragma unroll
-    for (int t = 0; t < OV::TPW; ++t)
+    for (int t = 0; t < OV::TPW; ++t) {
+      const f32x4 u4 = ld4(rec + R.u + sq_index(16 * ov.ti(t) + 4 * ov.q, vc, VD));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = ov.row(t, e);
-        sB1[i * LX + vc] = rec[R.u + i * VD + vc] - an[t][e];
+        sB1[i * LX + vc] = u4[e] - an[t][e];
         sB2[i * LX + vc] = ad[t][e];
       }
+    }
   }
   __syncthreads();   // (kg and Aqk give their space to the small matrices)
   {  // dAqk = tril(do v_new^T)  -> S1

@@ -138,7 +138,7 @@ inline hipError_t launch(void (*kern)(A...), dim3 grid, dim3 block, hipStream_t 
 //   G [64][K] in-chunk natural-log cumsum of the decay (rows past the end keep
 //   the last value), kn / qn [64][K] normalised k and q, beta [64] (activated),
 //   A [64][64] = (I + L)^-1, aqk [64][64] (scaled, zero above the diagonal),
-//   w [64][K], u [64][V].
+//   w [64][K], u [64][V] stored [16][V][4] (four consecutive rows of a column together).
 struct BwdRec {
   size_t G, kn, qn, beta, A, aqk, w, u, bytes;
 };
