@@ -277,13 +277,13 @@ __global__ __launch_bounds__(VD * 4) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4*>(dst + sq_index(16 * t + 4 * g, col, VD)) = H[t];
     }
-    // then the loads: u (v_new starts at u), -w, and k, G, G_C for kg^T
+    // then the loads: u (v_new starts at u), -w and kg
     f32x4 vn[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) vn[rt] = ld4(rec + R.u + sq_index(16 * rt + 4 * g, col, VD));
     const float gcv = tid < KD ? Gc[tid] : 0.f;
     // (a wave past the last fragment loads the last one again and skips its write)
-    float xw[IW][8], xk[IK][8], xg[IK][8], xc[IK][8];
+    float xw[IW][8], xk[IK][8];
 #pragma unroll
     for (int i = 0; i < IW; ++i) {
       const int f = min(wave + NW * i, NFW - 1);
@@ -293,9 +293,7 @@ __global__ __launch_bounds__(VD * 4) void bwd_state_kernel(BwdArgs a) {
     for (int i = 0; i < IK; ++i) {
       const int f = min(wave + NW * i, NFK - 1);
       const int t = 32 * (f % 2) + (lane >> 1), k0 = 16 * (f / 2) + 8 * (lane & 1);
-      ld8(rec + R.kn + t * KD + k0, xk[i]);
-      ld8(rec + R.G + t * KD + k0, xg[i]);
-      ld8(Gc + k0, xc[i]);
+      ld8(rec + R.kg + t * KD + k0, xk[i]);
     }
     __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
 #pragma unroll
@@ -310,11 +308,7 @@ __global__ __launch_bounds__(VD * 4) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < IK; ++i) {
       const int f = wave + NW * i;
-      if (f < NFK) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xk[i][j] *= ex2(xc[i][j] - xg[i][j]);
-        stage_t(fK + f * FRB, lane, xk[i]);
-      }
+      if (f < NFK) stage_t(fK + f * FRB, lane, xk[i]);
     }
     wave_lds_sync();
 #pragma unroll
@@ -406,14 +400,11 @@ __global__ __launch_bounds__(VD * 4) void bwd_scan_kernel(BwdArgs a) {
     // then the loads (a wave past the last fragment of a kind loads the last
     // one again and skips its write)
     const float gcv = tid < KD ? Gc[tid] : 0.f;
-    float xg[IG][8], xgg[IG][8], xgc[IG][8], xa[IA][8], xq[IQ][8], xqg[IQ][8], xw[IQ][8];
+    float xg[IG][8], xa[IA][8], xq[IQ][8], xw[IQ][8];
 #pragma unroll
     for (int i = 0; i < IG; ++i) {
       const int f = min(wave + NW * i, NFG - 1);
-      const int o = (16 * (f / NKB) + r16) * KD + 32 * (f % NKB) + 4 * g;
-      ld8s(rec + R.kn + o, xg[i]);
-      ld8s(rec + R.G + o, xgg[i]);
-      ld8s(Gc + 32 * (f % NKB) + 4 * g, xgc[i]);
+      ld8s(rec + R.kg + (16 * (f / NKB) + r16) * KD + 32 * (f % NKB) + 4 * g, xg[i]);
     }
 #pragma unroll
     for (int i = 0; i < IA; ++i) {
@@ -424,8 +415,7 @@ __global__ __launch_bounds__(VD * 4) void bwd_scan_kernel(BwdArgs a) {
     for (int i = 0; i < IQ; ++i) {
       const int f = min(wave + NW * i, NFQ - 1);   // f = 2 * (block of 16 K) + (block of 32 tokens)
       const int o = (32 * (f % 2) + (lane >> 1)) * KD + 16 * (f / 2) + 8 * (lane & 1);
-      ld8(rec + R.qn + o, xq[i]);
-      ld8(rec + R.G + o, xqg[i]);
+      ld8(rec + R.qg + o, xq[i]);
       ld8(rec + R.w + o, xw[i]);
     }
     // do: this wave's two fragments (column block = wave), rows past the chunk zero
@@ -449,11 +439,7 @@ __global__ __launch_bounds__(VD * 4) void bwd_scan_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < IG; ++i) {
       const int f = wave + NW * i;
-      if (f < NFG) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xg[i][j] *= ex2(xgc[i][j] - xgg[i][j]);
-        frag_put(fG + f * FRB, lane, split8(xg[i]));
-      }
+      if (f < NFG) frag_put(fG + f * FRB, lane, split8(xg[i]));
     }
     // transposed fragments: stage, gather, split
 #pragma unroll
@@ -464,10 +450,7 @@ __global__ __launch_bounds__(VD * 4) void bwd_scan_kernel(BwdArgs a) {
       const int f = wave + NW * i;
       if (f < NFQ) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xq[i][j] *= a.scale * ex2(xqg[i][j]);
-          xw[i][j] = -xw[i][j];
-        }
+        for (int j = 0; j < 8; ++j) xw[i][j] = -xw[i][j];
         stage_t(fQ + f * FRB, lane, xq[i]);
         stage_t(fWT + f * FRB, lane, xw[i]);
       }
@@ -688,6 +671,18 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     *reinterpret_cast<f32x4*>(rec + R.G + i) = *reinterpret_cast<const f32x4*>(&sG[r * LX + c]);
     *reinterpret_cast<f32x4*>(rec + R.kn + i) = *reinterpret_cast<const f32x4*>(&sK[r * LX + c]);
     *reinterpret_cast<f32x4*>(rec + R.qn + i) = *reinterpret_cast<const f32x4*>(&sX[r * LX + c]);
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(&sG[r * LX + c]);
+    const f32x4 gC = *reinterpret_cast<const f32x4*>(&sG[(P.C - 1) * LX + c]);
+    const f32x4 kv = *reinterpret_cast<const f32x4*>(&sK[r * LX + c]);
+    const f32x4 qv = *reinterpret_cast<const f32x4*>(&sX[r * LX + c]);
+    f32x4 kgv, qgv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kgv[e] = kv[e] * ex2(gC[e] - gv[e]);
+      qgv[e] = a.scale * qv[e] * ex2(gv[e]);
+    }
+    *reinterpret_cast<f32x4*>(rec + R.kg + i) = kgv;
+    *reinterpret_cast<f32x4*>(rec + R.qg + i) = qgv;
   }
   if (tid < BT) rec[R.beta + tid] = sB[tid];
 
@@ -1018,7 +1013,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   float* sBX = sB3;   // b k 2^G once do is no longer needed
   {  // every load issued before any use
     constexpr int ND = BT * VD / 4 / NTH, NK = BT * KD / 4 / NTH, NQ = BT * BT / 4 / NTH;
-    f32x4 xd[ND], xk[NK], xg[NK], xq[NQ];
+    f32x4 xd[ND], xk[NK], xq[NQ];
 #pragma unroll
     for (int s2 = 0; s2 < ND; ++s2) {
       const int i4 = tid + NTH * s2, r = 4 * i4 / VD, cc = 4 * i4 % VD;
@@ -1027,8 +1022,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int s2 = 0; s2 < NK; ++s2) {
       const int i4 = tid + NTH * s2;
-      xk[s2] = *reinterpret_cast<const f32x4*>(kn + 4 * i4);
-      xg[s2] = *reinterpret_cast<const f32x4*>(G + 4 * i4);
+      xk[s2] = *reinterpret_cast<const f32x4*>(rec + R.kg + 4 * i4);
     }
 #pragma unroll
     for (int s2 = 0; s2 < NQ; ++s2) xq[s2] = *reinterpret_cast<const f32x4*>(rec + R.aqk + 4 * (tid + NTH * s2));
@@ -1040,10 +1034,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int s2 = 0; s2 < NK; ++s2) {
       const int i4 = tid + NTH * s2, r = 4 * i4 / KD, cc = 4 * i4 % KD;
-      f32x4 x;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) x[p] = xk[s2][p] * ex2(sGC[cc + p] - xg[s2][p]);
-      *reinterpret_cast<f32x4*>(&sKG[r * LX + cc]) = x;
+      *reinterpret_cast<f32x4*>(&sKG[r * LX + cc]) = xk[s2];
     }
 #pragma unroll
     for (int s2 = 0; s2 < NQ; ++s2) {

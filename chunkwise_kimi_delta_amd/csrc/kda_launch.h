@@ -135,12 +135,14 @@ inline hipError_t launch(void (*kern)(A...), dim3 grid, dim3 block, hipStream_t 
 }
 
 // Backward record per (head, chunk), fp32 row-major, offsets in floats:
-//   G [64][K] in-chunk natural-log cumsum of the decay (rows past the end keep
+//   G [64][K] in-chunk cumsum of the decay in log2 units (rows past the end keep
 //   the last value), kn / qn [64][K] normalised k and q, beta [64] (activated),
 //   A [64][64] = (I + L)^-1, aqk [64][64] (scaled, zero above the diagonal),
-//   w [64][K], u [64][V] stored [16][V][4] (four consecutive rows of a column together).
+//   w [64][K], u [64][V] stored [16][V][4] (four consecutive rows of a column
+//   together), kg = kn 2^(G_C - G) and qg = scale qn 2^G [64][K] (G_C: the last
+//   row of G) for the state scans and the chunk kernel.
 struct BwdRec {
-  size_t G, kn, qn, beta, A, aqk, w, u, bytes;
+  size_t G, kn, qn, beta, A, aqk, w, u, kg, qg, bytes;
 };
 __host__ __device__ constexpr BwdRec bwd_rec(int K, int V) {
   BwdRec r{};
@@ -152,7 +154,9 @@ __host__ __device__ constexpr BwdRec bwd_rec(int K, int V) {
   r.aqk = r.A + 64 * 64;
   r.w = r.aqk + 64 * 64;
   r.u = r.w + 64 * (size_t)K;
-  r.bytes = al256((r.u + 64 * (size_t)V) * 4);
+  r.kg = r.u + 64 * (size_t)V;
+  r.qg = r.kg + 64 * (size_t)K;
+  r.bytes = al256((r.qg + 64 * (size_t)K) * 4);
   return r;
 }
 
