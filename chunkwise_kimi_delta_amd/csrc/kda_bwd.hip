@@ -14,9 +14,10 @@
 // ratios exp(G_i - G_j) of a chunk are never formed from a positive exponent:
 // a block of rows against an earlier block splits at the later block's first
 // row r into 2^(G_i - G_r) 2^(G_r - G_j), both <= 1 (G is the in-chunk cumsum,
-// non-increasing), and the pairs inside a 16-row block are split further at
-// the levels of a binary split, so prescaled operands turn the pair sums into
-// plain matrix products for any decay.
+// non-increasing), and the pairs inside a 16-row block use its row 8 as the
+// reference when no factor that makes exceeds 2^96, else the levels of a
+// binary split, so prescaled operands turn the pair sums into plain matrix
+// products for any decay.
 //
 // Per chunk (rows i < C, h the chunk-entry state, h' its exit state):
 //   v_new = u - w h,   o = qg h + Aqk v_new,   h' = D h + kg^T v_new
@@ -31,7 +32,8 @@
 // and the pair sums of dL and dAqk back into k, q, b and G.
 //
 // Kernels:
-//   bwd_prep_kernel   (chunk, head): gate, norms, sigmoid, G, L, Aqk, A, u, w -> fp32 record
+//   bwd_prep_kernel   (chunk, head): gate, norms, sigmoid, G, L, Aqk, A, u, w, kg, qg
+//                     -> fp32 record
 //   bwd_state_kernel  (sequence, head): the forward state recurrence, storing every
 //                     chunk-entry state
 //   bwd_scan_kernel   (sequence, head): the reverse recurrence of dh, storing each
