@@ -11,7 +11,7 @@
 #include <string>
 
 #include "../../include/kda.h"
-#include "kda_launch.h"
+#include "kda_bwd_launch.h"
 
 namespace {
 

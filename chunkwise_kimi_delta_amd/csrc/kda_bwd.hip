@@ -45,7 +45,7 @@
 //   bwd_qk_kernel     (token, q/k head): grouped-head sum and L2Norm backward
 //   bwd_gate_kernel / bwd_gate_sum_kernel: gate and sigmoid backward, dA_log and
 //                     dt_bias sums (two passes, fixed order: deterministic)
-#include "kda_launch.h"
+#include "kda_bwd_launch.h"
 
 #include <type_traits>
 

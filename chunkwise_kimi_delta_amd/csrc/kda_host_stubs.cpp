@@ -4,7 +4,7 @@
 // on a machine without a GPU.  They launch nothing and report success.
 #include <cstdio>
 
-#include "kda_launch.h"
+#include "kda_bwd_launch.h"
 
 namespace kda {
 hipError_t launch_chunk_offsets(const int32_t*, int, int32_t*, hipStream_t) { return hipSuccess; }

@@ -134,53 +134,6 @@ inline hipError_t launch(void (*kern)(A...), dim3 grid, dim3 block, hipStream_t 
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, 0, s);
 }
 
-// Backward record per (head, chunk), fp32 row-major, offsets in floats:
-//   G [64][K] in-chunk cumsum of the decay in log2 units (rows past the end keep
-//   the last value), kn / qn [64][K] normalised k and q, beta [64] (activated),
-//   A [64][64] = (I + L)^-1, aqk [64][64] (scaled, zero above the diagonal),
-//   w [64][K], u [64][V] stored [16][V][4] (four consecutive rows of a column
-//   together), kg = kn 2^(G_C - G) and qg = scale qn 2^G [64][K] (G_C: the last
-//   row of G) for the state scans and the chunk kernel.
-struct BwdRec {
-  size_t G, kn, qn, beta, A, aqk, w, u, kg, qg, bytes;
-};
-__host__ __device__ constexpr BwdRec bwd_rec(int K, int V) {
-  BwdRec r{};
-  r.G = 0;
-  r.kn = r.G + 64 * (size_t)K;
-  r.qn = r.kn + 64 * (size_t)K;
-  r.beta = r.qn + 64 * (size_t)K;
-  r.A = r.beta + 64;
-  r.aqk = r.A + 64 * 64;
-  r.w = r.aqk + 64 * 64;
-  r.u = r.w + 64 * (size_t)K;
-  r.kg = r.u + 64 * (size_t)V;
-  r.qg = r.kg + 64 * (size_t)K;
-  r.bytes = al256((r.qg + 64 * (size_t)K) * 4);
-  return r;
-}
-
-struct BwdArgs {
-  SeqInfo seq;
-  const void *q, *k, *v, *g, *beta, *dout;   // token tensors (dtype of q)
-  const float *A_log, *dt_bias, *dht;        // dht [N][Hv][K][V] or null
-  int Hk, Hv, nchunks;
-  uint32_t flags;
-  float scale, eps, lower_bound;
-  float* rec;                 // [Hv * nchunks] backward records
-  const float* h0;            // [N][Hv][K][V] or null (zero)
-  const float* h_store;       // [Hv * nchunks][K/4][V][4] chunk-entry states (four rows of a column together)
-  float* h_store_w;           // the same buffer, written by the state kernel
-  float* dh_store;            // [Hv * nchunks][K/4][V][4] gradients of the chunk-exit states (or null)
-  float* dh0;                 // [N][Hv][K][V] or null
-  float *dqn, *dkn;           // [tokens][Hv][K]: per value head, w.r.t. normalised q / k
-  float *dbeta_act, *dg_nat;  // [tokens][Hv] w.r.t. activated beta, [tokens][Hv][K] w.r.t. the decay
-  float *dq, *dk;             // [tokens][Hk][K]
-  float *dv, *dg, *dbeta;     // [tokens][Hv][V], [tokens][Hv][K], [tokens][Hv]
-  float *dA_log, *ddt_bias;   // [Hv], [Hv][K] or null
-  float* pairs;               // [Hv * nchunks][2][64][64]: dL and dAqk of each chunk
-};
-
 // dtype: 0 = fp32, 1 = bf16
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);
 hipError_t launch_intra(int K, int V, int dtype, const IntraArgs& a, hipStream_t s);
@@ -188,13 +141,6 @@ hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s
 hipError_t launch_merge(int K, int V, const MergeArgs& a, hipStream_t s, bool backward = false);
 hipError_t launch_prefix_merge(int K, int V, const PrefixMergeArgs& a, hipStream_t s);
 hipError_t launch_recurrent(int K, int V, int dtype, const RecurrentArgs& a, hipStream_t s);
-// Backward stage: 0 prep, 6 forward state scan (fp32), 1 reverse state scan,
-// 2 chunk-local backward (products), 7 its pair sums, 3 grouped heads +
-// L2Norm, 4 gate/sigmoid with block partial sums (into `part`), 5 the sums of
-// those partials.
-hipError_t launch_bwd(int K, int V, int dtype, const BwdArgs& a, int stage, int64_t tokens, float* part,
-                      hipStream_t s);
-constexpr int BWD_GATE_TOKENS = 512;   // tokens per gate workgroup (one partial each)
 // Device address of the fixed scratch on the stream's device (kda_noalloc.hip);
 // on failure `why` names the step that failed.
 hipError_t noalloc_scratch(hipStream_t stream, void** out, char* why, size_t why_len);
