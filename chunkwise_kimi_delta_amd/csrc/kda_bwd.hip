@@ -56,6 +56,23 @@ namespace {
 template <typename T> __device__ __forceinline__ float ldf(const T* p);
 template <> __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ldf<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+// One element through a buffer descriptor (zero past its end), as a float.
+template <typename T> __device__ __forceinline__ float ldb(rsrc_t r, uint32_t byte_off);
+template <> __device__ __forceinline__ float ldb<float>(rsrc_t r, uint32_t o) { return __uint_as_float(buf_load4(r, o)); }
+template <> __device__ __forceinline__ float ldb<bf16_t>(rsrc_t r, uint32_t o) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)o, 0, 0) << 16);
+}
+template <typename T> __device__ __forceinline__ f32x4 ldb4(rsrc_t r, uint32_t byte_off);
+template <> __device__ __forceinline__ f32x4 ldb4<float>(rsrc_t r, uint32_t o) { return __builtin_bit_cast(f32x4, buf_load16(r, o)); }
+template <> __device__ __forceinline__ f32x4 ldb4<bf16_t>(rsrc_t r, uint32_t o) {
+  const u32x2 u = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)o, 0, 0));
+  f32x4 x;
+  x[0] = __uint_as_float(u.x << 16);
+  x[1] = __uint_as_float(u.x & 0xffff0000u);
+  x[2] = __uint_as_float(u.y << 16);
+  x[3] = __uint_as_float(u.y & 0xffff0000u);
+  return x;
+}
 // Four consecutive elements as floats (8 bytes of bf16 or 16 bytes of fp32, aligned).
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 ld4(const bf16_t* p) {
@@ -645,6 +662,8 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
       if (live && (a.flags & F_SIGMOID)) b = sigmoid_f(b);
       sB[r] = b;
       sDiag[r] = a.scale * rq * rk * sqk;      // Aqk_rr (decay factor 1)
+      rec[R.rk + r] = rk;
+      rec[R.rq + r] = rq;
     }
   }
   __syncthreads();
@@ -666,13 +685,11 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     for (int r = 0; r < SR; ++r) sG[(r0 + r) * LX + cc] = x[r] + off;
   }
   __syncthreads();
-  // store G, normalised k and q, beta
+  // store G, kg, qg and beta
 #pragma unroll
   for (int s2 = 0; s2 < BT * KD / 4 / NTH; ++s2) {
     const int i = 4 * (tid + NTH * s2), r = i / KD, c = i % KD;
     *reinterpret_cast<f32x4*>(rec + R.G + i) = *reinterpret_cast<const f32x4*>(&sG[r * LX + c]);
-    *reinterpret_cast<f32x4*>(rec + R.kn + i) = *reinterpret_cast<const f32x4*>(&sK[r * LX + c]);
-    *reinterpret_cast<f32x4*>(rec + R.qn + i) = *reinterpret_cast<const f32x4*>(&sX[r * LX + c]);
     const f32x4 gv = *reinterpret_cast<const f32x4*>(&sG[r * LX + c]);
     const f32x4 gC = *reinterpret_cast<const f32x4*>(&sG[(P.C - 1) * LX + c]);
     const f32x4 kv = *reinterpret_cast<const f32x4*>(&sK[r * LX + c]);
@@ -979,7 +996,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sB3[BT * LX];
   // the three 64 x 64 matrices; before them the same space holds kg and Aqk
   __shared__ __attribute__((aligned(16))) float sSm[3 * BT * LS];
-  __shared__ float sBeta[BT], sGC[KD], sDD[KD];
+  __shared__ float sBeta[BT], sRk[BT], sGC[KD], sDD[KD];
   float* sS1 = sSm;
   float* sS2 = sSm + BT * LS;
   float* sS3 = sSm + 2 * BT * LS;
@@ -1004,10 +1021,18 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   const IT* dout = static_cast<const IT*>(a.dout);
   const IT* vin = static_cast<const IT*>(a.v);
   const float* G = rec + R.G;
-  const float* kn = rec + R.kn;
-  const float* qn = rec + R.qn;
+  const float* kgr = rec + R.kg;
+  const float* qgr = rec + R.qg;
   auto VV = [&](int i, int c) { return i < P.C ? ldf(vin + ((P.tok0 + i) * a.Hv + h) * VD + c) : 0.f; };
-  if (tid < BT) sBeta[tid] = rec[R.beta + tid];
+  // normalised k: the chunk's raw k rows through a descriptor bounded at its
+  // last token (rows past it read as zero), times each row's factor
+  const rsrc_t rk_in = make_rsrc(static_cast<const IT*>(a.k) + (P.tok0 * a.Hk + h / (a.Hv / a.Hk)) * KD,
+                                 (uint32_t)(P.C * a.Hk * KD * (int)sizeof(IT)));
+  auto KN = [&](int i, int c) { return ldb<IT>(rk_in, (uint32_t)((i * a.Hk * KD + c) * (int)sizeof(IT))) * sRk[i]; };
+  if (tid < BT) {
+    sBeta[tid] = rec[R.beta + tid];
+    sRk[tid] = rec[R.rk + tid];
+  }
   if (tid < KD) sGC[tid] = G[(P.C - 1) * KD + tid];
   __syncthreads();
   // staged once: do (fp32) into B3, kg and Aqk into the small matrices' space
@@ -1187,10 +1212,10 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
         const int i = ok.row(t, e);
         const float gi = G[i * KD + kc];
         const float ex = ex2(sGC[kc] - gi);
-        const float kgv = kn[i * KD + kc] * ex;
+        const float kgv = kgr[i * KD + kc];   // k^ 2^(G_C - G)
         const float eq = a.scale * ex2(gi);
         dk[t][e] += ex * ak[t][e];
-        dG[t][e] += eq * qn[i * KD + kc] * aq[t][e] - kgv * ak[t][e];
+        dG[t][e] += qgr[i * KD + kc] * aq[t][e] - kgv * ak[t][e];
         dGCp += kgv * ak[t][e];
         dq[t][e] += eq * aq[t][e];
       }
@@ -1213,7 +1238,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = ok.row(t, e), kk = ok.col();
-        const float ex = ex2(G[j * KD + kk]), X = kn[j * KD + kk] * ex;
+        const float ex = ex2(G[j * KD + kk]), X = KN(j, kk) * ex;
         const float dX = sBeta[j] * acc[t][e];
         dbK[t][e] += X * acc[t][e];
         dk[t][e] += ex * dX;
@@ -1393,8 +1418,11 @@ __global__ __launch_bounds__(NTH) void bwd_pairs_kernel(BwdArgs a) {
   const OK ok(tid);
   const float* rec = a.rec + P.slot * (int64_t)(R.bytes / 4);
   const float* G = rec + R.G;
-  const float* kn = rec + R.kn;
-  const float* qn = rec + R.qn;
+  // the chunk's raw q and k rows, bounded at its last token (rows past it read as zero)
+  const int64_t qk0 = (P.tok0 * a.Hk + h / (a.Hv / a.Hk)) * KD;
+  const uint32_t qk_bytes = (uint32_t)(P.C * a.Hk * KD * (int)sizeof(IT));
+  const rsrc_t rk_in = make_rsrc(static_cast<const IT*>(a.k) + qk0, qk_bytes);
+  const rsrc_t rq_in = make_rsrc(static_cast<const IT*>(a.q) + qk0, qk_bytes);
   if (tid < BT) sBeta[tid] = rec[R.beta + tid];
   {  // dL and dAqk
     const float* pr = a.pairs + P.slot * (int64_t)(2 * BT * BT);
@@ -1405,23 +1433,29 @@ __global__ __launch_bounds__(NTH) void bwd_pairs_kernel(BwdArgs a) {
       *reinterpret_cast<f32x4*>(&sS1[r * LS + cc]) = *reinterpret_cast<const f32x4*>(pr + BT * BT + i);
     }
   }
-  // stage G, k, q for the pair sums (16-byte pieces, all issued at once)
+  // stage G and the normalised k and q (raw rows times their factors) for the
+  // pair sums (4-element pieces, all issued at once; rows past the sequence
+  // end are zero)
   {
     constexpr int NP4 = BT * KD / 4 / NTH;
     f32x4 xg[NP4], xk[NP4], xq[NP4];
+    float fk[NP4], fq[NP4];
 #pragma unroll
     for (int s = 0; s < NP4; ++s) {
-      const int i = 4 * (tid + NTH * s);
+      const int i = 4 * (tid + NTH * s), r = i / KD, cc = i % KD;
+      const uint32_t o = (uint32_t)((r * a.Hk * KD + cc) * (int)sizeof(IT));
       xg[s] = *reinterpret_cast<const f32x4*>(G + i);
-      xk[s] = *reinterpret_cast<const f32x4*>(kn + i);
-      xq[s] = *reinterpret_cast<const f32x4*>(qn + i);
+      xk[s] = ldb4<IT>(rk_in, o);
+      xq[s] = ldb4<IT>(rq_in, o);
+      fk[s] = rec[R.rk + r];
+      fq[s] = rec[R.rq + r];
     }
 #pragma unroll
     for (int s = 0; s < NP4; ++s) {
       const int i = 4 * (tid + NTH * s), r = i / KD, cc = i % KD;
       *reinterpret_cast<f32x4*>(&sB1[r * LX + cc]) = xg[s];
-      *reinterpret_cast<f32x4*>(&sB2[r * LX + cc]) = xk[s];
-      *reinterpret_cast<f32x4*>(&sB3[r * LX + cc]) = xq[s];
+      *reinterpret_cast<f32x4*>(&sB2[r * LX + cc]) = xk[s] * fk[s];
+      *reinterpret_cast<f32x4*>(&sB3[r * LX + cc]) = xq[s] * fq[s];
     }
   }
   __syncthreads();

@@ -9,21 +9,23 @@ namespace kda {
 
 // Backward record per (head, chunk), fp32 row-major, offsets in floats:
 //   G [64][K] in-chunk cumsum of the decay in log2 units (rows past the end keep
-//   the last value), kn / qn [64][K] normalised k and q, beta [64] (activated),
-//   A [64][64] = (I + L)^-1, aqk [64][64] (scaled, zero above the diagonal),
-//   w [64][K], u [64][V] stored [16][V][4] (four consecutive rows of a column
-//   together), kg = kn 2^(G_C - G) and qg = scale qn 2^G [64][K] (G_C: the last
-//   row of G) for the state scans and the chunk kernel.
+//   the last value), beta [64] (activated), rk / rq [64] the factors that
+//   normalise each row of k and q (0 past the end; the normalised rows are the
+//   raw rows times these, formed where they are read), A [64][64] = (I + L)^-1,
+//   aqk [64][64] (scaled, zero above the diagonal), w [64][K], u [64][V] stored
+//   [16][V][4] (four consecutive rows of a column together), kg = k^ 2^(G_C - G)
+//   and qg = scale q^ 2^G [64][K] (k^, q^ the normalised rows, G_C the last row
+//   of G) for the state scans and the chunk kernel.
 struct BwdRec {
-  size_t G, kn, qn, beta, A, aqk, w, u, kg, qg, bytes;
+  size_t G, beta, rk, rq, A, aqk, w, u, kg, qg, bytes;
 };
 __host__ __device__ constexpr BwdRec bwd_rec(int K, int V) {
   BwdRec r{};
   r.G = 0;
-  r.kn = r.G + 64 * (size_t)K;
-  r.qn = r.kn + 64 * (size_t)K;
-  r.beta = r.qn + 64 * (size_t)K;
-  r.A = r.beta + 64;
+  r.beta = r.G + 64 * (size_t)K;
+  r.rk = r.beta + 64;
+  r.rq = r.rk + 64;
+  r.A = r.rq + 64;
   r.aqk = r.A + 64 * 64;
   r.w = r.aqk + 64 * 64;
   r.u = r.w + 64 * (size_t)K;
