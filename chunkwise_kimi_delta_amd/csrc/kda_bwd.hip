@@ -1219,6 +1219,11 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
         dGCp += kgv * ak[t][e];
         dq[t][e] += eq * aq[t][e];
       }
+    // the sums formed here, not where they are next used: deferred, they would
+    // keep this pass's loaded G, kg and qg values alive (and spilled) until the end
+#pragma unroll
+    for (int t = 0; t < OK::TPW; ++t) asm volatile("" : "+v"(dq[t]), "+v"(dk[t]), "+v"(dG[t]));
+    asm volatile("" : "+v"(dGCp));
     __syncthreads();   // every wave is done with v_new (B1) before dw replaces it
 #pragma unroll
     for (int t = 0; t < OK::TPW; ++t)
@@ -1245,6 +1250,8 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
         dG[t][e] += X * dX;
         sBX[j * LX + kk] = sBeta[j] * X;   // b k 2^G for dA (do's space is free)
       }
+#pragma unroll
+    for (int t = 0; t < OK::TPW; ++t) asm volatile("" : "+v"(dbK[t]), "+v"(dk[t]), "+v"(dG[t]));   // (as above)
   }
   {  // d(b v) = A^T dv_new: dv and b
     f32x4 acc[OV::TPW];
@@ -1264,6 +1271,8 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
         dbV[t][e] += vv[t][e] * acc[t][e];
         if (j < P.C) a.dv[((P.tok0 + j) * a.Hv + h) * VD + c] = sBeta[j] * acc[t][e];
       }
+#pragma unroll
+    for (int t = 0; t < OV::TPW; ++t) asm volatile("" : "+v"(dbV[t]));
   }
   __syncthreads();   // b k 2^G staged
   {  // dA = tril(dv_new (b v)^T + dw (b k e^G)^T)  -> S3 (b v straight from global memory, b k e^G from LDS)
