@@ -139,16 +139,18 @@ __device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-// Two workgroups per CU, except fp32 tokens with K or V = 128, whose LDS
-// (89 - 108 KB) leaves room for one.
-template <int KD, int VD, typename IT> constexpr int intra_min_blocks() { return (sizeof(IT) == 4 && (KD == 128 || VD == 128)) ? 1 : 2; }
+// Three workgroups per CU with bf16 tokens (at most 53 KB of LDS and 168
+// registers each); fp32 tokens need more LDS: two with K = V = 64, one otherwise.
+template <int KD, int VD, typename IT> constexpr int intra_min_blocks() {
+  return sizeof(IT) == 2 ? 3 : (KD == 128 || VD == 128) ? 1 : 2;
+}
 
 template <int KD, int VD, typename IT, bool FWD>
 __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_kernel(IntraArgs a) {
   using ST = IT;                                   // workspace type of w, qg, Aqk
   constexpr bool F32 = sizeof(IT) == 4;
   constexpr int NKS = KD / 32, NVS = VD / 32;
-  constexpr int P64 = 64 + 4;                      // row stride of sL / sA (floats)
+  constexpr int P64 = 64 + 4;                      // row stride of sLA (floats)
   constexpr int PB = KD + 8;                       // row stride of bf16 column operands
   constexpr int PT = 64 + 16 / (int)sizeof(ST);    // row stride of v^T / X^T (fp32 tokens)
   constexpr int NP = F32 ? 2 : 1;                  // bf16 parts of a column operand (hi [, lo])
@@ -158,13 +160,15 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
   constexpr int VX_BYTES = F32 ? (VD + KD) * PT * 4 : (VD + KD) / 16 * 2 * 1024;
   constexpr int UB = BOP_BYTES > VX_BYTES ? BOP_BYTES : VX_BYTES;
 
-  __shared__ __attribute__((aligned(16))) float sTot[4][KD];   // per-wave gate totals
+  __shared__ __attribute__((aligned(16))) float sTot[3][KD];   // gate totals of waves 0..2
   __shared__ __attribute__((aligned(16))) float sRef[4][KD];   // gamma of rows 16, 32, 48 and the chunk total
-  // sL (Akk) and sA ((I+L)^-1)
-  __shared__ __attribute__((aligned(16))) float sLA[2 * 64 * P64];
+  // L (strictly lower part, row-major) and A = (I+L)^-1 transposed (upper part
+  // and diagonal: A_ij at sLA[j][i] for i >= j) share one 64 x 64 array
+  __shared__ __attribute__((aligned(16))) float sLA[64 * P64];
   float* sL = sLA;
-  float* sA = sLA + 64 * P64;
-  __shared__ float sBeta[64];
+  // beta of row r in the row's padding column (sLA[r][64]; the padding is never
+  // touched otherwise), which keeps the LDS within a third of the CU's
+  auto sBeta = [&](int r) -> float& { return sLA[r * P64 + 64]; };
   // column operands of the off-diagonal levels, later reused for v^T and X^T
   __shared__ __attribute__((aligned(16))) unsigned char sU8[UB];
   bf16_t* b64hi = reinterpret_cast<bf16_t*>(sU8);  // rows 0..31, reference row 32
@@ -208,23 +212,15 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
   // back (a conditional load would make the compiler wait for each one).
   const bool gik = a.flags & F_GATE;
   constexpr int ES = (int)sizeof(IT);
-  float bias[NKS][8];
-  {
-    const rsrc_t rb = make_rsrc(a.dt_bias ? a.dt_bias + h * KD : a.A_log, (gik && a.dt_bias) ? KD * 4 : 0);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) load8b<float>(rb, (uint32_t)(32 * ks + 8 * quad) * 4, bias[ks]);
-  }
+  // gate bias rows: read per channel slice where they are used (L2-resident)
+  const rsrc_t rb = make_rsrc(a.dt_bias ? a.dt_bias + h * KD : a.A_log, (gik && a.dt_bias) ? KD * 4 : 0);
   float gl[NKS][8], kx[NKS][8], qx[NKS][8];
-  // v rows stay as loaded (8 values of the token dtype per slice) until their
-  // transpose: unpacking them here would make the first phase wait for them
-  u32x4 vr[NVS][ES / 2];
   float beta;
   {
     const rsrc_t rg = make_rsrc(static_cast<const IT*>(a.g) + (tok0 * a.Hv + h) * KD, (uint32_t)(C * a.Hv * KD * ES));
     const rsrc_t rk = make_rsrc(static_cast<const IT*>(a.k) + (tok0 * a.Hk + hk) * KD, (uint32_t)(C * a.Hk * KD * ES));
     const rsrc_t rq = make_rsrc(has_q ? static_cast<const IT*>(a.q) + (tok0 * a.Hk + hk) * KD : nullptr,
                                 has_q ? (uint32_t)(C * a.Hk * KD * ES) : 0u);
-    const rsrc_t rv = make_rsrc(static_cast<const IT*>(a.v) + (tok0 * a.Hv + h) * VD, (uint32_t)(C * a.Hv * VD * ES));
     const rsrc_t rbeta = make_rsrc(static_cast<const IT*>(a.beta) + tok0 * a.Hv + h, (uint32_t)(C * a.Hv * ES));
     const uint32_t ok = (uint32_t)(i * a.Hk * KD) * ES, og = (uint32_t)(i * a.Hv * KD) * ES;
 #pragma unroll
@@ -235,12 +231,6 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
       load8b<IT>(rq, ok + (32 * ks + 8 * quad) * ES, qx[ks]);
     }
     beta = load1b<IT>(rbeta, (uint32_t)(i * a.Hv) * ES);
-    __builtin_amdgcn_sched_barrier(0);   // keep beta ahead of the v rows in the queue
-    const uint32_t ov = (uint32_t)(i * a.Hv * VD) * ES;
-#pragma unroll
-    for (int vs = 0; vs < NVS; ++vs)
-#pragma unroll
-      for (int j = 0; j < ES / 2; ++j) vr[vs][j] = buf_load16(rv, ov + (32 * vs + 8 * quad) * ES + 16 * j);
   }
   // (after the row loads: its scalar read and exponential would hold them back)
   __builtin_amdgcn_sched_barrier(0);
@@ -258,9 +248,11 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
       const float cA = live ? -Aexp * LOG2E : 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
+        float bias[8];
+        load8b<float>(rb, (uint32_t)(32 * ks + 8 * quad) * 4, bias);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float z = gl[ks][e] + bias[ks][e];
+          const float z = gl[ks][e] + bias[e];
           // softplus(z) = max(z, 0) + ln(1 + e^-|z|)
           gl[ks][e] = fmaxf(cA * (fmaxf(z, 0.f) + LN2 * flog2(1.f + fexp2(-LOG2E * fabsf(z)))), lb2);
         }
@@ -277,6 +269,18 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
 #pragma unroll
       for (int e = 0; e < 8; ++e) gl[ks][e] = row_scan16(gl[ks][e]);
   }
+  // total decay of this wave's 16 rows (log2 units, largest over the channels):
+  // the row-15 lanes hold the tile totals; it decides the diagonal tile's form
+  float span = 0.f;
+  if (r16 == 15) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) span = fmaxf(span, -gl[ks][e]);
+  }
+  span = fmaxf(span, __shfl_xor(span, 16));
+  span = fmaxf(span, __shfl_xor(span, 32));
+  span = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(span), 15));
   float rq, rk, dqk;
   {
     float sqq = 0.f, skk = 0.f, sqk = 0.f;
@@ -299,14 +303,14 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
     rk = live ? (l2 ? 1.f / sqrtf(skk + a.eps) : 1.f) : 0.f;
     dqk = sqk;
   }
-  if (r16 == 15) {
+  if (r16 == 15 && wave < 3) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) store8(&sTot[wave][32 * ks + 8 * quad], gl[ks]);
   }
   // beta activation here, not at its load: the gate work above needs only the
   // gate rows, and waiting on beta means waiting on every load before it
   if (a.flags & F_SIGMOID) beta = live ? 1.f / (1.f + expf(-beta)) : 0.f;
-  if (quad == 0) sBeta[i] = beta;
+  if (quad == 0) sBeta(i) = beta;
   __syncthreads();
 
   // ---- finish the chunk cumsum; publish reference rows and the chunk decay
@@ -418,13 +422,10 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
     // kg = k * 2^(gamma_C - gamma) as bf16 hi/lo rows, transposed on the
     // matrix cores into kg^T fragments (16 channels x 32 tokens): this wave's
     // 16 tokens are half of fragment (kt, wave / 2), 8 bytes of each lane (hi)
-    // and 4 bytes (lo, as e4m3 after scaling by 2^10, clamped to its range).
-    // The lo bytes of the four waves are gathered in LDS (the inverse's space,
-    // unused until then) and stored as whole 16-byte lane words after the barrier.
+    // and 4 bytes (lo, as e4m3 after scaling by 2^10, clamped to its range),
+    // the lo bytes of the four waves interleaved into 16-byte lane words.
     unsigned char* kgh = rec + RL.kgh;
     const uint32_t kg_off = (uint32_t)((wave >> 1) * 64 + lane) * 16 + (wave & 1) * 8;
-    static_assert(KD * 64 <= 64 * P64 * 4, "the staged kg^T lo bytes fit the inverse's LDS");
-    unsigned char* kstage = reinterpret_cast<unsigned char*>(sA);
     const uint32_t kl_off = (uint32_t)lane * 16 + (wave >> 1) * 8 + (wave & 1) * 4;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -439,20 +440,11 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
         const f32x4 th = mfma(f.hi, sel[half], zero4());
         const f32x4 tl = mfma(f.lo, sel[half], zero4());
         *reinterpret_cast<u32x2*>(kgh + kt * 2 * 1024 + kg_off) = pack4(th);
-        *reinterpret_cast<uint32_t*>(kstage + kt * 1024 + kl_off) = pack4_fp8(tl * KGL_SCALE);
+        *reinterpret_cast<uint32_t*>(rec + RL.kgl + kt * 1024 + kl_off) = pack4_fp8(tl * KGL_SCALE);
       }
     }
   }
   __syncthreads();
-
-  // kg^T lo part: channel tiles KD / 64 * wave .. of the staged bytes, one
-  // contiguous 1 KiB store each
-#pragma unroll
-  for (int j = 0; j < KD / 64; ++j) {
-    const int kt = KD / 64 * wave + j;
-    *reinterpret_cast<u32x4*>(rec + RL.kgl + kt * 1024 + lane * 16) =
-        *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(sA) + kt * 1024 + lane * 16);
-  }
 
   // ---- Akk (L) and Aqk tiles on the matrix cores
   ST* Aqk_out = reinterpret_cast<ST*>(rec + RL.aqk);
@@ -473,27 +465,11 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
     // F_i = k_i 2^(gamma_i - gamma_8) and G_j = k_j 2^(gamma_8 - gamma_j), both
     // below 2^112 in scale, L_ij = beta_i F_i . G_j exactly as at the split
     // levels (entries with i <= j may overflow and are never read).  Decided
-    // per wave from the tile totals kept for the cumsum.
-    bool one_ref = false;
-    if (gik) {
-      float span = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        float t[8];
-        load8(&sTot[wave][32 * ks + 8 * quad], t);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) span = fmaxf(span, -t[e]);
-      }
-      span = fmaxf(span, __shfl_xor(span, 16));
-      span = fmaxf(span, __shfl_xor(span, 32));
-      one_ref = __builtin_amdgcn_readfirstlane(span < 112.f ? 1 : 0) != 0;
-    }
-    f32x4 dk[4], dq[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      dk[b] = zero4();
-      dq[b] = zero4();
-    }
+    // per wave from its own rows' totals (span, taken after the row scans).
+    const bool one_ref = gik && span < 112.f;
+    // dk, dq: the tile's entries (i > j for L, i >= j for Aqk); the split
+    // levels are formed one after another and each keeps only its own entries
+    f32x4 dk = zero4(), dq = zero4();
     if (one_ref) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -510,47 +486,57 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
         // A = G (rows j), B = F (columns i): this lane gets (i = r16, j = 4*quad + e)
         if constexpr (F32) {
           const Frag F = split8(kf), G = split8(kb);
-          dk[0] = mma3(G, F, dk[0]);
-          if (has_q) dq[0] = mma3(G, split8(qf), dq[0]);
+          dk = mma3(G, F, dk);
+          if (has_q) dq = mma3(G, split8(qf), dq);
         } else {
           const bf16x8 F = round8(kf), G = round8(kb);
-          dk[0] = mfma(G, F, dk[0]);
-          if (has_q) dq[0] = mfma(G, round8(qf), dq[0]);
+          dk = mfma(G, F, dk);
+          if (has_q) dq = mfma(G, round8(qf), dq);
         }
       }
     } else {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const bool up = (r16 >> b) & 1;
         // lane-uniform arithmetic only: a cross-lane move under a lane-dependent
         // branch would read from disabled lanes
         const float sgn = up ? 1.f : -1.f;
-        float kv[8], qv[8];
+        f32x4 tk = zero4(), tq = zero4();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float g = gl[ks][e];
-          float ex;
-          if (b == 0) ex = (up ? 0.f : 1.f) * (lane_from<0x101>(g) - g);   // lower rows: row r + 1 (row_shl:1)
-          else if (b == 1) ex = sgn * (g - lane_from<0xAA>(g));           // row (r & ~3) | 2 (quad_perm 2,2,2,2)
-          else if (b == 2) ex = sgn * (g - swizzle<0x98>(g));             // row (r & ~7) | 4
-          else ex = sgn * (g - swizzle<0x110>(g));                        // row 8
-          const float f = fexp2(ex);
-          kv[e] = kx[ks][e] * f;
-          qv[e] = qx[ks][e] * f;
+        for (int ks = 0; ks < NKS; ++ks) {
+          float kv[8], qv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float g = gl[ks][e];
+            float ex;
+            if (b == 0) ex = (up ? 0.f : 1.f) * (lane_from<0x101>(g) - g);   // lower rows: row r + 1 (row_shl:1)
+            else if (b == 1) ex = sgn * (g - lane_from<0xAA>(g));           // row (r & ~3) | 2 (quad_perm 2,2,2,2)
+            else if (b == 2) ex = sgn * (g - swizzle<0x98>(g));             // row (r & ~7) | 4
+            else ex = sgn * (g - swizzle<0x110>(g));                        // row 8
+            const float f = fexp2(ex);
+            kv[e] = kx[ks][e] * f;
+            qv[e] = qx[ks][e] * f;
+          }
+          if constexpr (F32) {
+            const Frag F = split8(kv);
+            tk = mma3(F, F, tk);
+            if (has_q) tq = mma3(F, split8(qv), tq);
+          } else {
+            const bf16x8 F = round8(kv);
+            tk = mfma(F, F, tk);
+            if (has_q) tq = mfma(F, round8(qv), tq);
+          }
         }
-        if constexpr (F32) {
-          const Frag F = split8(kv);
-          dk[b] = mma3(F, F, dk[b]);
-          if (has_q) dq[b] = mma3(F, split8(qv), dq[b]);
-        } else {
-          const bf16x8 F = round8(kv);
-          dk[b] = mfma(F, F, dk[b]);
-          if (has_q) dq[b] = mfma(F, round8(qv), dq[b]);
+        // entries (i, j) with i > j whose highest differing bit is b
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int il = r16, jl = 4 * quad + e;
+          if (il > jl && 31 - __clz(il ^ jl) == b) {
+            dk[e] = tk[e];
+            dq[e] = tq[e];
+          }
         }
       }
-    }
     }
     // diagonal tile output: this lane holds row i = r16, columns 4*quad .. +3,
     // and owns row i's beta, norms and q.k dot
@@ -561,10 +547,8 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
         const int il = r16, jl = 4 * quad + e;
         float vk = 0.f, vq = 0.f;
         if (il > jl) {
-          const int b = one_ref ? 0 : 31 - __clz(il ^ jl);   // (small-decay form: all in dk[0], dq[0])
-          vk = b == 0 ? dk[0][e] : b == 1 ? dk[1][e] : b == 2 ? dk[2][e] : dk[3][e];
-          vq = b == 0 ? dq[0][e] : b == 1 ? dq[1][e] : b == 2 ? dq[2][e] : dq[3][e];
-          vk *= beta;
+          vk = beta * dk[e];
+          vq = dq[e];
         } else if (il == jl) {
           vq = rq * rk * dqk;
         }
@@ -668,7 +652,7 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
         put(1, i, beta, ak[1], aq[1]);
       }
       if (l32) put(0, i, beta, ak[2], aq[2]);
-      if (wave == 0) put(2, 48 + r16, sBeta[48 + r16], ak[2], aq[2]);
+      if (wave == 0) put(2, 48 + r16, sBeta(48 + r16), ak[2], aq[2]);
     }
     if (has_q) {  // upper-triangle tiles of this row tile are zero
       for (int J = wave + 1; J < 4; ++J) store4(Aqk_out + frag_off(i, 16 * J + 4 * quad, 2), zero4());
@@ -676,7 +660,18 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
   }
   __syncthreads();
 
-  // ---- v^T and X^T = (k * 2^gamma)^T into LDS; diagonal 16x16 inverses
+  // ---- v^T and X^T = (k * 2^gamma)^T into LDS; diagonal 16x16 inverses.
+  // The v rows are read only now (8 values of the token dtype per slice): held
+  // from the top of the kernel they would stay live through every phase.
+  u32x4 vr[NVS][ES / 2];
+  {
+    const rsrc_t rv = make_rsrc(static_cast<const IT*>(a.v) + (tok0 * a.Hv + h) * VD, (uint32_t)(C * a.Hv * VD * ES));
+    const uint32_t ov = (uint32_t)(i * a.Hv * VD) * ES;
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+      for (int j = 0; j < ES / 2; ++j) vr[vs][j] = buf_load16(rv, ov + (32 * vs + 8 * quad) * ES + 16 * j);
+  }
   if constexpr (F32) {
 #pragma unroll
     for (int vs = 0; vs < NVS; ++vs)
@@ -704,7 +699,13 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
     for (int ks = 0; ks < NKS; ++ks) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = kx[ks][e] * fexp2(gl[ks][e]);
+      for (int e = 0; e < 8; ++e) {
+        // 2^gamma is formed again here: otherwise the compiler keeps the qg
+        // phase's values live (32 registers) through every phase in between
+        float gg = gl[ks][e];
+        asm volatile("" : "+v"(gg));
+        x[e] = kx[ks][e] * fexp2(gg);
+      }
       const bf16x8 xrow = round8(x);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -724,15 +725,13 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
       for (int kq = 0; kq < r; ++kq) s -= sL[(16 * b + r) * P64 + 16 * b + kq] * x[kq];
       x[r] = s;
     }
+    // column jj of A_bb (x[r] = A_bb[r][jj], zero for r < jj) as row 16b + jj of
+    // sLA: the upper part and the diagonal of the block take A_bb transposed,
+    // and its strictly lower part (L_bb, read only above) becomes zero
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sA[(16 * b + r) * P64 + 16 * b + jj] = x[r];
-  }
-  // zero the strictly upper blocks of A (read by the u/w products)
-  for (int idx = tid; idx < 6 * 256; idx += 256) {
-    const int t = idx >> 8, e = idx & 255;
-    const int I = t < 3 ? 0 : (t < 5 ? 1 : 2);
-    const int J = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
-    sA[(16 * I + (e >> 4)) * P64 + 16 * J + (e & 15)] = 0.f;
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<f32x4*>(&sLA[(16 * b + jj) * P64 + 16 * b + 4 * r4]) =
+          f32x4{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]};
   }
   __syncthreads();
 
@@ -750,8 +749,7 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
 #pragma unroll
     for (int m = 0; m < 3; ++m)
       if (m == J)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) col[m][e] = sA[(16 * J + 4 * quad + e) * P64 + 16 * J + r16];
+        col[m] = *reinterpret_cast<const f32x4*>(&sLA[(16 * J + r16) * P64 + 16 * J + 4 * quad]);
 #pragma unroll
     for (int I = 1; I < 4; ++I) {
       if (I <= J) continue;
@@ -763,15 +761,16 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
 #pragma unroll
         for (int pss = 0; pss < 4; ++pss) x = __builtin_amdgcn_mfma_f32_16x16x4f32(lrow[pss], col[m][pss], x, 0, 0, 0);
       }
-      const f32x4 arow = *reinterpret_cast<const f32x4*>(&sA[(16 * I + r16) * P64 + 16 * I + 4 * quad]);
+      // row r16 of A_II (the block's lower part holds zeros where A_II has them)
+      f32x4 arow;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) arow[e] = sLA[(16 * I + 4 * quad + e) * P64 + 16 * I + r16];
       f32x4 y = zero4();
 #pragma unroll
       for (int pss = 0; pss < 4; ++pss) y = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[pss], x[pss], y, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        col[I][e] = -y[e];
-        sA[(16 * I + 4 * quad + e) * P64 + 16 * J + r16] = -y[e];
-      }
+      col[I] = -y;
+      // A_IJ (I > J) transposed into block (J, I) of sLA, above L
+      *reinterpret_cast<f32x4*>(&sLA[(16 * J + r16) * P64 + 16 * I + 4 * quad]) = -y;
     }
   }
   __syncthreads();
@@ -790,10 +789,17 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
       const int j0 = F32 ? 32 * ks + 8 * quad : 32 * ks + 4 * quad;
       const int j1 = F32 ? j0 + 4 : j0 + 16;
       float ar[8], bt[8], x[8];
-      *reinterpret_cast<f32x4*>(&ar[0]) = *reinterpret_cast<const f32x4*>(&sA[(16 * I + r16) * P64 + j0]);
-      *reinterpret_cast<f32x4*>(&ar[4]) = *reinterpret_cast<const f32x4*>(&sA[(16 * I + r16) * P64 + j1]);
-      *reinterpret_cast<f32x4*>(&bt[0]) = *reinterpret_cast<const f32x4*>(&sBeta[j0]);
-      *reinterpret_cast<f32x4*>(&bt[4]) = *reinterpret_cast<const f32x4*>(&sBeta[j1]);
+      const int ia = 16 * I + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ar[e] = j0 + e <= ia ? sLA[(j0 + e) * P64 + ia] : 0.f;
+        ar[4 + e] = j1 + e <= ia ? sLA[(j1 + e) * P64 + ia] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bt[e] = sBeta(j0 + e);
+        bt[4 + e] = sBeta(j1 + e);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = ar[e] * bt[e];
       fa[ks] = split8(x);
