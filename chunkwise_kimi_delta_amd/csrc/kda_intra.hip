@@ -446,6 +446,10 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
   }
   __syncthreads();
 
+  // v rows (8 values of the token dtype per slice), read after the diagonal
+  // tiles: loaded with the other rows at the top they would stay live through
+  // every phase (the register count that allows three workgroups per CU)
+  u32x4 vr[NVS][ES / 2];
   // ---- Akk (L) and Aqk tiles on the matrix cores
   ST* Aqk_out = reinterpret_cast<ST*>(rec + RL.aqk);
   {
@@ -558,6 +562,14 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
       *reinterpret_cast<f32x4*>(&sL[i * P64 + 16 * wave + 4 * quad]) = vk4;
       if (has_q) store4(Aqk_out + frag_off(i, 16 * wave + 4 * quad, 2), vq4);
     }
+    {
+    const rsrc_t rv = make_rsrc(static_cast<const IT*>(a.v) + (tok0 * a.Hv + h) * VD, (uint32_t)(C * a.Hv * VD * ES));
+    const uint32_t ov = (uint32_t)(i * a.Hv * VD) * ES;
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+      for (int j = 0; j < ES / 2; ++j) vr[vs][j] = buf_load16(rv, ov + (32 * vs + 8 * quad) * ES + 16 * j);
+  }
     // Off-diagonal tiles: row operands (one per reference, shared by the column
     // tiles it meets) against column operands in LDS.  Level 64: tiles 2, 3
     // against 0, 1 (reference row 32) -> acc[0], acc[1], waves 2 and 3; level 32:
@@ -660,18 +672,7 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
   }
   __syncthreads();
 
-  // ---- v^T and X^T = (k * 2^gamma)^T into LDS; diagonal 16x16 inverses.
-  // The v rows are read only now (8 values of the token dtype per slice): held
-  // from the top of the kernel they would stay live through every phase.
-  u32x4 vr[NVS][ES / 2];
-  {
-    const rsrc_t rv = make_rsrc(static_cast<const IT*>(a.v) + (tok0 * a.Hv + h) * VD, (uint32_t)(C * a.Hv * VD * ES));
-    const uint32_t ov = (uint32_t)(i * a.Hv * VD) * ES;
-#pragma unroll
-    for (int vs = 0; vs < NVS; ++vs)
-#pragma unroll
-      for (int j = 0; j < ES / 2; ++j) vr[vs][j] = buf_load16(rv, ov + (32 * vs + 8 * quad) * ES + 16 * j);
-  }
+  // ---- v^T and X^T = (k * 2^gamma)^T into LDS; diagonal 16x16 inverses
   if constexpr (F32) {
 #pragma unroll
     for (int vs = 0; vs < NVS; ++vs)
