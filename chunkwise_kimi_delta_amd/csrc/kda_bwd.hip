@@ -580,7 +580,8 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sA[BT * LS];
   __shared__ float sB[BT], sDiag[BT];
   constexpr BwdRec R = bwd_rec(KD, VD);
-  const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
+  int gc, h;
+  chunk_head_of_block(blockIdx.x, gridDim.x, a.nchunks, a.Hv, a.Hk, gc, h);
   const ChunkPos P = chunk_pos(a.seq, gc, h, a.nchunks);
   const int hk = h / (a.Hv / a.Hk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
@@ -1009,7 +1010,8 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   static_assert((OK::NT + OV::NT) * BT <= BT * LS && (NTH / 64 / OK::NT) * KD <= BT * LS,
                 "reduction buffers fit the small matrices");
   constexpr BwdRec R = bwd_rec(KD, VD);
-  const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
+  int gc, h;
+  chunk_head_of_block(blockIdx.x, gridDim.x, a.nchunks, a.Hv, a.Hk, gc, h);
   const ChunkPos P = chunk_pos(a.seq, gc, h, a.nchunks);
   const int tid = threadIdx.x;
   const OK ok(tid);
@@ -1421,7 +1423,8 @@ __global__ __launch_bounds__(NTH) void bwd_pairs_kernel(BwdArgs a) {
   using OK = Own<KD>;
   static_assert(OK::NT * BT <= BT * LS && (NTH / KD) * KD <= BT * LS, "reduction buffers fit");
   constexpr BwdRec R = bwd_rec(KD, VD);
-  const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
+  int gc, h;
+  chunk_head_of_block(blockIdx.x, gridDim.x, a.nchunks, a.Hv, a.Hk, gc, h);
   const ChunkPos P = chunk_pos(a.seq, gc, h, a.nchunks);
   const int tid = threadIdx.x;
   const OK ok(tid);

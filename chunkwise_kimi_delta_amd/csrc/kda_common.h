@@ -42,6 +42,27 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// Block b of nb = nchunks * Hv chunk-local workgroups -> (chunk gc, value head
+// h).  Without grouped heads: head-major (consecutive blocks take consecutive
+// chunks of one head).  With Hv / Hk = R > 1 value heads per q/k head: the
+// dispatcher deals consecutive blocks to the 8 XCDs in turn, so block b is taken
+// as entry (b % 8) * nb / 8 + b / 8 of one list per XCD, and within that list
+// the R value heads that read the same q/k rows at the same chunk are adjacent:
+// those rows then come from HBM once into the XCD's L2 instead of once per
+// value head.
+__device__ __forceinline__ void chunk_head_of_block(int b, int nb, int nchunks, int Hv, int Hk, int& gc, int& h) {
+  const int R = Hv / Hk;
+  if (R == 1) {
+    gc = b % nchunks;
+    h = b / nchunks;
+    return;
+  }
+  const int L = (nb & 7) == 0 ? (b & 7) * (nb >> 3) + (b >> 3) : b;
+  const int rest = L / R;
+  gc = rest / Hk;
+  h = (rest % Hk) * R + L % R;
+}
+
 // Four floats -> four e4m3 bytes (round to nearest even), clamped to +-448 so
 // that no value converts to NaN.
 __device__ __forceinline__ uint32_t pack4_fp8(const f32x4& v) {

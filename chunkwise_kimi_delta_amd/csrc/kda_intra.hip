@@ -186,7 +186,8 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
   u32x4* sVF = reinterpret_cast<u32x4*>(sU8);      // bf16 tokens: fragment (ct, ks) at [(2ct + ks) * 64]
   u32x4* sXF = sVF + (VD / 16) * 2 * 64;
 
-  const int gc = blockIdx.x % a.nchunks, h = blockIdx.x / a.nchunks;
+  int gc, h;
+  chunk_head_of_block(blockIdx.x, gridDim.x, a.nchunks, a.Hv, a.Hk, gc, h);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave branches are scalar
   const int r16 = lane & 15, quad = lane >> 4;
