@@ -152,6 +152,20 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// Four floats <-> four fp16 values (round to nearest even), 8 bytes.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 pack4_f16(const f32x4& v) {
+  const f16x2 a = {(_Float16)v[0], (_Float16)v[1]}, b = {(_Float16)v[2], (_Float16)v[3]};
+  return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+__device__ __forceinline__ f32x4 unpack4_f16(const u32x2& u) {
+  // (the words are copied to scalars first: a bit cast taken straight from a
+  // vector element expression has been compiled as a cast of element 0)
+  const uint32_t w0 = u.x, w1 = u.y;
+  const f16x2 a = __builtin_bit_cast(f16x2, w0), b = __builtin_bit_cast(f16x2, w1);
+  return f32x4{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+}
+
 // Raw buffer loads: a resource descriptor for a byte range (base in SGPRs,
 // bounds checked by the hardware: reads past num_bytes return zeros) and a
 // 32-bit per-lane byte offset, so that per-lane addresses are computed once.
@@ -161,6 +175,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t num_bytes
 }
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);

@@ -667,8 +667,9 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
       if (l32) put(0, i, beta, ak[2], aq[2]);
       if (wave == 0) put(2, 48 + r16, sBeta(48 + r16), ak[2], aq[2]);
     }
-    if (has_q) {  // upper-triangle tiles of this row tile are zero
-      for (int J = wave + 1; J < 4; ++J) store4(Aqk_out + frag_off(i, 16 * J + 4 * quad, 2), zero4());
+    if (has_q) {  // upper-triangle tiles of this row tile are zero (those of the
+                  // all-zero 32 x 32 block, rows < 32 and tokens >= 32, are never read)
+      for (int J = wave + 1; J < (wave < 2 ? 2 : 4); ++J) store4(Aqk_out + frag_off(i, 16 * J + 4 * quad, 2), zero4());
     }
   }
   __syncthreads();
@@ -828,11 +829,15 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
       }
       return acc;
     };
-    float* uT = reinterpret_cast<float*>(rec + RL.ut);
 #pragma unroll
     for (int ct = 0; ct < VD / 16; ++ct) {
       const f32x4 acc = tile(sVT, sVF, ct, true);
-      *reinterpret_cast<f32x4*>(uT + cfrag_off(16 * I + 4 * quad, 16 * ct + r16, VD / 16)) = acc;
+      const int uo = cfrag_off(16 * I + 4 * quad, 16 * ct + r16, VD / 16);
+      if constexpr (F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(rec + RL.ut) + uo) = acc;
+      } else {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<_Float16*>(rec + RL.ut) + uo) = pack4_f16(acc);
+      }
     }
     // w^T tiles (X^T rows as the A operand): this lane holds token 16*I + r16,
     // channels 16*ct + 4*quad .. +3 -> one vector store

@@ -25,7 +25,11 @@ enum : uint32_t { F_GATE = 1u, F_SAFE = 2u, F_L2 = 4u, F_SIGMOID = 8u };
 //   qg  [64][K]  token dtype   scale * q * 2^gamma, like w (forward only)
 //   aqk [64][64] token dtype   tril(Aqk), rows = tokens, reduction = tokens (forward only)
 //   gd  [K]      fp32          2^gamma_C, the chunk decay (plain vector)
-//   ut  [64][V]  fp32          u as accumulator tiles (16 x 16, four values per lane)
+//   ut  [64][V]  fp16 | fp32   u as accumulator tiles (16 x 16, four values per lane):
+//                              fp16 with bf16 tokens (11 significant bits, 8 bytes
+//                              per lane and tile), fp32 with fp32 tokens
+// The strictly upper 32 x 32 block of aqk (rows 0..31, tokens 32..63) is zero and
+// neither written nor read.
 // Inside an operand fragment the reduction index is permuted by sigma: within
 // each aligned block of 32, index x sits in slot sig32(x), so that reduction
 // slot 8*g + i (g = lane / 16, i = 0..7) holds index 4*g + i for i < 4 and
@@ -35,6 +39,8 @@ struct RecLayout {
   size_t w, kgh, kgl, qg, aqk, gd, ut, bytes;
 };
 __host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+// bytes per element of u in the record, by token element size
+__host__ __device__ constexpr int ut_bytes(int es) { return es == 2 ? 2 : 4; }
 __host__ __device__ constexpr RecLayout rec_layout(int K, int V, int es, bool fwd) {
   RecLayout r{};
   r.w = 0;
@@ -44,7 +50,7 @@ __host__ __device__ constexpr RecLayout rec_layout(int K, int V, int es, bool fw
   r.aqk = al256(r.qg + (fwd ? (size_t)64 * K * es : 0));
   r.gd = al256(r.aqk + (fwd ? (size_t)64 * 64 * es : 0));
   r.ut = al256(r.gd + (size_t)K * 4);
-  r.bytes = al256(r.ut + (size_t)V * 64 * 4);
+  r.bytes = al256(r.ut + (size_t)V * 64 * ut_bytes(es));
   return r;
 }
 // Scale of the fp8 kgl values (2^10): kg^T - hi is below 2^-8 |kg| <= 2^-8

@@ -44,6 +44,8 @@
 // segment writes the sequence's final state.
 #include "kda_launch.h"
 
+#include <type_traits>
+
 namespace kda {
 
 namespace {
@@ -178,9 +180,12 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     // =========================== state waves ===========================
     const int s = wave;
     const int row0 = 32 * s;
+    constexpr int UB = ut_bytes(ES);                      // bytes per element of u
+    // u as stored (four fp16 or fp32 values), converted where it is used
+    using URaw = typename std::conditional<UB == 2, u32x2, u32x4>::type;
     struct Ops {
       Op<ST> w[4];                    // w rows 16*tt + r16, channels row0 + (slots of lane / 16)
-      f32x4 u[TPW][CT];               // u rows 16*(TPW*s + j) + 4*quad .. +3, column v0 + 16*ct + r16
+      URaw u[TPW][CT];                // u rows 16*(TPW*s + j) + 4*quad .. +3, column v0 + 16*ct + r16
       bf16x8 kh[2][2];                // kg^T rows row0 + 16*kt + r16, tokens 32*ks + (slots): hi
       uint64_t kl[2][2];              // the same, lo (e4m3, scaled by 2^10)
       float gd;                       // gdec row row0 + 16*((r16 >> 2) & 1) + 4*quad + (r16 & 3)
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     constexpr uint32_t FW = 512 * ES;                     // bytes per operand fragment
     const uint32_t o_w = L.w + (uint32_t)(s * 512 + lane * 8) * ES;
     const uint32_t o_u = mtile ? (uint32_t)L.bytes
-                               : L.ut + (uint32_t)((TPW * s * (VD / 16) + v0 / 16) * 256 + lane * 4) * 4;
+                               : L.ut + (uint32_t)((TPW * s * (VD / 16) + v0 / 16) * 256 + lane * 4) * UB;
     const uint32_t o_kg = (uint32_t)(2 * s * 2 * 512 + lane * 8) * 2;
     const uint32_t o_kl = (uint32_t)(2 * s * 1024 + lane * 16);     // e4m3: both token blocks per lane
     // (one gdec row per lane: lanes 0..7 of each 16-lane row hold the eight
@@ -205,8 +210,11 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
 #pragma unroll
       for (int j = 0; j < TPW; ++j)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          f.u[j][ct] = __builtin_bit_cast(f32x4, buf_load16(r, o_u + (mtile ? 0 : 1024 * ((VD / 16) * j + ct))));
+        for (int ct = 0; ct < CT; ++ct) {
+          const uint32_t o = o_u + (mtile ? 0 : 256 * UB * ((VD / 16) * j + ct));
+          if constexpr (UB == 2) f.u[j][ct] = buf_load8(r, o);
+          else f.u[j][ct] = buf_load16(r, o);
+        }
     };
     // ... and of the state update
     auto load_b = [&](Ops& f, int c) __attribute__((always_inline)) {
@@ -288,9 +296,11 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) sum[e] += x[e];
           }
-          f32x4 v;
+          f32x4 v, uv;
+          if constexpr (UB == 2) uv = unpack4_f16(cur.u[j][ct]);
+          else uv = __builtin_bit_cast(f32x4, cur.u[j][ct]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = cur.u[j][ct][e] - sum[e];
+          for (int e = 0; e < 4; ++e) v[e] = uv[e] - sum[e];
           sV[c & 1][tt][ct][lane] = half_frag(v);
           sV8[c & 1][tt][ct][lane] = pack4_fp8(v);
         }
