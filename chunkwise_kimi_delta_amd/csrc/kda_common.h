@@ -39,6 +39,11 @@ template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return f
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// The same tile shape on fp16 operands (11 significant bits each).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
@@ -154,6 +159,20 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
 
 // Four floats <-> four fp16 values (round to nearest even), 8 bytes.
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// fp32 -> fp16 hi/lo pairs: hi = RNE(x), lo = RNE(x - hi) (about 22 significant bits)
+struct Frag16 { f16x8 hi, lo; };
+__device__ __forceinline__ void split2_f16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const f16x2 h = {(_Float16)a, (_Float16)b};
+  const f16x2 l = {(_Float16)(a - (float)h[0]), (_Float16)(b - (float)h[1])};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+__device__ __forceinline__ f16x8 round8_f16(const float (&x)[8]) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (_Float16)x[i];
+  return r;
+}
 __device__ __forceinline__ u32x2 pack4_f16(const f32x4& v) {
   const f16x2 a = {(_Float16)v[0], (_Float16)v[1]}, b = {(_Float16)v[2], (_Float16)v[3]};
   return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};

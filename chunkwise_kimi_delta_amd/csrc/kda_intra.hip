@@ -39,6 +39,8 @@
 // With fp32 token tensors Akk and Aqk use bf16 hi/lo pairs (three passes).
 #include "kda_launch.h"
 
+#include <type_traits>
+
 namespace kda {
 
 namespace {
@@ -104,6 +106,15 @@ __device__ __forceinline__ bf16x8 select_operand(int half, int lane) {
     w[j] = (k0 + 2 * j == col ? 0x3f80u : 0u) | (k0 + 2 * j + 1 == col ? 0x3f800000u : 0u);
   return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
 }
+// The same with fp16 operands (1.0 = 0x3c00): A S_half on the fp16 matrix cores.
+__device__ __forceinline__ f16x8 select_operand_f16(int half, int lane) {
+  const int col = 16 * half + (lane & 15), k0 = 8 * (lane >> 4);
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = (k0 + 2 * j == col ? 0x3c00u : 0u) | (k0 + 2 * j + 1 == col ? 0x3c000000u : 0u);
+  return __builtin_bit_cast(f16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
 __device__ __forceinline__ u32x2 pack4(const f32x4& v) {
   return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
@@ -138,6 +149,7 @@ __device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store4(_Float16* p, const f32x4& v) { *reinterpret_cast<u32x2*>(p) = pack4_f16(v); }
 
 // Three workgroups per CU with bf16 tokens (at most 53 KB of LDS and 168
 // registers each); fp32 tokens need more LDS: two with K = V = 64, one otherwise.
@@ -420,11 +432,12 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
         store4(qg + frag_off(i, 32 * ks + 8 * quad + 4, NKS), x1);
       }
     }
-    // kg = k * 2^(gamma_C - gamma) as bf16 hi/lo rows, transposed on the
-    // matrix cores into kg^T fragments (16 channels x 32 tokens): this wave's
-    // 16 tokens are half of fragment (kt, wave / 2), 8 bytes of each lane (hi)
-    // and 4 bytes (lo, as e4m3 after scaling by 2^10, clamped to its range),
-    // the lo bytes of the four waves interleaved into 16-byte lane words.
+    // kg = k * 2^(gamma_C - gamma), transposed on the matrix cores into kg^T
+    // fragments (16 channels x 32 tokens): this wave's 16 tokens are half of
+    // fragment (kt, wave / 2), 8 bytes of each lane.  bf16 tokens: fp16 rows
+    // (|kg| <= 1, 11 significant bits).  fp32 tokens: bf16 hi rows, and the
+    // lo parts as e4m3 after scaling by 2^10 (clamped to its range), the lo
+    // bytes of the four waves interleaved into 16-byte lane words.
     unsigned char* kgh = rec + RL.kgh;
     const uint32_t kg_off = (uint32_t)((wave >> 1) * 64 + lane) * 16 + (wave & 1) * 8;
     const uint32_t kl_off = (uint32_t)lane * 16 + (wave >> 1) * 8 + (wave & 1) * 4;
@@ -434,14 +447,24 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
       load8(sRef[3] + 32 * ks + 8 * quad, gc);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = kx[ks][e] * fexp2(gc[e] - gl[ks][e]);
-      const Frag f = split8(x);
+      if constexpr (F32) {
+        const Frag f = split8(x);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int kt = 2 * ks + half;
-        const f32x4 th = mfma(f.hi, sel[half], zero4());
-        const f32x4 tl = mfma(f.lo, sel[half], zero4());
-        *reinterpret_cast<u32x2*>(kgh + kt * 2 * 1024 + kg_off) = pack4(th);
-        *reinterpret_cast<uint32_t*>(rec + RL.kgl + kt * 1024 + kl_off) = pack4_fp8(tl * KGL_SCALE);
+        for (int half = 0; half < 2; ++half) {
+          const int kt = 2 * ks + half;
+          const f32x4 th = mfma(f.hi, sel[half], zero4());
+          const f32x4 tl = mfma(f.lo, sel[half], zero4());
+          *reinterpret_cast<u32x2*>(kgh + kt * 2 * 1024 + kg_off) = pack4(th);
+          *reinterpret_cast<uint32_t*>(rec + RL.kgl + kt * 1024 + kl_off) = pack4_fp8(tl * KGL_SCALE);
+        }
+      } else {
+        const f16x8 f = round8_f16(x);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kt = 2 * ks + half;
+          const f32x4 th = mfma(f, select_operand_f16(half, lane), zero4());
+          *reinterpret_cast<u32x2*>(kgh + kt * 2 * 1024 + kg_off) = pack4_f16(th);
+        }
       }
     }
   }
@@ -452,7 +475,9 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
   // every phase (the register count that allows three workgroups per CU)
   u32x4 vr[NVS][ES / 2];
   // ---- Akk (L) and Aqk tiles on the matrix cores
-  ST* Aqk_out = reinterpret_cast<ST*>(rec + RL.aqk);
+  // Aqk: fp16 with bf16 tokens, fp32 with fp32 tokens
+  using AT = typename std::conditional<F32, float, _Float16>::type;
+  AT* Aqk_out = reinterpret_cast<AT*>(rec + RL.aqk);
   {
     // Diagonal tile of this wave: levels L = 2 << b for b = 0..3 (blocks of 2,
     // 4, 8, 16 rows).  At level b every row carries one factor, relative to the

@@ -18,12 +18,14 @@ enum : uint32_t { F_GATE = 1u, F_SAFE = 2u, F_L2 = 4u, F_SIGMOID = 8u };
 // fp8 kgl keeps the two token blocks of a channel tile side by side per lane
 // (8 bytes each), so one 1 KiB load fetches both:
 //   w   [64][K]  token dtype   operand fragments, rows = tokens, reduction = channels
-//   kgh [K][64]  bf16          hi part of kg^T, rows = channels, reduction = tokens
-//   kgl [K][64]  fp8 e4m3      lo part, 2^10 (kg^T - hi) (one byte per element;
+//   kgh [K][64]  fp16 | bf16   kg^T, rows = channels, reduction = tokens: fp16 with
+//                              bf16 tokens; with fp32 tokens its bf16 hi part and
+//   kgl [K][64]  fp8 e4m3      the lo part, 2^10 (kg^T - hi) (one byte per element;
 //                              channel tile kt, lane l, token block tb at
-//                              1024 kt + 16 l + 8 tb)
+//                              1024 kt + 16 l + 8 tb; fp32 tokens only)
 //   qg  [64][K]  token dtype   scale * q * 2^gamma, like w (forward only)
-//   aqk [64][64] token dtype   tril(Aqk), rows = tokens, reduction = tokens (forward only)
+//   aqk [64][64] fp16 | fp32   tril(Aqk), rows = tokens, reduction = tokens (forward
+//                              only; fp16 with bf16 tokens)
 //   gd  [K]      fp32          2^gamma_C, the chunk decay (plain vector)
 //   ut  [64][V]  fp16 | fp32   u as accumulator tiles (16 x 16, four values per lane):
 //                              fp16 with bf16 tokens (11 significant bits, 8 bytes
@@ -46,7 +48,7 @@ __host__ __device__ constexpr RecLayout rec_layout(int K, int V, int es, bool fw
   r.w = 0;
   r.kgh = al256(r.w + (size_t)64 * K * es);
   r.kgl = al256(r.kgh + (size_t)K * 64 * 2);
-  r.qg = al256(r.kgl + (size_t)K * 64);
+  r.qg = al256(r.kgl + (es == 2 ? 0 : (size_t)K * 64));
   r.aqk = al256(r.qg + (fwd ? (size_t)64 * K * es : 0));
   r.gd = al256(r.aqk + (fwd ? (size_t)64 * 64 * es : 0));
   r.ut = al256(r.gd + (size_t)K * 4);

@@ -24,10 +24,12 @@
 // served from L2; they store chunk c's output one step later, between the
 // barriers of chunk c + 1, where they would otherwise wait.
 //
-// Precision.  h and v_new enter the state products as bf16 hi/lo pairs; kg^T
-// comes as a bf16 hi part and an e4m3 lo part (scaled by 2^10), the lo part
-// meeting v_new in e4m3 in an accumulator of its own: kg^T is carried to ~13
-// significant bits, v_new and h to ~16; the bf16 output uses the hi parts only.
+// Precision.  h enters w h as a bf16 hi/lo pair (~16 significant bits).  With
+// bf16 tokens kg^T is stored in fp16 (11 bits, |kg| <= 1) and meets v_new as an
+// fp16 hi/lo pair (~22 bits); the output takes qg h in bf16 (hi parts) and
+// Aqk v_new in fp16 (Aqk fp16, v_new's hi part).  With fp32 tokens v_new is a
+// bf16 hi/lo pair and kg^T a bf16 hi part plus an e4m3 lo part (scaled by
+// 2^10) that meets v_new in e4m3 in an accumulator of its own (~13 bits).
 //
 // Summary mode scans the augmented state [S~ | M] (K x (V + K)) from [0 | I]
 // with u = [u | 0] and writes S~ and M ("KDA Context Parallelism (KCP)",
@@ -104,6 +106,24 @@ __device__ __forceinline__ u32x4 half_frag(const f32x4& v) {
   split2(v[2], v[3], h1, l1);
   return u32x4{h0, h1, l0, l1};
 }
+// The same split into fp16 hi (x, y) and lo (z, w).
+__device__ __forceinline__ u32x4 half_frag16(const f32x4& v) {
+  uint32_t h0, l0, h1, l1;
+  split2_f16(v[0], v[1], h0, l0);
+  split2_f16(v[2], v[3], h1, l1);
+  return u32x4{h0, h1, l0, l1};
+}
+__device__ __forceinline__ Frag16 join_halves16(const u32x4& a, const u32x4& b) {
+  Frag16 f;
+  f.hi = __builtin_bit_cast(f16x8, u32x4{a.x, a.y, b.x, b.y});
+  f.lo = __builtin_bit_cast(f16x8, u32x4{a.z, a.w, b.z, b.w});
+  return f;
+}
+// An fp16 operand fragment of Aqk as stored with bf16 tokens.
+struct OpA16 {
+  f16x8 v;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = __builtin_bit_cast(f16x8, buf_load16(r, off)); }
+};
 __device__ __forceinline__ Frag join_halves(const u32x4& a, const u32x4& b) {
   Frag f;
   f.hi = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
@@ -141,7 +161,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
 
   __shared__ f32x4 sP[NS][4][CT][64];                       // per-wave shares of w h
   __shared__ u32x4 sV[2][4][CT][64];                        // v_new half fragments, by chunk parity
-  __shared__ uint32_t sV8[2][4][CT][64];                    // v_new as e4m3 (for the kg^T lo pass)
+  __shared__ uint32_t sV8[2][F32 ? 4 : 1][CT][64];          // v_new as e4m3 (fp32 tokens: the kg^T lo pass)
   __shared__ bf16x8 sHh[SUM ? 1 : 2][NS][CT][64];           // h fragments (hi) for the output
   __shared__ bf16x8 sHl[(F32 && !SUM) ? 2 : 1][NS][CT][64]; // h fragments (lo), fp32 tokens
 
@@ -183,11 +203,13 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     constexpr int UB = ut_bytes(ES);                      // bytes per element of u
     // u as stored (four fp16 or fp32 values), converted where it is used
     using URaw = typename std::conditional<UB == 2, u32x2, u32x4>::type;
+    // kg^T: fp16 with bf16 tokens; bf16 hi + e4m3 lo with fp32 tokens
+    using KG = typename std::conditional<F32, bf16x8, f16x8>::type;
     struct Ops {
       Op<ST> w[4];                    // w rows 16*tt + r16, channels row0 + (slots of lane / 16)
       URaw u[TPW][CT];                // u rows 16*(TPW*s + j) + 4*quad .. +3, column v0 + 16*ct + r16
-      bf16x8 kh[2][2];                // kg^T rows row0 + 16*kt + r16, tokens 32*ks + (slots): hi
-      uint64_t kl[2][2];              // the same, lo (e4m3, scaled by 2^10)
+      KG kh[2][2];                    // kg^T rows row0 + 16*kt + r16, tokens 32*ks + (slots)
+      uint64_t kl[2][2];              // fp32 tokens: the lo part (e4m3, scaled by 2^10)
       float gd;                       // gdec row row0 + 16*((r16 >> 2) & 1) + 4*quad + (r16 & 3)
     };
     // fragment (tt, K-block s) of w; fragments (2s + kt, ks) of kg^T; u tiles
@@ -223,10 +245,12 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          f.kh[kt][ks] = __builtin_bit_cast(bf16x8, buf_load16(r, L.kgh + o_kg + 1024 * (2 * kt + ks)));
-        const u32x4 l = buf_load16(r, L.kgl + o_kl + 1024 * kt);
-        f.kl[kt][0] = (uint64_t)l.y << 32 | l.x;
-        f.kl[kt][1] = (uint64_t)l.w << 32 | l.z;
+          f.kh[kt][ks] = __builtin_bit_cast(KG, buf_load16(r, L.kgh + o_kg + 1024 * (2 * kt + ks)));
+        if constexpr (F32) {
+          const u32x4 l = buf_load16(r, L.kgl + o_kl + 1024 * kt);
+          f.kl[kt][0] = (uint64_t)l.y << 32 | l.x;
+          f.kl[kt][1] = (uint64_t)l.w << 32 | l.z;
+        }
       }
       f.gd = __uint_as_float(buf_load4(r, o_gd));
     };
@@ -301,20 +325,29 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
           else uv = __builtin_bit_cast(f32x4, cur.u[j][ct]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = uv[e] - sum[e];
-          sV[c & 1][tt][ct][lane] = half_frag(v);
-          sV8[c & 1][tt][ct][lane] = pack4_fp8(v);
+          if constexpr (F32) {
+            sV[c & 1][tt][ct][lane] = half_frag(v);
+            sV8[c & 1][tt][ct][lane] = pack4_fp8(v);
+          } else {
+            sV[c & 1][tt][ct][lane] = half_frag16(v);
+          }
         }
       }
       __syncthreads();                                           // B
       // ---- 3. h = Diag(gdec) h + kg^T v_new
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        Frag vb[2];
-        uint64_t v8[2];
+        using VF = typename std::conditional<F32, Frag, Frag16>::type;
+        VF vb[2];
+        uint64_t v8[2] = {0, 0};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          vb[ks] = join_halves(sV[c & 1][2 * ks][ct][lane], sV[c & 1][2 * ks + 1][ct][lane]);
-          v8[ks] = (uint64_t)sV8[c & 1][2 * ks][ct][lane] | ((uint64_t)sV8[c & 1][2 * ks + 1][ct][lane] << 32);
+          if constexpr (F32) {
+            vb[ks] = join_halves(sV[c & 1][2 * ks][ct][lane], sV[c & 1][2 * ks + 1][ct][lane]);
+            v8[ks] = (uint64_t)sV8[c & 1][2 * ks][ct][lane] | ((uint64_t)sV8[c & 1][2 * ks + 1][ct][lane] << 32);
+          } else {
+            vb[ks] = join_halves16(sV[c & 1][2 * ks][ct][lane], sV[c & 1][2 * ks + 1][ct][lane]);
+          }
         }
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
@@ -327,10 +360,12 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
           for (int ks = 0; ks < 2; ++ks) {
             acc = mfma(cur.kh[kt][ks], vb[ks].hi, acc);
             acc = mfma(cur.kh[kt][ks], vb[ks].lo, acc);
-            acc8 = mfma_fp8(cur.kl[kt][ks], v8[ks], acc8);
+            if constexpr (F32) acc8 = mfma_fp8(cur.kl[kt][ks], v8[ks], acc8);
           }
+          if constexpr (F32) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] += acc8[e] * (1.f / KGL_SCALE);
+            for (int e = 0; e < 4; ++e) acc[e] += acc8[e] * (1.f / KGL_SCALE);
+          }
           hs[kt][ct] = acc;
         }
       }
@@ -379,9 +414,10 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     const int ow = wave - NS;
     const int owu = __builtin_amdgcn_readfirstlane(ow);   // uniform: the Aqk block tests are scalar branches
     auto aqk_live = [](int tt, int ks) { return 32 * ks <= 16 * tt + 15; };
+    using AQ = typename std::conditional<F32, Op<ST>, OpA16>::type;   // Aqk: fp16 with bf16 tokens
     struct OF {
       Op<ST> q[TPO][NS];    // qg rows 16*(TPO*ow + j) + r16, channels 32*kb + (slots of lane / 16)
-      Op<ST> aq[TPO][2];    // Aqk rows 16*(TPO*ow + j) + r16, tokens 32*ks + (slots)
+      AQ aq[TPO][2];        // Aqk rows 16*(TPO*ow + j) + r16, tokens 32*ks + (slots)
     };
     // fragments (TPO*ow + j, kb) of qg and (TPO*ow + j, ks) of Aqk
     constexpr uint32_t FW = 512 * ES;
@@ -398,7 +434,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
           // token block ks of Aqk rows 16*tt .. +15 is zero when it lies wholly
           // above the diagonal: not loaded, and its product skipped
           if (aqk_live(TPO * owu + j, ks)) f.aq[j][ks].load(r, o_a + FW * (2 * j + ks));
-          else f.aq[j][ks] = Op<ST>{};
+          else f.aq[j][ks] = AQ{};
         }
       }
     };
@@ -453,9 +489,13 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
           if constexpr (F32) hl[kb] = sHl[b][kb][ct][lane];
           else hl[kb] = hh[kb];
         }
-        Frag vf[2];
+        using VF = typename std::conditional<F32, Frag, Frag16>::type;
+        VF vf[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) vf[ks] = join_halves(sV[b][2 * ks][ct][lane], sV[b][2 * ks + 1][ct][lane]);
+        for (int ks = 0; ks < 2; ++ks) {
+          if constexpr (F32) vf[ks] = join_halves(sV[b][2 * ks][ct][lane], sV[b][2 * ks + 1][ct][lane]);
+          else vf[ks] = join_halves16(sV[b][2 * ks][ct][lane], sV[b][2 * ks + 1][ct][lane]);
+        }
 #pragma unroll
         for (int j = 0; j < TPO; ++j) {
           // o^T tile tt = TPO*ow + j: this lane holds token 16*tt + r16, columns
@@ -467,7 +507,10 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
           // zero 32-token blocks are skipped)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
-            if (aqk_live(TPO * owu + j, ks)) acc = mma_out(vf[ks].hi, F32 ? vf[ks].lo : vf[ks].hi, use.aq[j][ks], acc);
+            if (aqk_live(TPO * owu + j, ks)) {
+              if constexpr (F32) acc = mma_out(vf[ks].hi, vf[ks].lo, use.aq[j][ks], acc);
+              else acc = mfma(vf[ks].hi, use.aq[j][ks].v, acc);
+            }
           pend[j][ct] = acc;
         }
       }

@@ -99,9 +99,9 @@ def _ws(lib, p, summary=False):
 def test_workspace_size_layer_and_monotone(lib):
     st, b = _ws(lib, _problem())
     assert st == 0
-    # One record per (head, chunk): w, qg (bf16 64x128), kg^T hi (bf16 128x64) and lo
-    # (e4m3 128x64), Aqk (bf16 64x64), the chunk decay (fp32 128) and u (fp16 64x128).
-    per = 64 * 128 * 2 * 2 + 128 * 64 * 2 + 128 * 64 + 64 * 64 * 2 + 128 * 4 + 128 * 64 * 2
+    # One record per (head, chunk): w, qg (bf16 64x128), kg^T (fp16 128x64), Aqk (fp16
+    # 64x64), the chunk decay (fp32 128) and u (fp16 64x128).
+    per = 64 * 128 * 2 * 2 + 128 * 64 * 2 + 64 * 64 * 2 + 128 * 4 + 128 * 64 * 2
     assert b >= 32 * 128 * per and b < 32 * 128 * per + 8 * 256
     prev = 0
     for T in (0, 1, 64, 65, 1000, 8192):
