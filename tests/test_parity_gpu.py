@@ -116,6 +116,17 @@ def test_beta_zero_is_pure_decay(gpu_lib):
     fwd_case(gpu_lib, p)
 
 
+@pytest.mark.parametrize("vscale", [1e-3, 1e3])
+def test_value_scale_far_from_unit(gpu_lib, vscale):
+    """With bf16 tokens the workspace keeps u = (I+L)^-1 (beta v) and the scan
+    v_new = u - w h in fp16 (normal from 6.1e-5 to 65504).  v scaled by 1e-3 and
+    by 1e3 (|v| up to about 4e3) both match the oracle to the usual bars, the
+    errors being relative to the outputs' size."""
+    p = ks.make("layer", T=200, H=2, h0_std=0.0)
+    p.v = ks.bf16_round(p.v * np.float32(vscale))
+    fwd_case(gpu_lib, p)
+
+
 def test_state_keeps_kg_at_fp16_precision(gpu_lib):
     """With bf16 tokens kg^T reaches the state in fp16 (11 significant bits)
     against v_new as an fp16 hi/lo pair; this case's final state measures
