@@ -391,8 +391,9 @@ kda_status_t plan_bwd(const kda_problem_t* p, BwdPlan& bp) {
   const size_t nblk = (size_t)((f.tokens + kda::BWD_GATE_TOKENS - 1) / kda::BWD_GATE_TOKENS);
   size_t off = align256(f.off_rec);            // the chunk map only; no forward records
   bp.off_rec = off;  off = align256(off + slots * kda::bwd_rec(p->K, p->V).bytes);
-  bp.off_h = off;    off = align256(off + slots * p->K * p->V * sizeof(float));
-  bp.off_dh = off;   off = align256(off + slots * p->K * p->V * sizeof(float));
+  // the chunk-entry states and the exit gradients in fp16 (2 bytes per element)
+  bp.off_h = off;    off = align256(off + slots * p->K * p->V * 2);
+  bp.off_dh = off;   off = align256(off + slots * p->K * p->V * 2);
   bp.off_dqn = off;  off = align256(off + th * p->K * sizeof(float));
   bp.off_dkn = off;  off = align256(off + th * p->K * sizeof(float));
   bp.off_db = off;   off = align256(off + th * sizeof(float));
@@ -459,9 +460,9 @@ kda_status_t kda_chunk_bwd(const kda_problem_t* p, const void* q, const void* k,
   a.flags = p->flags; a.scale = p->scale; a.eps = p->eps; a.lower_bound = p->lower_bound;
   a.rec = reinterpret_cast<float*>(ws + bp.off_rec);
   a.h0 = initial_state;
-  a.h_store = reinterpret_cast<const float*>(ws + bp.off_h);
-  a.h_store_w = reinterpret_cast<float*>(ws + bp.off_h);
-  a.dh_store = reinterpret_cast<float*>(ws + bp.off_dh);
+  a.h_store = reinterpret_cast<const _Float16*>(ws + bp.off_h);
+  a.h_store_w = reinterpret_cast<_Float16*>(ws + bp.off_h);
+  a.dh_store = reinterpret_cast<_Float16*>(ws + bp.off_dh);
   a.dh0 = dh0;
   a.dqn = reinterpret_cast<float*>(ws + bp.off_dqn);
   a.dkn = reinterpret_cast<float*>(ws + bp.off_dkn);

@@ -7,10 +7,13 @@
 // inter-chunk recurrence of the state gradient, the WY / intra-chunk
 // backward and the reverse cumsum of the gate gradient) and 2.5 (the gate
 // backward), and "Hyper-Parallel Chunk KDA" section 5.2 (backward stages).
-// All values are fp32.  The two state scans and the chunk kernel's passes over
-// K and V multiply bf16 hi/lo operand pairs (~16 significant bits per operand,
-// fp32 accumulation, three passes per product); the other chunk-local
-// products run on the fp32 matrix cores.  The decay
+// All values are fp32, except the chunk-entry states and the exit gradients
+// that the scans hand to the chunk kernel, stored in fp16 (11 significant
+// bits; magnitudes up to 65504, the forward's bound on v_new with bf16
+// tokens).  The two state scans and the chunk kernel's passes over K and V
+// multiply bf16 hi/lo operand pairs (~16 significant bits per operand, fp32
+// accumulation, three passes per product); the other chunk-local products run
+// on the fp32 matrix cores.  The decay
 // ratios exp(G_i - G_j) of a chunk are never formed from a positive exponent:
 // a block of rows against an earlier block splits at the later block's first
 // row r into 2^(G_i - G_r) 2^(G_r - G_j), both <= 1 (G is the in-chunk cumsum,
@@ -73,6 +76,8 @@ template <> __device__ __forceinline__ f32x4 ldb4<bf16_t>(rsrc_t r, uint32_t o) 
   x[3] = __uint_as_float(u.y & 0xffff0000u);
   return x;
 }
+// Four consecutive fp16 elements (8 bytes, aligned) as floats.
+__device__ __forceinline__ f32x4 ld4h(const _Float16* p) { return unpack4_f16(*reinterpret_cast<const u32x2*>(p)); }
 // Four consecutive elements as floats (8 bytes of bf16 or 16 bytes of fp32, aligned).
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 ld4(const bf16_t* p) {
@@ -258,7 +263,7 @@ __device__ __forceinline__ void quad_transpose(f32x4& x, int b) {
 }
 
 // The chunk-entry states for the backward, in fp32 from the fp32 records:
-// h <- D h + kg^T (u - w h), every entry state stored.  Operands per chunk:
+// h <- D h + kg^T (u - w h), every entry state stored (in fp16).  Operands per chunk:
 // -w as A[token][K] and kg^T = (k 2^(G_C - G))^T as A[K][token].
 template <int KD, int VD>
 __global__ __launch_bounds__(VD * 4) void bwd_state_kernel(BwdArgs a) {
@@ -292,9 +297,9 @@ __global__ __launch_bounds__(VD * 4) void bwd_state_kernel(BwdArgs a) {
     const float* rec = a.rec + slot * (int64_t)(R.bytes / 4);
     const float* Gc = rec + R.G + (min(BT, len - c * BT) - 1) * KD;
     {  // the chunk-entry state out
-      float* dst = a.h_store_w + slot * (int64_t)(KD * VD);
+      _Float16* dst = a.h_store_w + slot * (int64_t)(KD * VD);
 #pragma unroll
-      for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4*>(dst + sq_index(16 * t + 4 * g, col, VD)) = H[t];
+      for (int t = 0; t < NKT; ++t) *reinterpret_cast<u32x2*>(dst + sq_index(16 * t + 4 * g, col, VD)) = pack4_f16(H[t]);
     }
     // then the loads: u (v_new starts at u), -w and kg
     f32x4 vn[4];
@@ -412,9 +417,9 @@ __global__ __launch_bounds__(VD * 4) void bwd_scan_kernel(BwdArgs a) {
     const float* Gc = rec + R.G + (C - 1) * KD;
     // the exit gradient of this chunk out
     if (a.dh_store) {
-      float* dst = a.dh_store + slot * (int64_t)(KD * VD);
+      _Float16* dst = a.dh_store + slot * (int64_t)(KD * VD);
 #pragma unroll
-      for (int t = 0; t < NKT; ++t) *reinterpret_cast<f32x4*>(dst + sq_index(16 * t + 4 * g, col, VD)) = DH[t];
+      for (int t = 0; t < NKT; ++t) *reinterpret_cast<u32x2*>(dst + sq_index(16 * t + 4 * g, col, VD)) = pack4_f16(DH[t]);
     }
     // then the loads (a wave past the last fragment of a kind loads the last
     // one again and skips its write)
@@ -1018,8 +1023,8 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   const OV ov(tid);
   const OS os(tid);
   const float* rec = a.rec + P.slot * (int64_t)(R.bytes / 4);
-  const float* hc = a.h_store + P.slot * (int64_t)(KD * VD);
-  const float* dh = a.dh_store + P.slot * (int64_t)(KD * VD);
+  const _Float16* hc = a.h_store + P.slot * (int64_t)(KD * VD);
+  const _Float16* dh = a.dh_store + P.slot * (int64_t)(KD * VD);
   const IT* dout = static_cast<const IT*>(a.dout);
   const IT* vin = static_cast<const IT*>(a.v);
   const float* G = rec + R.G;
@@ -1098,11 +1103,11 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     for (int kb = 0; kb < KD / 32; ++kb) {
       const int k0 = 32 * kb + 8 * ov.q;
       float x[8];
-      *reinterpret_cast<f32x4*>(x) = *reinterpret_cast<const f32x4*>(hc + sq_index(k0, vc, VD));
-      *reinterpret_cast<f32x4*>(x + 4) = *reinterpret_cast<const f32x4*>(hc + sq_index(k0 + 4, vc, VD));
+      *reinterpret_cast<f32x4*>(x) = ld4h(hc + sq_index(k0, vc, VD));
+      *reinterpret_cast<f32x4*>(x + 4) = ld4h(hc + sq_index(k0 + 4, vc, VD));
       const Frag bh = split8(x);
-      *reinterpret_cast<f32x4*>(x) = *reinterpret_cast<const f32x4*>(dh + sq_index(k0, vc, VD));
-      *reinterpret_cast<f32x4*>(x + 4) = *reinterpret_cast<const f32x4*>(dh + sq_index(k0 + 4, vc, VD));
+      *reinterpret_cast<f32x4*>(x) = ld4h(dh + sq_index(k0, vc, VD));
+      *reinterpret_cast<f32x4*>(x + 4) = ld4h(dh + sq_index(k0 + 4, vc, VD));
       const Frag bd = split8(x);
 #pragma unroll
       for (int t = 0; t < OV::TPW; ++t) {
@@ -1170,13 +1175,13 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     // load per column for the four channels of the lane's quad, and a 4 x 4
     // transpose across the quad leaves each lane its own channel's columns.
     const int qb = ok.r16 & 3;   // this lane's place in its quad (= kc & 3)
-    const float* hq = hc + sq_index(kc & ~3, 8 * ok.q + qb, VD);
-    const float* dhq = dh + sq_index(kc & ~3, 8 * ok.q + qb, VD);
+    const _Float16* hq = hc + sq_index(kc & ~3, 8 * ok.q + qb, VD);
+    const _Float16* dhq = dh + sq_index(kc & ~3, 8 * ok.q + qb, VD);
     float dd = 0.f;   // this lane's quarter of the columns
 #pragma unroll
     for (int kb = 0; kb < VD / 32; ++kb) {
-      f32x4 h0 = ld4(hq + 4 * (32 * kb)), h1 = ld4(hq + 4 * (32 * kb + 4));
-      f32x4 d0 = ld4(dhq + 4 * (32 * kb)), d1 = ld4(dhq + 4 * (32 * kb + 4));
+      f32x4 h0 = ld4h(hq + 4 * (32 * kb)), h1 = ld4h(hq + 4 * (32 * kb + 4));
+      f32x4 d0 = ld4h(dhq + 4 * (32 * kb)), d1 = ld4h(dhq + 4 * (32 * kb + 4));
       quad_transpose(h0, qb);
       quad_transpose(h1, qb);
       quad_transpose(d0, qb);

@@ -44,9 +44,10 @@ struct BwdArgs {
   float scale, eps, lower_bound;
   float* rec;                 // [Hv * nchunks] backward records
   const float* h0;            // [N][Hv][K][V] or null (zero)
-  const float* h_store;       // [Hv * nchunks][K/4][V][4] chunk-entry states (four rows of a column together)
-  float* h_store_w;           // the same buffer, written by the state kernel
-  float* dh_store;            // [Hv * nchunks][K/4][V][4] gradients of the chunk-exit states (or null)
+  // fp16 [Hv * nchunks][K/4][V][4] chunk-entry states (four rows of a column together)
+  const _Float16* h_store;
+  _Float16* h_store_w;        // the same buffer, written by the state kernel
+  _Float16* dh_store;         // fp16 [Hv * nchunks][K/4][V][4] gradients of the chunk-exit states (or null)
   float* dh0;                 // [N][Hv][K][V] or null
   float *dqn, *dkn;           // [tokens][Hv][K]: per value head, w.r.t. normalised q / k
   float *dbeta_act, *dg_nat;  // [tokens][Hv] w.r.t. activated beta, [tokens][Hv][K] w.r.t. the decay
