@@ -234,8 +234,8 @@ kda_status_t kda_summary_merge_bwd(int32_t P, int32_t Hv, int32_t K, int32_t V,
  * the library holds on each GPU it runs on until the process ends.  It calls
  * no allocating routine.  Problems whose kda_chunk_fwd_workspace_size exceeds
  * KDA_NOALLOC_SCRATCH_BYTES are rejected with KDA_ERR_UNSUPPORTED (at K = V =
- * 128 in bf16 that is about 690 (head, 64-token chunk) pairs, e.g. 32 heads x
- * 1344 tokens).  Every call on one GPU shares that GPU's scratch: calls that
+ * 128 in bf16 that is about 900 (head, 64-token chunk) pairs, e.g. 32 heads x
+ * 1792 tokens).  Every call on one GPU shares that GPU's scratch: calls that
  * overlap on one GPU (two streams, two threads) race and must be serialised
  * by the caller.  The first call on a device looks up the scratch address on
  * that device (the stream's device is made current for the lookup and then
