@@ -7,10 +7,11 @@
 // inter-chunk recurrence of the state gradient, the WY / intra-chunk
 // backward and the reverse cumsum of the gate gradient) and 2.5 (the gate
 // backward), and "Hyper-Parallel Chunk KDA" section 5.2 (backward stages).
-// All values are fp32, except the chunk-entry states and the exit gradients
-// that the scans hand to the chunk kernel, stored in fp16 (11 significant
-// bits; magnitudes up to 65504, the forward's bound on v_new with bf16
-// tokens).  The two state scans and the chunk kernel's passes over K and V
+// Arithmetic is fp32.  Stored in fp16 (11 significant bits; magnitudes up to
+// 65504, the forward's bound on v_new with bf16 tokens): the record's w, u,
+// kg and qg, and the chunk-entry states and exit gradients that the scans
+// hand to the chunk kernel; the rest of the record (G, A, Aqk, beta, the norm
+// factors) stays fp32.  The two state scans and the chunk kernel's passes over K and V
 // multiply bf16 hi/lo operand pairs (~16 significant bits per operand, fp32
 // accumulation, three passes per product); the other chunk-local products run
 // on the fp32 matrix cores.  The decay
@@ -229,6 +230,26 @@ __device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
     x[4 + i] = b[i];
   }
 }
+// The same from fp16 sections of the record.
+__device__ __forceinline__ void ld8h(const _Float16* p, float (&x)[8]) {
+  const f32x4 a = ld4h(p), b = ld4h(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+__device__ __forceinline__ void ld8sh(const _Float16* p, float (&x)[8]) {
+  const f32x4 a = ld4h(p), b = ld4h(p + 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+// fp16 section of a record
+__device__ __forceinline__ const _Float16* h16(const float* p) { return reinterpret_cast<const _Float16*>(p); }
+__device__ __forceinline__ _Float16* h16(float* p) { return reinterpret_cast<_Float16*>(p); }
 // eight values at p[0..3] and p[16..19]: the slots of lane group g of a
 // fragment whose reduction index runs along the row (p = row + 32 kb + 4 g)
 __device__ __forceinline__ void ld8s(const float* p, float (&x)[8]) {
@@ -304,20 +325,20 @@ __global__ __launch_bounds__(VD * 4) void bwd_state_kernel(BwdArgs a) {
     // then the loads: u (v_new starts at u), -w and kg
     f32x4 vn[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) vn[rt] = ld4(rec + R.u + sq_index(16 * rt + 4 * g, col, VD));
+    for (int rt = 0; rt < 4; ++rt) vn[rt] = ld4h(h16(rec + R.u) + sq_index(16 * rt + 4 * g, col, VD));
     const float gcv = tid < KD ? Gc[tid] : 0.f;
     // (a wave past the last fragment loads the last one again and skips its write)
     float xw[IW][8], xk[IK][8];
 #pragma unroll
     for (int i = 0; i < IW; ++i) {
       const int f = min(wave + NW * i, NFW - 1);
-      ld8s(rec + R.w + (16 * (f / NKB) + r16) * KD + 32 * (f % NKB) + 4 * g, xw[i]);
+      ld8sh(h16(rec + R.w) + (16 * (f / NKB) + r16) * KD + 32 * (f % NKB) + 4 * g, xw[i]);
     }
 #pragma unroll
     for (int i = 0; i < IK; ++i) {
       const int f = min(wave + NW * i, NFK - 1);
       const int t = 32 * (f % 2) + (lane >> 1), k0 = 16 * (f / 2) + 8 * (lane & 1);
-      ld8(rec + R.kg + t * KD + k0, xk[i]);
+      ld8h(h16(rec + R.kg) + t * KD + k0, xk[i]);
     }
     __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
 #pragma unroll
@@ -428,7 +449,7 @@ __global__ __launch_bounds__(VD * 4) void bwd_scan_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < IG; ++i) {
       const int f = min(wave + NW * i, NFG - 1);
-      ld8s(rec + R.kg + (16 * (f / NKB) + r16) * KD + 32 * (f % NKB) + 4 * g, xg[i]);
+      ld8sh(h16(rec + R.kg) + (16 * (f / NKB) + r16) * KD + 32 * (f % NKB) + 4 * g, xg[i]);
     }
 #pragma unroll
     for (int i = 0; i < IA; ++i) {
@@ -439,8 +460,8 @@ __global__ __launch_bounds__(VD * 4) void bwd_scan_kernel(BwdArgs a) {
     for (int i = 0; i < IQ; ++i) {
       const int f = min(wave + NW * i, NFQ - 1);   // f = 2 * (block of 16 K) + (block of 32 tokens)
       const int o = (32 * (f % 2) + (lane >> 1)) * KD + 16 * (f / 2) + 8 * (lane & 1);
-      ld8(rec + R.qg + o, xq[i]);
-      ld8(rec + R.w + o, xw[i]);
+      ld8h(h16(rec + R.qg) + o, xq[i]);
+      ld8h(h16(rec + R.w) + o, xw[i]);
     }
     // do: this wave's two fragments (column block = wave), rows past the chunk zero
     float xd[2][8];
@@ -706,8 +727,8 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
       kgv[e] = kv[e] * ex2(gC[e] - gv[e]);
       qgv[e] = a.scale * qv[e] * ex2(gv[e]);
     }
-    *reinterpret_cast<f32x4*>(rec + R.kg + i) = kgv;
-    *reinterpret_cast<f32x4*>(rec + R.qg + i) = qgv;
+    *reinterpret_cast<u32x2*>(h16(rec + R.kg) + i) = pack4_f16(kgv);
+    *reinterpret_cast<u32x2*>(h16(rec + R.qg) + i) = pack4_f16(qgv);
   }
   if (tid < BT) rec[R.beta + tid] = sB[tid];
 
@@ -910,7 +931,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < TV::TPW; ++t)   // (u keeps four rows of a column together)
-      *reinterpret_cast<f32x4*>(rec + R.u + sq_index(16 * tv.rb + 4 * tv.q, 16 * (tv.cb0 + t) + tv.r16, VD)) = acc[t];
+      *reinterpret_cast<u32x2*>(h16(rec + R.u) + sq_index(16 * tv.rb + 4 * tv.q, 16 * (tv.cb0 + t) + tv.r16, VD)) = pack4_f16(acc[t]);
   }
   __syncthreads();
 #pragma unroll 4
@@ -937,7 +958,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     for (int t = 0; t < TK::TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        rec[R.w + (16 * tk.rb + 4 * tk.q + e) * KD + 16 * (tk.cb0 + t) + tk.r16] = acc[t][e];
+        h16(rec + R.w)[(16 * tk.rb + 4 * tk.q + e) * KD + 16 * (tk.cb0 + t) + tk.r16] = (_Float16)acc[t][e];
   }
 }
 
@@ -1028,8 +1049,8 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
   const IT* dout = static_cast<const IT*>(a.dout);
   const IT* vin = static_cast<const IT*>(a.v);
   const float* G = rec + R.G;
-  const float* kgr = rec + R.kg;
-  const float* qgr = rec + R.qg;
+  const _Float16* kgr = h16(rec + R.kg);
+  const _Float16* qgr = h16(rec + R.qg);
   auto VV = [&](int i, int c) { return i < P.C ? ldf(vin + ((P.tok0 + i) * a.Hv + h) * VD + c) : 0.f; };
   // normalised k: the chunk's raw k rows through a descriptor bounded at its
   // last token (rows past it read as zero), times each row's factor
@@ -1056,7 +1077,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int s2 = 0; s2 < NK; ++s2) {
       const int i4 = tid + NTH * s2;
-      xk[s2] = *reinterpret_cast<const f32x4*>(rec + R.kg + 4 * i4);
+      xk[s2] = ld4h(kgr + 4 * i4);
     }
 #pragma unroll
     for (int s2 = 0; s2 < NQ; ++s2) xq[s2] = *reinterpret_cast<const f32x4*>(rec + R.aqk + 4 * (tid + NTH * s2));
@@ -1098,7 +1119,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     // the K reductions as bf16 hi/lo products (three passes each): lane group q
     // takes rows 32 kb + 8 q .. +7 of h and dh' (two 16-byte loads in their
     // four-row layout) and the same channels of the w and kg rows
-    const float* wr = rec + R.w + ov.r16 * KD + 8 * ov.q;
+    const _Float16* wr = h16(rec + R.w) + ov.r16 * KD + 8 * ov.q;
 #pragma unroll
     for (int kb = 0; kb < KD / 32; ++kb) {
       const int k0 = 32 * kb + 8 * ov.q;
@@ -1111,7 +1132,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
       const Frag bd = split8(x);
 #pragma unroll
       for (int t = 0; t < OV::TPW; ++t) {
-        ld8(wr + 16 * ov.ti(t) * KD + 32 * kb, x);
+        ld8h(wr + 16 * ov.ti(t) * KD + 32 * kb, x);
         an[t] = mma3(split8(x), bh, an[t]);
         ld8(&sKG[(16 * ov.ti(t) + ov.r16) * LX + k0], x);
         ad[t] = mma3(split8(x), bd, ad[t]);
@@ -1130,7 +1151,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < OV::TPW; ++t) {
-      const f32x4 u4 = ld4(rec + R.u + sq_index(16 * ov.ti(t) + 4 * ov.q, vc, VD));
+      const f32x4 u4 = ld4h(h16(rec + R.u) + sq_index(16 * ov.ti(t) + 4 * ov.q, vc, VD));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = ov.row(t, e);
@@ -1219,10 +1240,10 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdArgs a) {
         const int i = ok.row(t, e);
         const float gi = G[i * KD + kc];
         const float ex = ex2(sGC[kc] - gi);
-        const float kgv = kgr[i * KD + kc];   // k^ 2^(G_C - G)
+        const float kgv = (float)kgr[i * KD + kc];   // k^ 2^(G_C - G)
         const float eq = a.scale * ex2(gi);
         dk[t][e] += ex * ak[t][e];
-        dG[t][e] += qgr[i * KD + kc] * aq[t][e] - kgv * ak[t][e];
+        dG[t][e] += (float)qgr[i * KD + kc] * aq[t][e] - kgv * ak[t][e];
         dGCp += kgv * ak[t][e];
         dq[t][e] += eq * aq[t][e];
       }

@@ -7,15 +7,16 @@
 
 namespace kda {
 
-// Backward record per (head, chunk), fp32 row-major, offsets in floats:
-//   G [64][K] in-chunk cumsum of the decay in log2 units (rows past the end keep
-//   the last value), beta [64] (activated), rk / rq [64] the factors that
-//   normalise each row of k and q (0 past the end; the normalised rows are the
-//   raw rows times these, formed where they are read), A [64][64] = (I + L)^-1,
-//   aqk [64][64] (scaled, zero above the diagonal), w [64][K], u [64][V] stored
-//   [16][V][4] (four consecutive rows of a column together), kg = k^ 2^(G_C - G)
-//   and qg = scale q^ 2^G [64][K] (k^, q^ the normalised rows, G_C the last row
-//   of G) for the state scans and the chunk kernel.
+// Backward record per (head, chunk), row-major, section offsets in floats:
+//   fp32: G [64][K] in-chunk cumsum of the decay in log2 units (rows past the
+//   end keep the last value), beta [64] (activated), rk / rq [64] the factors
+//   that normalise each row of k and q (0 past the end; the normalised rows are
+//   the raw rows times these, formed where they are read), A [64][64] =
+//   (I + L)^-1, aqk [64][64] (scaled, zero above the diagonal);
+//   fp16 (11 significant bits; magnitudes up to 65504): w [64][K], u [64][V]
+//   stored [16][V][4] (four consecutive rows of a column together),
+//   kg = k^ 2^(G_C - G) and qg = scale q^ 2^G [64][K] (k^, q^ the normalised
+//   rows, G_C the last row of G) for the state scans and the chunk kernel.
 struct BwdRec {
   size_t G, beta, rk, rq, A, aqk, w, u, kg, qg, bytes;
 };
@@ -28,10 +29,10 @@ __host__ __device__ constexpr BwdRec bwd_rec(int K, int V) {
   r.A = r.rq + 64;
   r.aqk = r.A + 64 * 64;
   r.w = r.aqk + 64 * 64;
-  r.u = r.w + 64 * (size_t)K;
-  r.kg = r.u + 64 * (size_t)V;
-  r.qg = r.kg + 64 * (size_t)K;
-  r.bytes = al256((r.qg + 64 * (size_t)K) * 4);
+  r.u = r.w + 32 * (size_t)K;           // (fp16 sections: half a float per element)
+  r.kg = r.u + 32 * (size_t)V;
+  r.qg = r.kg + 32 * (size_t)K;
+  r.bytes = al256((r.qg + 32 * (size_t)K) * 4);
   return r;
 }
 
