@@ -570,8 +570,24 @@ hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s
   if (a.seq.N == 0 || a.Hv == 0) return hipSuccess;
   if (a.seg_max < 1 || a.seg_len < 1) return hipErrorInvalidValue;
   const int VA = a.summary ? V + K : V;
-  constexpr int CTsel = 1;   // 16-column tiles (wider tiles leave CUs idle at the layer)
-  const long nb = (long)(VA / (16 * CTsel)) * a.Hv * a.seq.N * a.seg_max;
+  // 16-column tiles; the forward scan runs one workgroup per CU at a time.
+  // When its grid holds two or more rounds of those (bf16, K = V = 128),
+  // 32-column tiles: a workgroup then loads each chunk's shared operands once
+  // for twice the columns, and the scan is bound per CU by those loads (gqa
+  // 1912 -> 1564 us, varlen 1568 -> 1220 us).  With fewer tiles, wider tiles
+  // would leave CUs idle (the 32-head layer: 159 -> 261 us); the summary scan,
+  // without output waves, already runs several workgroups per CU and measured
+  // slower with them (2441 -> 2629 us at 512 summary tiles).
+  const long nb1 = (long)(VA / 16) * a.Hv * a.seq.N * a.seg_max;
+  int CTsel = 1;
+  if (!a.summary && dtype == 1 && K == 128 && V == 128) {
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (nb1 >= 2L * ncu) CTsel = 2;
+  }
+  const long nb = nb1 / CTsel;
   if (nb > 0x7fffffffL) return hipErrorInvalidValue;
   // K/32 state waves, plus the output waves in forward mode
   dim3 grid((unsigned)nb), block(K * 2 + (a.summary ? 0 : 64 * NOW));
@@ -581,6 +597,8 @@ hipError_t launch_scan(int K, int V, int dtype, const ScanArgs& a, hipStream_t s
     return a.fwd_records ? launch(scan_kernel<KK, VV, TT, true, CC, true>, grid, block, s, a)     \
                          : launch(scan_kernel<KK, VV, TT, true, CC, false>, grid, block, s, a);   \
   }
+  if (dtype == 1 && CTsel == 2 && K == 128 && V == 128)
+    return launch(scan_kernel<128, 128, bf16_t, false, 2, true>, grid, block, s, a);
   if (dtype == 1) {
     KDA_SCAN_CASE(128, 128, bf16_t, 1)
     KDA_SCAN_CASE(64, 64, bf16_t, 1)

@@ -478,6 +478,26 @@ def test_summary_small_matches_oracle(gpu_lib):
     check("S~", np64(S), rS, TOL_STATE)
 
 
+def test_wide_scan_tiles_forward(gpu_lib):
+    """64 heads x 8 column tiles of 16 = 512 tile scans, two rounds per CU: the
+    scan runs 32-column tiles (a workgroup loads each chunk's shared operands
+    once for two tiles)."""
+    fwd_case(gpu_lib, ks.make("layer", T=200, H=64))
+
+
+def test_many_tile_summary(gpu_lib):
+    """32 heads x (V + K) / 16 = 512 summary tile scans (16-column tiles; the
+    summary scan runs several workgroups per CU)."""
+    p = ks.make("layer", T=150, H=32, h0_std=0.0)
+    p.gate_in_kernel = False
+    rng = np.random.default_rng(7)
+    p.g = ks.bf16_round((-0.05 * rng.random(p.g.shape)).astype(np.float32))
+    M, S = _summary_gpu(gpu_lib, p)
+    rM, rS = orc.segment_summary(p)
+    check("M", np64(M), rM, TOL_STATE)
+    check("S~", np64(S), rS, TOL_STATE)
+
+
 @pytest.mark.parametrize("route", ["precomputed", "in_kernel"])
 def test_summary_deep_transition(gpu_lib, route):
     """M over 64 chunks in a regime where it stays O(0.1-1): a near-zero
