@@ -12,10 +12,10 @@
 //   A         = (I + L)^-1
 //   u = A (beta * v),  w = A (beta * k * 2^gamma)
 //   kg = k * 2^(gamma_C - gamma),  qg = scale * q * 2^gamma,  gdec = 2^gamma_C
-// Workspace per (head, chunk): w, qg [64][K] and Aqk [64][64] in the token
-// dtype; kg^T [K][64] as a bf16 hi part and an e4m3 lo part (together ~13
-// significant bits); u [64][V] and gdec [K] in fp32 (they feed the state
-// update directly).
+// Workspace per (head, chunk): w, qg [64][K] in the token dtype and gdec [K]
+// in fp32; with bf16 tokens kg^T [K][64], Aqk [64][64] and u [64][V] in fp16
+// (11 significant bits); with fp32 tokens Aqk and u in fp32 and kg^T as a bf16
+// hi part and an e4m3 lo part (together ~13 significant bits).
 //
 // Each wave owns 16 token rows and keeps them in registers in the matrix-core
 // operand layout (lane: row 16*wave + lane%16, channels 32*ks + 8*(lane/16) + e),
@@ -803,7 +803,7 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
   }
   __syncthreads();
 
-  // ---- u^T = (A diag(beta) v)^T (fp32),  w = A diag(beta) X (token dtype)
+  // ---- u^T = (A diag(beta) v)^T (fp16 | fp32),  w = A diag(beta) X (token dtype)
   // Both reduction slices are used by every wave: the strictly upper blocks
   // of A are zero in LDS, so the products need no per-wave bounds.
   {

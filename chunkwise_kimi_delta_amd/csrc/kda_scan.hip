@@ -1,5 +1,6 @@
 // Inter-chunk KDA state scan with the fused chunk output.  One workgroup per
-// (16-column value tile, value head, sequence).
+// (value tile of 16 columns, or of 32 when the grid holds two rounds or more,
+// value head, sequence).
 //
 // Follows "KDA Chunk Backward — TPU/Pallas Kernel Design", sections 1 and 1.2
 // (the forward output, v_new = u - w h, the inter-chunk recurrence) and the
@@ -16,7 +17,7 @@
 //      the next product; the workspace stores w, kg^T, qg and Aqk with the
 //      matching index permutation) and leaves it in LDS;       -- barrier A
 //   2. each state wave sums the shares of its own token tile(s), subtracts
-//      from u and leaves v_new as a bf16 hi/lo fragment in LDS; -- barrier B
+//      from u and leaves v_new as a hi/lo fragment in LDS;     -- barrier B
 //   3. every state wave updates its rows with the whole v_new, while two
 //      output waves form o from the same h and v_new fragments.
 // The output waves run their loads two chunks ahead and touch the workspace
