@@ -167,6 +167,18 @@ __device__ __forceinline__ void split2_f16(float a, float b, uint32_t& hi, uint3
   hi = __builtin_bit_cast(uint32_t, h);
   lo = __builtin_bit_cast(uint32_t, l);
 }
+// Two stacked accumulator tiles as one fp16 hi/lo operand fragment.
+__device__ __forceinline__ Frag16 split_pair16(const f32x4& x, const f32x4& y) {
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split2_f16(x[0], x[1], h0, l0);
+  split2_f16(x[2], x[3], h1, l1);
+  split2_f16(y[0], y[1], h2, l2);
+  split2_f16(y[2], y[3], h3, l3);
+  Frag16 f;
+  f.hi = __builtin_bit_cast(f16x8, u32x4{h0, h1, h2, h3});
+  f.lo = __builtin_bit_cast(f16x8, u32x4{l0, l1, l2, l3});
+  return f;
+}
 __device__ __forceinline__ f16x8 round8_f16(const float (&x)[8]) {
   f16x8 r;
 #pragma unroll

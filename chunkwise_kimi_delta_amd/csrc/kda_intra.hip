@@ -12,10 +12,10 @@
 //   A         = (I + L)^-1
 //   u = A (beta * v),  w = A (beta * k * 2^gamma)
 //   kg = k * 2^(gamma_C - gamma),  qg = scale * q * 2^gamma,  gdec = 2^gamma_C
-// Workspace per (head, chunk): w, qg [64][K] in the token dtype and gdec [K]
-// in fp32; with bf16 tokens kg^T [K][64], Aqk [64][64] and u [64][V] in fp16
-// (11 significant bits); with fp32 tokens Aqk and u in fp32 and kg^T as a bf16
-// hi part and an e4m3 lo part (together ~13 significant bits).
+// Workspace per (head, chunk): gdec [K] in fp32; with bf16 tokens w, qg [64][K],
+// kg^T [K][64], Aqk [64][64] and u [64][V] in fp16 (11 significant bits); with
+// fp32 tokens w, qg, Aqk and u in fp32 and kg^T as a bf16 hi part and an e4m3
+// lo part (together ~13 significant bits).
 //
 // Each wave owns 16 token rows and keeps them in registers in the matrix-core
 // operand layout (lane: row 16*wave + lane%16, channels 32*ks + 8*(lane/16) + e),
@@ -419,7 +419,9 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
       }
     }
     if (has_q) {
-      ST* qg = reinterpret_cast<ST*>(rec + RL.qg);
+      // qg: fp16 with bf16 tokens (the scan's h operand is an fp16 hi/lo pair)
+      using QT = typename std::conditional<F32, float, _Float16>::type;
+      QT* qg = reinterpret_cast<QT*>(rec + RL.qg);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         f32x4 x0, x1;
@@ -866,7 +868,8 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
     }
     // w^T tiles (X^T rows as the A operand): this lane holds token 16*I + r16,
     // channels 16*ct + 4*quad .. +3 -> one vector store
-    ST* wbase = reinterpret_cast<ST*>(rec + RL.w);
+    using WT = typename std::conditional<F32, float, _Float16>::type;   // w: fp16 with bf16 tokens
+    WT* wbase = reinterpret_cast<WT*>(rec + RL.w);
 #pragma unroll
     for (int ct = 0; ct < KD / 16; ++ct) {
       const f32x4 acc = tile(sXT, sXF, ct, false);

@@ -17,13 +17,14 @@ enum : uint32_t { F_GATE = 1u, F_SAFE = 2u, F_L2 = 4u, F_SIGMOID = 8u };
 // operand load of the scan is one contiguous 1 KiB (2 KiB for fp32) block; the
 // fp8 kgl keeps the two token blocks of a channel tile side by side per lane
 // (8 bytes each), so one 1 KiB load fetches both:
-//   w   [64][K]  token dtype   operand fragments, rows = tokens, reduction = channels
+//   w   [64][K]  fp16 | fp32   operand fragments, rows = tokens, reduction = channels
+//                              (fp16 with bf16 tokens)
 //   kgh [K][64]  fp16 | bf16   kg^T, rows = channels, reduction = tokens: fp16 with
 //                              bf16 tokens; with fp32 tokens its bf16 hi part and
 //   kgl [K][64]  fp8 e4m3      the lo part, 2^10 (kg^T - hi) (one byte per element;
 //                              channel tile kt, lane l, token block tb at
 //                              1024 kt + 16 l + 8 tb; fp32 tokens only)
-//   qg  [64][K]  token dtype   scale * q * 2^gamma, like w (forward only)
+//   qg  [64][K]  fp16 | fp32   scale * q * 2^gamma, like w (forward only)
 //   aqk [64][64] fp16 | fp32   tril(Aqk), rows = tokens, reduction = tokens (forward
 //                              only; fp16 with bf16 tokens)
 //   gd  [K]      fp32          2^gamma_C, the chunk decay (plain vector)

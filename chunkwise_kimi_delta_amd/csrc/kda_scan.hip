@@ -25,12 +25,13 @@
 // served from L2; they store chunk c's output one step later, between the
 // barriers of chunk c + 1, where they would otherwise wait.
 //
-// Precision.  h enters w h as a bf16 hi/lo pair (~16 significant bits).  With
-// bf16 tokens kg^T is stored in fp16 (11 bits, |kg| <= 1) and meets v_new as an
-// fp16 hi/lo pair (~22 bits); the output takes qg h in bf16 (hi parts) and
-// Aqk v_new in fp16 (Aqk fp16, v_new's hi part).  With fp32 tokens v_new is a
-// bf16 hi/lo pair and kg^T a bf16 hi part plus an e4m3 lo part (scaled by
-// 2^10) that meets v_new in e4m3 in an accumulator of its own (~13 bits).
+// Precision.  With bf16 tokens w, qg, Aqk and kg^T are stored in fp16 (11
+// bits, |kg| <= 1); h enters w h as an fp16 hi/lo pair (~22 bits), kg^T meets
+// v_new as an fp16 hi/lo pair, and the output takes qg h and Aqk v_new in fp16
+// (the hi parts of h and v_new).  With fp32 tokens h and v_new are bf16 hi/lo
+// pairs (~16 bits) against fp32 w, qg and Aqk, and kg^T is a bf16 hi part plus
+// an e4m3 lo part (scaled by 2^10) that meets v_new in e4m3 in an accumulator of
+// its own (~13 bits).
 //
 // Summary mode scans the augmented state [S~ | M] (K x (V + K)) from [0 | I]
 // with u = [u | 0] and writes S~ and M ("KDA Context Parallelism (KCP)",
@@ -71,6 +72,11 @@ template <> struct Op<float> {
   }
 };
 
+// An fp16 operand fragment as stored with bf16 tokens (w, qg, Aqk).
+struct Op16 {
+  f16x8 v;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = __builtin_bit_cast(f16x8, buf_load16(r, off)); }
+};
 // acc += A * (B.hi + B.lo) with A stored in the workspace
 __device__ __forceinline__ f32x4 mma_sb(const Op<bf16_t>& A, const Frag& B, f32x4 acc) {
   acc = mfma(A.v, B.hi, acc);
@@ -82,8 +88,15 @@ __device__ __forceinline__ f32x4 mma_sb(const Op<float>& A, const Frag& B, f32x4
   acc = mfma(f.lo, B.hi, acc);
   return mfma(f.hi, B.lo, acc);
 }
+__device__ __forceinline__ f32x4 mma_sb(const Op16& A, const Frag16& B, f32x4 acc) {
+  acc = mfma(A.v, B.hi, acc);
+  return mfma(A.v, B.lo, acc);
+}
 // Output products, A from LDS (hi [, lo]) and B stored: bf16 tokens use the
 // hi part only, fp32 tokens keep ~16 bits on both sides.
+__device__ __forceinline__ f32x4 mma_out(const f16x8& ahi, const f16x8&, const Op16& B, f32x4 acc) {
+  return mfma(ahi, B.v, acc);
+}
 __device__ __forceinline__ f32x4 mma_out(const bf16x8& ahi, const bf16x8&, const Op<bf16_t>& B, f32x4 acc) {
   return mfma(ahi, B.v, acc);
 }
@@ -120,11 +133,6 @@ __device__ __forceinline__ Frag16 join_halves16(const u32x4& a, const u32x4& b) 
   f.lo = __builtin_bit_cast(f16x8, u32x4{a.z, a.w, b.z, b.w});
   return f;
 }
-// An fp16 operand fragment of Aqk as stored with bf16 tokens.
-struct OpA16 {
-  f16x8 v;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = __builtin_bit_cast(f16x8, buf_load16(r, off)); }
-};
 __device__ __forceinline__ Frag join_halves(const u32x4& a, const u32x4& b) {
   Frag f;
   f.hi = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
@@ -153,6 +161,8 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
   constexpr RecLayout L = rec_layout(KD, VD, (int)sizeof(ST), RF);
   constexpr bool F32 = sizeof(ST) == 4;
   constexpr int ES = (int)sizeof(ST);
+  // w and qg fragments: fp16 with bf16 tokens, fp32 (split on use) with fp32 tokens
+  using OW = typename std::conditional<F32, Op<ST>, Op16>::type;
   constexpr int NS = KD / 32;         // state waves, 32 state rows each
   constexpr int TPW = 4 / NS;         // token tiles each state wave reduces
   constexpr int BV = 16 * CT;         // state columns per workgroup
@@ -163,7 +173,9 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
   __shared__ f32x4 sP[NS][4][CT][64];                       // per-wave shares of w h
   __shared__ u32x4 sV[2][4][CT][64];                        // v_new half fragments, by chunk parity
   __shared__ uint32_t sV8[2][F32 ? 4 : 1][CT][64];          // v_new as e4m3 (fp32 tokens: the kg^T lo pass)
-  __shared__ bf16x8 sHh[SUM ? 1 : 2][NS][CT][64];           // h fragments (hi) for the output
+  // h fragments (hi) for the output: fp16 with bf16 tokens, bf16 with fp32 tokens
+  using HT = typename std::conditional<F32, bf16x8, f16x8>::type;
+  __shared__ HT sHh[SUM ? 1 : 2][NS][CT][64];
   __shared__ bf16x8 sHl[(F32 && !SUM) ? 2 : 1][NS][CT][64]; // h fragments (lo), fp32 tokens
 
   // ---- block -> (tile, head, sequence); tiles of one (head, sequence) share an XCD
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     // kg^T: fp16 with bf16 tokens; bf16 hi + e4m3 lo with fp32 tokens
     using KG = typename std::conditional<F32, bf16x8, f16x8>::type;
     struct Ops {
-      Op<ST> w[4];                    // w rows 16*tt + r16, channels row0 + (slots of lane / 16)
+      OW w[4];                        // w rows 16*tt + r16, channels row0 + (slots of lane / 16)
       URaw u[TPW][CT];                // u rows 16*(TPW*s + j) + 4*quad .. +3, column v0 + 16*ct + r16
       KG kh[2][2];                    // kg^T rows row0 + 16*kt + r16, tokens 32*ks + (slots)
       uint64_t kl[2][2];              // fp32 tokens: the lo part (e4m3, scaled by 2^10)
@@ -299,7 +311,10 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
       // ---- 1. this wave's share of w h
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const Frag hb = split_pair(hs[0][ct], hs[1][ct]);
+        using HF = typename std::conditional<F32, Frag, Frag16>::type;
+        HF hb;
+        if constexpr (F32) hb = split_pair(hs[0][ct], hs[1][ct]);
+        else hb = split_pair16(hs[0][ct], hs[1][ct]);
         if constexpr (!SUM) {
           sHh[c & 1][s][ct][lane] = hb.hi;
           if constexpr (F32) sHl[c & 1][s][ct][lane] = hb.lo;
@@ -415,9 +430,9 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
     const int ow = wave - NS;
     const int owu = __builtin_amdgcn_readfirstlane(ow);   // uniform: the Aqk block tests are scalar branches
     auto aqk_live = [](int tt, int ks) { return 32 * ks <= 16 * tt + 15; };
-    using AQ = typename std::conditional<F32, Op<ST>, OpA16>::type;   // Aqk: fp16 with bf16 tokens
+    using AQ = typename std::conditional<F32, Op<ST>, Op16>::type;   // Aqk: fp16 with bf16 tokens
     struct OF {
-      Op<ST> q[TPO][NS];    // qg rows 16*(TPO*ow + j) + r16, channels 32*kb + (slots of lane / 16)
+      OW q[TPO][NS];        // qg rows 16*(TPO*ow + j) + r16, channels 32*kb + (slots of lane / 16)
       AQ aq[TPO][2];        // Aqk rows 16*(TPO*ow + j) + r16, tokens 32*ks + (slots)
     };
     // fragments (TPO*ow + j, kb) of qg and (TPO*ow + j, ks) of Aqk
@@ -483,7 +498,7 @@ __global__ __launch_bounds__(SUM ? KD * 2 : KD * 2 + 64 * NOW) void scan_kernel(
       const int b = c & 1;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        bf16x8 hh[NS], hl[NS];
+        HT hh[NS], hl[NS];
 #pragma unroll
         for (int kb = 0; kb < NS; ++kb) {
           hh[kb] = sHh[b][kb][ct][lane];
