@@ -158,7 +158,10 @@ kda_status_t kda_chunk_bwd_workspace_size(const kda_problem_t* p, size_t* bytes)
  * recomputed (the call runs the forward's kernels first, keeping every
  * chunk-entry state in the workspace), then the state gradient is carried
  * backwards over the chunks and every chunk's local backward runs in
- * parallel.  All gradients are fp32, computed in fp32.
+ * parallel.  All gradients are fp32, computed in fp32; the chunk-entry states,
+ * the state gradients and the per-chunk w, u, kg and qg are handed between the
+ * kernels in fp16 with either token dtype, so a state or state-gradient entry
+ * beyond 65504 turns the gradients non-finite rather than silently inexact.
  *  q ... cu_seqlens : as in kda_chunk_fwd; p->state_rows must be 0 (dense states).
  *  dout  : dL/do, [.., Hv, V] in p->dtype.   dht : fp32 [N,Hv,K,V] or NULL (zero).
  *  dq, dk : fp32 [.., Hk, K] (grouped heads summed over their value heads; with
