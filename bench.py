@@ -419,12 +419,13 @@ CU_NUM, SIMD_NUM, XCD_NUM, CLOCK_GHZ = 256, 1024, 8, 2.4
 
 def summarize_mfma(csv_path, out_json):
     """Matrix-core and vector-ALU activity per kernel from one rocprofv3 --pmc
-    run of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_{BF16,F32,F8},
-    SQ_INSTS_VALU, SQ_ACTIVE_INST_VALU, SQ_BUSY_CU_CYCLES and GRBM_GUI_ACTIVE.
-    GRBM_GUI_ACTIVE is summed over the XCDs: one XCD's count is the kernel's
-    cycles.  MFMA util = busy cycles / (kernel cycles x SIMDs); VALU active =
-    4 x SQ_ACTIVE_INST_VALU (quad-cycles) / (kernel cycles x SIMDs); each
-    MOPS counts 512 flop."""
+    run of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_{BF16,F16,F32}
+    (and _F8 where collected), SQ_INSTS_VALU, SQ_ACTIVE_INST_VALU,
+    SQ_BUSY_CU_CYCLES and GRBM_GUI_ACTIVE.  GRBM_GUI_ACTIVE is summed over the
+    XCDs: one XCD's count is the kernel's cycles.  MFMA util = busy cycles /
+    (kernel cycles x SIMDs); VALU active = 4 x SQ_ACTIVE_INST_VALU (quad-cycles)
+    / (kernel cycles x SIMDs); each MOPS counts 512 flop.  bf16 and fp16 products
+    share one dense peak, so their sum is the 16-bit fraction of it."""
     data = _per_dispatch_counters(csv_path)
     out = {"source_sha256": source_hash()}
     lines = []
@@ -436,16 +437,18 @@ def summarize_mfma(csv_path, out_json):
         cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / XCD_NUM
         us = cyc / (CLOCK_GHZ * 1e3)
         util = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * SIMD_NUM) if cyc else None
-        flops = {d: c.get(f"SQ_INSTS_VALU_MFMA_MOPS_{d}", 0.0) * 512 for d in ("BF16", "F32", "F8")}
+        flops = {d: c.get(f"SQ_INSTS_VALU_MFMA_MOPS_{d}", 0.0) * 512 for d in ("BF16", "F16", "F32", "F8")}
         valu = c.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (cyc * SIMD_NUM) if cyc else None
-        bf16_frac = flops["BF16"] / (us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12) if us else None
+        f16 = flops["BF16"] + flops["F16"]
+        f16_frac = f16 / (us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12) if us else None
         out[short] = {"kernel": names[0], "counters_mean_per_dispatch": c, "kernel_cycles": cyc,
                       "kernel_us_from_counter": us, "mfma_busy_frac": util, "mfma_flop": flops,
-                      "bf16_mfma_flop_frac_of_peak": bf16_frac, "valu_insts": c.get("SQ_INSTS_VALU"),
+                      "mfma16_flop_frac_of_peak": f16_frac, "valu_insts": c.get("SQ_INSTS_VALU"),
                       "valu_active_frac": valu}
         lines.append(f"{short}: {us:.1f} us; MFMA busy {100 * util:.1f}% of SIMD cycles; MFMA flop bf16 "
-                     f"{flops['BF16'] / 1e9:.2f} G ({100 * bf16_frac:.1f}% of the bf16 peak over the kernel), "
-                     f"f32 {flops['F32'] / 1e9:.3f} G, f8 {flops['F8'] / 1e9:.3f} G; VALU insts "
+                     f"{flops['BF16'] / 1e9:.2f} G + fp16 {flops['F16'] / 1e9:.2f} G ({100 * f16_frac:.1f}% "
+                     f"of the 16-bit peak over the kernel), f32 {flops['F32'] / 1e9:.3f} G, "
+                     f"f8 {flops['F8'] / 1e9:.3f} G; VALU insts "
                      f"{c.get('SQ_INSTS_VALU', 0) / 1e6:.1f} M, VALU active {100 * valu:.1f}% of SIMD cycles")
     with open(out_json, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -559,7 +562,7 @@ def main():
     }
     if mfma:
         res["mfma_counters"] = {k: {"mfma_busy_frac": v["mfma_busy_frac"],
-                                    "bf16_mfma_flop_frac_of_peak": v["bf16_mfma_flop_frac_of_peak"],
+                                    "mfma16_flop_frac_of_peak": v.get("mfma16_flop_frac_of_peak"),
                                     "valu_active_frac": v["valu_active_frac"]}
                                 for k, v in mfma.items() if isinstance(v, dict) and "mfma_busy_frac" in v}
     if not args.no_cpu_baseline:
