@@ -159,7 +159,7 @@ template <int KD, int VD, typename IT> constexpr int intra_min_blocks() {
 
 template <int KD, int VD, typename IT, bool FWD>
 __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_kernel(IntraArgs a) {
-  using ST = IT;                                   // workspace type of w, qg, Aqk
+  using ST = IT;                                   // staging type of v^T and X^T (fp32 tokens)
   constexpr bool F32 = sizeof(IT) == 4;
   constexpr int NKS = KD / 32, NVS = VD / 32;
   constexpr int P64 = 64 + 4;                      // row stride of sLA (floats)

@@ -54,12 +54,9 @@ namespace kda {
 
 namespace {
 
-// One 8-element matrix-core operand fragment as stored in the workspace.
+// One 8-element matrix-core operand fragment as stored in the workspace: fp32
+// with fp32 tokens (split into bf16 hi/lo on use), fp16 with bf16 tokens (Op16).
 template <typename ST> struct Op;
-template <> struct Op<bf16_t> {
-  bf16x8 v;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = __builtin_bit_cast(bf16x8, buf_load16(r, off)); }
-};
 template <> struct Op<float> {
   f32x4 a, b;
   __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
@@ -78,10 +75,6 @@ struct Op16 {
   __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = __builtin_bit_cast(f16x8, buf_load16(r, off)); }
 };
 // acc += A * (B.hi + B.lo) with A stored in the workspace
-__device__ __forceinline__ f32x4 mma_sb(const Op<bf16_t>& A, const Frag& B, f32x4 acc) {
-  acc = mfma(A.v, B.hi, acc);
-  return mfma(A.v, B.lo, acc);
-}
 __device__ __forceinline__ f32x4 mma_sb(const Op<float>& A, const Frag& B, f32x4 acc) {
   const Frag f = A.split();
   acc = mfma(f.hi, B.hi, acc);
@@ -95,9 +88,6 @@ __device__ __forceinline__ f32x4 mma_sb(const Op16& A, const Frag16& B, f32x4 ac
 // Output products, A from LDS (hi [, lo]) and B stored: bf16 tokens use the
 // hi part only, fp32 tokens keep ~16 bits on both sides.
 __device__ __forceinline__ f32x4 mma_out(const f16x8& ahi, const f16x8&, const Op16& B, f32x4 acc) {
-  return mfma(ahi, B.v, acc);
-}
-__device__ __forceinline__ f32x4 mma_out(const bf16x8& ahi, const bf16x8&, const Op<bf16_t>& B, f32x4 acc) {
   return mfma(ahi, B.v, acc);
 }
 __device__ __forceinline__ f32x4 mma_out(const bf16x8& ahi, const bf16x8& alo, const Op<float>& B, f32x4 acc) {
