@@ -133,9 +133,10 @@ kda_status_t kda_chunk_fwd_workspace_size(const kda_problem_t* p, size_t* bytes)
  * Numeric range with bf16 tokens: the workspace keeps u = (I+L)^-1 (beta v), w,
  * qg, Aqk and kg^T in fp16, and the state update takes v_new = u - w h as an fp16
  * hi/lo pair; these stay exact to about 11 bits for magnitudes from 6.1e-5 to
- * 65504 (with unit-norm keys, |v| up to about 1e4).  Larger magnitudes become infinities, so
- * o and the final state turn non-finite rather than silently inexact.  fp32
- * token runs carry these values in fp32 and bf16 hi/lo pairs (no such bound).
+ * 65504 (with unit-norm keys, |v| up to about 1e4; without KDA_QK_L2NORM, |scale q|
+ * and |k| up to 65504).  Larger magnitudes become infinities, so o and the final
+ * state turn non-finite rather than silently inexact.  fp32 token runs carry
+ * these values in fp32 and bf16 hi/lo pairs (no such bound).
  */
 kda_status_t kda_chunk_fwd(const kda_problem_t* p,
                            const void* q, const void* k, const void* v,
