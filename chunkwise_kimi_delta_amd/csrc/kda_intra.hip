@@ -149,7 +149,13 @@ __device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
-__device__ __forceinline__ void store4(_Float16* p, const f32x4& v) { *reinterpret_cast<u32x2*>(p) = pack4_f16(v); }
+// The fp16 record sections (w, qg, Aqk with bf16 tokens) are written with
+// non-temporal stores: the scan that reads them back after this kernel then
+// runs about 7% faster at the layer shape; the same hint on kg^T and u moved
+// time from the scan into this kernel instead.
+__device__ __forceinline__ void store4(_Float16* p, const f32x4& v) {
+  __builtin_nontemporal_store(pack4_f16(v), reinterpret_cast<u32x2*>(p));
+}
 
 // Three workgroups per CU with bf16 tokens (at most 53 KB of LDS and 168
 // registers each); fp32 tokens need more LDS: two with K = V = 64, one otherwise.
