@@ -149,10 +149,10 @@ __device__ __forceinline__ void store4(bf16_t* p, const f32x4& v) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
-// The fp16 record sections (w, qg, Aqk with bf16 tokens) are written with
+// The fp16 record sections w, qg, Aqk (and u, below) are written with
 // non-temporal stores: the scan that reads them back after this kernel then
-// runs about 7% faster at the layer shape; the same hint on kg^T and u moved
-// time from the scan into this kernel instead.
+// runs about 10% faster at the layer shape; the same hint on kg^T moved time
+// from the scan into this kernel instead.
 __device__ __forceinline__ void store4(_Float16* p, const f32x4& v) {
   __builtin_nontemporal_store(pack4_f16(v), reinterpret_cast<u32x2*>(p));
 }
@@ -869,7 +869,7 @@ __global__ __launch_bounds__(256, (intra_min_blocks<KD, VD, IT>())) void intra_k
       if constexpr (F32) {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(rec + RL.ut) + uo) = acc;
       } else {
-        *reinterpret_cast<u32x2*>(reinterpret_cast<_Float16*>(rec + RL.ut) + uo) = pack4_f16(acc);
+        __builtin_nontemporal_store(pack4_f16(acc), reinterpret_cast<u32x2*>(reinterpret_cast<_Float16*>(rec + RL.ut) + uo));
       }
     }
     // w^T tiles (X^T rows as the A operand): this lane holds token 16*I + r16,
